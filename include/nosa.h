@@ -1,0 +1,197 @@
+/*
+ * nosa.h -- C ABI of the MI355X (gfx950) NOSA sparse-attention library.
+ *
+ * The operation is the decode step of NOSA ("Native and Offloadable Sparse
+ * Attention") as the pages on it describe it:
+ *   - keys are mean-pooled into compressed keys (kernel 32, stride 16)
+ *     [page "NOSA-1B 性能基准全解析", section 三.3 两阶段注意力 and the config table
+ *     of section 四; page "从论文到代码", section 2: pooling of k with cu_seqlens];
+ *   - each query head scores the compressed keys (compressed attention), the
+ *     scores of the heads sharing a KV head are summed and mean-pooled into one
+ *     importance per 64-token block (CIS score pooling)
+ *     [page "NOSA-1B 模型家族全景", core principle and the cis_pooling.py note];
+ *   - the top-k blocks plus the forced local window (1024 tokens = 16 blocks)
+ *     are kept [page "NOSA-1B 性能基准全解析", section 三.2 显式局部性约束];
+ *   - exact softmax attention runs over the kept blocks only [same page, 三.3].
+ *
+ * Conventions shared by every entry point
+ *   - bf16 values are passed as their 16-bit patterns (nosa_bf16).
+ *   - Every pointer except the two struct pointers and `workspace_bytes`-style
+ *     host outputs is DEVICE memory owned by the caller; the library never
+ *     allocates, frees or keeps a pointer after a call returns.  Buffers must
+ *     stay alive until the work queued on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work; none synchronises the host.
+ *   - `max_seqlen_*` are host-side upper bounds of the device lengths, used to
+ *     size grids without a device-to-host copy.  A device length above its
+ *     bound, a non-monotone cu_seqlens or a block_table entry outside
+ *     [0, num_pages) is a contract violation that the library does not detect.
+ *   - Host-checkable arguments are validated before anything is enqueued: a
+ *     NULL required pointer gives NOSA_ERR_NULL, inconsistent sizes
+ *     NOSA_ERR_INVALID, a shape this build has no kernel for
+ *     NOSA_ERR_UNSUPPORTED, a short workspace NOSA_ERR_WORKSPACE, and a failed
+ *     HIP launch NOSA_ERR_HIP.  Nothing aborts.
+ *   - No global state: calls on different streams may run concurrently as
+ *     long as they do not share output or workspace buffers.
+ *
+ * Supported shapes on the GPU: head_dim 128, block_size 64, kernel 32,
+ * stride 16, window a multiple of 64, num_q_heads / num_kv_heads in [1, 16],
+ * at most 8192 blocks (512K tokens) per sequence.
+ *
+ * Terms: L_s = cu_seqlens_k[s+1] - cu_seqlens_k[s] is the KV length of
+ * sequence s, including the token being decoded.  n_c(L) = (L-32)/16 + 1 for
+ * L >= 32 (else 0) compressed keys; key j pools tokens [16j, 16j+32).
+ * nb(L) = ceil(L/64) blocks.  G = num_q_heads / num_kv_heads.
+ */
+#ifndef NOSA_H
+#define NOSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NOSA_ABI_VERSION 1
+
+typedef uint16_t nosa_bf16; /* bf16 bit pattern */
+
+typedef enum nosa_status {
+    NOSA_OK = 0,
+    NOSA_ERR_NULL = 1,        /* a required pointer is NULL                 */
+    NOSA_ERR_INVALID = 2,     /* sizes or parameters are inconsistent       */
+    NOSA_ERR_UNSUPPORTED = 3, /* valid, but no GPU kernel for this shape    */
+    NOSA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required    */
+    NOSA_ERR_HIP = 5          /* a HIP call or kernel launch failed         */
+} nosa_status;
+
+/* Method parameters [page "NOSA-1B 性能基准全解析", config table of section 四:
+ * TopK 64, window 1024, block 64, kernel 32 / stride 16; 16 query / 2 KV heads]. */
+typedef struct nosa_params {
+    int32_t num_q_heads;  /* Hq                                                   */
+    int32_t num_kv_heads; /* Hkv; must divide Hq                                  */
+    int32_t head_dim;     /* d (GPU: 128)                                         */
+    int32_t block_size;   /* tokens per KV block = per page (GPU: 64)             */
+    int32_t kernel;       /* pooling window in tokens (GPU: 32)                   */
+    int32_t stride;       /* pooling stride in tokens (GPU: 16)                   */
+    int32_t topk;         /* blocks chosen besides the window, >= 0               */
+    int32_t window;       /* local window in tokens, a multiple of block_size     */
+    float scale;          /* logit scale; <= 0 selects 1/sqrt(head_dim)          */
+} nosa_params;
+
+/* Paged KV cache [page "NOSA技术架构解析", section 2.1: a PagedAttention-style
+ * memory pool].  One page holds one block of block_size tokens for every KV
+ * head.  Logical block b of sequence s lives in page block_table[s][b].
+ *   k_pool  [num_pages][Hkv][block_size][d]   token-major
+ *   v_pool  [num_pages][Hkv][d][block_size]   channel-major inside a page
+ *   kc_pool [num_pages][Hkv][block_size/stride][d]: compressed key j of
+ *           sequence s is slot j % (block_size/stride) of page
+ *           block_table[s][j / (block_size/stride)], so it needs no table of
+ *           its own.
+ *   block_table [batch][max_blocks_per_seq] int32. */
+typedef struct nosa_paged_kv {
+    const nosa_bf16* k_pool;
+    const nosa_bf16* v_pool;
+    nosa_bf16* kc_pool;
+    const int32_t* block_table;
+    int32_t max_blocks_per_seq;
+    int32_t num_pages;
+} nosa_paged_kv;
+
+/* ABI version of the loaded library (NOSA_ABI_VERSION at its build). */
+int nosa_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* nosa_status_string(nosa_status status);
+
+/* Workspace bytes needed by nosa_block_scores, nosa_sparse_attend and
+ * nosa_decode_step for any batch of at most `batch` sequences whose lengths
+ * are bounded by max_seqlen_q (queries; 1 for decode) and max_seqlen_k.
+ * Host only; enqueues nothing.  Errors: NOSA_ERR_NULL (params or bytes NULL),
+ * NOSA_ERR_INVALID, NOSA_ERR_UNSUPPORTED. */
+nosa_status nosa_workspace_size(const nosa_params* params, int32_t batch, int32_t max_seqlen_q,
+                                int32_t max_seqlen_k, size_t* bytes);
+
+/* Compressed-key builder [page "NOSA-1B 性能基准全解析", sections 三.3-三.4: mean
+ * pooling with kernel 32 / stride 16].  For every sequence s and KV head,
+ * writes keys j in [n_c(kc_valid_len[s]), n_c(L_s)) into kc_pool: key j is
+ * the bf16 round-to-nearest-even of the exact mean of K over tokens
+ * [16j, 16j+32) (sums are formed in fp64, so the result does not depend on
+ * the summation order).  kc_valid_len (device, [batch] int32) is the number
+ * of tokens whose keys are already pooled; NULL rebuilds every key.  Keys
+ * outside that range are not touched.  cu_seqlens_k: device [batch+1]. */
+nosa_status nosa_compress_keys(const nosa_params* params, const nosa_paged_kv* kv,
+                               const int32_t* cu_seqlens_k, const int32_t* kc_valid_len,
+                               int32_t batch, int32_t max_seqlen_k, void* stream);
+
+/* Block importance [pages "NOSA-1B 性能基准全解析" 三.3 and "NOSA-1B 模型家族全景"
+ * core principle].  For the decode query of each sequence (row s of q, at
+ * position L_s - 1) and each KV head g:
+ *   z_h[j] = scale * q_h . Kc_j for the G heads h of g and every key j < n_c(L_s);
+ *   sigma[j] = sum_h softmax_h(z_h)[j];
+ *   block_scores[s][0][g][b] = mean of sigma over the keys overlapping block b
+ *   (keys 4b-1 .. 4b+3 that exist), -inf if none, for b < nb(L_s); -inf
+ *   padding up to max_nb = ceil(max_seqlen_k / block_size).
+ * q: device [batch][Hq][d] bf16.  block_scores: device fp32
+ * [batch][max_qblk][Hkv][max_nb] with max_qblk = ceil(max_seqlen_q/block_size)
+ * (1 for decode).  cu_seqlens_q must be NULL (decode) in this build; a
+ * non-NULL value gives NOSA_ERR_UNSUPPORTED.  Kc must be valid for L_s tokens.
+ * Needs `workspace` of nosa_workspace_size bytes (device, any contents). */
+nosa_status nosa_block_scores(const nosa_params* params, const nosa_paged_kv* kv,
+                              const nosa_bf16* q, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
+                              int32_t max_seqlen_k, float* block_scores, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Block selection [page "NOSA-1B 性能基准全解析", section 三.2: a 1024-token window
+ * of 64-token blocks is always attended and TopK adds the 64 best blocks].
+ * For each row (sequence s, KV head g): the window is the last
+ * min(nb, window/block_size) blocks; among the earlier blocks the
+ * min(topk, count) with the largest block_scores are added, ties going to the
+ * lower block index.  sel_idx receives the kept block ids in ascending order,
+ * padded with -1 to max_sel = topk + window/block_size; sel_count the number
+ * kept (= min(nb, topk + window/block_size)).
+ * block_scores: device fp32 [batch][max_qblk][Hkv][max_nb] as produced by
+ * nosa_block_scores.  sel_idx: device int32 [batch][max_qblk][Hkv][max_sel];
+ * sel_count: device int32 [batch][max_qblk][Hkv].  cu_seqlens_q: NULL. */
+nosa_status nosa_select_blocks(const nosa_params* params, const float* block_scores,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               int32_t* sel_idx, int32_t* sel_count, void* stream);
+
+/* Exact attention over the kept blocks [page "NOSA-1B 性能基准全解析", 三.2-三.3].
+ * For sequence s and query head h (KV head g = h / G): softmax over the
+ * tokens t < L_s of the blocks listed in sel_idx[s][0][g][0 .. sel_count) of
+ * scale * q_h . K[t], applied to V.  out: device fp32 [batch][Hq][d];
+ * lse: device fp32 [batch][Hq] (natural log of the softmax denominator) or
+ * NULL.  Block ids must be distinct and < nb(L_s).  cu_seqlens_q: NULL.
+ * Needs `workspace` (device, any contents). */
+nosa_status nosa_sparse_attend(const nosa_params* params, const nosa_paged_kv* kv,
+                               const nosa_bf16* q, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
+                               int32_t max_seqlen_k, const int32_t* sel_idx,
+                               const int32_t* sel_count, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* One whole decode step, all of the above in order:
+ *   1. append the compressed keys completed by the current token (keys
+ *      [n_c(L_s - 1), n_c(L_s)); Kc must already hold every key of the first
+ *      L_s - 1 tokens);
+ *   2. score, pool, select (as nosa_block_scores + nosa_select_blocks);
+ *   3. attend (as nosa_sparse_attend).
+ * q: device [batch][Hq][d] bf16, the query of each sequence at position
+ * L_s - 1 (its K/V must already be in the pages).  out / lse as in
+ * nosa_sparse_attend (lse may be NULL).  sel_idx / sel_count / block_scores
+ * are optional outputs (NULL = not written) with the layouts above
+ * (max_qblk = 1).  Needs `workspace` (device, any contents). */
+nosa_status nosa_decode_step(const nosa_params* params, const nosa_paged_kv* kv,
+                             const nosa_bf16* q, const int32_t* cu_seqlens_k, int32_t batch,
+                             int32_t max_seqlen_k, float* out, float* lse, int32_t* sel_idx,
+                             int32_t* sel_count, float* block_scores, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NOSA_H */

@@ -1,0 +1,143 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/nosa.h declares, and rejects bad arguments on the host before anything
+is enqueued (so none of these calls launches a kernel)."""
+import ctypes
+import os
+
+import pytest
+
+from block_sparse_attention_nosa_amd import nosa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nosa.LIB_PATH):
+        from block_sparse_attention_nosa_amd import build
+        build.build()
+    return nosa.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = nosa.header_functions()
+    assert set(names) >= {"nosa_abi_version", "nosa_status_string", "nosa_workspace_size",
+                          "nosa_compress_keys", "nosa_block_scores", "nosa_select_blocks",
+                          "nosa_sparse_attend", "nosa_decode_step"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert nosa.abi_version() == 1
+    for s in range(6):
+        assert nosa.status_string(s)
+    assert nosa.status_string(0) == "ok"
+    assert nosa.status_string(99) == "unknown status"
+
+
+def test_header_is_plain_c():
+    """Signatures use only C scalar types, plain pointers and the header's own
+    structs: no torch, HIP or C++ types cross the boundary."""
+    import re
+    txt = open(os.path.join(ROOT, "include", "nosa.h")).read()
+    code = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    for bad in ("torch", "at::", "Tensor", "hipStream_t", "std::", "template", "&"):
+        assert bad not in code, bad
+
+
+def _ws(p, B, q, k):
+    return nosa.nosa_workspace_size(p, B, q, k)
+
+
+def test_workspace_size_for_the_workloads(L):
+    assert _ws(nosa.params(topk=16), 1, 1, 4096) > 0
+    assert _ws(nosa.params(topk=64), 8, 1, 16640) > 0
+    assert _ws(nosa.params(topk=64), 32, 1, 32768) > 0
+    assert _ws(nosa.params(num_q_heads=32, num_kv_heads=8, topk=96), 16, 1, 65536) > 0
+    # monotone in the batch and the length
+    p = nosa.params()
+    assert _ws(p, 8, 1, 16384) <= _ws(p, 16, 1, 16384) <= _ws(p, 16, 1, 32768)
+    assert _ws(p, 0, 0, 0) >= 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_q_heads", 0, 2), ("num_kv_heads", 3, 2), ("window", 1000, 2),
+    ("topk", -1, 2), ("head_dim", 64, 3), ("block_size", 32, 3), ("kernel", 16, 3),
+    ("stride", 8, 3), ("block_size", 48, 2)])
+def test_parameter_errors(L, field, value, status):
+    p = nosa.params()
+    setattr(p, field, value)
+    with pytest.raises(nosa.NosaError) as e:
+        nosa.nosa_workspace_size(p, 8, 1, 16384)
+    assert e.value.status == status
+
+
+def test_group_too_large_is_unsupported(L):
+    p = nosa.params(num_q_heads=32, num_kv_heads=1)
+    with pytest.raises(nosa.NosaError) as e:
+        nosa.nosa_workspace_size(p, 1, 1, 4096)
+    assert e.value.status == 3
+
+
+def test_null_and_size_errors(L):
+    f = L.nosa_workspace_size
+    out = ctypes.c_size_t()
+    assert f(None, 1, 1, 4096, ctypes.byref(out)) == 1
+    p = nosa.params()
+    assert f(ctypes.byref(p), 1, 1, 4096, None) == 1
+    assert f(ctypes.byref(p), -1, 1, 4096, ctypes.byref(out)) == 2
+    assert f(ctypes.byref(p), 1, 1, 0, ctypes.byref(out)) == 2
+    assert f(ctypes.byref(p), 1, 1, 8192 * 64 + 1, ctypes.byref(out)) == 3
+    assert f(ctypes.byref(p), 1, 64, 4096, ctypes.byref(out)) == 3   # prefill not in decode ABI
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _kv(max_blocks=256, pages=16):
+    return nosa.nosa_paged_kv(FAKE, FAKE, FAKE, FAKE, max_blocks, pages)
+
+
+def test_decode_step_host_errors(L):
+    p = nosa.params()
+    kv = _kv()
+    call = lambda **kw: L.nosa_decode_step(
+        ctypes.byref(kw.get("p", p)), ctypes.byref(kw.get("kv", kv)) if kw.get("kv", kv) else None,
+        kw.get("q", FAKE), kw.get("cu", FAKE), kw.get("B", 8), kw.get("Lk", 16384),
+        kw.get("out", FAKE), None, kw.get("sel", None), kw.get("cnt", None), None,
+        kw.get("ws", FAKE), kw.get("wsb", 0), None)
+    assert call(q=None) == 1
+    assert call(out=None) == 1
+    assert call(cu=None) == 1
+    assert call(kv=None) == 1
+    assert call(sel=FAKE) == 1                     # sel without count
+    assert call(kv=_kv(max_blocks=100)) == 2       # table cannot reach max_seqlen_k
+    assert call(kv=_kv(pages=0)) == 2
+    assert call(ws=None, wsb=1 << 40) == 4
+    assert call(wsb=100) == 4                      # too small
+    assert call(B=0) == 0                          # empty batch: nothing to do
+    bad = nosa.params(window=100)
+    assert call(p=bad) == 2
+
+
+def test_other_entry_points_host_errors(L):
+    p = nosa.params()
+    kv = _kv()
+    assert L.nosa_compress_keys(ctypes.byref(p), ctypes.byref(kv), None, None, 8, 16384,
+                                None) == 1
+    assert L.nosa_compress_keys(ctypes.byref(p), None, FAKE, None, 8, 16384, None) == 1
+    assert L.nosa_compress_keys(ctypes.byref(p), ctypes.byref(kv), FAKE, None, 0, 16384,
+                                None) == 0
+    assert L.nosa_block_scores(ctypes.byref(p), ctypes.byref(kv), FAKE, None, FAKE, 8, 1, 16384,
+                               None, FAKE, 1 << 30, None) == 1
+    assert L.nosa_block_scores(ctypes.byref(p), ctypes.byref(kv), FAKE, FAKE, FAKE, 8, 1, 16384,
+                               FAKE, FAKE, 1 << 30, None) == 3        # q-blocks: not here
+    assert L.nosa_block_scores(ctypes.byref(p), ctypes.byref(kv), FAKE, None, FAKE, 8, 1, 16384,
+                               FAKE, FAKE, 16, None) == 4
+    assert L.nosa_select_blocks(ctypes.byref(p), None, None, FAKE, 8, 1, 16384, FAKE, FAKE,
+                                None) == 1
+    assert L.nosa_sparse_attend(ctypes.byref(p), ctypes.byref(kv), FAKE, None, FAKE, 8, 1, 16384,
+                                FAKE, FAKE, FAKE, None, FAKE, 8, None) == 4
+    assert L.nosa_sparse_attend(ctypes.byref(p), ctypes.byref(kv), FAKE, None, FAKE, 8, 1, 16384,
+                                None, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1

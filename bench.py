@@ -1,0 +1,233 @@
+"""Benchmark of the NOSA sparse decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+Workload (default, config 2): the NOSA-1B attention shape -- 16 query / 2 KV
+heads, head_dim 128 -- decode batch 8 at 16K context, top-k 64 blocks + the
+1024-token window, 8 planted blocks per KV head, 256 decode steps that append
+to K/V and the pooled keys.  Inputs are seeded synthetic bf16 N(0, 1) values
+generated on the GPU.  Eight independent layer caches (136 MB each) are used
+in rotation so consecutive steps cannot be served from the 256 MB Infinity
+Cache; step i runs layer i % 8 at decode position (i // 8) % 256.
+
+A step is the whole hot path for the batch: append the pooled key completed by
+the current token, score the pooled keys, pool the scores into block
+importance, select top-k + window, attend over the kept blocks, merge.  The
+timed region is K such steps back to back on one stream, bracketed by device
+synchronisations; inputs are resident in HBM before it starts.
+
+Printed: one JSON line with the throughput (decode tokens/s = batch / step
+time), the roofline of the dominant kernel (the sparse attention, timed with
+HIP events around its own launches on the launch stream) and the CPU
+reference's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+LAYERS = 8
+
+
+def algorithmic_bytes(w, lens, append: bool):
+    """Bytes the method must move for one decode step (intermediates excluded):
+    pooled keys read, K and V of the kept tokens, q in, out + lse written, and
+    the pooled-key append (32 K rows read, one key written) when the current
+    token completes a key.  Returns (step_bytes, attention_bytes)."""
+    d, G, Hkv = w.head_dim, w.group, w.num_kv_heads
+    wb = w.window // w.block_size
+    step = attn = 0
+    for L in lens:
+        nc = (L - w.kernel) // w.stride + 1 if L >= w.kernel else 0
+        nb = (L + w.block_size - 1) // w.block_size
+        count = min(nb, w.topk + wb)
+        tail = L - w.block_size * (nb - 1)
+        toks = (count - 1) * w.block_size + tail if wb > 0 else count * w.block_size
+        kv = toks * d * 2 * 2
+        q_out = G * d * 2 + G * d * 4 + G * 4
+        app = (w.kernel * d * 2 + d * 2) if append else 0
+        step += Hkv * (nc * d * 2 + kv + q_out + app)
+        attn += Hkv * (kv + q_out)
+    return step, attn
+
+
+def build_layers(w, nsteps, device="cuda"):
+    import torch
+    from block_sparse_attention_nosa_amd import nosa, synth
+    layers = []
+    for li in range(LAYERS):
+        wl = synth.Workload(**{**w.__dict__, "seed": w.seed + 7919 * li, "meta": {}})
+        inp = synth.make_inputs(wl, device=device)
+        pg = synth.to_paged(inp, wl, device=device)
+        kv = nosa.paged_kv(pg["k_pool"], pg["v_pool"], pg["kc_pool"], pg["block_table"])
+        p = nosa.params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.kernel,
+                        w.stride, w.topk, w.window)
+        lens0 = [L - 1 for L in w.lens]
+        nosa.nosa_compress_keys(p, kv, synth.cu_from_lens(lens0, device), None, w.batch,
+                                max(lens0))
+        layers.append(dict(inp=inp, pg=pg, kv=kv, p=p))
+        torch.cuda.synchronize()
+    return layers
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2048)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from block_sparse_attention_nosa_amd import nosa, synth
+
+    w = synth.config(args.config)
+    if w.q_lens is not None:
+        print("config %d is a prefill chunk, not a decode step" % args.config, file=sys.stderr)
+        sys.exit(2)
+    nsteps = w.extra_tokens + 1
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t_setup = time.time()
+    layers = build_layers(w, nsteps)
+    B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    lens_at = [[L + t for L in w.lens] for t in range(nsteps)]
+    cu_at = [synth.cu_from_lens(l, "cuda") for l in lens_at]
+    maxL = max(lens_at[-1])
+    p = layers[0]["p"]
+    ws = torch.zeros(nosa.nosa_workspace_size(p, B, 1, maxL), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, Hq, d, device=dev)
+    lse = torch.empty(B, Hq, device=dev)
+    max_sel = w.topk + w.window // w.block_size
+    sels = [torch.empty(B, 1, Hkv, max_sel, dtype=torch.int32, device=dev) for _ in layers]
+    cnts = [torch.empty(B, 1, Hkv, dtype=torch.int32, device=dev) for _ in layers]
+    qs = [l["inp"]["q"] for l in layers]
+    stream = torch.cuda.current_stream()
+    print(f"[bench] setup {time.time() - t_setup:.1f}s; workload {w.name}: B={B} heads={Hq}/{Hkv} "
+          f"L={w.lens[0]}..{maxL} topk={w.topk} layers={LAYERS}", file=sys.stderr, flush=True)
+
+    def step(i):
+        li = i % LAYERS
+        t = (i // LAYERS) % nsteps
+        L = layers[li]
+        nosa.nosa_decode_step(L["p"], L["kv"], qs[li], cu_at[t], B, maxL, out, lse, ws,
+                              sel_idx=sels[li], sel_count=cnts[li], stream=stream)
+        return t
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # ---- timed region: K whole decode steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    ts = [step(args.warmup + i) for i in range(args.steps)]
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    step_bytes = np.mean([algorithmic_bytes(w, lens_at[t], (lens_at[t][0] - w.kernel) % w.stride == 0)[0]
+                          for t in ts])
+    tokens_per_s = B / (ms_step * 1e-3)
+    print(f"[bench] {args.steps} steps in {ms_total:.2f} ms -> {ms_step * 1e3:.2f} us/step, "
+          f"{step_bytes / 1e6:.2f} MB/step, {step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
+    # ---- dominant kernel: sparse attention over the kept blocks, timed alone
+    # with events on its launch stream, same layers and positions
+    na = min(args.steps, 512)
+    attn_bytes = []
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ea.record(stream)
+    for i in range(na):
+        li = i % LAYERS
+        t = (i // LAYERS) % nsteps
+        L = layers[li]
+        nosa.nosa_sparse_attend(L["p"], L["kv"], qs[li], None, cu_at[t], B, 1, maxL, sels[li],
+                                cnts[li], out, lse, ws, stream=stream)
+        attn_bytes.append(algorithmic_bytes(w, lens_at[t], False)[1])
+    eb.record(stream)
+    torch.cuda.synchronize()
+    us_attn = ea.elapsed_time(eb) * 1e3 / na
+    attn_gbs = float(np.mean(attn_bytes)) / (us_attn * 1e-6) / 1e9
+
+    # ---- CPU reference on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, layers[0], lens_at, args.cpu_sample_seconds)
+
+    res = {
+        "metric": "sparse-attn decode tokens/s at 16K ctx, batch 8; achieved HBM GB/s vs peak",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16 N(0,1) K/V/q, planted blocks, permuted 64-token pages)",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": d, "context": w.lens[0] - 1, "decode_steps": nsteps,
+                   "topk_blocks": w.topk, "window_tokens": w.window, "block": w.block_size,
+                   "pool_kernel": w.kernel, "pool_stride": w.stride, "layer_caches": LAYERS},
+        "step_hbm": {"algorithmic_bytes": int(step_bytes),
+                     "achieved_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+                     "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {"kernel": "sparse attention (nosa_sparse_attend)", "bound": "hbm",
+                     "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "us_per_launch": round(us_attn, 3),
+                     "algorithmic_bytes_per_launch": int(np.mean(attn_bytes))},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, layer, lens_at, budget_s):
+    """The CPU reference as it stands, on host copies of layer 0: whole decode
+    steps (pooling, scoring, selection, attention) for the full batch, repeated
+    until about `budget_s` seconds of work."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_nosa_amd import synth
+    from oracle import oracle as ora
+
+    inp = layer["inp"]
+    host = dict(k=inp["k"].cpu(), v=inp["v"].cpu(), cu_k_store=inp["cu_k_store"].cpu())
+    q = synth.bits(inp["q"])
+    op = ora.Params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.kernel, w.stride,
+                    w.topk, w.window)
+    n, t0 = 0, time.time()
+    while True:
+        k, v, cu = synth.packed_live(host, w, n % len(lens_at))
+        ora.forward(op, q, None, synth.bits(k), synth.bits(v), cu.numpy())
+        n += 1
+        if time.time() - t0 >= budget_s or n >= 64:
+            break
+    dt = time.time() - t0
+    return {"value": round(w.batch * n / dt, 2), "unit": "tokens/s", "cores": ora.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} whole decode steps of {w.name} (batch {w.batch}, layer 0, positions "
+                      f"0..{n - 1}) on the host, fp64 reference with OpenMP over (sequence, head)"}
+
+
+if __name__ == "__main__":
+    main()

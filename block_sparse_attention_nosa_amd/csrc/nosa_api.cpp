@@ -28,6 +28,7 @@ nosa_status check_params(const nosa_params* p)
         p->stride != kPoolS)
         return NOSA_ERR_UNSUPPORTED;
     if (p->num_q_heads / p->num_kv_heads > kMaxGroup) return NOSA_ERR_UNSUPPORTED;
+    if (p->window / p->block_size > kMaxWindowBlocks) return NOSA_ERR_UNSUPPORTED;
     return NOSA_OK;
 }
 
@@ -61,13 +62,31 @@ int pick_score_tiles(long long tiles)
     return 1;
 }
 
-int pick_attn_rounds(long long blocks)
+// Blocks per wave (rounds) and workgroups per pair for `span` list entries
+// per pair: about 512 workgroups of 4 waves in total (two per CU), at most
+// `max_groups` partials per head.
+// Blocks per wave (rounds, one of the compiled 1, 2, 3, 4, 6, 8) and
+// workgroups per pair for `span` list entries per pair: about 512 workgroups
+// of 4 waves in total -- two per CU, one dispatch round -- and at most
+// `max_groups` partials per head.
+void pick_split(int span, long long pairs, int max_groups, int* groups, int* rounds)
 {
-    // aim at ~1024 workgroups of 4 waves; at most 4 blocks per wave
-    long long r = blocks / 4 / 1024;
-    if (r < 1) r = 1;
-    if (r > 4) r = 4;
-    return (int)r;
+    static const int kRounds[] = {1, 2, 3, 4, 6, 8};
+    if (span <= 0) {
+        *groups = 1;
+        *rounds = 1;
+        return;
+    }
+    const long long total_blocks = (long long)span * pairs;
+    int pick = 5;
+    for (int i = 0; i < 6; ++i)
+        if (total_blocks <= 4LL * 512 * kRounds[i]) {
+            pick = i;
+            break;
+        }
+    while (pick < 5 && ceil_div(span, 4 * kRounds[pick]) > max_groups) ++pick;
+    *rounds = kRounds[pick];
+    *groups = ceil_div(span, 4 * kRounds[pick]);
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -92,7 +111,6 @@ nosa_status make_plan(const nosa_params* p, int batch, int max_seqlen_k, Plan* p
     P.Lmax = max_seqlen_k;
     P.max_nc = num_keys(max_seqlen_k);
     P.max_nb = ceil_div(max_seqlen_k, kBlock);
-    P.sel_span = P.max_sel < P.max_nb ? P.max_sel : P.max_nb;
     const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->head_dim);
     P.scale_log2 = (float)(scale * 1.4426950408889634);
 
@@ -101,23 +119,51 @@ nosa_status make_plan(const nosa_params* p, int batch, int max_seqlen_k, Plan* p
     P.score_groups = ceil_div(nc1, 64 * P.score_tiles);
     P.nchunk = P.score_groups * 4;
     P.zstride = P.nchunk * 16 * P.score_tiles;
+    // the pooling step reads keys 4b-1 .. 4b+3 of every block b < max_nb
+    const int zneed = 4 * P.max_nb + 4;
+    if (P.zstride < zneed) P.zstride = ceil_div(zneed, 64) * 64;
 
-    const int span = P.sel_span > 0 ? P.sel_span : 1;
-    P.attn_rounds = pick_attn_rounds((long long)batch * P.Hkv * span);
-    P.nsplit = ceil_div(span, 4 * P.attn_rounds);
+    const int wn = P.wblocks < P.max_nb ? P.wblocks : P.max_nb;
+    P.win_groups = ceil_div(wn, 4);
+    const int ncand = P.max_nb > P.wblocks ? P.max_nb - P.wblocks : 0;
+    P.top_span = P.topk < ncand ? P.topk : ncand;
+    pick_split(P.top_span, (long long)batch * P.Hkv, kMaxSplit - P.win_groups, &P.top_groups,
+               &P.top_rounds);
+    P.nsplit = P.win_groups + P.top_groups;
+    const int aspan = P.max_sel < P.max_nb ? P.max_sel : P.max_nb;
+    pick_split(aspan, (long long)batch * P.Hkv, kMaxSplit, &P.attend_groups, &P.attend_rounds);
+    const int nparts = P.nsplit > P.attend_groups ? P.nsplit : P.attend_groups;
 
-    const size_t B = (size_t)batch;
+    const size_t B = (size_t)batch, pairs = B * P.Hkv;
     size_t off = 0;
-    P.off_z = off;      off += align256(B * P.Hq * (size_t)P.zstride * sizeof(float));
-    P.off_zpart = off;  off += align256(B * P.Hq * (size_t)P.nchunk * sizeof(float2));
-    P.off_scores = off; off += align256(B * P.Hkv * (size_t)P.max_nb * sizeof(float));
-    P.off_sel = off;    off += align256(B * P.Hkv * (size_t)P.max_sel * sizeof(int32_t));
-    P.off_cnt = off;    off += align256(B * P.Hkv * sizeof(int32_t));
-    P.off_po = off;     off += align256(B * P.Hq * (size_t)P.nsplit * kHeadDim * sizeof(float));
-    P.off_pml = off;    off += align256(B * P.Hq * (size_t)P.nsplit * sizeof(float2));
+    P.off_counter1 = off; off += align256(pairs * sizeof(uint32_t));
+    P.off_counter2 = off; off += align256(pairs * sizeof(uint32_t));
+    P.off_z = off;        off += align256(B * P.Hq * (size_t)P.zstride * sizeof(float));
+    P.off_zpart = off;    off += align256(B * P.Hq * (size_t)P.nchunk * sizeof(float2));
+    P.off_selpg = off;    off += align256(pairs * (size_t)(P.top_span > 0 ? P.top_span : 1) * sizeof(int2));
+    P.off_sel = off;      off += align256(pairs * (size_t)P.max_sel * sizeof(int32_t));
+    P.off_cnt = off;      off += align256(pairs * sizeof(int32_t));
+    P.off_po = off;       off += align256(B * P.Hq * (size_t)nparts * kHeadDim * sizeof(float));
+    P.off_pml = off;      off += align256(B * P.Hq * (size_t)nparts * sizeof(float2));
     P.bytes = off > 256 ? off : 256;
     *pl = P;
     return NOSA_OK;
+}
+
+Workspace carve(const Plan& pl, void* ws)
+{
+    char* base = static_cast<char*>(ws);
+    Workspace w;
+    w.counter1 = reinterpret_cast<uint32_t*>(base + pl.off_counter1);
+    w.counter2 = reinterpret_cast<uint32_t*>(base + pl.off_counter2);
+    w.z = reinterpret_cast<float*>(base + pl.off_z);
+    w.zpart = reinterpret_cast<float2*>(base + pl.off_zpart);
+    w.selpg = reinterpret_cast<int2*>(base + pl.off_selpg);
+    w.sel = reinterpret_cast<int32_t*>(base + pl.off_sel);
+    w.cnt = reinterpret_cast<int32_t*>(base + pl.off_cnt);
+    w.po = reinterpret_cast<float*>(base + pl.off_po);
+    w.pml = reinterpret_cast<float2*>(base + pl.off_pml);
+    return w;
 }
 
 }  // namespace nosa
@@ -125,9 +171,6 @@ nosa_status make_plan(const nosa_params* p, int batch, int max_seqlen_k, Plan* p
 using namespace nosa;
 
 namespace {
-
-template <class T>
-T* ws_at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
 nosa_status hip_status(hipError_t e) { return e == hipSuccess ? NOSA_OK : NOSA_ERR_HIP; }
 
@@ -191,8 +234,7 @@ nosa_status nosa_compress_keys(const nosa_params* params, const nosa_paged_kv* k
     if (st != NOSA_OK) return st;
     int gx = ceil_div(pl.max_nc > 0 ? pl.max_nc : 1, 16);
     if (kc_valid_len && gx > 64) gx = 64;  // grid-stride over whatever is left to pool
-    return hip_status(launch_kc_build(pl, *kv, cu_seqlens_k, kc_valid_len, false, gx,
-                                      as_stream(stream)));
+    return hip_status(launch_kc_build(pl, *kv, cu_seqlens_k, kc_valid_len, gx, as_stream(stream)));
 }
 
 nosa_status nosa_block_scores(const nosa_params* params, const nosa_paged_kv* kv,
@@ -215,13 +257,8 @@ nosa_status nosa_block_scores(const nosa_params* params, const nosa_paged_kv* kv
     st = make_plan(params, batch, max_seqlen_k, &pl);
     if (st != NOSA_OK) return st;
     if (!workspace || workspace_bytes < pl.bytes) return NOSA_ERR_WORKSPACE;
-    hipStream_t s = as_stream(stream);
-    float* z = ws_at<float>(workspace, pl.off_z);
-    float2* zpart = ws_at<float2>(workspace, pl.off_zpart);
-    st = hip_status(launch_scores(pl, *kv, q, cu_seqlens_k, z, zpart, s));
-    if (st != NOSA_OK) return st;
-    return hip_status(launch_select(pl, cu_seqlens_k, z, zpart, nullptr, block_scores, nullptr,
-                                    nullptr, s));
+    return hip_status(launch_scores_only(pl, *kv, q, cu_seqlens_k, carve(pl, workspace),
+                                         block_scores, as_stream(stream)));
 }
 
 nosa_status nosa_select_blocks(const nosa_params* params, const float* block_scores,
@@ -240,8 +277,8 @@ nosa_status nosa_select_blocks(const nosa_params* params, const float* block_sco
     Plan pl;
     st = make_plan(params, batch, max_seqlen_k, &pl);
     if (st != NOSA_OK) return st;
-    return hip_status(launch_select(pl, cu_seqlens_k, nullptr, nullptr, block_scores, nullptr,
-                                    sel_idx, sel_count, as_stream(stream)));
+    return hip_status(launch_select(pl, cu_seqlens_k, block_scores, sel_idx, sel_count,
+                                    as_stream(stream)));
 }
 
 nosa_status nosa_sparse_attend(const nosa_params* params, const nosa_paged_kv* kv,
@@ -265,12 +302,8 @@ nosa_status nosa_sparse_attend(const nosa_params* params, const nosa_paged_kv* k
     st = make_plan(params, batch, max_seqlen_k, &pl);
     if (st != NOSA_OK) return st;
     if (!workspace || workspace_bytes < pl.bytes) return NOSA_ERR_WORKSPACE;
-    hipStream_t s = as_stream(stream);
-    float* po = ws_at<float>(workspace, pl.off_po);
-    float2* pml = ws_at<float2>(workspace, pl.off_pml);
-    st = hip_status(launch_attend(pl, *kv, q, cu_seqlens_k, sel_idx, sel_count, po, pml, s));
-    if (st != NOSA_OK) return st;
-    return hip_status(launch_merge(pl, po, pml, out, lse, s));
+    return hip_status(launch_attend(pl, *kv, q, cu_seqlens_k, sel_idx, sel_count,
+                                    carve(pl, workspace), out, lse, as_stream(stream)));
 }
 
 nosa_status nosa_decode_step(const nosa_params* params, const nosa_paged_kv* kv,
@@ -292,23 +325,8 @@ nosa_status nosa_decode_step(const nosa_params* params, const nosa_paged_kv* kv,
     st = make_plan(params, batch, max_seqlen_k, &pl);
     if (st != NOSA_OK) return st;
     if (!workspace || workspace_bytes < pl.bytes) return NOSA_ERR_WORKSPACE;
-    hipStream_t s = as_stream(stream);
-    float* z = ws_at<float>(workspace, pl.off_z);
-    float2* zpart = ws_at<float2>(workspace, pl.off_zpart);
-    int32_t* sel = sel_idx ? sel_idx : ws_at<int32_t>(workspace, pl.off_sel);
-    int32_t* cnt = sel_count ? sel_count : ws_at<int32_t>(workspace, pl.off_cnt);
-    float* po = ws_at<float>(workspace, pl.off_po);
-    float2* pml = ws_at<float2>(workspace, pl.off_pml);
-    // the current token completes at most one pooled key per sequence
-    st = hip_status(launch_kc_build(pl, *kv, cu_seqlens_k, nullptr, true, 1, s));
-    if (st != NOSA_OK) return st;
-    st = hip_status(launch_scores(pl, *kv, q, cu_seqlens_k, z, zpart, s));
-    if (st != NOSA_OK) return st;
-    st = hip_status(launch_select(pl, cu_seqlens_k, z, zpart, nullptr, block_scores, sel, cnt, s));
-    if (st != NOSA_OK) return st;
-    st = hip_status(launch_attend(pl, *kv, q, cu_seqlens_k, sel, cnt, po, pml, s));
-    if (st != NOSA_OK) return st;
-    return hip_status(launch_merge(pl, po, pml, out, lse, s));
+    return hip_status(launch_decode(pl, *kv, q, cu_seqlens_k, carve(pl, workspace), out, lse,
+                                    sel_idx, sel_count, block_scores, as_stream(stream)));
 }
 
 }  // extern "C"

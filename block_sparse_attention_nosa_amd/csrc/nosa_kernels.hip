@@ -1,16 +1,21 @@
 // nosa_kernels.hip -- CDNA4 (gfx950) kernels of the NOSA sparse decode step.
 //
-// Five kernels, launched in this order by a decode step:
-//   kc_build  : pooled keys, key j = bf16(mean of K over tokens [16j, 16j+32))
-//   scores    : z_h[j] = scale*log2(e) * q_h . Kc_j on MFMA (16 keys x 16 heads
-//               per instruction group), per-wave max / sum(exp2) partials
-//   select    : per (sequence, KV head) workgroup: per-head log-sum-exp, block
-//               importance = mean over overlapping keys of sum_h exp2(z - lse),
-//               radix top-k over the candidates, window forced, ascending ids
-//   attend    : split-K flash decode over the kept 64-token blocks; QK^T and PV
-//               on MFMA with the G query heads of a KV head as the N (resp. M)
-//               dimension; fp32 online softmax; per-workgroup (m, l, o) partial
-//   merge     : combine the partials into out / lse
+// A decode step is two launches:
+//   step1 : per (sequence, KV head) pair, "score" workgroups compute
+//           z_h[j] = scale*log2(e) * q_h . Kc_j on MFMA with per-wave
+//           (max, sum exp2) partials -- the wave owning the key completed by the
+//           current token pools it from K first (fp64, one bf16 rounding) and
+//           stores it -- while "window" workgroups attend the local-window
+//           blocks, which need no selection.  The last score workgroup of a
+//           pair (atomic counter) turns the partials into per-head log-sum-exp,
+//           pools block importance, radix-selects the top-k candidates and
+//           writes their (block, page) list.
+//   step2 : workgroups attend the selected blocks (one block per wave, every
+//           K/V load of the block in flight at once); the last workgroup of a
+//           pair merges the window and top-k partials into out / lse.
+// Stand-alone entry points reuse the same pieces: kc_build (pooled keys),
+// step1 in scores mode (importance only), select (from given importance) and
+// step2 in attend mode (given block ids).
 //
 // Sources: page "NOSA-1B 性能基准全解析" (sections 三.2 local window and TopK
 // blocks, 三.3 two-stage attention with kernel 32 / stride 16 pooling, 三.4 the
@@ -22,8 +27,17 @@
 // r = l % 16, kq = l / 16): A supplies A[r][8kq .. 8kq+7], B supplies
 // B[8kq .. 8kq+7][r], the accumulator holds D[4kq + i][r] for i = 0..3.  The
 // contraction index may be permuted freely as long as A and B agree; every
-// kernel below maps k-step st, lane group kq to channels 32st + 8kq .. +7 so
-// that four lane groups read 64 contiguous bytes of a row.
+// kernel maps k-step st, lane group kq to channels 32st + 8kq .. +7 so that
+// four lane groups read 64 contiguous bytes of a row.
+//
+// Cross-workgroup hand-off ("last one done"): data that another workgroup of
+// the same launch reads (logits, per-wave partials, attention partials) is
+// written and read with agent-scope relaxed atomic accesses, which this chip
+// performs coherently across its L2s (sc1) without whole-cache write-back or
+// invalidation.  Each workgroup waits for its stores to complete, then bumps
+// the pair's counter; the workgroup that sees count-1 resets the counter to
+// zero for the next call and finishes the pair.  Counters therefore start and
+// end every call at zero.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -38,6 +52,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int D = kHeadDim;
 constexpr int BS = kBlock;
 constexpr int SL = kSlots;
+constexpr float kLn2 = 0.69314718055994531f;
 
 __device__ __forceinline__ int dev_num_keys(int L) { return L >= kPoolK ? (L - kPoolK) / kPoolS + 1 : 0; }
 
@@ -53,6 +68,25 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Agent-coherent 8-byte stores / loads for data handed between workgroups.
+__device__ __forceinline__ void st_pair(void* p, float a, float b)
+{
+    const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float2 ld_pair(const void* p)
+{
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)),
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+__device__ __forceinline__ float ld_one(const float* p)
+{
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Length of sequence s clamped to [0, Lmax], Lmax = min(host bound, what a
 // block-table row addresses): a device length above the host-side bound can
 // then never index past the table, the workspace rows or the LDS arrays.
@@ -63,7 +97,7 @@ __device__ __forceinline__ int seq_len(const int32_t* cu_k, int s, int Lmax)
     return L < Lmax ? L : Lmax;
 }
 
-// ------------------------------------------------------------ kc_build ---
+// ------------------------------------------------------- pooled keys ---
 
 // Round a double to bf16, nearest-even, in one step from its bit pattern.
 __device__ __forceinline__ uint32_t bf16_from_f64(double x)
@@ -86,19 +120,41 @@ __device__ __forceinline__ uint32_t bf16_from_f64(double x)
     return sign | (uint32_t)m;
 }
 
+__device__ __forceinline__ void acc8(double (&acc)[8], uint4 w)
+{
+    acc[0] += (double)bf16_lo(w.x); acc[1] += (double)bf16_hi(w.x);
+    acc[2] += (double)bf16_lo(w.y); acc[3] += (double)bf16_hi(w.y);
+    acc[4] += (double)bf16_lo(w.z); acc[5] += (double)bf16_hi(w.z);
+    acc[6] += (double)bf16_lo(w.w); acc[7] += (double)bf16_hi(w.w);
+}
+
+__device__ __forceinline__ uint4 round8(const double (&acc)[8])
+{
+    uint32_t o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = bf16_from_f64(acc[e] * (1.0 / kPoolK));
+    return make_uint4(o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16),
+                      o[6] | (o[7] << 16));
+}
+
+__device__ __forceinline__ uint16_t* kc_slot(uint16_t* kc_pool, const int32_t* trow, int Hkv, int g,
+                                             int j)
+{
+    return kc_pool + (((size_t)trow[j / SL] * Hkv + g) * SL + (j % SL)) * D;
+}
+
 // One workgroup = 16 keys x 16 channel chunks of 8.  Each thread sums the 32
 // tokens of its key for its 8 channels in fp64 (exact for bf16 inputs), then
 // scales by 1/32 (exact) and rounds once.  Keys [n_c(prev), n_c(L)) are
-// written, prev = valid_len[s], or L - 1 when appending for the current
-// token, or 0 for a full rebuild.
+// written, prev = valid_len[s] or 0 for a full rebuild.
 __global__ __launch_bounds__(256) void kc_build_kernel(
     const uint16_t* __restrict__ k_pool, uint16_t* __restrict__ kc_pool,
     const int32_t* __restrict__ table, int max_blocks, int Lmax, int Hkv,
-    const int32_t* __restrict__ cu_k, const int32_t* __restrict__ valid_len, int append_current)
+    const int32_t* __restrict__ cu_k, const int32_t* __restrict__ valid_len)
 {
     const int s = blockIdx.z, g = blockIdx.y;
     const int L = seq_len(cu_k, s, Lmax);
-    int prev = valid_len ? valid_len[s] : (append_current ? L - 1 : 0);
+    int prev = valid_len ? valid_len[s] : 0;
     prev = prev < 0 ? 0 : prev;
     const int j0 = dev_num_keys(prev), j1 = dev_num_keys(L);
     const int jl = threadIdx.x >> 4, cc = threadIdx.x & 15;
@@ -109,82 +165,557 @@ __global__ __launch_bounds__(256) void kc_build_kernel(
         for (int e = 0; e < 8; ++e) acc[e] = 0.0;
         for (int i = 0; i < kPoolK; ++i) {
             const int t = j * kPoolS + i;
-            const int page = trow[t / BS];
-            const uint4 w = ldg16(k_pool + (((size_t)page * Hkv + g) * BS + (t % BS)) * D + cc * 8);
-            acc[0] += (double)bf16_lo(w.x); acc[1] += (double)bf16_hi(w.x);
-            acc[2] += (double)bf16_lo(w.y); acc[3] += (double)bf16_hi(w.y);
-            acc[4] += (double)bf16_lo(w.z); acc[5] += (double)bf16_hi(w.z);
-            acc[6] += (double)bf16_lo(w.w); acc[7] += (double)bf16_hi(w.w);
+            acc8(acc, ldg16(k_pool + (((size_t)trow[t / BS] * Hkv + g) * BS + (t % BS)) * D + cc * 8));
         }
-        uint32_t o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = bf16_from_f64(acc[e] * (1.0 / kPoolK));
-        uint4 packed;
-        packed.x = o[0] | (o[1] << 16);
-        packed.y = o[2] | (o[3] << 16);
-        packed.z = o[4] | (o[5] << 16);
-        packed.w = o[6] | (o[7] << 16);
-        const int page = trow[j / SL];
-        *reinterpret_cast<uint4*>(kc_pool + (((size_t)page * Hkv + g) * SL + (j % SL)) * D + cc * 8) = packed;
+        *reinterpret_cast<uint4*>(kc_slot(kc_pool, trow, Hkv, g, j) + cc * 8) = round8(acc);
     }
 }
 
 hipError_t launch_kc_build(const Plan& pl, const nosa_paged_kv& kv, const int32_t* cu_k,
-                           const int32_t* valid_len, bool append_current, int grid_x,
-                           hipStream_t stream)
+                           const int32_t* valid_len, int grid_x, hipStream_t stream)
 {
     dim3 grid(grid_x, pl.Hkv, pl.B);
     hipLaunchKernelGGL(kc_build_kernel, grid, dim3(256), 0, stream, kv.k_pool, kv.kc_pool,
-                       kv.block_table, kv.max_blocks_per_seq, pl.Lmax, pl.Hkv, cu_k, valid_len,
-                       append_current ? 1 : 0);
+                       kv.block_table, kv.max_blocks_per_seq, pl.Lmax, pl.Hkv, cu_k, valid_len);
     return hipGetLastError();
 }
 
-// -------------------------------------------------------------- scores ---
+// ------------------------------------------------------ block attention ---
 
-// Workgroup = 4 waves; wave w of workgroup x scores keys
-// [(4x + w) * 16T, (4x + w + 1) * 16T) of one (sequence, KV head) as T MFMA
-// tiles: A = 16 pooled keys x 32 channels, B = 32 channels x 16 query heads
-// (heads >= G are zero).  z is written in log2 units, per-wave (max, sum exp2)
-// go to zpart.
-template <int T>
-__global__ __launch_bounds__(256) void scores_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc_pool,
-    const int32_t* __restrict__ table, int max_blocks, int Lmax, const int32_t* __restrict__ cu_k,
-    int Hq, int Hkv, int G, float scale_log2, float* __restrict__ z, int zstride,
-    float2* __restrict__ zpart, int nchunk)
+// Row order of the K tile inside the QK^T MFMA.  Tile t = 2u + v, row
+// m = 4c + i holds token 32u + 8c + 4v + i.  With this order the
+// accumulator of lane (r, kq) ends up holding, for head r, the tokens
+// 32u + 8kq + 0..7 across tiles 2u and 2u+1: exactly the A operand of the
+// PV MFMA over the 32 tokens of k-step u.
+__device__ __forceinline__ int qk_row_token(int t, int m)
 {
-    const int s = blockIdx.z, g = blockIdx.y;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r = lane & 15, kq = lane >> 4;
-    const int L = seq_len(cu_k, s, Lmax);
-    const int nc = dev_num_keys(L);
-    const int chunk = blockIdx.x * 4 + wave;
-    const int key0 = chunk * 16 * T;
-    const int32_t* trow = table + (size_t)s * max_blocks;
+    return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
+}
 
-    bf16x8 qb[4];
-    {
-        const uint16_t* qh = q + ((size_t)s * Hq + g * G + (r < G ? r : 0)) * D;
+// Query operand of one KV head's group: B[channel][head r] (heads >= G zero).
+__device__ __forceinline__ void load_q(const uint16_t* q, int Hq, int s, int h0, int G, int r,
+                                       int kq, bf16x8 (&qb)[4])
+{
+    const uint16_t* qh = q + ((size_t)s * Hq + h0 + (r < G ? r : 0)) * D;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            uint4 w = ldg16(qh + st * 32 + kq * 8);
-            if (r >= G) w = make_uint4(0, 0, 0, 0);
-            qb[st] = as_bf16x8(w);
+    for (int st = 0; st < 4; ++st) {
+        uint4 w = ldg16(qh + st * 32 + kq * 8);
+        if (r >= G) w = make_uint4(0, 0, 0, 0);
+        qb[st] = as_bf16x8(w);
+    }
+}
+
+struct AttnState {
+    float m, l;
+    f32x4 o[8];
+};
+
+__device__ __forceinline__ void attn_init(AttnState& A)
+{
+    A.m = -INFINITY;
+    A.l = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) A.o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// One wave attends one 64-token page: S^T = K q^T (4 tiles x 4 k-steps), fp32
+// online softmax in log2 units, O += P V (2 k-steps x 8 channel tiles).
+// `limit` = tokens of the page that exist (tokens >= limit are masked).
+__device__ __forceinline__ void attend_page(const uint16_t* __restrict__ kb,
+                                            const uint16_t* __restrict__ vb, int limit,
+                                            const bf16x8 (&qb)[4], float scale_log2, int r,
+                                            int kq, AttnState& A)
+{
+    uint4 ka[4][4], va[2][8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int tok = qk_row_token(t, r);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) ka[t][st] = ldg16(kb + tok * D + st * 32 + kq * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) va[u][nt] = ldg16(vb + (nt * 16 + r) * BS + u * 32 + kq * 8);
+    // Keep every load of the page in flight before the first use: a wave that
+    // attends one page pays one memory latency instead of one per few loads.
+    __builtin_amdgcn_sched_barrier(0);
+
+    float x[4][4];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(ka[t][st]), qb[st], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = 32 * (t >> 1) + 8 * kq + 4 * (t & 1) + i;
+            x[t][i] = tok < limit ? acc[i] * scale_log2 : -INFINITY;
+            bmax = fmaxf(bmax, x[t][i]);
         }
     }
-    uint4 a[T][4];
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    const float m_new = fmaxf(A.m, bmax);
+    const float alpha = exp2f(A.m - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[t][i] = exp2f(x[t][i] - m_new);
+            psum += x[t][i];
+        }
+    A.l = A.l * alpha + psum;
+    A.m = m_new;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * kq + i);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) A.o[nt][i] *= ai;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        bf16x8 pa;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pa[i] = (__bf16)x[2 * u][i];
+            pa[4 + i] = (__bf16)x[2 * u + 1][i];
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) A.o[nt] = mfma16(pa, as_bf16x8(va[u][nt]), A.o[nt]);
+    }
+}
+
+// LDS for combining the four wave states of a workgroup.
+struct CombineLds {
+    float m[4][16], l[4][16];
+    float o[4][16][D + 4];
+};
+
+// Merge the four waves' states in LDS and store one (m, l, o) partial per
+// head of the group at partial slot `split`.  Must be called by all 256
+// threads.  Heads with no data get m = -inf, l = 0, o = 0.
+__device__ void store_wg_partial(CombineLds& sh, const AttnState& A, int G, size_t head_row0,
+                                 int nsplit, int split, float* __restrict__ po,
+                                 float2* __restrict__ pml)
+{
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    float l = A.l;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (kq == 0) {
+        sh.m[wave][r] = A.m;
+        sh.l[wave][r] = l;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sh.o[wave][4 * kq + i][nt * 16 + r] = A.o[nt][i];
+    __syncthreads();
+    const int h = tid >> 4, c0 = (tid & 15) * 8;
+    if (h < G) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, sh.m[w][h]);
+        float wt[4], Lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            wt[w] = (M == -INFINITY || sh.m[w][h] == -INFINITY) ? 0.f : exp2f(sh.m[w][h] - M);
+            Lsum += wt[w] * sh.l[w][h];
+        }
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc[e] = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) acc[e] += wt[w] * sh.o[w][h][c0 + e];
+        }
+        const size_t prow = (head_row0 + h) * nsplit + split;
+        float* dst = po + prow * D + c0;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) st_pair(dst + e, acc[e], acc[e + 1]);
+        if ((tid & 15) == 0) st_pair(pml + prow, M, Lsum);
+    }
+}
+
+// Whole workgroup: "am I the last of `total` workgroups of this pair?"  Every
+// wave first waits for its (agent-coherent) stores to complete.  The last
+// workgroup resets the counter for the next call and invalidates its CU's L1
+// and its L2 once (agent-scope acquire), after which plain loads see every
+// other workgroup's stores.
+__device__ bool last_of_pair(uint32_t* counter, uint32_t total, int* flag_lds)
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev == total - 1;
+        if (last) {
+            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        *flag_lds = last;
+    }
+    __syncthreads();
+    return *flag_lds != 0;
+}
+
+// ------------------------------------------------------------ selection ---
+
+// Order-preserving map of a float onto uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Number of lanes of this wave below the calling lane whose bit is set.
+__device__ __forceinline__ int lanes_below(uint64_t mask)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+struct SelectLds {
+    float lse[kMaxGroup];
+    int cnt[2][4][16];  // per exchange parity, wave, value
+};
+
+// Importance of every block of the pair, from z and the per-wave partials,
+// into sI[0 .. nb): mean over the keys overlapping block b (keys 4b-1 .. 4b+3
+// that exist) of sigma[j] = sum_h exp2(z_h[j] - lse_h).  Each thread takes
+// four consecutive keys (one float4 of z per head, all loads issued before
+// use) and adds every key's sigma to the block(s) it overlaps with LDS
+// atomics.  Also writes scores_out.  Reads data of other workgroups: call
+// after last_of_pair().
+__device__ void pool_importance(const float* __restrict__ z, int zstride,
+                                const float2* __restrict__ zpart, int nchunk, size_t head_row0,
+                                int G, int nc, int nb, float* sI, SelectLds& sh,
+                                float* __restrict__ scores_out, int max_nb)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float* zg = z + head_row0 * zstride;
+    // the logits of this thread's first four keys (first eight heads) do not
+    // depend on the normalisers: issue them before reducing the partials
+    float4 zfirst[8];
+    const bool has_first = 4 * tid < nc;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        if (u < G && has_first) zfirst[u] = *reinterpret_cast<const float4*>(zg + (size_t)u * zstride + 4 * tid);
+    for (int b = tid; b < nb; b += 256) sI[b] = 0.f;
+    for (int h = wave; h < G; h += 4) {
+        // per-wave (max, sum exp2) partials of head h: one pass over them
+        const float2* zp = zpart + (head_row0 + h) * nchunk;
+        float m = -INFINITY, acc = 0.f;
+#pragma unroll 1
+        for (int c0 = 0; c0 < nchunk; c0 += 256) {
+            float2 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + u * 64 + lane;
+                v[u] = c < nchunk ? zp[c] : make_float2(-INFINITY, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (!(v[u].y > 0.f)) continue;
+                const float mn = fmaxf(m, v[u].x);
+                acc = acc * exp2f(m - mn) + v[u].y * exp2f(v[u].x - mn);
+                m = mn;
+            }
+        }
+        // combine the lanes' (m, acc)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float mo = __shfl_xor(m, off), ao = __shfl_xor(acc, off);
+            const float mn = fmaxf(m, mo);
+            acc = (mn == -INFINITY) ? 0.f : acc * exp2f(m - mn) + ao * exp2f(mo - mn);
+            m = mn;
+        }
+        if (lane == 0) sh.lse[h] = m + log2f(acc);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int j0 = 4 * tid; j0 < nc; j0 += 4 * 256) {
+        float sg[4] = {0.f, 0.f, 0.f, 0.f};
+        // heads in batches of 8: every load of a batch in flight at once
+#pragma unroll 1
+        for (int h0 = 0; h0 < G; h0 += 8) {
+            float4 zz[8];
+            const bool first = j0 == 4 * tid && h0 == 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (h0 + u < G)
+                    zz[u] = first ? zfirst[u]
+                                  : *reinterpret_cast<const float4*>(zg + (size_t)(h0 + u) * zstride + j0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (h0 + u < G) {
+                    const float lh = sh.lse[h0 + u];
+                    sg[0] += exp2f(zz[u].x - lh);
+                    sg[1] += exp2f(zz[u].y - lh);
+                    sg[2] += exp2f(zz[u].z - lh);
+                    sg[3] += exp2f(zz[u].w - lh);
+                }
+        }
+        // keys j0 .. j0+3 all overlap block j0/4; key j0+3 also overlaps the next
+        const int b = j0 >> 2;
+        float own = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (j0 + e < nc) own += sg[e];
+        atomicAdd(&sI[b], own);
+        if (j0 + 3 < nc && b + 1 < nb) atomicAdd(&sI[b + 1], sg[3]);
+    }
+    __syncthreads();
+    for (int b = tid; b < nb; b += 256) {
+        const int jlo = max(4 * b - 1, 0), jhi = min(4 * b + 3, nc - 1);
+        const float I = jlo <= jhi ? sI[b] / (float)(jhi - jlo + 1) : -INFINITY;
+        sI[b] = I;
+        if (scores_out) scores_out[b] = I;
+    }
+    if (scores_out)
+        for (int b = nb + tid; b < max_nb; b += 256) scores_out[b] = -INFINITY;
+    __syncthreads();
+}
+
+// Top-min(topk, ncand) of the candidates [0, ncand) by (importance desc, block
+// asc) with the window [ncand, nb) always kept.  Writes, when non-null:
+//   sel_out[0 .. max_sel): every kept block ascending, -1 padded; *cnt_out;
+//   selpg[0 .. top_span): (block, page) of the top-k picks ascending,
+//                         (-1, -1) padded; *ntop_out.
+// Must be called by all 256 threads; sI holds the importance in LDS.  Only
+// ballots, lane counts and one LDS exchange per step: no atomics, no shuffles.
+__device__ void select_blocks_wg(const float* sI, int nb, int wblocks, int topk, SelectLds& sh,
+                                 int32_t* __restrict__ sel_out, int32_t* __restrict__ cnt_out,
+                                 int max_sel, int2* __restrict__ selpg,
+                                 int32_t* __restrict__ ntop_out, int top_span,
+                                 const int32_t* __restrict__ trow)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ncand = nb > wblocks ? nb - wblocks : 0;
+    const int kk = topk < ncand ? topk : ncand;
+    const bool partial = kk > 0 && kk < ncand;
+    uint32_t T = 0;
+    int need = 0;
+    int step = 0;
+    // Per-wave counts -> LDS -> workgroup sums.  Lane v of every wave adds up
+    // value v of the four waves, so each lane ends with one sum (no loop over
+    // all values per lane); `par` alternates so one barrier per exchange does.
+    auto publish = [&](const int* c, int nv) -> int {
+        const int par = step & 1;
+        int mine = 0;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            if (v < nv && v == lane) mine = c[v];
+        if (lane < nv) sh.cnt[par][wave][lane] = mine;
+        __syncthreads();
+        ++step;
+        return par;
+    };
+    // candidate keys of this thread (candidate round*256 + tid), first 8 rounds
+    constexpr int KR = 8;
+    uint32_t keys[KR];
+    const int rounds = (ncand + 255) / 256;
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+        const int b = i * 256 + tid;
+        keys[i] = (i < rounds && b < ncand) ? order_key(sI[b]) : 0u;
+    }
+    auto key_at = [&](int i) -> uint32_t {
+        if (i < KR) {
+            uint32_t k = 0;
+#pragma unroll
+            for (int j = 0; j < KR; ++j)
+                if (j == i) k = keys[j];
+            return k;
+        }
+        const int b = i * 256 + tid;
+        return b < ncand ? order_key(sI[b]) : 0u;
+    };
+    if (partial) {
+        // The kk-th largest key T is the largest value with #{key >= T} >= kk.
+        // Build it four bits at a time from the top: count the keys at or
+        // above each of the 15 extensions of T (ballots + lane counts, one LDS
+        // exchange), keep the largest extension that still has >= kk keys.
+        for (int bit = 28; bit >= 0; bit -= 4) {
+            int c[15];
+#pragma unroll
+            for (int d = 0; d < 15; ++d) c[d] = 0;
+            for (int i = 0; i < rounds; ++i) {
+                const uint32_t key = key_at(i);
+#pragma unroll
+                for (int d = 0; d < 15; ++d)
+                    c[d] += __popcll(__ballot(key >= (T | ((uint32_t)(d + 1) << bit))));
+            }
+            const int par = publish(c, 15);
+            const int sum = lane < 15 ? sh.cnt[par][0][lane] + sh.cnt[par][1][lane] +
+                                            sh.cnt[par][2][lane] + sh.cnt[par][3][lane]
+                                      : 0;
+            // counts fall with the digit, so the digits that keep >= kk keys
+            // are 1 .. dsel and dsel is their number
+            const int dsel = (int)__popcll(__ballot(lane < 15 && sum >= kk));
+            T |= (uint32_t)dsel << bit;
+        }
+        int ca[1] = {0};
+        for (int i = 0; i < rounds; ++i) ca[0] += __popcll(__ballot(key_at(i) > T));
+        const int par = publish(ca, 1);
+        const int na = sh.cnt[par][0][0] + sh.cnt[par][1][0] + sh.cnt[par][2][0] + sh.cnt[par][3][0];
+        need = kk - na;  // ties at T to take, lowest block ids first
+    }
+    // Ascending compaction in rounds of 256 consecutive candidates (thread tid
+    // holds candidate round*256 + tid): ranks from ballots within the wave and
+    // per-wave totals across waves.
+    int eq_base = 0, sel_base = 0;
+    for (int i = 0; i < rounds; ++i) {
+        const int b = i * 256 + tid;
+        const bool valid = b < ncand;
+        bool take;
+        if (!partial) {
+            take = valid && kk > 0;
+        } else {
+            const uint32_t key = key_at(i);
+            const bool eq = valid && key == T;
+            const uint64_t meq = __ballot(eq);
+            int ce[1] = {(int)__popcll(meq)};
+            const int par = publish(ce, 1);
+            int eq_before = eq_base + lanes_below(meq);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int cw = sh.cnt[par][w][0];
+                if (w < wave) eq_before += cw;
+                eq_base += cw;
+            }
+            take = valid && (key > T || (eq && eq_before < need));
+        }
+        const uint64_t mt = __ballot(take);
+        int ct[1] = {(int)__popcll(mt)};
+        const int par = publish(ct, 1);
+        int pos = sel_base + lanes_below(mt);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int cw = sh.cnt[par][w][0];
+            if (w < wave) pos += cw;
+            sel_base += cw;
+        }
+        if (take) {
+            if (sel_out) sel_out[pos] = b;
+            if (selpg && pos < top_span) selpg[pos] = make_int2(b, trow[b]);
+        }
+    }
+    const int nsel = sel_base;
+    const int total = nsel + (nb - ncand);
+    if (sel_out) {
+        for (int b = ncand + tid; b < nb; b += 256) sel_out[nsel + (b - ncand)] = b;
+        for (int x = total + tid; x < max_sel; x += 256) sel_out[x] = -1;
+    }
+    if (selpg)
+        for (int x = nsel + tid; x < top_span; x += 256) selpg[x] = make_int2(-1, -1);
+    if (tid == 0) {
+        if (cnt_out) *cnt_out = total;
+        if (ntop_out) *ntop_out = nsel;
+    }
+}
+
+// --------------------------------------------------------------- step 1 ---
+
+struct Step1Args {
+    const uint16_t* q;
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    uint16_t* kc_pool;
+    const int32_t* table;
+    const int32_t* cu_k;
+    int max_blocks, Lmax, B, Hq, Hkv, G;
+    float scale_log2;
+    int score_groups;  // score workgroups per pair
+    int win_groups;    // window workgroups per pair (0 = none), one page per wave
+    int append;        // pool the key completed by the current token
+    float* z;
+    int zstride;
+    float2* zpart;
+    int nchunk;
+    uint32_t* counter;  // [pairs]
+    int do_select, topk, wblocks, max_nb, max_sel, top_span;
+    float* scores_out;  // [pairs][max_nb] or null
+    int32_t* sel_out;   // [pairs][max_sel] or null
+    int32_t* cnt_out;   // [pairs] or null
+    int2* selpg;        // [pairs][top_span] or null
+    int32_t* ntop;      // [pairs] or null
+    float* po;
+    float2* pml;
+    int nsplit;  // partial slots per head
+};
+
+constexpr size_t step1_lds_bytes(int max_nb)
+{
+    return sizeof(CombineLds) > (size_t)max_nb * 4 ? sizeof(CombineLds) : (size_t)max_nb * 4;
+}
+
+// Score workgroup (4 waves, T tiles of 16 keys each per wave) of one pair.
+template <int T>
+__device__ void score_part(const Step1Args& a, int s, int g, int grp, char* smem)
+{
+    __shared__ SelectLds sel_sh;
+    __shared__ int flag;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const int L = seq_len(a.cu_k, s, a.Lmax);
+    const int nc = dev_num_keys(L);
+    const int chunk = grp * 4 + wave;
+    const int key0 = chunk * 16 * T;
+    const int32_t* trow = a.table + (size_t)s * a.max_blocks;
+    const size_t head_row0 = (size_t)s * a.Hq + g * a.G;
+
+    bf16x8 qb[4];
+    load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
+    uint4 kv[T][4];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const int key = key0 + t * 16 + r;
         if (key < nc) {
-            const uint16_t* kp = kc_pool + (((size_t)trow[key / SL] * Hkv + g) * SL + key % SL) * D;
+            const uint16_t* kp = kc_slot(a.kc_pool, trow, a.Hkv, g, key);
 #pragma unroll
-            for (int st = 0; st < 4; ++st) a[t][st] = ldg16(kp + st * 32 + kq * 8);
+            for (int st = 0; st < 4; ++st) kv[t][st] = ldg16(kp + st * 32 + kq * 8);
         } else {
 #pragma unroll
-            for (int st = 0; st < 4; ++st) a[t][st] = make_uint4(0, 0, 0, 0);
+            for (int st = 0; st < 4; ++st) kv[t][st] = make_uint4(0, 0, 0, 0);
         }
+    }
+    // The key completed by the current token (tokens L-32 .. L-1) is pooled
+    // here from K, stored, and substituted into this wave's operand.
+    const int jn = nc - 1;
+    if (a.append && L >= kPoolK && (L - kPoolK) % kPoolS == 0 && jn >= key0 && jn < key0 + 16 * T) {
+        const int tr = lane >> 4, cc = lane & 15;  // 4 token phases x 16 channel chunks
+        double acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+        for (int i = tr; i < kPoolK; i += 4) {
+            const int t = jn * kPoolS + i;
+            acc8(acc, ldg16(a.k_pool + (((size_t)trow[t / BS] * a.Hkv + g) * BS + (t % BS)) * D + cc * 8));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc[e] += __shfl_xor(acc[e], 16);
+            acc[e] += __shfl_xor(acc[e], 32);
+        }
+        const uint4 key = round8(acc);  // channels 8cc .. 8cc+7, same in every phase
+        if (tr == 0) *reinterpret_cast<uint4*>(kc_slot(a.kc_pool, trow, a.Hkv, g, jn) + cc * 8) = key;
+        const int tloc = (jn - key0) / 16, rloc = (jn - key0) % 16;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                uint4 v;
+                v.x = __shfl(key.x, st * 4 + kq);
+                v.y = __shfl(key.y, st * 4 + kq);
+                v.z = __shfl(key.z, st * 4 + kq);
+                v.w = __shfl(key.w, st * 4 + kq);
+                if (t == tloc && r == rloc) kv[t][st] = v;
+            }
     }
     float mx = -INFINITY;
     float zv[T][4];
@@ -192,16 +723,17 @@ __global__ __launch_bounds__(256) void scores_kernel(
     for (int t = 0; t < T; ++t) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(a[t][st]), qb[st], acc);
+        for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(kv[t][st]), qb[st], acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int key = key0 + t * 16 + kq * 4 + i;
-            zv[t][i] = key < nc ? acc[i] * scale_log2 : -INFINITY;
+            zv[t][i] = key < nc ? acc[i] * a.scale_log2 : -INFINITY;
             mx = fmaxf(mx, zv[t][i]);
         }
-        if (r < G) {
-            float4 o = make_float4(zv[t][0], zv[t][1], zv[t][2], zv[t][3]);
-            *reinterpret_cast<float4*>(z + ((size_t)s * Hq + g * G + r) * zstride + key0 + t * 16 + kq * 4) = o;
+        if (r < a.G) {
+            float* zd = a.z + (head_row0 + r) * a.zstride + key0 + t * 16 + kq * 4;
+            st_pair(zd, zv[t][0], zv[t][1]);
+            st_pair(zd + 2, zv[t][2], zv[t][3]);
         }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -215,436 +747,388 @@ __global__ __launch_bounds__(256) void scores_kernel(
     }
     sum += __shfl_xor(sum, 16);
     sum += __shfl_xor(sum, 32);
-    if (kq == 0 && r < G) zpart[((size_t)s * Hq + g * G + r) * nchunk + chunk] = make_float2(mx, sum);
-}
+    if (kq == 0 && r < a.G) st_pair(a.zpart + (head_row0 + r) * a.nchunk + chunk, mx, sum);
 
-hipError_t launch_scores(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
-                         const int32_t* cu_k, float* z, float2* zpart, hipStream_t stream)
-{
-    dim3 grid(pl.score_groups, pl.Hkv, pl.B);
-#define NOSA_SCORES(T)                                                                        \
-    hipLaunchKernelGGL(scores_kernel<T>, grid, dim3(256), 0, stream, q, kv.kc_pool,           \
-                       kv.block_table, kv.max_blocks_per_seq, pl.Lmax, cu_k, pl.Hq, pl.Hkv, pl.G, \
-                       pl.scale_log2, z, pl.zstride, zpart, pl.nchunk)
-    switch (pl.score_tiles) {
-        case 1: NOSA_SCORES(1); break;
-        case 2: NOSA_SCORES(2); break;
-        case 4: NOSA_SCORES(4); break;
-        default: NOSA_SCORES(8); break;
-    }
-#undef NOSA_SCORES
-    return hipGetLastError();
-}
+    const size_t pair = (size_t)s * a.Hkv + g;
+    if (!last_of_pair(a.counter + pair, (uint32_t)a.score_groups, &flag)) return;
 
-// -------------------------------------------------------------- select ---
-
-// Order-preserving map of a float onto uint32 (larger float -> larger key).
-__device__ __forceinline__ uint32_t order_key(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Exclusive prefix sum over the 256 threads of the workgroup; returns this
-// thread's prefix and writes the total to *total.  Uses `scratch` (>= 4 ints).
-__device__ int block_exclusive_scan(int v, int* scratch, int* total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) scratch[wave] = x;
-    __syncthreads();
-    int base = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const int t = scratch[w];
-        if (w < wave) base += t;
-        all += t;
-    }
-    __syncthreads();
-    *total = all;
-    return base + x - v;
-}
-
-// One workgroup per (KV head, sequence).  LDS: the block importances of the
-// sequence (max_nb floats) + small tables.
-__global__ __launch_bounds__(256) void select_kernel(
-    const float* __restrict__ z, int zstride, const float2* __restrict__ zpart, int nchunk,
-    const float* __restrict__ scores_in, float* __restrict__ scores_out,
-    int32_t* __restrict__ sel, int32_t* __restrict__ cnt, const int32_t* __restrict__ cu_k,
-    int Lmax, int Hq, int Hkv, int G, int max_nb, int max_sel, int topk, int wblocks)
-{
-    extern __shared__ float sI[];
-    __shared__ float s_lse[kMaxGroup];
-    __shared__ int hist[256];
-    __shared__ int scan_tmp[8];
-    __shared__ int s_digit, s_need;
-
-    const int g = blockIdx.x, s = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int L = seq_len(cu_k, s, Lmax);
-    const int nc = dev_num_keys(L);
+    // ---- last score workgroup of the pair: importance, then selection
+    float* sI = reinterpret_cast<float*>(smem);
     const int nb = (L + BS - 1) / BS;
-    const size_t row = (size_t)s * Hkv + g;
-
-    if (z) {
-        // per-head log2-sum-exp2 over all keys, from the per-wave partials
-        for (int h = wave; h < G; h += 4) {
-            const float2* zp = zpart + ((size_t)s * Hq + g * G + h) * nchunk;
-            float m = -INFINITY;
-            for (int c = lane; c < nchunk; c += 64) m = fmaxf(m, zp[c].x);
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-            float acc = 0.f;
-            if (m != -INFINITY)
-                for (int c = lane; c < nchunk; c += 64) {
-                    const float2 v = zp[c];
-                    if (v.y > 0.f) acc += v.y * exp2f(v.x - m);
-                }
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-            if (lane == 0) s_lse[h] = m + log2f(acc);
-        }
-        __syncthreads();
-        // block importance: mean over the keys overlapping the block of the
-        // group's summed softmax probabilities
-        const float* zg = z + ((size_t)s * Hq + g * G) * zstride;
-        for (int b = tid; b < nb; b += 256) {
-            const int jlo = max(4 * b - 1, 0), jhi = min(4 * b + 3, nc - 1);
-            float I = -INFINITY;
-            if (jlo <= jhi) {
-                float acc = 0.f;
-                for (int j = jlo; j <= jhi; ++j) {
-                    float sj = 0.f;
-                    for (int h = 0; h < G; ++h) sj += exp2f(zg[(size_t)h * zstride + j] - s_lse[h]);
-                    acc += sj;
-                }
-                I = acc / (float)(jhi - jlo + 1);
-            }
-            sI[b] = I;
-            if (scores_out) scores_out[row * max_nb + b] = I;
-        }
-        if (scores_out)
-            for (int b = nb + tid; b < max_nb; b += 256) scores_out[row * max_nb + b] = -INFINITY;
-    } else {
-        for (int b = tid; b < nb; b += 256) sI[b] = scores_in[row * max_nb + b];
-    }
-    if (!sel) return;
-    __syncthreads();
-
-    const int ncand = nb > wblocks ? nb - wblocks : 0;
-    const int kk = topk < ncand ? topk : ncand;
-    uint32_t thresh = 0;
-    int need = 0;
-    const bool partial = kk > 0 && kk < ncand;
-    if (partial) {
-        // radix select of the kk-th largest key, 8 bits at a time from the top
-        uint32_t prefix = 0, pmask = 0;
-        need = kk;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            hist[tid] = 0;
-            __syncthreads();
-            for (int b = tid; b < ncand; b += 256) {
-                const uint32_t key = order_key(sI[b]);
-                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
-            }
-            __syncthreads();
-            // reverse the bin order so the exclusive scan is over larger digits
-            const int rev = hist[255 - tid];
-            int tot;
-            const int above_rev = block_exclusive_scan(rev, scan_tmp, &tot);
-            // thread tid handles digit 255 - tid: keys with digit > (255 - tid)
-            const int digit = 255 - tid;
-            if (above_rev < need && above_rev + rev >= need) {
-                s_digit = digit;
-                s_need = need - above_rev;
-            }
-            __syncthreads();
-            prefix |= (uint32_t)s_digit << shift;
-            pmask |= 0xffu << shift;
-            need = s_need;
-            __syncthreads();
-        }
-        thresh = prefix;
-    }
-
-    // ascending compaction of the chosen candidates; thread tid owns a
-    // contiguous run of candidate ids
-    const int per = (ncand + 255) / 256;
-    const int b0 = min(tid * per, ncand), b1 = min(b0 + per, ncand);
-    int eq_before = 0, tot;
-    if (partial) {
-        int eq = 0;
-        for (int b = b0; b < b1; ++b) eq += order_key(sI[b]) == thresh;
-        eq_before = block_exclusive_scan(eq, scan_tmp, &tot);
-    }
-    int nmine = 0;
-    {
-        int eqr = eq_before;
-        for (int b = b0; b < b1; ++b) {
-            bool take;
-            if (!partial) {
-                take = kk > 0;
-            } else {
-                const uint32_t key = order_key(sI[b]);
-                take = key > thresh || (key == thresh && eqr < need);
-                eqr += key == thresh;
-            }
-            nmine += take;
-        }
-    }
-    int nsel;
-    int pos = block_exclusive_scan(nmine, scan_tmp, &nsel);
-    int32_t* out = sel + row * max_sel;
-    {
-        int eqr = eq_before;
-        for (int b = b0; b < b1; ++b) {
-            bool take;
-            if (!partial) {
-                take = kk > 0;
-            } else {
-                const uint32_t key = order_key(sI[b]);
-                take = key > thresh || (key == thresh && eqr < need);
-                eqr += key == thresh;
-            }
-            if (take) out[pos++] = b;
-        }
-    }
-    const int total = nsel + (nb - ncand);
-    for (int b = ncand + tid; b < nb; b += 256) out[nsel + (b - ncand)] = b;
-    for (int x = total + tid; x < max_sel; x += 256) out[x] = -1;
-    if (tid == 0) cnt[row] = total;
+    pool_importance(a.z, a.zstride, a.zpart, a.nchunk, head_row0, a.G, nc, nb, sI, sel_sh,
+                    a.scores_out ? a.scores_out + pair * a.max_nb : nullptr, a.max_nb);
+    if (!a.do_select) return;
+    select_blocks_wg(sI, nb, a.wblocks, a.topk, sel_sh, a.sel_out ? a.sel_out + pair * a.max_sel : nullptr,
+                     a.cnt_out ? a.cnt_out + pair : nullptr, a.max_sel,
+                     a.selpg ? a.selpg + pair * a.top_span : nullptr, a.ntop ? a.ntop + pair : nullptr,
+                     a.top_span, trow);
 }
 
-hipError_t launch_select(const Plan& pl, const int32_t* cu_k, const float* z,
-                         const float2* zpart, const float* scores_in, float* scores_out,
-                         int32_t* sel, int32_t* cnt, hipStream_t stream)
+// Window workgroup: wave w attends window slot 4*grp + w, slot x being block
+// nb - min(nb, wblocks) + x, and the workgroup stores one partial.
+__device__ void window_part(const Step1Args& a, int s, int g, int grp, char* smem)
 {
-    dim3 grid(pl.Hkv, pl.B);
-    const size_t lds = sizeof(float) * (size_t)(pl.max_nb > 0 ? pl.max_nb : 1);
-    hipLaunchKernelGGL(select_kernel, grid, dim3(256), lds, stream, z, pl.zstride, zpart,
-                       pl.nchunk, scores_in, scores_out, sel, cnt, cu_k, pl.Lmax,
-                       pl.Hq, pl.Hkv, pl.G, pl.max_nb, pl.max_sel, pl.topk, pl.wblocks);
-    return hipGetLastError();
-}
-
-// -------------------------------------------------------------- attend ---
-
-// Row order of the K tile inside the QK^T MFMA.  Tile t = 2u + v, row
-// m = 4c + i holds token 32u + 8c + 4v + i.  With this order the
-// accumulator of lane (r, kq) ends up holding, for head r, the tokens
-// 32u + 8kq + 0..7 across tiles 2u and 2u+1: exactly the A operand of the
-// PV MFMA over the 32 tokens of k-step u.
-__device__ __forceinline__ int qk_row_token(int t, int m)
-{
-    return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
-}
-
-// Workgroup = 4 waves = one split of one (sequence, KV head).  Wave w handles
-// the selected blocks split*4R + 4*rr + w, rr < R.  Per block: 16 MFMAs for
-// S^T = K q^T (64 tokens x 16 heads), online softmax in fp32, 16 MFMAs for
-// O += P V (16 heads x 128 channels).  The four wave partials are merged in
-// LDS into one (m, l, o) partial per workgroup.
-template <int R>
-__global__ __launch_bounds__(256) void attend_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
-    const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ table, int max_blocks,
-    int Lmax, const int32_t* __restrict__ cu_k, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ cnt, int max_sel, int Hq, int Hkv, int G, float scale_log2,
-    float* __restrict__ po, float2* __restrict__ pml, int nsplit)
-{
-    __shared__ float sm[4][16], sl[4][16];
-    __shared__ float so[4][16][D + 4];
-
-    const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, kq = lane >> 4;
+    const int L = seq_len(a.cu_k, s, a.Lmax);
+    const int nb = (L + BS - 1) / BS;
+    const int wn = nb < a.wblocks ? nb : a.wblocks;
+    AttnState A;
+    attn_init(A);
+    bf16x8 qb[4];
+    load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
+    const int slot = grp * 4 + wave;
+    if (slot < wn) {
+        const int b = nb - wn + slot;
+        const int page = a.table[(size_t)s * a.max_blocks + b];
+        const uint16_t* kb = a.k_pool + ((size_t)page * a.Hkv + g) * BS * D;
+        const uint16_t* vb = a.v_pool + ((size_t)page * a.Hkv + g) * D * BS;
+        attend_page(kb, vb, L - b * BS, qb, a.scale_log2, r, kq, A);
+    }
+    store_wg_partial(*reinterpret_cast<CombineLds*>(smem), A, a.G, (size_t)s * a.Hq + g * a.G,
+                     a.nsplit, grp, a.po, a.pml);
+}
+
+template <int T>
+__global__ __launch_bounds__(256) void step1_kernel(Step1Args a)
+{
+    extern __shared__ __align__(16) char smem[];
+    // window workgroups first: they need no hand-off, and dispatching them
+    // early keeps them off the tail of the launch
+    const int npairs = a.B * a.Hkv;
+    int wg = blockIdx.x;
+    if (wg < npairs * a.win_groups) {
+        const int pair = wg / a.win_groups, grp = wg % a.win_groups;
+        window_part(a, pair / a.Hkv, pair % a.Hkv, grp, smem);
+    } else {
+        wg -= npairs * a.win_groups;
+        const int pair = wg / a.score_groups, grp = wg % a.score_groups;
+        score_part<T>(a, pair / a.Hkv, pair % a.Hkv, grp, smem);
+    }
+}
+
+// --------------------------------------------------------------- step 2 ---
+
+struct Step2Args {
+    const uint16_t* q;
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    const int32_t* table;
+    const int32_t* cu_k;
+    int max_blocks, Lmax, B, Hq, Hkv, G;
+    float scale_log2;
+    int groups;         // workgroups per pair
+    int rounds;         // blocks per wave
+    const int2* selpg;  // decode mode: [pairs][span] (block, page), -1 padded
+    const int32_t* sel; // attend mode: [pairs][max_sel] block ids
+    const int32_t* cnt; //              [pairs]
+    int span, max_sel;
+    float* po;
+    float2* pml;
+    int nsplit, split0;  // partial slots per head; this kernel writes [split0, split0+groups)
+    uint32_t* counter;   // [pairs]
+    float* out;
+    float* lse;
+};
+
+constexpr int kMergeBatch = 24;  // partial outputs loaded at once per thread
+
+struct MergeLds {
+    float2 ml[kMaxGroup][kMaxSplit];  // (max, sum) of every partial
+    float w[kMaxGroup][kMaxSplit];    // its weight exp2(m_i - M)
+    float M[kMaxGroup], L[kMaxGroup];
+};
+
+// Combine the nsplit partials of every head of the pair into out / lse.  All
+// (m, l) go to LDS in one parallel pass, each head's weights are formed once,
+// then thread (head, 4 channels) sums the weighted outputs with its loads
+// issued eight partials at a time.  Reads data of other workgroups: call
+// after last_of_pair().
+__device__ void merge_pair(const Step2Args& a, int s, int g, MergeLds& sh)
+{
+    const int tid = threadIdx.x;
+    const int G = a.G, ns = a.nsplit;
+    const size_t row0 = (size_t)s * a.Hq + g * G;
+    for (int e = tid; e < G * ns; e += 256) {
+        const int h = e / ns, i = e % ns;
+        sh.ml[h][i] = a.pml[(row0 + h) * ns + i];
+    }
+    __syncthreads();
+    if (tid < G) {
+        float M = -INFINITY;
+        for (int i = 0; i < ns; ++i) M = fmaxf(M, sh.ml[tid][i].x);
+        float L = 0.f;
+        for (int i = 0; i < ns; ++i) {
+            const float2 v = sh.ml[tid][i];
+            const float w = (M == -INFINITY || v.x == -INFINITY) ? 0.f : exp2f(v.x - M);
+            sh.w[tid][i] = w;
+            L += w * v.y;
+        }
+        sh.M[tid] = M;
+        sh.L[tid] = L;
+    }
+    __syncthreads();
+    for (int item = tid; item < G * 32; item += 256) {
+        const int h = item >> 5, c = (item & 31) * 4;
+        const float* op = a.po + (row0 + h) * ns * D + c;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 1
+        for (int i0 = 0; i0 < ns; i0 += kMergeBatch) {
+            float4 o[kMergeBatch];
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u)
+                if (i0 + u < ns) o[u] = *reinterpret_cast<const float4*>(op + (size_t)(i0 + u) * D);
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                if (i0 + u >= ns) break;
+                const float w = sh.w[h][i0 + u];
+                acc.x += w * o[u].x;
+                acc.y += w * o[u].y;
+                acc.z += w * o[u].z;
+                acc.w += w * o[u].w;
+            }
+        }
+        const float L = sh.L[h];
+        const bool empty = !(L > 0.f);
+        const float inv = empty ? 0.f : 1.f / L;
+        *reinterpret_cast<float4*>(a.out + (row0 + h) * D + c) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        if (a.lse && c == 0) a.lse[row0 + h] = empty ? -INFINITY : (sh.M[h] + log2f(L)) * kLn2;
+    }
+}
+
+// Workgroup = 4 waves; wave w handles entries (grp*rounds + rr)*4 + w of the
+// pair's list, rr < rounds, one 64-token block at a time.
+template <bool kDecode, int R>
+__global__ __launch_bounds__(256) void step2_kernel(Step2Args a)
+{
+    __shared__ union {
+        CombineLds comb;
+        MergeLds merge;
+    } sh;
+    __shared__ int flag;
+    const int pair = blockIdx.x / a.groups, grp = blockIdx.x % a.groups;
+    const int s = pair / a.Hkv, g = pair % a.Hkv;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const int L = seq_len(a.cu_k, s, a.Lmax);
+    const int nb = (L + BS - 1) / BS;
+    const int32_t* trow = a.table + (size_t)s * a.max_blocks;
+    int n = 0;
+    if (!kDecode) n = min(a.cnt[pair], a.max_sel);
+    AttnState A;
+    attn_init(A);
+    bf16x8 qb[4];
+    load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+        const int idx = (grp * R + rr) * 4 + wave;
+        int b = -1, page = -1;
+        if (kDecode) {
+            if (idx < a.span) {
+                const int2 e = a.selpg[(size_t)pair * a.span + idx];
+                b = e.x;
+                page = e.y;
+            }
+        } else if (idx < n) {
+            b = a.sel[(size_t)pair * a.max_sel + idx];
+            if (b >= 0 && b < nb) page = trow[b];
+        }
+        if (b < 0 || b >= nb) continue;
+        const uint16_t* kb = a.k_pool + ((size_t)page * a.Hkv + g) * BS * D;
+        const uint16_t* vb = a.v_pool + ((size_t)page * a.Hkv + g) * D * BS;
+        attend_page(kb, vb, L - b * BS, qb, a.scale_log2, r, kq, A);
+    }
+    store_wg_partial(sh.comb, A, a.G, (size_t)s * a.Hq + g * a.G, a.nsplit, a.split0 + grp, a.po,
+                     a.pml);
+    if (!last_of_pair(a.counter + pair, (uint32_t)a.groups, &flag)) return;
+    merge_pair(a, s, g, sh.merge);
+}
+
+// ------------------------------------------------------ select (alone) ---
+
+// Selection from given importance: one workgroup per pair.
+__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ scores_in,
+                                                     int32_t* __restrict__ sel,
+                                                     int32_t* __restrict__ cnt,
+                                                     const int32_t* __restrict__ cu_k, int Lmax,
+                                                     int Hkv, int max_nb, int max_sel, int topk,
+                                                     int wblocks)
+{
+    extern __shared__ __align__(16) char smem[];
+    __shared__ SelectLds sh;
+    float* sI = reinterpret_cast<float*>(smem);
+    const int g = blockIdx.x, s = blockIdx.y;
     const int L = seq_len(cu_k, s, Lmax);
     const int nb = (L + BS - 1) / BS;
-    const size_t row = (size_t)s * Hkv + g;
-    const int count = min(cnt[row], max_sel);
-    const int32_t* mysel = sel + row * max_sel;
-    const int32_t* trow = table + (size_t)s * max_blocks;
-
-    bf16x8 qb[4];
-    {
-        const uint16_t* qh = q + ((size_t)s * Hq + g * G + (r < G ? r : 0)) * D;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            uint4 w = ldg16(qh + st * 32 + kq * 8);
-            if (r >= G) w = make_uint4(0, 0, 0, 0);
-            qb[st] = as_bf16x8(w);
-        }
-    }
-
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 o[8];
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int rr = 0; rr < R; ++rr) {
-        const int idx = split * 4 * R + rr * 4 + wave;
-        if (idx >= count) break;
-        const int b = mysel[idx];
-        if (b < 0 || b >= nb) continue;
-        const int page = trow[b];
-        const uint16_t* kb = k_pool + ((size_t)page * Hkv + g) * BS * D;
-        const uint16_t* vb = v_pool + ((size_t)page * Hkv + g) * D * BS;
-        uint4 ka[4][4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int tok = qk_row_token(t, r);
-#pragma unroll
-            for (int st = 0; st < 4; ++st) ka[t][st] = ldg16(kb + tok * D + st * 32 + kq * 8);
-        }
-        uint4 va[2][8];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) va[u][nt] = ldg16(vb + (nt * 16 + r) * BS + u * 32 + kq * 8);
-
-        const int limit = L - b * BS;  // tokens of this block that exist
-        float x[4][4];
-        float bmax = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(ka[t][st]), qb[st], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = 32 * (t >> 1) + 8 * kq + 4 * (t & 1) + i;
-                x[t][i] = tok < limit ? acc[i] * scale_log2 : -INFINITY;
-                bmax = fmaxf(bmax, x[t][i]);
-            }
-        }
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-        const float m_new = fmaxf(m_run, bmax);
-        const float alpha = exp2f(m_run - m_new);
-        float psum = 0.f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[t][i] = exp2f(x[t][i] - m_new);
-                psum += x[t][i];
-            }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float ai = __shfl(alpha, 4 * kq + i);
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) o[nt][i] *= ai;
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            bf16x8 pa;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pa[i] = (__bf16)x[2 * u][i];
-                pa[4 + i] = (__bf16)x[2 * u + 1][i];
-            }
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) o[nt] = mfma16(pa, as_bf16x8(va[u][nt]), o[nt]);
-        }
-    }
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (kq == 0) {
-        sm[wave][r] = m_run;
-        sl[wave][r] = l_run;
-    }
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) so[wave][4 * kq + i][nt * 16 + r] = o[nt][i];
+    const size_t pair = (size_t)s * Hkv + g;
+    for (int b = threadIdx.x; b < nb; b += 256) sI[b] = scores_in[pair * max_nb + b];
     __syncthreads();
+    select_blocks_wg(sI, nb, wblocks, topk, sh, sel + pair * max_sel, cnt + pair, max_sel, nullptr,
+                     nullptr, 0, nullptr);
+}
 
-    const int h = tid >> 4, c0 = (tid & 15) * 8;
-    if (h < G) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][h]);
-        float wt[4], Lsum = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            wt[w] = (M == -INFINITY || sm[w][h] == -INFINITY) ? 0.f : exp2f(sm[w][h] - M);
-            Lsum += wt[w] * sl[w][h];
-        }
-        float acc[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            acc[e] = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) acc[e] += wt[w] * so[w][h][c0 + e];
-        }
-        const size_t prow = ((size_t)s * Hq + g * G + h) * nsplit + split;
-        float4* dst = reinterpret_cast<float4*>(po + prow * D + c0);
-        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-        if ((tid & 15) == 0) pml[prow] = make_float2(M, Lsum);
+// ---------------------------------------------------------- launchers ---
+
+template <bool kDecode>
+static hipError_t launch_step2(const Step2Args& b, int grid, hipStream_t stream)
+{
+    switch (b.rounds) {
+        case 1: hipLaunchKernelGGL((step2_kernel<kDecode, 1>), dim3(grid), dim3(256), 0, stream, b); break;
+        case 2: hipLaunchKernelGGL((step2_kernel<kDecode, 2>), dim3(grid), dim3(256), 0, stream, b); break;
+        case 3: hipLaunchKernelGGL((step2_kernel<kDecode, 3>), dim3(grid), dim3(256), 0, stream, b); break;
+        case 4: hipLaunchKernelGGL((step2_kernel<kDecode, 4>), dim3(grid), dim3(256), 0, stream, b); break;
+        case 6: hipLaunchKernelGGL((step2_kernel<kDecode, 6>), dim3(grid), dim3(256), 0, stream, b); break;
+        default: hipLaunchKernelGGL((step2_kernel<kDecode, 8>), dim3(grid), dim3(256), 0, stream, b); break;
     }
+    return hipGetLastError();
+}
+
+static Step1Args step1_args(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
+                            const int32_t* cu_k, const Workspace& w)
+{
+    Step1Args a{};
+    a.q = q;
+    a.k_pool = kv.k_pool;
+    a.v_pool = kv.v_pool;
+    a.kc_pool = kv.kc_pool;
+    a.table = kv.block_table;
+    a.cu_k = cu_k;
+    a.max_blocks = kv.max_blocks_per_seq;
+    a.Lmax = pl.Lmax;
+    a.B = pl.B;
+    a.Hq = pl.Hq;
+    a.Hkv = pl.Hkv;
+    a.G = pl.G;
+    a.scale_log2 = pl.scale_log2;
+    a.score_groups = pl.score_groups;
+    a.z = w.z;
+    a.zstride = pl.zstride;
+    a.zpart = w.zpart;
+    a.nchunk = pl.nchunk;
+    a.counter = w.counter1;
+    a.topk = pl.topk;
+    a.wblocks = pl.wblocks;
+    a.max_nb = pl.max_nb;
+    a.max_sel = pl.max_sel;
+    a.top_span = pl.top_span;
+    a.po = w.po;
+    a.pml = w.pml;
+    a.nsplit = pl.nsplit;
+    return a;
+}
+
+static hipError_t launch_step1(const Plan& pl, const Step1Args& a, int win_groups,
+                               hipStream_t stream)
+{
+    const int npairs = pl.B * pl.Hkv;
+    dim3 grid(npairs * (pl.score_groups + win_groups));
+    const size_t lds = step1_lds_bytes(pl.max_nb);
+#define NOSA_STEP1(T) hipLaunchKernelGGL(step1_kernel<T>, grid, dim3(256), lds, stream, a)
+    switch (pl.score_tiles) {
+        case 1: NOSA_STEP1(1); break;
+        case 2: NOSA_STEP1(2); break;
+        case 4: NOSA_STEP1(4); break;
+        default: NOSA_STEP1(8); break;
+    }
+#undef NOSA_STEP1
+    return hipGetLastError();
+}
+
+hipError_t launch_scores_only(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
+                              const int32_t* cu_k, const Workspace& w, float* scores_out,
+                              hipStream_t stream)
+{
+    Step1Args a = step1_args(pl, kv, q, cu_k, w);
+    a.win_groups = 0;
+    a.append = 0;
+    a.do_select = 0;
+    a.scores_out = scores_out;
+    return launch_step1(pl, a, 0, stream);
+}
+
+hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
+                         const int32_t* cu_k, const Workspace& w, float* out, float* lse,
+                         int32_t* sel_out, int32_t* cnt_out, float* scores_out,
+                         hipStream_t stream)
+{
+    Step1Args a = step1_args(pl, kv, q, cu_k, w);
+    a.win_groups = pl.win_groups;
+    a.append = 1;
+    a.do_select = 1;
+    a.scores_out = scores_out;
+    a.sel_out = sel_out;
+    a.cnt_out = cnt_out;
+    a.selpg = w.selpg;
+    a.ntop = nullptr;
+    hipError_t e = launch_step1(pl, a, pl.win_groups, stream);
+    if (e != hipSuccess) return e;
+
+    Step2Args b{};
+    b.q = q;
+    b.k_pool = kv.k_pool;
+    b.v_pool = kv.v_pool;
+    b.table = kv.block_table;
+    b.cu_k = cu_k;
+    b.max_blocks = kv.max_blocks_per_seq;
+    b.Lmax = pl.Lmax;
+    b.B = pl.B;
+    b.Hq = pl.Hq;
+    b.Hkv = pl.Hkv;
+    b.G = pl.G;
+    b.scale_log2 = pl.scale_log2;
+    b.groups = pl.top_groups;
+    b.rounds = pl.top_rounds;
+    b.selpg = w.selpg;
+    b.span = pl.top_span;
+    b.po = w.po;
+    b.pml = w.pml;
+    b.nsplit = pl.nsplit;
+    b.split0 = pl.win_groups;
+    b.counter = w.counter2;
+    b.out = out;
+    b.lse = lse;
+    return launch_step2<true>(b, pl.B * pl.Hkv * pl.top_groups, stream);
 }
 
 hipError_t launch_attend(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
                          const int32_t* cu_k, const int32_t* sel, const int32_t* cnt,
-                         float* po, float2* pml, hipStream_t stream)
+                         const Workspace& w, float* out, float* lse, hipStream_t stream)
 {
-    dim3 grid(pl.nsplit, pl.Hkv, pl.B);
-#define NOSA_ATTEND(R)                                                                        \
-    hipLaunchKernelGGL(attend_kernel<R>, grid, dim3(256), 0, stream, q, kv.k_pool, kv.v_pool, \
-                       kv.block_table, kv.max_blocks_per_seq, pl.Lmax, cu_k, sel, cnt,        \
-                       pl.max_sel,                                                            \
-                       pl.Hq, pl.Hkv, pl.G, pl.scale_log2, po, pml, pl.nsplit)
-    switch (pl.attn_rounds) {
-        case 1: NOSA_ATTEND(1); break;
-        case 2: NOSA_ATTEND(2); break;
-        case 3: NOSA_ATTEND(3); break;
-        default: NOSA_ATTEND(4); break;
-    }
-#undef NOSA_ATTEND
-    return hipGetLastError();
+    Step2Args b{};
+    b.q = q;
+    b.k_pool = kv.k_pool;
+    b.v_pool = kv.v_pool;
+    b.table = kv.block_table;
+    b.cu_k = cu_k;
+    b.max_blocks = kv.max_blocks_per_seq;
+    b.Lmax = pl.Lmax;
+    b.B = pl.B;
+    b.Hq = pl.Hq;
+    b.Hkv = pl.Hkv;
+    b.G = pl.G;
+    b.scale_log2 = pl.scale_log2;
+    b.groups = pl.attend_groups;
+    b.rounds = pl.attend_rounds;
+    b.sel = sel;
+    b.cnt = cnt;
+    b.max_sel = pl.max_sel;
+    b.po = w.po;
+    b.pml = w.pml;
+    b.nsplit = pl.attend_groups;
+    b.split0 = 0;
+    b.counter = w.counter2;
+    b.out = out;
+    b.lse = lse;
+    return launch_step2<false>(b, pl.B * pl.Hkv * pl.attend_groups, stream);
 }
 
-// --------------------------------------------------------------- merge ---
-
-// One workgroup of 128 threads (one per channel) per (query head, sequence).
-__global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ po,
-                                                    const float2* __restrict__ pml, int nsplit,
-                                                    float* __restrict__ out,
-                                                    float* __restrict__ lse, int Hq)
+hipError_t launch_select(const Plan& pl, const int32_t* cu_k, const float* scores_in,
+                         int32_t* sel, int32_t* cnt, hipStream_t stream)
 {
-    const int h = blockIdx.x, s = blockIdx.y, c = threadIdx.x;
-    const size_t rowq = (size_t)s * Hq + h;
-    const float2* ml = pml + rowq * nsplit;
-    float M = -INFINITY;
-    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, ml[i].x);
-    float acc = 0.f, Lsum = 0.f;
-    if (M != -INFINITY)
-        for (int i = 0; i < nsplit; ++i) {
-            const float2 v = ml[i];
-            if (v.x == -INFINITY) continue;
-            const float w = exp2f(v.x - M);
-            Lsum += w * v.y;
-            acc += w * po[(rowq * nsplit + i) * D + c];
-        }
-    const bool empty = !(Lsum > 0.f);
-    out[rowq * D + c] = empty ? 0.f : acc / Lsum;
-    if (lse && c == 0) lse[rowq] = empty ? -INFINITY : (M + log2f(Lsum)) * 0.69314718055994531f;
-}
-
-hipError_t launch_merge(const Plan& pl, const float* po, const float2* pml, float* out,
-                        float* lse, hipStream_t stream)
-{
-    dim3 grid(pl.Hq, pl.B);
-    hipLaunchKernelGGL(merge_kernel, grid, dim3(D), 0, stream, po, pml, pl.nsplit, out, lse,
-                       pl.Hq);
+    const size_t lds = sizeof(float) * (size_t)(pl.max_nb > 0 ? pl.max_nb : 1);
+    hipLaunchKernelGGL(select_kernel, dim3(pl.Hkv, pl.B), dim3(256), lds, stream, scores_in, sel,
+                       cnt, cu_k, pl.Lmax, pl.Hkv, pl.max_nb, pl.max_sel, pl.topk, pl.wblocks);
     return hipGetLastError();
 }
 

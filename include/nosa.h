@@ -33,9 +33,16 @@
  *     HIP launch NOSA_ERR_HIP.  Nothing aborts.
  *   - No global state: calls on different streams may run concurrently as
  *     long as they do not share output or workspace buffers.
+ *   - Workspace: device memory of nosa_workspace_size() bytes that must be
+ *     zero-filled before its first use (e.g. allocated with torch.zeros).
+ *     Its head holds per-(sequence, KV head) hand-off counters that every
+ *     call returns to zero, so a workspace is reused across calls without
+ *     clearing; the rest is scratch.  Calls sharing a workspace must be
+ *     ordered (same stream): overlapping calls on one workspace race.
  *
  * Supported shapes on the GPU: head_dim 128, block_size 64, kernel 32,
- * stride 16, window a multiple of 64, num_q_heads / num_kv_heads in [1, 16],
+ * stride 16, window a multiple of 64 of at most 8192 tokens,
+ * num_q_heads / num_kv_heads in [1, 16],
  * at most 8192 blocks (512K tokens) per sequence.
  *
  * Terms: L_s = cu_seqlens_k[s+1] - cu_seqlens_k[s] is the KV length of
@@ -137,7 +144,7 @@ nosa_status nosa_compress_keys(const nosa_params* params, const nosa_paged_kv* k
  * [batch][max_qblk][Hkv][max_nb] with max_qblk = ceil(max_seqlen_q/block_size)
  * (1 for decode).  cu_seqlens_q must be NULL (decode) in this build; a
  * non-NULL value gives NOSA_ERR_UNSUPPORTED.  Kc must be valid for L_s tokens.
- * Needs `workspace` of nosa_workspace_size bytes (device, any contents). */
+ * Needs a zero-initialised `workspace` of nosa_workspace_size bytes. */
 nosa_status nosa_block_scores(const nosa_params* params, const nosa_paged_kv* kv,
                               const nosa_bf16* q, const int32_t* cu_seqlens_q,
                               const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
@@ -166,7 +173,7 @@ nosa_status nosa_select_blocks(const nosa_params* params, const float* block_sco
  * scale * q_h . K[t], applied to V.  out: device fp32 [batch][Hq][d];
  * lse: device fp32 [batch][Hq] (natural log of the softmax denominator) or
  * NULL.  Block ids must be distinct and < nb(L_s).  cu_seqlens_q: NULL.
- * Needs `workspace` (device, any contents). */
+ * Needs a zero-initialised `workspace` (see above). */
 nosa_status nosa_sparse_attend(const nosa_params* params, const nosa_paged_kv* kv,
                                const nosa_bf16* q, const int32_t* cu_seqlens_q,
                                const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
@@ -184,7 +191,7 @@ nosa_status nosa_sparse_attend(const nosa_params* params, const nosa_paged_kv* k
  * L_s - 1 (its K/V must already be in the pages).  out / lse as in
  * nosa_sparse_attend (lse may be NULL).  sel_idx / sel_count / block_scores
  * are optional outputs (NULL = not written) with the layouts above
- * (max_qblk = 1).  Needs `workspace` (device, any contents). */
+ * (max_qblk = 1).  Needs a zero-initialised `workspace` (see above). */
 nosa_status nosa_decode_step(const nosa_params* params, const nosa_paged_kv* kv,
                              const nosa_bf16* q, const int32_t* cu_seqlens_k, int32_t batch,
                              int32_t max_seqlen_k, float* out, float* lse, int32_t* sel_idx,

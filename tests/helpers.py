@@ -82,7 +82,7 @@ def gpu_kc_logical(c: DecodeCase, s: int, nc: int) -> np.ndarray:
 
 def workspace(c: DecodeCase, max_seqlen_k: int) -> torch.Tensor:
     n = nosa.nosa_workspace_size(c.p, c.B, 1, max_seqlen_k)
-    return torch.empty(n, dtype=torch.uint8, device="cuda")
+    return torch.zeros(n, dtype=torch.uint8, device="cuda")
 
 
 def gpu_decode_step(c: DecodeCase, step: int = 0):

@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnosa.so")
-SOURCES = [os.path.join(CSRC, "nosa_kernels.hip"), os.path.join(CSRC, "nosa_api.cpp")]
+SOURCES = [os.path.join(CSRC, "nosa_kernels.hip"), os.path.join(CSRC, "nosa_prefill.hip"),
+           os.path.join(CSRC, "nosa_api.cpp")]
 ARCH = "gfx950"
 
 

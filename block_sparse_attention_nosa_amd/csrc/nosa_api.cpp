@@ -150,6 +150,25 @@ nosa_status make_plan(const nosa_params* p, int batch, int max_seqlen_k, Plan* p
     return NOSA_OK;
 }
 
+void make_pf_plan(const Plan& pl, int max_seqlen_q, PfPlan* pf)
+{
+    PfPlan F;
+    F.max_seqlen_q = max_seqlen_q;
+    F.max_qblk = ceil_div(max_seqlen_q > 0 ? max_seqlen_q : 1, 64);
+    F.npairs = pl.B * F.max_qblk * pl.Hkv;
+    F.rows = 64 * pl.G;
+    F.rtw = pl.G <= 1 ? 1 : pl.G <= 2 ? 2 : pl.G <= 4 ? 4 : 8;
+    F.row_groups = ceil_div(4 * pl.G, 4 * F.rtw);
+    F.key_splits = ceil_div(pl.max_nc > 0 ? pl.max_nc : 1, 256);
+    F.attn_groups = ceil_div(4 * pl.G, 8);
+    const size_t np = (size_t)F.npairs;
+    size_t off = 0;
+    F.off_part = off;   off += align256(np * F.rows * (size_t)F.key_splits * sizeof(float2));
+    F.off_colsum = off; off += align256(np * F.row_groups * (size_t)F.key_splits * 256 * sizeof(float));
+    F.bytes = off > 256 ? off : 256;
+    *pf = F;
+}
+
 Workspace carve(const Plan& pl, void* ws)
 {
     char* base = static_cast<char*>(ws);
@@ -174,10 +193,11 @@ namespace {
 
 nosa_status hip_status(hipError_t e) { return e == hipSuccess ? NOSA_OK : NOSA_ERR_HIP; }
 
-// Common checks of the query-side arguments (decode only in this build).
+// Query-side arguments: decode (cu_seqlens_q NULL, one query per sequence)
+// or a chunk per sequence (cu_seqlens_q given, at most max_seqlen_q queries).
 nosa_status check_queries(const int32_t* cu_seqlens_q, int max_seqlen_q)
 {
-    if (cu_seqlens_q != nullptr || max_seqlen_q > 1) return NOSA_ERR_UNSUPPORTED;
+    if (cu_seqlens_q == nullptr && max_seqlen_q > 1) return NOSA_ERR_INVALID;
     return NOSA_OK;
 }
 
@@ -208,11 +228,12 @@ nosa_status nosa_workspace_size(const nosa_params* params, int32_t batch, int32_
     if (st != NOSA_OK) return st;
     st = check_sizes(batch, max_seqlen_q, max_seqlen_k);
     if (st != NOSA_OK) return st;
-    if (max_seqlen_q > 1) return NOSA_ERR_UNSUPPORTED;
     Plan pl;
     st = make_plan(params, batch, max_seqlen_k, &pl);
     if (st != NOSA_OK) return st;
-    *bytes = pl.bytes;
+    PfPlan pf;
+    make_pf_plan(pl, max_seqlen_q, &pf);
+    *bytes = pl.bytes > pf.bytes ? pl.bytes : pf.bytes;
     return NOSA_OK;
 }
 
@@ -256,6 +277,13 @@ nosa_status nosa_block_scores(const nosa_params* params, const nosa_paged_kv* kv
     Plan pl;
     st = make_plan(params, batch, max_seqlen_k, &pl);
     if (st != NOSA_OK) return st;
+    if (cu_seqlens_q) {
+        PfPlan pf;
+        make_pf_plan(pl, max_seqlen_q, &pf);
+        if (!workspace || workspace_bytes < pf.bytes) return NOSA_ERR_WORKSPACE;
+        return hip_status(launch_pf_scores(pl, pf, *kv, q, cu_seqlens_q, cu_seqlens_k, workspace,
+                                           block_scores, as_stream(stream)));
+    }
     if (!workspace || workspace_bytes < pl.bytes) return NOSA_ERR_WORKSPACE;
     return hip_status(launch_scores_only(pl, *kv, q, cu_seqlens_k, carve(pl, workspace),
                                          block_scores, as_stream(stream)));
@@ -277,8 +305,8 @@ nosa_status nosa_select_blocks(const nosa_params* params, const float* block_sco
     Plan pl;
     st = make_plan(params, batch, max_seqlen_k, &pl);
     if (st != NOSA_OK) return st;
-    return hip_status(launch_select(pl, cu_seqlens_k, block_scores, sel_idx, sel_count,
-                                    as_stream(stream)));
+    return hip_status(launch_select(pl, cu_seqlens_k, cu_seqlens_q, max_seqlen_q, block_scores,
+                                    sel_idx, sel_count, as_stream(stream)));
 }
 
 nosa_status nosa_sparse_attend(const nosa_params* params, const nosa_paged_kv* kv,
@@ -301,6 +329,12 @@ nosa_status nosa_sparse_attend(const nosa_params* params, const nosa_paged_kv* k
     Plan pl;
     st = make_plan(params, batch, max_seqlen_k, &pl);
     if (st != NOSA_OK) return st;
+    if (cu_seqlens_q) {  // chunk attention: no workspace needed
+        PfPlan pf;
+        make_pf_plan(pl, max_seqlen_q, &pf);
+        return hip_status(launch_pf_attend(pl, pf, *kv, q, cu_seqlens_q, cu_seqlens_k, sel_idx,
+                                           sel_count, out, lse, as_stream(stream)));
+    }
     if (!workspace || workspace_bytes < pl.bytes) return NOSA_ERR_WORKSPACE;
     return hip_status(launch_attend(pl, *kv, q, cu_seqlens_k, sel_idx, sel_count,
                                     carve(pl, workspace), out, lse, as_stream(stream)));

@@ -1,0 +1,370 @@
+// nosa_device.h -- device code shared by the decode kernels (nosa_kernels.hip)
+// and the chunked-prefill kernels (nosa_prefill.hip): bf16 and MFMA helpers,
+// agent-coherent hand-off accesses, one-page attention on MFMA and the
+// workgroup top-k selector.  Internal; compiled into libnosa.so only.
+//
+// MFMA used: v_mfma_f32_16x16x32_bf16.  Operand layout (wave64, lane l,
+// r = l % 16, kq = l / 16): A supplies A[r][8kq .. 8kq+7], B supplies
+// B[8kq .. 8kq+7][r], the accumulator holds D[4kq + i][r] for i = 0..3.  The
+// contraction index may be permuted freely as long as A and B agree; the
+// kernels map k-step st, lane group kq to channels 32st + 8kq .. +7 so that
+// four lane groups read 64 contiguous bytes of a row.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "nosa_internal.h"
+
+namespace nosa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = kHeadDim;
+constexpr int BS = kBlock;
+constexpr int SL = kSlots;
+constexpr float kLn2 = 0.69314718055994531f;
+
+__device__ __forceinline__ int dev_num_keys(int L) { return L >= kPoolK ? (L - kPoolK) / kPoolS + 1 : 0; }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Agent-coherent 8-byte stores / loads for data handed between workgroups.
+__device__ __forceinline__ void st_pair(void* p, float a, float b)
+{
+    const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float2 ld_pair(const void* p)
+{
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)),
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+__device__ __forceinline__ float ld_one(const float* p)
+{
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Pooled key j of KV head g of a sequence: slot j % SL of page table[j / SL].
+__device__ __forceinline__ uint16_t* kc_slot(uint16_t* kc_pool, const int32_t* trow, int Hkv, int g,
+                                             int j)
+{
+    return kc_pool + (((size_t)trow[j / SL] * Hkv + g) * SL + (j % SL)) * D;
+}
+
+// Length of sequence s clamped to [0, Lmax], Lmax = min(host bound, what a
+// block-table row addresses): a device length above the host-side bound can
+// then never index past the table, the workspace rows or the LDS arrays.
+__device__ __forceinline__ int seq_len(const int32_t* cu_k, int s, int Lmax)
+{
+    int L = cu_k[s + 1] - cu_k[s];
+    L = L < 0 ? 0 : L;
+    return L < Lmax ? L : Lmax;
+}
+
+// ------------------------------------------------------ block attention ---
+
+// Row order of the K tile inside the QK^T MFMA.  Tile t = 2u + v, row
+// m = 4c + i holds token 32u + 8c + 4v + i.  With this order the
+// accumulator of lane (r, kq) ends up holding, for head r, the tokens
+// 32u + 8kq + 0..7 across tiles 2u and 2u+1: exactly the A operand of the
+// PV MFMA over the 32 tokens of k-step u.
+__device__ __forceinline__ int qk_row_token(int t, int m)
+{
+    return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
+}
+
+// Query operand of one KV head's group: B[channel][head r] (heads >= G zero).
+__device__ __forceinline__ void load_q(const uint16_t* q, int Hq, int s, int h0, int G, int r,
+                                       int kq, bf16x8 (&qb)[4])
+{
+    const uint16_t* qh = q + ((size_t)s * Hq + h0 + (r < G ? r : 0)) * D;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        uint4 w = ldg16(qh + st * 32 + kq * 8);
+        if (r >= G) w = make_uint4(0, 0, 0, 0);
+        qb[st] = as_bf16x8(w);
+    }
+}
+
+struct AttnState {
+    float m, l;
+    f32x4 o[8];
+};
+
+__device__ __forceinline__ void attn_init(AttnState& A)
+{
+    A.m = -INFINITY;
+    A.l = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) A.o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// One wave attends one 64-token page: S^T = K q^T (4 tiles x 4 k-steps), fp32
+// online softmax in log2 units, O += P V (2 k-steps x 8 channel tiles).
+// `limit` = tokens of the page that exist (tokens >= limit are masked).
+__device__ __forceinline__ void attend_page(const uint16_t* __restrict__ kb,
+                                            const uint16_t* __restrict__ vb, int limit,
+                                            const bf16x8 (&qb)[4], float scale_log2, int r,
+                                            int kq, AttnState& A)
+{
+    uint4 ka[4][4], va[2][8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int tok = qk_row_token(t, r);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) ka[t][st] = ldg16(kb + tok * D + st * 32 + kq * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) va[u][nt] = ldg16(vb + (nt * 16 + r) * BS + u * 32 + kq * 8);
+    // Keep every load of the page in flight before the first use: a wave that
+    // attends one page pays one memory latency instead of one per few loads.
+    __builtin_amdgcn_sched_barrier(0);
+
+    float x[4][4];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(ka[t][st]), qb[st], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = 32 * (t >> 1) + 8 * kq + 4 * (t & 1) + i;
+            x[t][i] = tok < limit ? acc[i] * scale_log2 : -INFINITY;
+            bmax = fmaxf(bmax, x[t][i]);
+        }
+    }
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    const float m_new = fmaxf(A.m, bmax);
+    const float alpha = exp2f(A.m - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[t][i] = exp2f(x[t][i] - m_new);
+            psum += x[t][i];
+        }
+    A.l = A.l * alpha + psum;
+    A.m = m_new;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * kq + i);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) A.o[nt][i] *= ai;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        bf16x8 pa;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pa[i] = (__bf16)x[2 * u][i];
+            pa[4 + i] = (__bf16)x[2 * u + 1][i];
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) A.o[nt] = mfma16(pa, as_bf16x8(va[u][nt]), A.o[nt]);
+    }
+}
+
+// Whole workgroup: "am I the last of `total` workgroups of this pair?"  Every
+// wave first waits for its (agent-coherent) stores to complete.  The last
+// workgroup resets the counter for the next call and invalidates its CU's L1
+// and its L2 once (agent-scope acquire), after which plain loads see every
+// other workgroup's stores.
+__device__ bool last_of_pair(uint32_t* counter, uint32_t total, int* flag_lds)
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev == total - 1;
+        if (last) {
+            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        *flag_lds = last;
+    }
+    __syncthreads();
+    return *flag_lds != 0;
+}
+
+// ------------------------------------------------------------ selection ---
+
+// Order-preserving map of a float onto uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Number of lanes of this wave below the calling lane whose bit is set.
+__device__ __forceinline__ int lanes_below(uint64_t mask)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+struct SelectLds {
+    float lse[kMaxGroup];
+    int cnt[2][4][16];  // per exchange parity, wave, value
+};
+
+// Top-min(topk, ncand) of the candidates [0, ncand) by (importance desc, block
+// asc) with the window [ncand, nb) always kept.  Writes, when non-null:
+//   sel_out[0 .. max_sel): every kept block ascending, -1 padded; *cnt_out;
+//   selpg[0 .. top_span): (block, page) of the top-k picks ascending,
+//                         (-1, -1) padded; *ntop_out.
+// Must be called by all 256 threads; sI holds the importance in LDS.  Only
+// ballots, lane counts and one LDS exchange per step: no atomics, no shuffles.
+__device__ void select_blocks_wg(const float* sI, int nb, int wblocks, int topk, SelectLds& sh,
+                                 int32_t* __restrict__ sel_out, int32_t* __restrict__ cnt_out,
+                                 int max_sel, int2* __restrict__ selpg,
+                                 int32_t* __restrict__ ntop_out, int top_span,
+                                 const int32_t* __restrict__ trow)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ncand = nb > wblocks ? nb - wblocks : 0;
+    const int kk = topk < ncand ? topk : ncand;
+    const bool partial = kk > 0 && kk < ncand;
+    uint32_t T = 0;
+    int need = 0;
+    int step = 0;
+    // Per-wave counts -> LDS -> workgroup sums.  Lane v of every wave adds up
+    // value v of the four waves, so each lane ends with one sum (no loop over
+    // all values per lane); `par` alternates so one barrier per exchange does.
+    auto publish = [&](const int* c, int nv) -> int {
+        const int par = step & 1;
+        int mine = 0;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            if (v < nv && v == lane) mine = c[v];
+        if (lane < nv) sh.cnt[par][wave][lane] = mine;
+        __syncthreads();
+        ++step;
+        return par;
+    };
+    // candidate keys of this thread (candidate round*256 + tid), first 8 rounds
+    constexpr int KR = 8;
+    uint32_t keys[KR];
+    const int rounds = (ncand + 255) / 256;
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+        const int b = i * 256 + tid;
+        keys[i] = (i < rounds && b < ncand) ? order_key(sI[b]) : 0u;
+    }
+    auto key_at = [&](int i) -> uint32_t {
+        if (i < KR) {
+            uint32_t k = 0;
+#pragma unroll
+            for (int j = 0; j < KR; ++j)
+                if (j == i) k = keys[j];
+            return k;
+        }
+        const int b = i * 256 + tid;
+        return b < ncand ? order_key(sI[b]) : 0u;
+    };
+    if (partial) {
+        // The kk-th largest key T is the largest value with #{key >= T} >= kk.
+        // Build it four bits at a time from the top: count the keys at or
+        // above each of the 15 extensions of T (ballots + lane counts, one LDS
+        // exchange), keep the largest extension that still has >= kk keys.
+        for (int bit = 28; bit >= 0; bit -= 4) {
+            int c[15];
+#pragma unroll
+            for (int d = 0; d < 15; ++d) c[d] = 0;
+            for (int i = 0; i < rounds; ++i) {
+                const uint32_t key = key_at(i);
+#pragma unroll
+                for (int d = 0; d < 15; ++d)
+                    c[d] += __popcll(__ballot(key >= (T | ((uint32_t)(d + 1) << bit))));
+            }
+            const int par = publish(c, 15);
+            const int sum = lane < 15 ? sh.cnt[par][0][lane] + sh.cnt[par][1][lane] +
+                                            sh.cnt[par][2][lane] + sh.cnt[par][3][lane]
+                                      : 0;
+            // counts fall with the digit, so the digits that keep >= kk keys
+            // are 1 .. dsel and dsel is their number
+            const int dsel = (int)__popcll(__ballot(lane < 15 && sum >= kk));
+            T |= (uint32_t)dsel << bit;
+        }
+        int ca[1] = {0};
+        for (int i = 0; i < rounds; ++i) ca[0] += __popcll(__ballot(key_at(i) > T));
+        const int par = publish(ca, 1);
+        const int na = sh.cnt[par][0][0] + sh.cnt[par][1][0] + sh.cnt[par][2][0] + sh.cnt[par][3][0];
+        need = kk - na;  // ties at T to take, lowest block ids first
+    }
+    // Ascending compaction in rounds of 256 consecutive candidates (thread tid
+    // holds candidate round*256 + tid): ranks from ballots within the wave and
+    // per-wave totals across waves.
+    int eq_base = 0, sel_base = 0;
+    for (int i = 0; i < rounds; ++i) {
+        const int b = i * 256 + tid;
+        const bool valid = b < ncand;
+        bool take;
+        if (!partial) {
+            take = valid && kk > 0;
+        } else {
+            const uint32_t key = key_at(i);
+            const bool eq = valid && key == T;
+            const uint64_t meq = __ballot(eq);
+            int ce[1] = {(int)__popcll(meq)};
+            const int par = publish(ce, 1);
+            int eq_before = eq_base + lanes_below(meq);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int cw = sh.cnt[par][w][0];
+                if (w < wave) eq_before += cw;
+                eq_base += cw;
+            }
+            take = valid && (key > T || (eq && eq_before < need));
+        }
+        const uint64_t mt = __ballot(take);
+        int ct[1] = {(int)__popcll(mt)};
+        const int par = publish(ct, 1);
+        int pos = sel_base + lanes_below(mt);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int cw = sh.cnt[par][w][0];
+            if (w < wave) pos += cw;
+            sel_base += cw;
+        }
+        if (take) {
+            if (sel_out) sel_out[pos] = b;
+            if (selpg && pos < top_span) selpg[pos] = make_int2(b, trow[b]);
+        }
+    }
+    const int nsel = sel_base;
+    const int total = nsel + (nb - ncand);
+    if (sel_out) {
+        for (int b = ncand + tid; b < nb; b += 256) sel_out[nsel + (b - ncand)] = b;
+        for (int x = total + tid; x < max_sel; x += 256) sel_out[x] = -1;
+    }
+    if (selpg)
+        for (int x = nsel + tid; x < top_span; x += 256) selpg[x] = make_int2(-1, -1);
+    if (tid == 0) {
+        if (cnt_out) *cnt_out = total;
+        if (ntop_out) *ntop_out = nsel;
+    }
+}
+
+}  // namespace nosa

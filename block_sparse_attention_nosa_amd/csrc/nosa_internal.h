@@ -60,9 +60,21 @@ struct Workspace {
     float2* pml;         // [B][Hq][nsplit'] partial (max, sum)
 };
 
+// Chunked prefill (queries at the end of each sequence, blocks of 64 queries).
+struct PfPlan {
+    int max_seqlen_q = 0, max_qblk = 0, npairs = 0;  // pairs = (sequence, q-block, KV head)
+    int rows = 0;         // 64 * G rows (query, head) per pair
+    int rtw = 1;          // row tiles of 16 per wave in the scoring passes
+    int row_groups = 0;   // scoring workgroups over the rows of a pair
+    int key_splits = 0;   // scoring workgroups over the pooled keys of a pair
+    int attn_groups = 0;  // attention workgroups (128 rows each) per pair
+    size_t off_part = 0, off_colsum = 0, bytes = 0;
+};
+
 // Builds the plan for a decode batch; returns NOSA_OK or an error.
 nosa_status make_plan(const nosa_params* p, int batch, int max_seqlen_k, Plan* plan);
 Workspace carve(const Plan& pl, void* ws);
+void make_pf_plan(const Plan& pl, int max_seqlen_q, PfPlan* pf);
 
 // ---- launchers (nosa_kernels.hip); all enqueue on `stream` and return the
 // ---- hipGetLastError() of the launches.
@@ -71,8 +83,9 @@ hipError_t launch_kc_build(const Plan& pl, const nosa_paged_kv& kv, const int32_
 hipError_t launch_scores_only(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
                               const int32_t* cu_k, const Workspace& w, float* scores_out,
                               hipStream_t stream);
-hipError_t launch_select(const Plan& pl, const int32_t* cu_k, const float* scores_in,
-                         int32_t* sel, int32_t* cnt, hipStream_t stream);
+// cu_q == nullptr: one decode query per sequence; else q-blocks of a chunk.
+hipError_t launch_select(const Plan& pl, const int32_t* cu_k, const int32_t* cu_q, int max_seqlen_q,
+                         const float* scores_in, int32_t* sel, int32_t* cnt, hipStream_t stream);
 hipError_t launch_attend(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
                          const int32_t* cu_k, const int32_t* sel, const int32_t* cnt,
                          const Workspace& w, float* out, float* lse, hipStream_t stream);
@@ -80,5 +93,13 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
                          const int32_t* cu_k, const Workspace& w, float* out, float* lse,
                          int32_t* sel_out, int32_t* cnt_out, float* scores_out,
                          hipStream_t stream);
+
+hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
+                            const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
+                            void* ws, float* scores, hipStream_t stream);
+hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
+                            const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
+                            const int32_t* sel, const int32_t* cnt, float* out, float* lse,
+                            hipStream_t stream);
 
 }  // namespace nosa

@@ -23,12 +23,8 @@
 // attention filters KV blocks, CIS score mean pooling), page "NOSA技术架构解析"
 // (section 2.1: paged KV pool; section 5.1: importance scores kept in fp32).
 //
-// MFMA used: v_mfma_f32_16x16x32_bf16.  Operand layout (wave64, lane l,
-// r = l % 16, kq = l / 16): A supplies A[r][8kq .. 8kq+7], B supplies
-// B[8kq .. 8kq+7][r], the accumulator holds D[4kq + i][r] for i = 0..3.  The
-// contraction index may be permuted freely as long as A and B agree; every
-// kernel maps k-step st, lane group kq to channels 32st + 8kq .. +7 so that
-// four lane groups read 64 contiguous bytes of a row.
+// Shared device helpers (MFMA operand layout, one-page attention, the
+// selector) are in nosa_device.h.
 //
 // Cross-workgroup hand-off ("last one done"): data that another workgroup of
 // the same launch reads (logits, per-wave partials, attention partials) is
@@ -42,60 +38,9 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "nosa_internal.h"
+#include "nosa_device.h"
 
 namespace nosa {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int D = kHeadDim;
-constexpr int BS = kBlock;
-constexpr int SL = kSlots;
-constexpr float kLn2 = 0.69314718055994531f;
-
-__device__ __forceinline__ int dev_num_keys(int L) { return L >= kPoolK ? (L - kPoolK) / kPoolS + 1 : 0; }
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Agent-coherent 8-byte stores / loads for data handed between workgroups.
-__device__ __forceinline__ void st_pair(void* p, float a, float b)
-{
-    const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
-    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float2 ld_pair(const void* p)
-{
-    const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)),
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
-}
-
-__device__ __forceinline__ float ld_one(const float* p)
-{
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Length of sequence s clamped to [0, Lmax], Lmax = min(host bound, what a
-// block-table row addresses): a device length above the host-side bound can
-// then never index past the table, the workspace rows or the LDS arrays.
-__device__ __forceinline__ int seq_len(const int32_t* cu_k, int s, int Lmax)
-{
-    int L = cu_k[s + 1] - cu_k[s];
-    L = L < 0 ? 0 : L;
-    return L < Lmax ? L : Lmax;
-}
 
 // ------------------------------------------------------- pooled keys ---
 
@@ -137,12 +82,6 @@ __device__ __forceinline__ uint4 round8(const double (&acc)[8])
                       o[6] | (o[7] << 16));
 }
 
-__device__ __forceinline__ uint16_t* kc_slot(uint16_t* kc_pool, const int32_t* trow, int Hkv, int g,
-                                             int j)
-{
-    return kc_pool + (((size_t)trow[j / SL] * Hkv + g) * SL + (j % SL)) * D;
-}
-
 // One workgroup = 16 keys x 16 channel chunks of 8.  Each thread sums the 32
 // tokens of its key for its 8 channels in fp64 (exact for bf16 inputs), then
 // scales by 1/32 (exact) and rounds once.  Keys [n_c(prev), n_c(L)) are
@@ -178,114 +117,6 @@ hipError_t launch_kc_build(const Plan& pl, const nosa_paged_kv& kv, const int32_
     hipLaunchKernelGGL(kc_build_kernel, grid, dim3(256), 0, stream, kv.k_pool, kv.kc_pool,
                        kv.block_table, kv.max_blocks_per_seq, pl.Lmax, pl.Hkv, cu_k, valid_len);
     return hipGetLastError();
-}
-
-// ------------------------------------------------------ block attention ---
-
-// Row order of the K tile inside the QK^T MFMA.  Tile t = 2u + v, row
-// m = 4c + i holds token 32u + 8c + 4v + i.  With this order the
-// accumulator of lane (r, kq) ends up holding, for head r, the tokens
-// 32u + 8kq + 0..7 across tiles 2u and 2u+1: exactly the A operand of the
-// PV MFMA over the 32 tokens of k-step u.
-__device__ __forceinline__ int qk_row_token(int t, int m)
-{
-    return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
-}
-
-// Query operand of one KV head's group: B[channel][head r] (heads >= G zero).
-__device__ __forceinline__ void load_q(const uint16_t* q, int Hq, int s, int h0, int G, int r,
-                                       int kq, bf16x8 (&qb)[4])
-{
-    const uint16_t* qh = q + ((size_t)s * Hq + h0 + (r < G ? r : 0)) * D;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        uint4 w = ldg16(qh + st * 32 + kq * 8);
-        if (r >= G) w = make_uint4(0, 0, 0, 0);
-        qb[st] = as_bf16x8(w);
-    }
-}
-
-struct AttnState {
-    float m, l;
-    f32x4 o[8];
-};
-
-__device__ __forceinline__ void attn_init(AttnState& A)
-{
-    A.m = -INFINITY;
-    A.l = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) A.o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-}
-
-// One wave attends one 64-token page: S^T = K q^T (4 tiles x 4 k-steps), fp32
-// online softmax in log2 units, O += P V (2 k-steps x 8 channel tiles).
-// `limit` = tokens of the page that exist (tokens >= limit are masked).
-__device__ __forceinline__ void attend_page(const uint16_t* __restrict__ kb,
-                                            const uint16_t* __restrict__ vb, int limit,
-                                            const bf16x8 (&qb)[4], float scale_log2, int r,
-                                            int kq, AttnState& A)
-{
-    uint4 ka[4][4], va[2][8];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int tok = qk_row_token(t, r);
-#pragma unroll
-        for (int st = 0; st < 4; ++st) ka[t][st] = ldg16(kb + tok * D + st * 32 + kq * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) va[u][nt] = ldg16(vb + (nt * 16 + r) * BS + u * 32 + kq * 8);
-    // Keep every load of the page in flight before the first use: a wave that
-    // attends one page pays one memory latency instead of one per few loads.
-    __builtin_amdgcn_sched_barrier(0);
-
-    float x[4][4];
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(ka[t][st]), qb[st], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tok = 32 * (t >> 1) + 8 * kq + 4 * (t & 1) + i;
-            x[t][i] = tok < limit ? acc[i] * scale_log2 : -INFINITY;
-            bmax = fmaxf(bmax, x[t][i]);
-        }
-    }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float m_new = fmaxf(A.m, bmax);
-    const float alpha = exp2f(A.m - m_new);
-    float psum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[t][i] = exp2f(x[t][i] - m_new);
-            psum += x[t][i];
-        }
-    A.l = A.l * alpha + psum;
-    A.m = m_new;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha, 4 * kq + i);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) A.o[nt][i] *= ai;
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        bf16x8 pa;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pa[i] = (__bf16)x[2 * u][i];
-            pa[4 + i] = (__bf16)x[2 * u + 1][i];
-        }
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) A.o[nt] = mfma16(pa, as_bf16x8(va[u][nt]), A.o[nt]);
-    }
 }
 
 // LDS for combining the four wave states of a workgroup.
@@ -340,50 +171,6 @@ __device__ void store_wg_partial(CombineLds& sh, const AttnState& A, int G, size
         if ((tid & 15) == 0) st_pair(pml + prow, M, Lsum);
     }
 }
-
-// Whole workgroup: "am I the last of `total` workgroups of this pair?"  Every
-// wave first waits for its (agent-coherent) stores to complete.  The last
-// workgroup resets the counter for the next call and invalidates its CU's L1
-// and its L2 once (agent-scope acquire), after which plain loads see every
-// other workgroup's stores.
-__device__ bool last_of_pair(uint32_t* counter, uint32_t total, int* flag_lds)
-{
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev =
-            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = prev == total - 1;
-        if (last) {
-            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        }
-        *flag_lds = last;
-    }
-    __syncthreads();
-    return *flag_lds != 0;
-}
-
-// ------------------------------------------------------------ selection ---
-
-// Order-preserving map of a float onto uint32 (larger float -> larger key).
-__device__ __forceinline__ uint32_t order_key(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Number of lanes of this wave below the calling lane whose bit is set.
-__device__ __forceinline__ int lanes_below(uint64_t mask)
-{
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
-struct SelectLds {
-    float lse[kMaxGroup];
-    int cnt[2][4][16];  // per exchange parity, wave, value
-};
 
 // Importance of every block of the pair, from z and the per-wave partials,
 // into sI[0 .. nb): mean over the keys overlapping block b (keys 4b-1 .. 4b+3
@@ -480,144 +267,6 @@ __device__ void pool_importance(const float* __restrict__ z, int zstride,
     if (scores_out)
         for (int b = nb + tid; b < max_nb; b += 256) scores_out[b] = -INFINITY;
     __syncthreads();
-}
-
-// Top-min(topk, ncand) of the candidates [0, ncand) by (importance desc, block
-// asc) with the window [ncand, nb) always kept.  Writes, when non-null:
-//   sel_out[0 .. max_sel): every kept block ascending, -1 padded; *cnt_out;
-//   selpg[0 .. top_span): (block, page) of the top-k picks ascending,
-//                         (-1, -1) padded; *ntop_out.
-// Must be called by all 256 threads; sI holds the importance in LDS.  Only
-// ballots, lane counts and one LDS exchange per step: no atomics, no shuffles.
-__device__ void select_blocks_wg(const float* sI, int nb, int wblocks, int topk, SelectLds& sh,
-                                 int32_t* __restrict__ sel_out, int32_t* __restrict__ cnt_out,
-                                 int max_sel, int2* __restrict__ selpg,
-                                 int32_t* __restrict__ ntop_out, int top_span,
-                                 const int32_t* __restrict__ trow)
-{
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int ncand = nb > wblocks ? nb - wblocks : 0;
-    const int kk = topk < ncand ? topk : ncand;
-    const bool partial = kk > 0 && kk < ncand;
-    uint32_t T = 0;
-    int need = 0;
-    int step = 0;
-    // Per-wave counts -> LDS -> workgroup sums.  Lane v of every wave adds up
-    // value v of the four waves, so each lane ends with one sum (no loop over
-    // all values per lane); `par` alternates so one barrier per exchange does.
-    auto publish = [&](const int* c, int nv) -> int {
-        const int par = step & 1;
-        int mine = 0;
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-            if (v < nv && v == lane) mine = c[v];
-        if (lane < nv) sh.cnt[par][wave][lane] = mine;
-        __syncthreads();
-        ++step;
-        return par;
-    };
-    // candidate keys of this thread (candidate round*256 + tid), first 8 rounds
-    constexpr int KR = 8;
-    uint32_t keys[KR];
-    const int rounds = (ncand + 255) / 256;
-#pragma unroll
-    for (int i = 0; i < KR; ++i) {
-        const int b = i * 256 + tid;
-        keys[i] = (i < rounds && b < ncand) ? order_key(sI[b]) : 0u;
-    }
-    auto key_at = [&](int i) -> uint32_t {
-        if (i < KR) {
-            uint32_t k = 0;
-#pragma unroll
-            for (int j = 0; j < KR; ++j)
-                if (j == i) k = keys[j];
-            return k;
-        }
-        const int b = i * 256 + tid;
-        return b < ncand ? order_key(sI[b]) : 0u;
-    };
-    if (partial) {
-        // The kk-th largest key T is the largest value with #{key >= T} >= kk.
-        // Build it four bits at a time from the top: count the keys at or
-        // above each of the 15 extensions of T (ballots + lane counts, one LDS
-        // exchange), keep the largest extension that still has >= kk keys.
-        for (int bit = 28; bit >= 0; bit -= 4) {
-            int c[15];
-#pragma unroll
-            for (int d = 0; d < 15; ++d) c[d] = 0;
-            for (int i = 0; i < rounds; ++i) {
-                const uint32_t key = key_at(i);
-#pragma unroll
-                for (int d = 0; d < 15; ++d)
-                    c[d] += __popcll(__ballot(key >= (T | ((uint32_t)(d + 1) << bit))));
-            }
-            const int par = publish(c, 15);
-            const int sum = lane < 15 ? sh.cnt[par][0][lane] + sh.cnt[par][1][lane] +
-                                            sh.cnt[par][2][lane] + sh.cnt[par][3][lane]
-                                      : 0;
-            // counts fall with the digit, so the digits that keep >= kk keys
-            // are 1 .. dsel and dsel is their number
-            const int dsel = (int)__popcll(__ballot(lane < 15 && sum >= kk));
-            T |= (uint32_t)dsel << bit;
-        }
-        int ca[1] = {0};
-        for (int i = 0; i < rounds; ++i) ca[0] += __popcll(__ballot(key_at(i) > T));
-        const int par = publish(ca, 1);
-        const int na = sh.cnt[par][0][0] + sh.cnt[par][1][0] + sh.cnt[par][2][0] + sh.cnt[par][3][0];
-        need = kk - na;  // ties at T to take, lowest block ids first
-    }
-    // Ascending compaction in rounds of 256 consecutive candidates (thread tid
-    // holds candidate round*256 + tid): ranks from ballots within the wave and
-    // per-wave totals across waves.
-    int eq_base = 0, sel_base = 0;
-    for (int i = 0; i < rounds; ++i) {
-        const int b = i * 256 + tid;
-        const bool valid = b < ncand;
-        bool take;
-        if (!partial) {
-            take = valid && kk > 0;
-        } else {
-            const uint32_t key = key_at(i);
-            const bool eq = valid && key == T;
-            const uint64_t meq = __ballot(eq);
-            int ce[1] = {(int)__popcll(meq)};
-            const int par = publish(ce, 1);
-            int eq_before = eq_base + lanes_below(meq);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const int cw = sh.cnt[par][w][0];
-                if (w < wave) eq_before += cw;
-                eq_base += cw;
-            }
-            take = valid && (key > T || (eq && eq_before < need));
-        }
-        const uint64_t mt = __ballot(take);
-        int ct[1] = {(int)__popcll(mt)};
-        const int par = publish(ct, 1);
-        int pos = sel_base + lanes_below(mt);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int cw = sh.cnt[par][w][0];
-            if (w < wave) pos += cw;
-            sel_base += cw;
-        }
-        if (take) {
-            if (sel_out) sel_out[pos] = b;
-            if (selpg && pos < top_span) selpg[pos] = make_int2(b, trow[b]);
-        }
-    }
-    const int nsel = sel_base;
-    const int total = nsel + (nb - ncand);
-    if (sel_out) {
-        for (int b = ncand + tid; b < nb; b += 256) sel_out[nsel + (b - ncand)] = b;
-        for (int x = total + tid; x < max_sel; x += 256) sel_out[x] = -1;
-    }
-    if (selpg)
-        for (int x = nsel + tid; x < top_span; x += 256) selpg[x] = make_int2(-1, -1);
-    if (tid == 0) {
-        if (cnt_out) *cnt_out = total;
-        if (ntop_out) *ntop_out = nsel;
-    }
 }
 
 // --------------------------------------------------------------- step 1 ---
@@ -947,21 +596,33 @@ __global__ __launch_bounds__(256) void step2_kernel(Step2Args a)
 
 // ------------------------------------------------------ select (alone) ---
 
-// Selection from given importance: one workgroup per pair.
+// Selection from given importance: one workgroup per row of the importance
+// (sequence, or sequence x q-block, times KV head).  For a decode row the
+// blocks are those of the L tokens; for q-block r of a chunk of Lq queries
+// they end at the block of the q-block's last query, L - Lq + min(64r + 64, Lq) - 1.
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ scores_in,
                                                      int32_t* __restrict__ sel,
                                                      int32_t* __restrict__ cnt,
-                                                     const int32_t* __restrict__ cu_k, int Lmax,
-                                                     int Hkv, int max_nb, int max_sel, int topk,
-                                                     int wblocks)
+                                                     const int32_t* __restrict__ cu_k,
+                                                     const int32_t* __restrict__ cu_q, int Lqmax,
+                                                     int max_qblk, int Lmax, int Hkv, int max_nb,
+                                                     int max_sel, int topk, int wblocks)
 {
     extern __shared__ __align__(16) char smem[];
     __shared__ SelectLds sh;
     float* sI = reinterpret_cast<float*>(smem);
-    const int g = blockIdx.x, s = blockIdx.y;
+    const int g = blockIdx.x, sr = blockIdx.y;
+    const int s = sr / max_qblk, qb = sr % max_qblk;
     const int L = seq_len(cu_k, s, Lmax);
-    const int nb = (L + BS - 1) / BS;
-    const size_t pair = (size_t)s * Hkv + g;
+    int nb = (L + BS - 1) / BS;
+    if (cu_q) {
+        int Lq = cu_q[s + 1] - cu_q[s];
+        Lq = Lq < 0 ? 0 : (Lq > Lqmax ? Lqmax : Lq);
+        Lq = Lq < L ? Lq : L;
+        const int left = Lq - 64 * qb;
+        nb = left > 0 ? (L - Lq + 64 * qb + (left < 64 ? left : 64) - 1) / BS + 1 : 0;
+    }
+    const size_t pair = (size_t)sr * Hkv + g;
     for (int b = threadIdx.x; b < nb; b += 256) sI[b] = scores_in[pair * max_nb + b];
     __syncthreads();
     select_blocks_wg(sI, nb, wblocks, topk, sh, sel + pair * max_sel, cnt + pair, max_sel, nullptr,
@@ -1123,12 +784,14 @@ hipError_t launch_attend(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
     return launch_step2<false>(b, pl.B * pl.Hkv * pl.attend_groups, stream);
 }
 
-hipError_t launch_select(const Plan& pl, const int32_t* cu_k, const float* scores_in,
-                         int32_t* sel, int32_t* cnt, hipStream_t stream)
+hipError_t launch_select(const Plan& pl, const int32_t* cu_k, const int32_t* cu_q, int max_seqlen_q,
+                         const float* scores_in, int32_t* sel, int32_t* cnt, hipStream_t stream)
 {
     const size_t lds = sizeof(float) * (size_t)(pl.max_nb > 0 ? pl.max_nb : 1);
-    hipLaunchKernelGGL(select_kernel, dim3(pl.Hkv, pl.B), dim3(256), lds, stream, scores_in, sel,
-                       cnt, cu_k, pl.Lmax, pl.Hkv, pl.max_nb, pl.max_sel, pl.topk, pl.wblocks);
+    const int max_qblk = cu_q ? ceil_div(max_seqlen_q, 64) : 1;
+    hipLaunchKernelGGL(select_kernel, dim3(pl.Hkv, pl.B * max_qblk), dim3(256), lds, stream,
+                       scores_in, sel, cnt, cu_k, cu_q, max_seqlen_q, max_qblk, pl.Lmax, pl.Hkv,
+                       pl.max_nb, pl.max_sel, pl.topk, pl.wblocks);
     return hipGetLastError();
 }
 

@@ -1,0 +1,536 @@
+// nosa_prefill.hip -- CDNA4 (gfx950) kernels of the chunked sparse prefill:
+// a chunk of Lq queries at the end of a sequence's context, taken in query
+// blocks of 64 consecutive queries from the chunk start.  For every
+// (sequence, query block, KV head) -- a "pair" below -- the method runs as in
+// decode with the query block in place of the single query
+// [page "NOSA技术架构解析", section 1.3: the fully sparse mode also prefills
+// sparsely; page "NOSA-1B 性能基准全解析", sections 三.2-三.3 for the steps]:
+//   * pooled-key scores of every query of the block and every head of the
+//     group, softmax per (query, head) over the keys that query can see
+//     (window end 16j + 32 <= p + 1), summed over the block's queries and
+//     the group's heads, mean-pooled into 64-token block importance;
+//   * top-k over the blocks before the window, the window being the 16 blocks
+//     ending at the block of the query block's last query;
+//   * exact attention of every query over the kept blocks, causal (t <= p).
+// Kernels: pf_score_kernel<1> (per-row (max, sum exp2) partials per key
+// split), pf_score_kernel<2> (column sums of exp2(z - lse_row) per key),
+// pf_pool_kernel (block importance), the shared selector, pf_attend_kernel.
+// All contractions run on v_mfma_f32_16x16x32_bf16 with rows = (query, head)
+// pairs of the block in tiles of 16.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "nosa_device.h"
+
+namespace nosa {
+
+constexpr int kQB = 64;   // queries per query block
+constexpr int kKPS = 256; // pooled keys per split of the scoring passes
+
+struct PfArgs {
+    const uint16_t* q;
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    const uint16_t* kc_pool;
+    const int32_t* table;
+    const int32_t* cu_k;
+    const int32_t* cu_q;
+    int max_blocks, Lmax, Lqmax, B, Hq, Hkv, G, max_qblk;
+    float scale_log2;
+    int rows;        // 64 * G rows per pair: row = query * G + head
+    int row_groups;  // workgroups over the rows of a pair
+    int key_splits;  // workgroups over the pooled keys of a pair
+    int zlen;        // key_splits * kKPS
+    float2* part;    // [pairs][rows][key_splits] per-row (max, sum exp2)
+    float* colsum;   // [pairs][row_groups][zlen] per-key sums over a row group
+    float* scores;   // [pairs][max_nb] block importance
+    int max_nb;
+    const int32_t* sel;  // [pairs][max_sel]
+    const int32_t* cnt;  // [pairs]
+    int max_sel;
+    float* out;  // [total_q][Hq][D]
+    float* lse;  // [total_q][Hq] or null
+};
+
+// Geometry of one pair.
+struct PfPair {
+    int s, r, g;
+    int L, Lq, q0;   // KV length, chunk length, first q row of the sequence
+    int p0, nq;      // position of the block's first query, queries in the block
+    int nck;         // pooled keys visible to the block's last query
+    int nb;          // blocks up to the block of the last query
+    bool empty;
+};
+
+__device__ __forceinline__ PfPair pf_pair(const PfArgs& a, int pair)
+{
+    PfPair P;
+    P.g = pair % a.Hkv;
+    const int sr = pair / a.Hkv;
+    P.s = sr / a.max_qblk;
+    P.r = sr % a.max_qblk;
+    P.L = seq_len(a.cu_k, P.s, a.Lmax);
+    int Lq = a.cu_q[P.s + 1] - a.cu_q[P.s];
+    Lq = Lq < 0 ? 0 : (Lq > a.Lqmax ? a.Lqmax : Lq);
+    P.Lq = Lq < P.L ? Lq : P.L;
+    P.q0 = a.cu_q[P.s];
+    P.p0 = P.L - P.Lq + kQB * P.r;
+    const int left = P.Lq - kQB * P.r;
+    P.nq = left < kQB ? left : kQB;
+    P.empty = P.nq <= 0;
+    const int p_last = P.p0 + (P.nq > 0 ? P.nq : 1) - 1;
+    P.nck = dev_num_keys(p_last + 1);
+    P.nb = p_last / BS + 1;
+    return P;
+}
+
+// ------------------------------------------------------------- scoring ---
+
+struct PfScoreLds {
+    float lse[32 * 16];          // per row of the workgroup (pass 2)
+    float ksum[4][kKPS];         // per wave, per key of the split (pass 2)
+};
+
+// Workgroup = 4 waves x RTW row tiles of 16 rows, over the kKPS pooled keys of
+// one split.  PASS 1 writes per-row (max, sum exp2) over the split's visible
+// keys; PASS 2 writes, for every key, sum over the workgroup's rows of
+// exp2(z - lse_row) (lse from the pass-1 partials), in a fixed order.
+template <int PASS, int RTW>
+__global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
+{
+    __shared__ PfScoreLds sh;
+    const int per_pair = a.row_groups * a.key_splits;
+    const int pair = blockIdx.x / per_pair;
+    const int rg = (blockIdx.x % per_pair) / a.key_splits;
+    const int ks = blockIdx.x % a.key_splits;
+    const PfPair P = pf_pair(a, pair);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const int key_lo = ks * kKPS;
+    const int key_hi = min(key_lo + kKPS, P.nck);
+    const int32_t* trow = a.table + (size_t)P.s * a.max_blocks;
+    const int row_tile0 = (rg * 4 + wave) * RTW;  // first row tile of this wave
+    const int wg_row0 = rg * 4 * RTW * 16;        // first row of the workgroup
+
+    if (PASS == 2) {
+        // lse of every row of the workgroup from the pass-1 partials
+        for (int x = tid; x < 4 * RTW * 16; x += 256) {
+            const int row = wg_row0 + x;
+            float m = -INFINITY, acc = 0.f;
+            if (row < a.rows && !P.empty) {
+                const float2* pp = a.part + ((size_t)pair * a.rows + row) * a.key_splits;
+                for (int i = 0; i < a.key_splits; ++i) {
+                    const float2 v = pp[i];
+                    if (!(v.y > 0.f)) continue;
+                    const float mn = fmaxf(m, v.x);
+                    acc = acc * exp2f(m - mn) + v.y * exp2f(v.x - mn);
+                    m = mn;
+                }
+            }
+            sh.lse[x] = acc > 0.f ? m + log2f(acc) : INFINITY;  // +inf: row contributes 0
+        }
+        __syncthreads();
+    }
+
+    // query operand of the wave's row tiles; rows of absent queries are zero
+    bf16x8 qb[RTW][4];
+    int qpos[RTW];  // query position of this lane's row r in each tile (-1: none)
+#pragma unroll
+    for (int u = 0; u < RTW; ++u) {
+        const int row = (row_tile0 + u) * 16 + r;
+        const int qi = row / a.G, h = row % a.G;
+        const bool ok = !P.empty && row < a.rows && qi < P.nq;
+        qpos[u] = ok ? P.p0 + qi : -1;
+        const uint16_t* qr = a.q + ((size_t)(P.q0 + kQB * P.r + (ok ? qi : 0)) * a.Hq + P.g * a.G + h) * D;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            uint4 w = ok ? ldg16(qr + st * 32 + kq * 8) : make_uint4(0, 0, 0, 0);
+            qb[u][st] = as_bf16x8(w);
+        }
+    }
+    float lse_r[RTW];
+    if (PASS == 2) {
+#pragma unroll
+        for (int u = 0; u < RTW; ++u) lse_r[u] = sh.lse[(wave * RTW + u) * 16 + r];
+    }
+    float m_run[RTW], s_run[RTW];
+#pragma unroll
+    for (int u = 0; u < RTW; ++u) {
+        m_run[u] = -INFINITY;
+        s_run[u] = 0.f;
+    }
+
+    for (int kt = key_lo; kt < key_hi; kt += 16) {
+        uint4 kf[4];
+        const int key = kt + r;
+        if (key < key_hi) {
+            const uint16_t* kp = kc_slot(const_cast<uint16_t*>(a.kc_pool), trow, a.Hkv, P.g, key);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) kf[st] = ldg16(kp + st * 32 + kq * 8);
+        } else {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) kf[st] = make_uint4(0, 0, 0, 0);
+        }
+        float colacc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < RTW; ++u) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(kf[st]), qb[u][st], acc);
+            // visible: key < n_c(p + 1)  <=>  16 * key + 32 <= p + 1
+            float zz[4];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int kj = kt + 4 * kq + i;
+                const bool vis = qpos[u] >= 0 && kj < key_hi && kj * kPoolS + kPoolK <= qpos[u] + 1;
+                zz[i] = vis ? acc[i] * a.scale_log2 : -INFINITY;
+                tmax = fmaxf(tmax, zz[i]);
+            }
+            if (PASS == 1) {
+                if (tmax != -INFINITY) {
+                    const float mn = fmaxf(m_run[u], tmax);
+                    float add = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) add += exp2f(zz[i] - mn);
+                    s_run[u] = s_run[u] * exp2f(m_run[u] - mn) + add;
+                    m_run[u] = mn;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) colacc[i] += exp2f(zz[i] - lse_r[u]);
+            }
+        }
+        if (PASS == 2) {
+            // sum over the 16 rows (lanes r) of each key; lane r == 0 holds it
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) colacc[i] += __shfl_xor(colacc[i], off);
+            }
+            if (r == 0)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sh.ksum[wave][kt - key_lo + 4 * kq + i] = colacc[i];
+        }
+    }
+
+    if (PASS == 1) {
+#pragma unroll
+        for (int u = 0; u < RTW; ++u) {
+            float m = m_run[u], s = s_run[u];
+#pragma unroll
+            for (int off = 16; off < 64; off <<= 1) {
+                const float mo = __shfl_xor(m, off), so = __shfl_xor(s, off);
+                const float mn = fmaxf(m, mo);
+                s = mn == -INFINITY ? 0.f : s * exp2f(m - mn) + so * exp2f(mo - mn);
+                m = mn;
+            }
+            const int row = (row_tile0 + u) * 16 + r;
+            if (kq == 0 && row < a.rows)
+                a.part[((size_t)pair * a.rows + row) * a.key_splits + ks] = make_float2(m, s);
+        }
+    } else {
+        __syncthreads();
+        float* dst = a.colsum + ((size_t)pair * a.row_groups + rg) * a.zlen + key_lo;
+        for (int x = tid; x < kKPS; x += 256) {
+            const int kj = key_lo + x;
+            float v = 0.f;
+            if (kj < key_hi) v = ((sh.ksum[0][x] + sh.ksum[1][x]) + sh.ksum[2][x]) + sh.ksum[3][x];
+            dst[x] = v;
+        }
+    }
+}
+
+// Block importance of a pair: sigma[j] = sum over row groups (fixed order) of
+// the column sums; importance of block b = mean of sigma over the keys 4b-1 ..
+// 4b+3 that the block's last query sees.  One workgroup per pair.
+__global__ __launch_bounds__(256) void pf_pool_kernel(PfArgs a)
+{
+    extern __shared__ __align__(16) char smem[];
+    float* sI = reinterpret_cast<float*>(smem);
+    const int pair = blockIdx.x;
+    const PfPair P = pf_pair(a, pair);
+    const int tid = threadIdx.x;
+    float* out = a.scores + (size_t)pair * a.max_nb;
+    const int nb = P.empty ? 0 : P.nb;
+    for (int b = tid; b < nb; b += 256) sI[b] = 0.f;
+    __syncthreads();
+    const float* cs = a.colsum + (size_t)pair * a.row_groups * a.zlen;
+    for (int j0 = 4 * tid; j0 < (P.empty ? 0 : P.nck); j0 += 4 * 256) {
+        float sg[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = 0.f;
+            for (int q = 0; q < a.row_groups; ++q) v += cs[(size_t)q * a.zlen + j0 + e];
+            sg[e] = j0 + e < P.nck ? v : 0.f;
+        }
+        const int b = j0 >> 2;
+        atomicAdd(&sI[b], (sg[0] + sg[1]) + (sg[2] + sg[3]));
+        if (j0 + 3 < P.nck && b + 1 < nb) atomicAdd(&sI[b + 1], sg[3]);
+    }
+    __syncthreads();
+    for (int b = tid; b < a.max_nb; b += 256) {
+        float I = -INFINITY;
+        if (b < nb) {
+            const int jlo = max(4 * b - 1, 0), jhi = min(4 * b + 3, P.nck - 1);
+            if (jlo <= jhi) I = sI[b] / (float)(jhi - jlo + 1);
+        }
+        out[b] = I;
+    }
+}
+
+// ------------------------------------------------------------ attention ---
+
+// K page in LDS: 64 rows of 128 bf16 padded to 272 bytes; V page: 128 channel
+// rows of 64 bf16 padded to 144 bytes.  Both paddings make the 16-byte
+// fragment reads of 16 lanes land on distinct bank groups.
+constexpr int kKRow = 136;  // bf16 per padded K row
+constexpr int kVRow = 72;   // bf16 per padded V row
+
+struct PfAttnLds {
+    uint16_t k[64 * kKRow];
+    uint16_t v[128 * kVRow];
+};
+
+// Workgroup = 4 waves x 2 row tiles (128 rows) of one pair; loops over the
+// pair's kept pages, each staged once through LDS for all 8 row tiles, the
+// next page's loads in flight while the current one is computed.
+__global__ __launch_bounds__(256) void pf_attend_kernel(PfArgs a, int attn_groups)
+{
+    __shared__ PfAttnLds sh;
+    const int pair = blockIdx.x / attn_groups, ag = blockIdx.x % attn_groups;
+    const PfPair P = pf_pair(a, pair);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const int32_t* trow = a.table + (size_t)P.s * a.max_blocks;
+    const int n = P.empty ? 0 : min(a.cnt[pair], a.max_sel);
+    const int32_t* sl = a.sel + (size_t)pair * a.max_sel;
+
+    bf16x8 qb[2][4];
+    int qpos[2];
+    int qrow[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int row = ((ag * 4 + wave) * 2 + u) * 16 + r;
+        const int qi = row / a.G, h = row % a.G;
+        const bool ok = !P.empty && row < a.rows && qi < P.nq;
+        qpos[u] = ok ? P.p0 + qi : -1;
+        qrow[u] = ok ? (P.q0 + kQB * P.r + qi) * a.Hq + P.g * a.G + h : -1;
+        const uint16_t* qr = a.q + (size_t)(ok ? qrow[u] : 0) * D;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            uint4 w = ok ? ldg16(qr + st * 32 + kq * 8) : make_uint4(0, 0, 0, 0);
+            qb[u][st] = as_bf16x8(w);
+        }
+    }
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    f32x4 o[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) o[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // global -> register staging of one page: thread tid moves K chunks
+    // tid + 256c (row = chunk / 16, 16-byte column chunk % 16) and V chunks
+    // tid + 256c (row = chunk / 8, column chunk % 8), c < 4
+    uint4 stk[4], stv[4];
+    auto fetch = [&](int idx) {
+        int b = idx < n ? sl[idx] : -1;
+        if (b < 0 || b >= P.nb) b = -1;
+        const int page = b >= 0 ? trow[b] : 0;
+        const uint16_t* kb = a.k_pool + ((size_t)page * a.Hkv + P.g) * BS * D;
+        const uint16_t* vb = a.v_pool + ((size_t)page * a.Hkv + P.g) * D * BS;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int ch = tid + 256 * c;
+            stk[c] = b >= 0 ? ldg16(kb + (ch >> 4) * D + (ch & 15) * 8) : make_uint4(0, 0, 0, 0);
+            stv[c] = b >= 0 ? ldg16(vb + (ch >> 3) * BS + (ch & 7) * 8) : make_uint4(0, 0, 0, 0);
+        }
+        return b;
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int ch = tid + 256 * c;
+            *reinterpret_cast<uint4*>(&sh.k[(ch >> 4) * kKRow + (ch & 15) * 8]) = stk[c];
+            *reinterpret_cast<uint4*>(&sh.v[(ch >> 3) * kVRow + (ch & 7) * 8]) = stv[c];
+        }
+    };
+
+    int b_cur = n > 0 ? fetch(0) : -1;
+    stash();
+    __syncthreads();
+    for (int idx = 0; idx < n; ++idx) {
+        const int b_next = idx + 1 < n ? fetch(idx + 1) : -1;  // in flight during compute
+        if (b_cur >= 0) {
+            // S^T = K q^T for both row tiles: K fragments from LDS, shared
+            float x[2][4][4];
+            float bmax[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int tok = qk_row_token(t, r);
+                bf16x8 kf[4];
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    kf[st] = as_bf16x8(*reinterpret_cast<const uint4*>(&sh.k[tok * kKRow + st * 32 + kq * 8]));
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) acc = mfma16(kf[st], qb[u][st], acc);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tk = b_cur * BS + 32 * (t >> 1) + 8 * kq + 4 * (t & 1) + i;
+                        const bool vis = qpos[u] >= 0 && tk <= qpos[u] && tk < P.L;
+                        x[u][t][i] = vis ? acc[i] * a.scale_log2 : -INFINITY;
+                        bmax[u] = fmaxf(bmax[u], x[u][t][i]);
+                    }
+                }
+            }
+            bf16x8 pa[2][2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float bm = bmax[u];
+                bm = fmaxf(bm, __shfl_xor(bm, 16));
+                bm = fmaxf(bm, __shfl_xor(bm, 32));
+                const float m_new = fmaxf(m_run[u], bm);
+                // a row with nothing visible yet keeps m = -inf and adds nothing
+                const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run[u] - m_new);
+                float psum = 0.f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float e = m_new == -INFINITY ? 0.f : exp2f(x[u][t][i] - m_new);
+                        x[u][t][i] = e;
+                        psum += e;
+                    }
+                l_run[u] = l_run[u] * alpha + psum;
+                m_run[u] = m_new;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha, 4 * kq + i);
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) o[u][nt][i] *= ai;
+                }
+#pragma unroll
+                for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pa[u][uu][i] = (__bf16)x[u][2 * uu][i];
+                        pa[u][uu][4 + i] = (__bf16)x[u][2 * uu + 1][i];
+                    }
+            }
+            // O += P V: V fragments from LDS, shared by both row tiles
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) {
+                    const bf16x8 vf = as_bf16x8(
+                        *reinterpret_cast<const uint4*>(&sh.v[(nt * 16 + r) * kVRow + uu * 32 + kq * 8]));
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) o[u][nt] = mfma16(pa[u][uu], vf, o[u][nt]);
+                }
+        }
+        __syncthreads();  // every wave is done with the current page
+        if (idx + 1 < n) stash();
+        __syncthreads();
+        b_cur = b_next;
+    }
+
+    // normalise and store: lane holds O[rows 4kq + i][channels 16nt + r]
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        float l = l_run[u];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        if (kq == 0 && qrow[u] >= 0 && a.lse)
+            a.lse[qrow[u]] = l > 0.f ? (m_run[u] + log2f(l)) * 0.69314718055994531f : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float inv_i = __shfl(inv, 4 * kq + i);
+            const int row_i = __shfl(qrow[u], 4 * kq + i);
+            if (row_i < 0) continue;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) a.out[(size_t)row_i * D + nt * 16 + r] = o[u][nt][i] * inv_i;
+        }
+    }
+}
+
+// ---------------------------------------------------------- launchers ---
+
+static PfArgs pf_args(const Plan& pl, const PfPlan& pf, const nosa_paged_kv* kv,
+                      const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k)
+{
+    PfArgs a{};
+    a.q = q;
+    if (kv) {
+        a.k_pool = kv->k_pool;
+        a.v_pool = kv->v_pool;
+        a.kc_pool = kv->kc_pool;
+        a.table = kv->block_table;
+        a.max_blocks = kv->max_blocks_per_seq;
+    }
+    a.cu_k = cu_k;
+    a.cu_q = cu_q;
+    a.Lmax = pl.Lmax;
+    a.Lqmax = pf.max_seqlen_q;
+    a.B = pl.B;
+    a.Hq = pl.Hq;
+    a.Hkv = pl.Hkv;
+    a.G = pl.G;
+    a.max_qblk = pf.max_qblk;
+    a.scale_log2 = pl.scale_log2;
+    a.rows = pf.rows;
+    a.row_groups = pf.row_groups;
+    a.key_splits = pf.key_splits;
+    a.zlen = pf.key_splits * kKPS;
+    a.max_nb = pl.max_nb;
+    a.max_sel = pl.max_sel;
+    return a;
+}
+
+hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
+                            const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
+                            void* ws, float* scores, hipStream_t stream)
+{
+    PfArgs a = pf_args(pl, pf, &kv, q, cu_q, cu_k);
+    a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + pf.off_part);
+    a.colsum = reinterpret_cast<float*>(static_cast<char*>(ws) + pf.off_colsum);
+    a.scores = scores;
+    const dim3 grid(pf.npairs * pf.row_groups * pf.key_splits);
+#define NOSA_PF(PASS, R) hipLaunchKernelGGL((pf_score_kernel<PASS, R>), grid, dim3(256), 0, stream, a)
+    for (int pass = 1; pass <= 2; ++pass) {
+        switch (pf.rtw) {
+            case 1: if (pass == 1) NOSA_PF(1, 1); else NOSA_PF(2, 1); break;
+            case 2: if (pass == 1) NOSA_PF(1, 2); else NOSA_PF(2, 2); break;
+            case 4: if (pass == 1) NOSA_PF(1, 4); else NOSA_PF(2, 4); break;
+            default: if (pass == 1) NOSA_PF(1, 8); else NOSA_PF(2, 8); break;
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+#undef NOSA_PF
+    const size_t lds = sizeof(float) * (size_t)(pl.max_nb > 0 ? pl.max_nb : 1);
+    hipLaunchKernelGGL(pf_pool_kernel, dim3(pf.npairs), dim3(256), lds, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
+                            const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
+                            const int32_t* sel, const int32_t* cnt, float* out, float* lse,
+                            hipStream_t stream)
+{
+    PfArgs a = pf_args(pl, pf, &kv, q, cu_q, cu_k);
+    a.sel = sel;
+    a.cnt = cnt;
+    a.out = out;
+    a.lse = lse;
+    hipLaunchKernelGGL(pf_attend_kernel, dim3(pf.npairs * pf.attn_groups), dim3(256), 0, stream, a,
+                       pf.attn_groups);
+    return hipGetLastError();
+}
+
+}  // namespace nosa

@@ -89,7 +89,9 @@ def test_null_and_size_errors(L):
     assert f(ctypes.byref(p), -1, 1, 4096, ctypes.byref(out)) == 2
     assert f(ctypes.byref(p), 1, 1, 0, ctypes.byref(out)) == 2
     assert f(ctypes.byref(p), 1, 1, 8192 * 64 + 1, ctypes.byref(out)) == 3
-    assert f(ctypes.byref(p), 1, 64, 4096, ctypes.byref(out)) == 3   # prefill not in decode ABI
+    assert f(ctypes.byref(p), 1, 64, 4096, ctypes.byref(out)) == 0   # a 64-query chunk
+    assert out.value > 0
+    assert f(ctypes.byref(p), 1, 8192, 4096, ctypes.byref(out)) == 2  # more queries than keys
 
 
 FAKE = 0x1000  # never dereferenced: every call below fails validation first
@@ -131,8 +133,10 @@ def test_other_entry_points_host_errors(L):
                                 None) == 0
     assert L.nosa_block_scores(ctypes.byref(p), ctypes.byref(kv), FAKE, None, FAKE, 8, 1, 16384,
                                None, FAKE, 1 << 30, None) == 1
-    assert L.nosa_block_scores(ctypes.byref(p), ctypes.byref(kv), FAKE, FAKE, FAKE, 8, 1, 16384,
-                               FAKE, FAKE, 1 << 30, None) == 3        # q-blocks: not here
+    assert L.nosa_block_scores(ctypes.byref(p), ctypes.byref(kv), FAKE, FAKE, FAKE, 8, 64, 16384,
+                               FAKE, FAKE, 16, None) == 4             # chunk: workspace too small
+    assert L.nosa_block_scores(ctypes.byref(p), ctypes.byref(kv), FAKE, None, FAKE, 8, 64, 16384,
+                               FAKE, FAKE, 1 << 30, None) == 2        # 64 queries need cu_seqlens_q
     assert L.nosa_block_scores(ctypes.byref(p), ctypes.byref(kv), FAKE, None, FAKE, 8, 1, 16384,
                                FAKE, FAKE, 16, None) == 4
     assert L.nosa_select_blocks(ctypes.byref(p), None, None, FAKE, 8, 1, 16384, FAKE, FAKE,

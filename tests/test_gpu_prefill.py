@@ -1,0 +1,172 @@
+"""GPU parity of the chunked sparse prefill (cu_seqlens_q given): block
+importance per 64-query block, selection, causal attention on MFMA.  The
+131072-token workload is checked on sampled query blocks: the CPU reference
+solves each sampled block as its own problem with the context cut after the
+block's last query, which is the same computation (nothing later is visible)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_nosa_amd import nosa, synth
+from oracle import oracle as ora
+
+from helpers import OUT_MAX_ABS, OUT_MEAN_ABS, TIE_BAND, build_kc, log, make_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(lens, q_lens, hq=16, hkv=2, topk=8, window=1024, seed=3):
+    return synth.Workload(lens=list(lens), q_lens=list(q_lens), num_q_heads=hq, num_kv_heads=hkv,
+                          topk=topk, window=window, seed=seed, name="pf")
+
+
+def gpu_prefill(c):
+    w = c.w
+    B = w.batch
+    maxL, maxLq = max(w.lens), max(w.q_lens)
+    max_qblk = max(1, math.ceil(maxLq / 64))
+    max_nb = math.ceil(maxL / 64)
+    max_sel = w.topk + w.window // 64
+    q = c.inp["q"].cuda()
+    cu_q = c.inp["cu_q"].cuda().to(torch.int32)
+    cu_k = synth.cu_from_lens(w.lens, "cuda")
+    scores = torch.full((B, max_qblk, w.num_kv_heads, max_nb), float("nan"), device="cuda")
+    ws = torch.zeros(nosa.nosa_workspace_size(c.p, B, maxLq, maxL), dtype=torch.uint8,
+                     device="cuda")
+    nosa.nosa_block_scores(c.p, c.kv, q, cu_q, cu_k, B, maxLq, maxL, scores, ws)
+    sel = torch.full((B, max_qblk, w.num_kv_heads, max_sel), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, max_qblk, w.num_kv_heads), -7, dtype=torch.int32, device="cuda")
+    nosa.nosa_select_blocks(c.p, scores, cu_q, cu_k, B, maxLq, maxL, sel, cnt)
+    out = torch.full((q.shape[0], w.num_q_heads, 128), float("nan"), device="cuda")
+    lse = torch.full((q.shape[0], w.num_q_heads), float("nan"), device="cuda")
+    nosa.nosa_sparse_attend(c.p, c.kv, q, cu_q, cu_k, B, maxLq, maxL, sel, cnt, out, lse, ws)
+    torch.cuda.synchronize()
+    res = dict(scores=scores.cpu().numpy(), sel=sel.cpu().numpy(), cnt=cnt.cpu().numpy(),
+               out=out.cpu().numpy(), lse=lse.cpu().numpy())
+    return res, (q, cu_q, cu_k, out, lse, ws)
+
+
+def attend_with(c, sel_np, cnt_np, args):
+    q, cu_q, cu_k, out, lse, ws = args
+    w = c.w
+    sel = torch.as_tensor(np.ascontiguousarray(sel_np), dtype=torch.int32).cuda()
+    cnt = torch.as_tensor(np.ascontiguousarray(cnt_np), dtype=torch.int32).cuda()
+    out.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    nosa.nosa_sparse_attend(c.p, c.kv, q, cu_q, cu_k, w.batch, max(w.q_lens), max(w.lens), sel,
+                            cnt, out, lse, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def qblock_nb(L, Lq, r):
+    p_last = L - Lq + min(64 * r + 64, Lq) - 1
+    return p_last // 64 + 1
+
+
+def check_rows(g, o, rows, w, tag):
+    """rows: list of (s, r, s_o, r_o): GPU row (s, r) against reference row (s_o, r_o)."""
+    wb = w.window // 64
+    exempt = 0
+    for (s, r, so, ro) in rows:
+        L, Lq = w.lens[s], w.q_lens[s]
+        nb = qblock_nb(L, Lq, r)
+        for gi in range(w.num_kv_heads):
+            gs = g["scores"][s, r, gi, :nb].astype(np.float64)
+            os_ = o["scores"][so, ro, gi, :nb]
+            fin = np.isfinite(os_)
+            assert np.array_equal(fin, np.isfinite(gs)), (tag, s, r, gi)
+            if fin.any():
+                floor = 1e-6 * np.abs(os_[fin]).max()
+                rel = np.abs(gs[fin] - os_[fin]) / (np.abs(os_[fin]) + floor)
+                assert rel.max() <= TIE_BAND, (tag, s, r, gi, rel.max())
+            n = int(o["cnt"][so, ro, gi])
+            assert int(g["cnt"][s, r, gi]) == n, (tag, s, r, gi)
+            a = g["sel"][s, r, gi, :n].tolist()
+            b = o["sel"][so, ro, gi, :n].tolist()
+            if a != b:
+                ncand = max(nb - wb, 0)
+                sc = os_[:ncand]
+                k = min(w.topk, ncand)
+                order = sorted(range(ncand), key=lambda x: (-sc[x], x))
+                kth = sc[order[k - 1]]
+                nxt = sc[order[k]] if k < ncand else -np.inf
+                assert abs(kth - nxt) / max(abs(kth), abs(nxt)) < TIE_BAND, (tag, s, r, gi)
+                for x in set(a) ^ set(b):
+                    assert abs(sc[x] - kth) <= TIE_BAND * abs(kth), (tag, s, r, gi, x)
+                exempt += 1
+    return exempt
+
+
+def compare_out(gout, glse, oout, olse, tag):
+    err = np.abs(gout.astype(np.float64) - oout)
+    assert np.isfinite(gout).all(), tag
+    assert err.max() <= OUT_MAX_ABS and err.mean() <= OUT_MEAN_ABS, (tag, err.max(), err.mean())
+    lerr = np.abs(glse.astype(np.float64) - olse)
+    fin = np.isfinite(olse)
+    assert np.array_equal(fin, np.isfinite(glse)), tag
+    assert (lerr[fin].max() if fin.any() else 0) <= 1e-3 * max(1.0, np.abs(olse[fin]).max()), tag
+
+
+def _full(c, tag):
+    w = c.w
+    build_kc(c, w.lens)
+    g, args = gpu_prefill(c)
+    o = ora.forward(c.op, synth.bits(c.inp["q"]), c.inp["cu_q"].numpy(), synth.bits(c.inp["k"]),
+                    synth.bits(c.inp["v"]), synth.cu_from_lens(w.lens).numpy())
+    rows = [(s, r, s, r) for s in range(w.batch) for r in range(math.ceil(w.q_lens[s] / 64))]
+    ex = check_rows(g, o, rows, w, tag)
+    out, lse = attend_with(c, o["sel"], o["cnt"], args)
+    compare_out(out, lse, o["out"], o["lse"], tag + " attend(oracle sets)")
+    if ex == 0:
+        compare_out(g["out"], g["lse"], o["out"], o["lse"], tag + " chain")
+    log(f"{tag}: ok (tie exemptions {ex})")
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (32, 8), (16, 1), (12, 3), (8, 8)])
+def test_prefill_head_groups(hq, hkv):
+    log(f"case: prefill heads {hq}/{hkv}")
+    c = make_case(_wl([3000], [200], hq=hq, hkv=hkv, seed=hq + hkv))
+    _full(c, f"pf{hq}/{hkv}")
+
+
+@pytest.mark.parametrize("lens,q_lens", [
+    ([700], [150]), ([1280], [128]), ([1281], [1]), ([2000, 1100, 64], [64, 300, 64]),
+    ([3333, 40], [333, 40]), ([5000], [5000])])
+def test_prefill_lengths(lens, q_lens):
+    log(f"case: prefill lens {lens} q {q_lens}")
+    c = make_case(_wl(lens, q_lens, seed=sum(lens) + sum(q_lens)))
+    _full(c, f"pf{lens}/{q_lens}")
+
+
+@pytest.mark.parametrize("topk", [0, 3, 1000])
+def test_prefill_topk(topk):
+    log(f"case: prefill topk {topk}")
+    c = make_case(_wl([4000], [260], topk=topk, seed=topk + 7))
+    _full(c, f"pf topk {topk}")
+
+
+def test_prefill_131072_sampled_query_blocks():
+    log("case: prefill-2048-of-131072, sampled query blocks")
+    w = synth.config(5)
+    c = make_case(w, gen_device="cuda")
+    build_kc(c, w.lens)
+    g, _ = gpu_prefill(c)
+    L, Lq = w.lens[0], w.q_lens[0]
+    assert np.isfinite(g["out"]).all()
+    ex = 0
+    for r in (0, 13, 31):
+        p_last = L - Lq + 64 * r + 63
+        k = c.inp["k"][:p_last + 1]
+        v = c.inp["v"][:p_last + 1]
+        q = c.inp["q"][64 * r:64 * r + 64]
+        o = ora.forward(c.op, synth.bits(q), np.array([0, 64], np.int32), synth.bits(k),
+                        synth.bits(v), np.array([0, p_last + 1], np.int32))
+        e = check_rows(g, o, [(0, r, 0, 0)], w, f"c5 r{r}")
+        ex += e
+        if e == 0:
+            compare_out(g["out"][64 * r:64 * r + 64], g["lse"][64 * r:64 * r + 64], o["out"],
+                        o["lse"], f"c5 r{r}")
+        log(f"c5 q-block {r}: ok (exemptions {e})")

@@ -52,19 +52,18 @@ nosa_status check_sizes(int batch, int max_seqlen_q, int max_seqlen_k)
     return NOSA_OK;
 }
 
-int pick_score_tiles(long long tiles)
+// Tiles of 16 pooled keys each wave of a pair's scoring workgroup keeps in
+// flight per batch: enough that one batch covers the pair when it is short,
+// at most 8 (128 keys, 32 loads of 16 bytes per lane).
+int pick_score_tiles(int nc)
 {
-    // aim at ~2048 waves in flight; at most 8 tiles (128 keys) per wave
-    long long t = tiles / 2048;
-    if (t >= 8) return 8;
-    if (t >= 4) return 4;
-    if (t >= 2) return 2;
-    return 1;
+    const int per_wave = ceil_div(ceil_div(nc, 16), 8);
+    if (per_wave <= 1) return 1;
+    if (per_wave <= 2) return 2;
+    if (per_wave <= 4) return 4;
+    return 8;
 }
 
-// Blocks per wave (rounds) and workgroups per pair for `span` list entries
-// per pair: about 512 workgroups of 4 waves in total (two per CU), at most
-// `max_groups` partials per head.
 // Blocks per wave (rounds, one of the compiled 1, 2, 3, 4, 6, 8) and
 // workgroups per pair for `span` list entries per pair: about 512 workgroups
 // of 4 waves in total -- two per CU, one dispatch round -- and at most
@@ -115,16 +114,15 @@ nosa_status make_plan(const nosa_params* p, int batch, int max_seqlen_k, Plan* p
     P.scale_log2 = (float)(scale * 1.4426950408889634);
 
     const int nc1 = P.max_nc > 0 ? P.max_nc : 1;
-    P.score_tiles = pick_score_tiles((long long)batch * P.Hkv * ceil_div(nc1, 16));
-    P.score_groups = ceil_div(nc1, 64 * P.score_tiles);
-    P.nchunk = P.score_groups * 4;
-    P.zstride = P.nchunk * 16 * P.score_tiles;
-    // the pooling step reads keys 4b-1 .. 4b+3 of every block b < max_nb
-    const int zneed = 4 * P.max_nb + 4;
-    if (P.zstride < zneed) P.zstride = ceil_div(zneed, 64) * 64;
+    P.score_tiles = pick_score_tiles(nc1);
+    // logits of every key, rounded up to whole tiles; the pooling step reads
+    // keys up to 4b+3 of every block b < max_nb
+    const int zneed = ceil_div(nc1, 16) * 16 > 4 * P.max_nb + 4 ? ceil_div(nc1, 16) * 16
+                                                                 : 4 * P.max_nb + 4;
+    P.zstride = ceil_div(zneed, 64) * 64;
 
     const int wn = P.wblocks < P.max_nb ? P.wblocks : P.max_nb;
-    P.win_groups = ceil_div(wn, 4);
+    P.win_groups = ceil_div(wn, kStep1Waves);
     const int ncand = P.max_nb > P.wblocks ? P.max_nb - P.wblocks : 0;
     P.top_span = P.topk < ncand ? P.topk : ncand;
     pick_split(P.top_span, (long long)batch * P.Hkv, kMaxSplit - P.win_groups, &P.top_groups,
@@ -136,10 +134,8 @@ nosa_status make_plan(const nosa_params* p, int batch, int max_seqlen_k, Plan* p
 
     const size_t B = (size_t)batch, pairs = B * P.Hkv;
     size_t off = 0;
-    P.off_counter1 = off; off += align256(pairs * sizeof(uint32_t));
     P.off_counter2 = off; off += align256(pairs * sizeof(uint32_t));
     P.off_z = off;        off += align256(B * P.Hq * (size_t)P.zstride * sizeof(float));
-    P.off_zpart = off;    off += align256(B * P.Hq * (size_t)P.nchunk * sizeof(float2));
     P.off_selpg = off;    off += align256(pairs * (size_t)(P.top_span > 0 ? P.top_span : 1) * sizeof(int2));
     P.off_sel = off;      off += align256(pairs * (size_t)P.max_sel * sizeof(int32_t));
     P.off_cnt = off;      off += align256(pairs * sizeof(int32_t));
@@ -173,10 +169,8 @@ Workspace carve(const Plan& pl, void* ws)
 {
     char* base = static_cast<char*>(ws);
     Workspace w;
-    w.counter1 = reinterpret_cast<uint32_t*>(base + pl.off_counter1);
     w.counter2 = reinterpret_cast<uint32_t*>(base + pl.off_counter2);
     w.z = reinterpret_cast<float*>(base + pl.off_z);
-    w.zpart = reinterpret_cast<float2*>(base + pl.off_zpart);
     w.selpg = reinterpret_cast<int2*>(base + pl.off_selpg);
     w.sel = reinterpret_cast<int32_t*>(base + pl.off_sel);
     w.cnt = reinterpret_cast<int32_t*>(base + pl.off_cnt);

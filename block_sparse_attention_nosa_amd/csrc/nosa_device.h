@@ -224,53 +224,76 @@ __device__ __forceinline__ int lanes_below(uint64_t mask)
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+constexpr int kSelMaxRounds = kMaxBlocks / 256;  // candidate rounds of a 4-wave selector
+
 struct SelectLds {
     float lse[kMaxGroup];
-    int cnt[2][4][16];  // per exchange parity, wave, value
+    int hist[4][256];                 // digit counts per level (zero before the selector runs)
+    int cnt[2][kSelMaxRounds][8];     // per (round, wave): tied candidates, taken candidates
 };
+
+// Zeroes the digit counts; all NT threads, and a barrier before the selector.
+template <int NT>
+__device__ __forceinline__ void select_lds_clear(SelectLds& sh)
+{
+    int* h = &sh.hist[0][0];
+    for (int i = threadIdx.x; i < 4 * 256; i += NT) h[i] = 0;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
+// 1, 2, 4, 8 within each row of 16 lanes, then the last lane of row 0 is
+// added to rows 1 and 3 and the last lane of row 1 to rows 2 and 3.  A lane
+// that a move does not write receives 0.
+__device__ __forceinline__ int wave_incl_scan(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xe, true);   // row_shr:4, lanes 4..15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xc, true);   // row_shr:8, lanes 8..15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+    return x;
+}
 
 // Top-min(topk, ncand) of the candidates [0, ncand) by (importance desc, block
 // asc) with the window [ncand, nb) always kept.  Writes, when non-null:
 //   sel_out[0 .. max_sel): every kept block ascending, -1 padded; *cnt_out;
 //   selpg[0 .. top_span): (block, page) of the top-k picks ascending,
 //                         (-1, -1) padded; *ntop_out.
-// Must be called by all 256 threads; sI holds the importance in LDS.  Only
-// ballots, lane counts and one LDS exchange per step: no atomics, no shuffles.
-__device__ void select_blocks_wg(const float* sI, int nb, int wblocks, int topk, SelectLds& sh,
-                                 int32_t* __restrict__ sel_out, int32_t* __restrict__ cnt_out,
-                                 int max_sel, int2* __restrict__ selpg,
-                                 int32_t* __restrict__ ntop_out, int top_span,
-                                 const int32_t* __restrict__ trow)
+// Must be called by all NW*64 threads, sh.hist zeroed and a barrier passed
+// since; sI holds the importance in LDS; page ids come from `pages` (LDS copy
+// of the block-table row) when given, else from `trow`.
+//
+// The k-th largest order key is found a byte at a time from the top: one
+// LDS histogram of the next byte over the candidates that still share the
+// prefix, one barrier, then every wave scans the 256 counts itself.  The
+// search stops as soon as the candidates sharing the prefix are exactly the
+// ones still needed, so for distinct keys it usually ends after two bytes.
+// The taken candidates are then compacted in ascending order from per-wave
+// ballot counts (one barrier, two when tied keys straddle the cut).
+template <int NW>
+__device__ __forceinline__ void select_blocks_wg(const float* sI, int nb, int wblocks, int topk, SelectLds& sh,
+                                                 int32_t* __restrict__ sel_out, int32_t* __restrict__ cnt_out,
+                                                 int max_sel, int2* __restrict__ selpg,
+                                                 int32_t* __restrict__ ntop_out, int top_span,
+                                                 const int32_t* __restrict__ trow, const int32_t* pages = nullptr)
 {
+    static_assert(NW >= 4 && NW <= 8, "per-round counts are sized for 4 to 8 waves");
+    constexpr int NT = NW * 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ncand = nb > wblocks ? nb - wblocks : 0;
     const int kk = topk < ncand ? topk : ncand;
     const bool partial = kk > 0 && kk < ncand;
-    uint32_t T = 0;
-    int need = 0;
-    int step = 0;
-    // Per-wave counts -> LDS -> workgroup sums.  Lane v of every wave adds up
-    // value v of the four waves, so each lane ends with one sum (no loop over
-    // all values per lane); `par` alternates so one barrier per exchange does.
-    auto publish = [&](const int* c, int nv) -> int {
-        const int par = step & 1;
-        int mine = 0;
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-            if (v < nv && v == lane) mine = c[v];
-        if (lane < nv) sh.cnt[par][wave][lane] = mine;
-        __syncthreads();
-        ++step;
-        return par;
-    };
-    // candidate keys of this thread (candidate round*256 + tid), first 8 rounds
+    const int rounds = (ncand + NT - 1) / NT;  // <= kMaxBlocks / 256 = kSelMaxRounds
+    // candidate keys of this thread (candidate round*NT + tid), first KR rounds
     constexpr int KR = 8;
     uint32_t keys[KR];
-    const int rounds = (ncand + 255) / 256;
+    // all KR reads issued together; indexes clamped into [0, ncand) (sI has
+    // at least one entry), lanes past ncand are masked wherever keys are used
 #pragma unroll
     for (int i = 0; i < KR; ++i) {
-        const int b = i * 256 + tid;
-        keys[i] = (i < rounds && b < ncand) ? order_key(sI[b]) : 0u;
+        const int b = i * NT + tid;
+        keys[i] = order_key(sI[b < ncand ? b : (ncand > 0 ? ncand - 1 : 0)]);
     }
     auto key_at = [&](int i) -> uint32_t {
         if (i < KR) {
@@ -280,87 +303,130 @@ __device__ void select_blocks_wg(const float* sI, int nb, int wblocks, int topk,
                 if (j == i) k = keys[j];
             return k;
         }
-        const int b = i * 256 + tid;
+        const int b = i * NT + tid;
         return b < ncand ? order_key(sI[b]) : 0u;
     };
+    // Candidates whose key >> shift is above P are taken; of those equal to
+    // P, the `need` lowest blocks; there are n_eq of them.
+    int shift = 32, need = kk, n_eq = kk;
+    uint32_t P = 0;
     if (partial) {
-        // The kk-th largest key T is the largest value with #{key >= T} >= kk.
-        // Build it four bits at a time from the top: count the keys at or
-        // above each of the 15 extensions of T (ballots + lane counts, one LDS
-        // exchange), keep the largest extension that still has >= kk keys.
-        for (int bit = 28; bit >= 0; bit -= 4) {
-            int c[15];
-#pragma unroll
-            for (int d = 0; d < 15; ++d) c[d] = 0;
+        int above = 0;
+#pragma unroll 1
+        for (int level = 0; level < 4; ++level) {
+            const int sh_lo = 24 - 8 * level;
             for (int i = 0; i < rounds; ++i) {
+                const int b = i * NT + tid;
                 const uint32_t key = key_at(i);
-#pragma unroll
-                for (int d = 0; d < 15; ++d)
-                    c[d] += __popcll(__ballot(key >= (T | ((uint32_t)(d + 1) << bit))));
+                const bool match = b < ncand && (level == 0 || (key >> (sh_lo + 8)) == P);
+                if (match) atomicAdd(&sh.hist[level][(key >> sh_lo) & 255], 1);
             }
-            const int par = publish(c, 15);
-            const int sum = lane < 15 ? sh.cnt[par][0][lane] + sh.cnt[par][1][lane] +
-                                            sh.cnt[par][2][lane] + sh.cnt[par][3][lane]
-                                      : 0;
-            // counts fall with the digit, so the digits that keep >= kk keys
-            // are 1 .. dsel and dsel is their number
-            const int dsel = (int)__popcll(__ballot(lane < 15 && sum >= kk));
-            T |= (uint32_t)dsel << bit;
+            __syncthreads();
+            // lane l holds digits 255-4l .. 252-4l, so the lane prefix sum
+            // counts from the top digit down
+            int v[4], loc = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[j] = sh.hist[level][255 - 4 * lane - j];
+                loc += v[j];
+            }
+            const int incl = wave_incl_scan(loc);
+            // first lane whose digits reach kk candidates at or above them
+            const uint64_t reach = __ballot(above + incl >= kk);
+            const int l0 = (int)__builtin_ctzll(reach);  // exists: all candidates sharing P count
+            // in lane l0, the first of its digits (from the top) that reaches kk
+            int acc = above + incl - loc, dj = 3, before = 0, at = 0;
+            bool found = false;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (!found && acc + v[j] >= kk) {
+                    found = true;
+                    dj = j;
+                    before = acc;
+                    at = v[j];
+                }
+                acc += v[j];
+            }
+            const int digit = __builtin_amdgcn_readlane(255 - 4 * lane - dj, l0);
+            above = __builtin_amdgcn_readlane(before, l0);
+            n_eq = __builtin_amdgcn_readlane(at, l0);
+            P = (P << 8) | (uint32_t)digit;
+            shift = sh_lo;
+            need = kk - above;
+            if (n_eq == need) break;  // every candidate sharing the prefix is taken
         }
-        int ca[1] = {0};
-        for (int i = 0; i < rounds; ++i) ca[0] += __popcll(__ballot(key_at(i) > T));
-        const int par = publish(ca, 1);
-        const int na = sh.cnt[par][0][0] + sh.cnt[par][1][0] + sh.cnt[par][2][0] + sh.cnt[par][3][0];
-        need = kk - na;  // ties at T to take, lowest block ids first
     }
-    // Ascending compaction in rounds of 256 consecutive candidates (thread tid
-    // holds candidate round*256 + tid): ranks from ballots within the wave and
-    // per-wave totals across waves.
-    int eq_base = 0, sel_base = 0;
-    for (int i = 0; i < rounds; ++i) {
-        const int b = i * 256 + tid;
-        const bool valid = b < ncand;
-        bool take;
-        if (!partial) {
-            take = valid && kk > 0;
-        } else {
+    // Ascending compaction: candidate i*NT + tid in round i; per (round,
+    // wave) counts through LDS, one barrier per pass.
+    const bool ranked = partial && n_eq > need;
+    if (ranked) {
+        for (int i = 0; i < rounds; ++i) {
+            const int b = i * NT + tid;
             const uint32_t key = key_at(i);
-            const bool eq = valid && key == T;
-            const uint64_t meq = __ballot(eq);
-            int ce[1] = {(int)__popcll(meq)};
-            const int par = publish(ce, 1);
-            int eq_before = eq_base + lanes_below(meq);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const int cw = sh.cnt[par][w][0];
-                if (w < wave) eq_before += cw;
-                eq_base += cw;
-            }
-            take = valid && (key > T || (eq && eq_before < need));
+            const bool eq = b < ncand && (key >> shift) == P;
+            const uint64_t m = __ballot(eq);
+            if (lane == 0) sh.cnt[0][i][wave] = (int)__popcll(m);
         }
+        __syncthreads();
+    }
+    uint32_t takebits = 0;
+    {
+        int eq_base = 0;
+        for (int i = 0; i < rounds; ++i) {
+            const int b = i * NT + tid;
+            const bool valid = b < ncand;
+            bool take;
+            if (!partial) {
+                take = valid && kk > 0;
+            } else {
+                const uint32_t key = key_at(i);
+                const uint32_t kp = shift < 32 ? key >> shift : 0u;
+                const bool gt = kp > P, eq = kp == P;
+                if (ranked) {
+                    const uint64_t m = __ballot(valid && eq);
+                    int r = eq_base + lanes_below(m);
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) {
+                        const int c = sh.cnt[0][i][w];
+                        if (w < wave) r += c;
+                        eq_base += c;
+                    }
+                    take = valid && (gt || (eq && r < need));
+                } else {
+                    take = valid && (gt || eq);
+                }
+            }
+            const uint64_t mt = __ballot(take);
+            if (lane == 0) sh.cnt[1][i][wave] = (int)__popcll(mt);
+            if (take) takebits |= 1u << i;
+        }
+    }
+    __syncthreads();
+    int sel_base = 0;
+    for (int i = 0; i < rounds; ++i) {
+        const bool take = (takebits >> i) & 1u;
         const uint64_t mt = __ballot(take);
-        int ct[1] = {(int)__popcll(mt)};
-        const int par = publish(ct, 1);
         int pos = sel_base + lanes_below(mt);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int cw = sh.cnt[par][w][0];
-            if (w < wave) pos += cw;
-            sel_base += cw;
+        for (int w = 0; w < NW; ++w) {
+            const int c = sh.cnt[1][i][w];
+            if (w < wave) pos += c;
+            sel_base += c;
         }
         if (take) {
+            const int b = i * NT + tid;
             if (sel_out) sel_out[pos] = b;
-            if (selpg && pos < top_span) selpg[pos] = make_int2(b, trow[b]);
+            if (selpg && pos < top_span) selpg[pos] = make_int2(b, pages ? pages[b] : trow[b]);
         }
     }
     const int nsel = sel_base;
     const int total = nsel + (nb - ncand);
     if (sel_out) {
-        for (int b = ncand + tid; b < nb; b += 256) sel_out[nsel + (b - ncand)] = b;
-        for (int x = total + tid; x < max_sel; x += 256) sel_out[x] = -1;
+        for (int b = ncand + tid; b < nb; b += NT) sel_out[nsel + (b - ncand)] = b;
+        for (int x = total + tid; x < max_sel; x += NT) sel_out[x] = -1;
     }
     if (selpg)
-        for (int x = nsel + tid; x < top_span; x += 256) selpg[x] = make_int2(-1, -1);
+        for (int x = nsel + tid; x < top_span; x += NT) selpg[x] = make_int2(-1, -1);
     if (tid == 0) {
         if (cnt_out) *cnt_out = total;
         if (ntop_out) *ntop_out = nsel;

@@ -21,6 +21,7 @@ constexpr int kMaxGroup = 16;            // query heads per KV head (MFMA N = 16
 constexpr int kMaxBlocks = 8192;         // blocks per sequence (LDS of the selector)
 constexpr int kMaxSplit = 64;            // attention partials per head (LDS of the merge)
 constexpr int kMaxWindowBlocks = 128;    // window blocks (one page per wave of step 1)
+constexpr int kStep1Waves = 8;           // waves of a step-1 workgroup
 
 inline int num_keys(int L) { return L >= kPoolK ? (L - kPoolK) / kPoolS + 1 : 0; }
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -32,10 +33,11 @@ struct Plan {
     int max_seqlen_k = 0, max_nc = 0, max_nb = 0;
     int Lmax = 0;  // device lengths are clamped to this (<= max_seqlen_k, table reach)
     float scale_log2 = 0.f;  // logit scale * log2(e)
-    // scoring: T tiles of 16 keys per wave, 4 waves per workgroup
-    int score_tiles = 1, score_groups = 0, nchunk = 0, zstride = 0;
-    // attention: one 64-token block per wave, 4 waves per workgroup
-    int win_groups = 0;     // window workgroups per pair (step 1), one page per wave
+    // scoring: one workgroup of 8 waves per pair, T tiles of 16 keys per
+    // wave in flight
+    int score_tiles = 1, zstride = 0;
+    // attention: one 64-token block per wave
+    int win_groups = 0;     // window workgroups of 8 waves per pair (step 1)
     int top_span = 0;       // top-k entries per pair = min(topk, max_nb - window blocks)
     int top_groups = 0;     // top-k workgroups per pair (step 2), >= 1
     int top_rounds = 1;     // top-k blocks per wave
@@ -43,16 +45,14 @@ struct Plan {
     int attend_groups = 0;  // workgroups per pair of the stand-alone attention
     int attend_rounds = 1;  // blocks per wave of the stand-alone attention
     // workspace layout (bytes from the start of the workspace)
-    size_t off_counter1 = 0, off_counter2 = 0, off_z = 0, off_zpart = 0, off_selpg = 0,
+    size_t off_counter2 = 0, off_z = 0, off_selpg = 0,
            off_sel = 0, off_cnt = 0, off_po = 0, off_pml = 0, bytes = 0;
 };
 
 // Device pointers carved out of the caller's workspace.
 struct Workspace {
-    uint32_t* counter1;  // [pairs] hand-off counters of step 1 (zero between calls)
     uint32_t* counter2;  // [pairs] hand-off counters of step 2 (zero between calls)
     float* z;            // [B][Hq][zstride] logits, log2 units
-    float2* zpart;       // [B][Hq][nchunk] per-wave (max, sum exp2)
     int2* selpg;         // [pairs][top_span] (block, page) of the top-k picks
     int32_t* sel;        // [pairs][max_sel] kept blocks (when the caller passes none)
     int32_t* cnt;        // [pairs]

@@ -137,14 +137,16 @@ __device__ void store_wg_partial(CombineLds& sh, const AttnState& A, int G, size
     float l = A.l;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    if (kq == 0) {
-        sh.m[wave][r] = A.m;
-        sh.l[wave][r] = l;
+    if (wave < 4) {  // a 512-thread caller has folded waves 4..7 in already
+        if (kq == 0) {
+            sh.m[wave][r] = A.m;
+            sh.l[wave][r] = l;
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sh.o[wave][4 * kq + i][nt * 16 + r] = A.o[nt][i];
     }
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sh.o[wave][4 * kq + i][nt * 16 + r] = A.o[nt][i];
     __syncthreads();
     const int h = tid >> 4, c0 = (tid & 15) * 8;
     if (h < G) {
@@ -172,83 +174,93 @@ __device__ void store_wg_partial(CombineLds& sh, const AttnState& A, int G, size
     }
 }
 
-// Importance of every block of the pair, from z and the per-wave partials,
-// into sI[0 .. nb): mean over the keys overlapping block b (keys 4b-1 .. 4b+3
-// that exist) of sigma[j] = sum_h exp2(z_h[j] - lse_h).  Each thread takes
-// four consecutive keys (one float4 of z per head, all loads issued before
-// use) and adds every key's sigma to the block(s) it overlaps with LDS
-// atomics.  Also writes scores_out.  Reads data of other workgroups: call
-// after last_of_pair().
-__device__ void pool_importance(const float* __restrict__ z, int zstride,
-                                const float2* __restrict__ zpart, int nchunk, size_t head_row0,
-                                int G, int nc, int nb, float* sI, SelectLds& sh,
-                                float* __restrict__ scores_out, int max_nb)
+// Eight-wave version of store_wg_partial: waves 4..7 first fold their state
+// into waves 0..3 through LDS, then the four-wave combine runs.  Must be
+// called by all 512 threads.
+__device__ void store_wg_partial8(CombineLds& sh, AttnState& A, int G, size_t head_row0,
+                                  int nsplit, int split, float* __restrict__ po,
+                                  float2* __restrict__ pml)
 {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float* zg = z + head_row0 * zstride;
-    // the logits of this thread's first four keys (first eight heads) do not
-    // depend on the normalisers: issue them before reducing the partials
-    float4 zfirst[8];
-    const bool has_first = 4 * tid < nc;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-        if (u < G && has_first) zfirst[u] = *reinterpret_cast<const float4*>(zg + (size_t)u * zstride + 4 * tid);
-    for (int b = tid; b < nb; b += 256) sI[b] = 0.f;
-    for (int h = wave; h < G; h += 4) {
-        // per-wave (max, sum exp2) partials of head h: one pass over them
-        const float2* zp = zpart + (head_row0 + h) * nchunk;
-        float m = -INFINITY, acc = 0.f;
-#pragma unroll 1
-        for (int c0 = 0; c0 < nchunk; c0 += 256) {
-            float2 v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = c0 + u * 64 + lane;
-                v[u] = c < nchunk ? zp[c] : make_float2(-INFINITY, 0.f);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (!(v[u].y > 0.f)) continue;
-                const float mn = fmaxf(m, v[u].x);
-                acc = acc * exp2f(m - mn) + v[u].y * exp2f(v[u].x - mn);
-                m = mn;
-            }
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    __shared__ float m_lo[4][16];
+    float l = A.l;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (wave >= 4) {
+        if (kq == 0) {
+            sh.m[wave - 4][r] = A.m;
+            sh.l[wave - 4][r] = l;
         }
-        // combine the lanes' (m, acc)
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float mo = __shfl_xor(m, off), ao = __shfl_xor(acc, off);
-            const float mn = fmaxf(m, mo);
-            acc = (mn == -INFINITY) ? 0.f : acc * exp2f(m - mn) + ao * exp2f(mo - mn);
-            m = mn;
-        }
-        if (lane == 0) sh.lse[h] = m + log2f(acc);
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sh.o[wave - 4][4 * kq + i][nt * 16 + r] = A.o[nt][i];
+    } else if (kq == 0) {
+        m_lo[wave][r] = A.m;
     }
     __syncthreads();
+    if (wave < 4) {
+        // rows of this lane's accumulators: heads 4kq + i; of its (m, l): head r
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * kq + i;
+            const float ma = m_lo[wave][h], mb = sh.m[wave][h];
+            const float M = fmaxf(ma, mb);
+            const float wa = (M == -INFINITY || ma == -INFINITY) ? 0.f : exp2f(ma - M);
+            const float wb = (M == -INFINITY || mb == -INFINITY) ? 0.f : exp2f(mb - M);
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+                A.o[nt][i] = A.o[nt][i] * wa + sh.o[wave][h][nt * 16 + r] * wb;
+        }
+        const float ma = A.m, mb = sh.m[wave][r];
+        const float M = fmaxf(ma, mb);
+        const float wa = (M == -INFINITY || ma == -INFINITY) ? 0.f : exp2f(ma - M);
+        const float wb = (M == -INFINITY || mb == -INFINITY) ? 0.f : exp2f(mb - M);
+        A.l = l * wa + sh.l[wave][r] * wb;  // already summed over the lane groups
+        A.m = M;
+    }
+    __syncthreads();
+    // four-wave combine (the l above is complete: keep the lane-group sum from
+    // adding it four times)
+    if (wave < 4 && kq != 0) A.l = 0.f;
+    store_wg_partial(sh, A, G, head_row0, nsplit, split, po, pml);
+}
+
+// Block importance of the pair into sI[0 .. nb): mean over the keys
+// overlapping block b (keys 4b-1 .. 4b+3 that exist) of
+// sigma[j] = sum_h exp2(z_h[j] - lse_h).  Each thread takes four consecutive
+// keys (one float4 of z per head, eight heads per batch of loads) and adds
+// their sum to block j/4 and the last key's sigma to block j/4 + 1: two
+// additions per block, so the result does not depend on their order.
+// z was written by this workgroup (call after a barrier).  Also writes
+// scores_out.  Must be called by all NT threads.
+template <int NT>
+__device__ void pool_pair(const float* __restrict__ zg, int zstride, const float* lse, int G,
+                          int nc, int nb, float* sI, float* __restrict__ scores_out, int max_nb)
+{
+    const int tid = threadIdx.x;
+    for (int b = tid; b < nb; b += NT) sI[b] = 0.f;
+    __syncthreads();
 #pragma unroll 1
-    for (int j0 = 4 * tid; j0 < nc; j0 += 4 * 256) {
+    for (int j0 = 4 * tid; j0 < nc; j0 += 4 * NT) {
         float sg[4] = {0.f, 0.f, 0.f, 0.f};
-        // heads in batches of 8: every load of a batch in flight at once
 #pragma unroll 1
         for (int h0 = 0; h0 < G; h0 += 8) {
             float4 zz[8];
-            const bool first = j0 == 4 * tid && h0 == 0;
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (h0 + u < G)
-                    zz[u] = first ? zfirst[u]
-                                  : *reinterpret_cast<const float4*>(zg + (size_t)(h0 + u) * zstride + j0);
+                if (h0 + u < G) zz[u] = *reinterpret_cast<const float4*>(zg + (size_t)(h0 + u) * zstride + j0);
 #pragma unroll
             for (int u = 0; u < 8; ++u)
                 if (h0 + u < G) {
-                    const float lh = sh.lse[h0 + u];
+                    const float lh = lse[h0 + u];
                     sg[0] += exp2f(zz[u].x - lh);
                     sg[1] += exp2f(zz[u].y - lh);
                     sg[2] += exp2f(zz[u].z - lh);
                     sg[3] += exp2f(zz[u].w - lh);
                 }
         }
-        // keys j0 .. j0+3 all overlap block j0/4; key j0+3 also overlaps the next
         const int b = j0 >> 2;
         float own = 0.f;
 #pragma unroll
@@ -258,18 +270,21 @@ __device__ void pool_importance(const float* __restrict__ z, int zstride,
         if (j0 + 3 < nc && b + 1 < nb) atomicAdd(&sI[b + 1], sg[3]);
     }
     __syncthreads();
-    for (int b = tid; b < nb; b += 256) {
+    for (int b = tid; b < nb; b += NT) {
         const int jlo = max(4 * b - 1, 0), jhi = min(4 * b + 3, nc - 1);
         const float I = jlo <= jhi ? sI[b] / (float)(jhi - jlo + 1) : -INFINITY;
         sI[b] = I;
         if (scores_out) scores_out[b] = I;
     }
     if (scores_out)
-        for (int b = nb + tid; b < max_nb; b += 256) scores_out[b] = -INFINITY;
+        for (int b = nb + tid; b < max_nb; b += NT) scores_out[b] = -INFINITY;
     __syncthreads();
 }
 
 // --------------------------------------------------------------- step 1 ---
+
+constexpr int kPairWaves = kStep1Waves;  // waves of a step-1 workgroup (512 threads)
+constexpr int kPairThreads = kPairWaves * 64;
 
 struct Step1Args {
     const uint16_t* q;
@@ -280,140 +295,217 @@ struct Step1Args {
     const int32_t* cu_k;
     int max_blocks, Lmax, B, Hq, Hkv, G;
     float scale_log2;
-    int score_groups;  // score workgroups per pair
-    int win_groups;    // window workgroups per pair (0 = none), one page per wave
-    int append;        // pool the key completed by the current token
-    float* z;
+    int win_groups;  // window workgroups per pair (0 = none), one page per wave
+    int append;      // pool the key completed by the current token
+    float* z;        // [B][Hq][zstride] logits (log2 units), private to the pair's workgroup
     int zstride;
-    float2* zpart;
-    int nchunk;
-    uint32_t* counter;  // [pairs]
     int do_select, topk, wblocks, max_nb, max_sel, top_span;
     float* scores_out;  // [pairs][max_nb] or null
     int32_t* sel_out;   // [pairs][max_sel] or null
     int32_t* cnt_out;   // [pairs] or null
     int2* selpg;        // [pairs][top_span] or null
-    int32_t* ntop;      // [pairs] or null
     float* po;
     float2* pml;
     int nsplit;  // partial slots per head
+    int lds_pages;  // the pair workgroup copies its block-table row into LDS
 };
 
-constexpr size_t step1_lds_bytes(int max_nb)
+// LDS of a step-1 workgroup (dynamic): the block importance and the page ids
+// of the pair (pair workgroups) or the wave states (window workgroups).
+inline size_t step1_lds_bytes(int max_nb, bool pages)
 {
-    return sizeof(CombineLds) > (size_t)max_nb * 4 ? sizeof(CombineLds) : (size_t)max_nb * 4;
+    const size_t pair = (size_t)max_nb * (sizeof(float) + (pages ? sizeof(int32_t) : 0));
+    return pair > sizeof(CombineLds) ? pair : sizeof(CombineLds);
 }
+constexpr size_t kStep1LdsBudget = 60 * 1024;  // dynamic LDS of a step-1 workgroup
 
-// Score workgroup (4 waves, T tiles of 16 keys each per wave) of one pair.
+struct PairLds {
+    float m[kPairWaves][kMaxGroup], s[kPairWaves][kMaxGroup];
+    SelectLds sel;
+};
+
+// The per-pair workgroup: scores every pooled key of one (sequence, KV head)
+// -- tiles of 16 keys strided over its eight waves, T tiles' loads in flight
+// per wave -- with per-wave (max, sum exp2) per head, keeps the logits in the
+// workspace (read back only by this workgroup), then pools block importance
+// and selects.  The wave owning the key completed by the current token
+// (tokens L-32 .. L-1) pools it from K first, stores it and substitutes it
+// into its MFMA operand.
 template <int T>
-__device__ void score_part(const Step1Args& a, int s, int g, int grp, char* smem)
+__device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
 {
-    __shared__ SelectLds sel_sh;
-    __shared__ int flag;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __shared__ PairLds sh;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
     const int L = seq_len(a.cu_k, s, a.Lmax);
     const int nc = dev_num_keys(L);
-    const int chunk = grp * 4 + wave;
-    const int key0 = chunk * 16 * T;
+    const int nb = (L + BS - 1) / BS;
     const int32_t* trow = a.table + (size_t)s * a.max_blocks;
     const size_t head_row0 = (size_t)s * a.Hq + g * a.G;
-
-    bf16x8 qb[4];
-    load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
-    uint4 kv[T][4];
+    const size_t pair = (size_t)s * a.Hkv + g;
+    float* sI = reinterpret_cast<float*>(smem);
+    int32_t* spg = reinterpret_cast<int32_t*>(smem + sizeof(float) * a.max_nb);
+    // The block-table row goes to LDS first (four loads in flight per
+    // thread), so no key load below waits on a table load: loads complete in
+    // order, so a table load issued behind other loads would wait for them.
+    if (a.lds_pages) {
+        for (int b0 = tid; b0 < nb; b0 += 4 * kPairThreads) {
+            int v[4];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int key = key0 + t * 16 + r;
-        if (key < nc) {
-            const uint16_t* kp = kc_slot(a.kc_pool, trow, a.Hkv, g, key);
+            for (int u = 0; u < 4; ++u) {
+                const int b = b0 + u * kPairThreads;
+                v[u] = b < nb ? trow[b] : 0;
+            }
 #pragma unroll
-            for (int st = 0; st < 4; ++st) kv[t][st] = ldg16(kp + st * 32 + kq * 8);
-        } else {
-#pragma unroll
-            for (int st = 0; st < 4; ++st) kv[t][st] = make_uint4(0, 0, 0, 0);
+            for (int u = 0; u < 4; ++u)
+                if (b0 + u * kPairThreads < nb) spg[b0 + u * kPairThreads] = v[u];
         }
     }
-    // The key completed by the current token (tokens L-32 .. L-1) is pooled
-    // here from K, stored, and substituted into this wave's operand.
+
+    select_lds_clear<kPairThreads>(sh.sel);
+    bf16x8 qb[4];
+    load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
+    __syncthreads();
     const int jn = nc - 1;
-    if (a.append && L >= kPoolK && (L - kPoolK) % kPoolS == 0 && jn >= key0 && jn < key0 + 16 * T) {
+    const bool appending = a.append && L >= kPoolK && (L - kPoolK) % kPoolS == 0;
+    const int ntiles = (nc + 15) / 16;
+    // The wave whose batch holds key jn pools it before its first batch.
+    const bool app_mine = appending && ((jn / 16) / T) % kPairWaves == wave;
+    uint4 appkey = make_uint4(0, 0, 0, 0);
+    if (app_mine) {
         const int tr = lane >> 4, cc = lane & 15;  // 4 token phases x 16 channel chunks
+        // tokens 16jn + tr + 4i, i < 8: their pages first, then all loads
+        int kpg[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int b = (jn * kPoolS + tr + 4 * i) / BS;
+            kpg[i] = a.lds_pages ? spg[b] : trow[b];
+        }
+        uint4 kr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = jn * kPoolS + tr + 4 * i;
+            kr[i] = ldg16(a.k_pool + (((size_t)kpg[i] * a.Hkv + g) * BS + (t % BS)) * D + cc * 8);
+        }
         double acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-        for (int i = tr; i < kPoolK; i += 4) {
-            const int t = jn * kPoolS + i;
-            acc8(acc, ldg16(a.k_pool + (((size_t)trow[t / BS] * a.Hkv + g) * BS + (t % BS)) * D + cc * 8));
-        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc8(acc, kr[i]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             acc[e] += __shfl_xor(acc[e], 16);
             acc[e] += __shfl_xor(acc[e], 32);
         }
-        const uint4 key = round8(acc);  // channels 8cc .. 8cc+7, same in every phase
-        if (tr == 0) *reinterpret_cast<uint4*>(kc_slot(a.kc_pool, trow, a.Hkv, g, jn) + cc * 8) = key;
-        const int tloc = (jn - key0) / 16, rloc = (jn - key0) % 16;
+        appkey = round8(acc);  // channels 8cc .. 8cc+7, same in every phase
+        if (tr == 0) {
+            const int pj = a.lds_pages ? spg[jn / SL] : trow[jn / SL];
+            *reinterpret_cast<uint4*>(a.kc_pool + (((size_t)pj * a.Hkv + g) * SL + jn % SL) * D + cc * 8) = appkey;
+        }
+    }
+    float m_run = -INFINITY, s_run = 0.f;  // head r, over this lane's keys
+    for (int t0 = wave * T; t0 < ntiles; t0 += kPairWaves * T) {
+        const int key0 = t0 * 16;
+        // page ids of this lane's keys for the whole batch before any key load
+        int pg[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t)
+        for (int t = 0; t < T; ++t) {
+            const int key = key0 + t * 16 + r;
+            const int b = (key < nc ? key : 0) / SL;
+            pg[t] = a.lds_pages ? spg[b] : trow[b];
+        }
+        uint4 kv[T][4];
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                uint4 v;
-                v.x = __shfl(key.x, st * 4 + kq);
-                v.y = __shfl(key.y, st * 4 + kq);
-                v.z = __shfl(key.z, st * 4 + kq);
-                v.w = __shfl(key.w, st * 4 + kq);
-                if (t == tloc && r == rloc) kv[t][st] = v;
+        for (int t = 0; t < T; ++t) {
+            const int key = key0 + t * 16 + r;
+            if (key < nc) {
+                const uint16_t* kp = a.kc_pool + (((size_t)pg[t] * a.Hkv + g) * SL + key % SL) * D;
+#pragma unroll
+                for (int st = 0; st < 4; ++st) kv[t][st] = ldg16(kp + st * 32 + kq * 8);
+            } else {
+#pragma unroll
+                for (int st = 0; st < 4; ++st) kv[t][st] = make_uint4(0, 0, 0, 0);
             }
-    }
-    float mx = -INFINITY;
-    float zv[T][4];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(kv[t][st]), qb[st], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = key0 + t * 16 + kq * 4 + i;
-            zv[t][i] = key < nc ? acc[i] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, zv[t][i]);
         }
-        if (r < a.G) {
-            float* zd = a.z + (head_row0 + r) * a.zstride + key0 + t * 16 + kq * 4;
-            st_pair(zd, zv[t][0], zv[t][1]);
-            st_pair(zd + 2, zv[t][2], zv[t][3]);
+        if (app_mine && jn >= key0 && jn < key0 + 16 * T) {
+            const int tloc = (jn - key0) / 16, rloc = (jn - key0) % 16;
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    uint4 v;
+                    v.x = __shfl(appkey.x, st * 4 + kq);
+                    v.y = __shfl(appkey.y, st * 4 + kq);
+                    v.z = __shfl(appkey.z, st * 4 + kq);
+                    v.w = __shfl(appkey.w, st * 4 + kq);
+                    if (t == tloc && r == rloc) kv[t][st] = v;
+                }
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            if (key0 + t * 16 >= nc) break;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(kv[t][st]), qb[st], acc);
+            float zv[4];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = key0 + t * 16 + kq * 4 + i;
+                zv[i] = key < nc ? acc[i] * a.scale_log2 : -INFINITY;
+                tmax = fmaxf(tmax, zv[i]);
+            }
+            if (r < a.G)
+                *reinterpret_cast<float4*>(a.z + (head_row0 + r) * a.zstride + key0 + t * 16 + kq * 4) =
+                    make_float4(zv[0], zv[1], zv[2], zv[3]);
+            if (tmax != -INFINITY) {
+                const float mn = fmaxf(m_run, tmax);
+                float add = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) add += exp2f(zv[i] - mn);
+                s_run = s_run * exp2f(m_run - mn) + add;
+                m_run = mn;
+            }
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    float sum = 0.f;
-    if (mx != -INFINITY) {
+    // per-wave partials of every head -> LDS -> per-head log2-sum-exp2
 #pragma unroll
-        for (int t = 0; t < T; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sum += exp2f(zv[t][i] - mx);
+    for (int off = 16; off < 64; off <<= 1) {
+        const float mo = __shfl_xor(m_run, off), so = __shfl_xor(s_run, off);
+        const float mn = fmaxf(m_run, mo);
+        s_run = mn == -INFINITY ? 0.f : s_run * exp2f(m_run - mn) + so * exp2f(mo - mn);
+        m_run = mn;
     }
-    sum += __shfl_xor(sum, 16);
-    sum += __shfl_xor(sum, 32);
-    if (kq == 0 && r < a.G) st_pair(a.zpart + (head_row0 + r) * a.nchunk + chunk, mx, sum);
-
-    const size_t pair = (size_t)s * a.Hkv + g;
-    if (!last_of_pair(a.counter + pair, (uint32_t)a.score_groups, &flag)) return;
-
-    // ---- last score workgroup of the pair: importance, then selection
-    float* sI = reinterpret_cast<float*>(smem);
-    const int nb = (L + BS - 1) / BS;
-    pool_importance(a.z, a.zstride, a.zpart, a.nchunk, head_row0, a.G, nc, nb, sI, sel_sh,
-                    a.scores_out ? a.scores_out + pair * a.max_nb : nullptr, a.max_nb);
+    if (kq == 0 && r < a.G) {
+        sh.m[wave][r] = m_run;
+        sh.s[wave][r] = s_run;
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's logits have reached L2
+    __syncthreads();
+    if (tid < a.G) {
+        float m = -INFINITY, acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kPairWaves; ++w) {
+            const float mw = sh.m[w][tid], sw = sh.s[w][tid];
+            if (!(sw > 0.f)) continue;
+            const float mn = fmaxf(m, mw);
+            acc = acc * exp2f(m - mn) + sw * exp2f(mw - mn);
+            m = mn;
+        }
+        sh.sel.lse[tid] = m + log2f(acc);
+    }
+    __syncthreads();
+    pool_pair<kPairThreads>(a.z + head_row0 * a.zstride, a.zstride, sh.sel.lse, a.G, nc, nb, sI,
+                            a.scores_out ? a.scores_out + pair * a.max_nb : nullptr, a.max_nb);
     if (!a.do_select) return;
-    select_blocks_wg(sI, nb, a.wblocks, a.topk, sel_sh, a.sel_out ? a.sel_out + pair * a.max_sel : nullptr,
-                     a.cnt_out ? a.cnt_out + pair : nullptr, a.max_sel,
-                     a.selpg ? a.selpg + pair * a.top_span : nullptr, a.ntop ? a.ntop + pair : nullptr,
-                     a.top_span, trow);
+    select_blocks_wg<kPairWaves>(sI, nb, a.wblocks, a.topk, sh.sel,
+                                 a.sel_out ? a.sel_out + pair * a.max_sel : nullptr,
+                                 a.cnt_out ? a.cnt_out + pair : nullptr, a.max_sel,
+                                 a.selpg ? a.selpg + pair * a.top_span : nullptr, nullptr,
+                                 a.top_span, trow, a.lds_pages ? spg : nullptr);
 }
 
-// Window workgroup: wave w attends window slot 4*grp + w, slot x being block
+// Window workgroup: wave w attends window slot 8*grp + w, slot x being block
 // nb - min(nb, wblocks) + x, and the workgroup stores one partial.
 __device__ void window_part(const Step1Args& a, int s, int g, int grp, char* smem)
 {
@@ -426,7 +518,7 @@ __device__ void window_part(const Step1Args& a, int s, int g, int grp, char* sme
     attn_init(A);
     bf16x8 qb[4];
     load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
-    const int slot = grp * 4 + wave;
+    const int slot = grp * kPairWaves + wave;
     if (slot < wn) {
         const int b = nb - wn + slot;
         const int page = a.table[(size_t)s * a.max_blocks + b];
@@ -434,25 +526,23 @@ __device__ void window_part(const Step1Args& a, int s, int g, int grp, char* sme
         const uint16_t* vb = a.v_pool + ((size_t)page * a.Hkv + g) * D * BS;
         attend_page(kb, vb, L - b * BS, qb, a.scale_log2, r, kq, A);
     }
-    store_wg_partial(*reinterpret_cast<CombineLds*>(smem), A, a.G, (size_t)s * a.Hq + g * a.G,
-                     a.nsplit, grp, a.po, a.pml);
+    store_wg_partial8(*reinterpret_cast<CombineLds*>(smem), A, a.G, (size_t)s * a.Hq + g * a.G,
+                      a.nsplit, grp, a.po, a.pml);
 }
 
 template <int T>
-__global__ __launch_bounds__(256) void step1_kernel(Step1Args a)
+__global__ __launch_bounds__(512) void step1_kernel(Step1Args a)
 {
     extern __shared__ __align__(16) char smem[];
-    // window workgroups first: they need no hand-off, and dispatching them
-    // early keeps them off the tail of the launch
+    // pair workgroups first: they carry the launch's critical path
     const int npairs = a.B * a.Hkv;
     int wg = blockIdx.x;
-    if (wg < npairs * a.win_groups) {
+    if (wg < npairs) {
+        pair_part<T>(a, wg / a.Hkv, wg % a.Hkv, smem);
+    } else {
+        wg -= npairs;
         const int pair = wg / a.win_groups, grp = wg % a.win_groups;
         window_part(a, pair / a.Hkv, pair % a.Hkv, grp, smem);
-    } else {
-        wg -= npairs * a.win_groups;
-        const int pair = wg / a.score_groups, grp = wg % a.score_groups;
-        score_part<T>(a, pair / a.Hkv, pair % a.Hkv, grp, smem);
     }
 }
 
@@ -624,9 +714,10 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
     }
     const size_t pair = (size_t)sr * Hkv + g;
     for (int b = threadIdx.x; b < nb; b += 256) sI[b] = scores_in[pair * max_nb + b];
+    select_lds_clear<256>(sh);
     __syncthreads();
-    select_blocks_wg(sI, nb, wblocks, topk, sh, sel + pair * max_sel, cnt + pair, max_sel, nullptr,
-                     nullptr, 0, nullptr);
+    select_blocks_wg<4>(sI, nb, wblocks, topk, sh, sel + pair * max_sel, cnt + pair, max_sel,
+                        nullptr, nullptr, 0, nullptr);
 }
 
 // ---------------------------------------------------------- launchers ---
@@ -662,12 +753,8 @@ static Step1Args step1_args(const Plan& pl, const nosa_paged_kv& kv, const nosa_
     a.Hkv = pl.Hkv;
     a.G = pl.G;
     a.scale_log2 = pl.scale_log2;
-    a.score_groups = pl.score_groups;
     a.z = w.z;
     a.zstride = pl.zstride;
-    a.zpart = w.zpart;
-    a.nchunk = pl.nchunk;
-    a.counter = w.counter1;
     a.topk = pl.topk;
     a.wblocks = pl.wblocks;
     a.max_nb = pl.max_nb;
@@ -676,16 +763,16 @@ static Step1Args step1_args(const Plan& pl, const nosa_paged_kv& kv, const nosa_
     a.po = w.po;
     a.pml = w.pml;
     a.nsplit = pl.nsplit;
+    a.lds_pages = step1_lds_bytes(pl.max_nb, true) <= kStep1LdsBudget;
     return a;
 }
 
-static hipError_t launch_step1(const Plan& pl, const Step1Args& a, int win_groups,
-                               hipStream_t stream)
+static hipError_t launch_step1(const Plan& pl, const Step1Args& a, hipStream_t stream)
 {
     const int npairs = pl.B * pl.Hkv;
-    dim3 grid(npairs * (pl.score_groups + win_groups));
-    const size_t lds = step1_lds_bytes(pl.max_nb);
-#define NOSA_STEP1(T) hipLaunchKernelGGL(step1_kernel<T>, grid, dim3(256), lds, stream, a)
+    dim3 grid(npairs * (1 + a.win_groups));
+    const size_t lds = step1_lds_bytes(pl.max_nb, a.lds_pages);
+#define NOSA_STEP1(T) hipLaunchKernelGGL(step1_kernel<T>, grid, dim3(kPairThreads), lds, stream, a)
     switch (pl.score_tiles) {
         case 1: NOSA_STEP1(1); break;
         case 2: NOSA_STEP1(2); break;
@@ -705,7 +792,7 @@ hipError_t launch_scores_only(const Plan& pl, const nosa_paged_kv& kv, const nos
     a.append = 0;
     a.do_select = 0;
     a.scores_out = scores_out;
-    return launch_step1(pl, a, 0, stream);
+    return launch_step1(pl, a, stream);
 }
 
 hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
@@ -721,8 +808,7 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
     a.sel_out = sel_out;
     a.cnt_out = cnt_out;
     a.selpg = w.selpg;
-    a.ntop = nullptr;
-    hipError_t e = launch_step1(pl, a, pl.win_groups, stream);
+    hipError_t e = launch_step1(pl, a, stream);
     if (e != hipSuccess) return e;
 
     Step2Args b{};

@@ -60,11 +60,41 @@ __device__ __forceinline__ float ld_one(const float* p)
     return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Pooled key j of KV head g of a sequence: slot j % SL of page table[j / SL].
-__device__ __forceinline__ uint16_t* kc_slot(uint16_t* kc_pool, const int32_t* trow, int Hkv, int g,
+// ------------------------------------------------------- page layouts ---
+// Every page of every pool is stored in the order the MFMA operands are
+// loaded, so that one 16-byte-per-lane load instruction of a wave reads 1 KB
+// of contiguous memory (lane l at byte 16 l) instead of sixteen 64-byte
+// pieces of sixteen rows.  Offsets below are in bf16 elements from the start
+// of the page of one KV head and address 8 consecutive elements.
+
+// K page (64 tokens x 128 channels): 16 blocks of 1 KB; block 4t + st is the
+// A operand of QK^T tile t, k-step st: lane 16 kq + m holds channels
+// 32 st + 8 kq .. +7 of token qk_row_token(t, m).  Offset of channels
+// 8 c8 .. 8 c8 + 7 of token x:
+__device__ __forceinline__ int k_chunk(int x, int c8)
+{
+    const int t = 2 * (x >> 5) + ((x >> 2) & 1), m = 4 * ((x >> 3) & 3) + (x & 3);
+    return (((t * 4 + (c8 >> 2)) * 4 + (c8 & 3)) * 16 + m) * 8;
+}
+
+// V page (64 tokens x 128 channels): 16 blocks of 1 KB; block 8u + nt is the
+// B operand of PV k-step u (tokens 32u .. 32u + 31), channel tile nt: lane
+// 16 kq + r holds tokens 32u + 8kq .. +7 of channel 16 nt + r.  Offset of
+// tokens 8 x8 .. 8 x8 + 7 of channel c:
+__device__ __forceinline__ int v_chunk(int c, int x8)
+{
+    return ((((x8 >> 2) * 8 + (c >> 4)) * 4 + (x8 & 3)) * 16 + (c & 15)) * 8;
+}
+
+// Pooled-key page (4 keys x 128 channels, 1 KB): channel chunk major,
+// [16 chunks][4 slots][8].  Offset of channels 8 c8 .. 8 c8 + 7 of slot j:
+__device__ __forceinline__ int kc_chunk(int slot, int c8) { return (c8 * SL + slot) * 8; }
+
+// Start of the pooled-key page holding key j of KV head g of a sequence.
+__device__ __forceinline__ uint16_t* kc_page(uint16_t* kc_pool, const int32_t* trow, int Hkv, int g,
                                              int j)
 {
-    return kc_pool + (((size_t)trow[j / SL] * Hkv + g) * SL + (j % SL)) * D;
+    return kc_pool + ((size_t)trow[j / SL] * Hkv + g) * SL * D;
 }
 
 // Length of sequence s clamped to [0, Lmax], Lmax = min(host bound, what a
@@ -123,17 +153,17 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ kb,
                                             const bf16x8 (&qb)[4], float scale_log2, int r,
                                             int kq, AttnState& A)
 {
+    // operand blocks in lane order (k_chunk / v_chunk): 1 KB per load
+    const int lane8 = (16 * kq + r) * 8;
     uint4 ka[4][4], va[2][8];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int tok = qk_row_token(t, r);
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int st = 0; st < 4; ++st) ka[t][st] = ldg16(kb + tok * D + st * 32 + kq * 8);
-    }
+        for (int st = 0; st < 4; ++st) ka[t][st] = ldg16(kb + (t * 4 + st) * 512 + lane8);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) va[u][nt] = ldg16(vb + (nt * 16 + r) * BS + u * 32 + kq * 8);
+        for (int nt = 0; nt < 8; ++nt) va[u][nt] = ldg16(vb + (u * 8 + nt) * 512 + lane8);
     // Keep every load of the page in flight before the first use: a wave that
     // attends one page pays one memory latency instead of one per few loads.
     __builtin_amdgcn_sched_barrier(0);

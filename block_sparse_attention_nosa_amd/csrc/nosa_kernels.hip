@@ -104,9 +104,9 @@ __global__ __launch_bounds__(256) void kc_build_kernel(
         for (int e = 0; e < 8; ++e) acc[e] = 0.0;
         for (int i = 0; i < kPoolK; ++i) {
             const int t = j * kPoolS + i;
-            acc8(acc, ldg16(k_pool + (((size_t)trow[t / BS] * Hkv + g) * BS + (t % BS)) * D + cc * 8));
+            acc8(acc, ldg16(k_pool + ((size_t)trow[t / BS] * Hkv + g) * BS * D + k_chunk(t % BS, cc)));
         }
-        *reinterpret_cast<uint4*>(kc_slot(kc_pool, trow, Hkv, g, j) + cc * 8) = round8(acc);
+        *reinterpret_cast<uint4*>(kc_page(kc_pool, trow, Hkv, g, j) + kc_chunk(j % SL, cc)) = round8(acc);
     }
 }
 
@@ -233,10 +233,11 @@ __device__ void store_wg_partial8(CombineLds& sh, AttnState& A, int G, size_t he
 // keys (one float4 of z per head, eight heads per batch of loads) and adds
 // their sum to block j/4 and the last key's sigma to block j/4 + 1: two
 // additions per block, so the result does not depend on their order.
-// z was written by this workgroup (call after a barrier).  Also writes
+// z (in LDS or global memory) was written by this workgroup (call after a
+// barrier).  Also writes
 // scores_out.  Must be called by all NT threads.
 template <int NT>
-__device__ void pool_pair(const float* __restrict__ zg, int zstride, const float* lse, int G,
+__device__ __forceinline__ void pool_pair(const float* __restrict__ zg, int zstride, const float* lse, int G,
                           int nc, int nb, float* sI, float* __restrict__ scores_out, int max_nb)
 {
     const int tid = threadIdx.x;
@@ -299,6 +300,7 @@ struct Step1Args {
     int append;      // pool the key completed by the current token
     float* z;        // [B][Hq][zstride] logits (log2 units), private to the pair's workgroup
     int zstride;
+    int zl_stride;   // logits kept in LDS instead, [G][zl_stride] (0 = in z)
     int do_select, topk, wblocks, max_nb, max_sel, top_span;
     float* scores_out;  // [pairs][max_nb] or null
     int32_t* sel_out;   // [pairs][max_sel] or null
@@ -310,14 +312,21 @@ struct Step1Args {
     int lds_pages;  // the pair workgroup copies its block-table row into LDS
 };
 
-// LDS of a step-1 workgroup (dynamic): the block importance and the page ids
-// of the pair (pair workgroups) or the wave states (window workgroups).
-inline size_t step1_lds_bytes(int max_nb, bool pages)
+// LDS of a step-1 workgroup (dynamic): the block importance, the page ids
+// and the logits of the pair (pair workgroups) or the wave states (window
+// workgroups).
+__host__ __device__ inline size_t step1_z_offset(int max_nb, bool pages)
 {
-    const size_t pair = (size_t)max_nb * (sizeof(float) + (pages ? sizeof(int32_t) : 0));
+    const size_t b = (size_t)max_nb * (sizeof(float) + (pages ? sizeof(int32_t) : 0));
+    return (b + 15) / 16 * 16;
+}
+inline size_t step1_lds_bytes(int max_nb, bool pages, size_t zbytes)
+{
+    const size_t pair = step1_z_offset(max_nb, pages) + zbytes;
     return pair > sizeof(CombineLds) ? pair : sizeof(CombineLds);
 }
-constexpr size_t kStep1LdsBudget = 60 * 1024;  // dynamic LDS of a step-1 workgroup
+constexpr size_t kStep1LdsBudget = 60 * 1024;  // page ids in LDS below this
+constexpr size_t kStep1StaticLds = 10 * 1024;  // bound on the kernel's static LDS
 
 struct PairLds {
     float m[kPairWaves][kMaxGroup], s[kPairWaves][kMaxGroup];
@@ -331,7 +340,7 @@ struct PairLds {
 // and selects.  The wave owning the key completed by the current token
 // (tokens L-32 .. L-1) pools it from K first, stores it and substitutes it
 // into its MFMA operand.
-template <int T>
+template <int T, bool ZL>
 __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
 {
     __shared__ PairLds sh;
@@ -345,6 +354,10 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
     const size_t pair = (size_t)s * a.Hkv + g;
     float* sI = reinterpret_cast<float*>(smem);
     int32_t* spg = reinterpret_cast<int32_t*>(smem + sizeof(float) * a.max_nb);
+    // logits of head h, key j: zb[h * zs + j], in LDS or in the workspace
+    const int zs = ZL ? a.zl_stride : a.zstride;
+    float* zb = ZL ? reinterpret_cast<float*>(smem + step1_z_offset(a.max_nb, a.lds_pages))
+                   : a.z + head_row0 * a.zstride;
     // The block-table row goes to LDS first (four loads in flight per
     // thread), so no key load below waits on a table load: loads complete in
     // order, so a table load issued behind other loads would wait for them.
@@ -385,7 +398,7 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int t = jn * kPoolS + tr + 4 * i;
-            kr[i] = ldg16(a.k_pool + (((size_t)kpg[i] * a.Hkv + g) * BS + (t % BS)) * D + cc * 8);
+            kr[i] = ldg16(a.k_pool + ((size_t)kpg[i] * a.Hkv + g) * BS * D + k_chunk(t % BS, cc));
         }
         double acc[8];
 #pragma unroll
@@ -400,7 +413,7 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
         appkey = round8(acc);  // channels 8cc .. 8cc+7, same in every phase
         if (tr == 0) {
             const int pj = a.lds_pages ? spg[jn / SL] : trow[jn / SL];
-            *reinterpret_cast<uint4*>(a.kc_pool + (((size_t)pj * a.Hkv + g) * SL + jn % SL) * D + cc * 8) = appkey;
+            *reinterpret_cast<uint4*>(a.kc_pool + ((size_t)pj * a.Hkv + g) * SL * D + kc_chunk(jn % SL, cc)) = appkey;
         }
     }
     float m_run = -INFINITY, s_run = 0.f;  // head r, over this lane's keys
@@ -419,9 +432,9 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
         for (int t = 0; t < T; ++t) {
             const int key = key0 + t * 16 + r;
             if (key < nc) {
-                const uint16_t* kp = a.kc_pool + (((size_t)pg[t] * a.Hkv + g) * SL + key % SL) * D;
+                const uint16_t* kp = a.kc_pool + ((size_t)pg[t] * a.Hkv + g) * SL * D;
 #pragma unroll
-                for (int st = 0; st < 4; ++st) kv[t][st] = ldg16(kp + st * 32 + kq * 8);
+                for (int st = 0; st < 4; ++st) kv[t][st] = ldg16(kp + kc_chunk(key % SL, st * 4 + kq));
             } else {
 #pragma unroll
                 for (int st = 0; st < 4; ++st) kv[t][st] = make_uint4(0, 0, 0, 0);
@@ -456,7 +469,7 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
                 tmax = fmaxf(tmax, zv[i]);
             }
             if (r < a.G)
-                *reinterpret_cast<float4*>(a.z + (head_row0 + r) * a.zstride + key0 + t * 16 + kq * 4) =
+                *reinterpret_cast<float4*>(zb + r * zs + key0 + t * 16 + kq * 4) =
                     make_float4(zv[0], zv[1], zv[2], zv[3]);
             if (tmax != -INFINITY) {
                 const float mn = fmaxf(m_run, tmax);
@@ -480,7 +493,7 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
         sh.m[wave][r] = m_run;
         sh.s[wave][r] = s_run;
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's logits have reached L2
+    if (!ZL) __builtin_amdgcn_s_waitcnt(0);  // this wave's logits have reached L2
     __syncthreads();
     if (tid < a.G) {
         float m = -INFINITY, acc = 0.f;
@@ -495,7 +508,7 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
         sh.sel.lse[tid] = m + log2f(acc);
     }
     __syncthreads();
-    pool_pair<kPairThreads>(a.z + head_row0 * a.zstride, a.zstride, sh.sel.lse, a.G, nc, nb, sI,
+    pool_pair<kPairThreads>(zb, zs, sh.sel.lse, a.G, nc, nb, sI,
                             a.scores_out ? a.scores_out + pair * a.max_nb : nullptr, a.max_nb);
     if (!a.do_select) return;
     select_blocks_wg<kPairWaves>(sI, nb, a.wblocks, a.topk, sh.sel,
@@ -530,7 +543,7 @@ __device__ void window_part(const Step1Args& a, int s, int g, int grp, char* sme
                       a.nsplit, grp, a.po, a.pml);
 }
 
-template <int T>
+template <int T, bool ZL>
 __global__ __launch_bounds__(512) void step1_kernel(Step1Args a)
 {
     extern __shared__ __align__(16) char smem[];
@@ -538,7 +551,7 @@ __global__ __launch_bounds__(512) void step1_kernel(Step1Args a)
     const int npairs = a.B * a.Hkv;
     int wg = blockIdx.x;
     if (wg < npairs) {
-        pair_part<T>(a, wg / a.Hkv, wg % a.Hkv, smem);
+        pair_part<T, ZL>(a, wg / a.Hkv, wg % a.Hkv, smem);
     } else {
         wg -= npairs;
         const int pair = wg / a.win_groups, grp = wg % a.win_groups;
@@ -578,45 +591,65 @@ struct MergeLds {
     float M[kMaxGroup], L[kMaxGroup];
 };
 
-// Combine the nsplit partials of every head of the pair into out / lse.  All
-// (m, l) go to LDS in one parallel pass, each head's weights are formed once,
-// then thread (head, 4 channels) sums the weighted outputs with its loads
-// issued eight partials at a time.  Reads data of other workgroups: call
-// after last_of_pair().
+// Combine the nsplit partials of every head of the pair into out / lse.
+// Thread (head, 4 channels) issues the loads of its first batch of partial
+// outputs before the (m, l) of all partials go to LDS, so both travel at
+// once; 16 lanes per head then form the head's max, weights and sum with
+// lane shuffles.  Reads data of other workgroups: call after last_of_pair().
 __device__ void merge_pair(const Step2Args& a, int s, int g, MergeLds& sh)
 {
     const int tid = threadIdx.x;
     const int G = a.G, ns = a.nsplit;
     const size_t row0 = (size_t)s * a.Hq + g * G;
+    const int nitems = G * 32;  // (head, 4 channels) items, <= 512
+    auto po_row = [&](int item) { return a.po + (row0 + (item >> 5)) * ns * D + (item & 31) * 4; };
+    float4 o[kMergeBatch];
+    if (tid < nitems) {
+        const float* op = po_row(tid);
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u)
+            if (u < ns) o[u] = *reinterpret_cast<const float4*>(op + (size_t)u * D);
+    }
     for (int e = tid; e < G * ns; e += 256) {
         const int h = e / ns, i = e % ns;
         sh.ml[h][i] = a.pml[(row0 + h) * ns + i];
     }
     __syncthreads();
-    if (tid < G) {
+    {
+        // 16 lanes per head: lane j takes partials j, j + 16, ...
+        const int h = tid >> 4, j = tid & 15;
         float M = -INFINITY;
-        for (int i = 0; i < ns; ++i) M = fmaxf(M, sh.ml[tid][i].x);
+        if (h < G)
+            for (int i = j; i < ns; i += 16) M = fmaxf(M, sh.ml[h][i].x);
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
         float L = 0.f;
-        for (int i = 0; i < ns; ++i) {
-            const float2 v = sh.ml[tid][i];
-            const float w = (M == -INFINITY || v.x == -INFINITY) ? 0.f : exp2f(v.x - M);
-            sh.w[tid][i] = w;
-            L += w * v.y;
+        if (h < G)
+            for (int i = j; i < ns; i += 16) {
+                const float2 v = sh.ml[h][i];
+                const float w = (M == -INFINITY || v.x == -INFINITY) ? 0.f : exp2f(v.x - M);
+                sh.w[h][i] = w;
+                L += w * v.y;
+            }
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) L += __shfl_xor(L, off, 16);
+        if (h < G && j == 0) {
+            sh.M[h] = M;
+            sh.L[h] = L;
         }
-        sh.M[tid] = M;
-        sh.L[tid] = L;
     }
     __syncthreads();
-    for (int item = tid; item < G * 32; item += 256) {
+    for (int item = tid; item < nitems; item += 256) {
         const int h = item >> 5, c = (item & 31) * 4;
-        const float* op = a.po + (row0 + h) * ns * D + c;
+        const float* op = po_row(item);
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 1
         for (int i0 = 0; i0 < ns; i0 += kMergeBatch) {
-            float4 o[kMergeBatch];
+            if (item != tid || i0 > 0) {
 #pragma unroll
-            for (int u = 0; u < kMergeBatch; ++u)
-                if (i0 + u < ns) o[u] = *reinterpret_cast<const float4*>(op + (size_t)(i0 + u) * D);
+                for (int u = 0; u < kMergeBatch; ++u)
+                    if (i0 + u < ns) o[u] = *reinterpret_cast<const float4*>(op + (size_t)(i0 + u) * D);
+            }
 #pragma unroll
             for (int u = 0; u < kMergeBatch; ++u) {
                 if (i0 + u >= ns) break;
@@ -763,16 +796,49 @@ static Step1Args step1_args(const Plan& pl, const nosa_paged_kv& kv, const nosa_
     a.po = w.po;
     a.pml = w.pml;
     a.nsplit = pl.nsplit;
-    a.lds_pages = step1_lds_bytes(pl.max_nb, true) <= kStep1LdsBudget;
+    a.lds_pages = step1_lds_bytes(pl.max_nb, true, 0) <= kStep1LdsBudget;
     return a;
 }
 
-static hipError_t launch_step1(const Plan& pl, const Step1Args& a, hipStream_t stream)
+// Largest LDS a workgroup may use on the current device (queried once per
+// device).
+static size_t device_lds_limit()
+{
+    static size_t cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * 1024;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            v <= 0)
+            v = 64 * 1024;
+        cached[dev] = (size_t)v;
+    }
+    return cached[dev];
+}
+
+template <int T, bool ZL>
+static void launch_step1_t(dim3 grid, size_t lds, const Step1Args& a, hipStream_t stream)
+{
+    if (lds > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&step1_kernel<T, ZL>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL((step1_kernel<T, ZL>), grid, dim3(kPairThreads), lds, stream, a);
+}
+
+static hipError_t launch_step1(const Plan& pl, Step1Args a, hipStream_t stream)
 {
     const int npairs = pl.B * pl.Hkv;
     dim3 grid(npairs * (1 + a.win_groups));
-    const size_t lds = step1_lds_bytes(pl.max_nb, a.lds_pages);
-#define NOSA_STEP1(T) hipLaunchKernelGGL(step1_kernel<T>, grid, dim3(kPairThreads), lds, stream, a)
+    // logits in LDS when they fit beside everything else
+    const int zls = (pl.max_nc + 15) / 16 * 16 + 4;
+    const size_t zbytes = (size_t)pl.G * zls * sizeof(float);
+    const bool zl = step1_lds_bytes(pl.max_nb, a.lds_pages, zbytes) + kStep1StaticLds <= device_lds_limit();
+    a.zl_stride = zl ? zls : 0;
+    const size_t lds = step1_lds_bytes(pl.max_nb, a.lds_pages, zl ? zbytes : 0);
+#define NOSA_STEP1(T)                                           \
+    (zl ? launch_step1_t<T, true>(grid, lds, a, stream)         \
+        : launch_step1_t<T, false>(grid, lds, a, stream))
     switch (pl.score_tiles) {
         case 1: NOSA_STEP1(1); break;
         case 2: NOSA_STEP1(2); break;

@@ -165,9 +165,9 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
         uint4 kf[4];
         const int key = kt + r;
         if (key < key_hi) {
-            const uint16_t* kp = kc_slot(const_cast<uint16_t*>(a.kc_pool), trow, a.Hkv, P.g, key);
+            const uint16_t* kp = kc_page(const_cast<uint16_t*>(a.kc_pool), trow, a.Hkv, P.g, key);
 #pragma unroll
-            for (int st = 0; st < 4; ++st) kf[st] = ldg16(kp + st * 32 + kq * 8);
+            for (int st = 0; st < 4; ++st) kf[st] = ldg16(kp + kc_chunk(key % SL, st * 4 + kq));
         } else {
 #pragma unroll
             for (int st = 0; st < 4; ++st) kf[st] = make_uint4(0, 0, 0, 0);
@@ -331,9 +331,12 @@ __global__ __launch_bounds__(256) void pf_attend_kernel(PfArgs a, int attn_group
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) o[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // global -> register staging of one page: thread tid moves K chunks
-    // tid + 256c (row = chunk / 16, 16-byte column chunk % 16) and V chunks
-    // tid + 256c (row = chunk / 8, column chunk % 8), c < 4
+    // global -> register staging of one page: thread tid moves the 16-byte
+    // chunks tid + 256c (c < 4) of the K and V pages, contiguous in memory;
+    // their rows and columns in LDS follow from the page layouts (k_chunk,
+    // v_chunk): K chunk q is channels 8(4 st + kq) .. of token
+    // qk_row_token(t, m) with q = 64(4t + st) + 16kq + m; V chunk q is tokens
+    // 8(4u + kq) .. of channel 16 nt + r with q = 64(8u + nt) + 16kq + r
     uint4 stk[4], stv[4];
     auto fetch = [&](int idx) {
         int b = idx < n ? sl[idx] : -1;
@@ -344,8 +347,8 @@ __global__ __launch_bounds__(256) void pf_attend_kernel(PfArgs a, int attn_group
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int ch = tid + 256 * c;
-            stk[c] = b >= 0 ? ldg16(kb + (ch >> 4) * D + (ch & 15) * 8) : make_uint4(0, 0, 0, 0);
-            stv[c] = b >= 0 ? ldg16(vb + (ch >> 3) * BS + (ch & 7) * 8) : make_uint4(0, 0, 0, 0);
+            stk[c] = b >= 0 ? ldg16(kb + ch * 8) : make_uint4(0, 0, 0, 0);
+            stv[c] = b >= 0 ? ldg16(vb + ch * 8) : make_uint4(0, 0, 0, 0);
         }
         return b;
     };
@@ -353,8 +356,10 @@ __global__ __launch_bounds__(256) void pf_attend_kernel(PfArgs a, int attn_group
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int ch = tid + 256 * c;
-            *reinterpret_cast<uint4*>(&sh.k[(ch >> 4) * kKRow + (ch & 15) * 8]) = stk[c];
-            *reinterpret_cast<uint4*>(&sh.v[(ch >> 3) * kVRow + (ch & 7) * 8]) = stv[c];
+            const int ktok = qk_row_token(ch >> 8, ch & 15), kc8 = ((ch >> 6) & 3) * 4 + ((ch >> 4) & 3);
+            const int vch = ((ch >> 6) & 7) * 16 + (ch & 15), vx8 = (ch >> 9) * 4 + ((ch >> 4) & 3);
+            *reinterpret_cast<uint4*>(&sh.k[ktok * kKRow + kc8 * 8]) = stk[c];
+            *reinterpret_cast<uint4*>(&sh.v[vch * kVRow + vx8 * 8]) = stv[c];
         }
     };
 

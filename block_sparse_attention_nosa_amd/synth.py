@@ -19,10 +19,12 @@ Recipe (the same for every workload):
 
 Packed layouts (what the CPU reference reads):
   q [total_q][Hq][d], k / v [total_k][Hkv][d]  (bf16), cu_seqlens int32.
-Paged layouts (what the library reads):
-  k_pool  [num_pages][Hkv][block_size][d]      token-major
-  v_pool  [num_pages][Hkv][d][block_size]      channel-major within a page
-  kc_pool [num_pages][Hkv][block_size/stride][d]
+Paged layouts (what the library reads): one page holds block_size tokens of
+one KV head; pages are [num_pages][Hkv][page elements] and the elements of a
+page are in the library's operand order (see page_index below):
+  k_pool  [num_pages][Hkv][block_size * d]
+  v_pool  [num_pages][Hkv][block_size * d]
+  kc_pool [num_pages][Hkv][block_size / stride * d]
   block_table [B][max_blocks] int32 (unused entries 0).
 """
 from __future__ import annotations
@@ -136,6 +138,34 @@ def packed_live(inp: dict, w: Workload, step: int = 0):
     return torch.cat(ks), torch.cat(vs), cu_from_lens([L + step for L in w.lens])
 
 
+def page_index(kind: str, block_size: int = 64, d: int = 128, stride: int = 16) -> torch.Tensor:
+    """For each stored element of a page, the index of the element it holds
+    in the logical page ([token][channel] for "k" and "v", [slot][channel]
+    for "kc"), so that stored = logical.flatten()[page_index(kind)].
+
+    Stored offsets, element e of 8 (all pages of 64 tokens x 128 channels):
+      k : (((4t + st) * 4 + kq) * 16 + m) * 8 + e holds channel 32st + 8kq + e
+          of token 32(t // 2) + 8(m // 4) + 4(t % 2) + m % 4;
+      v : (((8u + nt) * 4 + kq) * 16 + r) * 8 + e holds token 32u + 8kq + e of
+          channel 16nt + r;
+      kc: (c8 * 4 + j) * 8 + e holds channel 8c8 + e of slot j.
+    """
+    assert block_size == 64 and d == 128 and stride == 16
+    o = torch.arange(block_size * d if kind != "kc" else block_size // stride * d)
+    e = o & 7
+    if kind == "k":
+        m, kq, st, t = (o >> 3) & 15, (o >> 7) & 3, (o >> 9) & 3, o >> 11
+        tok = 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3)
+        return tok * d + 32 * st + 8 * kq + e
+    if kind == "v":
+        r, kq, nt, u = (o >> 3) & 15, (o >> 7) & 3, (o >> 9) & 7, o >> 12
+        return (32 * u + 8 * kq + e) * d + 16 * nt + r
+    if kind == "kc":
+        j, c8 = (o >> 3) & 3, o >> 5
+        return j * d + 8 * c8 + e
+    raise ValueError(kind)
+
+
 def to_paged(inp: dict, w: Workload, permute: bool = True, device=None) -> dict:
     """Scatter the packed K/V into the paged pools (see the module docstring)."""
     k, v = inp["k"], inp["v"]
@@ -150,8 +180,10 @@ def to_paged(inp: dict, w: Workload, permute: bool = True, device=None) -> dict:
     else:
         perm = torch.arange(num_pages, device=device)
     table = torch.zeros(w.batch, max_blocks, dtype=torch.int32, device=device)
-    k_pool = torch.zeros(num_pages, Hkv, bs, d, dtype=torch.bfloat16, device=device)
-    v_pool = torch.zeros(num_pages, Hkv, d, bs, dtype=torch.bfloat16, device=device)
+    k_pool = torch.zeros(num_pages, Hkv, bs * d, dtype=torch.bfloat16, device=device)
+    v_pool = torch.zeros(num_pages, Hkv, bs * d, dtype=torch.bfloat16, device=device)
+    kidx = page_index("k", bs, d, w.stride).to(device)
+    vidx = page_index("v", bs, d, w.stride).to(device)
     logical = 0
     for s, n in enumerate(inp["stored_lens"]):
         base = int(inp["cu_k_store"][s])
@@ -163,13 +195,13 @@ def to_paged(inp: dict, w: Workload, permute: bool = True, device=None) -> dict:
             vs = torch.cat([vs, torch.zeros(pad, Hkv, d, dtype=vs.dtype, device=device)])
         pages = perm[logical:logical + nbs[s]]
         table[s, :nbs[s]] = pages.to(torch.int32)
-        # [nb, bs, Hkv, d] -> [nb, Hkv, bs, d] and [nb, Hkv, d, bs]
-        kb = ks.view(nbs[s], bs, Hkv, d)
-        vb = vs.view(nbs[s], bs, Hkv, d)
-        k_pool[pages.long()] = kb.permute(0, 2, 1, 3)
-        v_pool[pages.long()] = vb.permute(0, 2, 3, 1)
+        # [nb, bs, Hkv, d] -> logical pages [nb, Hkv, bs * d] -> stored order
+        kb = ks.view(nbs[s], bs, Hkv, d).permute(0, 2, 1, 3).reshape(nbs[s], Hkv, bs * d)
+        vb = vs.view(nbs[s], bs, Hkv, d).permute(0, 2, 1, 3).reshape(nbs[s], Hkv, bs * d)
+        k_pool[pages.long()] = kb[:, :, kidx]
+        v_pool[pages.long()] = vb[:, :, vidx]
         logical += nbs[s]
-    kc_pool = torch.zeros(num_pages, Hkv, bs // w.stride, d, dtype=torch.bfloat16,
+    kc_pool = torch.zeros(num_pages, Hkv, bs // w.stride * d, dtype=torch.bfloat16,
                           device=device)
     return dict(k_pool=k_pool, v_pool=v_pool, kc_pool=kc_pool, block_table=table,
                 max_blocks=max_blocks, num_pages=num_pages)

@@ -90,13 +90,25 @@ typedef struct nosa_params {
 /* Paged KV cache [page "NOSA技术架构解析", section 2.1: a PagedAttention-style
  * memory pool].  One page holds one block of block_size tokens for every KV
  * head.  Logical block b of sequence s lives in page block_table[s][b].
- *   k_pool  [num_pages][Hkv][block_size][d]   token-major
- *   v_pool  [num_pages][Hkv][d][block_size]   channel-major inside a page
- *   kc_pool [num_pages][Hkv][block_size/stride][d]: compressed key j of
+ *   k_pool  [num_pages][Hkv][block_size * d]
+ *   v_pool  [num_pages][Hkv][block_size * d]
+ *   kc_pool [num_pages][Hkv][block_size / stride * d]: compressed key j of
  *           sequence s is slot j % (block_size/stride) of page
  *           block_table[s][j / (block_size/stride)], so it needs no table of
  *           its own.
- *   block_table [batch][max_blocks_per_seq] int32. */
+ *   block_table [batch][max_blocks_per_seq] int32.
+ * Inside a page (of one KV head) elements are stored in matrix-core operand
+ * order, in runs of 8 consecutive elements (16 bytes); with token x,
+ * channel c, slot j and e = the element's index inside its run:
+ *   k : offset (((4t + st) * 4 + kq) * 16 + m) * 8 + e holds token
+ *       x = 32(t/2) + 8(m/4) + 4(t%2) + m%4, channel c = 32 st + 8 kq + e;
+ *   v : offset (((8u + nt) * 4 + kq) * 16 + r) * 8 + e holds token
+ *       x = 32u + 8kq + e, channel c = 16 nt + r;
+ *   kc: offset (c8 * 4 + j) * 8 + e holds channel 8 c8 + e of slot j.
+ * with t, st, kq in [0, 4), u in [0, 2), nt in [0, 8), m, r, c8 in [0, 16)
+ * and j in [0, block_size / stride).  Each 1 KB run
+ * of 64 x 16 bytes is what one wave's 16-byte-per-lane load fetches for one
+ * matrix-core step.  The library writes kc_pool; the caller writes K and V. */
 typedef struct nosa_paged_kv {
     const nosa_bf16* k_pool;
     const nosa_bf16* v_pool;

@@ -73,10 +73,16 @@ def build_kc(c: DecodeCase, lens, valid=None):
 def gpu_kc_logical(c: DecodeCase, s: int, nc: int) -> np.ndarray:
     """GPU pooled keys of sequence s in logical order: [Hkv][nc][d] bf16 bits."""
     slots = c.w.block_size // c.w.stride
+    d = c.w.head_dim
     table = c.pg["block_table"][s].cpu()
     j = torch.arange(nc)
     pages = table[(j // slots)].long()
-    kc = c.pg["kc_pool"].cpu()[pages, :, (j % slots)]      # [nc, Hkv, d]
+    # stored page -> logical [slot][channel]
+    idx = synth.page_index("kc", c.w.block_size, d, c.w.stride)
+    stored = c.pg["kc_pool"].cpu()
+    logical = torch.empty_like(stored)
+    logical[:, :, idx] = stored
+    kc = logical.view(stored.shape[0], stored.shape[1], slots, d)[pages, :, (j % slots)]  # [nc, Hkv, d]
     return synth.bits(kc.permute(1, 0, 2))
 
 

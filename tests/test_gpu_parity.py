@@ -55,6 +55,16 @@ def test_decode_step_head_groups(hq, hkv):
     _full_check(c, tag=f"{hq}/{hkv}")
 
 
+@pytest.mark.parametrize("hq,hkv,L", [(16, 1, 40000), (8, 1, 70000)])
+def test_decode_step_logits_beyond_lds(hq, hkv, L):
+    """A group of 16 heads over 40K tokens (8 over 70K) has more logits than
+    one workgroup's LDS holds next to its other arrays: the step keeps them in
+    the workspace instead of in LDS."""
+    log(f"case: logits beyond LDS, heads {hq}/{hkv}, L={L}")
+    c = make_case(_wl([L, 1000], hq=hq, hkv=hkv, topk=32, planted=3, seed=L + hq))
+    _full_check(c, tag=f"zglobal {hq}/{hkv}")
+
+
 @pytest.mark.parametrize("lens", [
     [1], [17], [31], [32], [33], [63, 64, 65], [1023, 1024, 1025],
     [1088, 1089, 1090, 1151], [2047, 2048, 2049], [5000, 40, 3333, 64 * 17 + 5]])

@@ -53,15 +53,16 @@ nosa_status check_sizes(int batch, int max_seqlen_q, int max_seqlen_k)
 }
 
 // Tiles of 16 pooled keys each wave of a pair's scoring workgroup keeps in
-// flight per batch: enough that one batch covers the pair when it is short,
-// at most 8 (128 keys, 32 loads of 16 bytes per lane).
+// flight per batch (one of the compiled 1, 2, 3, 5, 7, 9, 12): enough that
+// one batch covers the pair when it is short, at most 12 (192 keys, 48 loads
+// of 16 bytes per lane).
 int pick_score_tiles(int nc)
 {
+    static const int kTiles[] = {1, 2, 3, 5, 7, 9, 12};
     const int per_wave = ceil_div(ceil_div(nc, 16), 8);
-    if (per_wave <= 1) return 1;
-    if (per_wave <= 2) return 2;
-    if (per_wave <= 4) return 4;
-    return 8;
+    for (int t : kTiles)
+        if (per_wave <= t) return t;
+    return 12;
 }
 
 // Blocks per wave (rounds, one of the compiled 1, 2, 3, 4, 6, 8) and

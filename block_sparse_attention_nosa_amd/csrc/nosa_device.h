@@ -32,6 +32,10 @@ __device__ __forceinline__ int dev_num_keys(int L) { return L >= kPoolK ? (L - k
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// 2^x with the hardware instruction (results below 2^-126 flush to zero,
+// which no softmax weight or sum here is sensitive to).
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -185,13 +189,13 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ kb,
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
     const float m_new = fmaxf(A.m, bmax);
-    const float alpha = exp2f(A.m - m_new);
+    const float alpha = fexp2(A.m - m_new);
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[t][i] = exp2f(x[t][i] - m_new);
+            x[t][i] = fexp2(x[t][i] - m_new);
             psum += x[t][i];
         }
     A.l = A.l * alpha + psum;

@@ -156,7 +156,7 @@ __device__ void store_wg_partial(CombineLds& sh, const AttnState& A, int G, size
         float wt[4], Lsum = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            wt[w] = (M == -INFINITY || sh.m[w][h] == -INFINITY) ? 0.f : exp2f(sh.m[w][h] - M);
+            wt[w] = (M == -INFINITY || sh.m[w][h] == -INFINITY) ? 0.f : fexp2(sh.m[w][h] - M);
             Lsum += wt[w] * sh.l[w][h];
         }
         float acc[8];
@@ -207,16 +207,16 @@ __device__ void store_wg_partial8(CombineLds& sh, AttnState& A, int G, size_t he
             const int h = 4 * kq + i;
             const float ma = m_lo[wave][h], mb = sh.m[wave][h];
             const float M = fmaxf(ma, mb);
-            const float wa = (M == -INFINITY || ma == -INFINITY) ? 0.f : exp2f(ma - M);
-            const float wb = (M == -INFINITY || mb == -INFINITY) ? 0.f : exp2f(mb - M);
+            const float wa = (M == -INFINITY || ma == -INFINITY) ? 0.f : fexp2(ma - M);
+            const float wb = (M == -INFINITY || mb == -INFINITY) ? 0.f : fexp2(mb - M);
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt)
                 A.o[nt][i] = A.o[nt][i] * wa + sh.o[wave][h][nt * 16 + r] * wb;
         }
         const float ma = A.m, mb = sh.m[wave][r];
         const float M = fmaxf(ma, mb);
-        const float wa = (M == -INFINITY || ma == -INFINITY) ? 0.f : exp2f(ma - M);
-        const float wb = (M == -INFINITY || mb == -INFINITY) ? 0.f : exp2f(mb - M);
+        const float wa = (M == -INFINITY || ma == -INFINITY) ? 0.f : fexp2(ma - M);
+        const float wb = (M == -INFINITY || mb == -INFINITY) ? 0.f : fexp2(mb - M);
         A.l = l * wa + sh.l[wave][r] * wb;  // already summed over the lane groups
         A.m = M;
     }
@@ -256,10 +256,10 @@ __device__ __forceinline__ void pool_pair(const float* __restrict__ zg, int zstr
             for (int u = 0; u < 8; ++u)
                 if (h0 + u < G) {
                     const float lh = lse[h0 + u];
-                    sg[0] += exp2f(zz[u].x - lh);
-                    sg[1] += exp2f(zz[u].y - lh);
-                    sg[2] += exp2f(zz[u].z - lh);
-                    sg[3] += exp2f(zz[u].w - lh);
+                    sg[0] += fexp2(zz[u].x - lh);
+                    sg[1] += fexp2(zz[u].y - lh);
+                    sg[2] += fexp2(zz[u].z - lh);
+                    sg[3] += fexp2(zz[u].w - lh);
                 }
         }
         const int b = j0 >> 2;
@@ -309,23 +309,21 @@ struct Step1Args {
     float* po;
     float2* pml;
     int nsplit;  // partial slots per head
-    int lds_pages;  // the pair workgroup copies its block-table row into LDS
 };
 
 // LDS of a step-1 workgroup (dynamic): the block importance, the page ids
 // and the logits of the pair (pair workgroups) or the wave states (window
 // workgroups).
-__host__ __device__ inline size_t step1_z_offset(int max_nb, bool pages)
+__host__ __device__ inline size_t step1_z_offset(int max_nb)
 {
-    const size_t b = (size_t)max_nb * (sizeof(float) + (pages ? sizeof(int32_t) : 0));
+    const size_t b = (size_t)max_nb * (sizeof(float) + sizeof(int32_t));
     return (b + 15) / 16 * 16;
 }
-inline size_t step1_lds_bytes(int max_nb, bool pages, size_t zbytes)
+inline size_t step1_lds_bytes(int max_nb, size_t zbytes)
 {
-    const size_t pair = step1_z_offset(max_nb, pages) + zbytes;
+    const size_t pair = step1_z_offset(max_nb) + zbytes;
     return pair > sizeof(CombineLds) ? pair : sizeof(CombineLds);
 }
-constexpr size_t kStep1LdsBudget = 60 * 1024;  // page ids in LDS below this
 constexpr size_t kStep1StaticLds = 10 * 1024;  // bound on the kernel's static LDS
 
 struct PairLds {
@@ -356,23 +354,21 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
     int32_t* spg = reinterpret_cast<int32_t*>(smem + sizeof(float) * a.max_nb);
     // logits of head h, key j: zb[h * zs + j], in LDS or in the workspace
     const int zs = ZL ? a.zl_stride : a.zstride;
-    float* zb = ZL ? reinterpret_cast<float*>(smem + step1_z_offset(a.max_nb, a.lds_pages))
+    float* zb = ZL ? reinterpret_cast<float*>(smem + step1_z_offset(a.max_nb))
                    : a.z + head_row0 * a.zstride;
     // The block-table row goes to LDS first (four loads in flight per
     // thread), so no key load below waits on a table load: loads complete in
     // order, so a table load issued behind other loads would wait for them.
-    if (a.lds_pages) {
-        for (int b0 = tid; b0 < nb; b0 += 4 * kPairThreads) {
-            int v[4];
+    for (int b0 = tid; b0 < nb; b0 += 4 * kPairThreads) {
+        int v[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int b = b0 + u * kPairThreads;
-                v[u] = b < nb ? trow[b] : 0;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (b0 + u * kPairThreads < nb) spg[b0 + u * kPairThreads] = v[u];
+        for (int u = 0; u < 4; ++u) {
+            const int b = b0 + u * kPairThreads;
+            v[u] = b < nb ? trow[b] : 0;
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (b0 + u * kPairThreads < nb) spg[b0 + u * kPairThreads] = v[u];
     }
 
     select_lds_clear<kPairThreads>(sh.sel);
@@ -382,9 +378,9 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
     const int jn = nc - 1;
     const bool appending = a.append && L >= kPoolK && (L - kPoolK) % kPoolS == 0;
     const int ntiles = (nc + 15) / 16;
-    // The wave whose batch holds key jn pools it before its first batch.
-    const bool app_mine = appending && ((jn / 16) / T) % kPairWaves == wave;
-    uint4 appkey = make_uint4(0, 0, 0, 0);
+    // The wave whose batch holds key jn pools it and stores it before its
+    // first batch, which then loads it like every other key.
+    const bool app_mine = appending && (jn / 16) % kPairWaves == wave;
     if (app_mine) {
         const int tr = lane >> 4, cc = lane & 15;  // 4 token phases x 16 channel chunks
         // tokens 16jn + tr + 4i, i < 8: their pages first, then all loads
@@ -392,7 +388,7 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int b = (jn * kPoolS + tr + 4 * i) / BS;
-            kpg[i] = a.lds_pages ? spg[b] : trow[b];
+            kpg[i] = spg[b];
         }
         uint4 kr[8];
 #pragma unroll
@@ -410,53 +406,43 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
             acc[e] += __shfl_xor(acc[e], 16);
             acc[e] += __shfl_xor(acc[e], 32);
         }
-        appkey = round8(acc);  // channels 8cc .. 8cc+7, same in every phase
+        const uint4 appkey = round8(acc);  // channels 8cc .. 8cc+7, same in every phase
         if (tr == 0) {
-            const int pj = a.lds_pages ? spg[jn / SL] : trow[jn / SL];
+            const int pj = spg[jn / SL];
             *reinterpret_cast<uint4*>(a.kc_pool + ((size_t)pj * a.Hkv + g) * SL * D + kc_chunk(jn % SL, cc)) = appkey;
         }
+        // the key has reached L2 before this wave loads its tiles below (no
+        // other wave reads this page in this launch)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_s_waitcnt(0);
     }
     float m_run = -INFINITY, s_run = 0.f;  // head r, over this lane's keys
-    for (int t0 = wave * T; t0 < ntiles; t0 += kPairWaves * T) {
-        const int key0 = t0 * 16;
-        // page ids of this lane's keys for the whole batch before any key load
-        int pg[T];
+    // tile i of the pair (keys 16i .. 16i + 15) goes to wave i % 8, T tiles
+    // of a wave per batch: tiles wave + 8 (bT + t), t < T
+    for (int b0 = wave; b0 < ntiles; b0 += kPairWaves * T) {
+        // page ids of this lane's keys for the whole batch before any key
+        // load; rows past the last key load that key again (their logits are
+        // masked below), so the loads need no branch
+        int pg[T], kr[T];
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const int key = key0 + t * 16 + r;
-            const int b = (key < nc ? key : 0) / SL;
-            pg[t] = a.lds_pages ? spg[b] : trow[b];
+            const int key = (b0 + kPairWaves * t) * 16 + r;
+            kr[t] = key < nc ? key : nc - 1;
+            pg[t] = spg[kr[t] / SL];
         }
         uint4 kv[T][4];
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const int key = key0 + t * 16 + r;
-            if (key < nc) {
-                const uint16_t* kp = a.kc_pool + ((size_t)pg[t] * a.Hkv + g) * SL * D;
+            const uint16_t* kp = a.kc_pool + ((size_t)pg[t] * a.Hkv + g) * SL * D;
 #pragma unroll
-                for (int st = 0; st < 4; ++st) kv[t][st] = ldg16(kp + kc_chunk(key % SL, st * 4 + kq));
-            } else {
-#pragma unroll
-                for (int st = 0; st < 4; ++st) kv[t][st] = make_uint4(0, 0, 0, 0);
-            }
+            for (int st = 0; st < 4; ++st) kv[t][st] = ldg16(kp + kc_chunk(kr[t] % SL, st * 4 + kq));
         }
-        if (app_mine && jn >= key0 && jn < key0 + 16 * T) {
-            const int tloc = (jn - key0) / 16, rloc = (jn - key0) % 16;
-#pragma unroll
-            for (int t = 0; t < T; ++t)
-#pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    uint4 v;
-                    v.x = __shfl(appkey.x, st * 4 + kq);
-                    v.y = __shfl(appkey.y, st * 4 + kq);
-                    v.z = __shfl(appkey.z, st * 4 + kq);
-                    v.w = __shfl(appkey.w, st * 4 + kq);
-                    if (t == tloc && r == rloc) kv[t][st] = v;
-                }
-        }
+        // every load of the batch is in flight before the first use
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            if (key0 + t * 16 >= nc) break;
+            const int key0 = (b0 + kPairWaves * t) * 16;
+            if (key0 >= nc) continue;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(kv[t][st]), qb[st], acc);
@@ -464,19 +450,19 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
             float tmax = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = key0 + t * 16 + kq * 4 + i;
+                const int key = key0 + kq * 4 + i;
                 zv[i] = key < nc ? acc[i] * a.scale_log2 : -INFINITY;
                 tmax = fmaxf(tmax, zv[i]);
             }
             if (r < a.G)
-                *reinterpret_cast<float4*>(zb + r * zs + key0 + t * 16 + kq * 4) =
+                *reinterpret_cast<float4*>(zb + r * zs + key0 + kq * 4) =
                     make_float4(zv[0], zv[1], zv[2], zv[3]);
             if (tmax != -INFINITY) {
                 const float mn = fmaxf(m_run, tmax);
                 float add = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) add += exp2f(zv[i] - mn);
-                s_run = s_run * exp2f(m_run - mn) + add;
+                for (int i = 0; i < 4; ++i) add += fexp2(zv[i] - mn);
+                s_run = s_run * fexp2(m_run - mn) + add;
                 m_run = mn;
             }
         }
@@ -486,7 +472,7 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
     for (int off = 16; off < 64; off <<= 1) {
         const float mo = __shfl_xor(m_run, off), so = __shfl_xor(s_run, off);
         const float mn = fmaxf(m_run, mo);
-        s_run = mn == -INFINITY ? 0.f : s_run * exp2f(m_run - mn) + so * exp2f(mo - mn);
+        s_run = mn == -INFINITY ? 0.f : s_run * fexp2(m_run - mn) + so * fexp2(mo - mn);
         m_run = mn;
     }
     if (kq == 0 && r < a.G) {
@@ -502,7 +488,7 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
             const float mw = sh.m[w][tid], sw = sh.s[w][tid];
             if (!(sw > 0.f)) continue;
             const float mn = fmaxf(m, mw);
-            acc = acc * exp2f(m - mn) + sw * exp2f(mw - mn);
+            acc = acc * fexp2(m - mn) + sw * fexp2(mw - mn);
             m = mn;
         }
         sh.sel.lse[tid] = m + log2f(acc);
@@ -515,7 +501,7 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
                                  a.sel_out ? a.sel_out + pair * a.max_sel : nullptr,
                                  a.cnt_out ? a.cnt_out + pair : nullptr, a.max_sel,
                                  a.selpg ? a.selpg + pair * a.top_span : nullptr, nullptr,
-                                 a.top_span, trow, a.lds_pages ? spg : nullptr);
+                                 a.top_span, trow, spg);
 }
 
 // Window workgroup: wave w attends window slot 8*grp + w, slot x being block
@@ -627,7 +613,7 @@ __device__ void merge_pair(const Step2Args& a, int s, int g, MergeLds& sh)
         if (h < G)
             for (int i = j; i < ns; i += 16) {
                 const float2 v = sh.ml[h][i];
-                const float w = (M == -INFINITY || v.x == -INFINITY) ? 0.f : exp2f(v.x - M);
+                const float w = (M == -INFINITY || v.x == -INFINITY) ? 0.f : fexp2(v.x - M);
                 sh.w[h][i] = w;
                 L += w * v.y;
             }
@@ -796,7 +782,6 @@ static Step1Args step1_args(const Plan& pl, const nosa_paged_kv& kv, const nosa_
     a.po = w.po;
     a.pml = w.pml;
     a.nsplit = pl.nsplit;
-    a.lds_pages = step1_lds_bytes(pl.max_nb, true, 0) <= kStep1LdsBudget;
     return a;
 }
 
@@ -833,17 +818,22 @@ static hipError_t launch_step1(const Plan& pl, Step1Args a, hipStream_t stream)
     // logits in LDS when they fit beside everything else
     const int zls = (pl.max_nc + 15) / 16 * 16 + 4;
     const size_t zbytes = (size_t)pl.G * zls * sizeof(float);
-    const bool zl = step1_lds_bytes(pl.max_nb, a.lds_pages, zbytes) + kStep1StaticLds <= device_lds_limit();
+    const size_t limit = device_lds_limit();
+    if (step1_lds_bytes(pl.max_nb, 0) + kStep1StaticLds > limit) return hipErrorInvalidValue;
+    const bool zl = step1_lds_bytes(pl.max_nb, zbytes) + kStep1StaticLds <= limit;
     a.zl_stride = zl ? zls : 0;
-    const size_t lds = step1_lds_bytes(pl.max_nb, a.lds_pages, zl ? zbytes : 0);
+    const size_t lds = step1_lds_bytes(pl.max_nb, zl ? zbytes : 0);
 #define NOSA_STEP1(T)                                           \
     (zl ? launch_step1_t<T, true>(grid, lds, a, stream)         \
         : launch_step1_t<T, false>(grid, lds, a, stream))
     switch (pl.score_tiles) {
         case 1: NOSA_STEP1(1); break;
         case 2: NOSA_STEP1(2); break;
-        case 4: NOSA_STEP1(4); break;
-        default: NOSA_STEP1(8); break;
+        case 3: NOSA_STEP1(3); break;
+        case 5: NOSA_STEP1(5); break;
+        case 7: NOSA_STEP1(7); break;
+        case 9: NOSA_STEP1(9); break;
+        default: NOSA_STEP1(12); break;
     }
 #undef NOSA_STEP1
     return hipGetLastError();

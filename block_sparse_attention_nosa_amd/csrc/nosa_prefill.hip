@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
                     const float2 v = pp[i];
                     if (!(v.y > 0.f)) continue;
                     const float mn = fmaxf(m, v.x);
-                    acc = acc * exp2f(m - mn) + v.y * exp2f(v.x - mn);
+                    acc = acc * fexp2(m - mn) + v.y * fexp2(v.x - mn);
                     m = mn;
                 }
             }
@@ -193,13 +193,13 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
                     const float mn = fmaxf(m_run[u], tmax);
                     float add = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) add += exp2f(zz[i] - mn);
-                    s_run[u] = s_run[u] * exp2f(m_run[u] - mn) + add;
+                    for (int i = 0; i < 4; ++i) add += fexp2(zz[i] - mn);
+                    s_run[u] = s_run[u] * fexp2(m_run[u] - mn) + add;
                     m_run[u] = mn;
                 }
             } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) colacc[i] += exp2f(zz[i] - lse_r[u]);
+                for (int i = 0; i < 4; ++i) colacc[i] += fexp2(zz[i] - lse_r[u]);
             }
         }
         if (PASS == 2) {
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
             for (int off = 16; off < 64; off <<= 1) {
                 const float mo = __shfl_xor(m, off), so = __shfl_xor(s, off);
                 const float mn = fmaxf(m, mo);
-                s = mn == -INFINITY ? 0.f : s * exp2f(m - mn) + so * exp2f(mo - mn);
+                s = mn == -INFINITY ? 0.f : s * fexp2(m - mn) + so * fexp2(mo - mn);
                 m = mn;
             }
             const int row = (row_tile0 + u) * 16 + r;
@@ -401,13 +401,13 @@ __global__ __launch_bounds__(256) void pf_attend_kernel(PfArgs a, int attn_group
                 bm = fmaxf(bm, __shfl_xor(bm, 32));
                 const float m_new = fmaxf(m_run[u], bm);
                 // a row with nothing visible yet keeps m = -inf and adds nothing
-                const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run[u] - m_new);
+                const float alpha = m_new == -INFINITY ? 1.f : fexp2(m_run[u] - m_new);
                 float psum = 0.f;
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float e = m_new == -INFINITY ? 0.f : exp2f(x[u][t][i] - m_new);
+                        const float e = m_new == -INFINITY ? 0.f : fexp2(x[u][t][i] - m_new);
                         x[u][t][i] = e;
                         psum += e;
                     }

@@ -66,12 +66,13 @@ int pick_score_tiles(int nc)
 }
 
 // Blocks per wave (rounds, one of the compiled 1, 2, 3, 4, 6, 8) and
-// workgroups per pair for `span` list entries per pair: about 512 workgroups
-// of 4 waves in total -- two per CU, one dispatch round -- and at most
-// `max_groups` partials per head.
+// workgroups per pair for `span` list entries per pair: about 512
+// workgroups of kStep2Waves (4) waves in total -- two per CU, one dispatch
+// round -- and at most `max_groups` partials per head.
 void pick_split(int span, long long pairs, int max_groups, int* groups, int* rounds)
 {
     static const int kRounds[] = {1, 2, 3, 4, 6, 8};
+    constexpr int W = kStep2Waves;
     if (span <= 0) {
         *groups = 1;
         *rounds = 1;
@@ -80,13 +81,13 @@ void pick_split(int span, long long pairs, int max_groups, int* groups, int* rou
     const long long total_blocks = (long long)span * pairs;
     int pick = 5;
     for (int i = 0; i < 6; ++i)
-        if (total_blocks <= 4LL * 512 * kRounds[i]) {
+        if (total_blocks <= (long long)W * 512 * kRounds[i]) {
             pick = i;
             break;
         }
-    while (pick < 5 && ceil_div(span, 4 * kRounds[pick]) > max_groups) ++pick;
+    while (pick < 5 && ceil_div(span, W * kRounds[pick]) > max_groups) ++pick;
     *rounds = kRounds[pick];
-    *groups = ceil_div(span, 4 * kRounds[pick]);
+    *groups = ceil_div(span, W * kRounds[pick]);
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -135,7 +136,6 @@ nosa_status make_plan(const nosa_params* p, int batch, int max_seqlen_k, Plan* p
 
     const size_t B = (size_t)batch, pairs = B * P.Hkv;
     size_t off = 0;
-    P.off_counter2 = off; off += align256(pairs * sizeof(uint32_t));
     P.off_z = off;        off += align256(B * P.Hq * (size_t)P.zstride * sizeof(float));
     P.off_selpg = off;    off += align256(pairs * (size_t)(P.top_span > 0 ? P.top_span : 1) * sizeof(int2));
     P.off_sel = off;      off += align256(pairs * (size_t)P.max_sel * sizeof(int32_t));
@@ -170,7 +170,6 @@ Workspace carve(const Plan& pl, void* ws)
 {
     char* base = static_cast<char*>(ws);
     Workspace w;
-    w.counter2 = reinterpret_cast<uint32_t*>(base + pl.off_counter2);
     w.z = reinterpret_cast<float*>(base + pl.off_z);
     w.selpg = reinterpret_cast<int2*>(base + pl.off_selpg);
     w.sel = reinterpret_cast<int32_t*>(base + pl.off_sel);

@@ -45,25 +45,6 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Agent-coherent 8-byte stores / loads for data handed between workgroups.
-__device__ __forceinline__ void st_pair(void* p, float a, float b)
-{
-    const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
-    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ float2 ld_pair(const void* p)
-{
-    const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)),
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
-}
-
-__device__ __forceinline__ float ld_one(const float* p)
-{
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ------------------------------------------------------- page layouts ---
 // Every page of every pool is stored in the order the MFMA operands are
 // loaded, so that one 16-byte-per-lane load instruction of a wave reads 1 KB
@@ -217,29 +198,6 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ kb,
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) A.o[nt] = mfma16(pa, as_bf16x8(va[u][nt]), A.o[nt]);
     }
-}
-
-// Whole workgroup: "am I the last of `total` workgroups of this pair?"  Every
-// wave first waits for its (agent-coherent) stores to complete.  The last
-// workgroup resets the counter for the next call and invalidates its CU's L1
-// and its L2 once (agent-scope acquire), after which plain loads see every
-// other workgroup's stores.
-__device__ bool last_of_pair(uint32_t* counter, uint32_t total, int* flag_lds)
-{
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev =
-            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = prev == total - 1;
-        if (last) {
-            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        }
-        *flag_lds = last;
-    }
-    __syncthreads();
-    return *flag_lds != 0;
 }
 
 // ------------------------------------------------------------ selection ---

@@ -22,6 +22,7 @@ constexpr int kMaxBlocks = 8192;         // blocks per sequence (LDS of the sele
 constexpr int kMaxSplit = 64;            // attention partials per head (LDS of the merge)
 constexpr int kMaxWindowBlocks = 128;    // window blocks (one page per wave of step 1)
 constexpr int kStep1Waves = 8;           // waves of a step-1 workgroup
+constexpr int kStep2Waves = 4;           // waves of an attention workgroup
 
 inline int num_keys(int L) { return L >= kPoolK ? (L - kPoolK) / kPoolS + 1 : 0; }
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -45,13 +46,12 @@ struct Plan {
     int attend_groups = 0;  // workgroups per pair of the stand-alone attention
     int attend_rounds = 1;  // blocks per wave of the stand-alone attention
     // workspace layout (bytes from the start of the workspace)
-    size_t off_counter2 = 0, off_z = 0, off_selpg = 0,
+    size_t off_z = 0, off_selpg = 0,
            off_sel = 0, off_cnt = 0, off_po = 0, off_pml = 0, bytes = 0;
 };
 
 // Device pointers carved out of the caller's workspace.
 struct Workspace {
-    uint32_t* counter2;  // [pairs] hand-off counters of step 2 (zero between calls)
     float* z;            // [B][Hq][zstride] logits, log2 units
     int2* selpg;         // [pairs][top_span] (block, page) of the top-k picks
     int32_t* sel;        // [pairs][max_sel] kept blocks (when the caller passes none)

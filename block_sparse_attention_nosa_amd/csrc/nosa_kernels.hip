@@ -167,10 +167,10 @@ __device__ void store_wg_partial(CombineLds& sh, const AttnState& A, int G, size
             for (int w = 0; w < 4; ++w) acc[e] += wt[w] * sh.o[w][h][c0 + e];
         }
         const size_t prow = (head_row0 + h) * nsplit + split;
-        float* dst = po + prow * D + c0;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) st_pair(dst + e, acc[e], acc[e + 1]);
-        if ((tid & 15) == 0) st_pair(pml + prow, M, Lsum);
+        float4* dst = reinterpret_cast<float4*>(po + prow * D + c0);
+        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        if ((tid & 15) == 0) pml[prow] = make_float2(M, Lsum);
     }
 }
 
@@ -359,16 +359,19 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
     // The block-table row goes to LDS first (four loads in flight per
     // thread), so no key load below waits on a table load: loads complete in
     // order, so a table load issued behind other loads would wait for them.
-    for (int b0 = tid; b0 < nb; b0 += 4 * kPairThreads) {
+    // It is read up to the host bound max_nb (<= max_blocks_per_seq), so its
+    // loads and the query's do not wait for the length; entries past nb are
+    // never used.
+    for (int b0 = tid; b0 < a.max_nb; b0 += 4 * kPairThreads) {
         int v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int b = b0 + u * kPairThreads;
-            v[u] = b < nb ? trow[b] : 0;
+            v[u] = b < a.max_nb ? trow[b] : 0;
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            if (b0 + u * kPairThreads < nb) spg[b0 + u * kPairThreads] = v[u];
+            if (b0 + u * kPairThreads < a.max_nb) spg[b0 + u * kPairThreads] = v[u];
     }
 
     select_lds_clear<kPairThreads>(sh.sel);
@@ -564,107 +567,74 @@ struct Step2Args {
     float* po;
     float2* pml;
     int nsplit, split0;  // partial slots per head; this kernel writes [split0, split0+groups)
-    uint32_t* counter;   // [pairs]
-    float* out;
-    float* lse;
 };
 
-constexpr int kMergeBatch = 24;  // partial outputs loaded at once per thread
+// Combination of the nsplit partials (m_i, l_i, o_i) of each head row into
+// out = sum_i 2^(m_i - M) o_i / L and lse = (M + log2 L) ln 2, with
+// M = max_i m_i and L = sum_i 2^(m_i - M) l_i (empty rows: out 0, lse -inf).
+// One workgroup of 128 threads per row, thread c = channel c; partials are
+// taken 32 at a time with every load of a batch in flight, the running
+// (M, L, acc) rescaled between batches.  A launch of its own, so the
+// partials of every workgroup of the step are complete when it starts.
+constexpr int kMergeBatch = 32;
 
-struct MergeLds {
-    float2 ml[kMaxGroup][kMaxSplit];  // (max, sum) of every partial
-    float w[kMaxGroup][kMaxSplit];    // its weight exp2(m_i - M)
-    float M[kMaxGroup], L[kMaxGroup];
-};
-
-// Combine the nsplit partials of every head of the pair into out / lse.
-// Thread (head, 4 channels) issues the loads of its first batch of partial
-// outputs before the (m, l) of all partials go to LDS, so both travel at
-// once; 16 lanes per head then form the head's max, weights and sum with
-// lane shuffles.  Reads data of other workgroups: call after last_of_pair().
-__device__ void merge_pair(const Step2Args& a, int s, int g, MergeLds& sh)
+__global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ po,
+                                                    const float2* __restrict__ pml, int nsplit,
+                                                    float* __restrict__ out, float* __restrict__ lse)
 {
-    const int tid = threadIdx.x;
-    const int G = a.G, ns = a.nsplit;
-    const size_t row0 = (size_t)s * a.Hq + g * G;
-    const int nitems = G * 32;  // (head, 4 channels) items, <= 512
-    auto po_row = [&](int item) { return a.po + (row0 + (item >> 5)) * ns * D + (item & 31) * 4; };
-    float4 o[kMergeBatch];
-    if (tid < nitems) {
-        const float* op = po_row(tid);
-#pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u)
-            if (u < ns) o[u] = *reinterpret_cast<const float4*>(op + (size_t)u * D);
-    }
-    for (int e = tid; e < G * ns; e += 256) {
-        const int h = e / ns, i = e % ns;
-        sh.ml[h][i] = a.pml[(row0 + h) * ns + i];
-    }
-    __syncthreads();
-    {
-        // 16 lanes per head: lane j takes partials j, j + 16, ...
-        const int h = tid >> 4, j = tid & 15;
-        float M = -INFINITY;
-        if (h < G)
-            for (int i = j; i < ns; i += 16) M = fmaxf(M, sh.ml[h][i].x);
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 16));
-        float L = 0.f;
-        if (h < G)
-            for (int i = j; i < ns; i += 16) {
-                const float2 v = sh.ml[h][i];
-                const float w = (M == -INFINITY || v.x == -INFINITY) ? 0.f : fexp2(v.x - M);
-                sh.w[h][i] = w;
-                L += w * v.y;
-            }
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) L += __shfl_xor(L, off, 16);
-        if (h < G && j == 0) {
-            sh.M[h] = M;
-            sh.L[h] = L;
-        }
-    }
-    __syncthreads();
-    for (int item = tid; item < nitems; item += 256) {
-        const int h = item >> 5, c = (item & 31) * 4;
-        const float* op = po_row(item);
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const size_t row = blockIdx.x;
+    const int c = threadIdx.x;
+    const float2* ml = pml + row * nsplit;
+    const float* op = po + row * nsplit * D + c;
+    float M = -INFINITY, L = 0.f, acc = 0.f;
 #pragma unroll 1
-        for (int i0 = 0; i0 < ns; i0 += kMergeBatch) {
-            if (item != tid || i0 > 0) {
+    for (int i0 = 0; i0 < nsplit; i0 += kMergeBatch) {
+        float2 v[kMergeBatch];
+        float o[kMergeBatch];
 #pragma unroll
-                for (int u = 0; u < kMergeBatch; ++u)
-                    if (i0 + u < ns) o[u] = *reinterpret_cast<const float4*>(op + (size_t)(i0 + u) * D);
-            }
-#pragma unroll
-            for (int u = 0; u < kMergeBatch; ++u) {
-                if (i0 + u >= ns) break;
-                const float w = sh.w[h][i0 + u];
-                acc.x += w * o[u].x;
-                acc.y += w * o[u].y;
-                acc.z += w * o[u].z;
-                acc.w += w * o[u].w;
-            }
+        for (int u = 0; u < kMergeBatch; ++u) {
+            const bool ok = i0 + u < nsplit;
+            v[u] = ok ? ml[i0 + u] : make_float2(-INFINITY, 0.f);
+            o[u] = ok ? op[(size_t)(i0 + u) * D] : 0.f;
         }
-        const float L = sh.L[h];
-        const bool empty = !(L > 0.f);
-        const float inv = empty ? 0.f : 1.f / L;
-        *reinterpret_cast<float4*>(a.out + (row0 + h) * D + c) =
-            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-        if (a.lse && c == 0) a.lse[row0 + h] = empty ? -INFINITY : (sh.M[h] + log2f(L)) * kLn2;
+        float Mb = M;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) Mb = fmaxf(Mb, v[u].x);
+        if (Mb == -INFINITY) continue;
+        const float r = M == -INFINITY ? 0.f : fexp2(M - Mb);
+        L *= r;
+        acc *= r;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            const float w = v[u].x == -INFINITY ? 0.f : fexp2(v[u].x - Mb);
+            L += w * v[u].y;
+            acc += w * o[u];
+        }
+        M = Mb;
     }
+    const bool empty = !(L > 0.f);
+    out[row * D + c] = empty ? 0.f : acc / L;
+    if (lse && c == 0) lse[row] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
 }
 
-// Workgroup = 4 waves; wave w handles entries (grp*rounds + rr)*4 + w of the
-// pair's list, rr < rounds, one 64-token block at a time.
-template <bool kDecode, int R>
-__global__ __launch_bounds__(256) void step2_kernel(Step2Args a)
+static hipError_t launch_merge(const Plan& pl, const Workspace& w, int nsplit, float* out, float* lse,
+                               hipStream_t stream)
 {
-    __shared__ union {
-        CombineLds comb;
-        MergeLds merge;
-    } sh;
-    __shared__ int flag;
+    const int rows = pl.B * pl.Hq;
+    if (rows > 0)
+        hipLaunchKernelGGL(merge_kernel, dim3(rows), dim3(D), 0, stream, w.po, w.pml, nsplit, out,
+                           lse);
+    return hipGetLastError();
+}
+
+// Workgroup = kStep2Waves (4) waves; wave w handles entries
+// (grp*rounds + rr)*4 + w of the pair's list, rr < rounds, one 64-token
+// block at a time.
+static_assert(kStep2Waves == 4, "store_wg_partial combines four waves");
+template <bool kDecode, int R>
+__global__ __launch_bounds__(kStep2Waves * 64) void step2_kernel(Step2Args a)
+{
+    __shared__ CombineLds sh;
     const int pair = blockIdx.x / a.groups, grp = blockIdx.x % a.groups;
     const int s = pair / a.Hkv, g = pair % a.Hkv;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -680,7 +650,7 @@ __global__ __launch_bounds__(256) void step2_kernel(Step2Args a)
     load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-        const int idx = (grp * R + rr) * 4 + wave;
+        const int idx = (grp * R + rr) * kStep2Waves + wave;
         int b = -1, page = -1;
         if (kDecode) {
             if (idx < a.span) {
@@ -697,10 +667,7 @@ __global__ __launch_bounds__(256) void step2_kernel(Step2Args a)
         const uint16_t* vb = a.v_pool + ((size_t)page * a.Hkv + g) * D * BS;
         attend_page(kb, vb, L - b * BS, qb, a.scale_log2, r, kq, A);
     }
-    store_wg_partial(sh.comb, A, a.G, (size_t)s * a.Hq + g * a.G, a.nsplit, a.split0 + grp, a.po,
-                     a.pml);
-    if (!last_of_pair(a.counter + pair, (uint32_t)a.groups, &flag)) return;
-    merge_pair(a, s, g, sh.merge);
+    store_wg_partial(sh, A, a.G, (size_t)s * a.Hq + g * a.G, a.nsplit, a.split0 + grp, a.po, a.pml);
 }
 
 // ------------------------------------------------------ select (alone) ---
@@ -745,12 +712,12 @@ template <bool kDecode>
 static hipError_t launch_step2(const Step2Args& b, int grid, hipStream_t stream)
 {
     switch (b.rounds) {
-        case 1: hipLaunchKernelGGL((step2_kernel<kDecode, 1>), dim3(grid), dim3(256), 0, stream, b); break;
-        case 2: hipLaunchKernelGGL((step2_kernel<kDecode, 2>), dim3(grid), dim3(256), 0, stream, b); break;
-        case 3: hipLaunchKernelGGL((step2_kernel<kDecode, 3>), dim3(grid), dim3(256), 0, stream, b); break;
-        case 4: hipLaunchKernelGGL((step2_kernel<kDecode, 4>), dim3(grid), dim3(256), 0, stream, b); break;
-        case 6: hipLaunchKernelGGL((step2_kernel<kDecode, 6>), dim3(grid), dim3(256), 0, stream, b); break;
-        default: hipLaunchKernelGGL((step2_kernel<kDecode, 8>), dim3(grid), dim3(256), 0, stream, b); break;
+        case 1: hipLaunchKernelGGL((step2_kernel<kDecode, 1>), dim3(grid), dim3(kStep2Waves * 64), 0, stream, b); break;
+        case 2: hipLaunchKernelGGL((step2_kernel<kDecode, 2>), dim3(grid), dim3(kStep2Waves * 64), 0, stream, b); break;
+        case 3: hipLaunchKernelGGL((step2_kernel<kDecode, 3>), dim3(grid), dim3(kStep2Waves * 64), 0, stream, b); break;
+        case 4: hipLaunchKernelGGL((step2_kernel<kDecode, 4>), dim3(grid), dim3(kStep2Waves * 64), 0, stream, b); break;
+        case 6: hipLaunchKernelGGL((step2_kernel<kDecode, 6>), dim3(grid), dim3(kStep2Waves * 64), 0, stream, b); break;
+        default: hipLaunchKernelGGL((step2_kernel<kDecode, 8>), dim3(grid), dim3(kStep2Waves * 64), 0, stream, b); break;
     }
     return hipGetLastError();
 }
@@ -888,10 +855,9 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
     b.pml = w.pml;
     b.nsplit = pl.nsplit;
     b.split0 = pl.win_groups;
-    b.counter = w.counter2;
-    b.out = out;
-    b.lse = lse;
-    return launch_step2<true>(b, pl.B * pl.Hkv * pl.top_groups, stream);
+    e = launch_step2<true>(b, pl.B * pl.Hkv * pl.top_groups, stream);
+    if (e != hipSuccess) return e;
+    return launch_merge(pl, w, pl.nsplit, out, lse, stream);
 }
 
 hipError_t launch_attend(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
@@ -920,10 +886,9 @@ hipError_t launch_attend(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
     b.pml = w.pml;
     b.nsplit = pl.attend_groups;
     b.split0 = 0;
-    b.counter = w.counter2;
-    b.out = out;
-    b.lse = lse;
-    return launch_step2<false>(b, pl.B * pl.Hkv * pl.attend_groups, stream);
+    hipError_t e = launch_step2<false>(b, pl.B * pl.Hkv * pl.attend_groups, stream);
+    if (e != hipSuccess) return e;
+    return launch_merge(pl, w, pl.attend_groups, out, lse, stream);
 }
 
 hipError_t launch_select(const Plan& pl, const int32_t* cu_k, const int32_t* cu_q, int max_seqlen_q,

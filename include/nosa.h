@@ -33,12 +33,22 @@
  *     HIP launch NOSA_ERR_HIP.  Nothing aborts.
  *   - No global state: calls on different streams may run concurrently as
  *     long as they do not share output or workspace buffers.
- *   - Workspace: device memory of nosa_workspace_size() bytes that must be
- *     zero-filled before its first use (e.g. allocated with torch.zeros).
- *     Its head holds per-(sequence, KV head) hand-off counters that every
- *     call returns to zero, so a workspace is reused across calls without
- *     clearing; the rest is scratch.  Calls sharing a workspace must be
+ *   - Workspace: device scratch memory of nosa_workspace_size() bytes, with
+ *     no initial contents required and none kept between calls; reused
+ *     across calls without clearing.  Calls sharing a workspace must be
  *     ordered (same stream): overlapping calls on one workspace race.
+ *   - Queries: cu_seqlens_q NULL is decode (one query per sequence, row s of
+ *     q, at position L_s - 1).  Otherwise cu_seqlens_q (device [batch+1])
+ *     packs Lq_s <= L_s queries per sequence, the last Lq_s positions
+ *     L_s - Lq_s .. L_s - 1 of its context (a prefill chunk), and the chunk
+ *     is cut into query blocks of 64 consecutive queries from its start;
+ *     query block r ends at position p_r = L_s - Lq_s + min(64r + 64, Lq_s) - 1
+ *     and sees the blocks nb_r = p_r / block_size + 1 that hold tokens
+ *     <= p_r.  [Page "NOSA技术架构解析", sections 1.1 and 1.3: besides full
+ *     prefill with sparse decode, a mode runs prefill sparse as well; the
+ *     64-query block is this library's unit for it, the decode step being
+ *     the one-query case.]  max_qblk = ceil(max_seqlen_q / 64) (1 for
+ *     decode).
  *
  * Supported shapes on the GPU: head_dim 128, block_size 64, kernel 32,
  * stride 16, window a multiple of 64 of at most 8192 tokens,
@@ -145,18 +155,17 @@ nosa_status nosa_compress_keys(const nosa_params* params, const nosa_paged_kv* k
                                int32_t batch, int32_t max_seqlen_k, void* stream);
 
 /* Block importance [pages "NOSA-1B 性能基准全解析" 三.3 and "NOSA-1B 模型家族全景"
- * core principle].  For the decode query of each sequence (row s of q, at
- * position L_s - 1) and each KV head g:
- *   z_h[j] = scale * q_h . Kc_j for the G heads h of g and every key j < n_c(L_s);
- *   sigma[j] = sum_h softmax_h(z_h)[j];
- *   block_scores[s][0][g][b] = mean of sigma over the keys overlapping block b
- *   (keys 4b-1 .. 4b+3 that exist), -inf if none, for b < nb(L_s); -inf
- *   padding up to max_nb = ceil(max_seqlen_k / block_size).
- * q: device [batch][Hq][d] bf16.  block_scores: device fp32
- * [batch][max_qblk][Hkv][max_nb] with max_qblk = ceil(max_seqlen_q/block_size)
- * (1 for decode).  cu_seqlens_q must be NULL (decode) in this build; a
- * non-NULL value gives NOSA_ERR_UNSUPPORTED.  Kc must be valid for L_s tokens.
- * Needs a zero-initialised `workspace` of nosa_workspace_size bytes. */
+ * core principle].  For each row (sequence s, query block r, KV head g), with
+ * the query block's queries i (one for decode) and the G heads h of g:
+ *   z_ih[j] = scale * q_ih . Kc_j for every key j < n_c(p_r + 1);
+ *   sigma[j] = sum_i sum_h softmax_ih(z_ih)[j];
+ *   block_scores[s][r][g][b] = mean of sigma over the keys overlapping block b
+ *   (keys 4b-1 .. 4b+3 that exist), -inf if none, for b < nb_r; -inf padding
+ *   up to max_nb = ceil(max_seqlen_k / block_size); rows of absent query
+ *   blocks are all -inf.
+ * q: device [total queries][Hq][d] bf16 (decode: [batch][Hq][d]).
+ * block_scores: device fp32 [batch][max_qblk][Hkv][max_nb].  Kc must be
+ * valid for L_s tokens.  Needs a `workspace` of nosa_workspace_size bytes. */
 nosa_status nosa_block_scores(const nosa_params* params, const nosa_paged_kv* kv,
                               const nosa_bf16* q, const int32_t* cu_seqlens_q,
                               const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
@@ -165,27 +174,29 @@ nosa_status nosa_block_scores(const nosa_params* params, const nosa_paged_kv* kv
 
 /* Block selection [page "NOSA-1B 性能基准全解析", section 三.2: a 1024-token window
  * of 64-token blocks is always attended and TopK adds the 64 best blocks].
- * For each row (sequence s, KV head g): the window is the last
- * min(nb, window/block_size) blocks; among the earlier blocks the
- * min(topk, count) with the largest block_scores are added, ties going to the
- * lower block index.  sel_idx receives the kept block ids in ascending order,
- * padded with -1 to max_sel = topk + window/block_size; sel_count the number
- * kept (= min(nb, topk + window/block_size)).
+ * For each row (sequence s, query block r, KV head g) with nb = nb_r blocks:
+ * the window is the last min(nb, window/block_size) blocks; among the
+ * earlier blocks the min(topk, count) with the largest block_scores are
+ * added, ties going to the lower block index.  sel_idx receives the kept
+ * block ids in ascending order, padded with -1 to
+ * max_sel = topk + window/block_size; sel_count the number kept
+ * (= min(nb, topk + window/block_size); 0 for absent query blocks).
  * block_scores: device fp32 [batch][max_qblk][Hkv][max_nb] as produced by
  * nosa_block_scores.  sel_idx: device int32 [batch][max_qblk][Hkv][max_sel];
- * sel_count: device int32 [batch][max_qblk][Hkv].  cu_seqlens_q: NULL. */
+ * sel_count: device int32 [batch][max_qblk][Hkv]. */
 nosa_status nosa_select_blocks(const nosa_params* params, const float* block_scores,
                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                int32_t* sel_idx, int32_t* sel_count, void* stream);
 
 /* Exact attention over the kept blocks [page "NOSA-1B 性能基准全解析", 三.2-三.3].
- * For sequence s and query head h (KV head g = h / G): softmax over the
- * tokens t < L_s of the blocks listed in sel_idx[s][0][g][0 .. sel_count) of
- * scale * q_h . K[t], applied to V.  out: device fp32 [batch][Hq][d];
- * lse: device fp32 [batch][Hq] (natural log of the softmax denominator) or
- * NULL.  Block ids must be distinct and < nb(L_s).  cu_seqlens_q: NULL.
- * Needs a zero-initialised `workspace` (see above). */
+ * For query i of query block r of sequence s (at position p) and query head
+ * h (KV head g = h / G): softmax over the tokens t <= p of the blocks listed
+ * in sel_idx[s][r][g][0 .. sel_count) of scale * q_ih . K[t], applied to V
+ * (decode: p = L_s - 1, r = 0).  out: device fp32 [total queries][Hq][d];
+ * lse: device fp32 [total queries][Hq] (natural log of the softmax
+ * denominator, -inf for a query that sees no token) or NULL.  Block ids must
+ * be distinct and < nb_r.  Needs a `workspace` (see above). */
 nosa_status nosa_sparse_attend(const nosa_params* params, const nosa_paged_kv* kv,
                                const nosa_bf16* q, const int32_t* cu_seqlens_q,
                                const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
@@ -203,7 +214,7 @@ nosa_status nosa_sparse_attend(const nosa_params* params, const nosa_paged_kv* k
  * L_s - 1 (its K/V must already be in the pages).  out / lse as in
  * nosa_sparse_attend (lse may be NULL).  sel_idx / sel_count / block_scores
  * are optional outputs (NULL = not written) with the layouts above
- * (max_qblk = 1).  Needs a zero-initialised `workspace` (see above). */
+ * (max_qblk = 1).  Needs a `workspace` (see above). */
 nosa_status nosa_decode_step(const nosa_params* params, const nosa_paged_kv* kv,
                              const nosa_bf16* q, const int32_t* cu_seqlens_k, int32_t batch,
                              int32_t max_seqlen_k, float* out, float* lse, int32_t* sel_idx,

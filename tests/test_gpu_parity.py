@@ -228,14 +228,13 @@ def test_stream_argument_is_honoured():
     assert np.array_equal(out.cpu().numpy(), ref["out"])
 
 
-def test_workspace_counters_return_to_zero_and_reuse():
-    """Every call leaves the workspace's hand-off counters at zero, so one
-    workspace serves consecutive calls of different sizes."""
+def test_workspace_reuse_across_sizes():
+    """One workspace (sized for the largest call) serves consecutive calls of
+    different sizes: nothing a call leaves behind changes the next one."""
     log("case: workspace reuse")
     big = make_case(_wl([5000, 3000, 4000], topk=6, planted=2, seed=31))
     small = make_case(_wl([1500], topk=6, planted=1, seed=32))
     ws = workspace(big, 5000)
-    pairs_big = 3 * 2
     for c in (big, small, big):
         lens = live_lens(c, 0)
         build_kc(c, [L - 1 for L in lens])
@@ -244,9 +243,6 @@ def test_workspace_counters_return_to_zero_and_reuse():
         nosa.nosa_decode_step(c.p, c.kv, c.inp["q"].cuda(), cu_dev(lens), c.B, max(lens), out,
                               lse, ws)
         torch.cuda.synchronize()
-        # the hand-off counters of the attention step sit at offset 0
-        head = ws[:4 * pairs_big].cpu().numpy()
-        assert not head.any(), "counters not reset"
         o = oracle_step(c, 0)
         if c is small:
             np.testing.assert_array_less(np.abs(out.cpu().numpy() - o["out"]), 1e-2)

@@ -21,6 +21,15 @@ Printed: one JSON line with the throughput (decode tokens/s = batch / step
 time), the roofline of the dominant kernel (the sparse attention, timed with
 HIP events around its own launches on the launch stream) and the CPU
 reference's throughput on a bounded sample of the same workload.
+
+Traffic counters (kept out of the timed run):
+    rocprofv3 --pmc FETCH_SIZE -d DIR_F -o run --output-format csv -- python bench.py --pmc-probe
+    rocprofv3 --pmc WRITE_SIZE -d DIR_W -o run --output-format csv -- python bench.py --pmc-probe
+    python bench.py --pmc-summary DIR_F DIR_W > profiles/attention-decode-b8-16k_traffic.md
+The probe runs a plain copy of 256 MiB (calibration: bytes per counter unit)
+and the library's kernels on the default workload; the summary scales each
+kernel's counters by the copy's factors.  The JSON line reports that traffic
+only while the kernel sources hash to the value recorded with it.
 """
 from __future__ import annotations
 
@@ -35,6 +44,36 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
 LAYERS = 8
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention-decode-b8-16k_traffic.md")
+CALIB_BYTES = 256 << 20   # bytes read (and written) by the calibration copy
+
+
+def sources_sha256():
+    """Hash of the kernel sources (the traffic figures are valid for these)."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "block_sparse_attention_nosa_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Bytes per attention launch from the committed counter summary, or None
+    when it is missing or was taken on other kernel sources."""
+    try:
+        vals = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if line.startswith("- ") and ": " in line:
+                    k, v = line[2:].strip().split(": ", 1)
+                    vals[k] = v.strip("` ")
+        if vals.get("sources_sha256") != sources_sha256():
+            return None
+        return int(vals["attention_traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes(w, lens, append: bool):
@@ -86,7 +125,17 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run the calibration copy and the kernels once each for counters")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs of --pmc-probe")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="table of a rocprofv3 --kernel-trace --stats csv run")
     args = ap.parse_args()
+    if args.pmc_summary:
+        return pmc_summary(*args.pmc_summary)
+    if args.trace_summary:
+        return trace_summary(args.trace_summary)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -119,6 +168,9 @@ def main():
     stream = torch.cuda.current_stream()
     print(f"[bench] setup {time.time() - t_setup:.1f}s; workload {w.name}: B={B} heads={Hq}/{Hkv} "
           f"L={w.lens[0]}..{maxL} topk={w.topk} layers={LAYERS}", file=sys.stderr, flush=True)
+
+    if args.pmc_probe:
+        return pmc_probe(w, layers, lens_at, cu_at, maxL, ws, out, lse, sels, cnts, qs)
 
     def step(i):
         li = i % LAYERS
@@ -217,7 +269,7 @@ def main():
                      "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": {"kernel": "step2_kernel (nosa_sparse_attend: attention over the kept pages + merge)", "bound": "hbm",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "us_per_launch": round(us_attn, 3),
                      "algorithmic_bytes_per_launch": int(np.mean(attn_bytes))},
         "cpu_baseline": cpu,
@@ -312,6 +364,117 @@ def prefill_main(w, args):
                         "traffic": None, "scoring_gflop": round(fs / 1e9, 2),
                         "attention_gflop": round(fa / 1e9, 2)}}
     print(json.dumps(res), flush=True)
+
+
+def pmc_probe(w, layers, lens_at, cu_at, maxL, ws, out, lse, sels, cnts, qs):
+    """One pass of every kernel for counter collection: the calibration copy
+    (CALIB_BYTES read, CALIB_BYTES written), then per layer one decode step
+    and one stand-alone attention over its selection."""
+    import torch
+    from block_sparse_attention_nosa_amd import nosa
+    a = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        torch.bitwise_not(a, out=b)  # a kernel used nowhere else: reads a, writes b
+    torch.cuda.synchronize()
+    B = w.batch
+    for li, L in enumerate(layers):
+        nosa.nosa_decode_step(L["p"], L["kv"], qs[li], cu_at[0], B, maxL, out, lse, ws,
+                              sel_idx=sels[li], sel_count=cnts[li])
+        nosa.nosa_sparse_attend(L["p"], L["kv"], qs[li], None, cu_at[0], B, 1, maxL, sels[li],
+                                cnts[li], out, lse, ws)
+    torch.cuda.synchronize()
+    attn = algorithmic_bytes(w, lens_at[0], False)[1]
+    print(f"[pmc-probe] done; attention algorithmic bytes per launch {attn}", file=sys.stderr)
+
+
+def _pmc_rows(d, counter):
+    """(kernel name, value) per dispatch of one counter from a rocprofv3 csv run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def pmc_summary(fetch_dir, write_dir):
+    """Markdown summary of FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel,
+    scaled to bytes by the calibration copy, and the attention's traffic per
+    launch (its attention kernel plus its merge)."""
+    import numpy as np
+    from block_sparse_attention_nosa_amd import synth
+    w = synth.config(2)
+    attn_alg = algorithmic_bytes(w, w.lens, False)[1]
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for name, v in _pmc_rows(d, counter):
+            per.setdefault(name, {}).setdefault(counter, []).append(v)
+    calib = [n for n in per if "bitwise_not" in n.lower() or "BitwiseNot" in n]
+    if not calib:
+        raise SystemExit("calibration copy kernel not found")
+    c = per[calib[0]]
+    f_fetch = CALIB_BYTES / (np.median(c["FETCH_SIZE"]) * 1024.0)
+    f_write = CALIB_BYTES / (np.median(c["WRITE_SIZE"]) * 1024.0)
+    lines = ["# HBM traffic of the decode-b8-16k kernels (rocprofv3 counters)", "",
+             "Commands (from the repository root):", "",
+             "    rocprofv3 --pmc FETCH_SIZE -d DIR_F -o run --output-format csv -- python3 bench.py --pmc-probe",
+             "    rocprofv3 --pmc WRITE_SIZE -d DIR_W -o run --output-format csv -- python3 bench.py --pmc-probe",
+             "    python3 bench.py --pmc-summary DIR_F DIR_W", "",
+             f"Calibration: a plain copy reading and writing {CALIB_BYTES >> 20} MiB; "
+             f"bytes per counter KiB: fetch {f_fetch * 1024:.1f}, write {f_write * 1024:.1f} "
+             f"(factors {f_fetch:.3f} / {f_write:.3f} of the nominal 1024).", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched MB | written MB |",
+             "|---|---:|---:|---:|---:|---:|"]
+    traffic = {}
+    for name in sorted(per):
+        v = per[name]
+        if "FETCH_SIZE" not in v or "WRITE_SIZE" not in v:
+            continue
+        if not ("nosa::" in name or name in calib):
+            continue
+        fk, wk = float(np.mean(v["FETCH_SIZE"])), float(np.mean(v["WRITE_SIZE"]))
+        fb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
+        traffic[name] = fb + wb
+        lines.append(f"| `{name[:90]}` | {len(v['FETCH_SIZE'])} | {fk:.0f} | {wk:.0f} | "
+                     f"{fb / 1e6:.2f} | {wb / 1e6:.2f} |")
+    attn_k = [n for n in traffic if "step2_kernel<false" in n]
+    merge_k = [n for n in traffic if "merge_kernel" in n]
+    if not attn_k or not merge_k:
+        raise SystemExit("attention kernels not found")
+    attn_t = traffic[attn_k[0]] + traffic[merge_k[0]]
+    lines += ["", "The attention launch (nosa_sparse_attend) is its attention kernel plus its merge "
+              "kernel; the merge row averages the dispatches of both entry points.", "",
+              f"- attention_traffic_bytes_per_launch: {int(attn_t)}",
+              f"- attention_algorithmic_bytes_per_launch: {int(attn_alg)}",
+              f"- traffic_over_algorithmic: {attn_t / attn_alg:.3f}",
+              f"- sources_sha256: {sources_sha256()}"]
+    print("\n".join(lines))
+
+
+def trace_summary(d):
+    """Markdown rows (library kernels) of a rocprofv3 kernel_stats.csv."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    print("| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |")
+    print("|---|---:|---:|---:|---:|---:|")
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            if "nosa::" not in r["Name"]:
+                continue
+            name = r["Name"].split("(")[0] if r["Name"].startswith("nosa::") else r["Name"].split("(nosa")[0]
+            print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                  f"{float(r['Percentage']):.1f}% |")
 
 
 def cpu_baseline(w, layer, lens_at, budget_s):

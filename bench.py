@@ -59,9 +59,12 @@ def sources_sha256():
     return h.hexdigest()
 
 
-def recorded_traffic():
+def recorded_traffic(workload):
     """Bytes per attention launch from the committed counter summary, or None
-    when it is missing or was taken on other kernel sources."""
+    when it is missing, covers another workload or was taken on other kernel
+    sources."""
+    if workload != "decode-b8-16k":
+        return None
     try:
         vals = {}
         with open(TRAFFIC_FILE) as fh:
@@ -247,8 +250,10 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(w, layers[0], lens_at, args.cpu_sample_seconds)
 
+    ctx_name = (f"{round((w.lens[0] - 1) / 1024)}K" if len(set(w.lens)) == 1 else "varlen")
     res = {
-        "metric": "sparse-attn decode tokens/s at 16K ctx, batch 8; achieved HBM GB/s vs peak",
+        "metric": f"sparse-attn decode tokens/s at {ctx_name} ctx, batch {B}; "
+                  "achieved HBM GB/s vs peak",
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -269,7 +274,7 @@ def main():
                      "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": {"kernel": "step2_kernel (nosa_sparse_attend: attention over the kept pages + merge)", "bound": "hbm",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(w.name),
                      "us_per_launch": round(us_attn, 3),
                      "algorithmic_bytes_per_launch": int(np.mean(attn_bytes))},
         "cpu_baseline": cpu,

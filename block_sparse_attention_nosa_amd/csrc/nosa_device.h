@@ -217,6 +217,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask)
 }
 
 constexpr int kSelMaxRounds = kMaxBlocks / 256;  // candidate rounds of a 4-wave selector
+constexpr int kSelKeyRounds = 8;                  // candidate rounds whose keys stay in registers
 
 struct SelectLds {
     float lse[kMaxGroup];
@@ -254,7 +255,9 @@ __device__ __forceinline__ int wave_incl_scan(int x)
 //                         (-1, -1) padded; *ntop_out.
 // Must be called by all NW*64 threads, sh.hist zeroed and a barrier passed
 // since; sI holds the importance in LDS; page ids come from `pages` (LDS copy
-// of the block-table row) when given, else from `trow`.
+// of the block-table row) when given, else from `trow`.  With KEYS_GIVEN the
+// caller passes the order keys of its candidates i*NT + tid, i < KR, in
+// keys[] (those rounds are then not read from sI).
 //
 // The k-th largest order key is found a byte at a time from the top: one
 // LDS histogram of the next byte over the candidates that still share the
@@ -263,8 +266,9 @@ __device__ __forceinline__ int wave_incl_scan(int x)
 // ones still needed, so for distinct keys it usually ends after two bytes.
 // The taken candidates are then compacted in ascending order from per-wave
 // ballot counts (one barrier, two when tied keys straddle the cut).
-template <int NW>
-__device__ __forceinline__ void select_blocks_wg(const float* sI, int nb, int wblocks, int topk, SelectLds& sh,
+template <int NW, bool KEYS_GIVEN>
+__device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds], const float* sI, int nb,
+                                                 int wblocks, int topk, SelectLds& sh,
                                                  int32_t* __restrict__ sel_out, int32_t* __restrict__ cnt_out,
                                                  int max_sel, int2* __restrict__ selpg,
                                                  int32_t* __restrict__ ntop_out, int top_span,
@@ -278,14 +282,16 @@ __device__ __forceinline__ void select_blocks_wg(const float* sI, int nb, int wb
     const bool partial = kk > 0 && kk < ncand;
     const int rounds = (ncand + NT - 1) / NT;  // <= kMaxBlocks / 256 = kSelMaxRounds
     // candidate keys of this thread (candidate round*NT + tid), first KR rounds
-    constexpr int KR = 8;
-    uint32_t keys[KR];
-    // all KR reads issued together; indexes clamped into [0, ncand) (sI has
-    // at least one entry), lanes past ncand are masked wherever keys are used
+    constexpr int KR = kSelKeyRounds;
+    if (!KEYS_GIVEN) {
+        // all KR reads issued together; indexes clamped into [0, ncand) (sI
+        // has at least one entry), lanes past ncand are masked wherever keys
+        // are used
 #pragma unroll
-    for (int i = 0; i < KR; ++i) {
-        const int b = i * NT + tid;
-        keys[i] = order_key(sI[b < ncand ? b : (ncand > 0 ? ncand - 1 : 0)]);
+        for (int i = 0; i < KR; ++i) {
+            const int b = i * NT + tid;
+            keys[i] = order_key(sI[b < ncand ? b : (ncand > 0 ? ncand - 1 : 0)]);
+        }
     }
     auto key_at = [&](int i) -> uint32_t {
         if (i < KR) {

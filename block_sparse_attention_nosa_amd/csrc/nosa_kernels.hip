@@ -229,29 +229,37 @@ __device__ void store_wg_partial8(CombineLds& sh, AttnState& A, int G, size_t he
 
 // Block importance of the pair into sI[0 .. nb): mean over the keys
 // overlapping block b (keys 4b-1 .. 4b+3 that exist) of
-// sigma[j] = sum_h exp2(z_h[j] - lse_h).  Each thread takes four consecutive
-// keys (one float4 of z per head, eight heads per batch of loads) and adds
-// their sum to block j/4 and the last key's sigma to block j/4 + 1: two
-// additions per block, so the result does not depend on their order.
-// z (in LDS or global memory) was written by this workgroup (call after a
-// barrier).  Also writes
-// scores_out.  Must be called by all NT threads.
+// sigma[j] = sum_h 2^(z_h[j] - lse_h).  Thread tid computes whole blocks
+// b = tid + i NT from their five keys (key 4b-1 is also its left neighbour's
+// last key), so no block needs a second contribution; the order key of each
+// block it computed is returned in keys[i] (i < kSelKeyRounds, 0 past nb).
+// z (in LDS or global memory, at least 4 max_nb + 4 entries per head; keys
+// at or past nc are never read) was written by this workgroup (call after a
+// barrier).  Also writes scores_out.  All NT threads; ends with a barrier.
 template <int NT>
-__device__ __forceinline__ void pool_pair(const float* __restrict__ zg, int zstride, const float* lse, int G,
-                          int nc, int nb, float* sI, float* __restrict__ scores_out, int max_nb)
+__device__ __forceinline__ void pool_pair(const float* __restrict__ zg, int zstride, const float* lse,
+                                          int G, int nc, int nb, float* sI,
+                                          float* __restrict__ scores_out, int max_nb,
+                                          uint32_t (&keys)[kSelKeyRounds])
 {
     const int tid = threadIdx.x;
-    for (int b = tid; b < nb; b += NT) sI[b] = 0.f;
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSelKeyRounds; ++i) keys[i] = 0u;
 #pragma unroll 1
-    for (int j0 = 4 * tid; j0 < nc; j0 += 4 * NT) {
-        float sg[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0, b = tid; b < nb; ++i, b += NT) {
+        const int j0 = 4 * b;
+        float sg[4] = {0.f, 0.f, 0.f, 0.f}, sp = 0.f;
 #pragma unroll 1
         for (int h0 = 0; h0 < G; h0 += 8) {
             float4 zz[8];
+            float zp[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (h0 + u < G) zz[u] = *reinterpret_cast<const float4*>(zg + (size_t)(h0 + u) * zstride + j0);
+                if (h0 + u < G) {
+                    const float* zr = zg + (size_t)(h0 + u) * zstride;
+                    zz[u] = *reinterpret_cast<const float4*>(zr + j0);
+                    zp[u] = b > 0 ? zr[j0 - 1] : 0.f;
+                }
 #pragma unroll
             for (int u = 0; u < 8; ++u)
                 if (h0 + u < G) {
@@ -260,22 +268,20 @@ __device__ __forceinline__ void pool_pair(const float* __restrict__ zg, int zstr
                     sg[1] += fexp2(zz[u].y - lh);
                     sg[2] += fexp2(zz[u].z - lh);
                     sg[3] += fexp2(zz[u].w - lh);
+                    sp += fexp2(zp[u] - lh);
                 }
         }
-        const int b = j0 >> 2;
-        float own = 0.f;
+        const int jlo = max(j0 - 1, 0), jhi = min(j0 + 3, nc - 1);
+        float sum = (b > 0 && j0 - 1 < nc) ? sp : 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (j0 + e < nc) own += sg[e];
-        atomicAdd(&sI[b], own);
-        if (j0 + 3 < nc && b + 1 < nb) atomicAdd(&sI[b + 1], sg[3]);
-    }
-    __syncthreads();
-    for (int b = tid; b < nb; b += NT) {
-        const int jlo = max(4 * b - 1, 0), jhi = min(4 * b + 3, nc - 1);
-        const float I = jlo <= jhi ? sI[b] / (float)(jhi - jlo + 1) : -INFINITY;
+            if (j0 + e < nc) sum += sg[e];
+        const float I = jlo <= jhi ? sum / (float)(jhi - jlo + 1) : -INFINITY;
         sI[b] = I;
         if (scores_out) scores_out[b] = I;
+#pragma unroll
+        for (int r = 0; r < kSelKeyRounds; ++r)
+            if (r == i) keys[r] = order_key(I);
     }
     if (scores_out)
         for (int b = nb + tid; b < max_nb; b += NT) scores_out[b] = -INFINITY;
@@ -485,22 +491,29 @@ __device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
     if (!ZL) __builtin_amdgcn_s_waitcnt(0);  // this wave's logits have reached L2
     __syncthreads();
     if (tid < a.G) {
-        float m = -INFINITY, acc = 0.f;
+        // all sixteen LDS reads first, then independent exponentials
+        float mw[kPairWaves], sw[kPairWaves];
 #pragma unroll
         for (int w = 0; w < kPairWaves; ++w) {
-            const float mw = sh.m[w][tid], sw = sh.s[w][tid];
-            if (!(sw > 0.f)) continue;
-            const float mn = fmaxf(m, mw);
-            acc = acc * fexp2(m - mn) + sw * fexp2(mw - mn);
-            m = mn;
+            mw[w] = sh.m[w][tid];
+            sw[w] = sh.s[w][tid];
         }
+        float m = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kPairWaves; ++w)
+            if (sw[w] > 0.f) m = fmaxf(m, mw[w]);
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kPairWaves; ++w)
+            if (sw[w] > 0.f) acc += sw[w] * fexp2(mw[w] - m);
         sh.sel.lse[tid] = m + log2f(acc);
     }
     __syncthreads();
+    uint32_t keys[kSelKeyRounds];
     pool_pair<kPairThreads>(zb, zs, sh.sel.lse, a.G, nc, nb, sI,
-                            a.scores_out ? a.scores_out + pair * a.max_nb : nullptr, a.max_nb);
+                            a.scores_out ? a.scores_out + pair * a.max_nb : nullptr, a.max_nb, keys);
     if (!a.do_select) return;
-    select_blocks_wg<kPairWaves>(sI, nb, a.wblocks, a.topk, sh.sel,
+    select_blocks_wg<kPairWaves, true>(keys, sI, nb, a.wblocks, a.topk, sh.sel,
                                  a.sel_out ? a.sel_out + pair * a.max_sel : nullptr,
                                  a.cnt_out ? a.cnt_out + pair : nullptr, a.max_sel,
                                  a.selpg ? a.selpg + pair * a.top_span : nullptr, nullptr,
@@ -702,7 +715,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
     for (int b = threadIdx.x; b < nb; b += 256) sI[b] = scores_in[pair * max_nb + b];
     select_lds_clear<256>(sh);
     __syncthreads();
-    select_blocks_wg<4>(sI, nb, wblocks, topk, sh, sel + pair * max_sel, cnt + pair, max_sel,
+    uint32_t keys[kSelKeyRounds];
+    select_blocks_wg<4, false>(keys, sI, nb, wblocks, topk, sh, sel + pair * max_sel, cnt + pair, max_sel,
                         nullptr, nullptr, 0, nullptr);
 }
 
@@ -783,7 +797,11 @@ static hipError_t launch_step1(const Plan& pl, Step1Args a, hipStream_t stream)
     const int npairs = pl.B * pl.Hkv;
     dim3 grid(npairs * (1 + a.win_groups));
     // logits in LDS when they fit beside everything else
-    const int zls = (pl.max_nc + 15) / 16 * 16 + 4;
+    // the scoring writes whole tiles of 16 keys, the pooling reads keys up to
+    // 4 max_nb + 3 (never past n_c, but the float4 covering them)
+    const int zneed = (pl.max_nc + 15) / 16 * 16 > 4 * pl.max_nb + 4 ? (pl.max_nc + 15) / 16 * 16
+                                                                    : 4 * pl.max_nb + 4;
+    const int zls = zneed + 4;
     const size_t zbytes = (size_t)pl.G * zls * sizeof(float);
     const size_t limit = device_lds_limit();
     if (step1_lds_bytes(pl.max_nb, 0) + kStep1StaticLds > limit) return hipErrorInvalidValue;

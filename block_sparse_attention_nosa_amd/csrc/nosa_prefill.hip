@@ -90,7 +90,26 @@ __device__ __forceinline__ PfPair pf_pair(const PfArgs& a, int pair)
 struct PfScoreLds {
     float lse[32 * 16];          // per row of the workgroup (pass 2)
     float ksum[4][kKPS];         // per wave, per key of the split (pass 2)
+    int32_t pages[kKPS / SL];    // page of each group of SL pooled keys of the split
 };
+
+// Sum over the 16 lanes of each row of 16 (DPP shifts within the row; the
+// total lands in lane 15 of the row).
+template <int CTRL, int BANK_MASK>
+__device__ __forceinline__ float dpp_row_f(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf,
+                                                                 BANK_MASK, true));
+}
+
+__device__ __forceinline__ float row16_sum_to_last(float x)
+{
+    x += dpp_row_f<0x111, 0xf>(x);  // row_shr:1
+    x += dpp_row_f<0x112, 0xf>(x);  // row_shr:2
+    x += dpp_row_f<0x114, 0xe>(x);  // row_shr:4, lanes 4..15
+    x += dpp_row_f<0x118, 0xc>(x);  // row_shr:8, lanes 8..15
+    return x;
+}
 
 // Workgroup = 4 waves x RTW row tiles of 16 rows, over the kKPS pooled keys of
 // one split.  PASS 1 writes per-row (max, sum exp2) over the split's visible
@@ -112,25 +131,43 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
     const int32_t* trow = a.table + (size_t)P.s * a.max_blocks;
     const int row_tile0 = (rg * 4 + wave) * RTW;  // first row tile of this wave
     const int wg_row0 = rg * 4 * RTW * 16;        // first row of the workgroup
+    // page ids of the split's pooled keys first: a table load queued behind
+    // key loads would wait for them
+    for (int x = tid; x < kKPS / SL; x += 256) {
+        const int key = key_lo + SL * x;
+        sh.pages[x] = key < key_hi ? trow[key / SL] : 0;
+    }
+    if (PASS == 1) __syncthreads();
 
     if (PASS == 2) {
         // lse of every row of the workgroup from the pass-1 partials
+        // (partials read 16 at a time, all loads of a batch in flight, then
+        // combined; a loop-carried load chain would wait on each)
         for (int x = tid; x < 4 * RTW * 16; x += 256) {
             const int row = wg_row0 + x;
             float m = -INFINITY, acc = 0.f;
             if (row < a.rows && !P.empty) {
                 const float2* pp = a.part + ((size_t)pair * a.rows + row) * a.key_splits;
-                for (int i = 0; i < a.key_splits; ++i) {
-                    const float2 v = pp[i];
-                    if (!(v.y > 0.f)) continue;
-                    const float mn = fmaxf(m, v.x);
-                    acc = acc * fexp2(m - mn) + v.y * fexp2(v.x - mn);
-                    m = mn;
+                for (int i0 = 0; i0 < a.key_splits; i0 += 16) {
+                    float2 v[16];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+                        v[u] = i0 + u < a.key_splits ? pp[i0 + u] : make_float2(-INFINITY, 0.f);
+                    float mb = m;
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+                        if (v[u].y > 0.f) mb = fmaxf(mb, v[u].x);
+                    if (mb == -INFINITY) continue;
+                    acc = m == -INFINITY ? 0.f : acc * fexp2(m - mb);
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+                        if (v[u].y > 0.f) acc += v[u].y * fexp2(v[u].x - mb);
+                    m = mb;
                 }
             }
             sh.lse[x] = acc > 0.f ? m + log2f(acc) : INFINITY;  // +inf: row contributes 0
         }
-        __syncthreads();
+        __syncthreads();  // also publishes the page ids
     }
 
     // query operand of the wave's row tiles; rows of absent queries are zero
@@ -149,6 +186,18 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
             qb[u][st] = as_bf16x8(w);
         }
     }
+    // per row tile: does every row hold a query, and the first query position
+    // (the rows of a tile are 16 consecutive (query, head) pairs)
+    bool all_vis[RTW];
+    int tile_p0[RTW];
+#pragma unroll
+    for (int u = 0; u < RTW; ++u) {
+        all_vis[u] = __ballot(qpos[u] < 0) == 0;  // wave-uniform
+        int p = qpos[u] < 0 ? 0x7fffffff : qpos[u];
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) p = min(p, __shfl_xor(p, off));
+        tile_p0[u] = __builtin_amdgcn_readfirstlane(p);
+    }
     float lse_r[RTW];
     if (PASS == 2) {
 #pragma unroll
@@ -161,32 +210,41 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
         s_run[u] = 0.f;
     }
 
-    for (int kt = key_lo; kt < key_hi; kt += 16) {
-        uint4 kf[4];
-        const int key = kt + r;
-        if (key < key_hi) {
-            const uint16_t* kp = kc_page(const_cast<uint16_t*>(a.kc_pool), trow, a.Hkv, P.g, key);
+    // Two key tiles in flight: the loads of tile kt + 16 are issued before
+    // tile kt is computed.  Rows past key_hi load the last key again (their
+    // logits are masked).
+    auto load_tile = [&](int kt, uint4 (&kf)[4]) {
+        const int key = min(kt + r, key_hi - 1);
+        const uint16_t* kp = a.kc_pool + ((size_t)sh.pages[(key - key_lo) / SL] * a.Hkv + P.g) * SL * D;
 #pragma unroll
-            for (int st = 0; st < 4; ++st) kf[st] = ldg16(kp + kc_chunk(key % SL, st * 4 + kq));
-        } else {
-#pragma unroll
-            for (int st = 0; st < 4; ++st) kf[st] = make_uint4(0, 0, 0, 0);
-        }
+        for (int st = 0; st < 4; ++st) kf[st] = ldg16(kp + kc_chunk(key % SL, st * 4 + kq));
+    };
+    auto tile = [&](int kt, const uint4 (&kf)[4]) {
         float colacc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < RTW; ++u) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(kf[st]), qb[u][st], acc);
-            // visible: key < n_c(p + 1)  <=>  16 * key + 32 <= p + 1
+            // visible: key < n_c(p + 1)  <=>  16 * key + 32 <= p + 1; when every
+            // key of the tile is visible to every row of the tile (the common
+            // case) the per-element test is skipped
             float zz[4];
             float tmax = -INFINITY;
+            if (all_vis[u] && kt + 16 <= key_hi && (kt + 15) * kPoolS + kPoolK <= tile_p0[u] + 1) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kj = kt + 4 * kq + i;
-                const bool vis = qpos[u] >= 0 && kj < key_hi && kj * kPoolS + kPoolK <= qpos[u] + 1;
-                zz[i] = vis ? acc[i] * a.scale_log2 : -INFINITY;
-                tmax = fmaxf(tmax, zz[i]);
+                for (int i = 0; i < 4; ++i) {
+                    zz[i] = acc[i] * a.scale_log2;
+                    tmax = fmaxf(tmax, zz[i]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int kj = kt + 4 * kq + i;
+                    const bool vis = qpos[u] >= 0 && kj < key_hi && kj * kPoolS + kPoolK <= qpos[u] + 1;
+                    zz[i] = vis ? acc[i] * a.scale_log2 : -INFINITY;
+                    tmax = fmaxf(tmax, zz[i]);
+                }
             }
             if (PASS == 1) {
                 if (tmax != -INFINITY) {
@@ -203,15 +261,24 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
             }
         }
         if (PASS == 2) {
-            // sum over the 16 rows (lanes r) of each key; lane r == 0 holds it
+            // sum over the 16 rows (lanes r) of each key; lane r == 15 holds it
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) colacc[i] += __shfl_xor(colacc[i], off);
-            }
-            if (r == 0)
+            for (int i = 0; i < 4; ++i) colacc[i] = row16_sum_to_last(colacc[i]);
+            if (r == 15)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sh.ksum[wave][kt - key_lo + 4 * kq + i] = colacc[i];
+        }
+    };
+    // (the loads are issued unconditionally -- past key_hi they repeat the
+    // last key -- so no branch makes the compiler wait for all of them)
+    if (key_lo < key_hi) {
+        uint4 kfa[4], kfb[4];
+        load_tile(key_lo, kfa);
+        for (int kt = key_lo; kt < key_hi; kt += 32) {
+            load_tile(kt + 16, kfb);
+            tile(kt, kfa);
+            load_tile(kt + 32, kfa);
+            if (kt + 16 < key_hi) tile(kt + 16, kfb);
         }
     }
 
@@ -282,30 +349,45 @@ __global__ __launch_bounds__(256) void pf_pool_kernel(PfArgs a)
 
 // ------------------------------------------------------------ attention ---
 
-// K page in LDS: 64 rows of 128 bf16 padded to 272 bytes; V page: 128 channel
-// rows of 64 bf16 padded to 144 bytes.  Both paddings make the 16-byte
-// fragment reads of 16 lanes land on distinct bank groups.
-constexpr int kKRow = 136;  // bf16 per padded K row
-constexpr int kVRow = 72;   // bf16 per padded V row
-
+// A K and a V page in LDS, in the pages' own operand order (a straight copy):
+// the fragment of QK^T tile t, k-step st is run 4t + st, that of PV k-step
+// u, channel tile nt is run 8u + nt, lane l at byte 16 l of its run, so a
+// wave's fragment read is 1 KB of consecutive LDS.
 struct PfAttnLds {
-    uint16_t k[64 * kKRow];
-    uint16_t v[128 * kVRow];
+    uint16_t k[2][BS * D];
+    uint16_t v[2][BS * D];
 };
 
 // Workgroup = 4 waves x 2 row tiles (128 rows) of one pair; loops over the
-// pair's kept pages, each staged once through LDS for all 8 row tiles, the
-// next page's loads in flight while the current one is computed.
-__global__ __launch_bounds__(256) void pf_attend_kernel(PfArgs a, int attn_groups)
+// pair's kept pages, each staged once through LDS for all 8 row tiles.  The
+// (block, page) list goes to LDS first; page i + 1's loads are issued before
+// page i is computed and land in the other LDS buffer after it, so one
+// barrier per page suffices.
+//
+// Workgroups are dealt to the eight XCDs round-robin by index, so index b is
+// mapped to the logical workgroup (b % 8) * per_xcd + b / 8: the attn_groups
+// workgroups of a pair, which read the same pages, run on one XCD and share
+// its L2.  Indices past the last logical workgroup exit at once.
+__global__ __launch_bounds__(256) void pf_attend_kernel(PfArgs a, int attn_groups, int total,
+                                                        int per_xcd)
 {
     __shared__ PfAttnLds sh;
-    const int pair = blockIdx.x / attn_groups, ag = blockIdx.x % attn_groups;
+    extern __shared__ __align__(16) char smem[];
+    int2* list = reinterpret_cast<int2*>(smem);  // [max_sel] (block, page)
+    const int lid = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (lid >= total) return;
+    const int pair = lid / attn_groups, ag = lid % attn_groups;
     const PfPair P = pf_pair(a, pair);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
     const int32_t* trow = a.table + (size_t)P.s * a.max_blocks;
     const int n = P.empty ? 0 : min(a.cnt[pair], a.max_sel);
     const int32_t* sl = a.sel + (size_t)pair * a.max_sel;
+    for (int x = tid; x < n; x += 256) {
+        int b = sl[x];
+        if (b < 0 || b >= P.nb) b = -1;
+        list[x] = make_int2(b, b >= 0 ? trow[b] : 0);
+    }
 
     bf16x8 qb[2][4];
     int qpos[2];
@@ -330,60 +412,63 @@ __global__ __launch_bounds__(256) void pf_attend_kernel(PfArgs a, int attn_group
     for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) o[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();  // the list
 
-    // global -> register staging of one page: thread tid moves the 16-byte
-    // chunks tid + 256c (c < 4) of the K and V pages, contiguous in memory;
-    // their rows and columns in LDS follow from the page layouts (k_chunk,
-    // v_chunk): K chunk q is channels 8(4 st + kq) .. of token
-    // qk_row_token(t, m) with q = 64(4t + st) + 16kq + m; V chunk q is tokens
-    // 8(4u + kq) .. of channel 16 nt + r with q = 64(8u + nt) + 16kq + r
+    // thread tid moves the 16-byte chunks tid + 256c (c < 4) of a K and a V
+    // page: the same offsets in global memory and in LDS
     uint4 stk[4], stv[4];
-    auto fetch = [&](int idx) {
-        int b = idx < n ? sl[idx] : -1;
-        if (b < 0 || b >= P.nb) b = -1;
-        const int page = b >= 0 ? trow[b] : 0;
+    // (unconditional loads: past the list, or for a dropped entry, page 0 is
+    // read and never used; a branch around the loads makes the compiler wait
+    // for every outstanding load at the loop head)
+    auto fetch = [&](int idx, uint4 (&k4)[4], uint4 (&v4)[4]) {
+        const int page = idx < n ? list[idx].y : 0;
         const uint16_t* kb = a.k_pool + ((size_t)page * a.Hkv + P.g) * BS * D;
         const uint16_t* vb = a.v_pool + ((size_t)page * a.Hkv + P.g) * D * BS;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int ch = tid + 256 * c;
-            stk[c] = b >= 0 ? ldg16(kb + ch * 8) : make_uint4(0, 0, 0, 0);
-            stv[c] = b >= 0 ? ldg16(vb + ch * 8) : make_uint4(0, 0, 0, 0);
+            k4[c] = ldg16(kb + ch * 8);
+            v4[c] = ldg16(vb + ch * 8);
         }
-        return b;
     };
-    auto stash = [&]() {
+    auto stash = [&](int buf, const uint4 (&k4)[4], const uint4 (&v4)[4]) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int ch = tid + 256 * c;
-            const int ktok = qk_row_token(ch >> 8, ch & 15), kc8 = ((ch >> 6) & 3) * 4 + ((ch >> 4) & 3);
-            const int vch = ((ch >> 6) & 7) * 16 + (ch & 15), vx8 = (ch >> 9) * 4 + ((ch >> 4) & 3);
-            *reinterpret_cast<uint4*>(&sh.k[ktok * kKRow + kc8 * 8]) = stk[c];
-            *reinterpret_cast<uint4*>(&sh.v[vch * kVRow + vx8 * 8]) = stv[c];
+            *reinterpret_cast<uint4*>(&sh.k[buf][ch * 8]) = k4[c];
+            *reinterpret_cast<uint4*>(&sh.v[buf][ch * 8]) = v4[c];
         }
     };
-
-    int b_cur = n > 0 ? fetch(0) : -1;
-    stash();
-    __syncthreads();
-    for (int idx = 0; idx < n; ++idx) {
-        const int b_next = idx + 1 < n ? fetch(idx + 1) : -1;  // in flight during compute
-        if (b_cur >= 0) {
-            // S^T = K q^T for both row tiles: K fragments from LDS, shared
-            float x[2][4][4];
-            float bmax[2] = {-INFINITY, -INFINITY};
+    // every row of the workgroup holds a query, and the smallest position:
+    // pages entirely at or before it need no causal mask
+    const bool rows_full = __syncthreads_and(qpos[0] >= 0 && qpos[1] >= 0);
+    int pmin = min(qpos[0] < 0 ? 0x7fffffff : qpos[0], qpos[1] < 0 ? 0x7fffffff : qpos[1]);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int tok = qk_row_token(t, r);
-                bf16x8 kf[4];
+    for (int off = 1; off < 64; off <<= 1) pmin = min(pmin, __shfl_xor(pmin, off));
+    pmin = __builtin_amdgcn_readfirstlane(pmin);  // per wave (its own rows)
+    auto compute = [&](int buf, int b_cur) {
+        // S^T = K q^T for both row tiles: K fragments from LDS, shared
+        float x[2][4][4];
+        float bmax[2] = {-INFINITY, -INFINITY};
+        const bool full = rows_full && b_cur * BS + BS - 1 <= pmin && b_cur * BS + BS <= P.L;
 #pragma unroll
-                for (int st = 0; st < 4; ++st)
-                    kf[st] = as_bf16x8(*reinterpret_cast<const uint4*>(&sh.k[tok * kKRow + st * 32 + kq * 8]));
+        for (int t = 0; t < 4; ++t) {
+            bf16x8 kf[4];
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int st = 0; st < 4; ++st)
+                kf[st] = as_bf16x8(*reinterpret_cast<const uint4*>(&sh.k[buf][((t * 4 + st) * 64 + lane) * 8]));
 #pragma unroll
-                    for (int st = 0; st < 4; ++st) acc = mfma16(kf[st], qb[u][st], acc);
+            for (int u = 0; u < 2; ++u) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < 4; ++st) acc = mfma16(kf[st], qb[u][st], acc);
+                if (full) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        x[u][t][i] = acc[i] * a.scale_log2;
+                        bmax[u] = fmaxf(bmax[u], x[u][t][i]);
+                    }
+                } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int tk = b_cur * BS + 32 * (t >> 1) + 8 * kq + 4 * (t & 1) + i;
@@ -393,55 +478,68 @@ __global__ __launch_bounds__(256) void pf_attend_kernel(PfArgs a, int attn_group
                     }
                 }
             }
-            bf16x8 pa[2][2];
+        }
+        bf16x8 pa[2][2];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                float bm = bmax[u];
-                bm = fmaxf(bm, __shfl_xor(bm, 16));
-                bm = fmaxf(bm, __shfl_xor(bm, 32));
-                const float m_new = fmaxf(m_run[u], bm);
-                // a row with nothing visible yet keeps m = -inf and adds nothing
-                const float alpha = m_new == -INFINITY ? 1.f : fexp2(m_run[u] - m_new);
-                float psum = 0.f;
+        for (int u = 0; u < 2; ++u) {
+            float bm = bmax[u];
+            bm = fmaxf(bm, __shfl_xor(bm, 16));
+            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            const float m_new = fmaxf(m_run[u], bm);
+            // a row with nothing visible yet keeps m = -inf and adds nothing
+            const float alpha = m_new == -INFINITY ? 1.f : fexp2(m_run[u] - m_new);
+            float psum = 0.f;
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float e = m_new == -INFINITY ? 0.f : fexp2(x[u][t][i] - m_new);
-                        x[u][t][i] = e;
-                        psum += e;
-                    }
-                l_run[u] = l_run[u] * alpha + psum;
-                m_run[u] = m_new;
+                for (int i = 0; i < 4; ++i) {
+                    const float e = m_new == -INFINITY ? 0.f : fexp2(x[u][t][i] - m_new);
+                    x[u][t][i] = e;
+                    psum += e;
+                }
+            l_run[u] = l_run[u] * alpha + psum;
+            // the accumulators are rescaled only when some row's maximum moved
+            if (__ballot(m_new != m_run[u]) != 0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float ai = __shfl(alpha, 4 * kq + i);
 #pragma unroll
                     for (int nt = 0; nt < 8; ++nt) o[u][nt][i] *= ai;
                 }
-#pragma unroll
-                for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        pa[u][uu][i] = (__bf16)x[u][2 * uu][i];
-                        pa[u][uu][4 + i] = (__bf16)x[u][2 * uu + 1][i];
-                    }
             }
-            // O += P V: V fragments from LDS, shared by both row tiles
+            m_run[u] = m_new;
 #pragma unroll
             for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
-                for (int nt = 0; nt < 8; ++nt) {
-                    const bf16x8 vf = as_bf16x8(
-                        *reinterpret_cast<const uint4*>(&sh.v[(nt * 16 + r) * kVRow + uu * 32 + kq * 8]));
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) o[u][nt] = mfma16(pa[u][uu], vf, o[u][nt]);
+                for (int i = 0; i < 4; ++i) {
+                    pa[u][uu][i] = (__bf16)x[u][2 * uu][i];
+                    pa[u][uu][4 + i] = (__bf16)x[u][2 * uu + 1][i];
                 }
         }
-        __syncthreads();  // every wave is done with the current page
-        if (idx + 1 < n) stash();
+        // O += P V: V fragments from LDS, shared by both row tiles
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                const bf16x8 vf =
+                    as_bf16x8(*reinterpret_cast<const uint4*>(&sh.v[buf][((uu * 8 + nt) * 64 + lane) * 8]));
+#pragma unroll
+                for (int u = 0; u < 2; ++u) o[u][nt] = mfma16(pa[u][uu], vf, o[u][nt]);
+            }
+    };
+
+    if (n > 0) {
+        fetch(0, stk, stv);
+        stash(0, stk, stv);
         __syncthreads();
-        b_cur = b_next;
+    }
+    for (int idx = 0; idx < n; ++idx) {
+        const int buf = idx & 1;
+        fetch(idx + 1, stk, stv);  // in flight while page idx is computed
+        const int b = list[idx].x;
+        if (b >= 0) compute(buf, b);
+        if (idx + 1 < n) stash(buf ^ 1, stk, stv);
+        __syncthreads();
     }
 
     // normalise and store: lane holds O[rows 4kq + i][channels 16nt + r]
@@ -533,8 +631,11 @@ hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_k
     a.cnt = cnt;
     a.out = out;
     a.lse = lse;
-    hipLaunchKernelGGL(pf_attend_kernel, dim3(pf.npairs * pf.attn_groups), dim3(256), 0, stream, a,
-                       pf.attn_groups);
+    const size_t lds = (size_t)(pl.max_sel > 0 ? pl.max_sel : 1) * sizeof(int2);
+    const int total = pf.npairs * pf.attn_groups;
+    const int per_xcd = (total + 7) / 8;
+    hipLaunchKernelGGL(pf_attend_kernel, dim3(8 * per_xcd), dim3(256), lds, stream, a, pf.attn_groups,
+                       total, per_xcd);
     return hipGetLastError();
 }
 

@@ -52,17 +52,17 @@ nosa_status check_sizes(int batch, int max_seqlen_q, int max_seqlen_k)
     return NOSA_OK;
 }
 
-// Tiles of 16 pooled keys each wave of a pair's scoring workgroup keeps in
-// flight per batch (one of the compiled 1, 2, 3, 5, 7, 9, 12): enough that
-// one batch covers the pair when it is short, at most 12 (192 keys, 48 loads
-// of 16 bytes per lane).
-int pick_score_tiles(int nc)
+// Tiles of 16 pooled keys per wave of a scoring workgroup (one of the
+// compiled 1, 2, 4, 8; a chunk is 64 T keys): the smallest T that keeps the
+// launch within about 1024 workgroups (four per CU) and a pair within
+// kMaxChunks chunks.  Small T spreads a short context over many CUs: one CU
+// streams only about 100 GB/s.
+int pick_score_tiles(int nc, long long pairs)
 {
-    static const int kTiles[] = {1, 2, 3, 5, 7, 9, 12};
-    const int per_wave = ceil_div(ceil_div(nc, 16), 8);
-    for (int t : kTiles)
-        if (per_wave <= t) return t;
-    return 12;
+    const int tiles = ceil_div(nc > 0 ? nc : 1, 16);
+    for (int t : {1, 2, 4})
+        if (ceil_div(tiles, 4 * t) <= kMaxChunks && pairs * ceil_div(tiles, 4 * t) <= 1024) return t;
+    return 8;
 }
 
 // Blocks per wave (rounds, one of the compiled 1, 2, 3, 4, 6, 8) and
@@ -115,31 +115,27 @@ nosa_status make_plan(const nosa_params* p, int batch, int max_seqlen_k, Plan* p
     const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->head_dim);
     P.scale_log2 = (float)(scale * 1.4426950408889634);
 
-    const int nc1 = P.max_nc > 0 ? P.max_nc : 1;
-    P.score_tiles = pick_score_tiles(nc1);
-    // logits of every key, rounded up to whole tiles; the pooling step reads
-    // keys up to 4b+3 of every block b < max_nb
-    const int zneed = ceil_div(nc1, 16) * 16 > 4 * P.max_nb + 4 ? ceil_div(nc1, 16) * 16
-                                                                 : 4 * P.max_nb + 4;
-    P.zstride = ceil_div(zneed, 64) * 64;
+    const long long npairs = (long long)batch * P.Hkv;
+    P.score_tiles = pick_score_tiles(P.max_nc, npairs);
+    P.chunk_keys = 64 * P.score_tiles;
+    P.nchunks = ceil_div(P.max_nc > 0 ? P.max_nc : 1, P.chunk_keys);
+    P.nbk = P.nchunks * 16 * P.score_tiles;
+    P.gp = ceil_div(P.G, 4) * 4;
 
-    const int wn = P.wblocks < P.max_nb ? P.wblocks : P.max_nb;
-    P.win_groups = ceil_div(wn, kStep1Waves);
     const int ncand = P.max_nb > P.wblocks ? P.max_nb - P.wblocks : 0;
     P.top_span = P.topk < ncand ? P.topk : ncand;
-    pick_split(P.top_span, (long long)batch * P.Hkv, kMaxSplit - P.win_groups, &P.top_groups,
-               &P.top_rounds);
-    P.nsplit = P.win_groups + P.top_groups;
+    P.wslots = P.wblocks < P.max_nb ? P.wblocks : P.max_nb;
+    pick_split(P.top_span, npairs, kMaxSplit, &P.top_groups, &P.top_rounds);
+    P.nsplit = P.top_groups + P.wslots;
     const int aspan = P.max_sel < P.max_nb ? P.max_sel : P.max_nb;
     pick_split(aspan, (long long)batch * P.Hkv, kMaxSplit, &P.attend_groups, &P.attend_rounds);
     const int nparts = P.nsplit > P.attend_groups ? P.nsplit : P.attend_groups;
 
     const size_t B = (size_t)batch, pairs = B * P.Hkv;
     size_t off = 0;
-    P.off_z = off;        off += align256(B * P.Hq * (size_t)P.zstride * sizeof(float));
-    P.off_selpg = off;    off += align256(pairs * (size_t)(P.top_span > 0 ? P.top_span : 1) * sizeof(int2));
-    P.off_sel = off;      off += align256(pairs * (size_t)P.max_sel * sizeof(int32_t));
-    P.off_cnt = off;      off += align256(pairs * sizeof(int32_t));
+    P.off_cml = off;      off += align256(pairs * P.nchunks * (size_t)P.G * sizeof(float2));
+    P.off_spill = off;    off += align256(pairs * P.nchunks * (size_t)P.G * sizeof(float));
+    P.off_bpart = off;    off += align256(pairs * P.nbk * (size_t)P.gp * sizeof(float));
     P.off_po = off;       off += align256(B * P.Hq * (size_t)nparts * kHeadDim * sizeof(float));
     P.off_pml = off;      off += align256(B * P.Hq * (size_t)nparts * sizeof(float2));
     P.bytes = off > 256 ? off : 256;
@@ -170,10 +166,9 @@ Workspace carve(const Plan& pl, void* ws)
 {
     char* base = static_cast<char*>(ws);
     Workspace w;
-    w.z = reinterpret_cast<float*>(base + pl.off_z);
-    w.selpg = reinterpret_cast<int2*>(base + pl.off_selpg);
-    w.sel = reinterpret_cast<int32_t*>(base + pl.off_sel);
-    w.cnt = reinterpret_cast<int32_t*>(base + pl.off_cnt);
+    w.cml = reinterpret_cast<float2*>(base + pl.off_cml);
+    w.spill = reinterpret_cast<float*>(base + pl.off_spill);
+    w.bpart = reinterpret_cast<float*>(base + pl.off_bpart);
     w.po = reinterpret_cast<float*>(base + pl.off_po);
     w.pml = reinterpret_cast<float2*>(base + pl.off_pml);
     return w;

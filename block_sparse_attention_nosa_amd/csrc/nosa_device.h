@@ -1,7 +1,7 @@
 // nosa_device.h -- device code shared by the decode kernels (nosa_kernels.hip)
 // and the chunked-prefill kernels (nosa_prefill.hip): bf16 and MFMA helpers,
-// agent-coherent hand-off accesses, one-page attention on MFMA and the
-// workgroup top-k selector.  Internal; compiled into libnosa.so only.
+// page layouts, one-page attention on MFMA and the workgroup top-k selector.
+// Internal; compiled into libnosa.so only.
 //
 // MFMA used: v_mfma_f32_16x16x32_bf16.  Operand layout (wave64, lane l,
 // r = l % 16, kq = l / 16): A supplies A[r][8kq .. 8kq+7], B supplies
@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "nosa_internal.h"
 
@@ -133,26 +135,49 @@ __device__ __forceinline__ void attn_init(AttnState& A)
 // One wave attends one 64-token page: S^T = K q^T (4 tiles x 4 k-steps), fp32
 // online softmax in log2 units, O += P V (2 k-steps x 8 channel tiles).
 // `limit` = tokens of the page that exist (tokens >= limit are masked).
+// The MFMA operands of one page (32 loads of 16 bytes per lane).
+struct PageRegs {
+    uint4 k[4][4], v[2][8];
+};
+
+// Issues every load of a page: operand blocks in lane order (k_chunk /
+// v_chunk), 1 KB per load.  `lane8` is the lane's element offset in a block,
+// (16 kq + r) * 8 (0 makes every lane read the block's first 16 bytes).
+__device__ __forceinline__ void load_page(const uint16_t* __restrict__ kb,
+                                          const uint16_t* __restrict__ vb, int lane8, PageRegs& p)
+{
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) p.k[t][st] = ldg16(kb + (t * 4 + st) * 512 + lane8);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) p.v[u][nt] = ldg16(vb + (u * 8 + nt) * 512 + lane8);
+}
+
+__device__ __forceinline__ void attend_loaded(const PageRegs& p, int limit, const bf16x8 (&qb)[4],
+                                              float scale_log2, int r, int kq, AttnState& A);
+
 __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ kb,
                                             const uint16_t* __restrict__ vb, int limit,
                                             const bf16x8 (&qb)[4], float scale_log2, int r,
                                             int kq, AttnState& A)
 {
-    // operand blocks in lane order (k_chunk / v_chunk): 1 KB per load
-    const int lane8 = (16 * kq + r) * 8;
-    uint4 ka[4][4], va[2][8];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int st = 0; st < 4; ++st) ka[t][st] = ldg16(kb + (t * 4 + st) * 512 + lane8);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) va[u][nt] = ldg16(vb + (u * 8 + nt) * 512 + lane8);
+    PageRegs p;
+    load_page(kb, vb, (16 * kq + r) * 8, p);
     // Keep every load of the page in flight before the first use: a wave that
     // attends one page pays one memory latency instead of one per few loads.
     __builtin_amdgcn_sched_barrier(0);
+    attend_loaded(p, limit, qb, scale_log2, r, kq, A);
+}
 
+// Online-softmax update of A with one page whose operands are in p.
+__device__ __forceinline__ void attend_loaded(const PageRegs& p, int limit, const bf16x8 (&qb)[4],
+                                              float scale_log2, int r, int kq, AttnState& A)
+{
+    const auto& ka = p.k;
+    const auto& va = p.v;
     float x[4][4];
     float bmax = -INFINITY;
 #pragma unroll
@@ -202,6 +227,8 @@ __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ kb,
 
 // ------------------------------------------------------------ selection ---
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x);
+
 // Order-preserving map of a float onto uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t order_key(float f)
 {
@@ -219,18 +246,44 @@ __device__ __forceinline__ int lanes_below(uint64_t mask)
 constexpr int kSelMaxRounds = kMaxBlocks / 256;  // candidate rounds of a 4-wave selector
 constexpr int kSelKeyRounds = 8;                  // candidate rounds whose keys stay in registers
 
-struct SelectLds {
+struct alignas(16) SelectLds {
     float lse[kMaxGroup];
-    int hist[4][256];                 // digit counts per level (zero before the selector runs)
+    int hist0[1024];                  // digit counts, first level (10-bit digits)
+    int hist[3][256];                 // digit counts, later levels (zero before the selector runs)
     int cnt[2][kSelMaxRounds][8];     // per (round, wave): tied candidates, taken candidates
+    uint32_t mm[2][8];                // per wave: smallest, largest candidate key
 };
 
 // Zeroes the digit counts; all NT threads, and a barrier before the selector.
 template <int NT>
 __device__ __forceinline__ void select_lds_clear(SelectLds& sh)
 {
+    int4* h0 = reinterpret_cast<int4*>(sh.hist0);
+    for (int i = threadIdx.x; i < 256; i += NT) h0[i] = make_int4(0, 0, 0, 0);
     int* h = &sh.hist[0][0];
-    for (int i = threadIdx.x; i < 4 * 256; i += NT) h[i] = 0;
+    for (int i = threadIdx.x; i < 3 * 256; i += NT) h[i] = 0;
+}
+
+// Smallest and largest order key of this thread's candidates (i*NT + tid <
+// ncand, i < KR, keys in registers) reduced over the wave and stored for
+// wave `wave` in sh.mm; the selector reads them after the caller's next
+// barrier (range_known).
+template <int NT, int KR>
+__device__ __forceinline__ void select_wave_range(const uint32_t (&keys)[KR], int ncand, SelectLds& sh)
+{
+    uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < KR; ++i)
+        if (i * NT + (int)threadIdx.x < ncand) {
+            lo = min(lo, keys[i]);
+            hi = max(hi, keys[i]);
+        }
+    lo = ~wave_max_u32(~lo);
+    hi = wave_max_u32(hi);
+    if ((threadIdx.x & 63) == 0) {
+        sh.mm[0][threadIdx.x >> 6] = lo;
+        sh.mm[1][threadIdx.x >> 6] = hi;
+    }
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
@@ -248,31 +301,78 @@ __device__ __forceinline__ int wave_incl_scan(int x)
     return x;
 }
 
+// Wave-wide reductions with DPP moves (the pattern of wave_incl_scan; a
+// lane that a move does not reach keeps the identity), read from lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x)
+{
+    int v = (int)x;
+    v = max((unsigned)v, (unsigned)__builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true));
+    v = max((unsigned)v, (unsigned)__builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true));
+    v = max((unsigned)v, (unsigned)__builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xe, true));
+    v = max((unsigned)v, (unsigned)__builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xc, true));
+    v = max((unsigned)v, (unsigned)__builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));
+    v = max((unsigned)v, (unsigned)__builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));
+    return (uint32_t)__builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ float wave_max_f(float x)
+{
+    constexpr int kNegInf = (int)0xff800000u;
+    int v = __float_as_int(x);
+    v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, v, 0x111, 0xf, 0xf, false))));
+    v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, v, 0x112, 0xf, 0xf, false))));
+    v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, v, 0x114, 0xf, 0xe, false))));
+    v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, v, 0x118, 0xf, 0xc, false))));
+    v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, v, 0x142, 0xa, 0xf, false))));
+    v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, v, 0x143, 0xc, 0xf, false))));
+    return __int_as_float(__builtin_amdgcn_readlane(v, 63));
+}
+
+__device__ __forceinline__ float wave_sum_f(float x)
+{
+    int v = __float_as_int(x);
+    v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true)));
+    v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true)));
+    v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xe, true)));
+    v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xc, true)));
+    v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false)));
+    v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(v, 63));
+}
+
 // Top-min(topk, ncand) of the candidates [0, ncand) by (importance desc, block
 // asc) with the window [ncand, nb) always kept.  Writes, when non-null:
 //   sel_out[0 .. max_sel): every kept block ascending, -1 padded; *cnt_out;
-//   selpg[0 .. top_span): (block, page) of the top-k picks ascending,
-//                         (-1, -1) padded; *ntop_out.
-// Must be called by all NW*64 threads, sh.hist zeroed and a barrier passed
-// since; sI holds the importance in LDS; page ids come from `pages` (LDS copy
-// of the block-table row) when given, else from `trow`.  With KEYS_GIVEN the
-// caller passes the order keys of its candidates i*NT + tid, i < KR, in
-// keys[] (those rounds are then not read from sI).
+//   list[0 .. list_n): (block, pages[block]) of top-k picks list_lo ..
+//                      list_lo + list_n - 1 in ascending block order,
+//                      (-1, -1) past the last pick (list may be in LDS).
+// Must be called by all NW*64 threads, the digit counts zeroed and a barrier
+// passed since; sI holds the importance in LDS (read only for candidates past
+// the register rounds when KEYS_GIVEN); `pages` is the block-table row (LDS
+// or global).  With KEYS_GIVEN the caller passes the order keys of its
+// candidates i*NT + tid, i < KR, in keys[] (those rounds are then not read
+// from sI).  With range_known every candidate is in registers and the caller
+// stored each wave's key range with select_wave_range before its last
+// barrier.  No barrier at the end: the caller synchronises before reading
+// what was written to LDS.
 //
-// The k-th largest order key is found a byte at a time from the top: one
-// LDS histogram of the next byte over the candidates that still share the
-// prefix, one barrier, then every wave scans the 256 counts itself.  The
-// search stops as soon as the candidates sharing the prefix are exactly the
-// ones still needed, so for distinct keys it usually ends after two bytes.
-// The taken candidates are then compacted in ascending order from per-wave
-// ballot counts (one barrier, two when tied keys straddle the cut).
+// The k-th largest order key is found by a radix search over u = key - kmin,
+// kmin and kmax being the smallest and largest candidate key: the first
+// digit is the top 10 bits of the range kmax - kmin (so the candidates spread
+// over its 1024 values however narrow their range), each later digit the
+// next 8 bits below.  A level is one LDS histogram of the digit over the
+// candidates that share the prefix found so far, one barrier, and a scan of
+// the 256 counts by every wave; the search stops as soon as the candidates
+// sharing the prefix are exactly the ones still needed, which for distinct
+// keys usually happens at the first level.  The taken candidates are then
+// compacted in ascending order from per-wave ballot counts (one barrier, two
+// when tied keys straddle the cut).
 template <int NW, bool KEYS_GIVEN>
 __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds], const float* sI, int nb,
                                                  int wblocks, int topk, SelectLds& sh,
                                                  int32_t* __restrict__ sel_out, int32_t* __restrict__ cnt_out,
-                                                 int max_sel, int2* __restrict__ selpg,
-                                                 int32_t* __restrict__ ntop_out, int top_span,
-                                                 const int32_t* __restrict__ trow, const int32_t* pages = nullptr)
+                                                 int max_sel, int2* list, int list_lo, int list_n,
+                                                 const int32_t* pages, bool range_known = false)
 {
     static_assert(NW >= 4 && NW <= 8, "per-round counts are sized for 4 to 8 waves");
     constexpr int NT = NW * 64;
@@ -304,64 +404,117 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
         const int b = i * NT + tid;
         return b < ncand ? order_key(sI[b]) : 0u;
     };
-    // Candidates whose key >> shift is above P are taken; of those equal to
-    // P, the `need` lowest blocks; there are n_eq of them.
+    // Candidates whose u >> shift is above P are taken; of those equal to P,
+    // the `need` lowest blocks; there are n_eq of them.  shift = 32: every
+    // candidate is equal (P = 0).
     int shift = 32, need = kk, n_eq = kk;
-    uint32_t P = 0;
+    uint32_t P = 0, kmin = 0;
     if (partial) {
-        int above = 0;
-#pragma unroll 1
-        for (int level = 0; level < 4; ++level) {
-            const int sh_lo = 24 - 8 * level;
+        // range of the candidate keys
+        if (!range_known) {
+            uint32_t lo = 0xffffffffu, hi = 0u;
             for (int i = 0; i < rounds; ++i) {
-                const int b = i * NT + tid;
                 const uint32_t key = key_at(i);
-                const bool match = b < ncand && (level == 0 || (key >> (sh_lo + 8)) == P);
-                if (match) atomicAdd(&sh.hist[level][(key >> sh_lo) & 255], 1);
+                if (i * NT + tid < ncand) {
+                    lo = min(lo, key);
+                    hi = max(hi, key);
+                }
+            }
+            lo = ~wave_max_u32(~lo);
+            hi = wave_max_u32(hi);
+            if (lane == 0) {
+                sh.mm[0][wave] = lo;
+                sh.mm[1][wave] = hi;
             }
             __syncthreads();
-            // lane l holds digits 255-4l .. 252-4l, so the lane prefix sum
-            // counts from the top digit down
-            int v[4], loc = 0;
+        }
+        kmin = 0xffffffffu;
+        uint32_t kmax = 0u;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[j] = sh.hist[level][255 - 4 * lane - j];
-                loc += v[j];
-            }
-            const int incl = wave_incl_scan(loc);
-            // first lane whose digits reach kk candidates at or above them
-            const uint64_t reach = __ballot(above + incl >= kk);
-            const int l0 = (int)__builtin_ctzll(reach);  // exists: all candidates sharing P count
-            // in lane l0, the first of its digits (from the top) that reaches kk
-            int acc = above + incl - loc, dj = 3, before = 0, at = 0;
-            bool found = false;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (!found && acc + v[j] >= kk) {
-                    found = true;
-                    dj = j;
-                    before = acc;
-                    at = v[j];
+        for (int w = 0; w < NW; ++w) {
+            kmin = min(kmin, sh.mm[0][w]);
+            kmax = max(kmax, sh.mm[1][w]);
+        }
+        const uint32_t range = kmax - kmin;
+        n_eq = ncand;
+        need = kk;
+        if (range != 0u) {
+            const int bits = 32 - __builtin_clz(range);
+            int sh_lo = bits > 10 ? bits - 10 : 0;
+            int prev = 32, above = 0;
+            // one level: histogram of (u >> sh_lo) & (nd - 1) over the
+            // candidates sharing the prefix, then every wave finds the digit
+            // holding the kk-th largest; lane l holds digits nd-1-DPL*l
+            // downwards (DPL per lane), so the lane prefix sum counts from
+            // the top digit down
+            auto level_pass = [&](int* hist, auto dpl_tag) -> bool {
+                constexpr int DPL = decltype(dpl_tag)::value;
+                constexpr int ND = 64 * DPL;
+                for (int i = 0; i < rounds; ++i) {
+                    const int b = i * NT + tid;
+                    const uint32_t u = key_at(i) - kmin;
+                    const bool match = b < ncand && (prev == 32 || (u >> prev) == P);
+                    if (match) atomicAdd(&hist[(u >> sh_lo) & (ND - 1)], 1);
                 }
-                acc += v[j];
+                __syncthreads();
+                int v[DPL], loc = 0;
+#pragma unroll
+                for (int j = 0; j < DPL; j += 4) {
+                    const int4 c4 = *reinterpret_cast<const int4*>(&hist[ND - DPL * (lane + 1) + DPL - 4 - j]);
+                    v[j] = c4.w;
+                    v[j + 1] = c4.z;
+                    v[j + 2] = c4.y;
+                    v[j + 3] = c4.x;
+                }
+#pragma unroll
+                for (int j = 0; j < DPL; ++j) loc += v[j];
+                const int incl = wave_incl_scan(loc);
+                // first lane whose digits reach kk candidates at or above them
+                const uint64_t reach = __ballot(above + incl >= kk);
+                const int l0 = (int)__builtin_ctzll(reach);  // exists: all candidates sharing P count
+                // in lane l0, the first of its digits (from the top) that reaches kk
+                int acc = above + incl - loc, dj = DPL - 1, before = 0, at = 0;
+                bool found = false;
+#pragma unroll
+                for (int j = 0; j < DPL; ++j) {
+                    if (!found && acc + v[j] >= kk) {
+                        found = true;
+                        dj = j;
+                        before = acc;
+                        at = v[j];
+                    }
+                    acc += v[j];
+                }
+                const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane(ND - 1 - DPL * lane - dj, l0);
+                above = __builtin_amdgcn_readlane(before, l0);
+                n_eq = __builtin_amdgcn_readlane(at, l0);
+                // the digit's bits below the prefix are the new ones
+                const int nbits = prev - sh_lo;  // 1 .. 10
+                P = prev == 32 ? digit : (P << nbits) | (digit & ((1u << nbits) - 1u));
+                prev = sh_lo;
+                shift = sh_lo;
+                need = kk - above;
+                return n_eq == need || sh_lo == 0;  // taken exactly, or u fully resolved
+            };
+            if (!level_pass(sh.hist0, std::integral_constant<int, 16>{})) {
+#pragma unroll 1
+                for (int level = 0; level < 3; ++level) {
+                    sh_lo = sh_lo > 8 ? sh_lo - 8 : 0;
+                    if (level_pass(sh.hist[level], std::integral_constant<int, 4>{})) break;
+                }
             }
-            const int digit = __builtin_amdgcn_readlane(255 - 4 * lane - dj, l0);
-            above = __builtin_amdgcn_readlane(before, l0);
-            n_eq = __builtin_amdgcn_readlane(at, l0);
-            P = (P << 8) | (uint32_t)digit;
-            shift = sh_lo;
-            need = kk - above;
-            if (n_eq == need) break;  // every candidate sharing the prefix is taken
         }
     }
     // Ascending compaction: candidate i*NT + tid in round i; per (round,
     // wave) counts through LDS, one barrier per pass.
     const bool ranked = partial && n_eq > need;
+    auto prefix = [&](uint32_t key) -> uint32_t {
+        return shift < 32 ? (key - kmin) >> shift : 0u;
+    };
     if (ranked) {
         for (int i = 0; i < rounds; ++i) {
             const int b = i * NT + tid;
-            const uint32_t key = key_at(i);
-            const bool eq = b < ncand && (key >> shift) == P;
+            const bool eq = b < ncand && prefix(key_at(i)) == P;
             const uint64_t m = __ballot(eq);
             if (lane == 0) sh.cnt[0][i][wave] = (int)__popcll(m);
         }
@@ -377,8 +530,7 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
             if (!partial) {
                 take = valid && kk > 0;
             } else {
-                const uint32_t key = key_at(i);
-                const uint32_t kp = shift < 32 ? key >> shift : 0u;
+                const uint32_t kp = prefix(key_at(i));
                 const bool gt = kp > P, eq = kp == P;
                 if (ranked) {
                     const uint64_t m = __ballot(valid && eq);
@@ -414,7 +566,8 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
         if (take) {
             const int b = i * NT + tid;
             if (sel_out) sel_out[pos] = b;
-            if (selpg && pos < top_span) selpg[pos] = make_int2(b, pages ? pages[b] : trow[b]);
+            if (list && pos >= list_lo && pos < list_lo + list_n)
+                list[pos - list_lo] = make_int2(b, pages[b]);
         }
     }
     const int nsel = sel_base;
@@ -423,12 +576,10 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
         for (int b = ncand + tid; b < nb; b += NT) sel_out[nsel + (b - ncand)] = b;
         for (int x = total + tid; x < max_sel; x += NT) sel_out[x] = -1;
     }
-    if (selpg)
-        for (int x = nsel + tid; x < top_span; x += NT) selpg[x] = make_int2(-1, -1);
-    if (tid == 0) {
-        if (cnt_out) *cnt_out = total;
-        if (ntop_out) *ntop_out = nsel;
-    }
+    if (list)
+        for (int x = (nsel > list_lo ? nsel - list_lo : 0) + tid; x < list_n; x += NT)
+            list[x] = make_int2(-1, -1);
+    if (tid == 0 && cnt_out) *cnt_out = total;
 }
 
 }  // namespace nosa

@@ -20,9 +20,10 @@ constexpr int kSlots = kBlock / kPoolS;  // compressed keys stored per page
 constexpr int kMaxGroup = 16;            // query heads per KV head (MFMA N = 16)
 constexpr int kMaxBlocks = 8192;         // blocks per sequence (LDS of the selector)
 constexpr int kMaxSplit = 64;            // attention partials per head (LDS of the merge)
-constexpr int kMaxWindowBlocks = 128;    // window blocks (one page per wave of step 1)
-constexpr int kStep1Waves = 8;           // waves of a step-1 workgroup
+constexpr int kMaxWindowBlocks = 128;    // window blocks (one page per wave)
+constexpr int kScoreWaves = 4;           // waves of a scoring workgroup
 constexpr int kStep2Waves = 4;           // waves of an attention workgroup
+constexpr int kMaxChunks = 64;           // scoring chunks per pair (one lane each when combined)
 
 inline int num_keys(int L) { return L >= kPoolK ? (L - kPoolK) / kPoolS + 1 : 0; }
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -34,28 +35,28 @@ struct Plan {
     int max_seqlen_k = 0, max_nc = 0, max_nb = 0;
     int Lmax = 0;  // device lengths are clamped to this (<= max_seqlen_k, table reach)
     float scale_log2 = 0.f;  // logit scale * log2(e)
-    // scoring: one workgroup of 8 waves per pair, T tiles of 16 keys per
-    // wave in flight
-    int score_tiles = 1, zstride = 0;
-    // attention: one 64-token block per wave
-    int win_groups = 0;     // window workgroups of 8 waves per pair (step 1)
+    // scoring: chunks of 64 T pooled keys (T tiles of 16 keys per wave of a
+    // four-wave workgroup), nchunks per pair, 16 T blocks per chunk
+    int score_tiles = 1, chunk_keys = 64, nchunks = 1;
+    int nbk = 16;           // blocks with a pooled-importance partial per pair = nchunks * 16 T
+    int gp = 4;             // G rounded up to a multiple of 4 (stride of the partial rows)
+    // attention: one 64-token block per wave, four-wave workgroups
     int top_span = 0;       // top-k entries per pair = min(topk, max_nb - window blocks)
-    int top_groups = 0;     // top-k workgroups per pair (step 2), >= 1
+    int top_groups = 0;     // top-k workgroups per pair of a decode step, >= 1
     int top_rounds = 1;     // top-k blocks per wave
-    int nsplit = 0;         // partials per head in a decode step = win_groups + top_groups
+    int wslots = 0;         // window pages per pair = min(window blocks, max_nb), a workgroup each
+    int nsplit = 0;         // partials per head in a decode step = top_groups + wslots
     int attend_groups = 0;  // workgroups per pair of the stand-alone attention
     int attend_rounds = 1;  // blocks per wave of the stand-alone attention
     // workspace layout (bytes from the start of the workspace)
-    size_t off_z = 0, off_selpg = 0,
-           off_sel = 0, off_cnt = 0, off_po = 0, off_pml = 0, bytes = 0;
+    size_t off_cml = 0, off_spill = 0, off_bpart = 0, off_po = 0, off_pml = 0, bytes = 0;
 };
 
 // Device pointers carved out of the caller's workspace.
 struct Workspace {
-    float* z;            // [B][Hq][zstride] logits, log2 units
-    int2* selpg;         // [pairs][top_span] (block, page) of the top-k picks
-    int32_t* sel;        // [pairs][max_sel] kept blocks (when the caller passes none)
-    int32_t* cnt;        // [pairs]
+    float2* cml;         // [pairs][G][nchunks] per head and chunk: (max z, sum 2^(z - max))
+    float* spill;        // [pairs][G][nchunks] 2^(z - max) of the chunk's last key
+    float* bpart;        // [pairs][nbk][gp] per block and head: sum of 2^(z - chunk max)
     float* po;           // [B][Hq][nsplit'][D] partial outputs
     float2* pml;         // [B][Hq][nsplit'] partial (max, sum)
 };

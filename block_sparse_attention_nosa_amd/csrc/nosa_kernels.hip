@@ -1,21 +1,20 @@
 // nosa_kernels.hip -- CDNA4 (gfx950) kernels of the NOSA sparse decode step.
 //
-// A decode step is two launches:
-//   step1 : per (sequence, KV head) pair, "score" workgroups compute
-//           z_h[j] = scale*log2(e) * q_h . Kc_j on MFMA with per-wave
-//           (max, sum exp2) partials -- the wave owning the key completed by the
-//           current token pools it from K first (fp64, one bf16 rounding) and
-//           stores it -- while "window" workgroups attend the local-window
-//           blocks, which need no selection.  The last score workgroup of a
-//           pair (atomic counter) turns the partials into per-head log-sum-exp,
-//           pools block importance, radix-selects the top-k candidates and
-//           writes their (block, page) list.
-//   step2 : workgroups attend the selected blocks (one block per wave, every
-//           K/V load of the block in flight at once); the last workgroup of a
-//           pair merges the window and top-k partials into out / lse.
-// Stand-alone entry points reuse the same pieces: kc_build (pooled keys),
-// step1 in scores mode (importance only), select (from given importance) and
-// step2 in attend mode (given block ids).
+// A decode step is three launches on the caller's stream:
+//   score : workgroup (pair, chunk) scores 64 T pooled keys of one (sequence,
+//           KV head) pair on MFMA and leaves per-chunk softmax partials; the
+//           chunk holding the key completed by the current token pools it
+//           from K first and stores it;
+//   top   : per pair, "top" workgroups each recompute the pair's selection
+//           from those partials (log-sum-exp, block importance, top-k) and
+//           attend their slice of the picks, while "window" workgroups attend
+//           the local window, which needs no selection;
+//   merge : combines the (m, l, o) partials of every head into out / lse.
+// Kernel boundaries order every hand-off: no workgroup reads another
+// workgroup's output within a launch, so there are no counters, fences or
+// zero-filled buffers.  The stand-alone entry points reuse the pieces:
+// kc_build (pooled keys), score + top in importance-only mode, select (from
+// given importance), attend (given block lists) + merge.
 //
 // Sources: page "NOSA-1B 性能基准全解析" (sections 三.2 local window and TopK
 // blocks, 三.3 two-stage attention with kernel 32 / stride 16 pooling, 三.4 the
@@ -25,15 +24,6 @@
 //
 // Shared device helpers (MFMA operand layout, one-page attention, the
 // selector) are in nosa_device.h.
-//
-// Cross-workgroup hand-off ("last one done"): data that another workgroup of
-// the same launch reads (logits, per-wave partials, attention partials) is
-// written and read with agent-scope relaxed atomic accesses, which this chip
-// performs coherently across its L2s (sc1) without whole-cache write-back or
-// invalidation.  Each workgroup waits for its stores to complete, then bumps
-// the pair's counter; the workgroup that sees count-1 resets the counter to
-// zero for the next call and finishes the pair.  Counters therefore start and
-// end every call at zero.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -174,412 +164,559 @@ __device__ void store_wg_partial(CombineLds& sh, const AttnState& A, int G, size
     }
 }
 
-// Eight-wave version of store_wg_partial: waves 4..7 first fold their state
-// into waves 0..3 through LDS, then the four-wave combine runs.  Must be
-// called by all 512 threads.
-__device__ void store_wg_partial8(CombineLds& sh, AttnState& A, int G, size_t head_row0,
-                                  int nsplit, int split, float* __restrict__ po,
-                                  float2* __restrict__ pml)
+// One page attended by the four waves of a workgroup, each loading a quarter
+// of it (8 KB: a CU keeps only about 28 KB of loads in flight, so a wave that
+// issues a whole 32 KB page stalls until most of it has arrived).  Wave w computes S for QK tile w (16 tokens, all heads); the
+// page maximum per head and P go through LDS; then wave w computes P V for
+// channel tiles 2w and 2w+1 over all 64 tokens.  Stores the page's (m, l, o)
+// partial per head at slot `split` (m, l in log2 units, o unnormalised).
+// All 256 threads; `limit` = tokens of the page that exist (>= 1).
+struct SplitPageLds {
+    float m[4][kMaxGroup], l[4][kMaxGroup];
+    uint4 p[2][64];  // PV A operand per k-step and lane (8 bf16)
+};
+
+__device__ void attend_page_split4(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
+                                   int limit, const bf16x8 (&qb)[4], float scale_log2, int G,
+                                   size_t head_row0, int nsplit, int split, float* __restrict__ po,
+                                   float2* __restrict__ pml, SplitPageLds& sh)
 {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, kq = lane >> 4;
-    __shared__ float m_lo[4][16];
-    float l = A.l;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (wave >= 4) {
-        if (kq == 0) {
-            sh.m[wave - 4][r] = A.m;
-            sh.l[wave - 4][r] = l;
-        }
+    const int lane8 = lane * 8;
+    uint4 ka[4], va[2][2];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
+    for (int st = 0; st < 4; ++st) ka[st] = ldg16(kb + (wave * 4 + st) * 512 + lane8);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sh.o[wave - 4][4 * kq + i][nt * 16 + r] = A.o[nt][i];
-    } else if (kq == 0) {
-        m_lo[wave][r] = A.m;
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) va[u][j] = ldg16(vb + (u * 8 + 2 * wave + j) * 512 + lane8);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(ka[st]), qb[st], acc);
+    // lane (r, kq): head r, tokens 32 (w >> 1) + 8 kq + 4 (w & 1) + i
+    float x[4], mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = 32 * (wave >> 1) + 8 * kq + 4 * (wave & 1) + i;
+        x[i] = tok < limit ? acc[i] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[i]);
     }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (kq == 0) sh.m[wave][r] = mx;
     __syncthreads();
-    if (wave < 4) {
-        // rows of this lane's accumulators: heads 4kq + i; of its (m, l): head r
+    float M = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 4 * kq + i;
-            const float ma = m_lo[wave][h], mb = sh.m[wave][h];
-            const float M = fmaxf(ma, mb);
-            const float wa = (M == -INFINITY || ma == -INFINITY) ? 0.f : fexp2(ma - M);
-            const float wb = (M == -INFINITY || mb == -INFINITY) ? 0.f : fexp2(mb - M);
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sh.m[w][r]);  // finite: token 0 exists
+    float ps = 0.f;
+    uint32_t pk[2];
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
-                A.o[nt][i] = A.o[nt][i] * wa + sh.o[wave][h][nt * 16 + r] * wb;
-        }
-        const float ma = A.m, mb = sh.m[wave][r];
-        const float M = fmaxf(ma, mb);
-        const float wa = (M == -INFINITY || ma == -INFINITY) ? 0.f : fexp2(ma - M);
-        const float wb = (M == -INFINITY || mb == -INFINITY) ? 0.f : fexp2(mb - M);
-        A.l = l * wa + sh.l[wave][r] * wb;  // already summed over the lane groups
-        A.m = M;
+    for (int i = 0; i < 4; ++i) x[i] = fexp2(x[i] - M);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ps += x[i];
+    {
+        bf16x8 t;
+        t[0] = (__bf16)x[0];
+        t[1] = (__bf16)x[1];
+        t[2] = (__bf16)x[2];
+        t[3] = (__bf16)x[3];
+        const uint4 w4 = __builtin_bit_cast(uint4, t);
+        pk[0] = w4.x;
+        pk[1] = w4.y;
     }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    if (kq == 0) sh.l[wave][r] = ps;
+    // elements 4 (w & 1) .. +3 of the k-step (w >> 1) operand of this lane
+    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(&sh.p[wave >> 1][lane]) + 8 * (wave & 1)) =
+        make_uint2(pk[0], pk[1]);
     __syncthreads();
-    // four-wave combine (the l above is complete: keep the lane-group sum from
-    // adding it four times)
-    if (wave < 4 && kq != 0) A.l = 0.f;
-    store_wg_partial(sh, A, G, head_row0, nsplit, split, po, pml);
+    f32x4 o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const bf16x8 pa = as_bf16x8(sh.p[u][lane]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) o[j] = mfma16(pa, as_bf16x8(va[u][j]), o[j]);
+    }
+    // o[j][i]: head 4 kq + i, channel 16 (2w + j) + r
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = 4 * kq + i;
+        if (h < G) {
+            float* dst = po + ((head_row0 + h) * nsplit + split) * D + 32 * wave + r;
+            dst[0] = o[0][i];
+            dst[16] = o[1][i];
+        }
+    }
+    if (wave == 0 && kq == 0 && r < G) {
+        const float L = sh.l[0][r] + sh.l[1][r] + sh.l[2][r] + sh.l[3][r];
+        pml[(head_row0 + r) * nsplit + split] = make_float2(M, L);
+    }
 }
 
-// Block importance of the pair into sI[0 .. nb): mean over the keys
-// overlapping block b (keys 4b-1 .. 4b+3 that exist) of
-// sigma[j] = sum_h 2^(z_h[j] - lse_h).  Thread tid computes whole blocks
-// b = tid + i NT from their five keys (key 4b-1 is also its left neighbour's
-// last key), so no block needs a second contribution; the order key of each
-// block it computed is returned in keys[i] (i < kSelKeyRounds, 0 past nb).
-// z (in LDS or global memory, at least 4 max_nb + 4 entries per head; keys
-// at or past nc are never read) was written by this workgroup (call after a
-// barrier).  Also writes scores_out.  All NT threads; ends with a barrier.
-template <int NT>
-__device__ __forceinline__ void pool_pair(const float* __restrict__ zg, int zstride, const float* lse,
-                                          int G, int nc, int nb, float* sI,
-                                          float* __restrict__ scores_out, int max_nb,
-                                          uint32_t (&keys)[kSelKeyRounds])
+// An empty partial (m = -inf, l = 0, o = 0) at slot `split`; all 256 threads.
+__device__ __forceinline__ void store_empty_partial(int G, size_t head_row0, int nsplit, int split,
+                                                    float* __restrict__ po, float2* __restrict__ pml)
 {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < kSelKeyRounds; ++i) keys[i] = 0u;
-#pragma unroll 1
-    for (int i = 0, b = tid; b < nb; ++i, b += NT) {
-        const int j0 = 4 * b;
-        float sg[4] = {0.f, 0.f, 0.f, 0.f}, sp = 0.f;
-#pragma unroll 1
-        for (int h0 = 0; h0 < G; h0 += 8) {
-            float4 zz[8];
-            float zp[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (h0 + u < G) {
-                    const float* zr = zg + (size_t)(h0 + u) * zstride;
-                    zz[u] = *reinterpret_cast<const float4*>(zr + j0);
-                    zp[u] = b > 0 ? zr[j0 - 1] : 0.f;
-                }
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (h0 + u < G) {
-                    const float lh = lse[h0 + u];
-                    sg[0] += fexp2(zz[u].x - lh);
-                    sg[1] += fexp2(zz[u].y - lh);
-                    sg[2] += fexp2(zz[u].z - lh);
-                    sg[3] += fexp2(zz[u].w - lh);
-                    sp += fexp2(zp[u] - lh);
-                }
-        }
-        const int jlo = max(j0 - 1, 0), jhi = min(j0 + 3, nc - 1);
-        float sum = (b > 0 && j0 - 1 < nc) ? sp : 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (j0 + e < nc) sum += sg[e];
-        const float I = jlo <= jhi ? sum / (float)(jhi - jlo + 1) : -INFINITY;
-        sI[b] = I;
-        if (scores_out) scores_out[b] = I;
-#pragma unroll
-        for (int r = 0; r < kSelKeyRounds; ++r)
-            if (r == i) keys[r] = order_key(I);
+    for (int x = threadIdx.x; x < G * (D / 4); x += 256) {
+        const int h = x / (D / 4), c4 = x % (D / 4);
+        reinterpret_cast<float4*>(po + ((head_row0 + h) * nsplit + split) * D)[c4] =
+            make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    if (scores_out)
-        for (int b = nb + tid; b < max_nb; b += NT) scores_out[b] = -INFINITY;
-    __syncthreads();
+    if ((int)threadIdx.x < G) pml[(head_row0 + threadIdx.x) * nsplit + split] = make_float2(-INFINITY, 0.f);
 }
 
-// --------------------------------------------------------------- step 1 ---
+// --------------------------------------------------------------- scoring ---
+//
+// Launch 1 of a decode step.  Workgroup (pair, c) scores pooled keys
+// [CK c, CK (c + 1)), CK = 64 T, of one (sequence, KV head) pair: wave w takes
+// tiles wT .. wT + T - 1 of 16 keys, every load in flight before the first
+// MFMA, so a short context is spread over many CUs (one CU streams only about
+// 100 GB/s).  Relative to the chunk's own per-head maximum m_h of
+// z_h[j] = scale log2(e) q_h . Kc_j it leaves, for every head h of the group:
+//   cml[pair][h][c]   = (m_h, sum over the chunk's keys of 2^(z_h[j] - m_h))
+//   bpart[pair][b][h] = sum over keys 4b-1 .. 4b+3 inside the chunk of
+//                       2^(z_h[j] - m_h), for the chunk's CK/4 blocks b
+//   spill[pair][h][c] = 2^(z_h[j] - m_h) of the chunk's last key j, which is
+//                       key 4b-1 of the first block b of the next chunk.
+// These are exact rescalings of the per-head softmax terms: the selection
+// multiplies them by 2^(m_h - lse_h) once every chunk's (m, sum) is known.
+// The chunk holding the key completed by the current token (tokens L-32 ..
+// L-1) pools it from K first (fp64 sum, one bf16 rounding), stores it to the
+// pooled-key page and substitutes it into its MFMA operand in registers.
 
-constexpr int kPairWaves = kStep1Waves;  // waves of a step-1 workgroup (512 threads)
-constexpr int kPairThreads = kPairWaves * 64;
-
-struct Step1Args {
+struct ScoreArgs {
     const uint16_t* q;
     const uint16_t* k_pool;
-    const uint16_t* v_pool;
     uint16_t* kc_pool;
     const int32_t* table;
     const int32_t* cu_k;
-    int max_blocks, Lmax, B, Hq, Hkv, G;
+    int max_blocks, num_pages, Lmax, Hq, Hkv, G, gp;
     float scale_log2;
-    int win_groups;  // window workgroups per pair (0 = none), one page per wave
-    int append;      // pool the key completed by the current token
-    float* z;        // [B][Hq][zstride] logits (log2 units), private to the pair's workgroup
-    int zstride;
-    int zl_stride;   // logits kept in LDS instead, [G][zl_stride] (0 = in z)
-    int do_select, topk, wblocks, max_nb, max_sel, top_span;
-    float* scores_out;  // [pairs][max_nb] or null
-    int32_t* sel_out;   // [pairs][max_sel] or null
-    int32_t* cnt_out;   // [pairs] or null
-    int2* selpg;        // [pairs][top_span] or null
-    float* po;
-    float2* pml;
-    int nsplit;  // partial slots per head
+    int append;  // pool the key completed by the current token
+    int nchunks, nbk;
+    float2* cml;
+    float* spill;
+    float* bpart;
 };
 
-// LDS of a step-1 workgroup (dynamic): the block importance, the page ids
-// and the logits of the pair (pair workgroups) or the wave states (window
-// workgroups).
-__host__ __device__ inline size_t step1_z_offset(int max_nb)
-{
-    const size_t b = (size_t)max_nb * (sizeof(float) + sizeof(int32_t));
-    return (b + 15) / 16 * 16;
-}
-inline size_t step1_lds_bytes(int max_nb, size_t zbytes)
-{
-    const size_t pair = step1_z_offset(max_nb) + zbytes;
-    return pair > sizeof(CombineLds) ? pair : sizeof(CombineLds);
-}
-constexpr size_t kStep1StaticLds = 10 * 1024;  // bound on the kernel's static LDS
+// LDS of a scoring workgroup: the chunk's logits, [G][CK + 4] floats.
+inline size_t score_lds_bytes(int T, int G) { return (size_t)G * (64 * T + 4) * sizeof(float); }
 
-struct PairLds {
-    float m[kPairWaves][kMaxGroup], s[kPairWaves][kMaxGroup];
-    SelectLds sel;
-};
-
-// The per-pair workgroup: scores every pooled key of one (sequence, KV head)
-// -- tiles of 16 keys strided over its eight waves, T tiles' loads in flight
-// per wave -- with per-wave (max, sum exp2) per head, keeps the logits in the
-// workspace (read back only by this workgroup), then pools block importance
-// and selects.  The wave owning the key completed by the current token
-// (tokens L-32 .. L-1) pools it from K first, stores it and substitutes it
-// into its MFMA operand.
-template <int T, bool ZL>
-__device__ void pair_part(const Step1Args& a, int s, int g, char* smem)
+template <int T>
+__global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
 {
-    __shared__ PairLds sh;
+    constexpr int CK = 64 * T;  // keys per chunk: kScoreWaves waves x T tiles x 16
+    constexpr int CB = CK / 4;  // blocks per chunk
+    constexpr int ZS = CK + 4;  // LDS row stride of the logits
+    static_assert(kScoreWaves == 4, "a chunk is four waves of T tiles");
+    extern __shared__ __align__(16) char smem[];
+    float* zl = reinterpret_cast<float*>(smem);  // [G][ZS]
+    __shared__ float wm[kScoreWaves][kMaxGroup], wsum[kScoreWaves][kMaxGroup];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
-    const int L = seq_len(a.cu_k, s, a.Lmax);
-    const int nc = dev_num_keys(L);
-    const int nb = (L + BS - 1) / BS;
+    const int pair = blockIdx.x / a.nchunks, c = blockIdx.x % a.nchunks;
+    const int s = pair / a.Hkv, g = pair % a.Hkv;
+    const int k0 = c * CK;
     const int32_t* trow = a.table + (size_t)s * a.max_blocks;
-    const size_t head_row0 = (size_t)s * a.Hq + g * a.G;
-    const size_t pair = (size_t)s * a.Hkv + g;
-    float* sI = reinterpret_cast<float*>(smem);
-    int32_t* spg = reinterpret_cast<int32_t*>(smem + sizeof(float) * a.max_nb);
-    // logits of head h, key j: zb[h * zs + j], in LDS or in the workspace
-    const int zs = ZL ? a.zl_stride : a.zstride;
-    float* zb = ZL ? reinterpret_cast<float*>(smem + step1_z_offset(a.max_nb))
-                   : a.z + head_row0 * a.zstride;
-    // The block-table row goes to LDS first (four loads in flight per
-    // thread), so no key load below waits on a table load: loads complete in
-    // order, so a table load issued behind other loads would wait for them.
-    // It is read up to the host bound max_nb (<= max_blocks_per_seq), so its
-    // loads and the query's do not wait for the length; entries past nb are
-    // never used.
-    for (int b0 = tid; b0 < a.max_nb; b0 += 4 * kPairThreads) {
-        int v[4];
+    const int kw = k0 + wave * T * 16;  // first key of this wave
+    // Table entries of this lane's keys, issued before the length is known
+    // (the row has max_blocks entries; those past the sequence may hold
+    // anything, so the page ids are clamped into the pool: their keys are
+    // masked), and the query.
+    int pg[T];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int b = b0 + u * kPairThreads;
-            v[u] = b < a.max_nb ? trow[b] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (b0 + u * kPairThreads < a.max_nb) spg[b0 + u * kPairThreads] = v[u];
+    for (int t = 0; t < T; ++t) {
+        const int blk = (kw + t * 16 + r) / SL;
+        pg[t] = trow[blk < a.max_blocks ? blk : a.max_blocks - 1];
     }
-
-    select_lds_clear<kPairThreads>(sh.sel);
     bf16x8 qb[4];
     load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
-    __syncthreads();
+    const int L = seq_len(a.cu_k, s, a.Lmax);
+    const int nc = dev_num_keys(L);
+    if (k0 >= nc) return;  // the pair has no key in this chunk (whole workgroup)
+    uint4 kv[T][4];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int p = min(max(pg[t], 0), a.num_pages - 1);
+        const uint16_t* kp = a.kc_pool + ((size_t)p * a.Hkv + g) * SL * D;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) kv[t][st] = ldg16(kp + kc_chunk((kw + t * 16 + r) % SL, st * 4 + kq));
+    }
     const int jn = nc - 1;
     const bool appending = a.append && L >= kPoolK && (L - kPoolK) % kPoolS == 0;
-    const int ntiles = (nc + 15) / 16;
-    // The wave whose batch holds key jn pools it and stores it before its
-    // first batch, which then loads it like every other key.
-    const bool app_mine = appending && (jn / 16) % kPairWaves == wave;
-    if (app_mine) {
+    if (appending && jn >= kw && jn < kw + T * 16) {  // wave-uniform
         const int tr = lane >> 4, cc = lane & 15;  // 4 token phases x 16 channel chunks
-        // tokens 16jn + tr + 4i, i < 8: their pages first, then all loads
+        // tokens 16 jn + tr + 4i, i < 8
         int kpg[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int b = (jn * kPoolS + tr + 4 * i) / BS;
-            kpg[i] = spg[b];
-        }
-        uint4 kr[8];
+        for (int i = 0; i < 8; ++i) kpg[i] = trow[(jn * kPoolS + tr + 4 * i) / BS];
+        uint4 kt[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int t = jn * kPoolS + tr + 4 * i;
-            kr[i] = ldg16(a.k_pool + ((size_t)kpg[i] * a.Hkv + g) * BS * D + k_chunk(t % BS, cc));
+            kt[i] = ldg16(a.k_pool + ((size_t)kpg[i] * a.Hkv + g) * BS * D + k_chunk(t % BS, cc));
         }
         double acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc8(acc, kr[i]);
+        for (int i = 0; i < 8; ++i) acc8(acc, kt[i]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             acc[e] += __shfl_xor(acc[e], 16);
             acc[e] += __shfl_xor(acc[e], 32);
         }
         const uint4 appkey = round8(acc);  // channels 8cc .. 8cc+7, same in every phase
-        if (tr == 0) {
-            const int pj = spg[jn / SL];
-            *reinterpret_cast<uint4*>(a.kc_pool + ((size_t)pj * a.Hkv + g) * SL * D + kc_chunk(jn % SL, cc)) = appkey;
-        }
-        // the key has reached L2 before this wave loads its tiles below (no
-        // other wave reads this page in this launch)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_s_waitcnt(0);
-    }
-    float m_run = -INFINITY, s_run = 0.f;  // head r, over this lane's keys
-    // tile i of the pair (keys 16i .. 16i + 15) goes to wave i % 8, T tiles
-    // of a wave per batch: tiles wave + 8 (bT + t), t < T
-    for (int b0 = wave; b0 < ntiles; b0 += kPairWaves * T) {
-        // page ids of this lane's keys for the whole batch before any key
-        // load; rows past the last key load that key again (their logits are
-        // masked below), so the loads need no branch
-        int pg[T], kr[T];
+        const int ta = (jn - kw) / 16, ra = (jn - kw) % 16;
+        int ppg = 0;
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int key = (b0 + kPairWaves * t) * 16 + r;
-            kr[t] = key < nc ? key : nc - 1;
-            pg[t] = spg[kr[t] / SL];
-        }
-        uint4 kv[T][4];
+        for (int t = 0; t < T; ++t)
+            if (t == ta) ppg = pg[t];
+        ppg = __shfl(ppg, ra);  // lane (ra, 0) holds key jn's page
+        if (tr == 0)
+            *reinterpret_cast<uint4*>(a.kc_pool + ((size_t)ppg * a.Hkv + g) * SL * D +
+                                      kc_chunk(jn % SL, cc)) = appkey;
+        // MFMA operand of key jn: lane (ra, kq), k-step st holds chunk 4 st + kq
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const uint16_t* kp = a.kc_pool + ((size_t)pg[t] * a.Hkv + g) * SL * D;
+        for (int st = 0; st < 4; ++st) {
+            const int src = st * 4 + kq;
+            const uint4 v = make_uint4(__shfl(appkey.x, src), __shfl(appkey.y, src),
+                                       __shfl(appkey.z, src), __shfl(appkey.w, src));
 #pragma unroll
-            for (int st = 0; st < 4; ++st) kv[t][st] = ldg16(kp + kc_chunk(kr[t] % SL, st * 4 + kq));
-        }
-        // every load of the batch is in flight before the first use
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int key0 = (b0 + kPairWaves * t) * 16;
-            if (key0 >= nc) continue;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(kv[t][st]), qb[st], acc);
-            float zv[4];
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = key0 + kq * 4 + i;
-                zv[i] = key < nc ? acc[i] * a.scale_log2 : -INFINITY;
-                tmax = fmaxf(tmax, zv[i]);
-            }
-            if (r < a.G)
-                *reinterpret_cast<float4*>(zb + r * zs + key0 + kq * 4) =
-                    make_float4(zv[0], zv[1], zv[2], zv[3]);
-            if (tmax != -INFINITY) {
-                const float mn = fmaxf(m_run, tmax);
-                float add = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) add += fexp2(zv[i] - mn);
-                s_run = s_run * fexp2(m_run - mn) + add;
-                m_run = mn;
-            }
+            for (int t = 0; t < T; ++t)
+                if (t == ta && r == ra) kv[t][st] = v;
         }
     }
-    // per-wave partials of every head -> LDS -> per-head log2-sum-exp2
+    __builtin_amdgcn_sched_barrier(0);
+    // logits -> LDS; this lane's (max, sum 2^(z - max)) for head r
+    float m_l = -INFINITY, s_l = 0.f;
+    float zv[T][4];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(kv[t][st]), qb[st], acc);
+        const int key0 = kw + t * 16 + kq * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            zv[t][i] = key0 + i < nc ? acc[i] * a.scale_log2 : -INFINITY;
+            m_l = fmaxf(m_l, zv[t][i]);
+        }
+        if (r < a.G)
+            *reinterpret_cast<float4*>(zl + r * ZS + (wave * T + t) * 16 + kq * 4) =
+                make_float4(zv[t][0], zv[t][1], zv[t][2], zv[t][3]);
+    }
+    if (m_l != -INFINITY) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_l += fexp2(zv[t][i] - m_l);
+    }
 #pragma unroll
     for (int off = 16; off < 64; off <<= 1) {
-        const float mo = __shfl_xor(m_run, off), so = __shfl_xor(s_run, off);
-        const float mn = fmaxf(m_run, mo);
-        s_run = mn == -INFINITY ? 0.f : s_run * fexp2(m_run - mn) + so * fexp2(mo - mn);
-        m_run = mn;
+        const float mo = __shfl_xor(m_l, off), so = __shfl_xor(s_l, off);
+        const float mn = fmaxf(m_l, mo);
+        s_l = mn == -INFINITY ? 0.f : s_l * fexp2(m_l - mn) + so * fexp2(mo - mn);
+        m_l = mn;
     }
     if (kq == 0 && r < a.G) {
-        sh.m[wave][r] = m_run;
-        sh.s[wave][r] = s_run;
+        wm[wave][r] = m_l;
+        wsum[wave][r] = s_l;
     }
-    if (!ZL) __builtin_amdgcn_s_waitcnt(0);  // this wave's logits have reached L2
     __syncthreads();
-    if (tid < a.G) {
-        // all sixteen LDS reads first, then independent exponentials
-        float mw[kPairWaves], sw[kPairWaves];
-#pragma unroll
-        for (int w = 0; w < kPairWaves; ++w) {
-            mw[w] = sh.m[w][tid];
-            sw[w] = sh.s[w][tid];
-        }
+    // per (block, head): the block's keys in this chunk, relative to the
+    // chunk maximum (finite: key k0 exists for every head)
+    const size_t prow = (size_t)pair * a.nbk + (size_t)c * CB;
+    const size_t crow = (size_t)pair * a.G * a.nchunks + c;  // + h * nchunks
+    for (int idx = tid; idx < a.G * CB; idx += kScoreWaves * 64) {
+        const int h = idx % a.G, bb = idx / a.G;
         float m = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kPairWaves; ++w)
-            if (sw[w] > 0.f) m = fmaxf(m, mw[w]);
-        float acc = 0.f;
+        for (int w = 0; w < kScoreWaves; ++w) m = fmaxf(m, wm[w][h]);
+        const float4 z4 = *reinterpret_cast<const float4*>(zl + h * ZS + 4 * bb);
+        float part = fexp2(z4.x - m) + fexp2(z4.y - m) + fexp2(z4.z - m) + fexp2(z4.w - m);
+        if (bb > 0) part += fexp2(zl[h * ZS + 4 * bb - 1] - m);
+        a.bpart[(prow + bb) * a.gp + h] = part;
+        if (bb == CB - 1) a.spill[crow + (size_t)h * a.nchunks] = fexp2(z4.w - m);
+    }
+    if (tid < a.G) {
+        float m = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kPairWaves; ++w)
-            if (sw[w] > 0.f) acc += sw[w] * fexp2(mw[w] - m);
-        sh.sel.lse[tid] = m + log2f(acc);
-    }
-    __syncthreads();
-    uint32_t keys[kSelKeyRounds];
-    pool_pair<kPairThreads>(zb, zs, sh.sel.lse, a.G, nc, nb, sI,
-                            a.scores_out ? a.scores_out + pair * a.max_nb : nullptr, a.max_nb, keys);
-    if (!a.do_select) return;
-    select_blocks_wg<kPairWaves, true>(keys, sI, nb, a.wblocks, a.topk, sh.sel,
-                                 a.sel_out ? a.sel_out + pair * a.max_sel : nullptr,
-                                 a.cnt_out ? a.cnt_out + pair : nullptr, a.max_sel,
-                                 a.selpg ? a.selpg + pair * a.top_span : nullptr, nullptr,
-                                 a.top_span, trow, spg);
-}
-
-// Window workgroup: wave w attends window slot 8*grp + w, slot x being block
-// nb - min(nb, wblocks) + x, and the workgroup stores one partial.
-__device__ void window_part(const Step1Args& a, int s, int g, int grp, char* smem)
-{
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r = lane & 15, kq = lane >> 4;
-    const int L = seq_len(a.cu_k, s, a.Lmax);
-    const int nb = (L + BS - 1) / BS;
-    const int wn = nb < a.wblocks ? nb : a.wblocks;
-    AttnState A;
-    attn_init(A);
-    bf16x8 qb[4];
-    load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
-    const int slot = grp * kPairWaves + wave;
-    if (slot < wn) {
-        const int b = nb - wn + slot;
-        const int page = a.table[(size_t)s * a.max_blocks + b];
-        const uint16_t* kb = a.k_pool + ((size_t)page * a.Hkv + g) * BS * D;
-        const uint16_t* vb = a.v_pool + ((size_t)page * a.Hkv + g) * D * BS;
-        attend_page(kb, vb, L - b * BS, qb, a.scale_log2, r, kq, A);
-    }
-    store_wg_partial8(*reinterpret_cast<CombineLds*>(smem), A, a.G, (size_t)s * a.Hq + g * a.G,
-                      a.nsplit, grp, a.po, a.pml);
-}
-
-template <int T, bool ZL>
-__global__ __launch_bounds__(512) void step1_kernel(Step1Args a)
-{
-    extern __shared__ __align__(16) char smem[];
-    // pair workgroups first: they carry the launch's critical path
-    const int npairs = a.B * a.Hkv;
-    int wg = blockIdx.x;
-    if (wg < npairs) {
-        pair_part<T, ZL>(a, wg / a.Hkv, wg % a.Hkv, smem);
-    } else {
-        wg -= npairs;
-        const int pair = wg / a.win_groups, grp = wg % a.win_groups;
-        window_part(a, pair / a.Hkv, pair % a.Hkv, grp, smem);
+        for (int w = 0; w < kScoreWaves; ++w) m = fmaxf(m, wm[w][tid]);
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kScoreWaves; ++w)
+            if (wsum[w][tid] > 0.f) sum += wsum[w][tid] * fexp2(wm[w][tid] - m);
+        a.cml[crow + (size_t)tid * a.nchunks] = make_float2(m, sum);
     }
 }
 
-// --------------------------------------------------------------- step 2 ---
+// ----------------------------------------------- selection + attention ---
+//
+// Launch 2 of a decode step, two kinds of four-wave workgroups per pair:
+//  - `wslots` window workgroups, one page of the local window each (slot x =
+//    block nb - wn + x, wn = min(nb, window blocks)), attended by the four
+//    waves together: the window needs no selection, so these stream from
+//    HBM on every CU while the top workgroups select; partial slot
+//    groups + x (an empty partial past wn);
+//  - `groups` top workgroups.  Every one recomputes the pair's selection
+//    from the scoring partials -- per-head log-sum-exp over the chunks,
+//    block importance, top-k -- a few microseconds of LDS work (latency,
+//    not bandwidth) that replaces a hand-off between workgroups; it then
+//    attends its slice of the picks, one page per wave (picks
+//    4 R k .. 4 R (k+1) - 1), and stores one partial at slot k.
+//
+// Block importance: I[b] = mean over keys j of 4b-1 .. 4b+3 below n_c of
+// sum_h 2^(z_h[j] - lse_h) -- the softmax over the pooled keys per query
+// head, summed over the group, pooled over the keys whose window overlaps
+// block b (page "NOSA-1B 模型家族全景", core principle, CIS score mean pooling;
+// page "NOSA-1B 性能基准全解析" section 三.3).
 
-struct Step2Args {
+constexpr int kMaxRounds = 8;  // top-k blocks per wave (compiled limit of the plan)
+
+struct TopArgs {
     const uint16_t* q;
     const uint16_t* k_pool;
     const uint16_t* v_pool;
     const int32_t* table;
     const int32_t* cu_k;
-    int max_blocks, Lmax, B, Hq, Hkv, G;
+    int max_blocks, Lmax, Hq, Hkv, G, gp;
     float scale_log2;
-    int groups;         // workgroups per pair
-    int rounds;         // blocks per wave
-    const int2* selpg;  // decode mode: [pairs][span] (block, page), -1 padded
-    const int32_t* sel; // attend mode: [pairs][max_sel] block ids
-    const int32_t* cnt; //              [pairs]
-    int span, max_sel;
+    int chunk_keys, cb_shift, nchunks, nbk;  // cb_shift = log2(chunk_keys / 4)
+    const float2* cml;
+    const float* spill;
+    const float* bpart;
+    int topk, wblocks, max_nb, max_sel;
+    int groups, rounds;  // top workgroups per pair; top-k blocks per wave
+    int wslots;          // window workgroups per pair (0 in importance-only mode)
+    int ntop, nwin;      // top / window workgroups of the launch
+    int tpx, wpx;        // top / window workgroups per XCD
+    int scores_only;     // importance only (no selection, no attention)
+    float* scores_out;   // [pairs][max_nb] or null (workgroup 0 of a pair writes)
+    int32_t* sel_out;    // [pairs][max_sel] or null (workgroup 0 of a pair writes)
+    int32_t* cnt_out;    // [pairs] or null
     float* po;
     float2* pml;
-    int nsplit, split0;  // partial slots per head; this kernel writes [split0, split0+groups)
+};
+
+struct alignas(16) TopLds {
+    union {
+        struct {
+            float f[kMaxChunks][kMaxGroup];   // 2^(m_ch - lse_h): chunk partials -> softmax weights
+            float fs[kMaxChunks][kMaxGroup];  // f[c][h] * spill[c][h]
+            SelectLds sel;
+        };
+        SplitPageLds page;  // window workgroups
+    };
+    CombineLds comb;
+    int2 list[kStep2Waves * kMaxRounds];
+};
+
+// Dynamic LDS of a top workgroup: the block-table row, and the importance
+// of blocks past the register rounds.
+inline size_t top_lds_bytes(int max_nb, int krb)
+{
+    const size_t row = ((size_t)max_nb * sizeof(int32_t) + 15) / 16 * 16;
+    return row + (max_nb > krb * 256 ? (size_t)max_nb * sizeof(float) : 16);
+}
+
+// Importance of block b from its partial row (heads 4u .. 4u+3 in bv[u]).
+template <int GP4>
+__device__ __forceinline__ float block_importance(int b, int nc, int cb_shift, int nvalid, int G,
+                                                  const float4 (&bv)[GP4], const TopLds& sh)
+{
+    const int c = b >> cb_shift;
+    float sum = 0.f;
+    if (c < nvalid) {
+#pragma unroll
+        for (int u = 0; u < GP4; ++u) {
+            const float4 f4 = *reinterpret_cast<const float4*>(&sh.f[c][4 * u]);
+            const float v[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
+            const float f[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * u + e < G) sum += f[e] * v[e];
+        }
+    }
+    if (b > 0 && (b & ((1 << cb_shift) - 1)) == 0 && 4 * b - 1 < nc)
+        for (int h = 0; h < G; ++h) sum += sh.fs[c - 1][h];
+    const int jlo = 4 * b - 1 > 0 ? 4 * b - 1 : 0;
+    const int jhi = 4 * b + 3 < nc - 1 ? 4 * b + 3 : nc - 1;
+    return jlo <= jhi ? sum / (float)(jhi - jlo + 1) : -INFINITY;
+}
+
+// KRB: candidate rounds of 256 blocks whose importance stays in registers
+// (1, 2, 4 or 8; blocks past KRB * 256 go through LDS, only when KRB = 8).
+// GP4: float4 loads per block of the partial row (G <= 4 GP4).
+template <int KRB, int GP4>
+__global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
+{
+    constexpr int NT = kStep2Waves * 64;
+    static_assert(KRB <= kSelKeyRounds, "register rounds of the selector");
+    extern __shared__ __align__(16) char smem[];
+    __shared__ TopLds sh;
+    // XCD x (workgroups are dealt to XCDs round-robin by index) runs top
+    // workgroups x * tpx .. x * tpx + tpx - 1 first, then window workgroups
+    // x * wpx .. x * wpx + wpx - 1: the same pairs, so they share an L2, and
+    // the CUs each get one top workgroup before any gets a second.
+    const int xcd = (int)(blockIdx.x % 8), pos = (int)(blockIdx.x / 8);
+    const bool window = pos >= a.tpx;
+    const int lid = window ? xcd * a.wpx + (pos - a.tpx) : xcd * a.tpx + pos;
+    if (lid >= (window ? a.nwin : a.ntop)) return;  // whole workgroup
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, kq = lane >> 4;
+    const int pair = window ? lid / a.wslots : lid / a.groups;
+    const int k = window ? lid % a.wslots : lid % a.groups;
+    const int s = pair / a.Hkv, g = pair % a.Hkv;
+    const int L = seq_len(a.cu_k, s, a.Lmax);
+    const int nb = (L + BS - 1) / BS;
+    const int nc = dev_num_keys(L);
+    const int32_t* trow = a.table + (size_t)s * a.max_blocks;
+    const size_t head_row0 = (size_t)s * a.Hq + g * a.G;
+    const int nsplit = a.groups + a.wslots;
+
+    if (window) {  // window slot k
+        const int wn = nb < a.wblocks ? nb : a.wblocks;
+        if (k < wn) {
+            bf16x8 qb[4];
+            load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
+            const int b = nb - wn + k;
+            const int page = trow[b];
+            attend_page_split4(a.k_pool + ((size_t)page * a.Hkv + g) * BS * D,
+                               a.v_pool + ((size_t)page * a.Hkv + g) * D * BS, L - b * BS, qb,
+                               a.scale_log2, a.G, head_row0, nsplit, a.groups + k, a.po, a.pml,
+                               sh.page);
+        } else {
+            store_empty_partial(a.G, head_row0, nsplit, a.groups + k, a.po, a.pml);
+        }
+        return;
+    }
+
+    // ---- top workgroup k: the pair's selection, then picks 4 R k .. 4 R (k+1) - 1
+    int32_t* spg = reinterpret_cast<int32_t*>(smem);  // block-table row
+    float* sI = reinterpret_cast<float*>(smem + ((size_t)a.max_nb * sizeof(int32_t) + 15) / 16 * 16);
+    const int CK = a.chunk_keys;
+    const int nvalid = (nc + CK - 1) / CK;  // chunks holding keys of this pair, <= 64
+
+    // Loads, in the order they are needed (they complete in order, so each
+    // wait below covers only what was issued before), none of them waiting
+    // for the sequence length: chunk partials (lane = chunk, heads wave + 4u;
+    // chunks past the pair's last are masked later), this thread's importance
+    // partials and block-table entries, the query.  Every address is clamped
+    // in range, so no load needs a branch.
+    float2 cv[4];
+    float sv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int h = wave + 4 * u < a.G ? wave + 4 * u : a.G - 1;
+        const size_t o = ((size_t)pair * a.G + h) * a.nchunks + (lane < a.nchunks ? lane : 0);
+        cv[u] = a.cml[o];
+        sv[u] = a.spill[o];
+    }
+    float4 bv[KRB][GP4];
+#pragma unroll
+    for (int i = 0; i < KRB; ++i) {
+        const int b = i * NT + tid < a.nbk ? i * NT + tid : a.nbk - 1;
+        const float4* src = reinterpret_cast<const float4*>(a.bpart + ((size_t)pair * a.nbk + b) * a.gp);
+#pragma unroll
+        for (int u = 0; u < GP4; ++u) bv[i][u] = src[u * 4 < a.gp ? u : 0];
+    }
+    int tv[KRB];
+#pragma unroll
+    for (int i = 0; i < KRB; ++i) tv[i] = trow[i * NT + tid < a.max_nb ? i * NT + tid : a.max_nb - 1];
+    bf16x8 qb[4];
+    load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
+    select_lds_clear<NT>(sh.sel);
+    // per-head log2-sum-exp2 over the chunks, then each chunk's weight
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int h = wave + 4 * u;
+        if (h >= a.G) break;
+        const bool ok = lane < nvalid;
+        const float m = ok ? cv[u].x : -INFINITY;
+        const float M = wave_max_f(m);
+        const float S = wave_sum_f(ok ? cv[u].y * fexp2(m - M) : 0.f);
+        const float lse = M + log2f(S);
+        const float f = ok ? fexp2(m - lse) : 0.f;
+        sh.f[lane][h] = f;
+        sh.fs[lane][h] = ok ? f * sv[u] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < KRB; ++i)
+        if (i * NT + tid < a.max_nb) spg[i * NT + tid] = tv[i];
+    __syncthreads();
+    uint32_t keys[kSelKeyRounds];
+#pragma unroll
+    for (int i = 0; i < kSelKeyRounds; ++i) keys[i] = 0u;
+    float* so = a.scores_out && k == 0 ? a.scores_out + (size_t)pair * a.max_nb : nullptr;
+#pragma unroll
+    for (int i = 0; i < KRB; ++i) {
+        const int b = i * NT + tid;
+        if (b < nb) {
+            const float I = block_importance<GP4>(b, nc, a.cb_shift, nvalid, a.G, bv[i], sh);
+            keys[i] = order_key(I);
+            if (so) so[b] = I;
+        }
+    }
+    // contexts past KRB * 256 blocks: the rest of the row and of the
+    // importance through LDS
+    for (int b = KRB * NT + tid; b < a.max_nb; b += NT) {
+        spg[b] = trow[b];
+        if (b >= nb) continue;
+        float4 bw[GP4];
+        const int bc = b < a.nbk ? b : a.nbk - 1;
+        const float4* src = reinterpret_cast<const float4*>(a.bpart + ((size_t)pair * a.nbk + bc) * a.gp);
+#pragma unroll
+        for (int u = 0; u < GP4; ++u) bw[u] = src[u * 4 < a.gp ? u : 0];
+        const float I = block_importance<GP4>(b, nc, a.cb_shift, nvalid, a.G, bw, sh);
+        sI[b] = I;
+        if (so) so[b] = I;
+    }
+    if (so)
+        for (int b = nb + tid; b < a.max_nb; b += NT) so[b] = -INFINITY;
+    if (a.scores_only) return;
+    const int ncand = nb > a.wblocks ? nb - a.wblocks : 0;
+    const bool in_regs = ncand <= KRB * NT;  // every candidate's key is in keys[]
+    if (in_regs) select_wave_range<NT, kSelKeyRounds>(keys, ncand, sh.sel);
+    __syncthreads();  // sI, the rest of the row, the key ranges
+    const int lo = k * a.rounds * kStep2Waves;
+    select_blocks_wg<kStep2Waves, true>(keys, sI, nb, a.wblocks, a.topk, sh.sel,
+                                        a.sel_out && k == 0 ? a.sel_out + (size_t)pair * a.max_sel : nullptr,
+                                        a.cnt_out && k == 0 ? a.cnt_out + pair : nullptr, a.max_sel,
+                                        sh.list, lo, a.rounds * kStep2Waves, spg, in_regs);
+    __syncthreads();  // the list
+    AttnState A;
+    attn_init(A);
+#pragma unroll 1
+    for (int rr = 0; rr < a.rounds; ++rr) {
+        const int2 e = sh.list[rr * kStep2Waves + wave];
+        if (e.x < 0) continue;
+        attend_page(a.k_pool + ((size_t)e.y * a.Hkv + g) * BS * D,
+                    a.v_pool + ((size_t)e.y * a.Hkv + g) * D * BS, L - e.x * BS, qb, a.scale_log2,
+                    r, kq, A);
+    }
+    store_wg_partial(sh.comb, A, a.G, head_row0, nsplit, k, a.po, a.pml);
+}
+
+// ------------------------------------------------ attention (alone) ---
+
+struct AttendArgs {
+    const uint16_t* q;
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    const int32_t* table;
+    const int32_t* cu_k;
+    int max_blocks, Lmax, Hq, Hkv, G;
+    float scale_log2;
+    int groups;          // workgroups per pair
+    const int32_t* sel;  // [pairs][max_sel] block ids
+    const int32_t* cnt;  // [pairs]
+    int max_sel;
+    float* po;
+    float2* pml;
 };
 
 // Combination of the nsplit partials (m_i, l_i, o_i) of each head row into
@@ -640,12 +777,12 @@ static hipError_t launch_merge(const Plan& pl, const Workspace& w, int nsplit, f
     return hipGetLastError();
 }
 
-// Workgroup = kStep2Waves (4) waves; wave w handles entries
-// (grp*rounds + rr)*4 + w of the pair's list, rr < rounds, one 64-token
-// block at a time.
+// Attention over given block lists: workgroup = kStep2Waves (4) waves; wave
+// w handles list entries (grp*R + rr)*4 + w, rr < R, one 64-token block at a
+// time, and the workgroup stores one partial per head at slot grp.
 static_assert(kStep2Waves == 4, "store_wg_partial combines four waves");
-template <bool kDecode, int R>
-__global__ __launch_bounds__(kStep2Waves * 64) void step2_kernel(Step2Args a)
+template <int R>
+__global__ __launch_bounds__(kStep2Waves * 64) void attend_kernel(AttendArgs a)
 {
     __shared__ CombineLds sh;
     const int pair = blockIdx.x / a.groups, grp = blockIdx.x % a.groups;
@@ -655,8 +792,7 @@ __global__ __launch_bounds__(kStep2Waves * 64) void step2_kernel(Step2Args a)
     const int L = seq_len(a.cu_k, s, a.Lmax);
     const int nb = (L + BS - 1) / BS;
     const int32_t* trow = a.table + (size_t)s * a.max_blocks;
-    int n = 0;
-    if (!kDecode) n = min(a.cnt[pair], a.max_sel);
+    const int n = min(a.cnt[pair], a.max_sel);
     AttnState A;
     attn_init(A);
     bf16x8 qb[4];
@@ -665,13 +801,7 @@ __global__ __launch_bounds__(kStep2Waves * 64) void step2_kernel(Step2Args a)
     for (int rr = 0; rr < R; ++rr) {
         const int idx = (grp * R + rr) * kStep2Waves + wave;
         int b = -1, page = -1;
-        if (kDecode) {
-            if (idx < a.span) {
-                const int2 e = a.selpg[(size_t)pair * a.span + idx];
-                b = e.x;
-                page = e.y;
-            }
-        } else if (idx < n) {
+        if (idx < n) {
             b = a.sel[(size_t)pair * a.max_sel + idx];
             if (b >= 0 && b < nb) page = trow[b];
         }
@@ -680,7 +810,7 @@ __global__ __launch_bounds__(kStep2Waves * 64) void step2_kernel(Step2Args a)
         const uint16_t* vb = a.v_pool + ((size_t)page * a.Hkv + g) * D * BS;
         attend_page(kb, vb, L - b * BS, qb, a.scale_log2, r, kq, A);
     }
-    store_wg_partial(sh, A, a.G, (size_t)s * a.Hq + g * a.G, a.nsplit, a.split0 + grp, a.po, a.pml);
+    store_wg_partial(sh, A, a.G, (size_t)s * a.Hq + g * a.G, a.groups, grp, a.po, a.pml);
 }
 
 // ------------------------------------------------------ select (alone) ---
@@ -716,55 +846,11 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
     select_lds_clear<256>(sh);
     __syncthreads();
     uint32_t keys[kSelKeyRounds];
-    select_blocks_wg<4, false>(keys, sI, nb, wblocks, topk, sh, sel + pair * max_sel, cnt + pair, max_sel,
-                        nullptr, nullptr, 0, nullptr);
+    select_blocks_wg<4, false>(keys, sI, nb, wblocks, topk, sh, sel + pair * max_sel, cnt + pair,
+                               max_sel, nullptr, 0, 0, nullptr);
 }
 
 // ---------------------------------------------------------- launchers ---
-
-template <bool kDecode>
-static hipError_t launch_step2(const Step2Args& b, int grid, hipStream_t stream)
-{
-    switch (b.rounds) {
-        case 1: hipLaunchKernelGGL((step2_kernel<kDecode, 1>), dim3(grid), dim3(kStep2Waves * 64), 0, stream, b); break;
-        case 2: hipLaunchKernelGGL((step2_kernel<kDecode, 2>), dim3(grid), dim3(kStep2Waves * 64), 0, stream, b); break;
-        case 3: hipLaunchKernelGGL((step2_kernel<kDecode, 3>), dim3(grid), dim3(kStep2Waves * 64), 0, stream, b); break;
-        case 4: hipLaunchKernelGGL((step2_kernel<kDecode, 4>), dim3(grid), dim3(kStep2Waves * 64), 0, stream, b); break;
-        case 6: hipLaunchKernelGGL((step2_kernel<kDecode, 6>), dim3(grid), dim3(kStep2Waves * 64), 0, stream, b); break;
-        default: hipLaunchKernelGGL((step2_kernel<kDecode, 8>), dim3(grid), dim3(kStep2Waves * 64), 0, stream, b); break;
-    }
-    return hipGetLastError();
-}
-
-static Step1Args step1_args(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
-                            const int32_t* cu_k, const Workspace& w)
-{
-    Step1Args a{};
-    a.q = q;
-    a.k_pool = kv.k_pool;
-    a.v_pool = kv.v_pool;
-    a.kc_pool = kv.kc_pool;
-    a.table = kv.block_table;
-    a.cu_k = cu_k;
-    a.max_blocks = kv.max_blocks_per_seq;
-    a.Lmax = pl.Lmax;
-    a.B = pl.B;
-    a.Hq = pl.Hq;
-    a.Hkv = pl.Hkv;
-    a.G = pl.G;
-    a.scale_log2 = pl.scale_log2;
-    a.z = w.z;
-    a.zstride = pl.zstride;
-    a.topk = pl.topk;
-    a.wblocks = pl.wblocks;
-    a.max_nb = pl.max_nb;
-    a.max_sel = pl.max_sel;
-    a.top_span = pl.top_span;
-    a.po = w.po;
-    a.pml = w.pml;
-    a.nsplit = pl.nsplit;
-    return a;
-}
 
 // Largest LDS a workgroup may use on the current device (queried once per
 // device).
@@ -783,44 +869,111 @@ static size_t device_lds_limit()
     return cached[dev];
 }
 
-template <int T, bool ZL>
-static void launch_step1_t(dim3 grid, size_t lds, const Step1Args& a, hipStream_t stream)
+static hipError_t launch_score(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
+                               const int32_t* cu_k, const Workspace& w, int append,
+                               hipStream_t stream)
 {
-    if (lds > 64 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&step1_kernel<T, ZL>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL((step1_kernel<T, ZL>), grid, dim3(kPairThreads), lds, stream, a);
+    ScoreArgs a{};
+    a.q = q;
+    a.k_pool = kv.k_pool;
+    a.kc_pool = kv.kc_pool;
+    a.table = kv.block_table;
+    a.cu_k = cu_k;
+    a.max_blocks = kv.max_blocks_per_seq;
+    a.num_pages = kv.num_pages;
+    a.Lmax = pl.Lmax;
+    a.Hq = pl.Hq;
+    a.Hkv = pl.Hkv;
+    a.G = pl.G;
+    a.gp = pl.gp;
+    a.scale_log2 = pl.scale_log2;
+    a.append = append;
+    a.nchunks = pl.nchunks;
+    a.nbk = pl.nbk;
+    a.cml = w.cml;
+    a.spill = w.spill;
+    a.bpart = w.bpart;
+    const dim3 grid(pl.B * pl.Hkv * pl.nchunks), block(kScoreWaves * 64);
+    const size_t lds = score_lds_bytes(pl.score_tiles, pl.G);  // <= 16 x 516 floats
+    switch (pl.score_tiles) {
+        case 1: hipLaunchKernelGGL(score_kernel<1>, grid, block, lds, stream, a); break;
+        case 2: hipLaunchKernelGGL(score_kernel<2>, grid, block, lds, stream, a); break;
+        case 4: hipLaunchKernelGGL(score_kernel<4>, grid, block, lds, stream, a); break;
+        default: hipLaunchKernelGGL(score_kernel<8>, grid, block, lds, stream, a); break;
+    }
+    return hipGetLastError();
 }
 
-static hipError_t launch_step1(const Plan& pl, Step1Args a, hipStream_t stream)
+static TopArgs top_args(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
+                        const int32_t* cu_k, const Workspace& w)
 {
-    const int npairs = pl.B * pl.Hkv;
-    dim3 grid(npairs * (1 + a.win_groups));
-    // logits in LDS when they fit beside everything else
-    // the scoring writes whole tiles of 16 keys, the pooling reads keys up to
-    // 4 max_nb + 3 (never past n_c, but the float4 covering them)
-    const int zneed = (pl.max_nc + 15) / 16 * 16 > 4 * pl.max_nb + 4 ? (pl.max_nc + 15) / 16 * 16
-                                                                    : 4 * pl.max_nb + 4;
-    const int zls = zneed + 4;
-    const size_t zbytes = (size_t)pl.G * zls * sizeof(float);
-    const size_t limit = device_lds_limit();
-    if (step1_lds_bytes(pl.max_nb, 0) + kStep1StaticLds > limit) return hipErrorInvalidValue;
-    const bool zl = step1_lds_bytes(pl.max_nb, zbytes) + kStep1StaticLds <= limit;
-    a.zl_stride = zl ? zls : 0;
-    const size_t lds = step1_lds_bytes(pl.max_nb, zl ? zbytes : 0);
-#define NOSA_STEP1(T)                                           \
-    (zl ? launch_step1_t<T, true>(grid, lds, a, stream)         \
-        : launch_step1_t<T, false>(grid, lds, a, stream))
-    switch (pl.score_tiles) {
-        case 1: NOSA_STEP1(1); break;
-        case 2: NOSA_STEP1(2); break;
-        case 3: NOSA_STEP1(3); break;
-        case 5: NOSA_STEP1(5); break;
-        case 7: NOSA_STEP1(7); break;
-        case 9: NOSA_STEP1(9); break;
-        default: NOSA_STEP1(12); break;
+    TopArgs a{};
+    a.q = q;
+    a.k_pool = kv.k_pool;
+    a.v_pool = kv.v_pool;
+    a.table = kv.block_table;
+    a.cu_k = cu_k;
+    a.max_blocks = kv.max_blocks_per_seq;
+    a.Lmax = pl.Lmax;
+    a.Hq = pl.Hq;
+    a.Hkv = pl.Hkv;
+    a.G = pl.G;
+    a.gp = pl.gp;
+    a.scale_log2 = pl.scale_log2;
+    a.chunk_keys = pl.chunk_keys;
+    a.cb_shift = 31 - __builtin_clz((unsigned)(pl.chunk_keys / 4));
+    a.nchunks = pl.nchunks;
+    a.nbk = pl.nbk;
+    a.cml = w.cml;
+    a.spill = w.spill;
+    a.bpart = w.bpart;
+    a.topk = pl.topk;
+    a.wblocks = pl.wblocks;
+    a.max_nb = pl.max_nb;
+    a.max_sel = pl.max_sel;
+    a.po = w.po;
+    a.pml = w.pml;
+    return a;
+}
+
+template <int KRB, int GP4>
+static void launch_top_t(dim3 grid, size_t lds, const TopArgs& a, hipStream_t stream)
+{
+    if (lds > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&top_kernel<KRB, GP4>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL((top_kernel<KRB, GP4>), grid, dim3(kStep2Waves * 64), lds, stream, a);
+}
+
+template <int KRB>
+static void launch_top_k(dim3 grid, size_t lds, int gp4, const TopArgs& a, hipStream_t stream)
+{
+    switch (gp4) {
+        case 1: launch_top_t<KRB, 1>(grid, lds, a, stream); break;
+        case 2: launch_top_t<KRB, 2>(grid, lds, a, stream); break;
+        default: launch_top_t<KRB, 4>(grid, lds, a, stream); break;
     }
-#undef NOSA_STEP1
+}
+
+// Grid: eight XCDs x (tpx top + wpx window workgroups); see top_kernel.
+static hipError_t launch_top(const Plan& pl, TopArgs a, hipStream_t stream)
+{
+    const int nr = ceil_div(pl.max_nb, kStep2Waves * 64);
+    const int krb = nr <= 1 ? 1 : nr <= 2 ? 2 : nr <= 4 ? 4 : 8;
+    const size_t lds = top_lds_bytes(pl.max_nb, krb);
+    if (lds + sizeof(TopLds) > device_lds_limit()) return hipErrorInvalidValue;
+    a.ntop = pl.B * pl.Hkv * a.groups;
+    a.nwin = pl.B * pl.Hkv * a.wslots;
+    a.tpx = ceil_div(a.ntop, 8);
+    a.wpx = ceil_div(a.nwin, 8);
+    const dim3 grid(8 * (a.tpx + a.wpx));
+    const int gp4 = pl.gp / 4;
+    switch (krb) {
+        case 1: launch_top_k<1>(grid, lds, gp4, a, stream); break;
+        case 2: launch_top_k<2>(grid, lds, gp4, a, stream); break;
+        case 4: launch_top_k<4>(grid, lds, gp4, a, stream); break;
+        default: launch_top_k<8>(grid, lds, gp4, a, stream); break;
+    }
     return hipGetLastError();
 }
 
@@ -828,12 +981,15 @@ hipError_t launch_scores_only(const Plan& pl, const nosa_paged_kv& kv, const nos
                               const int32_t* cu_k, const Workspace& w, float* scores_out,
                               hipStream_t stream)
 {
-    Step1Args a = step1_args(pl, kv, q, cu_k, w);
-    a.win_groups = 0;
-    a.append = 0;
-    a.do_select = 0;
+    hipError_t e = launch_score(pl, kv, q, cu_k, w, 0, stream);
+    if (e != hipSuccess) return e;
+    TopArgs a = top_args(pl, kv, q, cu_k, w);
+    a.groups = 1;
+    a.rounds = 1;
+    a.wslots = 0;
+    a.scores_only = 1;
     a.scores_out = scores_out;
-    return launch_step1(pl, a, stream);
+    return launch_top(pl, a, stream);
 }
 
 hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
@@ -841,39 +997,16 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
                          int32_t* sel_out, int32_t* cnt_out, float* scores_out,
                          hipStream_t stream)
 {
-    Step1Args a = step1_args(pl, kv, q, cu_k, w);
-    a.win_groups = pl.win_groups;
-    a.append = 1;
-    a.do_select = 1;
+    hipError_t e = launch_score(pl, kv, q, cu_k, w, 1, stream);
+    if (e != hipSuccess) return e;
+    TopArgs a = top_args(pl, kv, q, cu_k, w);
+    a.groups = pl.top_groups;
+    a.rounds = pl.top_rounds;
+    a.wslots = pl.wslots;
     a.scores_out = scores_out;
     a.sel_out = sel_out;
     a.cnt_out = cnt_out;
-    a.selpg = w.selpg;
-    hipError_t e = launch_step1(pl, a, stream);
-    if (e != hipSuccess) return e;
-
-    Step2Args b{};
-    b.q = q;
-    b.k_pool = kv.k_pool;
-    b.v_pool = kv.v_pool;
-    b.table = kv.block_table;
-    b.cu_k = cu_k;
-    b.max_blocks = kv.max_blocks_per_seq;
-    b.Lmax = pl.Lmax;
-    b.B = pl.B;
-    b.Hq = pl.Hq;
-    b.Hkv = pl.Hkv;
-    b.G = pl.G;
-    b.scale_log2 = pl.scale_log2;
-    b.groups = pl.top_groups;
-    b.rounds = pl.top_rounds;
-    b.selpg = w.selpg;
-    b.span = pl.top_span;
-    b.po = w.po;
-    b.pml = w.pml;
-    b.nsplit = pl.nsplit;
-    b.split0 = pl.win_groups;
-    e = launch_step2<true>(b, pl.B * pl.Hkv * pl.top_groups, stream);
+    e = launch_top(pl, a, stream);
     if (e != hipSuccess) return e;
     return launch_merge(pl, w, pl.nsplit, out, lse, stream);
 }
@@ -882,7 +1015,7 @@ hipError_t launch_attend(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
                          const int32_t* cu_k, const int32_t* sel, const int32_t* cnt,
                          const Workspace& w, float* out, float* lse, hipStream_t stream)
 {
-    Step2Args b{};
+    AttendArgs b{};
     b.q = q;
     b.k_pool = kv.k_pool;
     b.v_pool = kv.v_pool;
@@ -890,21 +1023,26 @@ hipError_t launch_attend(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
     b.cu_k = cu_k;
     b.max_blocks = kv.max_blocks_per_seq;
     b.Lmax = pl.Lmax;
-    b.B = pl.B;
     b.Hq = pl.Hq;
     b.Hkv = pl.Hkv;
     b.G = pl.G;
     b.scale_log2 = pl.scale_log2;
     b.groups = pl.attend_groups;
-    b.rounds = pl.attend_rounds;
     b.sel = sel;
     b.cnt = cnt;
     b.max_sel = pl.max_sel;
     b.po = w.po;
     b.pml = w.pml;
-    b.nsplit = pl.attend_groups;
-    b.split0 = 0;
-    hipError_t e = launch_step2<false>(b, pl.B * pl.Hkv * pl.attend_groups, stream);
+    const dim3 grid(pl.B * pl.Hkv * pl.attend_groups), block(kStep2Waves * 64);
+    switch (pl.attend_rounds) {
+        case 1: hipLaunchKernelGGL(attend_kernel<1>, grid, block, 0, stream, b); break;
+        case 2: hipLaunchKernelGGL(attend_kernel<2>, grid, block, 0, stream, b); break;
+        case 3: hipLaunchKernelGGL(attend_kernel<3>, grid, block, 0, stream, b); break;
+        case 4: hipLaunchKernelGGL(attend_kernel<4>, grid, block, 0, stream, b); break;
+        case 6: hipLaunchKernelGGL(attend_kernel<6>, grid, block, 0, stream, b); break;
+        default: hipLaunchKernelGGL(attend_kernel<8>, grid, block, 0, stream, b); break;
+    }
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_merge(pl, w, pl.attend_groups, out, lse, stream);
 }

@@ -256,9 +256,38 @@ __device__ void attend_page_split4(const uint16_t* __restrict__ kb, const uint16
     }
 }
 
+// Window slot x of pair (s, g): block nb - wn + x, wn = min(nb, wblocks),
+// attended by the four waves together, its partial at slot split0 + x (an
+// empty partial past wn).  All 256 threads.
+__device__ void store_empty_partial(int G, size_t head_row0, int nsplit, int split,
+                                    float* __restrict__ po, float2* __restrict__ pml);
+__device__ void window_slot(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                            const int32_t* table, const int32_t* cu_k, int max_blocks, int Lmax,
+                            int Hq, int Hkv, int G, float scale_log2, int wblocks, int s, int g,
+                            int x, int nsplit, int split0, float* po, float2* pml,
+                            SplitPageLds& sh)
+{
+    const int lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
+    const int L = seq_len(cu_k, s, Lmax);
+    const int nb = (L + BS - 1) / BS;
+    const int wn = nb < wblocks ? nb : wblocks;
+    const size_t head_row0 = (size_t)s * Hq + g * G;
+    if (x < wn) {
+        bf16x8 qb[4];
+        load_q(q, Hq, s, g * G, G, r, kq, qb);
+        const int b = nb - wn + x;
+        const int page = table[(size_t)s * max_blocks + b];
+        attend_page_split4(k_pool + ((size_t)page * Hkv + g) * BS * D,
+                           v_pool + ((size_t)page * Hkv + g) * D * BS, L - b * BS, qb, scale_log2, G,
+                           head_row0, nsplit, split0 + x, po, pml, sh);
+    } else {
+        store_empty_partial(G, head_row0, nsplit, split0 + x, po, pml);
+    }
+}
+
 // An empty partial (m = -inf, l = 0, o = 0) at slot `split`; all 256 threads.
-__device__ __forceinline__ void store_empty_partial(int G, size_t head_row0, int nsplit, int split,
-                                                    float* __restrict__ po, float2* __restrict__ pml)
+__device__ void store_empty_partial(int G, size_t head_row0, int nsplit, int split,
+                                    float* __restrict__ po, float2* __restrict__ pml)
 {
     for (int x = threadIdx.x; x < G * (D / 4); x += 256) {
         const int h = x / (D / 4), c4 = x % (D / 4);
@@ -286,10 +315,18 @@ __device__ __forceinline__ void store_empty_partial(int G, size_t head_row0, int
 // The chunk holding the key completed by the current token (tokens L-32 ..
 // L-1) pools it from K first (fp64 sum, one bf16 rounding), stores it to the
 // pooled-key page and substitutes it into its MFMA operand in registers.
+//
+// The local window needs no selection, so its pages (one four-wave
+// workgroup each, window_slot) ride in whichever launch has room: here,
+// after the npairs * nchunks scoring workgroups, when the attention launch
+// would need more than two workgroups per CU (the scoring reads little from
+// HBM, so the window streams alongside it); otherwise in the attention
+// launch, beside the selection, which reads nothing from HBM either.
 
 struct ScoreArgs {
     const uint16_t* q;
     const uint16_t* k_pool;
+    const uint16_t* v_pool;
     uint16_t* kc_pool;
     const int32_t* table;
     const int32_t* cu_k;
@@ -300,10 +337,20 @@ struct ScoreArgs {
     float2* cml;
     float* spill;
     float* bpart;
+    int nscore;                   // scoring workgroups = pairs * nchunks
+    int wslots, wblocks, split0;  // window workgroups per pair (0: none); partial slot of slot 0
+    int nsplit;
+    float* po;
+    float2* pml;
 };
 
-// LDS of a scoring workgroup: the chunk's logits, [G][CK + 4] floats.
-inline size_t score_lds_bytes(int T, int G) { return (size_t)G * (64 * T + 4) * sizeof(float); }
+// Dynamic LDS of the scoring launch: a chunk's logits, [G][CK + 4] floats,
+// or a window page's exchange.
+inline size_t score_lds_bytes(int T, int G)
+{
+    const size_t z = (size_t)G * (64 * T + 4) * sizeof(float);
+    return z > sizeof(SplitPageLds) ? z : sizeof(SplitPageLds);
+}
 
 template <int T>
 __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
@@ -317,6 +364,14 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
     __shared__ float wm[kScoreWaves][kMaxGroup], wsum[kScoreWaves][kMaxGroup];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
+    if ((int)blockIdx.x >= a.nscore) {  // window slot
+        const int w = (int)blockIdx.x - a.nscore;
+        const int pair = w / a.wslots;
+        window_slot(a.q, a.k_pool, a.v_pool, a.table, a.cu_k, a.max_blocks, a.Lmax, a.Hq, a.Hkv,
+                    a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv, w % a.wslots, a.nsplit,
+                    a.split0, a.po, a.pml, *reinterpret_cast<SplitPageLds*>(smem));
+        return;
+    }
     const int pair = blockIdx.x / a.nchunks, c = blockIdx.x % a.nchunks;
     const int s = pair / a.Hkv, g = pair % a.Hkv;
     const int k0 = c * CK;
@@ -456,18 +511,16 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
 
 // ----------------------------------------------- selection + attention ---
 //
-// Launch 2 of a decode step, two kinds of four-wave workgroups per pair:
-//  - `wslots` window workgroups, one page of the local window each (slot x =
-//    block nb - wn + x, wn = min(nb, window blocks)), attended by the four
-//    waves together: the window needs no selection, so these stream from
-//    HBM on every CU while the top workgroups select; partial slot
-//    groups + x (an empty partial past wn);
-//  - `groups` top workgroups.  Every one recomputes the pair's selection
-//    from the scoring partials -- per-head log-sum-exp over the chunks,
-//    block importance, top-k -- a few microseconds of LDS work (latency,
-//    not bandwidth) that replaces a hand-off between workgroups; it then
-//    attends its slice of the picks, one page per wave (picks
-//    4 R k .. 4 R (k+1) - 1), and stores one partial at slot k.
+// Launch 2 of a decode step: `groups` four-wave top workgroups per pair.
+// Every one recomputes the pair's selection from the scoring partials --
+// per-head log-sum-exp over the chunks, block importance, top-k -- a few
+// microseconds of LDS work (latency, not bandwidth) that replaces a hand-off
+// between workgroups (a kernel boundary is cheaper on this chip than any
+// in-launch hand-off with counters); it then attends its slice of the picks,
+// one page per wave (picks 4 R k .. 4 R (k+1) - 1), and stores one partial
+// at slot k.  Slots groups .. nsplit - 1 hold the window pages' partials,
+// from `wslots` window workgroups per pair in this launch or the scoring
+// launch (window_slot).
 //
 // Block importance: I[b] = mean over keys j of 4b-1 .. 4b+3 below n_c of
 // sum_h 2^(z_h[j] - lse_h) -- the softmax over the pooled keys per query
@@ -491,7 +544,8 @@ struct TopArgs {
     const float* bpart;
     int topk, wblocks, max_nb, max_sel;
     int groups, rounds;  // top workgroups per pair; top-k blocks per wave
-    int wslots;          // window workgroups per pair (0 in importance-only mode)
+    int wslots;          // window workgroups per pair in this launch (0: none)
+    int nsplit;          // partial slots per head
     int ntop, nwin;      // top / window workgroups of the launch
     int tpx, wpx;        // top / window workgroups per XCD
     int scores_only;     // importance only (no selection, no attention)
@@ -558,42 +612,31 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     static_assert(KRB <= kSelKeyRounds, "register rounds of the selector");
     extern __shared__ __align__(16) char smem[];
     __shared__ TopLds sh;
-    // XCD x (workgroups are dealt to XCDs round-robin by index) runs top
+    // Workgroups are dealt to the XCDs round-robin by index.  XCD x runs top
     // workgroups x * tpx .. x * tpx + tpx - 1 first, then window workgroups
-    // x * wpx .. x * wpx + wpx - 1: the same pairs, so they share an L2, and
-    // the CUs each get one top workgroup before any gets a second.
+    // x * wpx .. x * wpx + wpx - 1: the same pairs, so the top workgroups of
+    // a pair (which read the same partials) share an L2, and the CUs each
+    // get one top workgroup before any gets a second.
     const int xcd = (int)(blockIdx.x % 8), pos = (int)(blockIdx.x / 8);
     const bool window = pos >= a.tpx;
     const int lid = window ? xcd * a.wpx + (pos - a.tpx) : xcd * a.tpx + pos;
     if (lid >= (window ? a.nwin : a.ntop)) return;  // whole workgroup
+    if (window) {
+        const int pair = lid / a.wslots;
+        window_slot(a.q, a.k_pool, a.v_pool, a.table, a.cu_k, a.max_blocks, a.Lmax, a.Hq, a.Hkv,
+                    a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv, lid % a.wslots,
+                    a.nsplit, a.groups, a.po, a.pml, sh.page);
+        return;
+    }
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
-    const int pair = window ? lid / a.wslots : lid / a.groups;
-    const int k = window ? lid % a.wslots : lid % a.groups;
+    const int pair = lid / a.groups, k = lid % a.groups;
     const int s = pair / a.Hkv, g = pair % a.Hkv;
     const int L = seq_len(a.cu_k, s, a.Lmax);
     const int nb = (L + BS - 1) / BS;
     const int nc = dev_num_keys(L);
     const int32_t* trow = a.table + (size_t)s * a.max_blocks;
     const size_t head_row0 = (size_t)s * a.Hq + g * a.G;
-    const int nsplit = a.groups + a.wslots;
-
-    if (window) {  // window slot k
-        const int wn = nb < a.wblocks ? nb : a.wblocks;
-        if (k < wn) {
-            bf16x8 qb[4];
-            load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
-            const int b = nb - wn + k;
-            const int page = trow[b];
-            attend_page_split4(a.k_pool + ((size_t)page * a.Hkv + g) * BS * D,
-                               a.v_pool + ((size_t)page * a.Hkv + g) * D * BS, L - b * BS, qb,
-                               a.scale_log2, a.G, head_row0, nsplit, a.groups + k, a.po, a.pml,
-                               sh.page);
-        } else {
-            store_empty_partial(a.G, head_row0, nsplit, a.groups + k, a.po, a.pml);
-        }
-        return;
-    }
 
     // ---- top workgroup k: the pair's selection, then picks 4 R k .. 4 R (k+1) - 1
     int32_t* spg = reinterpret_cast<int32_t*>(smem);  // block-table row
@@ -698,7 +741,7 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
                     a.v_pool + ((size_t)e.y * a.Hkv + g) * D * BS, L - e.x * BS, qb, a.scale_log2,
                     r, kq, A);
     }
-    store_wg_partial(sh.comb, A, a.G, head_row0, nsplit, k, a.po, a.pml);
+    store_wg_partial(sh.comb, A, a.G, head_row0, a.nsplit, k, a.po, a.pml);
 }
 
 // ------------------------------------------------ attention (alone) ---
@@ -869,13 +912,31 @@ static size_t device_lds_limit()
     return cached[dev];
 }
 
+// with_window: also the window workgroups (partials at slots top_groups ..).
+// Compute units of the current device (queried once per device).
+static int device_cus()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        cached[dev] = v;
+    }
+    return cached[dev];
+}
+
 static hipError_t launch_score(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
                                const int32_t* cu_k, const Workspace& w, int append,
-                               hipStream_t stream)
+                               bool with_window, hipStream_t stream)
 {
     ScoreArgs a{};
     a.q = q;
     a.k_pool = kv.k_pool;
+    a.v_pool = kv.v_pool;
     a.kc_pool = kv.kc_pool;
     a.table = kv.block_table;
     a.cu_k = cu_k;
@@ -893,7 +954,14 @@ static hipError_t launch_score(const Plan& pl, const nosa_paged_kv& kv, const no
     a.cml = w.cml;
     a.spill = w.spill;
     a.bpart = w.bpart;
-    const dim3 grid(pl.B * pl.Hkv * pl.nchunks), block(kScoreWaves * 64);
+    a.nscore = pl.B * pl.Hkv * pl.nchunks;
+    a.wslots = with_window ? pl.wslots : 0;
+    a.wblocks = pl.wblocks;
+    a.split0 = pl.top_groups;
+    a.nsplit = pl.nsplit;
+    a.po = w.po;
+    a.pml = w.pml;
+    const dim3 grid(a.nscore + pl.B * pl.Hkv * a.wslots), block(kScoreWaves * 64);
     const size_t lds = score_lds_bytes(pl.score_tiles, pl.G);  // <= 16 x 516 floats
     switch (pl.score_tiles) {
         case 1: hipLaunchKernelGGL(score_kernel<1>, grid, block, lds, stream, a); break;
@@ -981,12 +1049,11 @@ hipError_t launch_scores_only(const Plan& pl, const nosa_paged_kv& kv, const nos
                               const int32_t* cu_k, const Workspace& w, float* scores_out,
                               hipStream_t stream)
 {
-    hipError_t e = launch_score(pl, kv, q, cu_k, w, 0, stream);
+    hipError_t e = launch_score(pl, kv, q, cu_k, w, 0, false, stream);
     if (e != hipSuccess) return e;
     TopArgs a = top_args(pl, kv, q, cu_k, w);
     a.groups = 1;
     a.rounds = 1;
-    a.wslots = 0;
     a.scores_only = 1;
     a.scores_out = scores_out;
     return launch_top(pl, a, stream);
@@ -997,12 +1064,17 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
                          int32_t* sel_out, int32_t* cnt_out, float* scores_out,
                          hipStream_t stream)
 {
-    hipError_t e = launch_score(pl, kv, q, cu_k, w, 1, stream);
+    // the window pages go beside the selection when both kinds of attention
+    // workgroups fit on the chip at once (two per CU), else beside the scoring
+    const long long pairs = (long long)pl.B * pl.Hkv;
+    const bool win_top = pairs * (pl.top_groups + pl.wslots) <= 2LL * device_cus();
+    hipError_t e = launch_score(pl, kv, q, cu_k, w, 1, !win_top, stream);
     if (e != hipSuccess) return e;
     TopArgs a = top_args(pl, kv, q, cu_k, w);
     a.groups = pl.top_groups;
     a.rounds = pl.top_rounds;
-    a.wslots = pl.wslots;
+    a.wslots = win_top ? pl.wslots : 0;
+    a.nsplit = pl.nsplit;
     a.scores_out = scores_out;
     a.sel_out = sel_out;
     a.cnt_out = cnt_out;

@@ -272,7 +272,7 @@ def main():
         "step_hbm": {"algorithmic_bytes": int(step_bytes),
                      "achieved_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "roofline": {"kernel": "step2_kernel (nosa_sparse_attend: attention over the kept pages + merge)", "bound": "hbm",
+        "roofline": {"kernel": "attend_kernel (nosa_sparse_attend: attention over the kept pages + merge)", "bound": "hbm",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(w.name),
                      "us_per_launch": round(us_attn, 3),
@@ -449,7 +449,7 @@ def pmc_summary(fetch_dir, write_dir):
         traffic[name] = fb + wb
         lines.append(f"| `{name[:90]}` | {len(v['FETCH_SIZE'])} | {fk:.0f} | {wk:.0f} | "
                      f"{fb / 1e6:.2f} | {wb / 1e6:.2f} |")
-    attn_k = [n for n in traffic if "step2_kernel<false" in n]
+    attn_k = [n for n in traffic if "attend_kernel<" in n]
     merge_k = [n for n in traffic if "merge_kernel" in n]
     if not attn_k or not merge_k:
         raise SystemExit("attention kernels not found")

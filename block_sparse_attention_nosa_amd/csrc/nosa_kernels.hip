@@ -578,25 +578,34 @@ inline size_t top_lds_bytes(int max_nb, int krb)
 }
 
 // Importance of block b from its partial row (heads 4u .. 4u+3 in bv[u]).
+// Straight-line: both LDS rows are read whatever b is (indexes clamped into
+// the 64 rows) and the terms that do not apply are dropped afterwards, so
+// the reads of several blocks can be in flight together.
 template <int GP4>
 __device__ __forceinline__ float block_importance(int b, int nc, int cb_shift, int nvalid, int G,
                                                   const float4 (&bv)[GP4], const TopLds& sh)
 {
     const int c = b >> cb_shift;
-    float sum = 0.f;
-    if (c < nvalid) {
+    const int cr = c < kMaxChunks ? c : kMaxChunks - 1;
+    const int cp = c > 0 ? (c <= kMaxChunks ? c - 1 : kMaxChunks - 1) : 0;
+    float own = 0.f, spill = 0.f;
 #pragma unroll
-        for (int u = 0; u < GP4; ++u) {
-            const float4 f4 = *reinterpret_cast<const float4*>(&sh.f[c][4 * u]);
-            const float v[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
-            const float f[4] = {f4.x, f4.y, f4.z, f4.w};
+    for (int u = 0; u < GP4; ++u) {
+        const float4 f4 = *reinterpret_cast<const float4*>(&sh.f[cr][4 * u]);
+        const float4 s4 = *reinterpret_cast<const float4*>(&sh.fs[cp][4 * u]);
+        const float v[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
+        const float f[4] = {f4.x, f4.y, f4.z, f4.w};
+        const float q[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (4 * u + e < G) sum += f[e] * v[e];
-        }
+        for (int e = 0; e < 4; ++e)
+            if (4 * u + e < G) {
+                own += f[e] * v[e];
+                spill += q[e];
+            }
     }
-    if (b > 0 && (b & ((1 << cb_shift) - 1)) == 0 && 4 * b - 1 < nc)
-        for (int h = 0; h < G; ++h) sum += sh.fs[c - 1][h];
+    // key 4b-1 lies in the previous chunk when b starts a chunk
+    const bool first = b > 0 && (b & ((1 << cb_shift) - 1)) == 0 && 4 * b - 1 < nc;
+    const float sum = (c < nvalid ? own : 0.f) + (first ? spill : 0.f);
     const int jlo = 4 * b - 1 > 0 ? 4 * b - 1 : 0;
     const int jhi = 4 * b + 3 < nc - 1 ? 4 * b + 3 : nc - 1;
     return jlo <= jhi ? sum / (float)(jhi - jlo + 1) : -INFINITY;
@@ -697,12 +706,11 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     float* so = a.scores_out && k == 0 ? a.scores_out + (size_t)pair * a.max_nb : nullptr;
 #pragma unroll
     for (int i = 0; i < KRB; ++i) {
+        if (i * NT >= nb) break;  // rounds wholly past the sequence
         const int b = i * NT + tid;
-        if (b < nb) {
-            const float I = block_importance<GP4>(b, nc, a.cb_shift, nvalid, a.G, bv[i], sh);
-            keys[i] = order_key(I);
-            if (so) so[b] = I;
-        }
+        const float I = block_importance<GP4>(b, nc, a.cb_shift, nvalid, a.G, bv[i], sh);
+        keys[i] = b < nb ? order_key(I) : 0u;
+        if (so && b < nb) so[b] = I;
     }
     // contexts past KRB * 256 blocks: the rest of the row and of the
     // importance through LDS

@@ -25,7 +25,10 @@
  *   - `max_seqlen_*` are host-side upper bounds of the device lengths, used to
  *     size grids without a device-to-host copy.  A device length above its
  *     bound, a non-monotone cu_seqlens or a block_table entry outside
- *     [0, num_pages) is a contract violation that the library does not detect.
+ *     [0, num_pages) for a block the sequence holds is a contract violation
+ *     that the library does not detect.  Entries past a sequence's last
+ *     block may hold anything (the row is read ahead of the length, and such
+ *     entries are clamped into the pool and never used).
  *   - Host-checkable arguments are validated before anything is enqueued: a
  *     NULL required pointer gives NOSA_ERR_NULL, inconsistent sizes
  *     NOSA_ERR_INVALID, a shape this build has no kernel for

@@ -393,16 +393,18 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
             keys[i] = order_key(sI[b < ncand ? b : (ncand > 0 ? ncand - 1 : 0)]);
         }
     }
-    auto key_at = [&](int i) -> uint32_t {
-        if (i < KR) {
-            uint32_t k = 0;
+    // f(i, key) for every candidate round i < rounds: the register rounds
+    // unrolled (constant indexes into keys[]), later ones read from sI
+    auto for_rounds = [&](auto&& f) {
 #pragma unroll
-            for (int j = 0; j < KR; ++j)
-                if (j == i) k = keys[j];
-            return k;
+        for (int i = 0; i < KR; ++i) {
+            if (i >= rounds) return;
+            f(i, keys[i]);
         }
-        const int b = i * NT + tid;
-        return b < ncand ? order_key(sI[b]) : 0u;
+        for (int i = KR; i < rounds; ++i) {
+            const int b = i * NT + tid;
+            f(i, b < ncand ? order_key(sI[b]) : 0u);
+        }
     };
     // Candidates whose u >> shift is above P are taken; of those equal to P,
     // the `need` lowest blocks; there are n_eq of them.  shift = 32: every
@@ -413,13 +415,12 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
         // range of the candidate keys
         if (!range_known) {
             uint32_t lo = 0xffffffffu, hi = 0u;
-            for (int i = 0; i < rounds; ++i) {
-                const uint32_t key = key_at(i);
+            for_rounds([&](int i, uint32_t key) {
                 if (i * NT + tid < ncand) {
                     lo = min(lo, key);
                     hi = max(hi, key);
                 }
-            }
+            });
             lo = ~wave_max_u32(~lo);
             hi = wave_max_u32(hi);
             if (lane == 0) {
@@ -450,12 +451,12 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
             auto level_pass = [&](int* hist, auto dpl_tag) -> bool {
                 constexpr int DPL = decltype(dpl_tag)::value;
                 constexpr int ND = 64 * DPL;
-                for (int i = 0; i < rounds; ++i) {
+                for_rounds([&](int i, uint32_t key) {
                     const int b = i * NT + tid;
-                    const uint32_t u = key_at(i) - kmin;
+                    const uint32_t u = key - kmin;
                     const bool match = b < ncand && (prev == 32 || (u >> prev) == P);
                     if (match) atomicAdd(&hist[(u >> sh_lo) & (ND - 1)], 1);
-                }
+                });
                 __syncthreads();
                 int v[DPL], loc = 0;
 #pragma unroll
@@ -512,25 +513,25 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
         return shift < 32 ? (key - kmin) >> shift : 0u;
     };
     if (ranked) {
-        for (int i = 0; i < rounds; ++i) {
+        for_rounds([&](int i, uint32_t key) {
             const int b = i * NT + tid;
-            const bool eq = b < ncand && prefix(key_at(i)) == P;
+            const bool eq = b < ncand && prefix(key) == P;
             const uint64_t m = __ballot(eq);
             if (lane == 0) sh.cnt[0][i][wave] = (int)__popcll(m);
-        }
+        });
         __syncthreads();
     }
     uint32_t takebits = 0;
     {
         int eq_base = 0;
-        for (int i = 0; i < rounds; ++i) {
+        for_rounds([&](int i, uint32_t key) {
             const int b = i * NT + tid;
             const bool valid = b < ncand;
             bool take;
             if (!partial) {
                 take = valid && kk > 0;
             } else {
-                const uint32_t kp = prefix(key_at(i));
+                const uint32_t kp = prefix(key);
                 const bool gt = kp > P, eq = kp == P;
                 if (ranked) {
                     const uint64_t m = __ballot(valid && eq);
@@ -549,11 +550,11 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
             const uint64_t mt = __ballot(take);
             if (lane == 0) sh.cnt[1][i][wave] = (int)__popcll(mt);
             if (take) takebits |= 1u << i;
-        }
+        });
     }
     __syncthreads();
     int sel_base = 0;
-    for (int i = 0; i < rounds; ++i) {
+    for_rounds([&](int i, uint32_t) {
         const bool take = (takebits >> i) & 1u;
         const uint64_t mt = __ballot(take);
         int pos = sel_base + lanes_below(mt);
@@ -569,7 +570,7 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
             if (list && pos >= list_lo && pos < list_lo + list_n)
                 list[pos - list_lo] = make_int2(b, pages[b]);
         }
-    }
+    });
     const int nsel = sel_base;
     const int total = nsel + (nb - ncand);
     if (sel_out) {

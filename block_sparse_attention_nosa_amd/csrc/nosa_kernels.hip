@@ -486,8 +486,12 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
     // chunk maximum (finite: key k0 exists for every head)
     const size_t prow = (size_t)pair * a.nbk + (size_t)c * CB;
     const size_t crow = (size_t)pair * a.G * a.nchunks + c;  // + h * nchunks
-    for (int idx = tid; idx < a.G * CB; idx += kScoreWaves * 64) {
-        const int h = idx % a.G, bb = idx / a.G;
+    for (int idx = tid; idx < a.gp * CB; idx += kScoreWaves * 64) {
+        const int h = idx % a.gp, bb = idx / a.gp;
+        if (h >= a.G) {  // padding of the row to gp heads: exact zeros
+            a.bpart[(prow + bb) * a.gp + h] = 0.f;
+            continue;
+        }
         float m = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kScoreWaves; ++w) m = fmaxf(m, wm[w][h]);
@@ -577,7 +581,8 @@ inline size_t top_lds_bytes(int max_nb, int krb)
     return row + (max_nb > krb * 256 ? (size_t)max_nb * sizeof(float) : 16);
 }
 
-// Importance of block b from its partial row (heads 4u .. 4u+3 in bv[u]).
+// Importance of block b from its partial row (heads 4u .. 4u+3 in bv[u];
+// the padding heads G .. 4 GP4 - 1 carry zero sums and zero weights).
 // Straight-line: both LDS rows are read whatever b is (indexes clamped into
 // the 64 rows) and the terms that do not apply are dropped afterwards, so
 // the reads of several blocks can be in flight together.
@@ -597,11 +602,10 @@ __device__ __forceinline__ float block_importance(int b, int nc, int cb_shift, i
         const float f[4] = {f4.x, f4.y, f4.z, f4.w};
         const float q[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (4 * u + e < G) {
-                own += f[e] * v[e];
-                spill += q[e];
-            }
+        for (int e = 0; e < 4; ++e) {  // heads past G: zero weights and zero sums
+            own += f[e] * v[e];
+            spill += q[e];
+        }
     }
     // key 4b-1 lies in the previous chunk when b starts a chunk
     const bool first = b > 0 && (b & ((1 << cb_shift) - 1)) == 0 && 4 * b - 1 < nc;
@@ -686,7 +690,13 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int h = wave + 4 * u;
-        if (h >= a.G) break;
+        if (h >= a.G) {  // heads G .. 4 GP4 - 1 read by block_importance: zero weights
+            if (h < 4 * GP4) {
+                sh.f[lane][h] = 0.f;
+                sh.fs[lane][h] = 0.f;
+            }
+            continue;
+        }
         const bool ok = lane < nvalid;
         const float m = ok ? cv[u].x : -INFINITY;
         const float M = wave_max_f(m);

@@ -111,7 +111,7 @@ def build_layers(w, nsteps, device="cuda"):
         pg = synth.to_paged(inp, wl, device=device)
         kv = nosa.paged_kv(pg["k_pool"], pg["v_pool"], pg["kc_pool"], pg["block_table"])
         p = nosa.params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.kernel,
-                        w.stride, w.topk, w.window)
+                        w.stride, w.topk, w.window, locality=w.locality)
         lens0 = [L - 1 for L in w.lens]
         nosa.nosa_compress_keys(p, kv, synth.cu_from_lens(lens0, device), None, w.batch,
                                 max(lens0))
@@ -128,6 +128,8 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--locality", type=float, default=0.0,
+                    help="share of the top-k budget forced to the blocks before the window")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run the calibration copy and the kernels once each for counters")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -149,6 +151,9 @@ def main():
     from block_sparse_attention_nosa_amd import nosa, synth
 
     w = synth.config(args.config)
+    if args.locality:
+        w = synth.Workload(**{**w.__dict__, "locality": args.locality,
+                              "name": f"{w.name}-locality{args.locality:g}"})
     if w.q_lens is not None:
         return prefill_main(w, args)
     nsteps = w.extra_tokens + 1
@@ -268,7 +273,8 @@ def main():
         "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": d, "context": w.lens[0] - 1, "decode_steps": nsteps,
                    "topk_blocks": w.topk, "window_tokens": w.window, "block": w.block_size,
-                   "pool_kernel": w.kernel, "pool_stride": w.stride, "layer_caches": LAYERS},
+                   "pool_kernel": w.kernel, "pool_stride": w.stride, "layer_caches": LAYERS,
+                   "locality": w.locality},
         "step_hbm": {"algorithmic_bytes": int(step_bytes),
                      "achieved_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
@@ -321,7 +327,7 @@ def prefill_main(w, args):
     pg = synth.to_paged(inp, w, device="cuda")
     kv = nosa.paged_kv(pg["k_pool"], pg["v_pool"], pg["kc_pool"], pg["block_table"])
     p = nosa.params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.kernel, w.stride,
-                    w.topk, w.window)
+                    w.topk, w.window, locality=w.locality)
     B, maxL, maxLq = w.batch, max(w.lens), max(w.q_lens)
     cu_k = synth.cu_from_lens(w.lens, "cuda")
     cu_q = inp["cu_q"].cuda().to(torch.int32)
@@ -495,7 +501,7 @@ def cpu_baseline(w, layer, lens_at, budget_s):
     host = dict(k=inp["k"].cpu(), v=inp["v"].cpu(), cu_k_store=inp["cu_k_store"].cpu())
     q = synth.bits(inp["q"])
     op = ora.Params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.kernel, w.stride,
-                    w.topk, w.window)
+                    w.topk, w.window, locality=w.locality)
     n, t0 = 0, time.time()
     while True:
         k, v, cu = synth.packed_live(host, w, n % len(lens_at))

@@ -12,6 +12,12 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Blocks of the topk budget given to the candidates nearest the window.
+int local_blocks(const nosa_params* p)
+{
+    return (int)floor((double)p->locality * p->topk + 0.5);
+}
+
 // Parameter checks shared by every entry point.
 nosa_status check_params(const nosa_params* p)
 {
@@ -23,12 +29,13 @@ nosa_status check_params(const nosa_params* p)
     if (p->window % p->block_size != 0) return NOSA_ERR_INVALID;
     if (p->block_size % p->stride != 0) return NOSA_ERR_INVALID;
     if (!(p->scale == p->scale)) return NOSA_ERR_INVALID;  // NaN
+    if (!(p->locality >= 0.f && p->locality <= 1.f)) return NOSA_ERR_INVALID;  // incl. NaN
     if (p->topk > (1 << 24) || p->window / p->block_size > (1 << 20)) return NOSA_ERR_INVALID;
     if (p->head_dim != kHeadDim || p->block_size != kBlock || p->kernel != kPoolK ||
         p->stride != kPoolS)
         return NOSA_ERR_UNSUPPORTED;
     if (p->num_q_heads / p->num_kv_heads > kMaxGroup) return NOSA_ERR_UNSUPPORTED;
-    if (p->window / p->block_size > kMaxWindowBlocks) return NOSA_ERR_UNSUPPORTED;
+    if (p->window / p->block_size + local_blocks(p) > kMaxWindowBlocks) return NOSA_ERR_UNSUPPORTED;
     return NOSA_OK;
 }
 
@@ -105,8 +112,10 @@ nosa_status make_plan(const nosa_params* p, int batch, int max_seqlen_k, Plan* p
     P.Hq = p->num_q_heads;
     P.Hkv = p->num_kv_heads;
     P.G = P.Hq / P.Hkv;
-    P.topk = p->topk;
-    P.wblocks = p->window / p->block_size;
+    // the locality share is exactly a longer forced window and a smaller top-k
+    const int k_loc = local_blocks(p);
+    P.topk = p->topk - k_loc;
+    P.wblocks = p->window / p->block_size + k_loc;
     P.max_sel = P.topk + P.wblocks;
     P.max_seqlen_k = max_seqlen_k;
     P.Lmax = max_seqlen_k;

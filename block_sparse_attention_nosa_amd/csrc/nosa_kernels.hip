@@ -338,7 +338,8 @@ struct ScoreArgs {
     float* spill;
     float* bpart;
     int nscore;                   // scoring workgroups = pairs * nchunks
-    int wslots, wblocks, split0;  // window workgroups per pair (0: none); partial slot of slot 0
+    int wslots, wblocks, split0;  // window pages per pair, a workgroup each (0: none);
+                                  // partial slot of slot 0
     int nsplit;
     float* po;
     float2* pml;
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
     __shared__ float wm[kScoreWaves][kMaxGroup], wsum[kScoreWaves][kMaxGroup];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
-    if ((int)blockIdx.x >= a.nscore) {  // window slot
+    if ((int)blockIdx.x >= a.nscore) {  // window workgroup: one page
         const int w = (int)blockIdx.x - a.nscore;
         const int pair = w / a.wslots;
         window_slot(a.q, a.k_pool, a.v_pool, a.table, a.cu_k, a.max_blocks, a.Lmax, a.Hq, a.Hkv,
@@ -548,7 +549,8 @@ struct TopArgs {
     const float* bpart;
     int topk, wblocks, max_nb, max_sel;
     int groups, rounds;  // top workgroups per pair; top-k blocks per wave
-    int wslots;          // window workgroups per pair in this launch (0: none)
+    int wslots;          // window slots (pages) per pair in this launch (0: none)
+    int wgroups;         // window workgroups per pair: wslots or ceil(wslots / 4)
     int nsplit;          // partial slots per head
     int ntop, nwin;      // top / window workgroups of the launch
     int tpx, wpx;        // top / window workgroups per XCD
@@ -634,16 +636,18 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     const bool window = pos >= a.tpx;
     const int lid = window ? xcd * a.wpx + (pos - a.tpx) : xcd * a.tpx + pos;
     if (lid >= (window ? a.nwin : a.ntop)) return;  // whole workgroup
-    if (window) {
-        const int pair = lid / a.wslots;
+    if (window && a.wgroups == a.wslots) {  // one window page, the four waves together
+        const int pair = lid / a.wgroups;
         window_slot(a.q, a.k_pool, a.v_pool, a.table, a.cu_k, a.max_blocks, a.Lmax, a.Hq, a.Hkv,
-                    a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv, lid % a.wslots,
+                    a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv, lid % a.wgroups,
                     a.nsplit, a.groups, a.po, a.pml, sh.page);
         return;
     }
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
-    const int pair = lid / a.groups, k = lid % a.groups;
+    // window workgroup j (a page per wave: slots 4 j + wave) or top workgroup k
+    const int pair = window ? lid / a.wgroups : lid / a.groups;
+    const int k = window ? lid % a.wgroups : lid % a.groups;
     const int s = pair / a.Hkv, g = pair % a.Hkv;
     const int L = seq_len(a.cu_k, s, a.Lmax);
     const int nb = (L + BS - 1) / BS;
@@ -651,6 +655,19 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     const int32_t* trow = a.table + (size_t)s * a.max_blocks;
     const size_t head_row0 = (size_t)s * a.Hq + g * a.G;
 
+    bf16x8 qb[4];
+    int rounds = 1;
+    if (window) {
+        // this wave's window page as a one-entry list; the attention below
+        // is the top workgroups' own
+        const int wn = nb < a.wblocks ? nb : a.wblocks;
+        const int x = 4 * k + wave;
+        int2 e = make_int2(-1, -1);
+        if (x < wn) e = make_int2(nb - wn + x, trow[nb - wn + x]);
+        if (lane == 0) sh.list[wave] = e;
+        load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
+        __syncthreads();
+    } else {
     // ---- top workgroup k: the pair's selection, then picks 4 R k .. 4 R (k+1) - 1
     int32_t* spg = reinterpret_cast<int32_t*>(smem);  // block-table row
     float* sI = reinterpret_cast<float*>(smem + ((size_t)a.max_nb * sizeof(int32_t) + 15) / 16 * 16);
@@ -683,7 +700,6 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     int tv[KRB];
 #pragma unroll
     for (int i = 0; i < KRB; ++i) tv[i] = trow[i * NT + tid < a.max_nb ? i * NT + tid : a.max_nb - 1];
-    bf16x8 qb[4];
     load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
     select_lds_clear<NT>(sh.sel);
     // per-head log2-sum-exp2 over the chunks, then each chunk's weight
@@ -749,17 +765,19 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
                                         a.cnt_out && k == 0 ? a.cnt_out + pair : nullptr, a.max_sel,
                                         sh.list, lo, a.rounds * kStep2Waves, spg, in_regs);
     __syncthreads();  // the list
+    rounds = a.rounds;
+    }
     AttnState A;
     attn_init(A);
 #pragma unroll 1
-    for (int rr = 0; rr < a.rounds; ++rr) {
+    for (int rr = 0; rr < rounds; ++rr) {
         const int2 e = sh.list[rr * kStep2Waves + wave];
         if (e.x < 0) continue;
         attend_page(a.k_pool + ((size_t)e.y * a.Hkv + g) * BS * D,
                     a.v_pool + ((size_t)e.y * a.Hkv + g) * D * BS, L - e.x * BS, qb, a.scale_log2,
                     r, kq, A);
     }
-    store_wg_partial(sh.comb, A, a.G, head_row0, a.nsplit, k, a.po, a.pml);
+    store_wg_partial(sh.comb, A, a.G, head_row0, a.nsplit, window ? a.groups + k : k, a.po, a.pml);
 }
 
 // ------------------------------------------------ attention (alone) ---
@@ -930,7 +948,6 @@ static size_t device_lds_limit()
     return cached[dev];
 }
 
-// with_window: also the window workgroups (partials at slots top_groups ..).
 // Compute units of the current device (queried once per device).
 static int device_cus()
 {
@@ -947,6 +964,8 @@ static int device_cus()
     return cached[dev];
 }
 
+// with_window: also the window workgroups (a page each; partials at slots
+// top_groups ..).
 static hipError_t launch_score(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
                                const int32_t* cu_k, const Workspace& w, int append,
                                bool with_window, hipStream_t stream)
@@ -1049,7 +1068,7 @@ static hipError_t launch_top(const Plan& pl, TopArgs a, hipStream_t stream)
     const size_t lds = top_lds_bytes(pl.max_nb, krb);
     if (lds + sizeof(TopLds) > device_lds_limit()) return hipErrorInvalidValue;
     a.ntop = pl.B * pl.Hkv * a.groups;
-    a.nwin = pl.B * pl.Hkv * a.wslots;
+    a.nwin = pl.B * pl.Hkv * a.wgroups;
     a.tpx = ceil_div(a.ntop, 8);
     a.wpx = ceil_div(a.nwin, 8);
     const dim3 grid(8 * (a.tpx + a.wpx));
@@ -1082,23 +1101,33 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
                          int32_t* sel_out, int32_t* cnt_out, float* scores_out,
                          hipStream_t stream)
 {
-    // the window pages go beside the selection when both kinds of attention
-    // workgroups fit on the chip at once (two per CU), else beside the scoring
-    const long long pairs = (long long)pl.B * pl.Hkv;
-    const bool win_top = pairs * (pl.top_groups + pl.wslots) <= 2LL * device_cus();
-    hipError_t e = launch_score(pl, kv, q, cu_k, w, 1, !win_top, stream);
+    // The window pages (known before any selection) go beside the selection
+    // when the attention launch then fits on the chip at once (two
+    // workgroups per CU): a page per workgroup if that fits, else a page per
+    // wave; otherwise beside the scoring, a page per workgroup.
+    const long long pairs = (long long)pl.B * pl.Hkv, room = 2LL * device_cus();
+    const int per_wave = ceil_div(pl.wslots, 4);
+    int wg_top = 0;
+    if (pairs * (pl.top_groups + pl.wslots) <= room)
+        wg_top = pl.wslots;
+    else if (pairs * (pl.top_groups + per_wave) <= room)
+        wg_top = per_wave;
+    // partials per head: the top workgroups', then one per window workgroup
+    const int nsplit = pl.top_groups + (wg_top > 0 ? wg_top : pl.wslots);
+    hipError_t e = launch_score(pl, kv, q, cu_k, w, 1, wg_top == 0, stream);
     if (e != hipSuccess) return e;
     TopArgs a = top_args(pl, kv, q, cu_k, w);
     a.groups = pl.top_groups;
     a.rounds = pl.top_rounds;
-    a.wslots = win_top ? pl.wslots : 0;
-    a.nsplit = pl.nsplit;
+    a.wslots = wg_top > 0 ? pl.wslots : 0;
+    a.wgroups = wg_top;
+    a.nsplit = nsplit;
     a.scores_out = scores_out;
     a.sel_out = sel_out;
     a.cnt_out = cnt_out;
     e = launch_top(pl, a, stream);
     if (e != hipSuccess) return e;
-    return launch_merge(pl, w, pl.nsplit, out, lse, stream);
+    return launch_merge(pl, w, nsplit, out, lse, stream);
 }
 
 hipError_t launch_attend(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,

@@ -33,7 +33,8 @@ class nosa_params(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("kernel", ctypes.c_int32), ("stride", ctypes.c_int32),
-                ("topk", ctypes.c_int32), ("window", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("topk", ctypes.c_int32), ("window", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("locality", ctypes.c_float)]
 
 
 class nosa_paged_kv(ctypes.Structure):
@@ -104,9 +105,9 @@ def _check(fn: str, status: int):
 
 
 def params(num_q_heads=16, num_kv_heads=2, head_dim=128, block_size=64, kernel=32, stride=16,
-           topk=64, window=1024, scale=0.0) -> nosa_params:
+           topk=64, window=1024, scale=0.0, locality=0.0) -> nosa_params:
     return nosa_params(num_q_heads, num_kv_heads, head_dim, block_size, kernel, stride, topk,
-                       window, scale)
+                       window, scale, locality)
 
 
 def paged_kv(k_pool, v_pool, kc_pool, block_table, max_blocks_per_seq=None,

@@ -48,6 +48,7 @@ class Workload:
     stride: int = 16
     topk: int = 64
     window: int = 1024
+    locality: float = 0.0            # share of topk given to the blocks nearest the window
     planted: int = 0                 # planted blocks per (sequence, KV head)
     q_lens: Optional[List[int]] = None  # queries per sequence (None: one, decode)
     seed: int = 0

@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define NOSA_ABI_VERSION 1
+#define NOSA_ABI_VERSION 2
 
 typedef uint16_t nosa_bf16; /* bf16 bit pattern */
 
@@ -98,7 +98,18 @@ typedef struct nosa_params {
     int32_t topk;         /* blocks chosen besides the window, >= 0               */
     int32_t window;       /* local window in tokens, a multiple of block_size     */
     float scale;          /* logit scale; <= 0 selects 1/sqrt(head_dim)          */
+    float locality;       /* gamma_0 in [0, 1]; 0 = plain top-k (see below)      */
 } nosa_params;
+
+/* Locality constraint [page "NOSA技术架构解析", section 1.2: a minimum locality
+ * gamma_0, the share of local KV blocks that must be kept, and a query-aware
+ * share kq/k of the budget; every setting the page prints (sections 1.2 and
+ * 4.1) has kq/k = 1 - gamma_0].  Of the topk budget, k_loc =
+ * floor(locality * topk + 0.5) blocks are the candidates nearest the window
+ * (kept whatever the query), the other topk - k_loc the best of the earlier
+ * candidates by importance.  Equivalently: window + k_loc * block_size tokens
+ * are forced and topk - k_loc blocks are selected, so window / block_size +
+ * k_loc must stay within the supported window (128 blocks). */
 
 /* Paged KV cache [page "NOSA技术架构解析", section 2.1: a PagedAttention-style
  * memory pool].  One page holds one block of block_size tokens for every KV

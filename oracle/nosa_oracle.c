@@ -110,6 +110,7 @@ int nosa_ref_check_params(const nosa_ref_params* p)
     if (p->block_size <= 0 || p->kernel <= 0 || p->stride <= 0) return -4;
     if (p->topk < 0 || p->window < 0) return -5;
     if (p->window % p->block_size != 0) return -6;
+    if (!(p->locality >= 0.0 && p->locality <= 1.0)) return -7;
     return 0;
 }
 
@@ -255,7 +256,15 @@ static int cand_cmp(const void* a, const void* b)
  * the coarse scores; page "NOSA-1B 模型家族全景", core principle: explicit local
  * window of 1024 tokens).  Window = the last window/block_size blocks up to and
  * including the block of the query block's last query; the topk best of the
- * earlier blocks are added.  Output ascending, padded with -1. */
+ * earlier blocks are added.  Output ascending, padded with -1.
+ *
+ * Locality constraint (page "NOSA技术架构解析", section 1.2: a minimum
+ * locality gamma_0 -- the share of local blocks that must be kept -- and a
+ * query-aware share kq/k of the budget; in every setting the page prints,
+ * 1.2 and 4.1, the two add up to one): of the topk budget,
+ * k_loc = round(gamma_0 * topk) goes to the candidates nearest the window
+ * (kept whatever the query), the other topk - k_loc to the best of the
+ * remaining candidates by score. */
 int nosa_ref_select_blocks(const nosa_ref_params* p, const double* scores, const int32_t* cu_q,
                            const int32_t* cu_k, int B, int max_qblk, int max_nb, int max_sel,
                            int32_t* sel, int32_t* count)
@@ -284,15 +293,21 @@ int nosa_ref_select_blocks(const nosa_ref_params* p, const double* scores, const
                 const double* sc = scores + (((size_t)s * max_qblk + r) * Hkv + g) * max_nb;
                 char* keep = (char*)calloc(nb, 1);
                 for (int b = first_win; b < nb; ++b) keep[b] = 1;
-                const int ncand = first_win;
-                if (ncand > 0 && p->topk > 0) {
+                /* the local share: the k_loc candidates right before the window */
+                const int k_loc = (int)floor(p->locality * p->topk + 0.5);
+                const int n_loc = k_loc < first_win ? k_loc : first_win;
+                for (int b = first_win - n_loc; b < first_win; ++b) keep[b] = 1;
+                /* the query-aware share among the candidates before those */
+                const int ncand = first_win - n_loc;
+                const int k_q = p->topk - k_loc;
+                if (ncand > 0 && k_q > 0) {
                     cand_t* c = (cand_t*)malloc(sizeof(cand_t) * ncand);
                     for (int b = 0; b < ncand; ++b) {
                         c[b].score = sc[b];
                         c[b].block = b;
                     }
                     qsort(c, ncand, sizeof(cand_t), cand_cmp);
-                    const int take = p->topk < ncand ? p->topk : ncand;
+                    const int take = k_q < ncand ? k_q : ncand;
                     for (int i = 0; i < take; ++i) keep[c[i].block] = 1;
                     free(c);
                 }

@@ -23,6 +23,8 @@ typedef struct nosa_ref_params {
     int topk;          /* blocks chosen in addition to the local window   */
     int window;        /* local window, tokens, multiple of block_size    */
     double scale;      /* <= 0 selects 1/sqrt(head_dim)                   */
+    double locality;   /* gamma_0 in [0, 1]: share of topk kept for the   */
+                       /* candidate blocks nearest the window             */
 } nosa_ref_params;
 
 int nosa_ref_check_params(const nosa_ref_params* p);

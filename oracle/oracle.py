@@ -32,7 +32,8 @@ class _Params(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int), ("num_kv_heads", ctypes.c_int),
                 ("head_dim", ctypes.c_int), ("block_size", ctypes.c_int),
                 ("kernel", ctypes.c_int), ("stride", ctypes.c_int), ("topk", ctypes.c_int),
-                ("window", ctypes.c_int), ("scale", ctypes.c_double)]
+                ("window", ctypes.c_int), ("scale", ctypes.c_double),
+                ("locality", ctypes.c_double)]
 
 
 @dataclass(frozen=True)
@@ -46,10 +47,12 @@ class Params:
     topk: int = 64
     window: int = 1024
     scale: float = 0.0  # <= 0 means 1/sqrt(head_dim)
+    locality: float = 0.0  # gamma_0: share of topk given to the blocks nearest the window
 
     def c(self) -> _Params:
         return _Params(self.num_q_heads, self.num_kv_heads, self.head_dim, self.block_size,
-                       self.kernel, self.stride, self.topk, self.window, float(self.scale))
+                       self.kernel, self.stride, self.topk, self.window, float(self.scale),
+                       float(self.locality))
 
     @property
     def group(self) -> int:

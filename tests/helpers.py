@@ -14,6 +14,8 @@ from __future__ import annotations
 import sys
 from dataclasses import dataclass
 
+import math
+
 import numpy as np
 import torch
 
@@ -48,9 +50,9 @@ def make_case(w: synth.Workload, gen_device="cpu", permute=True) -> DecodeCase:
     inp = synth.make_inputs(w, device=gen_device)
     pg = synth.to_paged(inp, w, permute=permute, device="cuda")
     p = nosa.params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.kernel, w.stride,
-                    w.topk, w.window)
+                    w.topk, w.window, locality=w.locality)
     op = ora.Params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.kernel, w.stride,
-                    w.topk, w.window)
+                    w.topk, w.window, locality=w.locality)
     kv = nosa.paged_kv(pg["k_pool"], pg["v_pool"], pg["kc_pool"], pg["block_table"])
     return DecodeCase(w, inp, pg, p, op, kv)
 
@@ -145,10 +147,18 @@ def oracle_step(c: DecodeCase, step: int = 0, seqs=None):
     return ora.forward(c.op, synth.bits(q), None, synth.bits(k), synth.bits(v), cu.numpy())
 
 
+def local_blocks(w: synth.Workload) -> int:
+    """Blocks of the top-k budget forced before the window (locality share)."""
+    return math.floor(w.locality * w.topk + 0.5)
+
+
 def compare_selection(gsel, gcnt, osel, ocnt, oscores, lens, w: synth.Workload):
     """Returns the number of rows where the near-tie exemption was used; raises
     AssertionError on any other disagreement."""
-    wb = w.window // w.block_size
+    # the locality share is forced like the window: tie analysis over the
+    # earlier candidates and the query-aware part of the budget
+    k_loc = local_blocks(w)
+    wb = w.window // w.block_size + k_loc
     exempt = 0
     B, _, Hkv, _ = osel.shape
     for s in range(B):
@@ -163,7 +173,7 @@ def compare_selection(gsel, gcnt, osel, ocnt, oscores, lens, w: synth.Workload):
             assert a == sorted(a) and len(set(a)) == n, (s, g, a)
             if a == b:
                 continue
-            k = min(w.topk, ncand)
+            k = min(w.topk - k_loc, ncand)
             sc = oscores[s, 0, g, :ncand]
             order = sorted(range(ncand), key=lambda x: (-sc[x], x))
             kth = sc[order[k - 1]]

@@ -29,7 +29,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert nosa.abi_version() == 1
+    assert nosa.abi_version() == 2
     for s in range(6):
         assert nosa.status_string(s)
     assert nosa.status_string(0) == "ok"
@@ -64,13 +64,23 @@ def test_workspace_size_for_the_workloads(L):
 @pytest.mark.parametrize("field,value,status", [
     ("num_q_heads", 0, 2), ("num_kv_heads", 3, 2), ("window", 1000, 2),
     ("topk", -1, 2), ("head_dim", 64, 3), ("block_size", 32, 3), ("kernel", 16, 3),
-    ("stride", 8, 3), ("block_size", 48, 2)])
+    ("stride", 8, 3), ("block_size", 48, 2), ("locality", -0.1, 2), ("locality", 1.5, 2),
+    ("locality", float("nan"), 2)])
 def test_parameter_errors(L, field, value, status):
     p = nosa.params()
     setattr(p, field, value)
     with pytest.raises(nosa.NosaError) as e:
         nosa.nosa_workspace_size(p, 8, 1, 16384)
     assert e.value.status == status
+
+
+def test_locality_window_limit(L):
+    # window 8192 tokens (128 blocks) leaves no room for local blocks
+    p = nosa.params(window=8192, topk=64, locality=0.5)
+    with pytest.raises(nosa.NosaError) as e:
+        nosa.nosa_workspace_size(p, 1, 1, 16384)
+    assert e.value.status == 3
+    assert nosa.nosa_workspace_size(nosa.params(window=1024, topk=64, locality=0.75), 8, 1, 16640) > 0
 
 
 def test_group_too_large_is_unsupported(L):

@@ -15,9 +15,10 @@ from helpers import (DecodeCase, build_kc, compare_outputs, compare_scores, comp
 pytestmark = pytest.mark.gpu
 
 
-def _wl(lens, hq=16, hkv=2, topk=16, planted=2, seed=7, window=1024):
+def _wl(lens, hq=16, hkv=2, topk=16, planted=2, seed=7, window=1024, locality=0.0):
     return synth.Workload(lens=list(lens), num_q_heads=hq, num_kv_heads=hkv, topk=topk,
-                          planted=planted, seed=seed, window=window, name="t")
+                          planted=planted, seed=seed, window=window, name="t",
+                          locality=locality)
 
 
 def _full_check(c: DecodeCase, step=0, tag=""):
@@ -86,6 +87,16 @@ def test_decode_step_window(window):
     log(f"case: window {window}")
     c = make_case(_wl([3000, 700], topk=5, planted=0, seed=window + 3, window=window))
     _full_check(c, tag=f"win{window}")
+
+
+@pytest.mark.parametrize("locality,topk", [(0.75, 64), (0.5, 5), (1.0, 16), (0.25, 96)])
+def test_decode_step_locality(locality, topk):
+    """Locality constraint: round(locality * topk) forced blocks before the
+    window, the rest by importance (varlen batch, both window placements)."""
+    log(f"case: locality {locality} topk {topk}")
+    c = make_case(_wl([9000, 2500, 700], topk=topk, planted=2, seed=int(locality * 40) + topk,
+                      locality=locality))
+    _full_check(c, tag=f"loc{locality}/{topk}")
 
 
 def test_planted_blocks_found_on_gpu():

@@ -12,14 +12,14 @@ import torch
 from block_sparse_attention_nosa_amd import nosa, synth
 from oracle import oracle as ora
 
-from helpers import OUT_MAX_ABS, OUT_MEAN_ABS, TIE_BAND, build_kc, log, make_case
+from helpers import OUT_MAX_ABS, OUT_MEAN_ABS, TIE_BAND, build_kc, local_blocks, log, make_case
 
 pytestmark = pytest.mark.gpu
 
 
-def _wl(lens, q_lens, hq=16, hkv=2, topk=8, window=1024, seed=3):
+def _wl(lens, q_lens, hq=16, hkv=2, topk=8, window=1024, seed=3, locality=0.0):
     return synth.Workload(lens=list(lens), q_lens=list(q_lens), num_q_heads=hq, num_kv_heads=hkv,
-                          topk=topk, window=window, seed=seed, name="pf")
+                          topk=topk, window=window, seed=seed, name="pf", locality=locality)
 
 
 def gpu_prefill(c):
@@ -68,7 +68,8 @@ def qblock_nb(L, Lq, r):
 
 def check_rows(g, o, rows, w, tag):
     """rows: list of (s, r, s_o, r_o): GPU row (s, r) against reference row (s_o, r_o)."""
-    wb = w.window // 64
+    k_loc = local_blocks(w)  # forced like the window
+    wb = w.window // 64 + k_loc
     exempt = 0
     for (s, r, so, ro) in rows:
         L, Lq = w.lens[s], w.q_lens[s]
@@ -89,7 +90,7 @@ def check_rows(g, o, rows, w, tag):
             if a != b:
                 ncand = max(nb - wb, 0)
                 sc = os_[:ncand]
-                k = min(w.topk, ncand)
+                k = min(w.topk - k_loc, ncand)
                 order = sorted(range(ncand), key=lambda x: (-sc[x], x))
                 kth = sc[order[k - 1]]
                 nxt = sc[order[k]] if k < ncand else -np.inf
@@ -146,6 +147,13 @@ def test_prefill_topk(topk):
     log(f"case: prefill topk {topk}")
     c = make_case(_wl([4000], [260], topk=topk, seed=topk + 7))
     _full(c, f"pf topk {topk}")
+
+
+@pytest.mark.parametrize("locality", [0.5, 0.75])
+def test_prefill_locality(locality):
+    log(f"case: prefill locality {locality}")
+    c = make_case(_wl([6000, 2200], [400, 130], topk=12, seed=int(locality * 8), locality=locality))
+    _full(c, f"pf loc {locality}")
 
 
 def test_prefill_131072_sampled_query_blocks():

@@ -277,6 +277,45 @@ def test_select_brute_force_subsets(oracle, seed):
         assert np.all(sel[0, 0, 0, len(want):] == -1)
 
 
+@pytest.mark.parametrize("locality", [0.25, 0.5, 0.75])
+def test_select_locality_brute_force(oracle, locality):
+    """Locality constraint: round(locality * k) of the budget are the candidates
+    right before the window whatever their scores; the rest is the max-sum
+    subset (lexicographic tie rule) of the earlier candidates."""
+    rng = np.random.default_rng(int(locality * 100))
+    nb, w = 15, 3
+    L = nb * 64 - 5
+    scores = rng.integers(0, 4, (1, 1, 1, nb)).astype(np.float64)
+    # the local candidates get the lowest scores, so plain top-k would drop them
+    ncand = nb - w
+    for k in range(0, ncand + 2):
+        k_loc = math.floor(locality * k + 0.5)
+        p = Params(num_q_heads=2, num_kv_heads=1, head_dim=8, window=w * 64, topk=k,
+                   locality=locality)
+        sc = scores.copy()
+        sc[0, 0, 0, ncand - min(k_loc, ncand):ncand] = -1.0
+        sel, cnt = oracle.select_blocks(p, sc, None, np.array([0, L], np.int32))
+        n_loc = min(k_loc, ncand)
+        rest = ncand - n_loc
+        kq = min(k - k_loc, rest)
+        best = max(itertools.combinations(range(rest), kq),
+                   key=lambda c: (sum(sc[0, 0, 0, list(c)]), [-x for x in c]))
+        want = sorted(best) + list(range(rest, nb))
+        assert cnt[0, 0, 0] == len(want) == min(nb, k + w), (k, locality)
+        assert sel[0, 0, 0, :len(want)].tolist() == want, (k, locality)
+
+
+def test_select_full_locality_is_a_sliding_window(oracle):
+    """locality 1: the selection is the last topk + window blocks, scores unused."""
+    p = Params(num_q_heads=2, num_kv_heads=1, head_dim=8, topk=5, locality=1.0)
+    for L in [100, 1500, 5000]:
+        nb = (L + 63) // 64
+        scores = np.random.default_rng(L).random((1, 1, 1, nb))
+        sel, cnt = oracle.select_blocks(p, scores, None, np.array([0, L], np.int32))
+        n = cnt[0, 0, 0]
+        assert sel[0, 0, 0, :n].tolist() == list(range(max(0, nb - 21), nb))
+
+
 def test_select_window_only_and_short_sequences(oracle):
     p = Params(num_q_heads=2, num_kv_heads=1, head_dim=8, topk=3)
     for L in [1, 63, 64, 65, 1024, 1025, 1088, 1089]:

@@ -191,6 +191,54 @@ namespace {
 
 nosa_status hip_status(hipError_t e) { return e == hipSuccess ? NOSA_OK : NOSA_ERR_HIP; }
 
+// Workspace of the whole-prompt prefill: the prefill scratch of one chunk,
+// then the chunk's bookkeeping, gathered queries, outputs, importance and
+// selection.
+struct PromptLayout {
+    int C = 0, mq = 0;  // chunk (queries), query blocks per chunk
+    size_t off_cuk = 0, off_cuq = 0, off_valid = 0, off_q = 0, off_out = 0, off_lse = 0,
+           off_scores = 0, off_sel = 0, off_cnt = 0, bytes = 0;
+};
+
+PromptLayout prompt_layout(const Plan& pl, const PfPlan& pf, int B, int C)
+{
+    PromptLayout Y;
+    Y.C = C;
+    Y.mq = C / kBlock;
+    const size_t b = (size_t)B, rows = b * C, qb = b * Y.mq * pl.Hkv;
+    size_t off = pf.bytes;
+    Y.off_cuk = off;    off += align256((b + 1) * sizeof(int32_t));
+    Y.off_cuq = off;    off += align256((b + 1) * sizeof(int32_t));
+    Y.off_valid = off;  off += align256(b * sizeof(int32_t));
+    Y.off_q = off;      off += align256(rows * pl.Hq * kHeadDim * sizeof(nosa_bf16));
+    Y.off_out = off;    off += align256(rows * pl.Hq * kHeadDim * sizeof(float));
+    Y.off_lse = off;    off += align256(rows * pl.Hq * sizeof(float));
+    Y.off_scores = off; off += align256(qb * (size_t)pl.max_nb * sizeof(float));
+    Y.off_sel = off;    off += align256(qb * (size_t)pl.max_sel * sizeof(int32_t));
+    Y.off_cnt = off;    off += align256(qb * sizeof(int32_t));
+    Y.bytes = off;
+    return Y;
+}
+
+// Chunk length actually used: the requested one, capped by the longest
+// prompt rounded up to whole blocks.
+nosa_status prompt_plan(const nosa_params* p, int batch, int max_seqlen, int chunk, Plan* pl,
+                        PfPlan* pf, PromptLayout* Y)
+{
+    nosa_status st = check_params(p);
+    if (st != NOSA_OK) return st;
+    if (chunk <= 0 || chunk % kBlock != 0) return NOSA_ERR_INVALID;
+    st = check_sizes(batch, batch > 0 ? 1 : 0, max_seqlen);
+    if (st != NOSA_OK) return st;
+    st = make_plan(p, batch, max_seqlen, pl);
+    if (st != NOSA_OK) return st;
+    const int cap = ceil_div(max_seqlen > 0 ? max_seqlen : 1, kBlock) * kBlock;
+    const int C = chunk < cap ? chunk : cap;
+    make_pf_plan(*pl, C, pf);
+    *Y = prompt_layout(*pl, *pf, batch, C);
+    return NOSA_OK;
+}
+
 // Query-side arguments: decode (cu_seqlens_q NULL, one query per sequence)
 // or a chunk per sequence (cu_seqlens_q given, at most max_seqlen_q queries).
 nosa_status check_queries(const int32_t* cu_seqlens_q, int max_seqlen_q)
@@ -336,6 +384,62 @@ nosa_status nosa_sparse_attend(const nosa_params* params, const nosa_paged_kv* k
     if (!workspace || workspace_bytes < pl.bytes) return NOSA_ERR_WORKSPACE;
     return hip_status(launch_attend(pl, *kv, q, cu_seqlens_k, sel_idx, sel_count,
                                     carve(pl, workspace), out, lse, as_stream(stream)));
+}
+
+nosa_status nosa_prefill_sparse_workspace_size(const nosa_params* params, int32_t batch, int32_t max_seqlen,
+                                        int32_t chunk, size_t* bytes)
+{
+    if (!params || !bytes) return NOSA_ERR_NULL;
+    Plan pl;
+    PfPlan pf;
+    PromptLayout Y;
+    const nosa_status st = prompt_plan(params, batch, max_seqlen, chunk, &pl, &pf, &Y);
+    if (st != NOSA_OK) return st;
+    *bytes = Y.bytes;
+    return NOSA_OK;
+}
+
+nosa_status nosa_prefill_sparse(const nosa_params* params, const nosa_paged_kv* kv, const nosa_bf16* q,
+                                const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                                int32_t chunk, float* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream)
+{
+    Plan pl;
+    PfPlan pf;
+    PromptLayout Y;
+    nosa_status st = prompt_plan(params, batch, max_seqlen, chunk, &pl, &pf, &Y);
+    if (st != NOSA_OK) return st;
+    st = check_kv(kv, max_seqlen, false);
+    if (st != NOSA_OK) return st;
+    if (!q || !cu_seqlens || !out) return NOSA_ERR_NULL;
+    if (batch == 0) return NOSA_OK;
+    if (!workspace || workspace_bytes < Y.bytes) return NOSA_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    int32_t* cu_k_c = reinterpret_cast<int32_t*>(ws + Y.off_cuk);
+    int32_t* cu_q_c = reinterpret_cast<int32_t*>(ws + Y.off_cuq);
+    int32_t* valid_c = reinterpret_cast<int32_t*>(ws + Y.off_valid);
+    nosa_bf16* qc = reinterpret_cast<nosa_bf16*>(ws + Y.off_q);
+    float* oc = reinterpret_cast<float*>(ws + Y.off_out);
+    float* lc = reinterpret_cast<float*>(ws + Y.off_lse);
+    float* scores = reinterpret_cast<float*>(ws + Y.off_scores);
+    int32_t* sel = reinterpret_cast<int32_t*>(ws + Y.off_sel);
+    int32_t* cnt = reinterpret_cast<int32_t*>(ws + Y.off_cnt);
+    const hipStream_t sm = as_stream(stream);
+    const int C = Y.C, nch = ceil_div(max_seqlen, C);
+    const int gx = ceil_div(C / kPoolS + 1, 16);  // pooled keys completed by one chunk, 16 per workgroup
+    for (int c = 0; c < nch; ++c) {
+        hipError_t e = launch_chunk_setup(cu_seqlens, batch, pl.Lmax, c, C, cu_k_c, cu_q_c, valid_c, sm);
+        if (e == hipSuccess) e = launch_chunk_gather(q, cu_seqlens, cu_q_c, batch, c, C, pl.Hq, qc, sm);
+        if (e == hipSuccess) e = launch_kc_build(pl, *kv, cu_k_c, valid_c, gx, sm);
+        if (e == hipSuccess) e = launch_pf_scores(pl, pf, *kv, qc, cu_q_c, cu_k_c, workspace, scores, sm);
+        if (e == hipSuccess) e = launch_select(pl, cu_k_c, cu_q_c, C, scores, sel, cnt, sm);
+        if (e == hipSuccess) e = launch_pf_attend(pl, pf, *kv, qc, cu_q_c, cu_k_c, sel, cnt, oc, lc, sm);
+        if (e == hipSuccess)
+            e = launch_chunk_scatter(oc, lse ? lc : nullptr, cu_seqlens, cu_q_c, batch, c, C, pl.Hq,
+                                     out, lse, sm);
+        if (e != hipSuccess) return NOSA_ERR_HIP;
+    }
+    return NOSA_OK;
 }
 
 nosa_status nosa_decode_step(const nosa_params* params, const nosa_paged_kv* kv,

@@ -103,4 +103,13 @@ hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_k
                             const int32_t* sel, const int32_t* cnt, float* out, float* lse,
                             hipStream_t stream);
 
+// Whole-prompt prefill, chunk by chunk (nosa_prefill.hip).
+hipError_t launch_chunk_setup(const int32_t* cu, int B, int Lmax, int c, int C, int32_t* cu_k_c,
+                              int32_t* cu_q_c, int32_t* valid_c, hipStream_t stream);
+hipError_t launch_chunk_gather(const nosa_bf16* q, const int32_t* cu, const int32_t* cu_q_c, int B,
+                               int c, int C, int Hq, nosa_bf16* qc, hipStream_t stream);
+hipError_t launch_chunk_scatter(const float* oc, const float* lc, const int32_t* cu,
+                                const int32_t* cu_q_c, int B, int c, int C, int Hq, float* out,
+                                float* lse, hipStream_t stream);
+
 }  // namespace nosa

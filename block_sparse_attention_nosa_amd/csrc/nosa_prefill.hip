@@ -639,4 +639,98 @@ hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_k
     return hipGetLastError();
 }
 
+// ------------------------------------------------- whole-prompt prefill ---
+//
+// A prompt is processed in chunks of C queries (C a multiple of 64): chunk c
+// of sequence s is its queries cC .. min(cC + C, L_s) - 1 against its first
+// min(cC + C, L_s) tokens, which is the chunk convention of the entry points
+// above with the query blocks of the whole prompt (64 from its start).  Per
+// chunk: the bookkeeping arrays, the chunk's query rows gathered into a
+// compact buffer, the pooled keys completed by its tokens, importance,
+// selection, attention, and the output rows scattered back.
+
+// cu_k_c / cu_q_c: the chunk's context lengths and query counts as
+// cumulative arrays; valid_c: tokens already pooled (cC, capped by L_s).
+__global__ __launch_bounds__(64) void chunk_setup_kernel(const int32_t* __restrict__ cu, int B,
+                                                         int Lmax, int c, int C,
+                                                         int32_t* __restrict__ cu_k_c,
+                                                         int32_t* __restrict__ cu_q_c,
+                                                         int32_t* __restrict__ valid_c)
+{
+    if (threadIdx.x != 0) return;
+    int k = 0, q = 0;
+    cu_k_c[0] = 0;
+    cu_q_c[0] = 0;
+    for (int s = 0; s < B; ++s) {
+        const int L = seq_len(cu, s, Lmax);
+        const long long e = (long long)(c + 1) * C, b = (long long)c * C;
+        const int end = e < L ? (int)e : L, start = b < L ? (int)b : L;
+        k += end;
+        q += end - start;
+        cu_k_c[s + 1] = k;
+        cu_q_c[s + 1] = q;
+        valid_c[s] = start;
+    }
+}
+
+// Workgroup (i, s): query row cC + i of sequence s (prompt row cu[s] + cC + i)
+// to chunk row cu_q_c[s] + i, if it exists.  Rows of Hq * 128 bf16.
+__global__ __launch_bounds__(256) void chunk_gather_kernel(const uint16_t* __restrict__ q,
+                                                           const int32_t* __restrict__ cu,
+                                                           const int32_t* __restrict__ cu_q_c,
+                                                           int c, int C, int Hq,
+                                                           uint16_t* __restrict__ qc)
+{
+    const int i = blockIdx.x, s = blockIdx.y;
+    if (i >= cu_q_c[s + 1] - cu_q_c[s]) return;
+    const uint4* src = reinterpret_cast<const uint4*>(q + ((size_t)cu[s] + (size_t)c * C + i) * Hq * D);
+    uint4* dst = reinterpret_cast<uint4*>(qc + ((size_t)cu_q_c[s] + i) * Hq * D);
+    for (int x = threadIdx.x; x < Hq * D / 8; x += 256) dst[x] = src[x];
+}
+
+// The reverse for the outputs: chunk row cu_q_c[s] + i of out (Hq * 128
+// fp32) and lse (Hq fp32, when given) to prompt row cu[s] + cC + i.
+__global__ __launch_bounds__(256) void chunk_scatter_kernel(const float* __restrict__ oc,
+                                                            const float* __restrict__ lc,
+                                                            const int32_t* __restrict__ cu,
+                                                            const int32_t* __restrict__ cu_q_c,
+                                                            int c, int C, int Hq,
+                                                            float* __restrict__ out,
+                                                            float* __restrict__ lse)
+{
+    const int i = blockIdx.x, s = blockIdx.y;
+    if (i >= cu_q_c[s + 1] - cu_q_c[s]) return;
+    const size_t src_row = (size_t)cu_q_c[s] + i, dst_row = (size_t)cu[s] + (size_t)c * C + i;
+    const float4* src = reinterpret_cast<const float4*>(oc + src_row * Hq * D);
+    float4* dst = reinterpret_cast<float4*>(out + dst_row * Hq * D);
+    for (int x = threadIdx.x; x < Hq * D / 4; x += 256) dst[x] = src[x];
+    if (lse && lc)
+        for (int h = threadIdx.x; h < Hq; h += 256) lse[dst_row * Hq + h] = lc[src_row * Hq + h];
+}
+
+hipError_t launch_chunk_setup(const int32_t* cu, int B, int Lmax, int c, int C, int32_t* cu_k_c,
+                              int32_t* cu_q_c, int32_t* valid_c, hipStream_t stream)
+{
+    hipLaunchKernelGGL(chunk_setup_kernel, dim3(1), dim3(64), 0, stream, cu, B, Lmax, c, C, cu_k_c,
+                       cu_q_c, valid_c);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_gather(const nosa_bf16* q, const int32_t* cu, const int32_t* cu_q_c, int B,
+                               int c, int C, int Hq, nosa_bf16* qc, hipStream_t stream)
+{
+    hipLaunchKernelGGL(chunk_gather_kernel, dim3(C, B), dim3(256), 0, stream, q, cu, cu_q_c, c, C,
+                       Hq, qc);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_scatter(const float* oc, const float* lc, const int32_t* cu,
+                                const int32_t* cu_q_c, int B, int c, int C, int Hq, float* out,
+                                float* lse, hipStream_t stream)
+{
+    hipLaunchKernelGGL(chunk_scatter_kernel, dim3(C, B), dim3(256), 0, stream, oc, lc, cu, cu_q_c,
+                       c, C, Hq, out, lse);
+    return hipGetLastError();
+}
+
 }  // namespace nosa

@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
             "nosa_select_blocks": [P, vp, vp, vp, i32, i32, i32, vp, vp, vp],
             "nosa_sparse_attend": [P, KV, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp],
             "nosa_decode_step": [P, KV, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
+            "nosa_prefill_sparse_workspace_size": [P, i32, i32, i32, ctypes.POINTER(sz)],
+            "nosa_prefill_sparse": [P, KV, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp],
         }
         for name, argtypes in sigs.items():
             f = getattr(L, name)
@@ -174,5 +176,22 @@ def nosa_decode_step(p, kv, q, cu_seqlens_k, batch, max_seqlen_k, out, lse, work
         ctypes.byref(p), ctypes.byref(kv), _ptr(q), _ptr(cu_seqlens_k), batch, max_seqlen_k,
         _ptr(out), _ptr(lse), _ptr(sel_idx), _ptr(sel_count), _ptr(block_scores),
         _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))
+
+
+def nosa_prefill_sparse_workspace_size(p: nosa_params, batch: int, max_seqlen: int,
+                                       chunk: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("nosa_prefill_sparse_workspace_size", lib().nosa_prefill_sparse_workspace_size(
+        ctypes.byref(p), batch, max_seqlen, chunk, ctypes.byref(out)))
+    return int(out.value)
+
+
+def nosa_prefill_sparse(p, kv, q, cu_seqlens, batch, max_seqlen, chunk, out, lse, workspace,
+                        stream=None):
+    _check("nosa_prefill_sparse", lib().nosa_prefill_sparse(
+        ctypes.byref(p), ctypes.byref(kv), _ptr(q), _ptr(cu_seqlens), batch, max_seqlen, chunk,
+        _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream)))

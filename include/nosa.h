@@ -235,6 +235,39 @@ nosa_status nosa_decode_step(const nosa_params* params, const nosa_paged_kv* kv,
                              int32_t* sel_count, float* block_scores, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Workspace bytes needed by nosa_prefill_sparse for at most `batch` prompts
+ * of at most max_seqlen tokens processed `chunk` queries at a time (chunk a
+ * positive multiple of block_size).  Host only; enqueues nothing.  Errors as
+ * nosa_workspace_size, plus NOSA_ERR_INVALID for a bad chunk. */
+nosa_status nosa_prefill_sparse_workspace_size(const nosa_params* params, int32_t batch,
+                                               int32_t max_seqlen, int32_t chunk, size_t* bytes);
+
+/* Sparse prefill of whole prompts [page "NOSA技术架构解析", section 1.3: the
+ * mode that is sparse from the first token on, beside the mode with a dense
+ * prefill and sparse decoding].  Every query of every prompt attends as in
+ * nosa_sparse_attend to the blocks selected for its query block (64 queries
+ * from position 0 on) by nosa_block_scores + nosa_select_blocks, with the
+ * keys of the prompt itself: the result equals those three calls with
+ * cu_seqlens_q = cu_seqlens_k = cu_seqlens.  The prompt is processed in
+ * chunks of `chunk` positions (the same for every sequence, a multiple of
+ * block_size); chunk c pools the compressed keys its tokens complete, then
+ * scores, selects and attends for its queries, so the workspace scales with
+ * the chunk and not with the prompt.  The chunk does not change the result.
+ * K and V of every prompt token must already be in the pages; kc_pool is
+ * written for every key of the prompts (as nosa_compress_keys with
+ * kc_valid_len NULL).  q: device [total tokens][Hq][d] bf16 in cu_seqlens
+ * order; cu_seqlens: device [batch+1], lengths <= max_seqlen.
+ * out: device fp32 [total tokens][Hq][d]; lse: device fp32 [total tokens][Hq]
+ * or NULL.  workspace: device, at least nosa_prefill_sparse_workspace_size
+ * bytes for the same (params, batch, max_seqlen, chunk), owned by the
+ * caller, contents irrelevant on entry.  Enqueued on `stream`; returns after
+ * enqueueing.  Errors: NOSA_ERR_NULL, NOSA_ERR_INVALID (bad sizes, chunk or
+ * table), NOSA_ERR_WORKSPACE, NOSA_ERR_UNSUPPORTED, NOSA_ERR_HIP. */
+nosa_status nosa_prefill_sparse(const nosa_params* params, const nosa_paged_kv* kv,
+                                const nosa_bf16* q, const int32_t* cu_seqlens, int32_t batch,
+                                int32_t max_seqlen, int32_t chunk, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

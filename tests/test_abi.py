@@ -23,7 +23,8 @@ def test_exports_every_declared_function(L):
     names = nosa.header_functions()
     assert set(names) >= {"nosa_abi_version", "nosa_status_string", "nosa_workspace_size",
                           "nosa_compress_keys", "nosa_block_scores", "nosa_select_blocks",
-                          "nosa_sparse_attend", "nosa_decode_step"}
+                          "nosa_sparse_attend", "nosa_decode_step", "nosa_prefill_sparse",
+                          "nosa_prefill_sparse_workspace_size"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -155,3 +156,27 @@ def test_other_entry_points_host_errors(L):
                                 FAKE, FAKE, FAKE, None, FAKE, 8, None) == 4
     assert L.nosa_sparse_attend(ctypes.byref(p), ctypes.byref(kv), FAKE, None, FAKE, 8, 1, 16384,
                                 None, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
+
+
+def test_prompt_prefill_host_errors(L):
+    p = nosa.params()
+    kv = _kv()
+    size = lambda ch, B=2, Lm=5000: nosa.nosa_prefill_sparse_workspace_size(p, B, Lm, ch)
+    assert size(512) > 0
+    assert size(512) < size(4096)                 # scratch scales with the chunk
+    assert size(8192) == size(5056)                # capped by the longest prompt (whole blocks)
+    for bad in (0, -64, 100):
+        with pytest.raises(nosa.NosaError) as e:
+            size(bad)
+        assert e.value.status == 2
+    call = lambda **kw: L.nosa_prefill_sparse(
+        ctypes.byref(p), ctypes.byref(kv), kw.get("q", FAKE), kw.get("cu", FAKE), kw.get("B", 2),
+        kw.get("Lm", 5000), kw.get("ch", 512), kw.get("out", FAKE), None, kw.get("ws", FAKE),
+        kw.get("wsb", 0), None)
+    assert call(q=None) == 1
+    assert call(cu=None) == 1
+    assert call(out=None) == 1
+    assert call(ch=96) == 2
+    assert call(Lm=16385) == 2                     # the table cannot reach it
+    assert call(wsb=100) == 4
+    assert call(B=0) == 0

@@ -43,6 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes
 LAYERS = 8
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention-decode-b8-16k_traffic.md")
 CALIB_BYTES = 256 << 20   # bytes read (and written) by the calibration copy
@@ -135,6 +136,15 @@ def main():
                          "(NOSA-1B head shape, top-k 64, window 1024) instead of a decode step")
     ap.add_argument("--chunk", type=int, default=4096,
                     help="queries per chunk of the whole-prompt prefill")
+    ap.add_argument("--offload", action="store_true",
+                    help="time the decode step over an offloaded KV cache (pages in pinned host "
+                         "memory, a block cache in device memory) instead of device pools")
+    ap.add_argument("--query-corr", type=float, default=0.9,
+                    help="offload: correlation of each step's query with the previous step's "
+                         "(q_t = c q_(t-1) + sqrt(1 - c^2) noise); 1 repeats the query")
+    ap.add_argument("--cache-blocks", type=int, default=0,
+                    help="offload: block-cache slots per (sequence, KV head); 0 = twice the "
+                         "query-aware budget, at most 256")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run the calibration copy and the kernels once each for counters")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -164,6 +174,8 @@ def main():
                               "name": f"{w.name}-locality{args.locality:g}"})
     if args.prompt:
         return prompt_main(w, args)
+    if args.offload:
+        return offload_main(w, args)
     if w.q_lens is not None:
         return prefill_main(w, args)
     nsteps = w.extra_tokens + 1
@@ -440,6 +452,152 @@ def prompt_main(w, args):
                         "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                         "traffic": None, "scoring_gflop": round(fs / 1e9, 2),
                         "attention_gflop": round(fa / 1e9, 2)}}
+    print(json.dumps(res), flush=True)
+
+
+def offload_main(w, args):
+    """Decode steps over an offloaded KV cache (not the headline metric): the
+    K/V pages of every layer cache in pinned host memory, the recent pages in
+    a device ring, a block cache per (sequence, KV head).  Each step's query
+    is correlated with the previous one (--query-corr), so consecutive
+    selections overlap the way decoding queries do; the step reads from host
+    memory only the picks its cache misses."""
+    import math
+    import numpy as np
+    import torch
+    from block_sparse_attention_nosa_amd import nosa, synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t_setup = time.time()
+    nsteps = w.extra_tokens + 1
+    layers = build_layers(w, nsteps)
+    B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    lens_at = [[L + t for L in w.lens] for t in range(nsteps)]
+    cu_at = [synth.cu_from_lens(l, "cuda") for l in lens_at]
+    maxL = max(lens_at[-1])
+    p = layers[0]["p"]
+    k_loc = math.floor(w.locality * w.topk + 0.5)
+    wb = w.window // w.block_size + k_loc
+    kq_budget = w.topk - k_loc
+    cap = args.cache_blocks or min(256, 2 * kq_budget)
+    # ring of recent pages: every block that is forced (or read by the key
+    # append) at some step of the run, so the ring is written once
+    lo = [max(0, (L + 63) // 64 - max(wb, 2)) for L in w.lens]
+    hi = [(L + nsteps - 1 + 63) // 64 - 1 for L in w.lens]
+    R = max(h - l + 1 for l, h in zip(lo, hi))
+    rho = args.query_corr
+    offs = []
+    for li, L in enumerate(layers):
+        pg = L["pg"]
+        k_host = torch.empty(pg["k_pool"].shape, dtype=torch.bfloat16, pin_memory=True)
+        v_host = torch.empty(pg["v_pool"].shape, dtype=torch.bfloat16, pin_memory=True)
+        k_host.copy_(pg["k_pool"].cpu())
+        v_host.copy_(pg["v_pool"].cpu())
+        page = pg["k_pool"].shape[-1]
+        k_ring = torch.zeros(B, R, Hkv, page, dtype=torch.bfloat16, device=dev)
+        v_ring = torch.zeros_like(k_ring)
+        for s in range(B):
+            for b in range(lo[s], hi[s] + 1):
+                pid = int(pg["block_table"][s, b])
+                k_ring[s, b % R] = pg["k_pool"][pid]
+                v_ring[s, b % R] = pg["v_pool"][pid]
+        cache_k = torch.zeros(B, Hkv, cap, page, dtype=torch.bfloat16, device=dev)
+        cache_v = torch.zeros_like(cache_k)
+        cmap = torch.full((B, Hkv, cap), -1, dtype=torch.int32, device=dev)
+        cused = torch.zeros((B, Hkv, cap), dtype=torch.int32, device=dev)
+        okv = nosa.offload_kv(k_host, v_host, pg["kc_pool"], pg["block_table"], k_ring, v_ring,
+                              cache_k, cache_v, cmap, cused)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed + 104729 * li)
+        qf = L["inp"]["q"].float()
+        qs = []
+        for t in range(nsteps):
+            if t:
+                qf = rho * qf + math.sqrt(max(0.0, 1 - rho * rho)) * torch.randn(
+                    qf.shape, generator=gen, device=dev)
+            qs.append(qf.to(torch.bfloat16))
+        # the device pools are not used any more: only the host copies are read
+        del pg["k_pool"], pg["v_pool"], L["kv"]
+        offs.append(dict(okv=okv, qs=qs, keep=(k_host, v_host, k_ring, v_ring, cache_k, cache_v,
+                                                cmap, cused)))
+    torch.cuda.empty_cache()
+    ws = torch.zeros(nosa.nosa_offload_workspace_size(p, B, maxL, cap), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty(B, Hq, d, device=dev)
+    lse = torch.empty(B, Hq, device=dev)
+    chunk = LAYERS * nsteps  # one graph runs every step of every layer cache once
+    fetch = torch.zeros(chunk, B, Hkv, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    print(f"[bench] setup {time.time() - t_setup:.1f}s; offloaded {w.name}: ring {R} blocks, "
+          f"cache {cap} blocks, query correlation {rho}", file=sys.stderr, flush=True)
+
+    def step(i):
+        li = i % LAYERS
+        t = (i // LAYERS) % nsteps
+        o = offs[li]
+        nosa.nosa_offload_decode_step(p, o["okv"], o["qs"][t], cu_at[t], B, maxL, out, lse, ws,
+                                      fetch_count=fetch[i % chunk])
+        return t
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, capture_error_mode="relaxed"):
+        ts = [step(args.warmup + i) for i in range(chunk)]
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // chunk)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / (reps * chunk)
+    fetched = fetch.double().sum().item() / chunk  # blocks per step, last replay
+    picks = np.mean([sum(min(kq_budget, max(0, (L + 63) // 64 - wb)) for L in lens_at[t]) * Hkv
+                     for t in ts])
+    blk_bytes = 2 * w.block_size * d * 2  # K and V of one block of one KV head
+    host_gbs = fetched * blk_bytes / (ms_step * 1e-3) / 1e9
+    # the link itself: one large pinned-host to device copy
+    src = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(4):
+        dst.copy_(src, non_blocking=True)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 4 * (256 << 20) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    print(f"[bench] {reps * chunk} offloaded steps: {ms_step * 1e3:.1f} us/step, "
+          f"{fetched:.1f} of {picks:.1f} picks read from host per step, {host_gbs:.1f} GB/s "
+          f"(host-to-device copy {copy_gbs:.1f} GB/s)", file=sys.stderr, flush=True)
+    res = {
+        "metric": "offloaded-KV sparse-attn decode tokens/s, batch 8, 16K ctx; host-link GB/s "
+                  "of the fetched blocks",
+        "value": round(B / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": reps * chunk, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded bf16 N(0,1) K/V, planted blocks, permuted pages; queries "
+                "correlated from step to step)",
+        "config": {"workload": w.name + "-offloaded", "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "context": w.lens[0] - 1, "decode_steps": nsteps, "topk_blocks": w.topk,
+                   "window_tokens": w.window, "locality": w.locality, "query_corr": rho,
+                   "cache_blocks": cap, "recent_blocks": R, "layer_caches": LAYERS,
+                   "picks_per_step": round(float(picks), 1),
+                   "fetched_blocks_per_step": round(fetched, 2),
+                   "fetched_fraction": round(fetched / picks, 4) if picks else 0.0},
+        "roofline": {"kernel": "top_kernel (offloaded: picks missing from the cache read from "
+                               "host memory)", "bound": "host-link",
+                     "achieved": round(host_gbs, 2), "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(host_gbs / HOST_LINK_PEAK_GBS, 4), "traffic": None,
+                     "measured_copy_gbs": round(copy_gbs, 2)},
+        "cpu_baseline": None,
+    }
     print(json.dumps(res), flush=True)
 
 

@@ -191,6 +191,38 @@ namespace {
 
 nosa_status hip_status(hipError_t e) { return e == hipSuccess ? NOSA_OK : NOSA_ERR_HIP; }
 
+// Block cache of the offloaded KV: at least the query-aware share of the
+// budget (every pick needs a slot), at most one slot per thread of a
+// workgroup.  The window must hold a block, so that every pick is a complete
+// block that no later step changes.
+nosa_status check_cache(const Plan& pl, int cache_blocks)
+{
+    if (cache_blocks < pl.topk || cache_blocks <= 0) return NOSA_ERR_INVALID;
+    if (cache_blocks > 256 || pl.wblocks < 1) return NOSA_ERR_UNSUPPORTED;
+    return NOSA_OK;
+}
+
+size_t offload_bytes(const Plan& pl, int cache_blocks)
+{
+    return pl.bytes + align256(2 * (size_t)pl.B * pl.Hkv * cache_blocks * sizeof(int32_t));
+}
+
+// The address at which the device reads pinned host memory p, or null when p
+// is not memory the device can read.
+const nosa_bf16* device_view(const nosa_bf16* p)
+{
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error of the query
+        return nullptr;
+    }
+    if (at.type != hipMemoryTypeHost || !at.devicePointer) return nullptr;
+    const char* dev = static_cast<const char*>(at.devicePointer);
+    if (at.hostPointer)
+        dev += reinterpret_cast<const char*>(p) - static_cast<const char*>(at.hostPointer);
+    return reinterpret_cast<const nosa_bf16*>(dev);
+}
+
 // Workspace of the whole-prompt prefill: the prefill scratch of one chunk,
 // then the chunk's bookkeeping, gathered queries, outputs, importance and
 // selection.
@@ -440,6 +472,74 @@ nosa_status nosa_prefill_sparse(const nosa_params* params, const nosa_paged_kv* 
         if (e != hipSuccess) return NOSA_ERR_HIP;
     }
     return NOSA_OK;
+}
+
+nosa_status nosa_offload_workspace_size(const nosa_params* params, int32_t batch,
+                                        int32_t max_seqlen_k, int32_t cache_blocks, size_t* bytes)
+{
+    if (!params || !bytes) return NOSA_ERR_NULL;
+    nosa_status st = check_sizes(batch, batch > 0 ? 1 : 0, max_seqlen_k);
+    if (st != NOSA_OK) return st;
+    Plan pl;
+    st = make_plan(params, batch, max_seqlen_k, &pl);
+    if (st != NOSA_OK) return st;
+    st = check_cache(pl, cache_blocks);
+    if (st != NOSA_OK) return st;
+    *bytes = offload_bytes(pl, cache_blocks);
+    return NOSA_OK;
+}
+
+nosa_status nosa_offload_decode_step(const nosa_params* params, const nosa_offload_kv* kv,
+                                     const nosa_bf16* q, const int32_t* cu_seqlens_k,
+                                     int32_t batch, int32_t max_seqlen_k, float* out, float* lse,
+                                     int32_t* sel_idx, int32_t* sel_count, int32_t* fetch_count,
+                                     void* workspace, size_t workspace_bytes, void* stream)
+{
+    nosa_status st = check_params(params);
+    if (st != NOSA_OK) return st;
+    st = check_sizes(batch, batch > 0 ? 1 : 0, max_seqlen_k);
+    if (st != NOSA_OK) return st;
+    if (!kv) return NOSA_ERR_NULL;
+    if (!kv->k_host || !kv->v_host || !kv->kc_pool || !kv->block_table || !kv->k_recent ||
+        !kv->v_recent || !kv->cache_k || !kv->cache_v || !kv->cache_map || !kv->cache_used)
+        return NOSA_ERR_NULL;
+    if (kv->max_blocks_per_seq <= 0 || kv->num_pages <= 0) return NOSA_ERR_INVALID;
+    if ((long long)kv->max_blocks_per_seq * kBlock < (long long)max_seqlen_k) return NOSA_ERR_INVALID;
+    if (!q || !cu_seqlens_k || !out) return NOSA_ERR_NULL;
+    if ((sel_idx == nullptr) != (sel_count == nullptr)) return NOSA_ERR_NULL;
+    if (batch == 0) return NOSA_OK;
+    Plan pl;
+    st = make_plan(params, batch, max_seqlen_k, &pl);
+    if (st != NOSA_OK) return st;
+    st = check_cache(pl, kv->cache_blocks);
+    if (st != NOSA_OK) return st;
+    const int need = pl.wblocks > 2 ? pl.wblocks : 2;
+    if (kv->recent_blocks < need) return NOSA_ERR_INVALID;
+    if (!workspace || workspace_bytes < offload_bytes(pl, kv->cache_blocks)) return NOSA_ERR_WORKSPACE;
+    Offload off;
+    off.k_host = device_view(kv->k_host);
+    off.v_host = device_view(kv->v_host);
+    if (!off.k_host || !off.v_host) return NOSA_ERR_INVALID;
+    off.k_recent = kv->k_recent;
+    off.v_recent = kv->v_recent;
+    off.recent = kv->recent_blocks;
+    off.cache_k = kv->cache_k;
+    off.cache_v = kv->cache_v;
+    off.cache_map = kv->cache_map;
+    off.cache_used = kv->cache_used;
+    off.cap = kv->cache_blocks;
+    off.map_next = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + pl.bytes);
+    off.used_next = off.map_next + (size_t)pl.B * pl.Hkv * kv->cache_blocks;
+    off.fetch_out = fetch_count;
+    nosa_paged_kv pk;
+    pk.k_pool = off.k_host;
+    pk.v_pool = off.v_host;
+    pk.kc_pool = kv->kc_pool;
+    pk.block_table = kv->block_table;
+    pk.max_blocks_per_seq = kv->max_blocks_per_seq;
+    pk.num_pages = kv->num_pages;
+    return hip_status(launch_decode(pl, pk, q, cu_seqlens_k, carve(pl, workspace), out, lse,
+                                    sel_idx, sel_count, nullptr, as_stream(stream), &off));
 }
 
 nosa_status nosa_decode_step(const nosa_params* params, const nosa_paged_kv* kv,

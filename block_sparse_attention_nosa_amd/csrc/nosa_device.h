@@ -156,6 +156,23 @@ __device__ __forceinline__ void load_page(const uint16_t* __restrict__ kb,
         for (int nt = 0; nt < 8; ++nt) p.v[u][nt] = ldg16(vb + (u * 8 + nt) * 512 + lane8);
 }
 
+// The page held in p back to memory at kb / vb, in the same order (a copy of
+// a page into another pool).
+__device__ __forceinline__ void store_page(uint16_t* __restrict__ kb, uint16_t* __restrict__ vb,
+                                           int lane8, const PageRegs& p)
+{
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            *reinterpret_cast<uint4*>(kb + (t * 4 + st) * 512 + lane8) = p.k[t][st];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+            *reinterpret_cast<uint4*>(vb + (u * 8 + nt) * 512 + lane8) = p.v[u][nt];
+}
+
 __device__ __forceinline__ void attend_loaded(const PageRegs& p, int limit, const bf16x8 (&qb)[4],
                                               float scale_log2, int r, int kq, AttnState& A);
 

@@ -72,6 +72,23 @@ struct PfPlan {
     size_t off_part = 0, off_colsum = 0, bytes = 0;
 };
 
+// Offloaded KV (device pointers; the host pools as the device sees them).
+struct Offload {
+    const nosa_bf16* k_host;
+    const nosa_bf16* v_host;
+    const nosa_bf16* k_recent;  // [batch][recent][Hkv][page]: block b in slot b % recent
+    const nosa_bf16* v_recent;
+    int recent = 0;
+    nosa_bf16* cache_k;         // [batch][Hkv][cap][page]
+    nosa_bf16* cache_v;
+    int32_t* cache_map;         // [batch][Hkv][cap]
+    int32_t* cache_used;        // [batch][Hkv][cap]: length at the last pick
+    int cap = 0;
+    int32_t* map_next;          // workspace, as cache_map
+    int32_t* used_next;         // workspace, as cache_used
+    int32_t* fetch_out;         // [batch][Hkv] or null
+};
+
 // Builds the plan for a decode batch; returns NOSA_OK or an error.
 nosa_status make_plan(const nosa_params* p, int batch, int max_seqlen_k, Plan* plan);
 Workspace carve(const Plan& pl, void* ws);
@@ -90,10 +107,12 @@ hipError_t launch_select(const Plan& pl, const int32_t* cu_k, const int32_t* cu_
 hipError_t launch_attend(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
                          const int32_t* cu_k, const int32_t* sel, const int32_t* cnt,
                          const Workspace& w, float* out, float* lse, hipStream_t stream);
+// off: offloaded KV (kv then holds the host pools' device view, kc_pool and
+// the block table).
 hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
                          const int32_t* cu_k, const Workspace& w, float* out, float* lse,
                          int32_t* sel_out, int32_t* cnt_out, float* scores_out,
-                         hipStream_t stream);
+                         hipStream_t stream, const Offload* off = nullptr);
 
 hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
                             const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,

@@ -25,6 +25,7 @@
 // Shared device helpers (MFMA operand layout, one-page attention, the
 // selector) are in nosa_device.h.
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -256,13 +257,21 @@ __device__ void attend_page_split4(const uint16_t* __restrict__ kb, const uint16
     }
 }
 
+// Page of window block b of sequence s: block-table entry, or with a ring of
+// `ring` recent pages per sequence (offloaded KV), ring slot b % ring.
+__device__ __forceinline__ int window_page(const int32_t* table, int max_blocks, int ring, int s,
+                                           int b)
+{
+    return ring > 0 ? s * ring + b % ring : table[(size_t)s * max_blocks + b];
+}
+
 // Window slot x of pair (s, g): block nb - wn + x, wn = min(nb, wblocks),
 // attended by the four waves together, its partial at slot split0 + x (an
 // empty partial past wn).  All 256 threads.
 __device__ void store_empty_partial(int G, size_t head_row0, int nsplit, int split,
                                     float* __restrict__ po, float2* __restrict__ pml);
 __device__ void window_slot(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
-                            const int32_t* table, const int32_t* cu_k, int max_blocks, int Lmax,
+                            const int32_t* table, int ring, const int32_t* cu_k, int max_blocks, int Lmax,
                             int Hq, int Hkv, int G, float scale_log2, int wblocks, int s, int g,
                             int x, int nsplit, int split0, float* po, float2* pml,
                             SplitPageLds& sh)
@@ -276,7 +285,7 @@ __device__ void window_slot(const uint16_t* q, const uint16_t* k_pool, const uin
         bf16x8 qb[4];
         load_q(q, Hq, s, g * G, G, r, kq, qb);
         const int b = nb - wn + x;
-        const int page = table[(size_t)s * max_blocks + b];
+        const int page = window_page(table, max_blocks, ring, s, b);
         attend_page_split4(k_pool + ((size_t)page * Hkv + g) * BS * D,
                            v_pool + ((size_t)page * Hkv + g) * D * BS, L - b * BS, qb, scale_log2, G,
                            head_row0, nsplit, split0 + x, po, pml, sh);
@@ -325,10 +334,11 @@ __device__ void store_empty_partial(int G, size_t head_row0, int nsplit, int spl
 
 struct ScoreArgs {
     const uint16_t* q;
-    const uint16_t* k_pool;
-    const uint16_t* v_pool;
+    const uint16_t* k_pool;  // window pages and the tokens of the appended key
+    const uint16_t* v_pool;  // (the recent-page ring when ring > 0)
     uint16_t* kc_pool;
     const int32_t* table;
+    int ring;                // recent pages per sequence (offloaded KV), else 0
     const int32_t* cu_k;
     int max_blocks, num_pages, Lmax, Hq, Hkv, G, gp;
     float scale_log2;
@@ -368,9 +378,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
     if ((int)blockIdx.x >= a.nscore) {  // window workgroup: one page
         const int w = (int)blockIdx.x - a.nscore;
         const int pair = w / a.wslots;
-        window_slot(a.q, a.k_pool, a.v_pool, a.table, a.cu_k, a.max_blocks, a.Lmax, a.Hq, a.Hkv,
-                    a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv, w % a.wslots, a.nsplit,
-                    a.split0, a.po, a.pml, *reinterpret_cast<SplitPageLds*>(smem));
+        window_slot(a.q, a.k_pool, a.v_pool, a.table, a.ring, a.cu_k, a.max_blocks, a.Lmax, a.Hq,
+                    a.Hkv, a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv, w % a.wslots,
+                    a.nsplit, a.split0, a.po, a.pml, *reinterpret_cast<SplitPageLds*>(smem));
         return;
     }
     const int pair = blockIdx.x / a.nchunks, c = blockIdx.x % a.nchunks;
@@ -408,7 +418,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
         // tokens 16 jn + tr + 4i, i < 8
         int kpg[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kpg[i] = trow[(jn * kPoolS + tr + 4 * i) / BS];
+        for (int i = 0; i < 8; ++i)
+            kpg[i] = window_page(a.table, a.max_blocks, a.ring, s, (jn * kPoolS + tr + 4 * i) / BS);
         uint4 kt[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -534,11 +545,29 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
 // page "NOSA-1B 性能基准全解析" section 三.3).
 
 constexpr int kMaxRounds = 8;  // top-k blocks per wave (compiled limit of the plan)
+constexpr int kMaxCacheSlots = 256;  // block-cache slots per pair (offloaded KV): one per thread
+constexpr int kFetch = 1 << 30;      // slot_of flag: the pick is read from host memory
 
 struct TopArgs {
     const uint16_t* q;
-    const uint16_t* k_pool;
+    const uint16_t* k_pool;  // top-k pages (host pools when offloaded)
     const uint16_t* v_pool;
+    const uint16_t* wk;      // window pages: the pools, or the recent-page ring
+    const uint16_t* wv;
+    int ring;                // recent pages per sequence (offloaded KV), else 0
+    int num_pages;
+    // offloaded KV: the block cache of each pair, `cap` pages; map[pair][slot]
+    // = block held, used[pair][slot] = sequence length when it was last
+    // picked (read); map_next / used_next = both after this step (written by
+    // workgroup 0 of the pair, installed by the merge launch)
+    uint16_t* cache_k;
+    uint16_t* cache_v;
+    const int32_t* map;
+    const int32_t* used;
+    int32_t* map_next;
+    int32_t* used_next;
+    int32_t* fetch_out;      // [pairs] picks read from host memory, or null
+    int cap;
     const int32_t* table;
     const int32_t* cu_k;
     int max_blocks, Lmax, Hq, Hkv, G, gp;
@@ -570,10 +599,20 @@ struct alignas(16) TopLds {
             SelectLds sel;
         };
         SplitPageLds page;  // window workgroups
+        struct {            // offloaded KV, after the selection
+            int4 age[kMaxCacheSlots / 4];  // eviction order key per slot (free slots)
+            int freeslot[kMaxCacheSlots];  // free slots, least recently picked first
+            int misspick[kMaxCacheSlots];  // picks not in the cache in pick order
+        } miss;
     };
     CombineLds comb;
-    int2 list[kStep2Waves * kMaxRounds];
+    // (block, page) of this workgroup's picks (the pair's every pick when the
+    // KV is offloaded)
+    int2 list[kMaxCacheSlots];
+    int slot_of[kMaxCacheSlots];  // offloaded KV: cache slot per pick (| kFetch)
+    int ocnt[2][kStep2Waves];
 };
+static_assert(kMaxCacheSlots >= kStep2Waves * kMaxRounds, "list of a top workgroup");
 
 // Dynamic LDS of a top workgroup: the block-table row, and the importance
 // of blocks past the register rounds.
@@ -620,7 +659,15 @@ __device__ __forceinline__ float block_importance(int b, int nc, int cb_shift, i
 // KRB: candidate rounds of 256 blocks whose importance stays in registers
 // (1, 2, 4 or 8; blocks past KRB * 256 go through LDS, only when KRB = 8).
 // GP4: float4 loads per block of the partial row (G <= 4 GP4).
-template <int KRB, int GP4>
+// OFF: offloaded KV.  The window pages come from the ring of recent pages in
+// device memory; the top-k picks from the pair's block cache.  Every top
+// workgroup of the pair derives the same slot assignment from the cache map
+// and the selection: picks already cached keep their slot; the others take
+// the free slots (those whose block was not picked), least recently picked
+// first, and are read from host memory, attended and written into their slot
+// in one pass.
+// Cached blocks lie before the window, so they are complete and never change.
+template <int KRB, int GP4, bool OFF>
 __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
 {
     constexpr int NT = kStep2Waves * 64;
@@ -638,7 +685,7 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     if (lid >= (window ? a.nwin : a.ntop)) return;  // whole workgroup
     if (window && a.wgroups == a.wslots) {  // one window page, the four waves together
         const int pair = lid / a.wgroups;
-        window_slot(a.q, a.k_pool, a.v_pool, a.table, a.cu_k, a.max_blocks, a.Lmax, a.Hq, a.Hkv,
+        window_slot(a.q, a.wk, a.wv, a.table, a.ring, a.cu_k, a.max_blocks, a.Lmax, a.Hq, a.Hkv,
                     a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv, lid % a.wgroups,
                     a.nsplit, a.groups, a.po, a.pml, sh.page);
         return;
@@ -656,14 +703,15 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     const size_t head_row0 = (size_t)s * a.Hq + g * a.G;
 
     bf16x8 qb[4];
-    int rounds = 1;
+    int rounds = 1, lbase = 0;
     if (window) {
         // this wave's window page as a one-entry list; the attention below
         // is the top workgroups' own
         const int wn = nb < a.wblocks ? nb : a.wblocks;
         const int x = 4 * k + wave;
         int2 e = make_int2(-1, -1);
-        if (x < wn) e = make_int2(nb - wn + x, trow[nb - wn + x]);
+        if (x < wn)
+            e = make_int2(nb - wn + x, window_page(a.table, a.max_blocks, a.ring, s, nb - wn + x));
         if (lane == 0) sh.list[wave] = e;
         load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
         __syncthreads();
@@ -701,6 +749,14 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
 #pragma unroll
     for (int i = 0; i < KRB; ++i) tv[i] = trow[i * NT + tid < a.max_nb ? i * NT + tid : a.max_nb - 1];
     load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
+    int cb = -1, cu = 0;  // offloaded KV: block in cache slot tid, length at its last pick
+    if (OFF) {
+        if (tid < a.cap) {
+            cb = a.map[(size_t)pair * a.cap + tid];
+            cu = a.used[(size_t)pair * a.cap + tid];
+        }
+        sh.slot_of[tid] = -1;
+    }
     select_lds_clear<NT>(sh.sel);
     // per-head log2-sum-exp2 over the chunks, then each chunk's weight
 #pragma unroll
@@ -763,19 +819,103 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     select_blocks_wg<kStep2Waves, true>(keys, sI, nb, a.wblocks, a.topk, sh.sel,
                                         a.sel_out && k == 0 ? a.sel_out + (size_t)pair * a.max_sel : nullptr,
                                         a.cnt_out && k == 0 ? a.cnt_out + pair : nullptr, a.max_sel,
-                                        sh.list, lo, a.rounds * kStep2Waves, spg, in_regs);
+                                        sh.list, OFF ? 0 : lo, OFF ? kMaxCacheSlots : a.rounds * kStep2Waves,
+                                        spg, in_regs);
     __syncthreads();  // the list
     rounds = a.rounds;
+    if (OFF) {
+        // picks 0 .. npk - 1 in sh.list, ascending block ids
+        lbase = lo;
+        const int npk = a.topk < ncand ? a.topk : ncand;
+        bool hit = false;
+        if (cb >= 0 && cb < ncand) {  // is slot tid's block a pick?  binary search
+            int x0 = 0, x1 = npk;
+            while (x0 < x1) {
+                const int mid = (x0 + x1) >> 1;
+                if (sh.list[mid].x < cb) x0 = mid + 1;
+                else x1 = mid;
+            }
+            if (x0 < npk && sh.list[x0].x == cb) {
+                sh.slot_of[x0] = tid;
+                hit = true;
+            }
+        }
+        __syncthreads();
+        const bool fre = tid < a.cap && !hit;
+        const bool mis = tid < npk && sh.slot_of[tid] < 0;
+        // eviction order of the free slots: empty ones, then by the length
+        // at the last pick, then by slot
+        const int age = fre ? (cb < 0 ? INT_MIN : cu) : INT_MAX;
+        reinterpret_cast<int*>(sh.miss.age)[tid] = age;
+        const uint64_t bm = __ballot(mis);
+        if (lane == 0) sh.ocnt[1][wave] = (int)__popcll(bm);
+        __syncthreads();
+        int rm = lanes_below(bm), nmiss = 0;
+#pragma unroll
+        for (int w = 0; w < kStep2Waves; ++w) {
+            if (w < wave) rm += sh.ocnt[1][w];
+            nmiss += sh.ocnt[1][w];
+        }
+        int rf = 0;  // rank of a free slot in eviction order
+        if (nmiss > 0 && fre) {
+            for (int u4 = 0; u4 < kMaxCacheSlots / 4; ++u4) {
+                const int4 v = sh.miss.age[u4];
+                const int u = 4 * u4;
+                rf += (v.x < age || (v.x == age && u < tid)) + (v.y < age || (v.y == age && u + 1 < tid)) +
+                      (v.z < age || (v.z == age && u + 2 < tid)) + (v.w < age || (v.w == age && u + 3 < tid));
+            }
+        }
+        if (fre && rf < nmiss) sh.miss.freeslot[rf] = tid;
+        if (mis) sh.miss.misspick[rm] = tid;
+        __syncthreads();
+        // cap >= topk, so there are at least as many free slots as misses
+        if (mis) sh.slot_of[tid] = sh.miss.freeslot[rm] | kFetch;
+        if (k == 0) {
+            if (tid < a.cap) {
+                const bool fill = fre && rf < nmiss;
+                a.map_next[(size_t)pair * a.cap + tid] = fill ? sh.list[sh.miss.misspick[rf]].x : cb;
+                a.used_next[(size_t)pair * a.cap + tid] = hit || fill ? L : cu;
+            }
+            if (tid == 0 && a.fetch_out) a.fetch_out[pair] = nmiss;
+        }
+        __syncthreads();  // slot_of
+    }
     }
     AttnState A;
     attn_init(A);
 #pragma unroll 1
     for (int rr = 0; rr < rounds; ++rr) {
-        const int2 e = sh.list[rr * kStep2Waves + wave];
+        const int p = lbase + rr * kStep2Waves + wave;
+        const int2 e = p < kMaxCacheSlots ? sh.list[p] : make_int2(-1, -1);
         if (e.x < 0) continue;
-        attend_page(a.k_pool + ((size_t)e.y * a.Hkv + g) * BS * D,
-                    a.v_pool + ((size_t)e.y * a.Hkv + g) * D * BS, L - e.x * BS, qb, a.scale_log2,
-                    r, kq, A);
+        const uint16_t* kb;
+        const uint16_t* vb;
+        if (window) {
+            kb = a.wk + ((size_t)e.y * a.Hkv + g) * BS * D;
+            vb = a.wv + ((size_t)e.y * a.Hkv + g) * D * BS;
+        } else if (OFF) {
+            const int so = sh.slot_of[p];
+            const size_t unit = (size_t)pair * a.cap + (so & (kFetch - 1));
+            uint16_t* ck = a.cache_k + unit * BS * D;
+            uint16_t* cv = a.cache_v + unit * BS * D;
+            if (so & kFetch) {  // from host memory, kept in the cache slot
+                const int pg = min(max(e.y, 0), a.num_pages - 1);
+                const int lane8 = (16 * kq + r) * 8;
+                PageRegs pr;
+                load_page(a.k_pool + ((size_t)pg * a.Hkv + g) * BS * D,
+                          a.v_pool + ((size_t)pg * a.Hkv + g) * D * BS, lane8, pr);
+                __builtin_amdgcn_sched_barrier(0);
+                store_page(ck, cv, lane8, pr);
+                attend_loaded(pr, L - e.x * BS, qb, a.scale_log2, r, kq, A);
+                continue;
+            }
+            kb = ck;
+            vb = cv;
+        } else {
+            kb = a.k_pool + ((size_t)e.y * a.Hkv + g) * BS * D;
+            vb = a.v_pool + ((size_t)e.y * a.Hkv + g) * D * BS;
+        }
+        attend_page(kb, vb, L - e.x * BS, qb, a.scale_log2, r, kq, A);
     }
     store_wg_partial(sh.comb, A, a.G, head_row0, a.nsplit, window ? a.groups + k : k, a.po, a.pml);
 }
@@ -805,14 +945,29 @@ struct AttendArgs {
 // taken 32 at a time with every load of a batch in flight, the running
 // (M, L, acc) rescaled between batches.  A launch of its own, so the
 // partials of every workgroup of the step are complete when it starts.
+// With offloaded KV the row of each group's first head also installs the
+// pair's new cache map and pick lengths (map_next -> map, used_next -> used,
+// `cap` entries each): every workgroup of the attention launch has read the
+// old ones by now.
 constexpr int kMergeBatch = 32;
 
 __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ po,
                                                     const float2* __restrict__ pml, int nsplit,
-                                                    float* __restrict__ out, float* __restrict__ lse)
+                                                    float* __restrict__ out, float* __restrict__ lse,
+                                                    const int32_t* __restrict__ map_next,
+                                                    const int32_t* __restrict__ used_next,
+                                                    int32_t* __restrict__ map,
+                                                    int32_t* __restrict__ used, int cap, int G)
 {
     const size_t row = blockIdx.x;
     const int c = threadIdx.x;
+    if (map && row % G == 0) {
+        const size_t pair = row / G;
+        for (int x = c; x < cap; x += D) {
+            map[pair * cap + x] = map_next[pair * cap + x];
+            used[pair * cap + x] = used_next[pair * cap + x];
+        }
+    }
     const float2* ml = pml + row * nsplit;
     const float* op = po + row * nsplit * D + c;
     float M = -INFINITY, L = 0.f, acc = 0.f;
@@ -847,12 +1002,14 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ po
 }
 
 static hipError_t launch_merge(const Plan& pl, const Workspace& w, int nsplit, float* out, float* lse,
-                               hipStream_t stream)
+                               hipStream_t stream, const Offload* off = nullptr)
 {
     const int rows = pl.B * pl.Hq;
     if (rows > 0)
         hipLaunchKernelGGL(merge_kernel, dim3(rows), dim3(D), 0, stream, w.po, w.pml, nsplit, out,
-                           lse);
+                           lse, off ? off->map_next : nullptr, off ? off->used_next : nullptr,
+                           off ? off->cache_map : nullptr, off ? off->cache_used : nullptr,
+                           off ? off->cap : 0, pl.G);
     return hipGetLastError();
 }
 
@@ -968,12 +1125,13 @@ static int device_cus()
 // top_groups ..).
 static hipError_t launch_score(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
                                const int32_t* cu_k, const Workspace& w, int append,
-                               bool with_window, hipStream_t stream)
+                               bool with_window, hipStream_t stream, const Offload* off = nullptr)
 {
     ScoreArgs a{};
     a.q = q;
-    a.k_pool = kv.k_pool;
-    a.v_pool = kv.v_pool;
+    a.k_pool = off ? off->k_recent : kv.k_pool;
+    a.v_pool = off ? off->v_recent : kv.v_pool;
+    a.ring = off ? off->recent : 0;
     a.kc_pool = kv.kc_pool;
     a.table = kv.block_table;
     a.cu_k = cu_k;
@@ -1016,6 +1174,9 @@ static TopArgs top_args(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16
     a.q = q;
     a.k_pool = kv.k_pool;
     a.v_pool = kv.v_pool;
+    a.wk = kv.k_pool;
+    a.wv = kv.v_pool;
+    a.num_pages = kv.num_pages;
     a.table = kv.block_table;
     a.cu_k = cu_k;
     a.max_blocks = kv.max_blocks_per_seq;
@@ -1041,22 +1202,26 @@ static TopArgs top_args(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16
     return a;
 }
 
-template <int KRB, int GP4>
+template <int KRB, int GP4, bool OFF>
 static void launch_top_t(dim3 grid, size_t lds, const TopArgs& a, hipStream_t stream)
 {
     if (lds > 64 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&top_kernel<KRB, GP4>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&top_kernel<KRB, GP4, OFF>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL((top_kernel<KRB, GP4>), grid, dim3(kStep2Waves * 64), lds, stream, a);
+    hipLaunchKernelGGL((top_kernel<KRB, GP4, OFF>), grid, dim3(kStep2Waves * 64), lds, stream, a);
 }
 
 template <int KRB>
 static void launch_top_k(dim3 grid, size_t lds, int gp4, const TopArgs& a, hipStream_t stream)
 {
+    const bool off = a.cap > 0;
     switch (gp4) {
-        case 1: launch_top_t<KRB, 1>(grid, lds, a, stream); break;
-        case 2: launch_top_t<KRB, 2>(grid, lds, a, stream); break;
-        default: launch_top_t<KRB, 4>(grid, lds, a, stream); break;
+        case 1: off ? launch_top_t<KRB, 1, true>(grid, lds, a, stream)
+                    : launch_top_t<KRB, 1, false>(grid, lds, a, stream); break;
+        case 2: off ? launch_top_t<KRB, 2, true>(grid, lds, a, stream)
+                    : launch_top_t<KRB, 2, false>(grid, lds, a, stream); break;
+        default: off ? launch_top_t<KRB, 4, true>(grid, lds, a, stream)
+                     : launch_top_t<KRB, 4, false>(grid, lds, a, stream); break;
     }
 }
 
@@ -1099,7 +1264,7 @@ hipError_t launch_scores_only(const Plan& pl, const nosa_paged_kv& kv, const nos
 hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
                          const int32_t* cu_k, const Workspace& w, float* out, float* lse,
                          int32_t* sel_out, int32_t* cnt_out, float* scores_out,
-                         hipStream_t stream)
+                         hipStream_t stream, const Offload* off)
 {
     // The window pages (known before any selection) go beside the selection
     // when the attention launch then fits on the chip at once (two
@@ -1114,9 +1279,24 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
         wg_top = per_wave;
     // partials per head: the top workgroups', then one per window workgroup
     const int nsplit = pl.top_groups + (wg_top > 0 ? wg_top : pl.wslots);
-    hipError_t e = launch_score(pl, kv, q, cu_k, w, 1, wg_top == 0, stream);
+    hipError_t e = launch_score(pl, kv, q, cu_k, w, 1, wg_top == 0, stream, off);
     if (e != hipSuccess) return e;
     TopArgs a = top_args(pl, kv, q, cu_k, w);
+    if (off) {
+        a.k_pool = off->k_host;
+        a.v_pool = off->v_host;
+        a.wk = off->k_recent;
+        a.wv = off->v_recent;
+        a.ring = off->recent;
+        a.cache_k = off->cache_k;
+        a.cache_v = off->cache_v;
+        a.map = off->cache_map;
+        a.used = off->cache_used;
+        a.map_next = off->map_next;
+        a.used_next = off->used_next;
+        a.fetch_out = off->fetch_out;
+        a.cap = off->cap;
+    }
     a.groups = pl.top_groups;
     a.rounds = pl.top_rounds;
     a.wslots = wg_top > 0 ? pl.wslots : 0;
@@ -1127,7 +1307,7 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
     a.cnt_out = cnt_out;
     e = launch_top(pl, a, stream);
     if (e != hipSuccess) return e;
-    return launch_merge(pl, w, nsplit, out, lse, stream);
+    return launch_merge(pl, w, nsplit, out, lse, stream, off);
 }
 
 hipError_t launch_attend(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,

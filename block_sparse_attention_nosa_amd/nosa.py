@@ -43,6 +43,16 @@ class nosa_paged_kv(ctypes.Structure):
                 ("max_blocks_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
 
 
+class nosa_offload_kv(ctypes.Structure):
+    _fields_ = [("k_host", ctypes.c_void_p), ("v_host", ctypes.c_void_p),
+                ("kc_pool", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("max_blocks_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("k_recent", ctypes.c_void_p), ("v_recent", ctypes.c_void_p),
+                ("recent_blocks", ctypes.c_int32), ("cache_blocks", ctypes.c_int32),
+                ("cache_k", ctypes.c_void_p), ("cache_v", ctypes.c_void_p),
+                ("cache_map", ctypes.c_void_p), ("cache_used", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -69,6 +79,9 @@ def lib() -> ctypes.CDLL:
             "nosa_decode_step": [P, KV, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
             "nosa_prefill_sparse_workspace_size": [P, i32, i32, i32, ctypes.POINTER(sz)],
             "nosa_prefill_sparse": [P, KV, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp],
+            "nosa_offload_workspace_size": [P, i32, i32, i32, ctypes.POINTER(sz)],
+            "nosa_offload_decode_step": [P, ctypes.POINTER(nosa_offload_kv), vp, vp, i32, i32, vp,
+                                         vp, vp, vp, vp, vp, sz, vp],
         }
         for name, argtypes in sigs.items():
             f = getattr(L, name)
@@ -193,5 +206,39 @@ def nosa_prefill_sparse(p, kv, q, cu_seqlens, batch, max_seqlen, chunk, out, lse
     _check("nosa_prefill_sparse", lib().nosa_prefill_sparse(
         ctypes.byref(p), ctypes.byref(kv), _ptr(q), _ptr(cu_seqlens), batch, max_seqlen, chunk,
         _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))
+
+
+def offload_kv(k_host, v_host, kc_pool, block_table, k_recent, v_recent, cache_k, cache_v,
+               cache_map, cache_used, max_blocks_per_seq=None, num_pages=None) -> nosa_offload_kv:
+    """Struct over an offloaded KV cache (the tensors must outlive every call
+    using it).  k_host / v_host: pinned CPU tensors [pages][Hkv][64 * 128];
+    k_recent / v_recent: [batch][recent][Hkv][64 * 128]; cache_k / cache_v:
+    [batch][Hkv][slots][64 * 128]; cache_map, cache_used: int32
+    [batch][Hkv][slots]."""
+    if max_blocks_per_seq is None:
+        max_blocks_per_seq = block_table.shape[1]
+    if num_pages is None:
+        num_pages = k_host.shape[0]
+    return nosa_offload_kv(_ptr(k_host), _ptr(v_host), _ptr(kc_pool), _ptr(block_table),
+                           int(max_blocks_per_seq), int(num_pages), _ptr(k_recent),
+                           _ptr(v_recent), int(k_recent.shape[1]), int(cache_map.shape[-1]),
+                           _ptr(cache_k), _ptr(cache_v), _ptr(cache_map), _ptr(cache_used))
+
+
+def nosa_offload_workspace_size(p: nosa_params, batch: int, max_seqlen_k: int,
+                                cache_blocks: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("nosa_offload_workspace_size", lib().nosa_offload_workspace_size(
+        ctypes.byref(p), batch, max_seqlen_k, cache_blocks, ctypes.byref(out)))
+    return int(out.value)
+
+
+def nosa_offload_decode_step(p, okv, q, cu_seqlens_k, batch, max_seqlen_k, out, lse, workspace,
+                             sel_idx=None, sel_count=None, fetch_count=None, stream=None):
+    _check("nosa_offload_decode_step", lib().nosa_offload_decode_step(
+        ctypes.byref(p), ctypes.byref(okv), _ptr(q), _ptr(cu_seqlens_k), batch, max_seqlen_k,
+        _ptr(out), _ptr(lse), _ptr(sel_idx), _ptr(sel_count), _ptr(fetch_count), _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream)))

@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define NOSA_ABI_VERSION 2
+#define NOSA_ABI_VERSION 3
 
 typedef uint16_t nosa_bf16; /* bf16 bit pattern */
 
@@ -141,6 +141,58 @@ typedef struct nosa_paged_kv {
     int32_t max_blocks_per_seq;
     int32_t num_pages;
 } nosa_paged_kv;
+
+/* Offloaded KV cache [page "NOSA-1B 性能基准全解析", section 三.1: most of the
+ * KV cache lives outside GPU memory, which holds only what is in use; page
+ * "NOSA技术架构解析", section 2.2: the host side is read directly, without
+ * staging copies, and only blocks that changed are transferred].  K and V
+ * pages of every block are in host memory; device memory holds the pooled
+ * keys of every block, the pages of the recent blocks, and a cache of the
+ * blocks picked by recent steps.
+ *   k_host, v_host  pinned host memory (hipHostMalloc, or a pinned torch
+ *                   tensor), [num_pages][Hkv][block_size * d] in the page
+ *                   layout above; page block_table[s][b] holds block b of
+ *                   sequence s.  Read by the GPU directly.
+ *   kc_pool, block_table, max_blocks_per_seq, num_pages: as in nosa_paged_kv
+ *                   (device).
+ *   k_recent, v_recent  device [batch][recent_blocks][Hkv][block_size * d]:
+ *                   block b of sequence s in slot b % recent_blocks.  Must
+ *                   hold the last max(2, W) blocks of each sequence, W =
+ *                   window / block_size + the locality share (the forced
+ *                   blocks, and the tokens of the key the step appends), the
+ *                   current token included; recent_blocks >= max(2, W).
+ *   cache_k, cache_v  device [batch][Hkv][cache_blocks][block_size * d]: the
+ *                   block cache of each (sequence, KV head), written by the
+ *                   library.
+ *   cache_map       device int32 [batch][Hkv][cache_blocks]: the block held
+ *                   by each cache slot, -1 for none.  The caller sets every
+ *                   entry to -1 before a sequence's first step (and whenever
+ *                   the sequence in that batch row changes); the library keeps
+ *                   it up to date afterwards.  cache_blocks must be at least
+ *                   the query-aware share of topk (topk minus the locality
+ *                   share) and at most 256.
+ *   cache_used      device int32 [batch][Hkv][cache_blocks]: the sequence
+ *                   length at the step that last picked each slot's block
+ *                   (written by the library; no initial contents needed).
+ *                   A miss takes the free slot (block not picked) that was
+ *                   picked least recently, empty slots first.
+ * Blocks before the recent ones must not change while they may be cached. */
+typedef struct nosa_offload_kv {
+    const nosa_bf16* k_host;
+    const nosa_bf16* v_host;
+    nosa_bf16* kc_pool;
+    const int32_t* block_table;
+    int32_t max_blocks_per_seq;
+    int32_t num_pages;
+    const nosa_bf16* k_recent;
+    const nosa_bf16* v_recent;
+    int32_t recent_blocks;
+    int32_t cache_blocks;
+    nosa_bf16* cache_k;
+    nosa_bf16* cache_v;
+    int32_t* cache_map;
+    int32_t* cache_used;
+} nosa_offload_kv;
 
 /* ABI version of the loaded library (NOSA_ABI_VERSION at its build). */
 int nosa_abi_version(void);
@@ -267,6 +319,32 @@ nosa_status nosa_prefill_sparse(const nosa_params* params, const nosa_paged_kv* 
                                 const nosa_bf16* q, const int32_t* cu_seqlens, int32_t batch,
                                 int32_t max_seqlen, int32_t chunk, float* out, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by nosa_offload_decode_step for at most `batch`
+ * sequences of at most max_seqlen_k tokens and `cache_blocks` cache slots
+ * per (sequence, KV head).  Host only.  Errors as nosa_workspace_size, plus
+ * NOSA_ERR_INVALID / NOSA_ERR_UNSUPPORTED for a cache size outside
+ * [topk - locality share, 256]. */
+nosa_status nosa_offload_workspace_size(const nosa_params* params, int32_t batch,
+                                        int32_t max_seqlen_k, int32_t cache_blocks, size_t* bytes);
+
+/* One decode step over an offloaded KV cache (see nosa_offload_kv): the same
+ * computation and results as nosa_decode_step over pools holding the same
+ * pages, bit for bit.  The window (and locality) pages are read from the
+ * recent ring, the top-k picks from the block cache; picks not in the cache
+ * are read from host memory by the attention itself and written into cache
+ * slots whose blocks were not picked, so a step transfers only the blocks its
+ * selection adds.  fetch_count (optional, device int32 [batch][Hkv]) receives
+ * the number of blocks read from host memory per (sequence, KV head).  Other
+ * arguments and outputs as nosa_decode_step.  Errors: those of
+ * nosa_decode_step; NOSA_ERR_INVALID when a host pool is not pinned memory the
+ * device can read, or the ring or cache is too small; NOSA_ERR_UNSUPPORTED for
+ * a window of no block or a cache of more than 256 slots. */
+nosa_status nosa_offload_decode_step(const nosa_params* params, const nosa_offload_kv* kv,
+                                     const nosa_bf16* q, const int32_t* cu_seqlens_k,
+                                     int32_t batch, int32_t max_seqlen_k, float* out, float* lse,
+                                     int32_t* sel_idx, int32_t* sel_count, int32_t* fetch_count,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,13 +24,14 @@ def test_exports_every_declared_function(L):
     assert set(names) >= {"nosa_abi_version", "nosa_status_string", "nosa_workspace_size",
                           "nosa_compress_keys", "nosa_block_scores", "nosa_select_blocks",
                           "nosa_sparse_attend", "nosa_decode_step", "nosa_prefill_sparse",
-                          "nosa_prefill_sparse_workspace_size"}
+                          "nosa_prefill_sparse_workspace_size", "nosa_offload_decode_step",
+                          "nosa_offload_workspace_size"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert nosa.abi_version() == 2
+    assert nosa.abi_version() == 3
     for s in range(6):
         assert nosa.status_string(s)
     assert nosa.status_string(0) == "ok"
@@ -180,3 +181,38 @@ def test_prompt_prefill_host_errors(L):
     assert call(Lm=16385) == 2                     # the table cannot reach it
     assert call(wsb=100) == 4
     assert call(B=0) == 0
+
+
+def test_offload_host_errors(L):
+    p = nosa.params(topk=64)
+    size = lambda cap, **kw: nosa.nosa_offload_workspace_size(kw.get("p", p), 8, 16640, cap)
+    assert size(64) > nosa.nosa_workspace_size(p, 8, 1, 16640)
+    assert size(128) > size(64)
+    for cap, status in ((63, 2), (0, 2), (257, 3)):
+        with pytest.raises(nosa.NosaError) as e:
+            size(cap)
+        assert e.value.status == status
+    with pytest.raises(nosa.NosaError) as e:      # a window of no block
+        size(64, p=nosa.params(topk=64, window=0))
+    assert e.value.status == 3
+    loc = nosa.params(topk=64, locality=0.5)      # the local half needs no cache slot
+    assert nosa.nosa_offload_workspace_size(loc, 8, 16640, 32) > 0
+    okv = nosa.nosa_offload_kv(FAKE, FAKE, FAKE, FAKE, 512, 16, FAKE, FAKE, 16, 64, FAKE, FAKE,
+                               FAKE, FAKE)
+    call = lambda o, **kw: L.nosa_offload_decode_step(
+        ctypes.byref(kw.get("p", p)), ctypes.byref(o) if o is not None else None, FAKE, FAKE,
+        kw.get("B", 8), 16640, FAKE, None, None, None, None, FAKE, kw.get("wsb", 0), None)
+    assert call(None) == 1
+    for f in ("k_host", "v_host", "kc_pool", "block_table", "k_recent", "v_recent", "cache_k",
+              "cache_v", "cache_map", "cache_used"):
+        bad = nosa.nosa_offload_kv(*[getattr(okv, n) for n, _ in okv._fields_])
+        setattr(bad, f, None)
+        assert call(bad) == 1, f
+    small = nosa.nosa_offload_kv(*[getattr(okv, n) for n, _ in okv._fields_])
+    small.recent_blocks = 15                      # the 16 window blocks do not fit
+    assert call(small) == 2
+    small.recent_blocks = 16
+    small.cache_blocks = 60                       # fewer slots than picks
+    assert call(small) == 2
+    assert call(okv, wsb=100) == 4
+    assert call(okv, B=0) == 0

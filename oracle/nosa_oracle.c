@@ -415,6 +415,58 @@ int nosa_ref_forward(const nosa_ref_params* p, const uint16_t* q, const int32_t*
     return 0;
 }
 
+/* ------------------------------------------ 0. projections and rotary ---- */
+
+/* The attention front end of one decode token per sequence (page "NOSA技术架构
+ * 解析", section 2.1: the QKV projection, the rotary position encoding and the
+ * importance scoring make up one step of the decode path).  Token b has the
+ * hidden state x[b][0 .. hidden) and position pos[b].  The projection is
+ * y[o] = sum_c w[o][c] x[b][c] over the rows o of w: Hq heads of q, then Hkv
+ * heads of k, then Hkv heads of v, head_dim rows each.  Within each q and k
+ * head, channel i and channel i + head_dim/2 (i < head_dim/2) are rotated as
+ * one pair by the angle pos[b] * inv_freq[i]: with c = cos, s = sin,
+ *   (y[i], y[i + d/2]) -> (y[i] c - y[i + d/2] s, y[i + d/2] c + y[i] s);
+ * v is not rotated.  Every result is rounded once to bf16.  inv_freq NULL
+ * means theta^(-2i/d).  Layouts: x [B][hidden], w [(Hq + 2 Hkv) d][hidden]
+ * (bf16 bits), q [B][Hq][d], k and v [B][Hkv][d] (bf16 bits). */
+int nosa_ref_qkv_rope(const nosa_ref_params* p, int hidden, double theta, const double* inv_freq,
+                      const uint16_t* x, const uint16_t* w, const int32_t* pos, int B,
+                      uint16_t* q, uint16_t* k, uint16_t* v)
+{
+    if (nosa_ref_check_params(p)) return -1;
+    const int Hq = p->num_q_heads, Hkv = p->num_kv_heads, d = p->head_dim, half = d / 2;
+    if (hidden <= 0 || B < 0 || d % 2) return -2;
+    if (!inv_freq && !(theta > 0.0)) return -3;
+    const int heads = Hq + 2 * Hkv;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < heads; ++h) {
+            double y[1024];
+            if (d > 1024) return -4;
+            for (int o = 0; o < d; ++o) {
+                double acc = 0.0;
+                const uint16_t* wr = w + ((size_t)h * d + o) * hidden;
+                for (int c = 0; c < hidden; ++c)
+                    acc += bf16_value(wr[c]) * bf16_value(x[(size_t)b * hidden + c]);
+                y[o] = acc;
+            }
+            if (h < Hq + Hkv) {  /* q and k heads: the rotary encoding */
+                for (int i = 0; i < half; ++i) {
+                    const double f = inv_freq ? inv_freq[i] : pow(theta, -2.0 * i / d);
+                    const double a = (double)pos[b] * f;
+                    const double cs = cos(a), sn = sin(a);
+                    const double lo = y[i], hi = y[i + half];
+                    y[i] = lo * cs - hi * sn;
+                    y[i + half] = hi * cs + lo * sn;
+                }
+            }
+            uint16_t* dst = h < Hq ? q + ((size_t)b * Hq + h) * d
+                          : h < Hq + Hkv ? k + ((size_t)b * Hkv + (h - Hq)) * d
+                                         : v + ((size_t)b * Hkv + (h - Hq - Hkv)) * d;
+            for (int o = 0; o < d; ++o) dst[o] = nosa_ref_bf16_round(y[o]);
+        }
+    return 0;
+}
+
 int nosa_ref_num_threads(void)
 {
 #ifdef _OPENMP

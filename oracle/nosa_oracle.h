@@ -45,6 +45,9 @@ int nosa_ref_sparse_attend(const nosa_ref_params* p, const uint16_t* q, const in
                            const uint16_t* k, const uint16_t* v, const int32_t* cu_k, int B,
                            const int32_t* sel, const int32_t* count, int max_qblk, int max_sel,
                            double* out, double* lse);
+int nosa_ref_qkv_rope(const nosa_ref_params* p, int hidden, double theta, const double* inv_freq,
+                      const uint16_t* x, const uint16_t* w, const int32_t* pos, int B,
+                      uint16_t* q, uint16_t* k, uint16_t* v);
 int nosa_ref_forward(const nosa_ref_params* p, const uint16_t* q, const int32_t* cu_q,
                      const uint16_t* k, const uint16_t* v, const int32_t* cu_k, int B,
                      int max_nc, int max_qblk, int max_nb, int max_sel, uint16_t* kc,

@@ -89,8 +89,10 @@ def lib():
         L.nosa_ref_select_blocks.argtypes = [P(_Params), vp, vp, vp, i, i, i, i, vp, vp]
         L.nosa_ref_sparse_attend.argtypes = [P(_Params), vp, vp, vp, vp, vp, i, vp, vp, i, i,
                                              vp, vp]
+        L.nosa_ref_qkv_rope.argtypes = [P(_Params), i, ctypes.c_double, vp, vp, vp, vp, i, vp,
+                                        vp, vp]
         for f in ("nosa_ref_compress_keys", "nosa_ref_block_scores", "nosa_ref_select_blocks",
-                  "nosa_ref_sparse_attend", "nosa_ref_check_params"):
+                  "nosa_ref_sparse_attend", "nosa_ref_check_params", "nosa_ref_qkv_rope"):
             getattr(L, f).restype = i
         _lib = L
     return _lib
@@ -145,6 +147,25 @@ def shapes(p: Params, cu_k, cu_q=None):
 def _check(rc, what):
     if rc != 0:
         raise ValueError(f"oracle {what} rejected its arguments (code {rc})")
+
+
+def qkv_rope(p: Params, x, w, pos, theta=10000.0, inv_freq=None):
+    """Front end of one decode token per sequence: (q [B][Hq][d], k and v
+    [B][Hkv][d]) as bf16 bits from x [B][hidden] and w [(Hq+2Hkv) d][hidden]
+    (bf16 bits) at positions pos [B]."""
+    x = _u16(x)
+    w = _u16(w)
+    pos = _i32(pos)
+    B, hidden = x.shape
+    d = p.head_dim
+    q = np.zeros((B, p.num_q_heads, d), dtype=np.uint16)
+    k = np.zeros((B, p.num_kv_heads, d), dtype=np.uint16)
+    v = np.zeros((B, p.num_kv_heads, d), dtype=np.uint16)
+    f = None if inv_freq is None else np.ascontiguousarray(inv_freq, dtype=np.float64)
+    _check(lib().nosa_ref_qkv_rope(ctypes.byref(p.c()), hidden, float(theta),
+                                   None if f is None else _ptr(f), _ptr(x), _ptr(w), _ptr(pos), B,
+                                   _ptr(q), _ptr(k), _ptr(v)), "qkv_rope")
+    return q, k, v
 
 
 def compress_keys(p: Params, k, cu_k, max_nc=None):

@@ -14,6 +14,7 @@ import pytest
 import scipy.special
 import torch
 
+from oracle import oracle as ora
 from oracle.oracle import Params
 from block_sparse_attention_nosa_amd import synth
 
@@ -441,3 +442,83 @@ def test_varlen_batch_equals_single_runs(oracle):
         for g in range(2):
             assert np.array_equal(full["sel"][s, 0, g, :n[g]], one["sel"][0, 0, g, :n[g]])
         assert np.array_equal(full["out"][s], one["out"][0])
+
+
+# ---- front end: projection and rotary encoding (nosa_ref_qkv_rope) ----
+
+def _bf16_bits(a):
+    """bf16 bit patterns of float64 values (torch's round-to-nearest-even)."""
+    t = torch.tensor(np.asarray(a, dtype=np.float64)).to(torch.float32).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _bf16_values(bits):
+    """float32 values of bf16 bit patterns (so that -0 == +0)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _eye_weights(Hq, Hkv, d):
+    """Every head's rows are the identity on the first d hidden channels."""
+    w = np.zeros(((Hq + 2 * Hkv) * d, d))
+    for h in range(Hq + 2 * Hkv):
+        w[h * d:(h + 1) * d] = np.eye(d)
+    return _bf16_bits(w)
+
+
+def test_qkv_rope_rotates_unit_vectors():
+    """Channel i is paired with channel i + d/2 and turned by pos * inv_freq[i],
+    counter-clockwise from the lower to the upper channel; v is not turned."""
+    import math
+    p = ora.Params(num_q_heads=1, num_kv_heads=1, head_dim=4, topk=1, window=64)
+    w = _eye_weights(1, 1, 4)
+    f = np.array([1.0, 0.5])
+    for c, pos in ((0, 1), (1, 2), (2, 1), (3, 2)):
+        x = np.zeros((1, 4))
+        x[0, c] = 1.0
+        q, k, v = ora.qkv_rope(p, _bf16_bits(x), w, [pos], inv_freq=f)
+        a = pos * f[c % 2]
+        want = np.zeros(4)
+        if c < 2:
+            want[c], want[c + 2] = math.cos(a), math.sin(a)
+        else:
+            want[c - 2], want[c] = -math.sin(a), math.cos(a)
+        assert np.array_equal(_bf16_values(q[0, 0]), _bf16_values(_bf16_bits(want))), (c, pos)
+        assert np.array_equal(_bf16_values(k[0, 0]), _bf16_values(_bf16_bits(want))), (c, pos)
+        assert np.array_equal(_bf16_values(v[0, 0]), x[0].astype(np.float32)), (c, pos)
+
+
+def test_qkv_rope_position_zero_is_the_projection():
+    """At position 0 every angle is 0: q, k, v are the rounded matrix product
+    (small integers: exact in any order)."""
+    rng = np.random.default_rng(4)
+    p = ora.Params(num_q_heads=4, num_kv_heads=2, head_dim=8, topk=1, window=64)
+    hidden = 24
+    w = rng.integers(-3, 4, size=((4 + 4) * 8, hidden)).astype(np.float64)
+    x = rng.integers(-3, 4, size=(3, hidden)).astype(np.float64)
+    q, k, v = ora.qkv_rope(p, _bf16_bits(x), _bf16_bits(w), [0, 0, 0])
+    y = x @ w.T  # [3][(Hq + 2 Hkv) d]
+    V = _bf16_values
+    assert np.array_equal(V(q.reshape(3, -1)), V(_bf16_bits(y[:, :32])))
+    assert np.array_equal(V(k.reshape(3, -1)), V(_bf16_bits(y[:, 32:48])))
+    assert np.array_equal(V(v.reshape(3, -1)), V(_bf16_bits(y[:, 48:])))
+
+
+def test_qkv_rope_is_a_complex_rotation():
+    """Pairs (y_i, y_(i+d/2)) as complex numbers y_i + 1j y_(i+d/2), multiplied
+    by exp(1j pos theta^(-2i/d)): the same numbers as the reference."""
+    rng = np.random.default_rng(5)
+    p = ora.Params(num_q_heads=2, num_kv_heads=1, head_dim=16, topk=1, window=64)
+    hidden, B, d = 32, 4, 16
+    w = rng.integers(-2, 3, size=(4 * d, hidden)).astype(np.float64)
+    x = rng.integers(-2, 3, size=(B, hidden)).astype(np.float64)
+    pos = [0, 7, 1000, 123457]
+    q, k, v = ora.qkv_rope(p, _bf16_bits(x), _bf16_bits(w), pos, theta=500000.0)
+    y = (x @ w.T).reshape(B, 4, d)
+    f = 500000.0 ** (-np.arange(d // 2) * 2.0 / d)
+    z = y[:, :3, :d // 2] + 1j * y[:, :3, d // 2:]
+    z = z * np.exp(1j * np.outer(pos, f))[:, None, :]
+    rot = np.concatenate([z.real, z.imag], axis=-1)
+    V = _bf16_values
+    assert np.array_equal(V(q), V(_bf16_bits(rot[:, :2]).reshape(q.shape)))
+    assert np.array_equal(V(k), V(_bf16_bits(rot[:, 2:3]).reshape(k.shape)))
+    assert np.array_equal(V(v), V(_bf16_bits(y[:, 3:]).reshape(v.shape)))

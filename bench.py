@@ -145,6 +145,10 @@ def main():
     ap.add_argument("--cache-blocks", type=int, default=0,
                     help="offload: block-cache slots per (sequence, KV head); 0 = twice the "
                          "query-aware budget, at most 256")
+    ap.add_argument("--front", type=int, default=0, metavar="HIDDEN",
+                    help="time the attention layer's decode step from hidden states of this "
+                         "width (QKV projection + rotary encoding + KV write, then the sparse "
+                         "attention) instead of the step from ready queries")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run the calibration copy and the kernels once each for counters")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -176,6 +180,8 @@ def main():
         return prompt_main(w, args)
     if args.offload:
         return offload_main(w, args)
+    if args.front:
+        return front_main(w, args)
     if w.q_lens is not None:
         return prefill_main(w, args)
     nsteps = w.extra_tokens + 1
@@ -452,6 +458,108 @@ def prompt_main(w, args):
                         "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                         "traffic": None, "scoring_gflop": round(fs / 1e9, 2),
                         "attention_gflop": round(fa / 1e9, 2)}}
+    print(json.dumps(res), flush=True)
+
+
+def front_main(w, args):
+    """Decode steps of an attention layer from its hidden states (not the
+    headline metric): per layer cache a packed QKV weight matrix (seeded
+    N(0, 1/hidden)) and hidden states; a step is the front-end launch
+    (projection, rotary encoding, K/V write into the pages) and the three
+    launches of the sparse step.  The front-end kernel is also timed alone."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_nosa_amd import nosa, synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    hidden = args.front
+    nsteps = w.extra_tokens + 1
+    layers = build_layers(w, nsteps)
+    B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    lens_at = [[L + t for L in w.lens] for t in range(nsteps)]
+    cu_at = [synth.cu_from_lens(l, "cuda") for l in lens_at]
+    maxL = max(lens_at[-1])
+    p = layers[0]["p"]
+    rows = (Hq + 2 * Hkv) * d
+    front = nosa.front_params(hidden, 10000.0)
+    for li, L in enumerate(layers):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed + 31337 * li)
+        wt = (torch.randn(rows, hidden, generator=gen, device=dev) / hidden ** 0.5).to(torch.bfloat16)
+        L["w"] = torch.empty_like(wt)
+        nosa.nosa_pack_qkv_weights(p, hidden, wt, L["w"])
+        L["x"] = torch.randn(B, hidden, generator=gen, device=dev).to(torch.bfloat16)
+        del wt
+    ws = torch.zeros(nosa.nosa_workspace_size(p, B, 1, maxL), dtype=torch.uint8, device=dev)
+    q_out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(B, Hq, d, device=dev)
+    lse = torch.empty(B, Hq, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def layer_step(i):
+        li = i % LAYERS
+        t = (i // LAYERS) % nsteps
+        L = layers[li]
+        nosa.nosa_layer_decode_step(p, front, L["kv"], L["x"], L["w"], cu_at[t], B, maxL, q_out,
+                                    out, lse, ws)
+
+    def front_only(i):
+        li = i % LAYERS
+        t = (i // LAYERS) % nsteps
+        L = layers[li]
+        nosa.nosa_qkv_rope_append(p, front, L["kv"], L["x"], L["w"], cu_at[t], B, maxL, q_out)
+
+    def timed(fn, n):
+        for i in range(16):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(16 + i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(4):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (4 * n)
+
+    n = 256
+    us_layer = timed(layer_step, n)
+    us_front = timed(front_only, n)
+    w_bytes = rows * hidden * 2
+    front_bytes = w_bytes + B * hidden * 2 + B * (Hq + 2 * Hkv) * d * 2
+    front_gbs = front_bytes / (us_front * 1e-6) / 1e9
+    attn_bytes = np.mean([algorithmic_bytes(w, lens_at[t], False)[0] for t in range(nsteps)])
+    step_bytes = attn_bytes + front_bytes
+    print(f"[bench] layer step from hidden {hidden}: {us_layer:.2f} us/step "
+          f"({step_bytes / 1e6:.2f} MB: {step_bytes / (us_layer * 1e-6) / 1e9:.0f} GB/s); "
+          f"front end alone {us_front:.2f} us ({front_gbs:.0f} GB/s)", file=sys.stderr, flush=True)
+    res = {
+        "metric": "attention-layer decode tokens/s from hidden states at 16K ctx, batch 8; "
+                  "achieved HBM GB/s vs peak",
+        "value": round(B / (us_layer * 1e-6), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": 4 * n, "warmup": 16, "ms_per_step": round(us_layer / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded bf16 N(0,1) hidden states and K/V, N(0, 1/hidden) weights, "
+                "planted blocks, permuted pages)",
+        "config": {"workload": w.name + f"-from-hidden{hidden}", "batch": B, "q_heads": Hq,
+                   "kv_heads": Hkv, "hidden": hidden, "context": w.lens[0] - 1,
+                   "topk_blocks": w.topk, "window_tokens": w.window, "layer_caches": LAYERS},
+        "step_hbm": {"algorithmic_bytes": int(step_bytes),
+                     "achieved_gbs": round(step_bytes / (us_layer * 1e-6) / 1e9, 1),
+                     "frac": round(step_bytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {"kernel": "front_kernel (QKV projection + rotary encoding + KV write)",
+                     "bound": "hbm", "achieved": round(front_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(front_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "us_per_launch": round(us_front, 3),
+                     "algorithmic_bytes_per_launch": int(front_bytes)},
+        "cpu_baseline": None,
+    }
     print(json.dumps(res), flush=True)
 
 

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnosa.so")
 SOURCES = [os.path.join(CSRC, "nosa_kernels.hip"), os.path.join(CSRC, "nosa_prefill.hip"),
-           os.path.join(CSRC, "nosa_api.cpp")]
+           os.path.join(CSRC, "nosa_front.hip"), os.path.join(CSRC, "nosa_api.cpp")]
 ARCH = "gfx950"
 
 

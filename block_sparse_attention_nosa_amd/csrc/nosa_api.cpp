@@ -191,6 +191,26 @@ namespace {
 
 nosa_status hip_status(hipError_t e) { return e == hipSuccess ? NOSA_OK : NOSA_ERR_HIP; }
 
+// Arguments of the front end; fills the plan of the decode batch.
+nosa_status front_check(const nosa_params* p, const nosa_front_params* f, const nosa_paged_kv* kv,
+                        const nosa_bf16* x, const nosa_bf16* w, const int32_t* cu_k, int batch,
+                        int max_seqlen_k, const nosa_bf16* q_out, Plan* pl)
+{
+    nosa_status st = check_params(p);
+    if (st != NOSA_OK) return st;
+    if (!f) return NOSA_ERR_NULL;
+    if (f->hidden <= 0 || f->hidden % 256 != 0) return NOSA_ERR_INVALID;
+    st = check_sizes(batch, batch > 0 ? 1 : 0, max_seqlen_k);
+    if (st != NOSA_OK) return st;
+    st = check_kv(kv, max_seqlen_k, false);
+    if (st != NOSA_OK) return st;
+    if (!x || !w || !cu_k || !q_out) return NOSA_ERR_NULL;
+    if (batch == 0) return NOSA_OK;
+    return make_plan(p, batch, max_seqlen_k, pl);
+}
+
+float front_theta(const nosa_front_params* f) { return f->rope_theta > 0.f ? f->rope_theta : 10000.f; }
+
 // Block cache of the offloaded KV: at least the query-aware share of the
 // budget (every pick needs a slot), at most one slot per thread of a
 // workgroup.  The window must hold a block, so that every pick is a complete
@@ -540,6 +560,54 @@ nosa_status nosa_offload_decode_step(const nosa_params* params, const nosa_offlo
     pk.num_pages = kv->num_pages;
     return hip_status(launch_decode(pl, pk, q, cu_seqlens_k, carve(pl, workspace), out, lse,
                                     sel_idx, sel_count, nullptr, as_stream(stream), &off));
+}
+
+nosa_status nosa_pack_qkv_weights(const nosa_params* params, int32_t hidden, const nosa_bf16* w,
+                                  nosa_bf16* packed, void* stream)
+{
+    nosa_status st = check_params(params);
+    if (st != NOSA_OK) return st;
+    if (!w || !packed) return NOSA_ERR_NULL;
+    if (hidden <= 0 || hidden % 256 != 0) return NOSA_ERR_INVALID;
+    return hip_status(launch_pack_qkv(params->num_q_heads, params->num_kv_heads, hidden, w, packed,
+                                      as_stream(stream)));
+}
+
+nosa_status nosa_qkv_rope_append(const nosa_params* params, const nosa_front_params* front,
+                                 const nosa_paged_kv* kv, const nosa_bf16* x,
+                                 const nosa_bf16* w_packed, const int32_t* cu_seqlens_k,
+                                 int32_t batch, int32_t max_seqlen_k, nosa_bf16* q_out,
+                                 void* stream)
+{
+    Plan pl;
+    nosa_status st = front_check(params, front, kv, x, w_packed, cu_seqlens_k, batch, max_seqlen_k,
+                                 q_out, &pl);
+    if (st != NOSA_OK || batch == 0) return st;
+    return hip_status(launch_front(pl, *kv, x, w_packed, front->hidden, front_theta(front),
+                                   front->inv_freq, cu_seqlens_k, q_out, as_stream(stream)));
+}
+
+nosa_status nosa_layer_decode_step(const nosa_params* params, const nosa_front_params* front,
+                                   const nosa_paged_kv* kv, const nosa_bf16* x,
+                                   const nosa_bf16* w_packed, const int32_t* cu_seqlens_k,
+                                   int32_t batch, int32_t max_seqlen_k, nosa_bf16* q_out,
+                                   float* out, float* lse, int32_t* sel_idx, int32_t* sel_count,
+                                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    Plan pl;
+    nosa_status st = front_check(params, front, kv, x, w_packed, cu_seqlens_k, batch, max_seqlen_k,
+                                 q_out, &pl);
+    if (st != NOSA_OK) return st;
+    if (!out) return NOSA_ERR_NULL;
+    if ((sel_idx == nullptr) != (sel_count == nullptr)) return NOSA_ERR_NULL;
+    if (batch == 0) return NOSA_OK;
+    if (!workspace || workspace_bytes < pl.bytes) return NOSA_ERR_WORKSPACE;
+    const hipStream_t sm = as_stream(stream);
+    hipError_t e = launch_front(pl, *kv, x, w_packed, front->hidden, front_theta(front),
+                                front->inv_freq, cu_seqlens_k, q_out, sm);
+    if (e != hipSuccess) return NOSA_ERR_HIP;
+    return hip_status(launch_decode(pl, *kv, q_out, cu_seqlens_k, carve(pl, workspace), out, lse,
+                                    sel_idx, sel_count, nullptr, sm));
 }
 
 nosa_status nosa_decode_step(const nosa_params* params, const nosa_paged_kv* kv,

@@ -131,4 +131,11 @@ hipError_t launch_chunk_scatter(const float* oc, const float* lc, const int32_t*
                                 const int32_t* cu_q_c, int B, int c, int C, int Hq, float* out,
                                 float* lse, hipStream_t stream);
 
+// Front end (nosa_front.hip).
+hipError_t launch_pack_qkv(int Hq, int Hkv, int hidden, const nosa_bf16* w, nosa_bf16* packed,
+                           hipStream_t stream);
+hipError_t launch_front(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* x,
+                        const nosa_bf16* w, int hidden, float theta, const float* inv_freq,
+                        const int32_t* cu_k, nosa_bf16* q_out, hipStream_t stream);
+
 }  // namespace nosa

@@ -53,6 +53,11 @@ class nosa_offload_kv(ctypes.Structure):
                 ("cache_map", ctypes.c_void_p), ("cache_used", ctypes.c_void_p)]
 
 
+class nosa_front_params(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("inv_freq", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -80,6 +85,11 @@ def lib() -> ctypes.CDLL:
             "nosa_prefill_sparse_workspace_size": [P, i32, i32, i32, ctypes.POINTER(sz)],
             "nosa_prefill_sparse": [P, KV, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp],
             "nosa_offload_workspace_size": [P, i32, i32, i32, ctypes.POINTER(sz)],
+            "nosa_pack_qkv_weights": [P, i32, vp, vp, vp],
+            "nosa_qkv_rope_append": [P, ctypes.POINTER(nosa_front_params), KV, vp, vp, vp, i32,
+                                     i32, vp, vp],
+            "nosa_layer_decode_step": [P, ctypes.POINTER(nosa_front_params), KV, vp, vp, vp, i32,
+                                       i32, vp, vp, vp, vp, vp, vp, sz, vp],
             "nosa_offload_decode_step": [P, ctypes.POINTER(nosa_offload_kv), vp, vp, i32, i32, vp,
                                          vp, vp, vp, vp, vp, sz, vp],
         }
@@ -240,5 +250,32 @@ def nosa_offload_decode_step(p, okv, q, cu_seqlens_k, batch, max_seqlen_k, out, 
     _check("nosa_offload_decode_step", lib().nosa_offload_decode_step(
         ctypes.byref(p), ctypes.byref(okv), _ptr(q), _ptr(cu_seqlens_k), batch, max_seqlen_k,
         _ptr(out), _ptr(lse), _ptr(sel_idx), _ptr(sel_count), _ptr(fetch_count), _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))
+
+
+def front_params(hidden: int, rope_theta: float = 10000.0, inv_freq=None) -> nosa_front_params:
+    """Front-end parameters (inv_freq: optional device float32 tensor [64])."""
+    return nosa_front_params(int(hidden), float(rope_theta), _ptr(inv_freq))
+
+
+def nosa_pack_qkv_weights(p, hidden, w, packed, stream=None):
+    _check("nosa_pack_qkv_weights", lib().nosa_pack_qkv_weights(
+        ctypes.byref(p), hidden, _ptr(w), _ptr(packed), _stream(stream)))
+
+
+def nosa_qkv_rope_append(p, front, kv, x, w_packed, cu_seqlens_k, batch, max_seqlen_k, q_out,
+                         stream=None):
+    _check("nosa_qkv_rope_append", lib().nosa_qkv_rope_append(
+        ctypes.byref(p), ctypes.byref(front), ctypes.byref(kv), _ptr(x), _ptr(w_packed),
+        _ptr(cu_seqlens_k), batch, max_seqlen_k, _ptr(q_out), _stream(stream)))
+
+
+def nosa_layer_decode_step(p, front, kv, x, w_packed, cu_seqlens_k, batch, max_seqlen_k, q_out,
+                           out, lse, workspace, sel_idx=None, sel_count=None, stream=None):
+    _check("nosa_layer_decode_step", lib().nosa_layer_decode_step(
+        ctypes.byref(p), ctypes.byref(front), ctypes.byref(kv), _ptr(x), _ptr(w_packed),
+        _ptr(cu_seqlens_k), batch, max_seqlen_k, _ptr(q_out), _ptr(out), _ptr(lse), _ptr(sel_idx),
+        _ptr(sel_count), _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream)))

@@ -346,6 +346,62 @@ nosa_status nosa_offload_decode_step(const nosa_params* params, const nosa_offlo
                                      int32_t* sel_idx, int32_t* sel_count, int32_t* fetch_count,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Attention front end [page "NOSA技术架构解析", section 2.1: the QKV projection,
+ * the rotary position encoding and the importance scoring are fused to cut
+ * the launches of a decode step].  For the current token of each sequence
+ * (position p = L_s - 1) with hidden state x[s][0 .. hidden):
+ *   y = W x over the (Hq + 2 Hkv) * head_dim rows of W: the Hq query heads,
+ *       then the Hkv key heads, then the Hkv value heads;
+ *   q and k heads: channel i and channel i + head_dim/2 (i < head_dim/2)
+ *       are turned as one pair by the angle p * inv_freq[i]:
+ *       (y_i, y_(i+d/2)) -> (y_i cos - y_(i+d/2) sin, y_(i+d/2) cos + y_i sin);
+ *   every value rounded to bf16 (fp32 accumulation, angles in fp64).
+ * The queries go to q_out; k and v are written into the token's slot of page
+ * block_table[s][p / block_size] of k_pool / v_pool (so the const of those
+ * two members is cast away: this call writes them). */
+typedef struct nosa_front_params {
+    int32_t hidden;         /* width of x: a positive multiple of 256            */
+    float rope_theta;       /* base of the angles; <= 0 selects 10000            */
+    const float* inv_freq;  /* device [head_dim / 2] angle per position of each  */
+                            /* pair, or NULL for rope_theta^(-2i / head_dim)     */
+} nosa_front_params;
+
+/* Packs row-major weights w [(Hq + 2 Hkv) * head_dim][hidden] (device bf16)
+ * into the order the front end reads (device, the same number of elements;
+ * owned by the caller, written here).  In the packed order, 16-row tile
+ * T = 8 h + j holds rows 8j .. 8j+7 and 64+8j .. 64+8j+7 of head h; for run
+ * kb of 256 hidden channels and k-step t, 64 lanes of 8 elements follow each
+ * other, lane 16 grp + m holding row m of the tile (rows 8j + m, then
+ * 64 + 8j + m - 8) at channels 256 kb + 32 t + 8 grp .. +7:
+ *   packed[(((T * hidden/256 + kb) * 8 + t) * 64 + lane) * 8 + e].
+ * Done once per weight matrix; enqueued on `stream`.  Errors: NOSA_ERR_NULL,
+ * NOSA_ERR_INVALID (hidden not a positive multiple of 256),
+ * NOSA_ERR_UNSUPPORTED (head_dim != 128), NOSA_ERR_HIP. */
+nosa_status nosa_pack_qkv_weights(const nosa_params* params, int32_t hidden, const nosa_bf16* w,
+                                  nosa_bf16* packed, void* stream);
+
+/* The front end alone (one launch): q_out device [batch][Hq][head_dim] bf16;
+ * x device [batch][hidden] bf16; w_packed from nosa_pack_qkv_weights;
+ * cu_seqlens_k as in nosa_decode_step, the current token's page must exist.
+ * Errors: NOSA_ERR_NULL, NOSA_ERR_INVALID, NOSA_ERR_UNSUPPORTED,
+ * NOSA_ERR_HIP. */
+nosa_status nosa_qkv_rope_append(const nosa_params* params, const nosa_front_params* front,
+                                 const nosa_paged_kv* kv, const nosa_bf16* x,
+                                 const nosa_bf16* w_packed, const int32_t* cu_seqlens_k,
+                                 int32_t batch, int32_t max_seqlen_k, nosa_bf16* q_out,
+                                 void* stream);
+
+/* One decode step of an attention layer from its hidden states: the front end
+ * (nosa_qkv_rope_append), then nosa_decode_step on the queries it made (four
+ * launches).  Arguments as in those two calls; q_out receives the queries.
+ * Needs a nosa_workspace_size workspace. */
+nosa_status nosa_layer_decode_step(const nosa_params* params, const nosa_front_params* front,
+                                   const nosa_paged_kv* kv, const nosa_bf16* x,
+                                   const nosa_bf16* w_packed, const int32_t* cu_seqlens_k,
+                                   int32_t batch, int32_t max_seqlen_k, nosa_bf16* q_out,
+                                   float* out, float* lse, int32_t* sel_idx, int32_t* sel_count,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

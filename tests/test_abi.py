@@ -25,7 +25,8 @@ def test_exports_every_declared_function(L):
                           "nosa_compress_keys", "nosa_block_scores", "nosa_select_blocks",
                           "nosa_sparse_attend", "nosa_decode_step", "nosa_prefill_sparse",
                           "nosa_prefill_sparse_workspace_size", "nosa_offload_decode_step",
-                          "nosa_offload_workspace_size"}
+                          "nosa_offload_workspace_size", "nosa_pack_qkv_weights",
+                          "nosa_qkv_rope_append", "nosa_layer_decode_step"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -216,3 +217,29 @@ def test_offload_host_errors(L):
     assert call(small) == 2
     assert call(okv, wsb=100) == 4
     assert call(okv, B=0) == 0
+
+
+def test_front_host_errors(L):
+    p = nosa.params()
+    kv = _kv()
+    f = nosa.front_params(2048)
+    assert L.nosa_pack_qkv_weights(ctypes.byref(p), 2048, None, FAKE, None) == 1
+    assert L.nosa_pack_qkv_weights(ctypes.byref(p), 100, FAKE, FAKE, None) == 2
+    assert L.nosa_pack_qkv_weights(ctypes.byref(nosa.params(head_dim=64)), 2048, FAKE, FAKE,
+                                   None) == 3
+    call = lambda **kw: L.nosa_qkv_rope_append(
+        ctypes.byref(p), ctypes.byref(kw.get("f", f)) if kw.get("f", f) else None,
+        ctypes.byref(kv), kw.get("x", FAKE), FAKE, FAKE, kw.get("B", 8), 16384,
+        kw.get("q", FAKE), None)
+    assert call(f=None) == 1
+    assert call(x=None) == 1
+    assert call(q=None) == 1
+    assert call(f=nosa.front_params(1000)) == 2
+    assert call(f=nosa.front_params(0)) == 2
+    assert call(B=0) == 0
+    step = lambda **kw: L.nosa_layer_decode_step(
+        ctypes.byref(p), ctypes.byref(f), ctypes.byref(kv), FAKE, FAKE, FAKE, 8, 16384, FAKE,
+        kw.get("out", FAKE), None, kw.get("sel", None), None, FAKE, kw.get("wsb", 0), None)
+    assert step(out=None) == 1
+    assert step(sel=FAKE) == 1
+    assert step(wsb=100) == 4

@@ -1269,16 +1269,30 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
     // The window pages (known before any selection) go beside the selection
     // when the attention launch then fits on the chip at once (two
     // workgroups per CU): a page per workgroup if that fits, else a page per
-    // wave; otherwise beside the scoring, a page per workgroup.
+    // wave, if need be with up to four top-k pages per wave instead of fewer
+    // (fewer top workgroups: the window pages then stream while the
+    // selection runs, when HBM is otherwise idle); otherwise beside the
+    // scoring, a page per workgroup.
     const long long pairs = (long long)pl.B * pl.Hkv, room = 2LL * device_cus();
     const int per_wave = ceil_div(pl.wslots, 4);
-    int wg_top = 0;
-    if (pairs * (pl.top_groups + pl.wslots) <= room)
+    int groups = pl.top_groups, rounds = pl.top_rounds, wg_top = 0;
+    if (pairs * (groups + pl.wslots) <= room) {
         wg_top = pl.wslots;
-    else if (pairs * (pl.top_groups + per_wave) <= room)
+    } else if (pairs * (groups + per_wave) <= room) {
         wg_top = per_wave;
+    } else {
+        for (int r = rounds + 1; r <= 4 && wg_top == 0; ++r) {
+            const int gr = ceil_div(pl.top_span > 0 ? pl.top_span : 1, kStep2Waves * r);
+            if (pairs * (gr + per_wave) <= room) {
+                groups = gr;
+                rounds = r;
+                wg_top = per_wave;
+            }
+        }
+    }
     // partials per head: the top workgroups', then one per window workgroup
-    const int nsplit = pl.top_groups + (wg_top > 0 ? wg_top : pl.wslots);
+    // (at most top_groups + wslots, the workspace's)
+    const int nsplit = groups + (wg_top > 0 ? wg_top : pl.wslots);
     hipError_t e = launch_score(pl, kv, q, cu_k, w, 1, wg_top == 0, stream, off);
     if (e != hipSuccess) return e;
     TopArgs a = top_args(pl, kv, q, cu_k, w);
@@ -1297,8 +1311,8 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
         a.fetch_out = off->fetch_out;
         a.cap = off->cap;
     }
-    a.groups = pl.top_groups;
-    a.rounds = pl.top_rounds;
+    a.groups = groups;
+    a.rounds = rounds;
     a.wslots = wg_top > 0 ? pl.wslots : 0;
     a.wgroups = wg_top;
     a.nsplit = nsplit;

@@ -368,7 +368,7 @@ struct PfAttnLds {
 // mapped to the logical workgroup (b % 8) * per_xcd + b / 8: the attn_groups
 // workgroups of a pair, which read the same pages, run on one XCD and share
 // its L2.  Indices past the last logical workgroup exit at once.
-__global__ __launch_bounds__(256) void pf_attend_kernel(PfArgs a, int attn_groups, int total,
+__global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_groups, int total,
                                                         int per_xcd)
 {
     __shared__ PfAttnLds sh;

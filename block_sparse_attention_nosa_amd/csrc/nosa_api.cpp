@@ -168,6 +168,16 @@ void make_pf_plan(const Plan& pl, int max_seqlen_q, PfPlan* pf)
     F.off_part = off;   off += align256(np * F.rows * (size_t)F.key_splits * sizeof(float2));
     F.off_colsum = off; off += align256(np * F.row_groups * (size_t)F.key_splits * 256 * sizeof(float));
     F.bytes = off > 256 ? off : 256;
+    const size_t groups = np * (size_t)F.attn_groups;
+    F.split_rows = (F.max_seqlen_q < 64 ? (F.max_seqlen_q > 0 ? F.max_seqlen_q : 1) : 64) * pl.G;
+    if (groups <= (size_t)kPfSplitGroups) {
+        const size_t prs = np * (size_t)F.split_rows;
+        off = F.bytes;
+        F.off_po = off;  off += align256(prs * 2 * kHeadDim * sizeof(float));
+        F.off_pml = off; off += align256(prs * 2 * sizeof(float) * 2);
+        F.bytes = off;
+    }
+    F.bytes_split = F.bytes;
     *pf = F;
 }
 
@@ -427,11 +437,12 @@ nosa_status nosa_sparse_attend(const nosa_params* params, const nosa_paged_kv* k
     Plan pl;
     st = make_plan(params, batch, max_seqlen_k, &pl);
     if (st != NOSA_OK) return st;
-    if (cu_seqlens_q) {  // chunk attention: no workspace needed
+    if (cu_seqlens_q) {  // chunk attention: the workspace is optional (split attention)
         PfPlan pf;
         make_pf_plan(pl, max_seqlen_q, &pf);
         return hip_status(launch_pf_attend(pl, pf, *kv, q, cu_seqlens_q, cu_seqlens_k, sel_idx,
-                                           sel_count, out, lse, as_stream(stream)));
+                                           sel_count, out, lse, workspace, workspace_bytes,
+                                           as_stream(stream)));
     }
     if (!workspace || workspace_bytes < pl.bytes) return NOSA_ERR_WORKSPACE;
     return hip_status(launch_attend(pl, *kv, q, cu_seqlens_k, sel_idx, sel_count,
@@ -485,7 +496,9 @@ nosa_status nosa_prefill_sparse(const nosa_params* params, const nosa_paged_kv* 
         if (e == hipSuccess) e = launch_kc_build(pl, *kv, cu_k_c, valid_c, gx, sm);
         if (e == hipSuccess) e = launch_pf_scores(pl, pf, *kv, qc, cu_q_c, cu_k_c, workspace, scores, sm);
         if (e == hipSuccess) e = launch_select(pl, cu_k_c, cu_q_c, C, scores, sel, cnt, sm);
-        if (e == hipSuccess) e = launch_pf_attend(pl, pf, *kv, qc, cu_q_c, cu_k_c, sel, cnt, oc, lc, sm);
+        if (e == hipSuccess)
+            e = launch_pf_attend(pl, pf, *kv, qc, cu_q_c, cu_k_c, sel, cnt, oc, lc, workspace,
+                                 pf.bytes, sm);
         if (e == hipSuccess)
             e = launch_chunk_scatter(oc, lse ? lc : nullptr, cu_seqlens, cu_q_c, batch, c, C, pl.Hq,
                                      out, lse, sm);

@@ -70,7 +70,13 @@ struct PfPlan {
     int key_splits = 0;   // scoring workgroups over the pooled keys of a pair
     int attn_groups = 0;  // attention workgroups (128 rows each) per pair
     size_t off_part = 0, off_colsum = 0, bytes = 0;
+    // split attention (launches of at most kPfSplitGroups workgroups): the
+    // halves' partials after the scoring scratch; bytes_split = the workspace
+    // that holds them (bytes when no launch of this plan can split)
+    size_t off_po = 0, off_pml = 0, bytes_split = 0;
+    int split_rows = 0;  // rows per pair in the partials: min(64, max_seqlen_q) * G
 };
+constexpr int kPfSplitGroups = 256;  // one workgroup per CU or fewer: split the pages
 
 // Offloaded KV (device pointers; the host pools as the device sees them).
 struct Offload {
@@ -117,10 +123,12 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
 hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
                             const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
                             void* ws, float* scores, hipStream_t stream);
+// ws / ws_bytes: workspace for the split attention's partials (may be null:
+// then the attention is not split).
 hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
                             const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
                             const int32_t* sel, const int32_t* cnt, float* out, float* lse,
-                            hipStream_t stream);
+                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Whole-prompt prefill, chunk by chunk (nosa_prefill.hip).
 hipError_t launch_chunk_setup(const int32_t* cu, int B, int Lmax, int c, int C, int32_t* cu_k_c,

@@ -51,6 +51,12 @@ struct PfArgs {
     int max_sel;
     float* out;  // [total_q][Hq][D]
     float* lse;  // [total_q][Hq] or null
+    // attention split over two workgroups per row group (ksplit = 2): each
+    // attends half of the kept pages and leaves unnormalised partials
+    int ksplit;
+    int rp;       // rows per pair in the partials: min(64, Lqmax) * G
+    float* po;    // [pairs][rp][2][D]
+    float2* pml;  // [pairs][rp][2] (max, sum) in log2 units
 };
 
 // Geometry of one pair.
@@ -368,14 +374,20 @@ struct PfAttnLds {
 // mapped to the logical workgroup (b % 8) * per_xcd + b / 8: the attn_groups
 // workgroups of a pair, which read the same pages, run on one XCD and share
 // its L2.  Indices past the last logical workgroup exit at once.
+//
+// With ksplit = 2 (a launch that would not give every CU two workgroups:
+// one workgroup's pages are then a latency-bound chain), logical workgroup
+// 2w + k attends the k-th half of row group w's pages and stores its
+// unnormalised partial; pf_merge_kernel combines the two.
 __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_groups, int total,
                                                         int per_xcd)
 {
     __shared__ PfAttnLds sh;
     extern __shared__ __align__(16) char smem[];
     int2* list = reinterpret_cast<int2*>(smem);  // [max_sel] (block, page)
-    const int lid = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-    if (lid >= total) return;
+    const int lid_k = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (lid_k >= total * a.ksplit) return;
+    const int lid = lid_k / a.ksplit, ks = lid_k % a.ksplit;
     const int pair = lid / attn_groups, ag = lid % attn_groups;
     const PfPair P = pf_pair(a, pair);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -528,18 +540,39 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
             }
     };
 
-    if (n > 0) {
-        fetch(0, stk, stv);
+    // this workgroup's pages: all, or half of them
+    const int i0 = n * ks / a.ksplit, i1 = n * (ks + 1) / a.ksplit;
+    if (i1 > i0) {
+        fetch(i0, stk, stv);
         stash(0, stk, stv);
         __syncthreads();
     }
-    for (int idx = 0; idx < n; ++idx) {
-        const int buf = idx & 1;
+    for (int idx = i0; idx < i1; ++idx) {
+        const int buf = (idx - i0) & 1;
         fetch(idx + 1, stk, stv);  // in flight while page idx is computed
         const int b = list[idx].x;
         if (b >= 0) compute(buf, b);
-        if (idx + 1 < n) stash(buf ^ 1, stk, stv);
+        if (idx + 1 < i1) stash(buf ^ 1, stk, stv);
         __syncthreads();
+    }
+    if (a.ksplit > 1) {  // unnormalised partial of this half, rows holding a query
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float l = l_run[u];
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            const int row0 = ((ag * 4 + wave) * 2 + u) * 16;  // the row tile in the pair
+            const size_t pr0 = (size_t)pair * a.rp + row0;
+            if (kq == 0 && qpos[u] >= 0) a.pml[(pr0 + r) * 2 + ks] = make_float2(m_run[u], l);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (__shfl(qpos[u], 4 * kq + i) < 0) continue;
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt)
+                    a.po[((pr0 + 4 * kq + i) * 2 + ks) * D + nt * 16 + r] = o[u][nt][i];
+            }
+        }
+        return;
     }
 
     // normalise and store: lane holds O[rows 4kq + i][channels 16nt + r]
@@ -560,6 +593,36 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
             for (int nt = 0; nt < 8; ++nt) a.out[(size_t)row_i * D + nt * 16 + r] = o[u][nt][i] * inv_i;
         }
     }
+}
+
+// The two halves of a split attention: row x of row group w from partials
+// (m_k, l_k, o_k), k < 2, in log2 units: out = sum 2^(m_k - M) o_k / L,
+// L = sum 2^(m_k - M) l_k, lse = (M + log2 L) ln 2; a row that saw nothing
+// gets 0 and -inf.  Workgroup (w, y): rows 8y .. 8y + 7 of row group w, a
+// thread per (row, 4 channels).
+__global__ __launch_bounds__(256) void pf_merge_kernel(PfArgs a, int attn_groups, int total)
+{
+    const int lid = blockIdx.x;
+    if (lid >= total) return;
+    const int pair = lid / attn_groups, ag = lid % attn_groups;
+    const PfPair P = pf_pair(a, pair);
+    const int row = ag * 128 + (int)blockIdx.y * 8 + (threadIdx.x >> 5), c4 = threadIdx.x & 31;
+    const int qi = row / a.G, h = row % a.G;
+    if (P.empty || row >= a.rows || qi >= P.nq) return;  // rows past the block's queries
+    const size_t pr = (size_t)pair * a.rp + row;
+    const float2 p0 = a.pml[pr * 2], p1 = a.pml[pr * 2 + 1];
+    const float4 o0 = reinterpret_cast<const float4*>(a.po + (pr * 2) * D)[c4];
+    const float4 o1 = reinterpret_cast<const float4*>(a.po + (pr * 2 + 1) * D)[c4];
+    const float M = fmaxf(p0.x, p1.x);
+    const float w0 = p0.x == -INFINITY ? 0.f : fexp2(p0.x - M);
+    const float w1 = p1.x == -INFINITY ? 0.f : fexp2(p1.x - M);
+    const float L = w0 * p0.y + w1 * p1.y;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const size_t qrow = (size_t)(P.q0 + kQB * P.r + qi) * a.Hq + P.g * a.G + h;
+    reinterpret_cast<float4*>(a.out + qrow * D)[c4] =
+        make_float4((w0 * o0.x + w1 * o1.x) * inv, (w0 * o0.y + w1 * o1.y) * inv,
+                    (w0 * o0.z + w1 * o1.z) * inv, (w0 * o0.w + w1 * o1.w) * inv);
+    if (a.lse && c4 == 0) a.lse[qrow] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
 // ---------------------------------------------------------- launchers ---
@@ -624,7 +687,7 @@ hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_k
 hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
                             const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
                             const int32_t* sel, const int32_t* cnt, float* out, float* lse,
-                            hipStream_t stream)
+                            void* ws, size_t ws_bytes, hipStream_t stream)
 {
     PfArgs a = pf_args(pl, pf, &kv, q, cu_q, cu_k);
     a.sel = sel;
@@ -633,9 +696,21 @@ hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_k
     a.lse = lse;
     const size_t lds = (size_t)(pl.max_sel > 0 ? pl.max_sel : 1) * sizeof(int2);
     const int total = pf.npairs * pf.attn_groups;
-    const int per_xcd = (total + 7) / 8;
+    // split the pages of each row group over two workgroups when the launch
+    // has at most kPfSplitGroups of them and the workspace holds the partials
+    a.ksplit = total <= kPfSplitGroups && ws && ws_bytes >= pf.bytes_split ? 2 : 1;
+    if (a.ksplit > 1) {
+        a.rp = pf.split_rows;
+        a.po = reinterpret_cast<float*>(static_cast<char*>(ws) + pf.off_po);
+        a.pml = reinterpret_cast<float2*>(static_cast<char*>(ws) + pf.off_pml);
+    }
+    const int per_xcd = (total * a.ksplit + 7) / 8;
     hipLaunchKernelGGL(pf_attend_kernel, dim3(8 * per_xcd), dim3(256), lds, stream, a, pf.attn_groups,
                        total, per_xcd);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.ksplit == 1 || total == 0) return e;
+    hipLaunchKernelGGL(pf_merge_kernel, dim3(total, 16), dim3(256), 0, stream, a, pf.attn_groups,
+                       total);
     return hipGetLastError();
 }
 

@@ -262,7 +262,10 @@ nosa_status nosa_select_blocks(const nosa_params* params, const float* block_sco
  * (decode: p = L_s - 1, r = 0).  out: device fp32 [total queries][Hq][d];
  * lse: device fp32 [total queries][Hq] (natural log of the softmax
  * denominator, -inf for a query that sees no token) or NULL.  Block ids must
- * be distinct and < nb_r.  Needs a `workspace` (see above). */
+ * be distinct and < nb_r.  Needs a `workspace` (see above) in decode; with
+ * cu_seqlens_q the workspace is optional: given, a launch of few workgroups
+ * splits each one's pages over two (their partials kept in it) and merges
+ * them; NULL attends each row group's pages in one workgroup. */
 nosa_status nosa_sparse_attend(const nosa_params* params, const nosa_paged_kv* kv,
                                const nosa_bf16* q, const int32_t* cu_seqlens_q,
                                const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
@@ -304,7 +307,10 @@ nosa_status nosa_prefill_sparse_workspace_size(const nosa_params* params, int32_
  * chunks of `chunk` positions (the same for every sequence, a multiple of
  * block_size); chunk c pools the compressed keys its tokens complete, then
  * scores, selects and attends for its queries, so the workspace scales with
- * the chunk and not with the prompt.  The chunk does not change the result.
+ * the chunk and not with the prompt.  The chunk does not change the
+ * selection; the outputs may differ in the rounding of the attention weights
+ * (bf16, relative to a running maximum), since an attention launch of few
+ * workgroups splits each one's pages over two and merges the two partials.
  * K and V of every prompt token must already be in the pages; kc_pool is
  * written for every key of the prompts (as nosa_compress_keys with
  * kc_valid_len NULL).  q: device [total tokens][Hq][d] bf16 in cu_seqlens

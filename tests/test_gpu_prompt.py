@@ -3,8 +3,11 @@ query of each prompt attends to the blocks selected for its 64-query block,
 chunk by chunk.  Checked against the oracle's forward with the prompt as both
 queries and keys; query blocks whose selection sits on a near-tie (relative
 gap below the tie band, where fp32 and fp64 may order two blocks differently)
-are compared through the stand-alone chain instead, which must agree with the
-whole-prompt call bit for bit."""
+are compared through the stand-alone chain instead.  Different chunk sizes
+and the stand-alone chain select the same blocks; their outputs agree within
+the rounding of the attention weights (a launch of few workgroups splits each
+one's pages over two and merges the halves, and each half rounds its weights
+to bf16 relative to its own running maximum)."""
 import math
 
 import numpy as np
@@ -39,6 +42,17 @@ def prompt_prefill(c, chunk):
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
+def _same(a, b, what):
+    """Outputs of two launches of the same attention on the same selection:
+    within the output bound, and the log-sum-exp within 1e-4 (fp32 sums)."""
+    assert np.isfinite(a[0]).all() and np.isfinite(b[0]).all(), what
+    err = np.abs(a[0].astype(np.float64) - b[0])
+    assert err.max() <= OUT_MAX_ABS and err.mean() <= OUT_MEAN_ABS / 10, (what, err.max(), err.mean())
+    fin = np.isfinite(b[1])
+    assert np.array_equal(fin, np.isfinite(a[1])), what
+    assert np.abs(a[1][fin] - b[1][fin]).max(initial=0.0) <= 1e-4 * max(1.0, np.abs(b[1][fin]).max(initial=0.0)), what
+
+
 def _check(c, chunks, tag):
     w = c.w
     c.pg["kc_pool"].fill_(0x7fc0)  # NaN bits: every key the queries use must be rebuilt
@@ -51,12 +65,10 @@ def _check(c, chunks, tag):
         if nc:
             assert np.array_equal(gpu_kc_logical(c, s, nc), o["kc"][s, :, :nc]), (tag, s)
     out, lse = res[chunks[0]]
-    for ch in chunks[1:]:  # the chunk does not change the result
-        assert np.array_equal(res[ch][0], out), (tag, ch)
-        assert np.array_equal(res[ch][1], lse, equal_nan=True), (tag, ch)
+    for ch in chunks[1:]:  # the chunk changes the result only by rounding
+        _same(res[ch], (out, lse), (tag, ch))
     g, _ = gpu_prefill(c)  # the stand-alone chain over the same prompt
-    assert np.array_equal(g["out"], out), tag
-    assert np.array_equal(g["lse"], lse, equal_nan=True), tag
+    _same((g["out"], g["lse"]), (out, lse), tag)
     keep = np.zeros(out.shape[0], bool)
     ex = 0
     for s, L in enumerate(w.lens):

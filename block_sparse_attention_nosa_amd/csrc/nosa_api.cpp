@@ -254,12 +254,11 @@ const nosa_bf16* device_view(const nosa_bf16* p)
 }
 
 // Workspace of the whole-prompt prefill: the prefill scratch of one chunk,
-// then the chunk's bookkeeping, gathered queries, outputs, importance and
-// selection.
+// then the chunk's bookkeeping, importance and selection.
 struct PromptLayout {
     int C = 0, mq = 0;  // chunk (queries), query blocks per chunk
-    size_t off_cuk = 0, off_cuq = 0, off_valid = 0, off_q = 0, off_out = 0, off_lse = 0,
-           off_scores = 0, off_sel = 0, off_cnt = 0, bytes = 0;
+    size_t off_cuk = 0, off_cuq = 0, off_valid = 0, off_qbase = 0, off_scores = 0, off_sel = 0,
+           off_cnt = 0, bytes = 0;
 };
 
 PromptLayout prompt_layout(const Plan& pl, const PfPlan& pf, int B, int C)
@@ -267,14 +266,12 @@ PromptLayout prompt_layout(const Plan& pl, const PfPlan& pf, int B, int C)
     PromptLayout Y;
     Y.C = C;
     Y.mq = C / kBlock;
-    const size_t b = (size_t)B, rows = b * C, qb = b * Y.mq * pl.Hkv;
+    const size_t b = (size_t)B, qb = b * Y.mq * pl.Hkv;
     size_t off = pf.bytes;
     Y.off_cuk = off;    off += align256((b + 1) * sizeof(int32_t));
     Y.off_cuq = off;    off += align256((b + 1) * sizeof(int32_t));
     Y.off_valid = off;  off += align256(b * sizeof(int32_t));
-    Y.off_q = off;      off += align256(rows * pl.Hq * kHeadDim * sizeof(nosa_bf16));
-    Y.off_out = off;    off += align256(rows * pl.Hq * kHeadDim * sizeof(float));
-    Y.off_lse = off;    off += align256(rows * pl.Hq * sizeof(float));
+    Y.off_qbase = off;  off += align256(b * sizeof(int32_t));
     Y.off_scores = off; off += align256(qb * (size_t)pl.max_nb * sizeof(float));
     Y.off_sel = off;    off += align256(qb * (size_t)pl.max_sel * sizeof(int32_t));
     Y.off_cnt = off;    off += align256(qb * sizeof(int32_t));
@@ -481,9 +478,7 @@ nosa_status nosa_prefill_sparse(const nosa_params* params, const nosa_paged_kv* 
     int32_t* cu_k_c = reinterpret_cast<int32_t*>(ws + Y.off_cuk);
     int32_t* cu_q_c = reinterpret_cast<int32_t*>(ws + Y.off_cuq);
     int32_t* valid_c = reinterpret_cast<int32_t*>(ws + Y.off_valid);
-    nosa_bf16* qc = reinterpret_cast<nosa_bf16*>(ws + Y.off_q);
-    float* oc = reinterpret_cast<float*>(ws + Y.off_out);
-    float* lc = reinterpret_cast<float*>(ws + Y.off_lse);
+    int32_t* qbase_c = reinterpret_cast<int32_t*>(ws + Y.off_qbase);
     float* scores = reinterpret_cast<float*>(ws + Y.off_scores);
     int32_t* sel = reinterpret_cast<int32_t*>(ws + Y.off_sel);
     int32_t* cnt = reinterpret_cast<int32_t*>(ws + Y.off_cnt);
@@ -491,17 +486,15 @@ nosa_status nosa_prefill_sparse(const nosa_params* params, const nosa_paged_kv* 
     const int C = Y.C, nch = ceil_div(max_seqlen, C);
     const int gx = ceil_div(C / kPoolS + 1, 16);  // pooled keys completed by one chunk, 16 per workgroup
     for (int c = 0; c < nch; ++c) {
-        hipError_t e = launch_chunk_setup(cu_seqlens, batch, pl.Lmax, c, C, cu_k_c, cu_q_c, valid_c, sm);
-        if (e == hipSuccess) e = launch_chunk_gather(q, cu_seqlens, cu_q_c, batch, c, C, pl.Hq, qc, sm);
+        hipError_t e = launch_chunk_setup(cu_seqlens, batch, pl.Lmax, c, C, cu_k_c, cu_q_c, valid_c,
+                                          qbase_c, sm);
         if (e == hipSuccess) e = launch_kc_build(pl, *kv, cu_k_c, valid_c, gx, sm);
-        if (e == hipSuccess) e = launch_pf_scores(pl, pf, *kv, qc, cu_q_c, cu_k_c, workspace, scores, sm);
+        if (e == hipSuccess)
+            e = launch_pf_scores(pl, pf, *kv, q, cu_q_c, cu_k_c, workspace, scores, sm, qbase_c);
         if (e == hipSuccess) e = launch_select(pl, cu_k_c, cu_q_c, C, scores, sel, cnt, sm);
         if (e == hipSuccess)
-            e = launch_pf_attend(pl, pf, *kv, qc, cu_q_c, cu_k_c, sel, cnt, oc, lc, workspace,
-                                 pf.bytes, sm);
-        if (e == hipSuccess)
-            e = launch_chunk_scatter(oc, lse ? lc : nullptr, cu_seqlens, cu_q_c, batch, c, C, pl.Hq,
-                                     out, lse, sm);
+            e = launch_pf_attend(pl, pf, *kv, q, cu_q_c, cu_k_c, sel, cnt, out, lse, workspace,
+                                 pf.bytes, sm, qbase_c);
         if (e != hipSuccess) return NOSA_ERR_HIP;
     }
     return NOSA_OK;

@@ -120,24 +120,24 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
                          int32_t* sel_out, int32_t* cnt_out, float* scores_out,
                          hipStream_t stream, const Offload* off = nullptr);
 
+// qbase (optional, device [B]): first q / out row of each sequence in place
+// of cu_q (the rows of a chunk inside a whole prompt).
 hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
                             const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
-                            void* ws, float* scores, hipStream_t stream);
+                            void* ws, float* scores, hipStream_t stream,
+                            const int32_t* qbase = nullptr);
 // ws / ws_bytes: workspace for the split attention's partials (may be null:
 // then the attention is not split).
 hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
                             const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
                             const int32_t* sel, const int32_t* cnt, float* out, float* lse,
-                            void* ws, size_t ws_bytes, hipStream_t stream);
+                            void* ws, size_t ws_bytes, hipStream_t stream,
+                            const int32_t* qbase = nullptr);
 
 // Whole-prompt prefill, chunk by chunk (nosa_prefill.hip).
 hipError_t launch_chunk_setup(const int32_t* cu, int B, int Lmax, int c, int C, int32_t* cu_k_c,
-                              int32_t* cu_q_c, int32_t* valid_c, hipStream_t stream);
-hipError_t launch_chunk_gather(const nosa_bf16* q, const int32_t* cu, const int32_t* cu_q_c, int B,
-                               int c, int C, int Hq, nosa_bf16* qc, hipStream_t stream);
-hipError_t launch_chunk_scatter(const float* oc, const float* lc, const int32_t* cu,
-                                const int32_t* cu_q_c, int B, int c, int C, int Hq, float* out,
-                                float* lse, hipStream_t stream);
+                              int32_t* cu_q_c, int32_t* valid_c, int32_t* qbase_c,
+                              hipStream_t stream);
 
 // Front end (nosa_front.hip).
 hipError_t launch_pack_qkv(int Hq, int Hkv, int hidden, const nosa_bf16* w, nosa_bf16* packed,

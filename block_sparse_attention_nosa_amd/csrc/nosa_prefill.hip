@@ -36,6 +36,7 @@ struct PfArgs {
     const int32_t* table;
     const int32_t* cu_k;
     const int32_t* cu_q;
+    const int32_t* qbase;  // [B] first q / out row of each sequence, or null: cu_q
     int max_blocks, Lmax, Lqmax, B, Hq, Hkv, G, max_qblk;
     float scale_log2;
     int rows;        // 64 * G rows per pair: row = query * G + head
@@ -80,7 +81,7 @@ __device__ __forceinline__ PfPair pf_pair(const PfArgs& a, int pair)
     int Lq = a.cu_q[P.s + 1] - a.cu_q[P.s];
     Lq = Lq < 0 ? 0 : (Lq > a.Lqmax ? a.Lqmax : Lq);
     P.Lq = Lq < P.L ? Lq : P.L;
-    P.q0 = a.cu_q[P.s];
+    P.q0 = a.qbase ? a.qbase[P.s] : a.cu_q[P.s];
     P.p0 = P.L - P.Lq + kQB * P.r;
     const int left = P.Lq - kQB * P.r;
     P.nq = left < kQB ? left : kQB;
@@ -660,9 +661,10 @@ static PfArgs pf_args(const Plan& pl, const PfPlan& pf, const nosa_paged_kv* kv,
 
 hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
                             const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
-                            void* ws, float* scores, hipStream_t stream)
+                            void* ws, float* scores, hipStream_t stream, const int32_t* qbase)
 {
     PfArgs a = pf_args(pl, pf, &kv, q, cu_q, cu_k);
+    a.qbase = qbase;
     a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + pf.off_part);
     a.colsum = reinterpret_cast<float*>(static_cast<char*>(ws) + pf.off_colsum);
     a.scores = scores;
@@ -687,9 +689,10 @@ hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_k
 hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
                             const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
                             const int32_t* sel, const int32_t* cnt, float* out, float* lse,
-                            void* ws, size_t ws_bytes, hipStream_t stream)
+                            void* ws, size_t ws_bytes, hipStream_t stream, const int32_t* qbase)
 {
     PfArgs a = pf_args(pl, pf, &kv, q, cu_q, cu_k);
+    a.qbase = qbase;
     a.sel = sel;
     a.cnt = cnt;
     a.out = out;
@@ -720,17 +723,19 @@ hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_k
 // of sequence s is its queries cC .. min(cC + C, L_s) - 1 against its first
 // min(cC + C, L_s) tokens, which is the chunk convention of the entry points
 // above with the query blocks of the whole prompt (64 from its start).  Per
-// chunk: the bookkeeping arrays, the chunk's query rows gathered into a
-// compact buffer, the pooled keys completed by its tokens, importance,
-// selection, attention, and the output rows scattered back.
+// chunk: the bookkeeping arrays, the pooled keys completed by its tokens,
+// importance, selection and attention, which read the queries from and write
+// the outputs to the prompt's own rows (qbase).
 
 // cu_k_c / cu_q_c: the chunk's context lengths and query counts as
-// cumulative arrays; valid_c: tokens already pooled (cC, capped by L_s).
+// cumulative arrays; valid_c: tokens already pooled (cC, capped by L_s);
+// qbase_c: the prompt row of the chunk's first query.
 __global__ __launch_bounds__(64) void chunk_setup_kernel(const int32_t* __restrict__ cu, int B,
                                                          int Lmax, int c, int C,
                                                          int32_t* __restrict__ cu_k_c,
                                                          int32_t* __restrict__ cu_q_c,
-                                                         int32_t* __restrict__ valid_c)
+                                                         int32_t* __restrict__ valid_c,
+                                                         int32_t* __restrict__ qbase_c)
 {
     if (threadIdx.x != 0) return;
     int k = 0, q = 0;
@@ -745,66 +750,16 @@ __global__ __launch_bounds__(64) void chunk_setup_kernel(const int32_t* __restri
         cu_k_c[s + 1] = k;
         cu_q_c[s + 1] = q;
         valid_c[s] = start;
+        qbase_c[s] = cu[s] + start;
     }
 }
 
-// Workgroup (i, s): query row cC + i of sequence s (prompt row cu[s] + cC + i)
-// to chunk row cu_q_c[s] + i, if it exists.  Rows of Hq * 128 bf16.
-__global__ __launch_bounds__(256) void chunk_gather_kernel(const uint16_t* __restrict__ q,
-                                                           const int32_t* __restrict__ cu,
-                                                           const int32_t* __restrict__ cu_q_c,
-                                                           int c, int C, int Hq,
-                                                           uint16_t* __restrict__ qc)
-{
-    const int i = blockIdx.x, s = blockIdx.y;
-    if (i >= cu_q_c[s + 1] - cu_q_c[s]) return;
-    const uint4* src = reinterpret_cast<const uint4*>(q + ((size_t)cu[s] + (size_t)c * C + i) * Hq * D);
-    uint4* dst = reinterpret_cast<uint4*>(qc + ((size_t)cu_q_c[s] + i) * Hq * D);
-    for (int x = threadIdx.x; x < Hq * D / 8; x += 256) dst[x] = src[x];
-}
-
-// The reverse for the outputs: chunk row cu_q_c[s] + i of out (Hq * 128
-// fp32) and lse (Hq fp32, when given) to prompt row cu[s] + cC + i.
-__global__ __launch_bounds__(256) void chunk_scatter_kernel(const float* __restrict__ oc,
-                                                            const float* __restrict__ lc,
-                                                            const int32_t* __restrict__ cu,
-                                                            const int32_t* __restrict__ cu_q_c,
-                                                            int c, int C, int Hq,
-                                                            float* __restrict__ out,
-                                                            float* __restrict__ lse)
-{
-    const int i = blockIdx.x, s = blockIdx.y;
-    if (i >= cu_q_c[s + 1] - cu_q_c[s]) return;
-    const size_t src_row = (size_t)cu_q_c[s] + i, dst_row = (size_t)cu[s] + (size_t)c * C + i;
-    const float4* src = reinterpret_cast<const float4*>(oc + src_row * Hq * D);
-    float4* dst = reinterpret_cast<float4*>(out + dst_row * Hq * D);
-    for (int x = threadIdx.x; x < Hq * D / 4; x += 256) dst[x] = src[x];
-    if (lse && lc)
-        for (int h = threadIdx.x; h < Hq; h += 256) lse[dst_row * Hq + h] = lc[src_row * Hq + h];
-}
-
 hipError_t launch_chunk_setup(const int32_t* cu, int B, int Lmax, int c, int C, int32_t* cu_k_c,
-                              int32_t* cu_q_c, int32_t* valid_c, hipStream_t stream)
+                              int32_t* cu_q_c, int32_t* valid_c, int32_t* qbase_c,
+                              hipStream_t stream)
 {
     hipLaunchKernelGGL(chunk_setup_kernel, dim3(1), dim3(64), 0, stream, cu, B, Lmax, c, C, cu_k_c,
-                       cu_q_c, valid_c);
-    return hipGetLastError();
-}
-
-hipError_t launch_chunk_gather(const nosa_bf16* q, const int32_t* cu, const int32_t* cu_q_c, int B,
-                               int c, int C, int Hq, nosa_bf16* qc, hipStream_t stream)
-{
-    hipLaunchKernelGGL(chunk_gather_kernel, dim3(C, B), dim3(256), 0, stream, q, cu, cu_q_c, c, C,
-                       Hq, qc);
-    return hipGetLastError();
-}
-
-hipError_t launch_chunk_scatter(const float* oc, const float* lc, const int32_t* cu,
-                                const int32_t* cu_q_c, int B, int c, int C, int Hq, float* out,
-                                float* lse, hipStream_t stream)
-{
-    hipLaunchKernelGGL(chunk_scatter_kernel, dim3(C, B), dim3(256), 0, stream, oc, lc, cu, cu_q_c,
-                       c, C, Hq, out, lse);
+                       cu_q_c, valid_c, qbase_c);
     return hipGetLastError();
 }
 

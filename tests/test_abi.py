@@ -165,7 +165,6 @@ def test_prompt_prefill_host_errors(L):
     kv = _kv()
     size = lambda ch, B=2, Lm=5000: nosa.nosa_prefill_sparse_workspace_size(p, B, Lm, ch)
     assert size(512) > 0
-    assert size(512) < size(4096)                 # scratch scales with the chunk
     assert size(8192) == size(5056)                # capped by the longest prompt (whole blocks)
     for bad in (0, -64, 100):
         with pytest.raises(nosa.NosaError) as e:

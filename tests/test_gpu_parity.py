@@ -75,6 +75,19 @@ def test_decode_step_lengths(lens):
     _full_check(c, tag=str(lens))
 
 
+@pytest.mark.parametrize("batch,hq,hkv", [(96, 16, 2), (40, 32, 8)])
+def test_decode_step_large_batch(batch, hq, hkv):
+    """Many (sequence, KV head) pairs: 192 and 320 of them, more attention
+    workgroups than the chip holds at once, so the window pages go to the
+    scoring launch or share the attention launch with longer top-k
+    workgroups."""
+    log(f"case: batch {batch}, heads {hq}/{hkv}")
+    g = torch.Generator().manual_seed(batch)
+    lens = torch.randint(900, 3200, (batch,), generator=g).tolist()
+    c = make_case(_wl(lens, hq=hq, hkv=hkv, topk=6, planted=1, seed=batch + hq))
+    _full_check(c, tag=f"batch {batch}")
+
+
 @pytest.mark.parametrize("topk", [0, 1, 3, 64, 500])
 def test_decode_step_topk(topk):
     log(f"case: topk {topk}")

@@ -97,6 +97,41 @@ void pick_split(int span, long long pairs, int max_groups, int* groups, int* rou
     *groups = ceil_div(span, W * kRounds[pick]);
 }
 
+// Split of the stand-alone attention: each pair's `span` list entries are
+// dealt round-robin to `groups` workgroups of four waves, `rounds` entries
+// per wave.  A CU streams only so many bytes at a time, so the launch time is
+// that of the busiest CU: the launch gets at most one workgroup per CU (of
+// kCusTarget), or two when one would need more than 8 entries per wave, and
+// every workgroup of a pair the same number of pages, give or take one.  (Two
+// per CU with one page per wave measured slower at 16K batch 8: twice the
+// partials for the merge.)  Batches too large for that fall back to
+// pick_split.
+void pick_attend_split(int span, long long pairs, int* groups, int* rounds)
+{
+    constexpr int kCusTarget = 256;
+    static const int kRounds[] = {1, 2, 3, 4, 6, 8};
+    if (span <= 0 || pairs <= 0) {
+        *groups = 1;
+        *rounds = 1;
+        return;
+    }
+    for (int per_cu = 1; per_cu <= 2; ++per_cu) {
+        const long long g = (long long)kCusTarget * per_cu / pairs;
+        if (g < 1) break;
+        int gmax = ceil_div(span, kStep2Waves);  // one page per wave at most
+        gmax = gmax < kMaxSplit ? gmax : kMaxSplit;
+        const int gr = (int)(g < gmax ? g : gmax);
+        const int need = ceil_div(ceil_div(span, gr), kStep2Waves);
+        for (int r : kRounds)
+            if (r >= need) {
+                *groups = gr;
+                *rounds = r;
+                return;
+            }
+    }
+    pick_split(span, pairs, kMaxSplit, groups, rounds);
+}
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -137,7 +172,7 @@ nosa_status make_plan(const nosa_params* p, int batch, int max_seqlen_k, Plan* p
     pick_split(P.top_span, npairs, kMaxSplit, &P.top_groups, &P.top_rounds);
     P.nsplit = P.top_groups + P.wslots;
     const int aspan = P.max_sel < P.max_nb ? P.max_sel : P.max_nb;
-    pick_split(aspan, (long long)batch * P.Hkv, kMaxSplit, &P.attend_groups, &P.attend_rounds);
+    pick_attend_split(aspan, (long long)batch * P.Hkv, &P.attend_groups, &P.attend_rounds);
     const int nparts = P.nsplit > P.attend_groups ? P.nsplit : P.attend_groups;
 
     const size_t B = (size_t)batch, pairs = B * P.Hkv;

@@ -19,7 +19,7 @@ constexpr int kPoolS = 16;   // pooling stride
 constexpr int kSlots = kBlock / kPoolS;  // compressed keys stored per page
 constexpr int kMaxGroup = 16;            // query heads per KV head (MFMA N = 16)
 constexpr int kMaxBlocks = 8192;         // blocks per sequence (LDS of the selector)
-constexpr int kMaxSplit = 64;            // attention partials per head (LDS of the merge)
+constexpr int kMaxSplit = 64;            // attention workgroups per pair (partials per head)
 constexpr int kMaxWindowBlocks = 128;    // window blocks (one page per wave)
 constexpr int kScoreWaves = 4;           // waves of a scoring workgroup
 constexpr int kStep2Waves = 4;           // waves of an attention workgroup

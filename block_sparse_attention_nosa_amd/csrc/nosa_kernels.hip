@@ -1013,9 +1013,11 @@ static hipError_t launch_merge(const Plan& pl, const Workspace& w, int nsplit, f
     return hipGetLastError();
 }
 
-// Attention over given block lists: workgroup = kStep2Waves (4) waves; wave
-// w handles list entries (grp*R + rr)*4 + w, rr < R, one 64-token block at a
-// time, and the workgroup stores one partial per head at slot grp.
+// Attention over given block lists: workgroup = kStep2Waves (4) waves; the
+// entries are dealt round-robin to the pair's workgroups (wave w of
+// workgroup grp takes entries (rr*4 + w)*groups + grp, rr < R), so every
+// workgroup gets the same number of pages, give or take one; one 64-token
+// block at a time, and the workgroup stores one partial per head at slot grp.
 static_assert(kStep2Waves == 4, "store_wg_partial combines four waves");
 template <int R>
 __global__ __launch_bounds__(kStep2Waves * 64) void attend_kernel(AttendArgs a)
@@ -1035,7 +1037,7 @@ __global__ __launch_bounds__(kStep2Waves * 64) void attend_kernel(AttendArgs a)
     load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-        const int idx = (grp * R + rr) * kStep2Waves + wave;
+        const int idx = (rr * kStep2Waves + wave) * a.groups + grp;
         int b = -1, page = -1;
         if (idx < n) {
             b = a.sel[(size_t)pair * a.max_sel + idx];

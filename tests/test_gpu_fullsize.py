@@ -10,8 +10,9 @@ import torch
 from block_sparse_attention_nosa_amd import synth
 from oracle import oracle as ora
 
-from helpers import (build_kc, compare_outputs, compare_scores, compare_selection, gpu_attend,
-                     gpu_decode_step, gpu_kc_logical, live_lens, log, make_case, oracle_step)
+from helpers import (TIE_BAND, build_kc, compare_outputs, compare_scores, compare_selection,
+                     gpu_attend, gpu_decode_step, gpu_kc_logical, live_lens, log, make_case,
+                     oracle_step)
 
 pytestmark = pytest.mark.gpu
 
@@ -89,3 +90,175 @@ def test_decode_b16_64k_gqa4_sampled():
             assert set(c.inp["planted"][s * w.num_kv_heads + gi]) <= set(sel.tolist())
     assert np.isfinite(g["out"]).all() and np.isfinite(g["lse"]).all()
     torch.cuda.empty_cache()
+
+
+def test_offload_b8_16k_steps():
+    """The 16K batch-8 workload over an offloaded KV cache, as the bench runs
+    it: four steps with correlated queries, each bit-identical to the step
+    over device pools, the cache holding every pick; sequences 0 and 7 of the
+    first step against the reference."""
+    import math
+    from helpers import cu_dev
+    from test_gpu_offload import Offloaded
+    from block_sparse_attention_nosa_amd import nosa
+    log("case: decode-b8-16k offloaded, 4 steps")
+    w = synth.config(2)
+    c = make_case(w, gen_device="cuda")
+    build_kc(c, [L - 1 for L in w.lens])
+    off = Offloaded(c, recent=20, cap=128)
+    off.kc.copy_(c.pg["kc_pool"])
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    qf = c.inp["q"].float()
+    B, maxL = c.B, max(w.lens) + 3
+    for t in range(4):
+        if t:
+            qf = 0.9 * qf + math.sqrt(0.19) * torch.randn(qf.shape, generator=gen, device="cuda")
+        q = qf.to(torch.bfloat16)
+        lens = [L + t for L in w.lens]
+        cu = cu_dev(lens)
+        off.fill_ring(lens)
+        res = []
+        for fn in ("dev", "off"):
+            out = torch.empty(B, 16, 128, device="cuda")
+            lse = torch.empty(B, 16, device="cuda")
+            sel = torch.empty(B, 1, 2, 80, dtype=torch.int32, device="cuda")
+            cnt = torch.empty(B, 1, 2, dtype=torch.int32, device="cuda")
+            if fn == "dev":
+                ws = torch.zeros(nosa.nosa_workspace_size(c.p, B, 1, maxL), dtype=torch.uint8,
+                                 device="cuda")
+                nosa.nosa_decode_step(c.p, c.kv, q, cu, B, maxL, out, lse, ws, sel_idx=sel,
+                                      sel_count=cnt)
+            else:
+                ws = torch.zeros(nosa.nosa_offload_workspace_size(c.p, B, maxL, 128),
+                                 dtype=torch.uint8, device="cuda")
+                nosa.nosa_offload_decode_step(c.p, off.okv, q, cu, B, maxL, out, lse, ws,
+                                              sel_idx=sel, sel_count=cnt)
+            torch.cuda.synchronize()
+            res.append((out, lse, sel, cnt))
+        for a, b in zip(res[0], res[1]):
+            assert torch.equal(a, b), t
+        sel, cnt = res[1][2].cpu().numpy(), res[1][3].cpu().numpy()
+        cmap = off.map.cpu().numpy()
+        for s in range(B):
+            nb = (lens[s] + 63) // 64
+            for g in range(2):
+                picks = {int(x) for x in sel[s, 0, g, :cnt[s, 0, g]] if x < nb - 16}
+                assert picks <= set(cmap[s, g].tolist()), (t, s, g)
+        if t == 0:
+            o = oracle_step(c, 0, seqs=[0, 7])
+            rows = [0, 7]
+            ex = compare_selection(sel[rows], cnt[rows], o["sel"], o["cnt"], o["scores"],
+                                   [lens[s] for s in rows], w)
+            if ex == 0:
+                compare_outputs(res[1][0].cpu().numpy()[rows], res[1][1].cpu().numpy()[rows],
+                                o["out"], o["lse"], "offloaded c2")
+        log(f"offloaded c2: step {t} ok")
+
+
+def test_layer_step_b8_16k_from_hidden():
+    """The 16K batch-8 workload from hidden states of width 2048 (the bench's
+    --front 2048): q, k, v within one bf16 ulp of the reference, the step on
+    them bit-identical to the decode step on the same queries, sequences 0 and
+    3 against the reference forward on the reference's q, k, v."""
+    from helpers import cu_dev
+    from test_gpu_front import _close_bf16, _slot_values
+    from block_sparse_attention_nosa_amd import nosa
+    log("case: decode-b8-16k from hidden states")
+    w = synth.config(2)
+    c = make_case(w, gen_device="cuda")
+    lens = list(w.lens)
+    build_kc(c, [L - 1 for L in lens])
+    hidden, B, maxL = 2048, c.B, max(lens)
+    gen = torch.Generator().manual_seed(11)
+    wt = (torch.randn(20 * 128, hidden, generator=gen) / hidden ** 0.5).to(torch.bfloat16)
+    x = torch.randn(B, hidden, generator=gen).to(torch.bfloat16)
+    packed = torch.empty_like(wt.cuda())
+    nosa.nosa_pack_qkv_weights(c.p, hidden, wt.cuda(), packed)
+    q_out = torch.empty(B, 16, 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(B, 16, 128, device="cuda")
+    lse = torch.empty(B, 16, device="cuda")
+    sel = torch.empty(B, 1, 2, 80, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(B, 1, 2, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(nosa.nosa_workspace_size(c.p, B, 1, maxL), dtype=torch.uint8, device="cuda")
+    cu = cu_dev(lens)
+    nosa.nosa_layer_decode_step(c.p, nosa.front_params(hidden), c.kv, x.cuda(), packed, cu, B,
+                                maxL, q_out, out, lse, ws, sel_idx=sel, sel_count=cnt)
+    torch.cuda.synchronize()
+    pos = np.array([L - 1 for L in lens], np.int32)
+    oq, ok, ov = ora.qkv_rope(c.op, synth.bits(x), synth.bits(wt), pos)
+    _close_bf16(synth.bits(q_out.cpu()), oq, "q")
+    gk, gv = _slot_values(c, lens)
+    _close_bf16(gk, ok, "k")
+    _close_bf16(gv, ov, "v")
+    # the same step on the front end's queries
+    out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+    build_kc(c, [L - 1 for L in lens])
+    nosa.nosa_decode_step(c.p, c.kv, q_out, cu, B, maxL, out2, lse2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    # the reference on its own q, k, v for sequences 0 and 3
+    rows = [0, 3]
+    k, v, cu_l = synth.packed_live(c.inp, w, 0)
+    kb, vb = synth.bits(k.cpu()).copy(), synth.bits(v.cpu()).copy()
+    cu_np = cu_l.numpy()
+    ks, vs, ls = [], [], []
+    for s in rows:
+        kk, vv = kb[cu_np[s]:cu_np[s + 1]].copy(), vb[cu_np[s]:cu_np[s + 1]].copy()
+        kk[-1], vv[-1] = ok[s], ov[s]
+        ks.append(kk)
+        vs.append(vv)
+        ls.append(lens[s])
+    o = ora.forward(c.op, oq[rows], None, np.concatenate(ks), np.concatenate(vs),
+                    synth.cu_from_lens(ls).numpy())
+    g_sel, g_cnt = sel.cpu().numpy()[rows], cnt.cpu().numpy()[rows]
+    ex = compare_selection(g_sel, g_cnt, o["sel"], o["cnt"], o["scores"], ls, w)
+    if ex == 0:
+        compare_outputs(out.cpu().numpy()[rows], lse.cpu().numpy()[rows], o["out"], o["lse"],
+                        "layer step c2")
+    log(f"layer step c2: ok (tie exemptions {ex})")
+
+
+def test_prompt_32k_sampled_query_blocks():
+    """The bench's whole-prompt workload (32768 tokens, chunks of 4096): query
+    blocks 0, 100, 300 and 511 against the reference (those without a near-tie), each solved as its own problem
+    cut after the block's last query (nothing later is visible)."""
+    from helpers import cu_dev
+    from test_gpu_prefill import check_rows, compare_out
+    from block_sparse_attention_nosa_amd import nosa
+    log("case: whole-prompt prefill, 32768 tokens, sampled query blocks")
+    L = 32768
+    w = synth.Workload(lens=[L], q_lens=[L], topk=64, planted=0, seed=1000 + L, name="prompt")
+    c = make_case(w, gen_device="cuda")
+    q = c.inp["q"]
+    out = torch.empty(L, 16, 128, device="cuda")
+    lse = torch.empty(L, 16, device="cuda")
+    ws = torch.zeros(nosa.nosa_prefill_sparse_workspace_size(c.p, 1, L, 4096), dtype=torch.uint8,
+                     device="cuda")
+    nosa.nosa_prefill_sparse(c.p, c.kv, q, cu_dev([L]), 1, L, 4096, out, lse, ws)
+    torch.cuda.synchronize()
+    go, gl = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(go).all()
+    compared = 0
+    for r in (0, 100, 300, 511):
+        p_last = 64 * r + 63
+        kk = c.inp["k"][:p_last + 1].cpu()
+        vv = c.inp["v"][:p_last + 1].cpu()
+        qq = q[64 * r:64 * r + 64].cpu()
+        o = ora.forward(c.op, synth.bits(qq), np.array([0, 64], np.int32), synth.bits(kk),
+                        synth.bits(vv), np.array([0, p_last + 1], np.int32))
+        # a near-tie at the k-th place makes either block a correct pick
+        nb = p_last // 64 + 1
+        ncand = max(nb - 16, 0)
+        tie = False
+        for g in range(2):
+            sc = np.sort(o["scores"][0, 0, g, :ncand])[::-1]
+            if 64 < ncand:
+                tie |= abs(sc[63] - sc[64]) / max(abs(sc[63]), abs(sc[64])) < TIE_BAND
+        if tie:
+            log(f"prompt 32K q-block {r}: near-tie, outputs not compared")
+            continue
+        compare_out(go[64 * r:64 * r + 64], gl[64 * r:64 * r + 64], o["out"], o["lse"],
+                    f"prompt r{r}")
+        compared += 1
+        log(f"prompt 32K q-block {r}: ok")
+    assert compared >= 2

@@ -263,7 +263,7 @@ float front_theta(const nosa_front_params* f) { return f->rope_theta > 0.f ? f->
 nosa_status check_cache(const Plan& pl, int cache_blocks)
 {
     if (cache_blocks < pl.topk || cache_blocks <= 0) return NOSA_ERR_INVALID;
-    if (cache_blocks > 256 || pl.wblocks < 1) return NOSA_ERR_UNSUPPORTED;
+    if (cache_blocks > kMaxCacheSlots || pl.wblocks < 1) return NOSA_ERR_UNSUPPORTED;
     return NOSA_OK;
 }
 

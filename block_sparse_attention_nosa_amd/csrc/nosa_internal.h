@@ -24,6 +24,7 @@ constexpr int kMaxWindowBlocks = 128;    // window blocks (one page per wave)
 constexpr int kScoreWaves = 4;           // waves of a scoring workgroup
 constexpr int kStep2Waves = 4;           // waves of an attention workgroup
 constexpr int kMaxChunks = 64;           // scoring chunks per pair (one lane each when combined)
+constexpr int kMaxCacheSlots = 256;      // block-cache slots per pair (offloaded KV): one per thread
 
 inline int num_keys(int L) { return L >= kPoolK ? (L - kPoolK) / kPoolS + 1 : 0; }
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }

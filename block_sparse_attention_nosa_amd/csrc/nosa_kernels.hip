@@ -545,7 +545,6 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
 // page "NOSA-1B 性能基准全解析" section 三.3).
 
 constexpr int kMaxRounds = 8;  // top-k blocks per wave (compiled limit of the plan)
-constexpr int kMaxCacheSlots = 256;  // block-cache slots per pair (offloaded KV): one per thread
 constexpr int kFetch = 1 << 30;      // slot_of flag: the pick is read from host memory
 
 struct TopArgs {

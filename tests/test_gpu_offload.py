@@ -202,6 +202,19 @@ def test_offload_heads_and_locality(hq, hkv, topk, locality):
     _run(c, off, 6, _queries(c, 2, 9), f"offload {hq}/{hkv} k{topk} loc{locality}")
 
 
+def test_offload_no_window_locality_only():
+    """Window 0 with a locality share: the forced set is the 8 local blocks
+    (the current token's block among them), served from the ring; the other
+    8 picks go through the cache."""
+    log("case: offload, no window, locality 0.5")
+    w = synth.Workload(lens=[3000, 4500], topk=16, window=0, planted=2, seed=17, name="offload",
+                       locality=0.5)
+    w.extra_tokens = 24
+    c = make_case(w)
+    off = Offloaded(c, recent=8, cap=8)
+    _run(c, off, 6, _queries(c, 2, 21), "offload window 0")
+
+
 def test_offload_short_sequences():
     log("case: offload short sequences (no candidates)")
     c = make_case(_wl([40, 700, 1030], seed=2, planted=0))

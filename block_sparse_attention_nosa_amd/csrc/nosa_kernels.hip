@@ -856,19 +856,21 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
             nmiss += sh.ocnt[1][w];
         }
         int rf = 0;  // rank of a free slot in eviction order
-        if (nmiss > 0 && fre) {
-            for (int u4 = 0; u4 < kMaxCacheSlots / 4; ++u4) {
-                const int4 v = sh.miss.age[u4];
-                const int u = 4 * u4;
-                rf += (v.x < age || (v.x == age && u < tid)) + (v.y < age || (v.y == age && u + 1 < tid)) +
-                      (v.z < age || (v.z == age && u + 2 < tid)) + (v.w < age || (v.w == age && u + 3 < tid));
+        if (nmiss > 0) {  // (workgroup-uniform: every pick cached skips the assignment)
+            if (fre) {
+                for (int u4 = 0; u4 < kMaxCacheSlots / 4; ++u4) {
+                    const int4 v = sh.miss.age[u4];
+                    const int u = 4 * u4;
+                    rf += (v.x < age || (v.x == age && u < tid)) + (v.y < age || (v.y == age && u + 1 < tid)) +
+                          (v.z < age || (v.z == age && u + 2 < tid)) + (v.w < age || (v.w == age && u + 3 < tid));
+                }
             }
+            if (fre && rf < nmiss) sh.miss.freeslot[rf] = tid;
+            if (mis) sh.miss.misspick[rm] = tid;
+            __syncthreads();
+            // cap >= topk, so there are at least as many free slots as misses
+            if (mis) sh.slot_of[tid] = sh.miss.freeslot[rm] | kFetch;
         }
-        if (fre && rf < nmiss) sh.miss.freeslot[rf] = tid;
-        if (mis) sh.miss.misspick[rm] = tid;
-        __syncthreads();
-        // cap >= topk, so there are at least as many free slots as misses
-        if (mis) sh.slot_of[tid] = sh.miss.freeslot[rm] | kFetch;
         if (k == 0) {
             if (tid < a.cap) {
                 const bool fill = fre && rf < nmiss;
@@ -877,7 +879,7 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
             }
             if (tid == 0 && a.fetch_out) a.fetch_out[pair] = nmiss;
         }
-        __syncthreads();  // slot_of
+        if (nmiss > 0) __syncthreads();  // slot_of (the hits' entries were set two barriers ago)
     }
     }
     AttnState A;

@@ -188,6 +188,31 @@ def compare_selection(gsel, gcnt, osel, ocnt, oscores, lens, w: synth.Workload):
     return exempt
 
 
+def check_selection_rule(gsel, gcnt, gscores, lens, w: synth.Workload):
+    """The fused step's selection is exactly the selection rule applied to its
+    own reported block scores (fp32, as the kernel compared them): the
+    top-k of the blocks before the forced ones by (score descending, block
+    ascending), then the forced blocks, ascending.  Bit-exact, ties included,
+    at any size: the selector is checked apart from the rounding of the
+    scores, which compare_scores bounds against the reference."""
+    k_loc = local_blocks(w)
+    wb = w.window // w.block_size + k_loc
+    B, _, Hkv, max_sel = gsel.shape
+    for s in range(B):
+        nb = (lens[s] + w.block_size - 1) // w.block_size
+        ncand = max(nb - wb, 0)
+        k = min(w.topk - k_loc, ncand)
+        for g in range(Hkv):
+            sc = gscores[s, 0, g, :ncand].astype(np.float32)
+            order = np.lexsort((np.arange(ncand), -sc.astype(np.float64)))[:k]
+            want = sorted(order.tolist()) + list(range(ncand, nb))
+            n = int(gcnt[s, 0, g])
+            assert n == len(want), (s, g, n, len(want))
+            got = gsel[s, 0, g, :n].tolist()
+            assert got == want, (s, g, "selection is not the rule on the step's own scores")
+            assert np.all(gsel[s, 0, g, n:] == -1), (s, g)
+
+
 def compare_outputs(gout, glse, oout, olse, what=""):
     err = np.abs(gout.astype(np.float64) - oout)
     assert np.isfinite(gout).all(), what

@@ -8,8 +8,8 @@ import torch
 from block_sparse_attention_nosa_amd import nosa, synth
 from oracle import oracle as ora
 
-from helpers import (DecodeCase, build_kc, compare_outputs, compare_scores, compare_selection,
-                     cu_dev, gpu_attend, gpu_decode_step, gpu_kc_logical, live_lens, log,
+from helpers import (DecodeCase, build_kc, check_selection_rule, compare_outputs, compare_scores,
+                     compare_selection, cu_dev, gpu_attend, gpu_decode_step, gpu_kc_logical, live_lens, log,
                      make_case, oracle_step, workspace)
 
 pytestmark = pytest.mark.gpu
@@ -31,6 +31,7 @@ def _full_check(c: DecodeCase, step=0, tag=""):
         nc = ora.num_keys(L, c.op)
         assert np.array_equal(gpu_kc_logical(c, s, nc), o["kc"][s, :, :nc]), (tag, s)
     compare_scores(g["scores"], o["scores"], lens, c.w)
+    check_selection_rule(g["sel"], g["cnt"], g["scores"], lens, c.w)
     ex = compare_selection(g["sel"], g["cnt"], o["sel"], o["cnt"], o["scores"], lens, c.w)
     # outputs: on the reference's own selection through nosa_sparse_attend, and
     # the fused step's output whenever its selection is the reference's
@@ -64,6 +65,18 @@ def test_decode_step_logits_beyond_lds(hq, hkv, L):
     log(f"case: logits beyond LDS, heads {hq}/{hkv}, L={L}")
     c = make_case(_wl([L, 1000], hq=hq, hkv=hkv, topk=32, planted=3, seed=L + hq))
     _full_check(c, tag=f"zglobal {hq}/{hkv}")
+
+
+@pytest.mark.parametrize("hq,hkv,lens", [(16, 2, [3000, 20000]), (8, 1, [70000])])
+def test_decode_step_tied_scores(hq, hkv, lens):
+    """A zero query: every logit is 0, so the block importances tie (up to
+    the rounding of their sums) and the pick between tied blocks falls to
+    the lower index; from tens to over a thousand candidate blocks (one and
+    several candidate rounds per selector thread)."""
+    log(f"case: tied scores, heads {hq}/{hkv}, lengths {lens}")
+    c = make_case(_wl(lens, hq=hq, hkv=hkv, topk=24, planted=0, seed=5))
+    c.inp["q"] = torch.zeros_like(c.inp["q"])
+    _full_check(c, tag="tied")
 
 
 @pytest.mark.parametrize("lens", [

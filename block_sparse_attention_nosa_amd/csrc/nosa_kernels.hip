@@ -294,6 +294,34 @@ __device__ void window_slot(const uint16_t* q, const uint16_t* k_pool, const uin
     }
 }
 
+// Window slots 4 j .. 4 j + 3 of pair (s, g), a page per wave (blocks
+// nb - wn + 4 j + wave, wn = min(nb, wblocks); waves past wn attend
+// nothing), the four wave states combined into the partial at slot
+// split0 + j.  All 256 threads.
+__device__ void window_group(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                             const int32_t* table, int ring, const int32_t* cu_k, int max_blocks,
+                             int Lmax, int Hq, int Hkv, int G, float scale_log2, int wblocks, int s,
+                             int g, int j, int nsplit, int split0, float* po, float2* pml,
+                             CombineLds& sh)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
+    const int L = seq_len(cu_k, s, Lmax);
+    const int nb = (L + BS - 1) / BS;
+    const int wn = nb < wblocks ? nb : wblocks;
+    const int x = 4 * j + wave;
+    AttnState A;
+    attn_init(A);
+    if (x < wn) {  // wave-uniform
+        bf16x8 qb[4];
+        load_q(q, Hq, s, g * G, G, r, kq, qb);
+        const int b = nb - wn + x;
+        const int page = window_page(table, max_blocks, ring, s, b);
+        attend_page(k_pool + ((size_t)page * Hkv + g) * BS * D, v_pool + ((size_t)page * Hkv + g) * D * BS,
+                    L - b * BS, qb, scale_log2, r, kq, A);
+    }
+    store_wg_partial(sh, A, G, (size_t)s * Hq + g * G, nsplit, split0 + j, po, pml);
+}
+
 // An empty partial (m = -inf, l = 0, o = 0) at slot `split`; all 256 threads.
 __device__ void store_empty_partial(int G, size_t head_row0, int nsplit, int split,
                                     float* __restrict__ po, float2* __restrict__ pml)
@@ -348,19 +376,22 @@ struct ScoreArgs {
     float* spill;
     float* bpart;
     int nscore;                   // scoring workgroups = pairs * nchunks
-    int wslots, wblocks, split0;  // window pages per pair, a workgroup each (0: none);
-                                  // partial slot of slot 0
+    int wslots, wblocks, split0;  // window pages per pair (0: none); partial slot of slot 0
+    int wgroups;                  // window workgroups per pair: wslots (a page each) or
+                                  // ceil(wslots / 4) (a page per wave, T = 8 only)
     int nsplit;
     float* po;
     float2* pml;
 };
 
 // Dynamic LDS of the scoring launch: a chunk's logits, [G][CK + 4] floats,
-// or a window page's exchange.
-inline size_t score_lds_bytes(int T, int G)
+// or a window page's exchange, or the four wave states of a window group.
+inline size_t score_lds_bytes(int T, int G, bool per_wave)
 {
-    const size_t z = (size_t)G * (64 * T + 4) * sizeof(float);
-    return z > sizeof(SplitPageLds) ? z : sizeof(SplitPageLds);
+    size_t z = (size_t)G * (64 * T + 4) * sizeof(float);
+    if (z < sizeof(SplitPageLds)) z = sizeof(SplitPageLds);
+    if (per_wave && z < sizeof(CombineLds)) z = sizeof(CombineLds);
+    return z;
 }
 
 template <int T>
@@ -375,11 +406,20 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
     __shared__ float wm[kScoreWaves][kMaxGroup], wsum[kScoreWaves][kMaxGroup];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
-    if ((int)blockIdx.x >= a.nscore) {  // window workgroup: one page
+    if ((int)blockIdx.x >= a.nscore) {  // window workgroup
         const int w = (int)blockIdx.x - a.nscore;
-        const int pair = w / a.wslots;
+        const int pair = w / a.wgroups;
+        if constexpr (T == 8) {
+            if (a.wgroups != a.wslots) {  // a page per wave
+                window_group(a.q, a.k_pool, a.v_pool, a.table, a.ring, a.cu_k, a.max_blocks, a.Lmax,
+                             a.Hq, a.Hkv, a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv,
+                             w % a.wgroups, a.nsplit, a.split0, a.po, a.pml,
+                             *reinterpret_cast<CombineLds*>(smem));
+                return;
+            }
+        }
         window_slot(a.q, a.k_pool, a.v_pool, a.table, a.ring, a.cu_k, a.max_blocks, a.Lmax, a.Hq,
-                    a.Hkv, a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv, w % a.wslots,
+                    a.Hkv, a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv, w % a.wgroups,
                     a.nsplit, a.split0, a.po, a.pml, *reinterpret_cast<SplitPageLds*>(smem));
         return;
     }
@@ -1124,11 +1164,12 @@ static int device_cus()
     return cached[dev];
 }
 
-// with_window: also the window workgroups (a page each; partials at slots
-// top_groups ..).
+// wgroups > 0: also the window workgroups, wgroups per pair (pl.wslots: a
+// page each; fewer: a page per wave, score_tiles = 8 only), their partials
+// at slots top_groups .. of nsplit.
 static hipError_t launch_score(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
-                               const int32_t* cu_k, const Workspace& w, int append,
-                               bool with_window, hipStream_t stream, const Offload* off = nullptr)
+                               const int32_t* cu_k, const Workspace& w, int append, int wgroups,
+                               int nsplit, hipStream_t stream, const Offload* off = nullptr)
 {
     ScoreArgs a{};
     a.q = q;
@@ -1153,14 +1194,17 @@ static hipError_t launch_score(const Plan& pl, const nosa_paged_kv& kv, const no
     a.spill = w.spill;
     a.bpart = w.bpart;
     a.nscore = pl.B * pl.Hkv * pl.nchunks;
-    a.wslots = with_window ? pl.wslots : 0;
+    a.wslots = wgroups > 0 ? pl.wslots : 0;
+    a.wgroups = wgroups > 0 ? wgroups : 1;
     a.wblocks = pl.wblocks;
     a.split0 = pl.top_groups;
-    a.nsplit = pl.nsplit;
+    a.nsplit = nsplit;
     a.po = w.po;
     a.pml = w.pml;
-    const dim3 grid(a.nscore + pl.B * pl.Hkv * a.wslots), block(kScoreWaves * 64);
-    const size_t lds = score_lds_bytes(pl.score_tiles, pl.G);  // <= 16 x 516 floats
+    const bool per_wave = wgroups > 0 && wgroups != pl.wslots;
+    if (per_wave && pl.score_tiles != 8) return hipErrorInvalidValue;
+    const dim3 grid(a.nscore + pl.B * pl.Hkv * (wgroups > 0 ? wgroups : 0)), block(kScoreWaves * 64);
+    const size_t lds = score_lds_bytes(pl.score_tiles, pl.G, per_wave);  // <= 16 x 516 floats
     switch (pl.score_tiles) {
         case 1: hipLaunchKernelGGL(score_kernel<1>, grid, block, lds, stream, a); break;
         case 2: hipLaunchKernelGGL(score_kernel<2>, grid, block, lds, stream, a); break;
@@ -1254,7 +1298,7 @@ hipError_t launch_scores_only(const Plan& pl, const nosa_paged_kv& kv, const nos
                               const int32_t* cu_k, const Workspace& w, float* scores_out,
                               hipStream_t stream)
 {
-    hipError_t e = launch_score(pl, kv, q, cu_k, w, 0, false, stream);
+    hipError_t e = launch_score(pl, kv, q, cu_k, w, 0, 0, pl.nsplit, stream);
     if (e != hipSuccess) return e;
     TopArgs a = top_args(pl, kv, q, cu_k, w);
     a.groups = 1;
@@ -1293,10 +1337,15 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
             }
         }
     }
+    // Beside the scoring, the 8-tile scoring kernel (long contexts) takes
+    // the window a page per wave: four times the bytes in flight per
+    // workgroup slot of a launch whose slots its registers limit to two per
+    // CU; the others a page per workgroup.
+    const int wg_score = wg_top > 0 || pl.wslots == 0 ? 0 : (pl.score_tiles == 8 ? per_wave : pl.wslots);
     // partials per head: the top workgroups', then one per window workgroup
     // (at most top_groups + wslots, the workspace's)
-    const int nsplit = groups + (wg_top > 0 ? wg_top : pl.wslots);
-    hipError_t e = launch_score(pl, kv, q, cu_k, w, 1, wg_top == 0, stream, off);
+    const int nsplit = groups + (wg_top > 0 ? wg_top : (wg_score > 0 ? wg_score : pl.wslots));
+    hipError_t e = launch_score(pl, kv, q, cu_k, w, 1, wg_score, nsplit, stream, off);
     if (e != hipSuccess) return e;
     TopArgs a = top_args(pl, kv, q, cu_k, w);
     if (off) {

@@ -10,8 +10,8 @@ import torch
 from block_sparse_attention_nosa_amd import synth
 from oracle import oracle as ora
 
-from helpers import (TIE_BAND, build_kc, compare_outputs, compare_scores, compare_selection,
-                     gpu_attend, gpu_decode_step, gpu_kc_logical, live_lens, log, make_case,
+from helpers import (TIE_BAND, build_kc, check_selection_rule, compare_outputs, compare_scores,
+                     compare_selection, gpu_attend, gpu_decode_step, gpu_kc_logical, live_lens, log, make_case,
                      oracle_step)
 
 pytestmark = pytest.mark.gpu
@@ -88,6 +88,25 @@ def test_decode_b16_64k_gqa4_sampled():
             assert np.all(np.diff(sel) > 0) and sel[-1] == nb - 1
             assert set(range(nb - 16, nb)) <= set(sel.tolist())
             assert set(c.inp["planted"][s * w.num_kv_heads + gi]) <= set(sel.tolist())
+    assert np.isfinite(g["out"]).all() and np.isfinite(g["lse"]).all()
+    torch.cuda.empty_cache()
+
+
+def test_decode_window_beside_long_scoring_varlen():
+    """32/8 heads, batch 16, long and short sequences mixed: the attention
+    launch is full, so the window pages ride in the scoring launch, a page
+    per wave of four-page workgroups (long contexts use the 8-tile scoring
+    kernel); the short sequences leave window waves and whole window
+    workgroups empty.  Sequences 0 and 12..15 against the reference, every
+    sequence's selection against the rule on its own scores."""
+    lens = [40000] * 12 + [100, 700, 1000, 2100]
+    log(f"case: window beside the scoring, lengths {lens}")
+    w = synth.Workload(lens=lens, num_q_heads=32, num_kv_heads=8, topk=96, planted=2, seed=21,
+                       window=1024, name="t")
+    c = make_case(w, gen_device="cuda")
+    build_kc(c, [L - 1 for L in w.lens])
+    g, _ = _check_step(c, 0, seqs=[0, 12, 13, 14, 15], tag="window-beside-scoring")
+    check_selection_rule(g["sel"], g["cnt"], g["scores"], live_lens(c, 0), w)
     assert np.isfinite(g["out"]).all() and np.isfinite(g["lse"]).all()
     torch.cuda.empty_cache()
 

@@ -87,11 +87,16 @@ __device__ __forceinline__ uint16_t* kc_page(uint16_t* kc_pool, const int32_t* t
 // Length of sequence s clamped to [0, Lmax], Lmax = min(host bound, what a
 // block-table row addresses): a device length above the host-side bound can
 // then never index past the table, the workspace rows or the LDS arrays.
-__device__ __forceinline__ int seq_len(const int32_t* cu_k, int s, int Lmax)
+__device__ __forceinline__ int seq_len_of(int cu0, int cu1, int Lmax)
 {
-    int L = cu_k[s + 1] - cu_k[s];
+    int L = cu1 - cu0;
     L = L < 0 ? 0 : L;
     return L < Lmax ? L : Lmax;
+}
+
+__device__ __forceinline__ int seq_len(const int32_t* cu_k, int s, int Lmax)
+{
+    return seq_len_of(cu_k[s], cu_k[s + 1], Lmax);
 }
 
 // ------------------------------------------------------ block attention ---

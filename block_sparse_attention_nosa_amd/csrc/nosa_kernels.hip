@@ -620,8 +620,8 @@ struct TopArgs {
     int wslots;          // window slots (pages) per pair in this launch (0: none)
     int wgroups;         // window workgroups per pair: wslots or ceil(wslots / 4)
     int nsplit;          // partial slots per head
-    int ntop, nwin;      // top / window workgroups of the launch
-    int tpx, wpx;        // top / window workgroups per XCD
+    int4 disp;           // top / window workgroups per XCD, top / window workgroups of the
+                         // launch (one argument, so one scalar load gates the early exit)
     int scores_only;     // importance only (no selection, no attention)
     float* scores_out;   // [pairs][max_nb] or null (workgroup 0 of a pair writes)
     int32_t* sel_out;    // [pairs][max_sel] or null (workgroup 0 of a pair writes)
@@ -695,6 +695,15 @@ __device__ __forceinline__ float block_importance(int b, int nc, int cb_shift, i
     return jlo <= jhi ? sum / (float)(jhi - jlo + 1) : -INFINITY;
 }
 
+// Global-memory (address space 1) views of the chunk partials: a kernel
+// argument pointer that has passed through an asm statement is otherwise a
+// flat pointer, and flat loads also hold up every wait for scalar loads.
+typedef float gf2 __attribute__((ext_vector_type(2)));
+typedef float gf4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) gf2* GlobalF2;
+typedef const __attribute__((address_space(1))) float* GlobalF1;
+typedef const __attribute__((address_space(1))) gf4* GlobalF4;
+
 // KRB: candidate rounds of 256 blocks whose importance stays in registers
 // (1, 2, 4 or 8; blocks past KRB * 256 go through LDS, only when KRB = 8).
 // GP4: float4 loads per block of the partial row (G <= 4 GP4).
@@ -719,9 +728,22 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     // a pair (which read the same partials) share an L2, and the CUs each
     // get one top workgroup before any gets a second.
     const int xcd = (int)(blockIdx.x % 8), pos = (int)(blockIdx.x / 8);
-    const bool window = pos >= a.tpx;
-    const int lid = window ? xcd * a.wpx + (pos - a.tpx) : xcd * a.tpx + pos;
-    if (lid >= (window ? a.nwin : a.ntop)) return;  // whole workgroup
+    int4 disp = a.disp;  // tpx, wpx, ntop, nwin
+    // The empty asm takes the four counts as scalar registers, so they are
+    // read together, in the one batch of argument loads that gates the
+    // early exit, instead of one dependent scalar load after another (not
+    // volatile: such an asm touches no memory, so the uniform loads after
+    // it stay scalar loads).
+    asm("" : "+s"(disp.x), "+s"(disp.y), "+s"(disp.z), "+s"(disp.w));
+    const bool window = pos >= disp.x;
+    const int lid = window ? xcd * disp.y + (pos - disp.x) : xcd * disp.x + pos;
+    if (lid >= (window ? disp.w : disp.z)) return;  // whole workgroup
+    // the chunk partials' addresses, in the argument batch that follows (a
+    // load of their own later would also wait for the sequence bounds)
+    GlobalF2 cml = (GlobalF2)a.cml;
+    GlobalF1 spill = (GlobalF1)a.spill;
+    GlobalF4 bpart4 = (GlobalF4)a.bpart;
+    asm("" : "+s"(cml), "+s"(spill), "+s"(bpart4));
     if (window && a.wgroups == a.wslots) {  // one window page, the four waves together
         const int pair = lid / a.wgroups;
         window_slot(a.q, a.wk, a.wv, a.table, a.ring, a.cu_k, a.max_blocks, a.Lmax, a.Hq, a.Hkv,
@@ -735,15 +757,19 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     const int pair = window ? lid / a.wgroups : lid / a.groups;
     const int k = window ? lid % a.wgroups : lid % a.groups;
     const int s = pair / a.Hkv, g = pair % a.Hkv;
-    const int L = seq_len(a.cu_k, s, a.Lmax);
-    const int nb = (L + BS - 1) / BS;
-    const int nc = dev_num_keys(L);
     const int32_t* trow = a.table + (size_t)s * a.max_blocks;
     const size_t head_row0 = (size_t)s * a.Hq + g * a.G;
+    // the sequence's bounds, read here (scalar loads) and used only after
+    // the top workgroups' first loads are issued
+    const int cu0 = a.cu_k[s], cu1 = a.cu_k[s + 1];
 
     bf16x8 qb[4];
     int rounds = 1, lbase = 0;
+    int L, nb, nc;  // sequence length, its blocks and pooled keys
     if (window) {
+        L = seq_len_of(cu0, cu1, a.Lmax);
+        nb = (L + BS - 1) / BS;
+        nc = dev_num_keys(L);
         // this wave's window page as a one-entry list; the attention below
         // is the top workgroups' own
         const int wn = nb < a.wblocks ? nb : a.wblocks;
@@ -759,11 +785,10 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     int32_t* spg = reinterpret_cast<int32_t*>(smem);  // block-table row
     float* sI = reinterpret_cast<float*>(smem + ((size_t)a.max_nb * sizeof(int32_t) + 15) / 16 * 16);
     const int CK = a.chunk_keys;
-    const int nvalid = (nc + CK - 1) / CK;  // chunks holding keys of this pair, <= 64
 
     // Loads, in the order they are needed (they complete in order, so each
     // wait below covers only what was issued before), none of them waiting
-    // for the sequence length: chunk partials (lane = chunk, heads wave + 4u;
+    // for the sequence length (read after them): chunk partials (lane = chunk, heads wave + 4u;
     // chunks past the pair's last are masked later), this thread's importance
     // partials and block-table entries, the query.  Every address is clamped
     // in range, so no load needs a branch.
@@ -773,16 +798,20 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     for (int u = 0; u < 4; ++u) {
         const int h = wave + 4 * u < a.G ? wave + 4 * u : a.G - 1;
         const size_t o = ((size_t)pair * a.G + h) * a.nchunks + (lane < a.nchunks ? lane : 0);
-        cv[u] = a.cml[o];
-        sv[u] = a.spill[o];
+        const gf2 c2 = cml[o];
+        cv[u] = make_float2(c2.x, c2.y);
+        sv[u] = spill[o];
     }
     float4 bv[KRB][GP4];
 #pragma unroll
     for (int i = 0; i < KRB; ++i) {
         const int b = i * NT + tid < a.nbk ? i * NT + tid : a.nbk - 1;
-        const float4* src = reinterpret_cast<const float4*>(a.bpart + ((size_t)pair * a.nbk + b) * a.gp);
+        GlobalF4 src = bpart4 + ((size_t)pair * a.nbk + b) * a.gp / 4;  // gp is a multiple of 4
 #pragma unroll
-        for (int u = 0; u < GP4; ++u) bv[i][u] = src[u * 4 < a.gp ? u : 0];
+        for (int u = 0; u < GP4; ++u) {
+            const gf4 x = src[u * 4 < a.gp ? u : 0];
+            bv[i][u] = make_float4(x.x, x.y, x.z, x.w);
+        }
     }
     int tv[KRB];
 #pragma unroll
@@ -796,6 +825,13 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
         }
         sh.slot_of[tid] = -1;
     }
+    // nothing above waits for the length, which arrives while those loads
+    // are in flight
+    __builtin_amdgcn_sched_barrier(0);
+    L = seq_len_of(cu0, cu1, a.Lmax);
+    nb = (L + BS - 1) / BS;
+    nc = dev_num_keys(L);
+    const int nvalid = (nc + CK - 1) / CK;  // chunks holding keys of this pair, <= 64
     select_lds_clear<NT>(sh.sel);
     // per-head log2-sum-exp2 over the chunks, then each chunk's weight
 #pragma unroll
@@ -983,7 +1019,9 @@ struct AttendArgs {
 // out = sum_i 2^(m_i - M) o_i / L and lse = (M + log2 L) ln 2, with
 // M = max_i m_i and L = sum_i 2^(m_i - M) l_i (empty rows: out 0, lse -inf).
 // One workgroup of 128 threads per row, thread c = channel c; partials are
-// taken 32 at a time with every load of a batch in flight, the running
+// taken 32 at a time with every load of a batch in flight (the (m, l) pairs
+// a lane each, their maximum and weighted sum by wave reductions, the
+// weights read back lane by lane for the channel sums), the running
 // (M, L, acc) rescaled between batches.  A launch of its own, so the
 // partials of every workgroup of the step are complete when it starts.
 // With offloaded KV the row of each group's first head also installs the
@@ -1000,41 +1038,43 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ po
                                                     int32_t* __restrict__ map,
                                                     int32_t* __restrict__ used, int cap, int G)
 {
+    // the empty asm reads every argument in one batch of scalar loads (not
+    // the count first for the loop test, then the rest); as its operands
+    // are inputs only, the pointers stay global ones
+    asm volatile("" ::"s"(po), "s"(pml), "s"(nsplit), "s"(out), "s"(lse), "s"(map_next),
+                 "s"(used_next), "s"(map), "s"(used), "s"(cap), "s"(G));
     const size_t row = blockIdx.x;
-    const int c = threadIdx.x;
-    if (map && row % G == 0) {
-        const size_t pair = row / G;
-        for (int x = c; x < cap; x += D) {
-            map[pair * cap + x] = map_next[pair * cap + x];
-            used[pair * cap + x] = used_next[pair * cap + x];
-        }
-    }
+    const int c = threadIdx.x, lane = c & 63;
     const float2* ml = pml + row * nsplit;
     const float* op = po + row * nsplit * D + c;
     float M = -INFINITY, L = 0.f, acc = 0.f;
 #pragma unroll 1
     for (int i0 = 0; i0 < nsplit; i0 += kMergeBatch) {
-        float2 v[kMergeBatch];
+        // partial i0 + u of the batch: its (m, l) in lane u (and u + 32) of
+        // each wave, its o value of channel c in o[u]; straight-line loads,
+        // indexes past nsplit read the last partial again and are masked
+        const int iu = i0 + (lane & (kMergeBatch - 1));
+        float2 v = ml[iu < nsplit ? iu : nsplit - 1];
         float o[kMergeBatch];
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) {
-            const bool ok = i0 + u < nsplit;
-            v[u] = ok ? ml[i0 + u] : make_float2(-INFINITY, 0.f);
-            o[u] = ok ? op[(size_t)(i0 + u) * D] : 0.f;
+        for (int u = 0; u < kMergeBatch; ++u) o[u] = op[(size_t)(i0 + u < nsplit ? i0 + u : nsplit - 1) * D];
+        if (iu >= nsplit) v = make_float2(-INFINITY, 0.f);
+        if (i0 == 0 && map && row % G == 0) {  // after the first loads are in flight
+            const size_t pair = row / G;
+            for (int x = c; x < cap; x += D) {
+                map[pair * cap + x] = map_next[pair * cap + x];
+                used[pair * cap + x] = used_next[pair * cap + x];
+            }
         }
-        float Mb = M;
-#pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) Mb = fmaxf(Mb, v[u].x);
+        const float Mb = fmaxf(M, wave_max_f(v.x));
         if (Mb == -INFINITY) continue;
         const float r = M == -INFINITY ? 0.f : fexp2(M - Mb);
-        L *= r;
+        const float w = v.x == -INFINITY ? 0.f : fexp2(v.x - Mb);  // 0 for masked partials
+        L = L * r + wave_sum_f(lane < kMergeBatch ? w * v.y : 0.f);
         acc *= r;
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) {
-            const float w = v[u].x == -INFINITY ? 0.f : fexp2(v[u].x - Mb);
-            L += w * v[u].y;
-            acc += w * o[u];
-        }
+        for (int u = 0; u < kMergeBatch; ++u)
+            acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u)) * o[u];
         M = Mb;
     }
     const bool empty = !(L > 0.f);
@@ -1279,11 +1319,9 @@ static hipError_t launch_top(const Plan& pl, TopArgs a, hipStream_t stream)
     const int krb = nr <= 1 ? 1 : nr <= 2 ? 2 : nr <= 4 ? 4 : 8;
     const size_t lds = top_lds_bytes(pl.max_nb, krb);
     if (lds + sizeof(TopLds) > device_lds_limit()) return hipErrorInvalidValue;
-    a.ntop = pl.B * pl.Hkv * a.groups;
-    a.nwin = pl.B * pl.Hkv * a.wgroups;
-    a.tpx = ceil_div(a.ntop, 8);
-    a.wpx = ceil_div(a.nwin, 8);
-    const dim3 grid(8 * (a.tpx + a.wpx));
+    const int ntop = pl.B * pl.Hkv * a.groups, nwin = pl.B * pl.Hkv * a.wgroups;
+    a.disp = make_int4(ceil_div(ntop, 8), ceil_div(nwin, 8), ntop, nwin);
+    const dim3 grid(8 * (a.disp.x + a.disp.y));
     const int gp4 = pl.gp / 4;
     switch (krb) {
         case 1: launch_top_k<1>(grid, lds, gp4, a, stream); break;

@@ -406,8 +406,13 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
     __shared__ float wm[kScoreWaves][kMaxGroup], wsum[kScoreWaves][kMaxGroup];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, kq = lane >> 4;
-    if ((int)blockIdx.x >= a.nscore) {  // window workgroup
-        const int w = (int)blockIdx.x - a.nscore;
+    // The counts that place the workgroup and its first loads, as scalar
+    // registers through an empty asm: read in the first batch of argument
+    // loads, not in later batches that each wait for the one before.
+    int nscore = a.nscore, nchunks = a.nchunks, Hkv = a.Hkv, max_blocks = a.max_blocks;
+    asm("" : "+s"(nscore), "+s"(nchunks), "+s"(Hkv), "+s"(max_blocks));
+    if ((int)blockIdx.x >= nscore) {  // window workgroup
+        const int w = (int)blockIdx.x - nscore;
         const int pair = w / a.wgroups;
         if constexpr (T == 8) {
             if (a.wgroups != a.wslots) {  // a page per wave
@@ -423,10 +428,10 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
                     a.nsplit, a.split0, a.po, a.pml, *reinterpret_cast<SplitPageLds*>(smem));
         return;
     }
-    const int pair = blockIdx.x / a.nchunks, c = blockIdx.x % a.nchunks;
-    const int s = pair / a.Hkv, g = pair % a.Hkv;
+    const int pair = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+    const int s = pair / Hkv, g = pair % Hkv;
     const int k0 = c * CK;
-    const int32_t* trow = a.table + (size_t)s * a.max_blocks;
+    const int32_t* trow = a.table + (size_t)s * max_blocks;
     const int kw = k0 + wave * T * 16;  // first key of this wave
     // Table entries of this lane's keys, issued before the length is known
     // (the row has max_blocks entries; those past the sequence may hold
@@ -436,12 +441,16 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const int blk = (kw + t * 16 + r) / SL;
-        pg[t] = trow[blk < a.max_blocks ? blk : a.max_blocks - 1];
+        pg[t] = trow[blk < max_blocks ? blk : max_blocks - 1];
     }
     bf16x8 qb[4];
     load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
     const int L = seq_len(a.cu_k, s, a.Lmax);
     const int nc = dev_num_keys(L);
+    // The table entries are taken as an operand here so that their loads
+    // stay ahead of the exit test below (they would otherwise move after
+    // it, one more memory round trip before the keys can be requested).
+    asm volatile("" ::"v"(pg[0]));
     if (k0 >= nc) return;  // the pair has no key in this chunk (whole workgroup)
     uint4 kv[T][4];
 #pragma unroll

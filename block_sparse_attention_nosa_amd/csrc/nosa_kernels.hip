@@ -712,6 +712,7 @@ typedef float gf4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(1))) gf2* GlobalF2;
 typedef const __attribute__((address_space(1))) float* GlobalF1;
 typedef const __attribute__((address_space(1))) gf4* GlobalF4;
+typedef const __attribute__((address_space(1))) int32_t* GlobalI1;
 
 // KRB: candidate rounds of 256 blocks whose importance stays in registers
 // (1, 2, 4 or 8; blocks past KRB * 256 go through LDS, only when KRB = 8).
@@ -1113,32 +1114,54 @@ template <int R>
 __global__ __launch_bounds__(kStep2Waves * 64) void attend_kernel(AttendArgs a)
 {
     __shared__ CombineLds sh;
-    const int pair = blockIdx.x / a.groups, grp = blockIdx.x % a.groups;
-    const int s = pair / a.Hkv, g = pair % a.Hkv;
+    // the placement counts and the index arrays in the first batch of
+    // argument loads (an empty asm that takes them as scalar registers; the
+    // arrays as global-memory pointers, so their loads stay global ones)
+    int groups = a.groups, Hkv = a.Hkv, max_sel = a.max_sel, Lmax = a.Lmax, max_blocks = a.max_blocks;
+    GlobalI1 cuk = (GlobalI1)a.cu_k, cnt = (GlobalI1)a.cnt, sel = (GlobalI1)a.sel,
+             table = (GlobalI1)a.table;
+    asm("" : "+s"(groups), "+s"(Hkv), "+s"(max_sel), "+s"(Lmax), "+s"(max_blocks), "+s"(cuk),
+        "+s"(cnt), "+s"(sel), "+s"(table));
+    const int pair = blockIdx.x / groups, grp = blockIdx.x % groups;
+    const int s = pair / Hkv, g = pair % Hkv;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, kq = lane >> 4;
-    const int L = seq_len(a.cu_k, s, a.Lmax);
-    const int nb = (L + BS - 1) / BS;
-    const int32_t* trow = a.table + (size_t)s * a.max_blocks;
-    const int n = min(a.cnt[pair], a.max_sel);
-    AttnState A;
-    attn_init(A);
+    // The query and every round's list entry are requested with the length
+    // and the count (indexes clamped into the row, checked once all are
+    // in), then every round's table entry: two memory round trips before
+    // the first page, whatever R.
     bf16x8 qb[4];
     load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
+    GlobalI1 srow = sel + (size_t)pair * max_sel;
+    int bl[R];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-        const int idx = (rr * kStep2Waves + wave) * a.groups + grp;
-        int b = -1, page = -1;
-        if (idx < n) {
-            b = a.sel[(size_t)pair * a.max_sel + idx];
-            if (b >= 0 && b < nb) page = trow[b];
-        }
-        if (b < 0 || b >= nb) continue;
+        const int idx = (rr * kStep2Waves + wave) * groups + grp;
+        bl[rr] = srow[idx < max_sel ? idx : max_sel - 1];
+    }
+    const int cu0 = cuk[s], cu1 = cuk[s + 1], npick = cnt[pair];  // one wait for the three
+    const int L = seq_len_of(cu0, cu1, Lmax);
+    const int nb = (L + BS - 1) / BS;
+    GlobalI1 trow = table + (size_t)s * max_blocks;
+    const int n = min(npick, max_sel);
+    int pl[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+        const int idx = (rr * kStep2Waves + wave) * groups + grp;
+        if (idx >= n || bl[rr] < 0 || bl[rr] >= nb) bl[rr] = -1;  // no page this round
+        pl[rr] = trow[bl[rr] >= 0 ? bl[rr] : 0];
+    }
+    AttnState A;
+    attn_init(A);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+        const int b = bl[rr], page = pl[rr];
+        if (b < 0) continue;
         const uint16_t* kb = a.k_pool + ((size_t)page * a.Hkv + g) * BS * D;
         const uint16_t* vb = a.v_pool + ((size_t)page * a.Hkv + g) * D * BS;
         attend_page(kb, vb, L - b * BS, qb, a.scale_log2, r, kq, A);
     }
-    store_wg_partial(sh, A, a.G, (size_t)s * a.Hq + g * a.G, a.groups, grp, a.po, a.pml);
+    store_wg_partial(sh, A, a.G, (size_t)s * a.Hq + g * a.G, groups, grp, a.po, a.pml);
 }
 
 // ------------------------------------------------------ select (alone) ---

@@ -298,7 +298,8 @@ __device__ void window_slot(const uint16_t* q, const uint16_t* k_pool, const uin
 // nb - wn + 4 j + wave, wn = min(nb, wblocks); waves past wn attend
 // nothing), the four wave states combined into the partial at slot
 // split0 + j.  All 256 threads.
-__device__ void window_group(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+__device__ __forceinline__ void window_group(const uint16_t* q, const uint16_t* k_pool,
+                                             const uint16_t* v_pool,
                              const int32_t* table, int ring, const int32_t* cu_k, int max_blocks,
                              int Lmax, int Hq, int Hkv, int G, float scale_log2, int wblocks, int s,
                              int g, int j, int nsplit, int split0, float* po, float2* pml,
@@ -375,7 +376,7 @@ struct ScoreArgs {
     float2* cml;
     float* spill;
     float* bpart;
-    int nscore;                   // scoring workgroups = pairs * nchunks
+    int nscore;                   // scoring workgroups = pairs * ceil(nchunks / CPW)
     int wslots, wblocks, split0;  // window pages per pair (0: none); partial slot of slot 0
     int wgroups;                  // window workgroups per pair: wslots (a page each) or
                                   // ceil(wslots / 4) (a page per wave, T = 8 only)
@@ -394,8 +395,31 @@ inline size_t score_lds_bytes(int T, int G, bool per_wave)
     return z;
 }
 
+// This lane's pooled keys of T tiles of 16 (tile t: page pgj[t], keys
+// kwj + 16 t + r), as MFMA operands; page ids clamped into the pool.
 template <int T>
-__global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
+__device__ __forceinline__ void load_chunk_keys(uint4 (&kv)[T][4], const int (&pgj)[T], int kwj,
+                                                const uint16_t* kc_pool, int num_pages, int Hkv,
+                                                int g, int r, int kq)
+{
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int p = min(max(pgj[t], 0), num_pages - 1);
+        const uint16_t* kp = kc_pool + ((size_t)p * Hkv + g) * SL * D;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) kv[t][st] = ldg16(kp + kc_chunk((kwj + t * 16 + r) % SL, st * 4 + kq));
+    }
+}
+
+// CPW: chunks per scoring workgroup (1 or 2; 2 only with T = 8).  With two,
+// the second chunk's keys are requested into the key registers as soon as
+// the first chunk's MFMAs have read them, so they stream while the first
+// chunk's logits go through LDS and its partials are stored: a long context
+// is then scored in one dispatch round of workgroups whose loads keep HBM
+// busy, instead of two rounds that all load, then all compute, together
+// (and two such workgroups must fit on a CU: the launch bounds say so).
+template <int T, int CPW>
+__global__ __launch_bounds__(kScoreWaves * 64, CPW) void score_kernel(ScoreArgs a)
 {
     constexpr int CK = 64 * T;  // keys per chunk: kScoreWaves waves x T tiles x 16
     constexpr int CB = CK / 4;  // blocks per chunk
@@ -428,21 +452,23 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
                     a.nsplit, a.split0, a.po, a.pml, *reinterpret_cast<SplitPageLds*>(smem));
         return;
     }
-    const int pair = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+    const int cpp = (nchunks + CPW - 1) / CPW;  // scoring workgroups per pair
+    const int pair = blockIdx.x / cpp, c0 = (blockIdx.x % cpp) * CPW;
     const int s = pair / Hkv, g = pair % Hkv;
-    const int k0 = c * CK;
     const int32_t* trow = a.table + (size_t)s * max_blocks;
-    const int kw = k0 + wave * T * 16;  // first key of this wave
-    // Table entries of this lane's keys, issued before the length is known
-    // (the row has max_blocks entries; those past the sequence may hold
-    // anything, so the page ids are clamped into the pool: their keys are
-    // masked), and the query.
+    // Table entries of this lane's keys in a chunk (the row has max_blocks
+    // entries; those past the sequence may hold anything, so the page ids
+    // are clamped into the pool: their keys are masked).  The first chunk's
+    // are issued before the length is known, with the query.
     int pg[T];
+    auto table_entries = [&](int cj) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int blk = (kw + t * 16 + r) / SL;
-        pg[t] = trow[blk < max_blocks ? blk : max_blocks - 1];
-    }
+        for (int t = 0; t < T; ++t) {
+            const int blk = (cj * CK + wave * T * 16 + t * 16 + r) / SL;
+            pg[t] = trow[blk < max_blocks ? blk : max_blocks - 1];
+        }
+    };
+    table_entries(c0);
     bf16x8 qb[4];
     load_q(a.q, a.Hq, s, g * a.G, a.G, r, kq, qb);
     const int L = seq_len(a.cu_k, s, a.Lmax);
@@ -451,17 +477,17 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
     // stay ahead of the exit test below (they would otherwise move after
     // it, one more memory round trip before the keys can be requested).
     asm volatile("" ::"v"(pg[0]));
-    if (k0 >= nc) return;  // the pair has no key in this chunk (whole workgroup)
+    if (c0 * CK >= nc) return;  // the pair has no key in these chunks (whole workgroup)
     uint4 kv[T][4];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int p = min(max(pg[t], 0), a.num_pages - 1);
-        const uint16_t* kp = a.kc_pool + ((size_t)p * a.Hkv + g) * SL * D;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) kv[t][st] = ldg16(kp + kc_chunk((kw + t * 16 + r) % SL, st * 4 + kq));
-    }
+    load_chunk_keys<T>(kv, pg, c0 * CK + wave * T * 16, a.kc_pool, a.num_pages, Hkv, g, r, kq);
     const int jn = nc - 1;
     const bool appending = a.append && L >= kPoolK && (L - kPoolK) % kPoolS == 0;
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+    const int c = c0 + j;
+    const int k0 = c * CK;
+    if (c >= nchunks || k0 >= nc) break;  // (whole workgroup)
+    const int kw = k0 + wave * T * 16;  // first key of this wave
     if (appending && jn >= kw && jn < kw + T * 16) {  // wave-uniform
         const int tr = lane >> 4, cc = lane & 15;  // 4 token phases x 16 channel chunks
         // tokens 16 jn + tr + 4i, i < 8
@@ -487,11 +513,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
         }
         const uint4 appkey = round8(acc);  // channels 8cc .. 8cc+7, same in every phase
         const int ta = (jn - kw) / 16, ra = (jn - kw) % 16;
-        int ppg = 0;
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-            if (t == ta) ppg = pg[t];
-        ppg = __shfl(ppg, ra);  // lane (ra, 0) holds key jn's page
+        const int jb = jn / SL;  // key jn's page
+        const int ppg = trow[jb < max_blocks ? jb : max_blocks - 1];
         if (tr == 0)
             *reinterpret_cast<uint4*>(a.kc_pool + ((size_t)ppg * a.Hkv + g) * SL * D +
                                       kc_chunk(jn % SL, cc)) = appkey;
@@ -525,6 +548,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
             *reinterpret_cast<float4*>(zl + r * ZS + (wave * T + t) * 16 + kq * 4) =
                 make_float4(zv[t][0], zv[t][1], zv[t][2], zv[t][3]);
     }
+    const bool next = j + 1 < CPW && c + 1 < nchunks && k0 + CK < nc;  // (whole workgroup)
+    if (next) table_entries(c + 1);  // the next chunk's, now that kv is free
     if (m_l != -INFINITY) {
 #pragma unroll
         for (int t = 0; t < T; ++t)
@@ -543,6 +568,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
         wsum[wave][r] = s_l;
     }
     __syncthreads();
+    if (next)  // its keys stream while this chunk's block sums and partials are made
+        load_chunk_keys<T>(kv, pg, k0 + CK + wave * T * 16, a.kc_pool, a.num_pages, Hkv, g, r, kq);
     // per (block, head): the block's keys in this chunk, relative to the
     // chunk maximum (finite: key k0 exists for every head)
     const size_t prow = (size_t)pair * a.nbk + (size_t)c * CB;
@@ -572,7 +599,10 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(ScoreArgs a)
             if (wsum[w][tid] > 0.f) sum += wsum[w][tid] * fexp2(wm[w][tid] - m);
         a.cml[crow + (size_t)tid * a.nchunks] = make_float2(m, sum);
     }
+    if (j + 1 < CPW) __syncthreads();  // zl, wm and wsum are rewritten by the next chunk
+    }
 }
+
 
 // ----------------------------------------------- selection + attention ---
 //
@@ -1265,7 +1295,11 @@ static hipError_t launch_score(const Plan& pl, const nosa_paged_kv& kv, const no
     a.cml = w.cml;
     a.spill = w.spill;
     a.bpart = w.bpart;
-    a.nscore = pl.B * pl.Hkv * pl.nchunks;
+    // two chunks per workgroup (8 tiles only) when the chunks would
+    // otherwise take more than one dispatch round of two workgroups per CU
+    const long long pairs = (long long)pl.B * pl.Hkv;
+    const int cpw = pl.score_tiles == 8 && pairs * pl.nchunks > 2LL * device_cus() ? 2 : 1;
+    a.nscore = (int)(pairs * ceil_div(pl.nchunks, cpw));
     a.wslots = wgroups > 0 ? pl.wslots : 0;
     a.wgroups = wgroups > 0 ? wgroups : 1;
     a.wblocks = pl.wblocks;
@@ -1278,10 +1312,13 @@ static hipError_t launch_score(const Plan& pl, const nosa_paged_kv& kv, const no
     const dim3 grid(a.nscore + pl.B * pl.Hkv * (wgroups > 0 ? wgroups : 0)), block(kScoreWaves * 64);
     const size_t lds = score_lds_bytes(pl.score_tiles, pl.G, per_wave);  // <= 16 x 516 floats
     switch (pl.score_tiles) {
-        case 1: hipLaunchKernelGGL(score_kernel<1>, grid, block, lds, stream, a); break;
-        case 2: hipLaunchKernelGGL(score_kernel<2>, grid, block, lds, stream, a); break;
-        case 4: hipLaunchKernelGGL(score_kernel<4>, grid, block, lds, stream, a); break;
-        default: hipLaunchKernelGGL(score_kernel<8>, grid, block, lds, stream, a); break;
+        case 1: hipLaunchKernelGGL((score_kernel<1, 1>), grid, block, lds, stream, a); break;
+        case 2: hipLaunchKernelGGL((score_kernel<2, 1>), grid, block, lds, stream, a); break;
+        case 4: hipLaunchKernelGGL((score_kernel<4, 1>), grid, block, lds, stream, a); break;
+        default:
+            if (cpw == 2) hipLaunchKernelGGL((score_kernel<8, 2>), grid, block, lds, stream, a);
+            else hipLaunchKernelGGL((score_kernel<8, 1>), grid, block, lds, stream, a);
+            break;
     }
     return hipGetLastError();
 }

@@ -1167,7 +1167,7 @@ __global__ __launch_bounds__(kStep2Waves * 64) void attend_kernel(AttendArgs a)
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
         const int idx = (rr * kStep2Waves + wave) * groups + grp;
-        bl[rr] = srow[idx < max_sel ? idx : max_sel - 1];
+        bl[rr] = max_sel > 0 ? srow[idx < max_sel ? idx : max_sel - 1] : -1;  // (no list: no read)
     }
     const int cu0 = cuk[s], cu1 = cuk[s + 1], npick = cnt[pair];  // one wait for the three
     const int L = seq_len_of(cu0, cu1, Lmax);

@@ -103,12 +103,15 @@ def gpu_decode_step(c: DecodeCase, step: int = 0):
     max_sel = W.topk + W.window // W.block_size
     out = torch.full((c.B, W.num_q_heads, W.head_dim), float("nan"), device="cuda")
     lse = torch.full((c.B, W.num_q_heads), float("nan"), device="cuda")
-    sel = torch.full((c.B, 1, W.num_kv_heads, max_sel), -7, dtype=torch.int32, device="cuda")
+    # (at least one column: an empty tensor has no address, and the list is
+    # passed whenever the counts are)
+    sel_buf = torch.full((c.B, 1, W.num_kv_heads, max(max_sel, 1)), -7, dtype=torch.int32, device="cuda")
+    sel = sel_buf if max_sel > 0 else sel_buf[..., :0]
     cnt = torch.full((c.B, 1, W.num_kv_heads), -7, dtype=torch.int32, device="cuda")
     scores = torch.full((c.B, 1, W.num_kv_heads, max_nb), float("nan"), device="cuda")
     ws = workspace(c, maxL)
     nosa.nosa_decode_step(c.p, c.kv, c.inp["q"].to("cuda"), cu_dev(lens), c.B, maxL, out, lse,
-                          ws, sel_idx=sel, sel_count=cnt, block_scores=scores)
+                          ws, sel_idx=sel_buf, sel_count=cnt, block_scores=scores)
     torch.cuda.synchronize()
     return dict(out=out.cpu().numpy(), lse=lse.cpu().numpy(), sel=sel.cpu().numpy(),
                 cnt=cnt.cpu().numpy(), scores=scores.cpu().numpy())

@@ -67,6 +67,31 @@ def test_decode_step_logits_beyond_lds(hq, hkv, L):
     _full_check(c, tag=f"zglobal {hq}/{hkv}")
 
 
+def test_empty_budget_no_topk_no_window():
+    """top-k 0 and no window: nothing is selected; the fused step and the
+    stand-alone attention (whose block lists then have no entries; a
+    one-entry buffer is passed, and must not be read) give out = 0 and
+    lse = -inf, as the reference does."""
+    log("case: top-k 0, window 0")
+    lens = [300, 2000, 64 * 9 + 5]
+    c = make_case(_wl(lens, topk=0, window=0, planted=0, seed=3))
+    build_kc(c, [L - 1 for L in lens])
+    g = gpu_decode_step(c, 0)
+    o = oracle_step(c, 0)
+    assert np.all(g["cnt"] == 0) and np.all(o["cnt"] == 0)
+    assert np.all(o["out"] == 0) and np.all(np.isneginf(o["lse"]))
+    assert np.all(g["out"] == 0) and np.all(np.isneginf(g["lse"]))
+    W = c.w
+    out = torch.full((c.B, W.num_q_heads, W.head_dim), float("nan"), device="cuda")
+    lse = torch.full((c.B, W.num_q_heads), float("nan"), device="cuda")
+    sel_d = torch.full((1,), 7, dtype=torch.int32, device="cuda")  # would be a block id if read
+    cnt_d = torch.zeros((c.B, 1, W.num_kv_heads), dtype=torch.int32, device="cuda")
+    nosa.nosa_sparse_attend(c.p, c.kv, c.inp["q"].to("cuda"), None, cu_dev(lens), c.B, 1, max(lens),
+                            sel_d, cnt_d, out, lse, workspace(c, max(lens)))
+    torch.cuda.synchronize()
+    assert torch.all(out == 0).item() and torch.all(torch.isneginf(lse)).item()
+
+
 @pytest.mark.parametrize("hq,hkv,lens", [(16, 2, [3000, 20000]), (8, 1, [70000])])
 def test_decode_step_tied_scores(hq, hkv, lens):
     """A zero query: every logit is 0, so the block importances tie (up to

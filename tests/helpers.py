@@ -132,9 +132,9 @@ def gpu_attend(c: DecodeCase, step: int, sel: np.ndarray, cnt: np.ndarray):
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
-def oracle_step(c: DecodeCase, step: int = 0, seqs=None):
-    """Reference results for the live lengths at `step` (optionally for a
-    subset of the sequences)."""
+def oracle_inputs(c: DecodeCase, step: int = 0, seqs=None):
+    """Host bit patterns (q, k, v) and cu_seqlens_k of the live tokens at
+    `step`, for every sequence or for the listed ones."""
     k, v, cu = synth.packed_live(c.inp, c.w, step)
     q = c.inp["q"]
     if seqs is not None:
@@ -147,7 +147,66 @@ def oracle_step(c: DecodeCase, step: int = 0, seqs=None):
         k, v = torch.cat(ks), torch.cat(vs)
         cu = synth.cu_from_lens(lens)
         q = q[list(seqs)]
-    return ora.forward(c.op, synth.bits(q), None, synth.bits(k), synth.bits(v), cu.numpy())
+    return synth.bits(q), synth.bits(k), synth.bits(v), cu.numpy()
+
+
+def oracle_step(c: DecodeCase, step: int = 0, seqs=None):
+    """Reference results for the live lengths at `step` (optionally for a
+    subset of the sequences)."""
+    q, k, v, cu = oracle_inputs(c, step, seqs)
+    return ora.forward(c.op, q, None, k, v, cu)
+
+
+def oracle_attend_on(c: DecodeCase, step: int, sel: np.ndarray, cnt: np.ndarray, seqs=None):
+    """The reference's attention over a given selection (rows of `sel` /
+    `cnt` in the order of `seqs`): how a step's output is checked when its
+    selection is a correct one other than the reference's (a near-tie)."""
+    q, k, v, cu = oracle_inputs(c, step, seqs)
+    max_sel = c.w.topk + c.w.window // c.w.block_size
+    sel = np.ascontiguousarray(sel[..., :max_sel], dtype=np.int32)
+    return ora.sparse_attend(c.op, q, None, k, v, cu, sel, np.ascontiguousarray(cnt, np.int32))
+
+
+def check_decode(c: DecodeCase, step: int, g: dict, seqs=None, tag: str = ""):
+    """Every check of a fused decode step `g` (gpu_decode_step's results) at
+    `step` against the reference, on the listed sequences (all by default):
+      * block importance within 1e-4 relative of the reference's;
+      * the selection is the rule applied to the step's own fp32 scores,
+        bit for bit (every sequence, not only the listed ones);
+      * the selection equals the reference's outside the near-tie band;
+      * the fused output against the reference's attention on the step's
+        own exported selection (always valid: a near-tie makes either set
+        correct, and the output is then the attention on the set taken);
+      * the fused output against the reference's output directly when the
+        selections agree;
+      * the stand-alone attention (nosa_sparse_attend) on the reference's
+        own selection against the reference's output, for the listed rows
+        (the other rows keep the step's own selection).
+    Returns the number of near-tie exemptions.  Nothing is skipped."""
+    lens = live_lens(c, step)
+    rows = list(range(c.B)) if seqs is None else list(seqs)
+    o = oracle_step(c, step, seqs=seqs)
+    sub = {k: g[k][rows] for k in ("sel", "cnt", "scores", "out", "lse")}
+    lens_s = [lens[s] for s in rows]
+    compare_scores(sub["scores"], o["scores"], lens_s, c.w)
+    check_selection_rule(g["sel"], g["cnt"], g["scores"], lens, c.w)
+    ex = compare_selection(sub["sel"], sub["cnt"], o["sel"], o["cnt"], o["scores"], lens_s, c.w)
+    oo, ol = oracle_attend_on(c, step, sub["sel"], sub["cnt"], seqs)
+    compare_outputs(sub["out"], sub["lse"], oo, ol, tag + " fused (own set)")
+    if ex == 0:
+        compare_outputs(sub["out"], sub["lse"], o["out"], o["lse"], tag + " fused")
+    sel_all = g["sel"].copy()
+    cnt_all = g["cnt"].copy()
+    n = min(sel_all.shape[-1], o["sel"].shape[-1])
+    for i, s in enumerate(rows):
+        sel_all[s] = -1
+        sel_all[s, ..., :n] = o["sel"][i, ..., :n]
+        cnt_all[s] = o["cnt"][i]
+    out, lse = gpu_attend(c, step, sel_all, cnt_all)
+    compare_outputs(out[rows], lse[rows], o["out"], o["lse"], tag + " attend(oracle set)")
+    log(f"{tag}: step {step} ok on sequences {rows if seqs is not None else 'all'} "
+        f"(tie exemptions {ex})")
+    return o, ex
 
 
 def local_blocks(w: synth.Workload) -> int:

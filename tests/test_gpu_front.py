@@ -167,9 +167,13 @@ def test_layer_decode_step_matches_reference(hq, hkv, topk, lens):
     g = dict(sel=sel.cpu().numpy(), cnt=cnt.cpu().numpy(), out=out.cpu().numpy(),
              lse=lse.cpu().numpy())
     ex = compare_selection(g["sel"], g["cnt"], o["sel"], o["cnt"], o["scores"], lens, W)
+    # the step's output against the reference's attention on the step's own
+    # set (always), and on the reference's set when the two agree
+    oo, ol = ora.sparse_attend(c.op, oq, None, kb, vb, cu_np, g["sel"], g["cnt"])
+    mx, mean = compare_outputs(g["out"], g["lse"], oo, ol, "layer step (own set)")
+    log(f"layer step: max abs {mx:.2e}, mean abs {mean:.2e}")
     if ex == 0:
-        mx, mean = compare_outputs(g["out"], g["lse"], o["out"], o["lse"], "layer step")
-        log(f"layer step: max abs {mx:.2e}, mean abs {mean:.2e}")
+        compare_outputs(g["out"], g["lse"], o["out"], o["lse"], "layer step")
     # the step used the front end's queries: same result as the decode step on q_out
     out2 = torch.full_like(out, float("nan"))
     lse2 = torch.full_like(lse, float("nan"))

@@ -10,8 +10,8 @@ import torch
 from block_sparse_attention_nosa_amd import synth
 from oracle import oracle as ora
 
-from helpers import (TIE_BAND, build_kc, check_selection_rule, compare_outputs, compare_scores,
-                     compare_selection, gpu_attend, gpu_decode_step, gpu_kc_logical, live_lens, log, make_case,
+from helpers import (TIE_BAND, build_kc, check_decode, oracle_attend_on, check_selection_rule, compare_outputs,
+                     compare_selection, gpu_decode_step, gpu_kc_logical, live_lens, log, make_case,
                      oracle_step)
 
 pytestmark = pytest.mark.gpu
@@ -19,20 +19,7 @@ pytestmark = pytest.mark.gpu
 
 def _check_step(c, step, seqs=None, tag=""):
     g = gpu_decode_step(c, step)
-    o = oracle_step(c, step, seqs=seqs)
-    lens = live_lens(c, step)
-    rows = list(range(c.B)) if seqs is None else list(seqs)
-    sub = {k: g[k][rows] for k in ("sel", "cnt", "scores", "out", "lse")}
-    lens_s = [lens[s] for s in rows]
-    compare_scores(sub["scores"], o["scores"], lens_s, c.w)
-    ex = compare_selection(sub["sel"], sub["cnt"], o["sel"], o["cnt"], o["scores"], lens_s, c.w)
-    if ex == 0:
-        compare_outputs(sub["out"], sub["lse"], o["out"], o["lse"], tag + " fused")
-    # attention on the reference's own selection through the stand-alone entry
-    if seqs is None:
-        out, lse = gpu_attend(c, step, o["sel"], o["cnt"])
-        compare_outputs(out, lse, o["out"], o["lse"], tag + " attend")
-    log(f"{tag}: step {step} ok (tie exemptions {ex})")
+    o, _ = check_decode(c, step, g, seqs=seqs, tag=tag)
     return g, o
 
 
@@ -73,22 +60,28 @@ def test_decode_varlen_b32_permuted_pages():
 
 
 def test_decode_b16_64k_gqa4_sampled():
-    log("case: decode-b16-64k, sequences 0 and 15 against the reference")
+    """The 64K batch-16 workload (32/8 heads, top-k 96) at two consecutive
+    steps (the first appends a pooled key): sequences 0, 5, 10 and 15 against
+    the reference at each step; every sequence's selection against the rule
+    on its own scores, its sizes, window and planted blocks."""
+    log("case: decode-b16-64k, sequences 0, 5, 10, 15 at steps 0 and 1")
     w = synth.config(4)
+    w.extra_tokens = 1
     c = make_case(w, gen_device="cuda")
     build_kc(c, [L - 1 for L in w.lens])
-    g, _ = _check_step(c, 0, seqs=[0, 15], tag="c4")
-    # every sequence: sizes, ordering and window of the selection are valid
-    for s in range(w.batch):
-        nb = (w.lens[s] + 63) // 64
-        for gi in range(w.num_kv_heads):
-            n = g["cnt"][s, 0, gi]
-            sel = g["sel"][s, 0, gi, :n]
-            assert n == min(nb, w.topk + 16)
-            assert np.all(np.diff(sel) > 0) and sel[-1] == nb - 1
-            assert set(range(nb - 16, nb)) <= set(sel.tolist())
-            assert set(c.inp["planted"][s * w.num_kv_heads + gi]) <= set(sel.tolist())
-    assert np.isfinite(g["out"]).all() and np.isfinite(g["lse"]).all()
+    for step in (0, 1):
+        g, _ = _check_step(c, step, seqs=[0, 5, 10, 15], tag="c4")
+        lens = live_lens(c, step)
+        for s in range(w.batch):
+            nb = (lens[s] + 63) // 64
+            for gi in range(w.num_kv_heads):
+                n = g["cnt"][s, 0, gi]
+                sel = g["sel"][s, 0, gi, :n]
+                assert n == min(nb, w.topk + 16)
+                assert np.all(np.diff(sel) > 0) and sel[-1] == nb - 1
+                assert set(range(nb - 16, nb)) <= set(sel.tolist())
+                assert set(c.inp["planted"][s * w.num_kv_heads + gi]) <= set(sel.tolist())
+        assert np.isfinite(g["out"]).all() and np.isfinite(g["lse"]).all()
     torch.cuda.empty_cache()
 
 
@@ -164,13 +157,16 @@ def test_offload_b8_16k_steps():
                 picks = {int(x) for x in sel[s, 0, g, :cnt[s, 0, g]] if x < nb - 16}
                 assert picks <= set(cmap[s, g].tolist()), (t, s, g)
         if t == 0:
-            o = oracle_step(c, 0, seqs=[0, 7])
             rows = [0, 7]
+            o = oracle_step(c, 0, seqs=rows)
             ex = compare_selection(sel[rows], cnt[rows], o["sel"], o["cnt"], o["scores"],
                                    [lens[s] for s in rows], w)
+            gout, glse = res[1][0].cpu().numpy()[rows], res[1][1].cpu().numpy()[rows]
+            # on the step's own set always; on the reference's when they agree
+            oo, ol = oracle_attend_on(c, 0, sel[rows], cnt[rows], seqs=rows)
+            compare_outputs(gout, glse, oo, ol, "offloaded c2 (own set)")
             if ex == 0:
-                compare_outputs(res[1][0].cpu().numpy()[rows], res[1][1].cpu().numpy()[rows],
-                                o["out"], o["lse"], "offloaded c2")
+                compare_outputs(gout, glse, o["out"], o["lse"], "offloaded c2")
         log(f"offloaded c2: step {t} ok")
 
 
@@ -231,18 +227,28 @@ def test_layer_step_b8_16k_from_hidden():
                     synth.cu_from_lens(ls).numpy())
     g_sel, g_cnt = sel.cpu().numpy()[rows], cnt.cpu().numpy()[rows]
     ex = compare_selection(g_sel, g_cnt, o["sel"], o["cnt"], o["scores"], ls, w)
+    g_out, g_lse = out.cpu().numpy()[rows], lse.cpu().numpy()[rows]
+    # the step's output against the reference's attention on the step's own
+    # set (always), and on the reference's set when the two agree
+    oo, ol = ora.sparse_attend(c.op, oq[rows], None, np.concatenate(ks), np.concatenate(vs),
+                               synth.cu_from_lens(ls).numpy(), g_sel, g_cnt)
+    compare_outputs(g_out, g_lse, oo, ol, "layer step c2 (own set)")
     if ex == 0:
-        compare_outputs(out.cpu().numpy()[rows], lse.cpu().numpy()[rows], o["out"], o["lse"],
-                        "layer step c2")
+        compare_outputs(g_out, g_lse, o["out"], o["lse"], "layer step c2")
     log(f"layer step c2: ok (tie exemptions {ex})")
 
 
 def test_prompt_32k_sampled_query_blocks():
     """The bench's whole-prompt workload (32768 tokens, chunks of 4096): query
-    blocks 0, 100, 300 and 511 against the reference (those without a near-tie), each solved as its own problem
-    cut after the block's last query (nothing later is visible)."""
+    blocks 0, 100, 300 and 511 against the reference, each solved as its own
+    problem cut after the block's last query (nothing later is visible).  The
+    stand-alone chain over the same prompt supplies the selection the prompt
+    prefill shares: its importance and selection against the reference (near-
+    tie band), and the prompt's output against the reference's attention on
+    that selection for every sampled block, and against the reference's
+    output where the selections agree.  Every sampled block is compared."""
     from helpers import cu_dev
-    from test_gpu_prefill import check_rows, compare_out
+    from test_gpu_prefill import check_rows, compare_out, gpu_prefill
     from block_sparse_attention_nosa_amd import nosa
     log("case: whole-prompt prefill, 32768 tokens, sampled query blocks")
     L = 32768
@@ -257,27 +263,23 @@ def test_prompt_32k_sampled_query_blocks():
     torch.cuda.synchronize()
     go, gl = out.cpu().numpy(), lse.cpu().numpy()
     assert np.isfinite(go).all()
+    del ws
+    g, _ = gpu_prefill(c)  # the pooled keys are the prompt prefill's own
     compared = 0
     for r in (0, 100, 300, 511):
         p_last = 64 * r + 63
-        kk = c.inp["k"][:p_last + 1].cpu()
-        vv = c.inp["v"][:p_last + 1].cpu()
-        qq = q[64 * r:64 * r + 64].cpu()
-        o = ora.forward(c.op, synth.bits(qq), np.array([0, 64], np.int32), synth.bits(kk),
-                        synth.bits(vv), np.array([0, p_last + 1], np.int32))
-        # a near-tie at the k-th place makes either block a correct pick
-        nb = p_last // 64 + 1
-        ncand = max(nb - 16, 0)
-        tie = False
-        for g in range(2):
-            sc = np.sort(o["scores"][0, 0, g, :ncand])[::-1]
-            if 64 < ncand:
-                tie |= abs(sc[63] - sc[64]) / max(abs(sc[63]), abs(sc[64])) < TIE_BAND
-        if tie:
-            log(f"prompt 32K q-block {r}: near-tie, outputs not compared")
-            continue
-        compare_out(go[64 * r:64 * r + 64], gl[64 * r:64 * r + 64], o["out"], o["lse"],
-                    f"prompt r{r}")
+        kk = synth.bits(c.inp["k"][:p_last + 1])
+        vv = synth.bits(c.inp["v"][:p_last + 1])
+        qq = synth.bits(q[64 * r:64 * r + 64])
+        cu_q, cu_k = np.array([0, 64], np.int32), np.array([0, p_last + 1], np.int32)
+        o = ora.forward(c.op, qq, cu_q, kk, vv, cu_k)
+        e = check_rows(g, o, [(0, r, 0, 0)], w, f"prompt r{r}")
+        rows = slice(64 * r, 64 * r + 64)
+        oo, ol = ora.sparse_attend(c.op, qq, cu_q, kk, vv, cu_k, g["sel"][:, r:r + 1],
+                                   g["cnt"][:, r:r + 1])
+        compare_out(go[rows], gl[rows], oo, ol, f"prompt r{r} (own set)")
+        if e == 0:
+            compare_out(go[rows], gl[rows], o["out"], o["lse"], f"prompt r{r}")
         compared += 1
-        log(f"prompt 32K q-block {r}: ok")
-    assert compared >= 2
+        log(f"prompt 32K q-block {r}: ok (tie exemptions {e})")
+    assert compared == 4

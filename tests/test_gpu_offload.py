@@ -153,6 +153,10 @@ def _run(c, off, steps, queries, tag):
     q = queries[(steps - 1) % len(queries)].cpu()
     o = ora.forward(c.op, synth.bits(q), None, synth.bits(k), synth.bits(v), cu.numpy())
     ex = compare_selection(gb["sel"], gb["cnt"], o["sel"], o["cnt"], o["scores"], lens, w)
+    # on the step's own set always; on the reference's when they agree
+    oo, ol = ora.sparse_attend(c.op, synth.bits(q), None, synth.bits(k), synth.bits(v), cu.numpy(),
+                               gb["sel"][..., :w.topk + w.window // 64], gb["cnt"])
+    compare_outputs(gb["out"], gb["lse"], oo, ol, tag + " (own set)")
     if ex == 0:
         compare_outputs(gb["out"], gb["lse"], o["out"], o["lse"], tag)
     log(f"{tag}: ok, {steps} steps, {total_fetch} blocks read from host, tie exemptions {ex}")

@@ -8,9 +8,9 @@ import torch
 from block_sparse_attention_nosa_amd import nosa, synth
 from oracle import oracle as ora
 
-from helpers import (DecodeCase, build_kc, check_selection_rule, compare_outputs, compare_scores,
-                     compare_selection, cu_dev, gpu_attend, gpu_decode_step, gpu_kc_logical, live_lens, log,
-                     make_case, oracle_step, workspace)
+from helpers import (DecodeCase, build_kc, check_decode, compare_outputs, compare_selection,
+                     cu_dev, gpu_decode_step, gpu_kc_logical, live_lens, log, make_case,
+                     oracle_attend_on, oracle_step, workspace)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,20 +25,13 @@ def _full_check(c: DecodeCase, step=0, tag=""):
     lens = live_lens(c, step)
     build_kc(c, [L - 1 for L in lens])
     g = gpu_decode_step(c, step)
-    o = oracle_step(c, step)
-    # pooled keys: bit-exact (the step appended the last one)
+    # pooled keys: bit-exact (the step appended the last one); then every
+    # check of the step (scores, selection rule, selection, outputs on both
+    # selections)
+    o, ex = check_decode(c, step, g, tag=tag)
     for s, L in enumerate(lens):
         nc = ora.num_keys(L, c.op)
         assert np.array_equal(gpu_kc_logical(c, s, nc), o["kc"][s, :, :nc]), (tag, s)
-    compare_scores(g["scores"], o["scores"], lens, c.w)
-    check_selection_rule(g["sel"], g["cnt"], g["scores"], lens, c.w)
-    ex = compare_selection(g["sel"], g["cnt"], o["sel"], o["cnt"], o["scores"], lens, c.w)
-    # outputs: on the reference's own selection through nosa_sparse_attend, and
-    # the fused step's output whenever its selection is the reference's
-    out, lse = gpu_attend(c, step, o["sel"], o["cnt"])
-    compare_outputs(out, lse, o["out"], o["lse"], tag + " attend(oracle set)")
-    if ex == 0:
-        compare_outputs(g["out"], g["lse"], o["out"], o["lse"], tag + " fused")
     return g, o, ex
 
 
@@ -191,11 +184,7 @@ def test_multi_step_decode_appends_keys():
     for step in range(33):
         g = gpu_decode_step(c, step)
         if step % 8 == 0 or step == 32:
-            lens = live_lens(c, step)
-            o = oracle_step(c, step)
-            ex = compare_selection(g["sel"], g["cnt"], o["sel"], o["cnt"], o["scores"], lens, w)
-            if ex == 0:
-                compare_outputs(g["out"], g["lse"], o["out"], o["lse"], f"step{step}")
+            check_decode(c, step, g, tag=f"step{step}")
     lens = live_lens(c, 32)
     kcs = [gpu_kc_logical(c, s, ora.num_keys(L, c.op)) for s, L in enumerate(lens)]
     build_kc(c, lens)
@@ -297,19 +286,33 @@ def test_stream_argument_is_honoured():
 
 def test_workspace_reuse_across_sizes():
     """One workspace (sized for the largest call) serves consecutive calls of
-    different sizes: nothing a call leaves behind changes the next one."""
+    different sizes: nothing a call leaves behind changes the next one.
+    Every call is checked against the reference (on its own exported
+    selection, and on the reference's when they agree), and the two calls on
+    the large batch are bitwise identical."""
     log("case: workspace reuse")
     big = make_case(_wl([5000, 3000, 4000], topk=6, planted=2, seed=31))
     small = make_case(_wl([1500], topk=6, planted=1, seed=32))
     ws = workspace(big, 5000)
+    results = []
     for c in (big, small, big):
         lens = live_lens(c, 0)
         build_kc(c, [L - 1 for L in lens])
-        out = torch.empty(c.B, 16, 128, device="cuda")
-        lse = torch.empty(c.B, 16, device="cuda")
+        out = torch.full((c.B, 16, 128), float("nan"), device="cuda")
+        lse = torch.full((c.B, 16), float("nan"), device="cuda")
+        sel = torch.full((c.B, 1, 2, 6 + 16), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((c.B, 1, 2), -7, dtype=torch.int32, device="cuda")
         nosa.nosa_decode_step(c.p, c.kv, c.inp["q"].cuda(), cu_dev(lens), c.B, max(lens), out,
-                              lse, ws)
+                              lse, ws, sel_idx=sel, sel_count=cnt)
         torch.cuda.synchronize()
+        g = dict(out=out.cpu().numpy(), lse=lse.cpu().numpy(), sel=sel.cpu().numpy(),
+                 cnt=cnt.cpu().numpy())
         o = oracle_step(c, 0)
-        if c is small:
-            np.testing.assert_array_less(np.abs(out.cpu().numpy() - o["out"]), 1e-2)
+        ex = compare_selection(g["sel"], g["cnt"], o["sel"], o["cnt"], o["scores"], lens, c.w)
+        oo, ol = oracle_attend_on(c, 0, g["sel"], g["cnt"])
+        compare_outputs(g["out"], g["lse"], oo, ol, f"reuse B={c.B} (own set)")
+        if ex == 0:
+            compare_outputs(g["out"], g["lse"], o["out"], o["lse"], f"reuse B={c.B}")
+        results.append(g)
+    for key in ("out", "lse", "sel", "cnt"):
+        assert np.array_equal(results[0][key], results[2][key]), key

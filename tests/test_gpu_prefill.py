@@ -61,6 +61,17 @@ def attend_with(c, sel_np, cnt_np, args):
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
+def oracle_attend_on_pf(c, sel, cnt):
+    """The reference's attention for every query of the case over the given
+    per-q-block selections [B][max_qblk][Hkv][>= max_sel]."""
+    w = c.w
+    max_sel = w.topk + w.window // 64
+    return ora.sparse_attend(c.op, synth.bits(c.inp["q"]), c.inp["cu_q"].cpu().numpy(),
+                             synth.bits(c.inp["k"]), synth.bits(c.inp["v"]),
+                             synth.cu_from_lens(w.lens).numpy(),
+                             np.ascontiguousarray(sel[..., :max_sel]), cnt)
+
+
 def qblock_nb(L, Lq, r):
     p_last = L - Lq + min(64 * r + 64, Lq) - 1
     return p_last // 64 + 1
@@ -115,12 +126,16 @@ def _full(c, tag):
     w = c.w
     build_kc(c, w.lens)
     g, args = gpu_prefill(c)
-    o = ora.forward(c.op, synth.bits(c.inp["q"]), c.inp["cu_q"].numpy(), synth.bits(c.inp["k"]),
+    o = ora.forward(c.op, synth.bits(c.inp["q"]), c.inp["cu_q"].cpu().numpy(), synth.bits(c.inp["k"]),
                     synth.bits(c.inp["v"]), synth.cu_from_lens(w.lens).numpy())
     rows = [(s, r, s, r) for s in range(w.batch) for r in range(math.ceil(w.q_lens[s] / 64))]
     ex = check_rows(g, o, rows, w, tag)
     out, lse = attend_with(c, o["sel"], o["cnt"], args)
     compare_out(out, lse, o["out"], o["lse"], tag + " attend(oracle sets)")
+    # the chain's output against the reference's attention on the chain's own
+    # sets (always), and against the reference's output when the sets agree
+    oo, ol = oracle_attend_on_pf(c, g["sel"], g["cnt"])
+    compare_out(g["out"], g["lse"], oo, ol, tag + " chain (own sets)")
     if ex == 0:
         compare_out(g["out"], g["lse"], o["out"], o["lse"], tag + " chain")
     log(f"{tag}: ok (tie exemptions {ex})")
@@ -157,24 +172,46 @@ def test_prefill_locality(locality):
 
 
 def test_prefill_131072_sampled_query_blocks():
+    """The 2048-query chunk at the end of a 131072-token context, eight of its
+    32 query blocks (first, last and six between) against the reference,
+    which solves each as its own problem cut after the block's last query.
+    For every sampled block: importance and selection (near-tie band), the
+    chain's output against the reference's attention on the chain's own
+    selection, the stand-alone attention on the reference's selection against
+    the reference's output, and the chain's output against it directly when
+    the selections agree.  Every sampled block is compared."""
     log("case: prefill-2048-of-131072, sampled query blocks")
     w = synth.config(5)
     c = make_case(w, gen_device="cuda")
     build_kc(c, w.lens)
-    g, _ = gpu_prefill(c)
+    g, args = gpu_prefill(c)
     L, Lq = w.lens[0], w.q_lens[0]
     assert np.isfinite(g["out"]).all()
+    sampled = (0, 4, 9, 13, 18, 22, 27, 31)
+    sel_o = g["sel"].copy()
+    cnt_o = g["cnt"].copy()
+    refs = {}
     ex = 0
-    for r in (0, 13, 31):
+    for r in sampled:
         p_last = L - Lq + 64 * r + 63
-        k = c.inp["k"][:p_last + 1]
-        v = c.inp["v"][:p_last + 1]
-        q = c.inp["q"][64 * r:64 * r + 64]
-        o = ora.forward(c.op, synth.bits(q), np.array([0, 64], np.int32), synth.bits(k),
-                        synth.bits(v), np.array([0, p_last + 1], np.int32))
+        k = synth.bits(c.inp["k"][:p_last + 1])
+        v = synth.bits(c.inp["v"][:p_last + 1])
+        q = synth.bits(c.inp["q"][64 * r:64 * r + 64])
+        cu_q, cu_k = np.array([0, 64], np.int32), np.array([0, p_last + 1], np.int32)
+        o = ora.forward(c.op, q, cu_q, k, v, cu_k)
         e = check_rows(g, o, [(0, r, 0, 0)], w, f"c5 r{r}")
         ex += e
+        rows = slice(64 * r, 64 * r + 64)
+        oo, ol = ora.sparse_attend(c.op, q, cu_q, k, v, cu_k, g["sel"][:, r:r + 1], g["cnt"][:, r:r + 1])
+        compare_out(g["out"][rows], g["lse"][rows], oo, ol, f"c5 r{r} chain (own set)")
         if e == 0:
-            compare_out(g["out"][64 * r:64 * r + 64], g["lse"][64 * r:64 * r + 64], o["out"],
-                        o["lse"], f"c5 r{r}")
-        log(f"c5 q-block {r}: ok (exemptions {e})")
+            compare_out(g["out"][rows], g["lse"][rows], o["out"], o["lse"], f"c5 r{r} chain")
+        sel_o[0, r] = o["sel"][0, 0]
+        cnt_o[0, r] = o["cnt"][0, 0]
+        refs[r] = o
+        log(f"c5 q-block {r}: chain ok (exemptions {e})")
+    out, lse = attend_with(c, sel_o, cnt_o, args)
+    for r in sampled:
+        rows = slice(64 * r, 64 * r + 64)
+        compare_out(out[rows], lse[rows], refs[r]["out"], refs[r]["lse"], f"c5 r{r} attend(oracle set)")
+    log(f"c5: {len(sampled)} of 32 query blocks compared, tie exemptions {ex}")

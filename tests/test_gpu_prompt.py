@@ -18,7 +18,7 @@ from block_sparse_attention_nosa_amd import nosa, synth
 from oracle import oracle as ora
 
 from helpers import OUT_MAX_ABS, OUT_MEAN_ABS, gpu_kc_logical, log, make_case
-from test_gpu_prefill import check_rows, gpu_prefill
+from test_gpu_prefill import check_rows, gpu_prefill, oracle_attend_on_pf
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +69,12 @@ def _check(c, chunks, tag):
         _same(res[ch], (out, lse), (tag, ch))
     g, _ = gpu_prefill(c)  # the stand-alone chain over the same prompt
     _same((g["out"], g["lse"]), (out, lse), tag)
+    # every query (near-ties included) against the reference's attention on
+    # the chain's selections, which the prompt prefill shares
+    oo, ol = oracle_attend_on_pf(c, g["sel"], g["cnt"])
+    err = np.abs(out.astype(np.float64) - oo)
+    assert err.max() <= OUT_MAX_ABS and err.mean() <= OUT_MEAN_ABS, (tag, "own sets", err.max(),
+                                                                      err.mean())
     keep = np.zeros(out.shape[0], bool)
     ex = 0
     for s, L in enumerate(w.lens):

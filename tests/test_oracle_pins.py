@@ -253,6 +253,67 @@ def test_prefill_block_scores_sum_of_single_queries(oracle):
         np.testing.assert_allclose(sc[0, r][:, full], acc[:, full], rtol=1e-12)
 
 
+@pytest.mark.parametrize("window", [0, 64])
+def test_prefill_block_scores_partial_visibility_brute_force(oracle, window):
+    """Importance of every block for q-blocks whose queries see different
+    sets of pooled keys (a chunk starting mid-block, so key and block
+    boundaries fall inside q-blocks; the last q-block is ragged), by brute
+    force: each query's softmax over exactly the keys it sees (scipy), summed
+    over the q-block's queries and the group's heads, then the mean over the
+    keys overlapping the block among those the q-block's last query sees.
+    With small windows the partially visible blocks are candidates, so the
+    selection built from these scores (top-k by score desc, index asc, plus
+    the window) must be the reference's as well."""
+    p = Params(num_q_heads=4, num_kv_heads=2, head_dim=16, window=window, topk=5)
+    rng = np.random.default_rng(17 + window)
+    L, Lq = 1000, 150
+    k = random_bits(rng, (L, 2, 16))
+    q = random_bits(rng, (Lq, 4, 16), scale=2.0)
+    cu_k = np.array([0, L], np.int32)
+    cu_q = np.array([0, Lq], np.int32)
+    kc = oracle.compress_keys(p, k, cu_k)
+    sc = oracle.block_scores(p, q, cu_q, kc, cu_k)
+    sel, cnt = oracle.select_blocks(p, sc, cu_q, cu_k)
+    assert sc.shape[1] == 3
+    kcf = bits_to_f64(kc[0])  # [Hkv][nc][d]
+    qf = bits_to_f64(q)       # [Lq][Hq][d]
+    checked_partial = 0
+    for r in range(3):
+        i0, i1 = 64 * r, min(64 * r + 64, Lq)
+        p_last = L - Lq + i1 - 1
+        nc_r = (p_last + 1 - 32) // 16 + 1
+        nb = p_last // 64 + 1
+        for g in range(2):
+            sigma = np.zeros(nc_r)
+            for i in range(i0, i1):
+                pos = L - Lq + i
+                vis = [j for j in range(nc_r) if 16 * j + 32 <= pos + 1]
+                for h in (2 * g, 2 * g + 1):
+                    z = np.array([kcf[g, j] @ qf[i, h] for j in vis]) / math.sqrt(16)
+                    sigma[vis] += scipy.special.softmax(z)
+            want = np.full(nb, -np.inf)
+            for b in range(nb):
+                J = [j for j in range(nc_r) if set(range(16 * j, 16 * j + 32)) &
+                     set(range(64 * b, 64 * b + 64))]
+                if J:
+                    want[b] = np.mean(sigma[J])
+                    first_q = L - Lq + i0
+                    checked_partial += max(J) * 16 + 32 > first_q + 1
+            got = sc[0, r, g, :nb]
+            assert np.array_equal(np.isinf(got), np.isinf(want)), (r, g)
+            fin = np.isfinite(want)
+            np.testing.assert_allclose(got[fin], want[fin], rtol=1e-12, atol=0)
+            assert np.all(np.isneginf(sc[0, r, g, nb:]))
+            # the selection from the brute-force scores
+            wb = min(window // 64, nb)
+            ncand = nb - wb
+            order = sorted(range(ncand), key=lambda b: (-want[b], b))[:min(p.topk, ncand)]
+            exp = sorted(order) + list(range(ncand, nb))
+            assert int(cnt[0, r, g]) == len(exp), (r, g)
+            assert sel[0, r, g, :len(exp)].tolist() == exp, (r, g)
+    assert checked_partial > 0
+
+
 # --------------------------------------------------------------- selection --
 
 @pytest.mark.parametrize("seed", range(6))

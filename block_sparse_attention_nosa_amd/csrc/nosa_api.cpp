@@ -651,11 +651,11 @@ nosa_status nosa_layer_decode_step(const nosa_params* params, const nosa_front_p
                                     sel_idx, sel_count, nullptr, sm));
 }
 
-nosa_status nosa_decode_step(const nosa_params* params, const nosa_paged_kv* kv,
-                             const nosa_bf16* q, const int32_t* cu_seqlens_k, int32_t batch,
-                             int32_t max_seqlen_k, float* out, float* lse, int32_t* sel_idx,
-                             int32_t* sel_count, float* block_scores, void* workspace,
-                             size_t workspace_bytes, void* stream)
+// Arguments of a decode step (all but the workspace); fills its plan.
+static nosa_status decode_check(const nosa_params* params, const nosa_paged_kv* kv,
+                                const nosa_bf16* q, const int32_t* cu_seqlens_k, int32_t batch,
+                                int32_t max_seqlen_k, const float* out, const int32_t* sel_idx,
+                                const int32_t* sel_count, Plan* pl)
 {
     nosa_status st = check_params(params);
     if (st != NOSA_OK) return st;
@@ -666,12 +666,39 @@ nosa_status nosa_decode_step(const nosa_params* params, const nosa_paged_kv* kv,
     if (!q || !cu_seqlens_k || !out) return NOSA_ERR_NULL;
     if ((sel_idx == nullptr) != (sel_count == nullptr)) return NOSA_ERR_NULL;
     if (batch == 0) return NOSA_OK;
+    return make_plan(params, batch, max_seqlen_k, pl);
+}
+
+nosa_status nosa_decode_step(const nosa_params* params, const nosa_paged_kv* kv,
+                             const nosa_bf16* q, const int32_t* cu_seqlens_k, int32_t batch,
+                             int32_t max_seqlen_k, float* out, float* lse, int32_t* sel_idx,
+                             int32_t* sel_count, float* block_scores, void* workspace,
+                             size_t workspace_bytes, void* stream)
+{
     Plan pl;
-    st = make_plan(params, batch, max_seqlen_k, &pl);
-    if (st != NOSA_OK) return st;
+    const nosa_status st = decode_check(params, kv, q, cu_seqlens_k, batch, max_seqlen_k, out,
+                                        sel_idx, sel_count, &pl);
+    if (st != NOSA_OK || batch == 0) return st;
     if (!workspace || workspace_bytes < pl.bytes) return NOSA_ERR_WORKSPACE;
     return hip_status(launch_decode(pl, *kv, q, cu_seqlens_k, carve(pl, workspace), out, lse,
                                     sel_idx, sel_count, block_scores, as_stream(stream)));
+}
+
+nosa_status nosa_decode_step_static(const nosa_params* params, const nosa_paged_kv* kv,
+                                    const nosa_bf16* q, const int32_t* cu_seqlens_k,
+                                    int32_t batch, int32_t max_seqlen_k, float* out, float* lse,
+                                    int32_t* sel_idx, int32_t* sel_count, float* block_scores,
+                                    void* stream)
+{
+    Plan pl;
+    const nosa_status st = decode_check(params, kv, q, cu_seqlens_k, batch, max_seqlen_k, out,
+                                        sel_idx, sel_count, &pl);
+    if (st != NOSA_OK || batch == 0) return st;
+    if (pl.bytes > kStaticScratchBytes) return NOSA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (static_scratch(&ws) != hipSuccess) return NOSA_ERR_HIP;
+    return hip_status(launch_decode(pl, *kv, q, cu_seqlens_k, carve(pl, ws), out, lse, sel_idx,
+                                    sel_count, block_scores, as_stream(stream)));
 }
 
 }  // extern "C"

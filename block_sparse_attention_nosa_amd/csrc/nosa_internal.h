@@ -25,6 +25,7 @@ constexpr int kScoreWaves = 4;           // waves of a scoring workgroup
 constexpr int kStep2Waves = 4;           // waves of an attention workgroup
 constexpr int kMaxChunks = 64;           // scoring chunks per pair (one lane each when combined)
 constexpr int kMaxCacheSlots = 256;      // block-cache slots per pair (offloaded KV): one per thread
+constexpr size_t kStaticScratchBytes = NOSA_STATIC_SCRATCH_BYTES;  // nosa_decode_step_static
 
 inline int num_keys(int L) { return L >= kPoolK ? (L - kPoolK) / kPoolS + 1 : 0; }
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -114,6 +115,10 @@ hipError_t launch_select(const Plan& pl, const int32_t* cu_k, const int32_t* cu_
 hipError_t launch_attend(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
                          const int32_t* cu_k, const int32_t* sel, const int32_t* cnt,
                          const Workspace& w, float* out, float* lse, hipStream_t stream);
+// Device address of this device's static scratch array (kStaticScratchBytes),
+// looked up on the first call on each device.
+hipError_t static_scratch(void** ptr);
+
 // off: offloaded KV (kv then holds the host pools' device view, kc_pool and
 // the block table).
 hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,

@@ -29,6 +29,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "nosa_device.h"
 
 namespace nosa {
@@ -1233,37 +1236,65 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
 
 // ---------------------------------------------------------- launchers ---
 
-// Largest LDS a workgroup may use on the current device (queried once per
-// device).
-static size_t device_lds_limit()
+// Per-device attribute caches: an attribute is read once per device and kept
+// in an atomic slot (0 = not read yet), so concurrent first calls on several
+// threads at worst read it twice and store the same value.
+constexpr int kMaxDevices = 64;
+
+static int device_attribute(std::atomic<int>* slots, hipDeviceAttribute_t attr, int fallback)
 {
-    static size_t cached[64] = {0};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * 1024;
-    if (cached[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-            v <= 0)
-            v = 64 * 1024;
-        cached[dev] = (size_t)v;
-    }
-    return cached[dev];
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return fallback;
+    int v = slots[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, attr, dev) != hipSuccess || v <= 0) v = fallback;
+    slots[dev].store(v, std::memory_order_relaxed);
+    return v;
 }
 
-// Compute units of the current device (queried once per device).
+// Largest LDS a workgroup may use on the current device.
+static size_t device_lds_limit()
+{
+    static std::atomic<int> cached[kMaxDevices];
+    return (size_t)device_attribute(cached, hipDeviceAttributeMaxSharedMemoryPerBlock, 64 * 1024);
+}
+
+// Compute units of the current device.
 static int device_cus()
 {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[kMaxDevices];
+    return device_attribute(cached, hipDeviceAttributeMultiprocessorCount, 256);
+}
+
+// Scratch of nosa_decode_step_static: the decode step's partials for callers
+// that cannot allocate.  Every device the library runs on holds its own copy
+// from module load until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, read once per device with that device current, and
+// only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr)
+{
+    static std::atomic<void*> addr[kMaxDevices];
+    static std::mutex mu;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            v <= 0)
-            v = 256;
-        cached[dev] = v;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(mu);
+        p = addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            addr[dev].store(p, std::memory_order_release);
+        }
     }
-    return cached[dev];
+    *ptr = p;
+    return hipSuccess;
 }
 
 // wgroups > 0: also the window workgroups, wgroups per pair (pl.wslots: a

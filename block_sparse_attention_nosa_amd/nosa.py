@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
             "nosa_select_blocks": [P, vp, vp, vp, i32, i32, i32, vp, vp, vp],
             "nosa_sparse_attend": [P, KV, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp],
             "nosa_decode_step": [P, KV, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
+            "nosa_decode_step_static": [P, KV, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp],
             "nosa_prefill_sparse_workspace_size": [P, i32, i32, i32, ctypes.POINTER(sz)],
             "nosa_prefill_sparse": [P, KV, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp],
             "nosa_offload_workspace_size": [P, i32, i32, i32, ctypes.POINTER(sz)],
@@ -200,6 +201,17 @@ def nosa_decode_step(p, kv, q, cu_seqlens_k, batch, max_seqlen_k, out, lse, work
         _ptr(out), _ptr(lse), _ptr(sel_idx), _ptr(sel_count), _ptr(block_scores),
         _ptr(workspace),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 32 << 20  # NOSA_STATIC_SCRATCH_BYTES
+
+
+def nosa_decode_step_static(p, kv, q, cu_seqlens_k, batch, max_seqlen_k, out, lse, sel_idx=None,
+                            sel_count=None, block_scores=None, stream=None):
+    _check("nosa_decode_step_static", lib().nosa_decode_step_static(
+        ctypes.byref(p), ctypes.byref(kv), _ptr(q), _ptr(cu_seqlens_k), batch, max_seqlen_k,
+        _ptr(out), _ptr(lse), _ptr(sel_idx), _ptr(sel_count), _ptr(block_scores),
         _stream(stream)))
 
 

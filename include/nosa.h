@@ -34,8 +34,11 @@
  *     NOSA_ERR_INVALID, a shape this build has no kernel for
  *     NOSA_ERR_UNSUPPORTED, a short workspace NOSA_ERR_WORKSPACE, and a failed
  *     HIP launch NOSA_ERR_HIP.  Nothing aborts.
- *   - No global state: calls on different streams may run concurrently as
- *     long as they do not share output or workspace buffers.
+ *   - Global state: a per-device cache of two device attributes (LDS per
+ *     workgroup, compute units), read once and thread-safe, and the static
+ *     scratch array of nosa_decode_step_static.  Calls of the other entry
+ *     points on different streams may run concurrently as long as they do not
+ *     share output or workspace buffers.
  *   - Workspace: device scratch memory of nosa_workspace_size() bytes, with
  *     no initial contents required and none kept between calls; reused
  *     across calls without clearing.  Calls sharing a workspace must be
@@ -73,7 +76,7 @@
 extern "C" {
 #endif
 
-#define NOSA_ABI_VERSION 3
+#define NOSA_ABI_VERSION 4
 
 typedef uint16_t nosa_bf16; /* bf16 bit pattern */
 
@@ -289,6 +292,31 @@ nosa_status nosa_decode_step(const nosa_params* params, const nosa_paged_kv* kv,
                              int32_t max_seqlen_k, float* out, float* lse, int32_t* sel_idx,
                              int32_t* sel_count, float* block_scores, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Bytes of the static scratch array of nosa_decode_step_static. */
+#define NOSA_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* nosa_decode_step for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture that must not allocate, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments (without
+ * the workspace), computation and results as nosa_decode_step, bit for bit
+ * (the same kernels and launch plan); the step's partials go to a scratch
+ * array the library holds in device memory, NOSA_STATIC_SCRATCH_BYTES per
+ * device, from module load until the process ends.  Allocates nothing: no
+ * hipMalloc, hipFree or allocating library routine.  The first call on a
+ * device looks the array's device address up (once per device, thread-safe).
+ * The array needs no initial contents and keeps whatever the last call left.
+ * Every call on one device shares that device's array, so calls that may
+ * overlap on one device (different streams, or host threads) race: order them
+ * on one stream.  Errors: those of nosa_decode_step, with NOSA_ERR_WORKSPACE
+ * when the step needs more than NOSA_STATIC_SCRATCH_BYTES (the size
+ * nosa_workspace_size(params, batch, 1, max_seqlen_k) reports), checked on
+ * the host before anything is enqueued. */
+nosa_status nosa_decode_step_static(const nosa_params* params, const nosa_paged_kv* kv,
+                                    const nosa_bf16* q, const int32_t* cu_seqlens_k,
+                                    int32_t batch, int32_t max_seqlen_k, float* out, float* lse,
+                                    int32_t* sel_idx, int32_t* sel_count, float* block_scores,
+                                    void* stream);
 
 /* Workspace bytes needed by nosa_prefill_sparse for at most `batch` prompts
  * of at most max_seqlen tokens processed `chunk` queries at a time (chunk a

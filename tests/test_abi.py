@@ -26,13 +26,14 @@ def test_exports_every_declared_function(L):
                           "nosa_sparse_attend", "nosa_decode_step", "nosa_prefill_sparse",
                           "nosa_prefill_sparse_workspace_size", "nosa_offload_decode_step",
                           "nosa_offload_workspace_size", "nosa_pack_qkv_weights",
-                          "nosa_qkv_rope_append", "nosa_layer_decode_step"}
+                          "nosa_qkv_rope_append", "nosa_layer_decode_step",
+                          "nosa_decode_step_static"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert nosa.abi_version() == 3
+    assert nosa.abi_version() == 4
     for s in range(6):
         assert nosa.status_string(s)
     assert nosa.status_string(0) == "ok"
@@ -134,6 +135,35 @@ def test_decode_step_host_errors(L):
     assert call(B=0) == 0                          # empty batch: nothing to do
     bad = nosa.params(window=100)
     assert call(p=bad) == 2
+
+
+def test_decode_step_static_host_errors(L):
+    """The entry point without a workspace: the same argument checks, and a
+    step whose partials would not fit the static scratch array is rejected
+    with NOSA_ERR_WORKSPACE before anything is enqueued."""
+    p = nosa.params()
+    call = lambda **kw: L.nosa_decode_step_static(
+        ctypes.byref(kw.get("p", p)), ctypes.byref(kw.get("kv", _kv(max_blocks=kw.get("mb", 256)))),
+        kw.get("q", FAKE), kw.get("cu", FAKE), kw.get("B", 8), kw.get("Lk", 16384),
+        kw.get("out", FAKE), None, kw.get("sel", None), kw.get("cnt", None), None, None)
+    assert call(q=None) == 1
+    assert call(out=None) == 1
+    assert call(sel=FAKE) == 1
+    assert call(mb=100) == 2
+    assert call(B=0) == 0
+    assert call(p=nosa.params(window=100)) == 2
+    # the largest step that fits and the first that does not
+    need = lambda B: nosa.nosa_workspace_size(p, B, 1, 16384)
+    B = 8
+    while need(B * 2) <= nosa.STATIC_SCRATCH_BYTES:
+        B *= 2
+    assert need(B) <= nosa.STATIC_SCRATCH_BYTES < need(B * 2)
+    assert call(B=B * 2) == 4
+    assert call(B=4096, Lk=65536, mb=1024) == 4
+    import re
+    m = re.search(r"#define NOSA_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)",
+                  open(os.path.join(ROOT, "include", "nosa.h")).read())
+    assert int(m.group(1)) << int(m.group(2)) == nosa.STATIC_SCRATCH_BYTES
 
 
 def test_other_entry_points_host_errors(L):

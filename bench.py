@@ -45,7 +45,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
 HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes
 LAYERS = 8
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention-decode-b8-16k_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode-b8-16k_traffic.md")
+TRACE_FILE = os.path.join(ROOT, "profiles", "decode-b8-16k_kernel_trace.md")
 CALIB_BYTES = 256 << 20   # bytes read (and written) by the calibration copy
 
 
@@ -60,10 +61,11 @@ def sources_sha256():
     return h.hexdigest()
 
 
-def recorded_traffic(workload):
-    """Bytes per attention launch from the committed counter summary, or None
-    when it is missing, covers another workload or was taken on other kernel
-    sources."""
+def recorded_traffic(workload, kind):
+    """HBM bytes per decode step (kind "step": its three kernels) or per
+    stand-alone attention launch (kind "attention") from the committed counter
+    summary, or None when it is missing, covers another workload or was taken
+    on other kernel sources."""
     if workload != "decode-b8-16k":
         return None
     try:
@@ -75,7 +77,7 @@ def recorded_traffic(workload):
                     vals[k] = v.strip("` ")
         if vals.get("sources_sha256") != sources_sha256():
             return None
-        return int(vals["attention_traffic_bytes_per_launch"])
+        return int(vals[f"{kind}_traffic_bytes"])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -102,18 +104,23 @@ def algorithmic_bytes(w, lens, append: bool):
     return step, attn
 
 
-def build_layers(w, nsteps, device="cuda"):
+def build_layers(w, nsteps, device="cuda", nlayers=LAYERS, full_kc=False):
+    """nlayers independent caches of workload w (seeds differ).  Pooled keys
+    are built for the tokens before the first decode position, or with
+    full_kc for every stored token (then any decode position can run in any
+    order: a step reads only the keys of its own tokens and re-appends the
+    key its token completes, bit for bit the same)."""
     import torch
     from block_sparse_attention_nosa_amd import nosa, synth
     layers = []
-    for li in range(LAYERS):
+    for li in range(nlayers):
         wl = synth.Workload(**{**w.__dict__, "seed": w.seed + 7919 * li, "meta": {}})
         inp = synth.make_inputs(wl, device=device)
         pg = synth.to_paged(inp, wl, device=device)
         kv = nosa.paged_kv(pg["k_pool"], pg["v_pool"], pg["kc_pool"], pg["block_table"])
         p = nosa.params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.kernel,
                         w.stride, w.topk, w.window, locality=w.locality)
-        lens0 = [L - 1 for L in w.lens]
+        lens0 = [L + w.extra_tokens if full_kc else L - 1 for L in w.lens]
         nosa.nosa_compress_keys(p, kv, synth.cu_from_lens(lens0, device), None, w.batch,
                                 max(lens0))
         layers.append(dict(inp=inp, pg=pg, kv=kv, p=p))
@@ -121,14 +128,150 @@ def build_layers(w, nsteps, device="cuda"):
     return layers
 
 
+def step_positions(npos, steps, replays):
+    """Decode position of every step of `replays` timed replays of `steps`
+    steps: spread evenly, in order, over all npos positions (each position at
+    least once when replays * steps >= npos), so window shifts (a new block)
+    and pooled-key appends fall inside the timed region whatever `steps` is."""
+    total = steps * replays
+    return [g * npos // total for g in range(total)]
+
+
+def time_decode(w, steps, warmup, min_replays=5, nlayers=LAYERS, check=True, static=False):
+    """Whole decode steps of workload w (one nosa_decode_step call on the
+    batch each): `warmup` eager steps, then replays of `steps` graph-captured
+    steps each, timed one replay at a time with events on the launch stream
+    between device synchronisations.  Step g of the run uses layer cache
+    g % nlayers at position step_positions(...)[g].  Returns the median and
+    every replay's time per step, the mean algorithmic bytes per step and the
+    objects the caller reuses."""
+    import math
+    import numpy as np
+    import torch
+    from block_sparse_attention_nosa_amd import nosa, synth
+    nsteps = w.extra_tokens + 1
+    layers = build_layers(w, nsteps, nlayers=nlayers, full_kc=True)
+    B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    lens_at = [[L + t for L in w.lens] for t in range(nsteps)]
+    cu_at = [synth.cu_from_lens(l, "cuda") for l in lens_at]
+    maxL = max(lens_at[-1])
+    p = layers[0]["p"]
+    ws = torch.zeros(nosa.nosa_workspace_size(p, B, 1, maxL), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, d, device="cuda")
+    lse = torch.empty(B, Hq, device="cuda")
+    max_sel = w.topk + w.window // w.block_size
+    sels = [torch.empty(B, 1, Hkv, max_sel, dtype=torch.int32, device="cuda") for _ in layers]
+    cnts = [torch.empty(B, 1, Hkv, dtype=torch.int32, device="cuda") for _ in layers]
+    qs = [l["inp"]["q"] for l in layers]
+    replays = max(min_replays, math.ceil(nsteps / max(1, steps)))
+    pos = step_positions(nsteps, steps, replays)
+
+    def step(g, t):
+        L = layers[g % nlayers]
+        if static:
+            nosa.nosa_decode_step_static(L["p"], L["kv"], qs[g % nlayers], cu_at[t], B, maxL,
+                                         out, lse, sel_idx=sels[g % nlayers],
+                                         sel_count=cnts[g % nlayers])
+        else:
+            nosa.nosa_decode_step(L["p"], L["kv"], qs[g % nlayers], cu_at[t], B, maxL, out, lse,
+                                  ws, sel_idx=sels[g % nlayers], sel_count=cnts[g % nlayers])
+
+    for i in range(warmup):
+        step(i, pos[i % len(pos)])
+    torch.cuda.synchronize()
+    # one replay = graphs of at most 256 steps each, replayed back to back
+    graphs = []
+    for r in range(replays):
+        gs = []
+        for c0 in range(0, steps, 256):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(c0, min(steps, c0 + 256)):
+                    step(r * steps + i, pos[r * steps + i])
+            gs.append(g)
+        graphs.append(gs)
+    stream = torch.cuda.current_stream()
+    if check:  # the replays run the steps: the last step's output is rebuilt from poison
+        out.fill_(float("nan"))
+        for g in graphs[0]:
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all(), "graph replay did not run the decode steps"
+    times = []
+    for r in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for g in graphs[r]:
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / steps)
+    step_bytes = float(np.mean([algorithmic_bytes(w, lens_at[t], (lens_at[t][0] - w.kernel) % w.stride == 0)[0]
+                                for t in pos]))
+    appends = sum(1 for t in pos if (lens_at[t][0] - w.kernel) % w.stride == 0)
+    shifts = sum(1 for t in pos if (lens_at[t][0] - 1) % w.block_size == 0)
+    del graphs
+    return dict(ms_per_step=float(np.median(times)), replay_ms=times, step_bytes=step_bytes,
+                replays=replays, positions=len(set(pos)), append_steps=appends,
+                shift_steps=shifts, layers=layers, lens_at=lens_at, cu_at=cu_at, maxL=maxL, ws=ws,
+                out=out, lse=lse, sels=sels, cnts=cnts, qs=qs, nsteps=nsteps)
+
+
+def copy_bandwidth(nbytes=2 << 30, reps=5):
+    """A plain device-to-device copy of nbytes (read + write), median of
+    reps: GB/s of bytes moved (2 nbytes per copy)."""
+    import numpy as np
+    import torch
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (float(np.median(ts)) * 1e-3) / 1e9
+
+
+def trace_average_us(path, kernel_prefix):
+    """Average duration of a kernel in a committed kernel-trace summary, if
+    the summary was taken on the current kernel sources."""
+    try:
+        txt = open(path).read()
+    except OSError:
+        return None
+    if f"sources_sha256: {sources_sha256()}" not in txt:
+        return None
+    for line in txt.splitlines():
+        if line.startswith("| `") and kernel_prefix in line:
+            cells = [c.strip() for c in line.strip("|").split("|")]
+            return float(cells[2])
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2048)  # multiple of 256, or <= 512
+    ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--replays", type=int, default=5,
+                    help="timed replays of --steps steps (at least 5; more when needed to cover "
+                         "every decode position); the line reports their median")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other decode workloads (varlen batch 32, 64K batch 16) that "
+                         "the default run also times")
+    ap.add_argument("--static", action="store_true",
+                    help="time nosa_decode_step_static (no workspace) instead of nosa_decode_step")
     ap.add_argument("--locality", type=float, default=0.0,
                     help="share of the top-k budget forced to the blocks before the window")
     ap.add_argument("--prompt", type=int, default=0, metavar="TOKENS",
@@ -149,6 +292,9 @@ def main():
                     help="time the attention layer's decode step from hidden states of this "
                          "width (QKV projection + rotary encoding + KV write, then the sparse "
                          "attention) instead of the step from ready queries")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="measure the chip's read ceilings instead: a 2 GiB stream read, a 2 GiB "
+                         "copy and a gather of 32 KB pages in random order")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run the calibration copy and the kernels once each for counters")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -169,6 +315,8 @@ def main():
     import torch
     from block_sparse_attention_nosa_amd import nosa, synth
 
+    if args.ceiling:
+        return ceiling_main(args)
     w = synth.config(args.config)
     if args.prompt:
         w = synth.Workload(lens=[args.prompt], q_lens=[args.prompt], topk=64, planted=0,
@@ -184,78 +332,46 @@ def main():
         return front_main(w, args)
     if w.q_lens is not None:
         return prefill_main(w, args)
-    nsteps = w.extra_tokens + 1
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     t_setup = time.time()
-    layers = build_layers(w, nsteps)
     B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
-    lens_at = [[L + t for L in w.lens] for t in range(nsteps)]
-    cu_at = [synth.cu_from_lens(l, "cuda") for l in lens_at]
-    maxL = max(lens_at[-1])
-    p = layers[0]["p"]
-    ws = torch.zeros(nosa.nosa_workspace_size(p, B, 1, maxL), dtype=torch.uint8, device=dev)
-    out = torch.empty(B, Hq, d, device=dev)
-    lse = torch.empty(B, Hq, device=dev)
-    max_sel = w.topk + w.window // w.block_size
-    sels = [torch.empty(B, 1, Hkv, max_sel, dtype=torch.int32, device=dev) for _ in layers]
-    cnts = [torch.empty(B, 1, Hkv, dtype=torch.int32, device=dev) for _ in layers]
-    qs = [l["inp"]["q"] for l in layers]
-    stream = torch.cuda.current_stream()
-    print(f"[bench] setup {time.time() - t_setup:.1f}s; workload {w.name}: B={B} heads={Hq}/{Hkv} "
-          f"L={w.lens[0]}..{maxL} topk={w.topk} layers={LAYERS}", file=sys.stderr, flush=True)
-
     if args.pmc_probe:
+        nsteps = w.extra_tokens + 1
+        layers = build_layers(w, nsteps)
+        lens_at = [[L + t for L in w.lens] for t in range(nsteps)]
+        cu_at = [synth.cu_from_lens(l, "cuda") for l in lens_at]
+        maxL = max(lens_at[-1])
+        ws = torch.zeros(nosa.nosa_workspace_size(layers[0]["p"], B, 1, maxL), dtype=torch.uint8,
+                         device=dev)
+        out, lse = torch.empty(B, Hq, d, device=dev), torch.empty(B, Hq, device=dev)
+        max_sel = w.topk + w.window // w.block_size
+        sels = [torch.empty(B, 1, Hkv, max_sel, dtype=torch.int32, device=dev) for _ in layers]
+        cnts = [torch.empty(B, 1, Hkv, dtype=torch.int32, device=dev) for _ in layers]
+        qs = [l["inp"]["q"] for l in layers]
         return pmc_probe(w, layers, lens_at, cu_at, maxL, ws, out, lse, sels, cnts, qs)
 
-    def step(i):
-        li = i % LAYERS
-        t = (i // LAYERS) % nsteps
-        L = layers[li]
-        # launched on the current stream (the capture stream while capturing)
-        nosa.nosa_decode_step(L["p"], L["kv"], qs[li], cu_at[t], B, maxL, out, lse, ws,
-                              sel_idx=sels[li], sel_count=cnts[li])
-        return t
-
-    # The steps are captured in a HIP graph (the library launches on the
-    # capture stream); replaying it removes host launch cost from the timing.
-    chunk = args.steps if args.steps <= 512 or args.steps % 256 else 256
-    reps = args.steps // chunk
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        ts = [step(args.warmup + i) for i in range(chunk)]
-    graph.replay()
-    torch.cuda.synchronize()
-    # the replay must have run the steps: the outputs of the last captured
-    # step are recomputed from a poisoned buffer
-    out.fill_(float("nan"))
-    graph.replay()
-    torch.cuda.synchronize()
-    assert torch.isfinite(out).all(), "graph replay did not run the decode steps"
-    # ---- timed region: K whole decode steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / args.steps
-    step_bytes = np.mean([algorithmic_bytes(w, lens_at[t], (lens_at[t][0] - w.kernel) % w.stride == 0)[0]
-                          for t in ts])
+    # ---- timed region: K whole decode steps per replay, median of the replays
+    r = time_decode(w, args.steps, args.warmup, max(5, args.replays), static=args.static)
+    ms_step, step_bytes = r["ms_per_step"], r["step_bytes"]
     tokens_per_s = B / (ms_step * 1e-3)
-    print(f"[bench] {args.steps} steps in {ms_total:.2f} ms -> {ms_step * 1e3:.2f} us/step, "
-          f"{step_bytes / 1e6:.2f} MB/step, {step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s",
-          file=sys.stderr, flush=True)
+    step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    print(f"[bench] setup+timing {time.time() - t_setup:.1f}s; workload {w.name}: B={B} "
+          f"heads={Hq}/{Hkv} L={w.lens[0]}..{r['maxL']} topk={w.topk} layers={LAYERS}; "
+          f"{r['replays']} replays of {args.steps} steps over {r['positions']} positions "
+          f"({r['append_steps']} appending, {r['shift_steps']} starting a block): "
+          f"median {ms_step * 1e3:.2f} us/step (replays "
+          f"{', '.join(f'{x * 1e3:.2f}' for x in r['replay_ms'])}), "
+          f"{step_bytes / 1e6:.2f} MB/step, {step_gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    layers, lens_at, cu_at, maxL = r["layers"], r["lens_at"], r["cu_at"], r["maxL"]
+    nsteps = r["nsteps"]
+    timing = {"replays": r["replays"], "steps_per_replay": args.steps, "statistic": "median",
+              "replay_us_per_step": [round(x * 1e3, 3) for x in r["replay_ms"]],
+              "decode_positions": r["positions"], "appending_steps": r["append_steps"],
+              "block_starting_steps": r["shift_steps"]}
 
-    # ---- dominant kernel: the sparse attention over the kept pages (one
-    # launch of nosa_sparse_attend = one kernel), timed alone with events on
-    # its launch stream around a graph of 256 launches over the same layers
-    # and positions
+    # ---- the stand-alone attention (nosa_sparse_attend: attend_kernel +
+    # merge) on the steps' selections, a 256-launch graph timed with events
     na = 256
     attn_bytes = []
     ga = torch.cuda.CUDAGraph()
@@ -264,11 +380,12 @@ def main():
             li = i % LAYERS
             t = (i // LAYERS) % nsteps
             L = layers[li]
-            nosa.nosa_sparse_attend(L["p"], L["kv"], qs[li], None, cu_at[t], B, 1, maxL, sels[li],
-                                    cnts[li], out, lse, ws)
+            nosa.nosa_sparse_attend(L["p"], L["kv"], r["qs"][li], None, cu_at[t], B, 1, maxL,
+                                    r["sels"][li], r["cnts"][li], r["out"], r["lse"], r["ws"])
             attn_bytes.append(algorithmic_bytes(w, lens_at[t], False)[1])
     ga.replay()
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ea.record(stream)
     for _ in range(4):
@@ -277,12 +394,39 @@ def main():
     torch.cuda.synchronize()
     us_attn = ea.elapsed_time(eb) * 1e3 / (4 * na)
     attn_gbs = float(np.mean(attn_bytes)) / (us_attn * 1e-6) / 1e9
+    del ga, layers, r
+    torch.cuda.empty_cache()
+
+    # ---- a plain 2 GiB device-to-device copy on the same box
+    copy_gbs = copy_bandwidth()
+
+    # ---- the other decode workloads, timed in the same run (not the headline)
+    extra = {}
+    if not args.no_extra and args.config == 2 and not args.locality and not args.static:
+        for n, nl in ((3, 4), (4, 2)):
+            wx = synth.config(n)
+            wx = synth.Workload(**{**wx.__dict__, "extra_tokens": 15})
+            rx = time_decode(wx, 64, 8, 5, nlayers=nl)
+            gbs = rx["step_bytes"] / (rx["ms_per_step"] * 1e-3) / 1e9
+            extra[wx.name] = {"us_per_step": round(rx["ms_per_step"] * 1e3, 2),
+                              "tokens_per_s": round(wx.batch / (rx["ms_per_step"] * 1e-3), 1),
+                              "algorithmic_bytes": int(rx["step_bytes"]),
+                              "achieved_gbs": round(gbs, 1),
+                              "frac": round(gbs / HBM_PEAK_GBS, 4),
+                              "replays": rx["replays"], "steps_per_replay": 64,
+                              "layer_caches": nl, "decode_positions": 16}
+            print(f"[bench] {wx.name}: {rx['ms_per_step'] * 1e3:.2f} us/step, "
+                  f"{gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.3f})", file=sys.stderr, flush=True)
+            del rx
+            torch.cuda.empty_cache()
 
     # ---- CPU reference on a bounded sample of the same workload
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(w, layers[0], lens_at, args.cpu_sample_seconds)
+        cpu = cpu_baseline(w, args.cpu_sample_seconds)
 
+    top_us = trace_average_us(TRACE_FILE, "top_kernel<") if w.name == "decode-b8-16k" else None
+    top_bytes = algorithmic_bytes(w, w.lens, False)[1]
     ctx_name = (f"{round((w.lens[0] - 1) / 1024)}K" if len(set(w.lens)) == 1 else "varlen")
     res = {
         "metric": f"sparse-attn decode tokens/s at {ctx_name} ctx, batch {B}; "
@@ -302,15 +446,30 @@ def main():
                    "head_dim": d, "context": w.lens[0] - 1, "decode_steps": nsteps,
                    "topk_blocks": w.topk, "window_tokens": w.window, "block": w.block_size,
                    "pool_kernel": w.kernel, "pool_stride": w.stride, "layer_caches": LAYERS,
-                   "locality": w.locality},
-        "step_hbm": {"algorithmic_bytes": int(step_bytes),
-                     "achieved_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
-                     "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "roofline": {"kernel": "attend_kernel (nosa_sparse_attend: attention over the kept pages + merge)", "bound": "hbm",
-                     "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(w.name),
-                     "us_per_launch": round(us_attn, 3),
-                     "algorithmic_bytes_per_launch": int(np.mean(attn_bytes))},
+                   "locality": w.locality, "entry_point": "nosa_decode_step_static"
+                   if args.static else "nosa_decode_step"},
+        "timing": timing,
+        "roofline": {"kernel": "nosa_decode_step: score_kernel + top_kernel + merge_kernel "
+                               "(the whole timed step)",
+                     "bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(w.name, "step"),
+                     "algorithmic_bytes_per_step": int(step_bytes),
+                     "frac_of_measured_copy": round(step_gbs / copy_gbs, 4),
+                     "measured_copy_gbs": round(copy_gbs, 1),
+                     "dominant_kernel": None if top_us is None else {
+                         "name": "top_kernel (selection + window and top-k pages)",
+                         "us_per_launch": top_us, "algorithmic_bytes": int(top_bytes),
+                         "achieved": round(top_bytes / (top_us * 1e-6) / 1e9, 1),
+                         "frac": round(top_bytes / (top_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "source": os.path.relpath(TRACE_FILE, ROOT)}},
+        "attend_only": {"kernel": "nosa_sparse_attend (attend_kernel + merge_kernel)",
+                        "us_per_launch": round(us_attn, 3),
+                        "algorithmic_bytes_per_launch": int(np.mean(attn_bytes)),
+                        "achieved": round(attn_gbs, 1),
+                        "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                        "traffic": recorded_traffic(w.name, "attention")},
+        "other_workloads": extra or None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -724,45 +883,65 @@ def pmc_probe(w, layers, lens_at, cu_at, maxL, ws, out, lse, sels, cnts, qs):
     for li, L in enumerate(layers):
         nosa.nosa_decode_step(L["p"], L["kv"], qs[li], cu_at[0], B, maxL, out, lse, ws,
                               sel_idx=sels[li], sel_count=cnts[li])
+        torch.cuda.synchronize()
         nosa.nosa_sparse_attend(L["p"], L["kv"], qs[li], None, cu_at[0], B, 1, maxL, sels[li],
                                 cnts[li], out, lse, ws)
-    torch.cuda.synchronize()
-    attn = algorithmic_bytes(w, lens_at[0], False)[1]
-    print(f"[pmc-probe] done; attention algorithmic bytes per launch {attn}", file=sys.stderr)
+        torch.cuda.synchronize()
+    step, attn = algorithmic_bytes(w, lens_at[0], False)
+    print(f"[pmc-probe] done; algorithmic bytes per step {step}, per attention launch {attn}",
+          file=sys.stderr)
 
 
-def _pmc_rows(d, counter):
-    """(kernel name, value) per dispatch of one counter from a rocprofv3 csv run."""
+def _csv_rows(d, pattern):
     import csv
     import glob
-    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
     if not files:
-        raise SystemExit(f"no counter_collection.csv under {d}")
+        raise SystemExit(f"no {pattern} under {d}")
     rows = []
     for f in files:
         with open(f) as fh:
-            for r in csv.DictReader(fh):
-                if r.get("Counter_Name") == counter:
-                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+            rows.extend(csv.DictReader(fh))
     return rows
+
+
+def _pmc_rows(d, counter):
+    """(dispatch id, kernel name, value) per dispatch of one counter from a
+    rocprofv3 csv run, in dispatch order."""
+    rows = [(int(r.get("Dispatch_Id", 0) or 0), r["Kernel_Name"], float(r["Counter_Value"]))
+            for r in _csv_rows(d, "*counter_collection.csv") if r.get("Counter_Name") == counter]
+    return sorted(rows)
 
 
 def pmc_summary(fetch_dir, write_dir):
     """Markdown summary of FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel,
-    scaled to bytes by the calibration copy, and the attention's traffic per
-    launch (its attention kernel plus its merge)."""
+    scaled to bytes by the calibration copy: the traffic of one decode step
+    (its scoring, top and merge dispatches) and of one stand-alone attention
+    launch (its attention and merge dispatches)."""
     import numpy as np
     from block_sparse_attention_nosa_amd import synth
     w = synth.config(2)
-    attn_alg = algorithmic_bytes(w, w.lens, False)[1]
-    per = {}
+    step_alg, attn_alg = algorithmic_bytes(w, w.lens, False)
+    per = {}   # role -> counter -> values
+    names = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        for name, v in _pmc_rows(d, counter):
-            per.setdefault(name, {}).setdefault(counter, []).append(v)
-    calib = [n for n in per if "bitwise_not" in n.lower() or "BitwiseNot" in n]
-    if not calib:
+        prev = None
+        for _, name, v in _pmc_rows(d, counter):
+            if "bitwise_not" in name.lower() or "BitwiseNot" in name:
+                role = "calibration copy"
+            elif "nosa::" not in name:
+                prev = None
+                continue
+            elif "merge_kernel" in name:
+                role = "merge_kernel (decode step)" if prev == "top" else "merge_kernel (attention)"
+            else:
+                role = name.split("(")[0].replace("void ", "")
+                prev = "top" if "top_kernel" in name else ("attend" if "attend_kernel" in name else prev)
+            names[role] = name
+            per.setdefault(role, {}).setdefault(counter, []).append(v)
+    c = per.get("calibration copy")
+    if not c:
         raise SystemExit("calibration copy kernel not found")
-    c = per[calib[0]]
     f_fetch = CALIB_BYTES / (np.median(c["FETCH_SIZE"]) * 1024.0)
     f_write = CALIB_BYTES / (np.median(c["WRITE_SIZE"]) * 1024.0)
     lines = ["# HBM traffic of the decode-b8-16k kernels (rocprofv3 counters)", "",
@@ -770,82 +949,205 @@ def pmc_summary(fetch_dir, write_dir):
              "    rocprofv3 --pmc FETCH_SIZE -d DIR_F -o run --output-format csv -- python3 bench.py --pmc-probe",
              "    rocprofv3 --pmc WRITE_SIZE -d DIR_W -o run --output-format csv -- python3 bench.py --pmc-probe",
              "    python3 bench.py --pmc-summary DIR_F DIR_W", "",
+             "The probe runs one decode step (nosa_decode_step) and one stand-alone attention "
+             "(nosa_sparse_attend) on each of the eight layer caches at the first decode position.",
+             "",
              f"Calibration: a plain copy reading and writing {CALIB_BYTES >> 20} MiB; "
              f"bytes per counter KiB: fetch {f_fetch * 1024:.1f}, write {f_write * 1024:.1f} "
              f"(factors {f_fetch:.3f} / {f_write:.3f} of the nominal 1024).", "",
              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched MB | written MB |",
              "|---|---:|---:|---:|---:|---:|"]
     traffic = {}
-    for name in sorted(per):
-        v = per[name]
+    for role in sorted(per):
+        v = per[role]
         if "FETCH_SIZE" not in v or "WRITE_SIZE" not in v:
-            continue
-        if not ("nosa::" in name or name in calib):
             continue
         fk, wk = float(np.mean(v["FETCH_SIZE"])), float(np.mean(v["WRITE_SIZE"]))
         fb, wb = fk * 1024 * f_fetch, wk * 1024 * f_write
-        traffic[name] = fb + wb
-        lines.append(f"| `{name[:90]}` | {len(v['FETCH_SIZE'])} | {fk:.0f} | {wk:.0f} | "
+        traffic[role] = fb + wb
+        lines.append(f"| `{role}` | {len(v['FETCH_SIZE'])} | {fk:.0f} | {wk:.0f} | "
                      f"{fb / 1e6:.2f} | {wb / 1e6:.2f} |")
-    attn_k = [n for n in traffic if "attend_kernel<" in n]
-    merge_k = [n for n in traffic if "merge_kernel" in n]
-    if not attn_k or not merge_k:
-        raise SystemExit("attention kernels not found")
-    attn_t = traffic[attn_k[0]] + traffic[merge_k[0]]
-    lines += ["", "The attention launch (nosa_sparse_attend) is its attention kernel plus its merge "
-              "kernel; the merge row averages the dispatches of both entry points.", "",
-              f"- attention_traffic_bytes_per_launch: {int(attn_t)}",
-              f"- attention_algorithmic_bytes_per_launch: {int(attn_alg)}",
-              f"- traffic_over_algorithmic: {attn_t / attn_alg:.3f}",
+
+    def pick(part):
+        ks = [k for k in traffic if part in k]
+        if not ks:
+            raise SystemExit(f"{part} not found")
+        return traffic[ks[0]]
+    step_t = pick("score_kernel") + pick("top_kernel") + pick("merge_kernel (decode step)")
+    attn_t = pick("attend_kernel") + pick("merge_kernel (attention)")
+    lines += ["", "A decode step is its scoring, top and merge dispatches; the stand-alone "
+              "attention its attention and merge dispatches (each merge dispatch is attributed "
+              "to the launch before it).", "",
+              f"- step_traffic_bytes: {int(step_t)}",
+              f"- step_algorithmic_bytes: {int(step_alg)}",
+              f"- step_traffic_over_algorithmic: {step_t / step_alg:.3f}",
+              f"- attention_traffic_bytes: {int(attn_t)}",
+              f"- attention_algorithmic_bytes: {int(attn_alg)}",
+              f"- attention_traffic_over_algorithmic: {attn_t / attn_alg:.3f}",
               f"- sources_sha256: {sources_sha256()}"]
     print("\n".join(lines))
 
 
 def trace_summary(d):
-    """Markdown rows (library kernels) of a rocprofv3 kernel_stats.csv."""
-    import csv
-    import glob
-    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
-    if not files:
-        raise SystemExit(f"no kernel_stats.csv under {d}")
+    """Markdown rows (library kernels) of a rocprofv3 kernel_stats.csv, and
+    the launch-level timeline of the decode step from the kernel trace:
+    per-kernel duration and the gap before it, medians over the steps (the
+    tracer itself stretches the gaps)."""
+    import numpy as np
     print("| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |")
     print("|---|---:|---:|---:|---:|---:|")
-    with open(files[0]) as fh:
-        for r in csv.DictReader(fh):
-            if "nosa::" not in r["Name"]:
-                continue
-            name = r["Name"].split("(")[0] if r["Name"].startswith("nosa::") else r["Name"].split("(nosa")[0]
-            print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                  f"{float(r['Percentage']):.1f}% |")
+    for r in _csv_rows(d, "*kernel_stats.csv"):
+        if "nosa::" not in r["Name"]:
+            continue
+        name = r["Name"].split("(")[0] if r["Name"].startswith("nosa::") else r["Name"].split("(nosa")[0]
+        print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+              f"{float(r['Percentage']):.1f}% |")
+    try:
+        tr = _csv_rows(d, "*kernel_trace.csv")
+    except SystemExit:
+        tr = []
+    ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in tr)
+    seq = []  # (score, top, merge) triples that follow each other
+    for i in range(len(ev) - 2):
+        a, b, c = ev[i], ev[i + 1], ev[i + 2]
+        if "score_kernel" in a[2] and "top_kernel" in b[2] and "merge_kernel" in c[2]:
+            seq.append((a, b, c))
+    if seq:
+        dur = lambda k: np.median([(t[k][1] - t[k][0]) / 1e3 for t in seq])
+        gap = lambda k: np.median([(t[k][0] - t[k - 1][1]) / 1e3 for t in seq])
+        whole = np.median([(t[2][1] - t[0][0]) / 1e3 for t in seq])
+        print("")
+        print(f"Decode-step timeline under the tracer (medians over {len(seq)} steps, us): "
+              f"score_kernel {dur(0):.2f} | gap {gap(1):.2f} | top_kernel {dur(1):.2f} | "
+              f"gap {gap(2):.2f} | merge_kernel {dur(2):.2f} | whole step {whole:.2f}")
+    print("")
+    print(f"- sources_sha256: {sources_sha256()}")
 
 
-def cpu_baseline(w, layer, lens_at, budget_s):
-    """The CPU reference as it stands, on host copies of layer 0: whole decode
-    steps (pooling, scoring, selection, attention) for the full batch, repeated
-    until about `budget_s` seconds of work."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, budget_s):
+    """The CPU reference as it stands, on host copies of layer 0 of the timed
+    workload: consecutive decode steps from the first position, each the
+    method's step as the GPU runs it -- append the pooled key the current
+    token completes (the earlier keys are kept from the step before), score,
+    pool, select, attend -- with every host thread (OpenMP over sequences and
+    heads) for about budget_s seconds, then with one thread for a third of
+    that.  Packing each step's live tokens for the reference is not timed."""
     import numpy as np
     import torch
     from block_sparse_attention_nosa_amd import synth
     from oracle import oracle as ora
 
-    inp = layer["inp"]
+    wl = synth.Workload(**{**w.__dict__, "meta": {}})  # layer 0's seed
+    inp = synth.make_inputs(wl, device="cuda")
     host = dict(k=inp["k"].cpu(), v=inp["v"].cpu(), cu_k_store=inp["cu_k_store"].cpu())
     q = synth.bits(inp["q"])
+    del inp
     op = ora.Params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.kernel, w.stride,
                     w.topk, w.window, locality=w.locality)
-    n, t0 = 0, time.time()
-    while True:
-        k, v, cu = synth.packed_live(host, w, n % len(lens_at))
-        ora.forward(op, q, None, synth.bits(k), synth.bits(v), cu.numpy())
-        n += 1
-        if time.time() - t0 >= budget_s or n >= 64:
-            break
-    dt = time.time() - t0
-    return {"value": round(w.batch * n / dt, 2), "unit": "tokens/s", "cores": ora.num_threads(),
+    nsteps = w.extra_tokens + 1
+    k0, _, cu0 = synth.packed_live(host, w, -1)  # the tokens before the first position
+    max_nc = ora.num_keys(max(w.lens) + w.extra_tokens, op)
+    all_threads = ora.num_threads()
+
+    def run(threads, budget):
+        ora.set_num_threads(threads)
+        kc = ora.compress_keys(op, synth.bits(k0), cu0.numpy(), max_nc=max_nc)
+        n, spent = 0, 0.0
+        while n < nsteps and spent < budget:
+            k, v, cu = synth.packed_live(host, w, n)
+            kb, vb, cun = synth.bits(k), synth.bits(v), cu.numpy()
+            valid = np.array([L - 1 for L in (cun[1:] - cun[:-1])], np.int32)
+            t0 = time.time()
+            ora.append_keys(op, kb, cun, valid, kc)
+            sc = ora.block_scores(op, q, None, kc, cun)
+            sel, cnt = ora.select_blocks(op, sc, None, cun)
+            ora.sparse_attend(op, q, None, kb, vb, cun, sel, cnt)
+            spent += time.time() - t0
+            n += 1
+        return n, spent
+
+    n, dt = run(all_threads, budget_s)
+    n1, dt1 = run(1, budget_s / 3)
+    ora.set_num_threads(all_threads)
+    return {"value": round(w.batch * n / dt, 2), "unit": "tokens/s", "cores": all_threads,
             "kind": "oracle",
-            "sample": f"{n} whole decode steps of {w.name} (batch {w.batch}, layer 0, positions "
-                      f"0..{n - 1}) on the host, fp64 reference with OpenMP over (sequence, head)"}
+            "sample": f"{n} consecutive decode steps of {w.name} (batch {w.batch}, layer 0, "
+                      f"positions 0..{n - 1}: pooled-key append, scoring, pooling, selection, "
+                      f"attention) on the host, fp64 reference, OpenMP over (sequence, head)",
+            "one_thread": {"value": round(w.batch * n1 / dt1, 2), "unit": "tokens/s",
+                           "steps": n1},
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count()}
+
+
+def ceiling_main(args):
+    """Read ceilings of the device: 2 GiB read as a stream (pages in order)
+    and as a gather of 32 KB pages in random order (the probe kernel of
+    libnosa_ceiling.so, a sweep of workgroup counts, median of 5 launches
+    each), and a 2 GiB device-to-device copy."""
+    import ctypes
+    import numpy as np
+    import torch
+    from block_sparse_attention_nosa_amd import build
+    if not os.path.exists(build.PROBE_LIB):
+        raise SystemExit(f"{build.PROBE_LIB} is missing: build it first")
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    lib.nosa_probe_read_pages.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.nosa_probe_read_pages.restype = ctypes.c_int
+    page, nbytes = 32768, 2 << 30
+    npages = nbytes // page
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").random_()
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    orders = {"stream": torch.arange(npages, dtype=torch.int32, device="cuda"),
+              "random_pages": torch.randperm(npages, generator=gen, device="cuda").to(torch.int32)}
+    stream = torch.cuda.current_stream()
+    res = {}
+    for kind, order in orders.items():
+        sweep = {}
+        for wgs in (256, 512, 1024, 2048, 4096):
+            sink = torch.empty(wgs * 4 * 64, dtype=torch.int32, device="cuda")
+            launch = lambda: lib.nosa_probe_read_pages(src.data_ptr(), order.data_ptr(), npages,
+                                                        wgs, sink.data_ptr(), stream.cuda_stream)
+            assert launch() == 0
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                launch()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            sweep[wgs] = round(nbytes / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+        best = max(sweep, key=sweep.get)
+        res[kind] = {"gbs": sweep[best], "workgroups": best, "sweep_gbs": sweep,
+                     "frac": round(sweep[best] / HBM_PEAK_GBS, 4)}
+        print(f"[ceiling] {kind}: {sweep}", file=sys.stderr, flush=True)
+    del src
+    torch.cuda.empty_cache()
+    copy = copy_bandwidth()
+    out = {"metric": "device read ceilings (2 GiB)", "value": res["random_pages"]["gbs"],
+           "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "dtype": "bytes",
+           "data": "random 16-bit words", "config": {"workload": "read-ceilings-2g",
+                                                      "page_bytes": page, "bytes": nbytes},
+           "stream_read": res["stream"], "random_page_gather": res["random_pages"],
+           "copy_2g": {"gbs": round(copy, 1), "frac": round(copy / HBM_PEAK_GBS, 4),
+                       "note": "bytes read + bytes written"},
+           "peak_gbs": HBM_PEAK_GBS,
+           "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -146,6 +146,38 @@ int nosa_ref_compress_keys(const nosa_ref_params* p, const uint16_t* k, const in
     return 0;
 }
 
+/* The same keys for a cache that grows (a decode step appends tokens): for
+ * each sequence, only keys j in [n_c(valid_len[s]), n_c(L_s)) are computed,
+ * the keys of the first valid_len[s] tokens being already in kc; nothing
+ * else in kc is touched.  Each key is the same exact window mean as above, so
+ * appending token by token gives the full build's keys. */
+int nosa_ref_append_keys(const nosa_ref_params* p, const uint16_t* k, const int32_t* cu_k,
+                         const int32_t* valid_len, int B, int max_nc, uint16_t* kc)
+{
+    if (nosa_ref_check_params(p)) return -1;
+    const int Hkv = p->num_kv_heads, d = p->head_dim;
+    for (int s = 0; s < B; ++s) {
+        if (nosa_ref_num_keys(seq_len(cu_k, s), p->kernel, p->stride) > max_nc) return -2;
+        if (valid_len[s] < 0 || valid_len[s] > seq_len(cu_k, s)) return -3;
+    }
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int s = 0; s < B; ++s)
+        for (int g = 0; g < Hkv; ++g) {
+            const int L = seq_len(cu_k, s);
+            const int j0 = nosa_ref_num_keys(valid_len[s], p->kernel, p->stride);
+            const int nc = nosa_ref_num_keys(L, p->kernel, p->stride);
+            for (int j = j0; j < nc; ++j)
+                for (int c = 0; c < d; ++c) {
+                    double sum = 0.0;
+                    for (int t = j * p->stride; t < j * p->stride + p->kernel; ++t)
+                        sum += bf16_value(k[((size_t)(cu_k[s] + t) * Hkv + g) * d + c]);
+                    kc[(((size_t)s * Hkv + g) * max_nc + j) * d + c] =
+                        nosa_ref_bf16_round(sum / p->kernel);
+                }
+        }
+    return 0;
+}
+
 /* --------------------------------------------- 2+3. block importance ------ */
 
 /* Importance of every KV block for every query block.
@@ -474,5 +506,16 @@ int nosa_ref_num_threads(void)
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Threads the parallel loops use from now on (n >= 1). */
+void nosa_ref_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
 #endif
 }

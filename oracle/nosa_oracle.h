@@ -35,6 +35,9 @@ int nosa_ref_num_threads(void);
 
 int nosa_ref_compress_keys(const nosa_ref_params* p, const uint16_t* k, const int32_t* cu_k,
                            int B, int max_nc, uint16_t* kc);
+int nosa_ref_append_keys(const nosa_ref_params* p, const uint16_t* k, const int32_t* cu_k,
+                         const int32_t* valid_len, int B, int max_nc, uint16_t* kc);
+void nosa_ref_set_num_threads(int n);
 int nosa_ref_block_scores(const nosa_ref_params* p, const uint16_t* q, const int32_t* cu_q,
                           const uint16_t* kc, int max_nc, const int32_t* cu_k, int B,
                           int max_qblk, int max_nb, double* scores);

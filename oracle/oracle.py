@@ -85,13 +85,17 @@ def lib():
         L.nosa_ref_num_threads.restype = i
         L.nosa_ref_check_params.argtypes = [P(_Params)]
         L.nosa_ref_compress_keys.argtypes = [P(_Params), vp, vp, i, i, vp]
+        L.nosa_ref_append_keys.argtypes = [P(_Params), vp, vp, vp, i, i, vp]
+        L.nosa_ref_set_num_threads.argtypes = [i]
+        L.nosa_ref_set_num_threads.restype = None
         L.nosa_ref_block_scores.argtypes = [P(_Params), vp, vp, vp, i, vp, i, i, i, vp]
         L.nosa_ref_select_blocks.argtypes = [P(_Params), vp, vp, vp, i, i, i, i, vp, vp]
         L.nosa_ref_sparse_attend.argtypes = [P(_Params), vp, vp, vp, vp, vp, i, vp, vp, i, i,
                                              vp, vp]
         L.nosa_ref_qkv_rope.argtypes = [P(_Params), i, ctypes.c_double, vp, vp, vp, vp, i, vp,
                                         vp, vp]
-        for f in ("nosa_ref_compress_keys", "nosa_ref_block_scores", "nosa_ref_select_blocks",
+        for f in ("nosa_ref_compress_keys", "nosa_ref_append_keys", "nosa_ref_block_scores",
+                  "nosa_ref_select_blocks",
                   "nosa_ref_sparse_attend", "nosa_ref_check_params", "nosa_ref_qkv_rope"):
             getattr(L, f).restype = i
         _lib = L
@@ -177,6 +181,23 @@ def compress_keys(p: Params, k, cu_k, max_nc=None):
     kc = np.zeros((B, p.num_kv_heads, max_nc, p.head_dim), dtype=np.uint16)
     _check(lib().nosa_ref_compress_keys(ctypes.byref(p.c()), _ptr(k), _ptr(cu_k), B, max_nc,
                                         _ptr(kc)), "compress_keys")
+    return kc
+
+
+def set_num_threads(n: int) -> None:
+    lib().nosa_ref_set_num_threads(int(n))
+
+
+def append_keys(p: Params, k, cu_k, valid_len, kc):
+    """Pooled keys of a grown cache, in place: for each sequence the keys of
+    tokens past valid_len[s] (kc [B][Hkv][max_nc][d] holds the earlier ones)."""
+    k = _u16(k)
+    cu_k = _i32(cu_k)
+    valid_len = _i32(valid_len)
+    assert kc.dtype == np.uint16 and kc.flags.c_contiguous
+    B = len(cu_k) - 1
+    _check(lib().nosa_ref_append_keys(ctypes.byref(p.c()), _ptr(k), _ptr(cu_k), _ptr(valid_len),
+                                      B, kc.shape[2], _ptr(kc)), "append_keys")
     return kc
 
 

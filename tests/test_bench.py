@@ -50,6 +50,24 @@ def test_prefill_flops_of_the_131072_chunk():
 
 
 def test_traffic_is_reported_only_for_its_sources(monkeypatch):
-    assert bench.recorded_traffic("decode-varlen-b32") is None  # not measured there
+    assert bench.recorded_traffic("decode-varlen-b32", "step") is None  # not measured there
     monkeypatch.setattr(bench, "sources_sha256", lambda: "0" * 64)
-    assert bench.recorded_traffic("decode-b8-16k") is None  # kernels changed since
+    assert bench.recorded_traffic("decode-b8-16k", "step") is None  # kernels changed since
+    assert bench.trace_average_us(bench.TRACE_FILE, "top_kernel<") is None
+
+
+def test_timed_positions_cover_every_decode_position():
+    """Whatever the number of timed steps, the replays' steps run through all
+    256 decode positions in order, so appending steps (one pooled key every 16
+    tokens) and steps that start a new block are timed too."""
+    import math
+    w = synth.config(2)
+    for steps in (1, 20, 256, 2048):
+        replays = max(5, math.ceil(256 / steps))
+        pos = bench.step_positions(256, steps, replays)
+        assert len(pos) == steps * replays
+        assert set(pos) == set(range(256)), steps
+        assert pos == sorted(pos)
+        lens = [[L + t for L in w.lens] for t in pos]
+        assert any((l[0] - w.kernel) % w.stride == 0 for l in lens)
+        assert any((l[0] - 1) % w.block_size == 0 for l in lens)

@@ -225,6 +225,38 @@ def test_scores_brute_force_tiny(oracle):
                     assert sc[s, 0, g, b] == -np.inf
 
 
+def test_append_keys_token_by_token_equals_full_build(oracle):
+    """Keys appended as the cache grows token by token (decode), and in two
+    larger increments, equal the full build bit for bit; nothing outside the
+    appended range is written."""
+    p = Params(num_q_heads=4, num_kv_heads=2, head_dim=8)
+    rng = np.random.default_rng(23)
+    lens = [100, 31, 77]
+    k = random_bits(rng, (sum(lens), 2, 8))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    full = oracle.compress_keys(p, k, cu)
+    max_nc = full.shape[2]
+    grown = np.full_like(full, 0x7fc0)  # NaN bits: every key must be written
+    for s, L in enumerate(lens):
+        kc_s = grown[s:s + 1]
+        base = cu[s]
+        for t in range(1, L + 1):  # the cache holds t tokens, t - 1 of them pooled
+            sub = np.ascontiguousarray(kc_s)
+            oracle.append_keys(p, k[base:base + t], np.array([0, t], np.int32),
+                               np.array([t - 1], np.int32), sub)
+            kc_s[:] = sub
+        nc = oracle.num_keys(L, p)
+        assert np.array_equal(grown[s, :, :nc], full[s, :, :nc]), s
+        assert np.all(grown[s, :, nc:] == 0x7fc0), s
+    two = np.full_like(full, 0x7fc0)
+    half = np.array([L // 2 for L in lens], np.int32)
+    oracle.append_keys(p, k, cu, np.zeros(3, np.int32), two)   # from nothing
+    oracle.append_keys(p, k, cu, half, two)                    # again from the half: same keys
+    for s, L in enumerate(lens):
+        nc = oracle.num_keys(L, p)
+        assert np.array_equal(two[s, :, :nc], full[s, :, :nc]), s
+
+
 def test_prefill_block_scores_sum_of_single_queries(oracle):
     """For blocks whose keys every query of the q-block sees, the q-block's
     importance is the sum of the single-query (decode) importances."""

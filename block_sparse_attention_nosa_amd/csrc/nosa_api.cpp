@@ -393,9 +393,10 @@ nosa_status nosa_compress_keys(const nosa_params* params, const nosa_paged_kv* k
     Plan pl;
     st = make_plan(params, batch, max_seqlen_k, &pl);
     if (st != NOSA_OK) return st;
-    int gx = ceil_div(pl.max_nc > 0 ? pl.max_nc : 1, 16);
-    if (kc_valid_len && gx > 64) gx = 64;  // grid-stride over whatever is left to pool
-    return hip_status(launch_kc_build(pl, *kv, cu_seqlens_k, kc_valid_len, gx, as_stream(stream)));
+    // an incremental build pools an unknown share of each sequence: a bounded
+    // grid whose waves stride over whatever is left
+    const int pages = kc_valid_len && pl.max_nb > 256 ? 256 : pl.max_nb;
+    return hip_status(launch_kc_build(pl, *kv, cu_seqlens_k, kc_valid_len, pages, as_stream(stream)));
 }
 
 nosa_status nosa_block_scores(const nosa_params* params, const nosa_paged_kv* kv,
@@ -519,7 +520,7 @@ nosa_status nosa_prefill_sparse(const nosa_params* params, const nosa_paged_kv* 
     int32_t* cnt = reinterpret_cast<int32_t*>(ws + Y.off_cnt);
     const hipStream_t sm = as_stream(stream);
     const int C = Y.C, nch = ceil_div(max_seqlen, C);
-    const int gx = ceil_div(C / kPoolS + 1, 16);  // pooled keys completed by one chunk, 16 per workgroup
+    const int gx = C / kBlock + 1;  // pages holding the first token of a key one chunk completes
     for (int c = 0; c < nch; ++c) {
         hipError_t e = launch_chunk_setup(cu_seqlens, batch, pl.Lmax, c, C, cu_k_c, cu_q_c, valid_c,
                                           qbase_c, sm);

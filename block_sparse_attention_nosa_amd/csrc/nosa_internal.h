@@ -105,7 +105,7 @@ void make_pf_plan(const Plan& pl, int max_seqlen_q, PfPlan* pf);
 // ---- launchers (nosa_kernels.hip); all enqueue on `stream` and return the
 // ---- hipGetLastError() of the launches.
 hipError_t launch_kc_build(const Plan& pl, const nosa_paged_kv& kv, const int32_t* cu_k,
-                           const int32_t* valid_len, int grid_x, hipStream_t stream);
+                           const int32_t* valid_len, int max_pages, hipStream_t stream);
 hipError_t launch_scores_only(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
                               const int32_t* cu_k, const Workspace& w, float* scores_out,
                               hipStream_t stream);

@@ -76,40 +76,180 @@ __device__ __forceinline__ uint4 round8(const double (&acc)[8])
                       o[6] | (o[7] << 16));
 }
 
-// One workgroup = 16 keys x 16 channel chunks of 8.  Each thread sums the 32
-// tokens of its key for its 8 channels in fp64 (exact for bf16 inputs), then
-// scales by 1/32 (exact) and rounds once.  Keys [n_c(prev), n_c(L)) are
-// written, prev = valid_len[s] or 0 for a full rebuild.
-__global__ __launch_bounds__(256) void kc_build_kernel(
+// Pooled keys from whole K pages.  Key j pools tokens [16 j, 16 j + 32):
+// 16-token groups j and j + 1, so keys 4b, 4b+1, 4b+2 lie inside page b and
+// key 4b+3 takes the last group of page b and the first of page b+1.  A wave
+// owns `ppw` consecutive pages of one (sequence, KV head) and streams them:
+// it reads each page once, a contiguous kilobyte per load instruction (the
+// pages are stored in operand order), the next page's loads in flight while
+// the current one is summed (block-table entries read a page ahead of those),
+// and puts each page into its own 16 KB of LDS token-major.  Lane (u, c8)
+// sums channels 8 c8 .. 8 c8 + 7 of group u of the page over its 16 tokens in
+// ascending order in fp64; key 4b + u is its group sum plus that of lane
+// (u + 1, c8) (one lane rotation), key 4b - 1 the previous page's last group
+// sum plus this page's first.  Each fp64 sum of bf16 values here is exact
+// while a key's nonzero values span at most 2^40 in magnitude (they are
+// multiples of the smallest one's last bit, and 32 of them fit 53 bits), so
+// the mean, scaled by 1/32 and rounded once to bf16, is then the exact one,
+// bit for bit whatever the order of the additions.  After the wave's last
+// page, lanes u = 0 read the first group of the next page for the last key.
+// Keys [n_c(prev), n_c(L)) are written, prev = valid_len[s] or 0 for a full
+// build.  Long runs per wave keep a page of loads in flight from start to
+// end (a wave fills and drains its pipeline once), so the grid is sized to
+// about two waves per SIMD.
+//
+// LDS slot of (token x, chunk c8): 16 x + (c8 ^ swz(x)), swz(x) = (x & 3) |
+// ((x & 8) >> 1).  A wave's store of one operand run (lanes: 16 tokens x 4
+// chunks) and its loads of one token per lane group (16 chunks) then touch
+// eight different 16-byte bank groups in every group of eight lanes.
+constexpr int kKcMinPagesPerWave = 2;
+constexpr int kKcTargetWaves = 2048;
+
+__device__ __forceinline__ int kc_lds_slot(int x, int c8)
+{
+    return 16 * x + (c8 ^ ((x & 3) | ((x & 8) >> 1)));
+}
+
+__global__ __launch_bounds__(256, 2) void kc_build_kernel(
     const uint16_t* __restrict__ k_pool, uint16_t* __restrict__ kc_pool,
     const int32_t* __restrict__ table, int max_blocks, int Lmax, int Hkv,
-    const int32_t* __restrict__ cu_k, const int32_t* __restrict__ valid_len)
+    const int32_t* __restrict__ cu_k, const int32_t* __restrict__ valid_len, int ppw)
 {
+    __shared__ uint4 tile[4][BS * D / 8];  // a page per wave, 16 KB
     const int s = blockIdx.z, g = blockIdx.y;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int L = seq_len(cu_k, s, Lmax);
     int prev = valid_len ? valid_len[s] : 0;
-    prev = prev < 0 ? 0 : prev;
+    prev = prev < 0 ? 0 : (prev > L ? L : prev);
     const int j0 = dev_num_keys(prev), j1 = dev_num_keys(L);
-    const int jl = threadIdx.x >> 4, cc = threadIdx.x & 15;
+    if (j0 >= j1) return;  // (whole workgroup)
+    const int b_lo = j0 / SL, b_hi = (j1 - 1) / SL;  // pages holding the first token of a new key
+    const int ntask = (b_hi - b_lo) / ppw + 1;
     const int32_t* trow = table + (size_t)s * max_blocks;
-    for (int j = j0 + (int)blockIdx.x * 16 + jl; j < j1; j += (int)gridDim.x * 16) {
-        double acc[8];
+    const int u = lane >> 4, c8 = lane & 15;         // group u of the page, chunk c8
+    const int r16 = lane & 15, kq4 = lane >> 4;      // this lane's token and chunk in a stored run
+    const int nbr = (lane + 16) & 63;                // lane (u + 1, c8), (0, c8) for u = 3
+    uint4* t = tile[wave];
+    for (int task = (int)blockIdx.x * 4 + wave; task < ntask; task += (int)gridDim.x * 4) {
+        const int b0 = b_lo + task * ppw;
+        const int npg = min(ppw, b_hi + 1 - b0);  // pages b0 .. b0 + npg - 1
+        const int jsp = 4 * (b0 + npg - 1) + 3;   // the last page's key 4b+3
+        const bool spill = jsp >= j0 && jsp < j1;  // then page b0 + npg exists
+        // table entry of the task's page i (the spill page for i = npg when
+        // it exists; unused ones are clamped to the first page)
+        auto pid = [&](int i) {
+            return trow[b0 + ((i < npg || (i == npg && spill)) ? i : 0)];
+        };
+        // The four keys of page bb (lane (u, c8): key 4 bb + u, chunk c8, in
+        // `own`) as one contiguous 1 KB store: lane l writes slot l & 3 of
+        // chunk l >> 2, taken from lane (l & 3, l >> 2) by a rotation of
+        // lanes; keys outside [j0, j1) are left as they are.  The page's id
+        // comes from the entries above (a table load here would wait, in
+        // order, behind the prefetched page).
+        auto store_page = [&](int bb, int page, uint4 own) {
+            const int src = (lane & 3) * 16 + (lane >> 2);
+            const uint4 val = make_uint4(__shfl(own.x, src), __shfl(own.y, src),
+                                         __shfl(own.z, src), __shfl(own.w, src));
+            const int j = 4 * bb + (lane & 3);
+            if (j >= j0 && j < j1)
+                *reinterpret_cast<uint4*>(kc_pool + ((size_t)page * Hkv + g) * SL * D + lane * 8) = val;
+        };
+        auto rotate = [&](const double (&a)[8], double (&b)[8]) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-        for (int i = 0; i < kPoolK; ++i) {
-            const int t = j * kPoolS + i;
-            acc8(acc, ldg16(k_pool + ((size_t)trow[t / BS] * Hkv + g) * BS * D + k_chunk(t % BS, cc)));
+            for (int e = 0; e < 8; ++e) b[e] = __shfl(a[e], nbr);
+        };
+        int p_prev = 0, p_cur = pid(0), p_n1 = pid(1);
+        double carry[8];  // lanes u = 3: the previous page's last group sum
+#pragma unroll
+        for (int e = 0; e < 8; ++e) carry[e] = 0.0;
+        uint4 kprev = make_uint4(0, 0, 0, 0);  // lanes u < 3: key 4 (b - 1) + u, rounded
+        uint4 v[16];
+        {
+            const uint16_t* pg = k_pool + ((size_t)p_cur * Hkv + g) * BS * D + lane * 8;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) v[r] = ldg16(pg + r * 512);
         }
-        *reinterpret_cast<uint4*>(kc_page(kc_pool, trow, Hkv, g, j) + kc_chunk(j % SL, cc)) = round8(acc);
+        for (int q = 0; q < npg; ++q) {
+            // The tile is the wave's own: LDS operations of a wave execute in
+            // program order, so only the compiler must keep the lanes' reads
+            // of one page and the writes of the next in order (a memory
+            // clobber).
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                t[kc_lds_slot(qk_row_token(r >> 2, r16), 4 * (r & 3) + kq4)] = v[r];
+            if (q + 1 < npg) {  // the next page into the freed buffer
+                const uint16_t* pg = k_pool + ((size_t)p_n1 * Hkv + g) * BS * D + lane * 8;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) v[r] = ldg16(pg + r * 512);
+            } else if (spill && u == 0) {  // the next page's first group, chunk c8
+                const uint16_t* pg = k_pool + ((size_t)p_n1 * Hkv + g) * BS * D;
+#pragma unroll
+                for (int x = 0; x < 16; ++x) v[x] = ldg16(pg + k_chunk(x, c8));
+            }
+            const int p_n2 = pid(q + 2);
+            asm volatile("" ::: "memory");
+            double gs[8], nb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gs[e] = 0.0;
+#pragma unroll 8
+            for (int k = 0; k < 16; ++k) acc8(gs, t[kc_lds_slot(16 * u + k, c8)]);
+            rotate(gs, nb);
+            // this lane's key: 4b + u (groups u and u + 1), or for u = 3 key
+            // 4b - 1 (the previous page's last group and this page's first)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) nb[e] = (u < 3 ? gs[e] : carry[e]) + nb[e];
+            if (u == 3) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) carry[e] = gs[e];
+            }
+            const uint4 kr = round8(nb);
+            const int b = b0 + q;
+            if (q > 0) store_page(b - 1, p_prev, u < 3 ? kprev : kr);  // page b - 1 is complete
+            kprev = kr;
+            if (q + 1 == npg) {  // page b: key 4b + 3 with the next page's first group
+                uint4 k3 = kr;
+                if (spill) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) gs[e] = 0.0;
+                    if (u == 0) {
+#pragma unroll
+                        for (int x = 0; x < 16; ++x) acc8(gs, v[x]);
+                    }
+                    rotate(gs, nb);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) nb[e] = carry[e] + nb[e];
+                    k3 = round8(nb);
+                }
+                store_page(b, p_cur, u < 3 ? kr : k3);
+            }
+            p_prev = p_cur;
+            p_cur = p_n1;
+            p_n1 = p_n2;
+        }
     }
 }
 
-hipError_t launch_kc_build(const Plan& pl, const nosa_paged_kv& kv, const int32_t* cu_k,
-                           const int32_t* valid_len, int grid_x, hipStream_t stream)
+// Pages per wave for a build whose pairs each hold up to max_pages pages of
+// new keys: enough that the launch has about kKcTargetWaves waves.
+static int kc_pages_per_wave(const Plan& pl, int max_pages)
 {
-    dim3 grid(grid_x, pl.Hkv, pl.B);
+    const long long total = (long long)pl.B * pl.Hkv * (max_pages > 0 ? max_pages : 1);
+    const long long ppw = (total + kKcTargetWaves - 1) / kKcTargetWaves;
+    return (int)(ppw < kKcMinPagesPerWave ? kKcMinPagesPerWave : (ppw > (1 << 20) ? (1 << 20) : ppw));
+}
+
+// max_pages: an upper bound of the pages holding a new key's first token per
+// (sequence, KV head) (a grid-stride loop covers whatever the grid misses).
+hipError_t launch_kc_build(const Plan& pl, const nosa_paged_kv& kv, const int32_t* cu_k,
+                           const int32_t* valid_len, int max_pages, hipStream_t stream)
+{
+    const int ppw = kc_pages_per_wave(pl, max_pages);
+    const int tasks = ceil_div(max_pages > 0 ? max_pages : 1, ppw);
+    dim3 grid(ceil_div(tasks, 4), pl.Hkv, pl.B);
     hipLaunchKernelGGL(kc_build_kernel, grid, dim3(256), 0, stream, kv.k_pool, kv.kc_pool,
-                       kv.block_table, kv.max_blocks_per_seq, pl.Lmax, pl.Hkv, cu_k, valid_len);
+                       kv.block_table, kv.max_blocks_per_seq, pl.Lmax, pl.Hkv, cu_k, valid_len,
+                       ppw);
     return hipGetLastError();
 }
 

@@ -215,8 +215,10 @@ nosa_status nosa_workspace_size(const nosa_params* params, int32_t batch, int32_
  * pooling with kernel 32 / stride 16].  For every sequence s and KV head,
  * writes keys j in [n_c(kc_valid_len[s]), n_c(L_s)) into kc_pool: key j is
  * the bf16 round-to-nearest-even of the exact mean of K over tokens
- * [16j, 16j+32) (sums are formed in fp64, so the result does not depend on
- * the summation order).  kc_valid_len (device, [batch] int32) is the number
+ * [16j, 16j+32).  The sums are formed in fp64, which is exact (so the order
+ * of the additions does not matter) while the window's nonzero values of a
+ * channel span at most 2^40 in magnitude; wider spans are rounded in fp64
+ * first.  kc_valid_len (device, [batch] int32) is the number
  * of tokens whose keys are already pooled; NULL rebuilds every key.  Keys
  * outside that range are not touched.  cu_seqlens_k: device [batch+1]. */
 nosa_status nosa_compress_keys(const nosa_params* params, const nosa_paged_kv* kv,

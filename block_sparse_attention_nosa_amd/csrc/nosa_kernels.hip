@@ -578,8 +578,13 @@ __global__ __launch_bounds__(kScoreWaves * 64, CPW) void score_kernel(ScoreArgs 
     // loads, not in later batches that each wait for the one before.
     int nscore = a.nscore, nchunks = a.nchunks, Hkv = a.Hkv, max_blocks = a.max_blocks;
     asm("" : "+s"(nscore), "+s"(nchunks), "+s"(Hkv), "+s"(max_blocks));
-    if ((int)blockIdx.x >= nscore) {  // window workgroup
-        const int w = (int)blockIdx.x - nscore;
+    // Scoring workgroups are dealt to the eight XCDs (round-robin by index)
+    // so that a pair's chunks run on one XCD, the one its attention
+    // workgroups use in the next launch: slot b is scoring workgroup
+    // (b % 8) * spx + b / 8 (spx = ceil(nscore / 8); past nscore: idle).
+    const int spx = (nscore + 7) >> 3;
+    if ((int)blockIdx.x >= 8 * spx) {  // window workgroup
+        const int w = (int)blockIdx.x - 8 * spx;
         const int pair = w / a.wgroups;
         if constexpr (T == 8) {
             if (a.wgroups != a.wslots) {  // a page per wave
@@ -595,8 +600,10 @@ __global__ __launch_bounds__(kScoreWaves * 64, CPW) void score_kernel(ScoreArgs 
                     a.nsplit, a.split0, a.po, a.pml, *reinterpret_cast<SplitPageLds*>(smem));
         return;
     }
+    const int sid = ((int)blockIdx.x & 7) * spx + ((int)blockIdx.x >> 3);
+    if (sid >= nscore) return;  // (whole workgroup)
     const int cpp = (nchunks + CPW - 1) / CPW;  // scoring workgroups per pair
-    const int pair = blockIdx.x / cpp, c0 = (blockIdx.x % cpp) * CPW;
+    const int pair = sid / cpp, c0 = (sid % cpp) * CPW;
     const int s = pair / Hkv, g = pair % Hkv;
     const int32_t* trow = a.table + (size_t)s * max_blocks;
     // Table entries of this lane's keys in a chunk (the row has max_blocks
@@ -1219,14 +1226,20 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ po
                                                     const int32_t* __restrict__ map_next,
                                                     const int32_t* __restrict__ used_next,
                                                     int32_t* __restrict__ map,
-                                                    int32_t* __restrict__ used, int cap, int G)
+                                                    int32_t* __restrict__ used, int cap, int G,
+                                                    size_t rows)
 {
     // the empty asm reads every argument in one batch of scalar loads (not
     // the count first for the loop test, then the rest); as its operands
     // are inputs only, the pointers stay global ones
     asm volatile("" ::"s"(po), "s"(pml), "s"(nsplit), "s"(out), "s"(lse), "s"(map_next),
-                 "s"(used_next), "s"(map), "s"(used), "s"(cap), "s"(G));
-    const size_t row = blockIdx.x;
+                 "s"(used_next), "s"(map), "s"(used), "s"(cap), "s"(G), "s"(rows));
+    // head rows dealt to the XCDs like the attention workgroups' pairs (a
+    // pair's rows on the XCD whose L2 holds its partials): slot b is row
+    // (b % 8) * rpx + b / 8, rpx = gridDim.x / 8 (past the last row: idle)
+    const int rpx = (int)gridDim.x >> 3;
+    const size_t row = (size_t)(((int)blockIdx.x & 7) * rpx + ((int)blockIdx.x >> 3));
+    if (row >= rows) return;  // (whole workgroup)
     const int c = threadIdx.x, lane = c & 63;
     const float2* ml = pml + row * nsplit;
     const float* op = po + row * nsplit * D + c;
@@ -1270,10 +1283,11 @@ static hipError_t launch_merge(const Plan& pl, const Workspace& w, int nsplit, f
 {
     const int rows = pl.B * pl.Hq;
     if (rows > 0)
-        hipLaunchKernelGGL(merge_kernel, dim3(rows), dim3(D), 0, stream, w.po, w.pml, nsplit, out,
-                           lse, off ? off->map_next : nullptr, off ? off->used_next : nullptr,
-                           off ? off->cache_map : nullptr, off ? off->cache_used : nullptr,
-                           off ? off->cap : 0, pl.G);
+        hipLaunchKernelGGL(merge_kernel, dim3(8 * ceil_div(rows, 8)), dim3(D), 0, stream, w.po,
+                           w.pml, nsplit, out, lse, off ? off->map_next : nullptr,
+                           off ? off->used_next : nullptr, off ? off->cache_map : nullptr,
+                           off ? off->cache_used : nullptr, off ? off->cap : 0, pl.G,
+                           (size_t)rows);
     return hipGetLastError();
 }
 
@@ -1480,7 +1494,8 @@ static hipError_t launch_score(const Plan& pl, const nosa_paged_kv& kv, const no
     a.pml = w.pml;
     const bool per_wave = wgroups > 0 && wgroups != pl.wslots;
     if (per_wave && pl.score_tiles != 8) return hipErrorInvalidValue;
-    const dim3 grid(a.nscore + pl.B * pl.Hkv * (wgroups > 0 ? wgroups : 0)), block(kScoreWaves * 64);
+    const dim3 grid(8 * ceil_div(a.nscore, 8) + pl.B * pl.Hkv * (wgroups > 0 ? wgroups : 0)),
+        block(kScoreWaves * 64);
     const size_t lds = score_lds_bytes(pl.score_tiles, pl.G, per_wave);  // <= 16 x 516 floats
     switch (pl.score_tiles) {
         case 1: hipLaunchKernelGGL((score_kernel<1, 1>), grid, block, lds, stream, a); break;

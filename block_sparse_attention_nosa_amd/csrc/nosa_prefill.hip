@@ -94,10 +94,17 @@ __device__ __forceinline__ PfPair pf_pair(const PfArgs& a, int pair)
 
 // ------------------------------------------------------------- scoring ---
 
+// The split's pooled-key pages are staged in LDS once per workgroup (its four
+// waves multiply the same keys with different rows), each 1 KB page padded to
+// kPfPageStride uint4: a key tile's operand reads (16 keys over four pages,
+// four chunks) then fall on distinct banks in every group of eight lanes.
+constexpr int kPfPageStride = (1024 + 64) / 16;
+
 struct PfScoreLds {
     float lse[32 * 16];          // per row of the workgroup (pass 2)
     float ksum[4][kKPS];         // per wave, per key of the split (pass 2)
     int32_t pages[kKPS / SL];    // page of each group of SL pooled keys of the split
+    uint4 kc[kKPS / SL][kPfPageStride];  // the split's pooled-key pages
 };
 
 // Sum over the 16 lanes of each row of 16 (DPP shifts within the row; the
@@ -177,6 +184,15 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
         __syncthreads();  // also publishes the page ids
     }
 
+    // the split's pooled-key pages into LDS: wave w copies pages w, w + 4, ...,
+    // a contiguous kilobyte per load (pages past the split's keys repeat
+    // page 0's row of the table entry; their keys are masked)
+    uint4 pgv[kKPS / SL / 4];
+#pragma unroll
+    for (int i = 0; i < kKPS / SL / 4; ++i) {
+        const int x = wave + 4 * i;
+        pgv[i] = ldg16(a.kc_pool + ((size_t)sh.pages[x] * a.Hkv + P.g) * SL * D + lane * 8);
+    }
     // query operand of the wave's row tiles; rows of absent queries are zero
     bf16x8 qb[RTW][4];
     int qpos[RTW];  // query position of this lane's row r in each tile (-1: none)
@@ -205,6 +221,9 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
         for (int off = 1; off < 16; off <<= 1) p = min(p, __shfl_xor(p, off));
         tile_p0[u] = __builtin_amdgcn_readfirstlane(p);
     }
+#pragma unroll
+    for (int i = 0; i < kKPS / SL / 4; ++i) sh.kc[wave + 4 * i][lane] = pgv[i];
+    __syncthreads();
     float lse_r[RTW];
     if (PASS == 2) {
 #pragma unroll
@@ -222,9 +241,9 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
     // logits are masked).
     auto load_tile = [&](int kt, uint4 (&kf)[4]) {
         const int key = min(kt + r, key_hi - 1);
-        const uint16_t* kp = a.kc_pool + ((size_t)sh.pages[(key - key_lo) / SL] * a.Hkv + P.g) * SL * D;
+        const uint4* kp = sh.kc[(key - key_lo) / SL];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) kf[st] = ldg16(kp + kc_chunk(key % SL, st * 4 + kq));
+        for (int st = 0; st < 4; ++st) kf[st] = kp[(st * 4 + kq) * SL + key % SL];
     };
     auto tile = [&](int kt, const uint4 (&kf)[4]) {
         float colacc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -239,11 +258,23 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
             float zz[4];
             float tmax = -INFINITY;
             if (all_vis[u] && kt + 16 <= key_hi && (kt + 15) * kPoolS + kPoolK <= tile_p0[u] + 1) {
+                // every key visible to every row: the scale folded into the
+                // exponent's fma, the maximum taken on the raw products
+                // (the scale is positive)
+                if (PASS == 1) {
+                    const float mn = fmaxf(m_run[u], fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])) *
+                                                         a.scale_log2);
+                    float add = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    zz[i] = acc[i] * a.scale_log2;
-                    tmax = fmaxf(tmax, zz[i]);
+                    for (int i = 0; i < 4; ++i) add += fexp2(__builtin_fmaf(acc[i], a.scale_log2, -mn));
+                    s_run[u] = s_run[u] * fexp2(m_run[u] - mn) + add;
+                    m_run[u] = mn;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        colacc[i] += fexp2(__builtin_fmaf(acc[i], a.scale_log2, -lse_r[u]));
                 }
+                continue;
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {

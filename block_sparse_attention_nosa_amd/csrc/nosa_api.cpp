@@ -202,6 +202,7 @@ void make_pf_plan(const Plan& pl, int max_seqlen_q, PfPlan* pf)
     size_t off = 0;
     F.off_part = off;   off += align256(np * F.rows * (size_t)F.key_splits * sizeof(float2));
     F.off_colsum = off; off += align256(np * F.row_groups * (size_t)F.key_splits * 256 * sizeof(float));
+    F.off_rlse = off;   off += align256(np * F.rows * sizeof(float));
     F.bytes = off > 256 ? off : 256;
     const size_t groups = np * (size_t)F.attn_groups;
     F.split_rows = (F.max_seqlen_q < 64 ? (F.max_seqlen_q > 0 ? F.max_seqlen_q : 1) : 64) * pl.G;

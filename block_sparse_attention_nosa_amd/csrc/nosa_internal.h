@@ -71,7 +71,7 @@ struct PfPlan {
     int row_groups = 0;   // scoring workgroups over the rows of a pair
     int key_splits = 0;   // scoring workgroups over the pooled keys of a pair
     int attn_groups = 0;  // attention workgroups (128 rows each) per pair
-    size_t off_part = 0, off_colsum = 0, bytes = 0;
+    size_t off_part = 0, off_colsum = 0, off_rlse = 0, bytes = 0;
     // split attention (launches of at most kPfSplitGroups workgroups): the
     // halves' partials after the scoring scratch; bytes_split = the workspace
     // that holds them (bytes when no launch of this plan can split)

@@ -44,6 +44,7 @@ struct PfArgs {
     int key_splits;  // workgroups over the pooled keys of a pair
     int zlen;        // key_splits * kKPS
     float2* part;    // [pairs][rows][key_splits] per-row (max, sum exp2)
+    float* rlse;     // [pairs][rows] lse (log2 units) of each row's scoring softmax
     float* colsum;   // [pairs][row_groups][zlen] per-key sums over a row group
     float* scores;   // [pairs][max_nb] block importance
     int max_nb;
@@ -107,30 +108,19 @@ struct PfScoreLds {
     uint4 kc[kKPS / SL][kPfPageStride];  // the split's pooled-key pages
 };
 
-// Sum over the 16 lanes of each row of 16 (DPP shifts within the row; the
-// total lands in lane 15 of the row).
-template <int CTRL, int BANK_MASK>
-__device__ __forceinline__ float dpp_row_f(float v)
+// max(a, b, c) without canonicalising the operands (NaN propagates, which
+// the products never are); gfx950 issues it as one v_maximum3_f32.
+__device__ __forceinline__ float vmax3(float a, float b, float c)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf,
-                                                                 BANK_MASK, true));
-}
-
-__device__ __forceinline__ float row16_sum_to_last(float x)
-{
-    x += dpp_row_f<0x111, 0xf>(x);  // row_shr:1
-    x += dpp_row_f<0x112, 0xf>(x);  // row_shr:2
-    x += dpp_row_f<0x114, 0xe>(x);  // row_shr:4, lanes 4..15
-    x += dpp_row_f<0x118, 0xc>(x);  // row_shr:8, lanes 8..15
-    return x;
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
 // Workgroup = 4 waves x RTW row tiles of 16 rows, over the kKPS pooled keys of
 // one split.  PASS 1 writes per-row (max, sum exp2) over the split's visible
 // keys; PASS 2 writes, for every key, sum over the workgroup's rows of
-// exp2(z - lse_row) (lse from the pass-1 partials), in a fixed order.
+// exp2(z - lse_row) (lse from pf_lse_kernel), in a fixed order.
 template <int PASS, int RTW>
-__global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
+__global__ __launch_bounds__(256, 2) void pf_score_kernel(PfArgs a)
 {
     __shared__ PfScoreLds sh;
     const int per_pair = a.row_groups * a.key_splits;
@@ -138,7 +128,9 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
     const int rg = (blockIdx.x % per_pair) / a.key_splits;
     const int ks = blockIdx.x % a.key_splits;
     const PfPair P = pf_pair(a, pair);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (P.empty) return;  // nothing of the pair is read (the pooling skips it)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, kq = lane >> 4;
     const int key_lo = ks * kKPS;
     const int key_hi = min(key_lo + kKPS, P.nck);
@@ -151,38 +143,15 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
         const int key = key_lo + SL * x;
         sh.pages[x] = key < key_hi ? trow[key / SL] : 0;
     }
-    if (PASS == 1) __syncthreads();
-
     if (PASS == 2) {
-        // lse of every row of the workgroup from the pass-1 partials
-        // (partials read 16 at a time, all loads of a batch in flight, then
-        // combined; a loop-carried load chain would wait on each)
+        // lse of every row of the workgroup (+inf past the pair's rows: the
+        // row adds exp2(-inf) = 0)
         for (int x = tid; x < 4 * RTW * 16; x += 256) {
             const int row = wg_row0 + x;
-            float m = -INFINITY, acc = 0.f;
-            if (row < a.rows && !P.empty) {
-                const float2* pp = a.part + ((size_t)pair * a.rows + row) * a.key_splits;
-                for (int i0 = 0; i0 < a.key_splits; i0 += 16) {
-                    float2 v[16];
-#pragma unroll
-                    for (int u = 0; u < 16; ++u)
-                        v[u] = i0 + u < a.key_splits ? pp[i0 + u] : make_float2(-INFINITY, 0.f);
-                    float mb = m;
-#pragma unroll
-                    for (int u = 0; u < 16; ++u)
-                        if (v[u].y > 0.f) mb = fmaxf(mb, v[u].x);
-                    if (mb == -INFINITY) continue;
-                    acc = m == -INFINITY ? 0.f : acc * fexp2(m - mb);
-#pragma unroll
-                    for (int u = 0; u < 16; ++u)
-                        if (v[u].y > 0.f) acc += v[u].y * fexp2(v[u].x - mb);
-                    m = mb;
-                }
-            }
-            sh.lse[x] = acc > 0.f ? m + log2f(acc) : INFINITY;  // +inf: row contributes 0
+            sh.lse[x] = row < a.rows ? a.rlse[(size_t)pair * a.rows + row] : INFINITY;
         }
-        __syncthreads();  // also publishes the page ids
     }
+    __syncthreads();
 
     // the split's pooled-key pages into LDS: wave w copies pages w, w + 4, ...,
     // a contiguous kilobyte per load (pages past the split's keys repeat
@@ -193,137 +162,122 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
         const int x = wave + 4 * i;
         pgv[i] = ldg16(a.kc_pool + ((size_t)sh.pages[x] * a.Hkv + P.g) * SL * D + lane * 8);
     }
-    // query operand of the wave's row tiles; rows of absent queries are zero
+    // query operand of the wave's row tiles; a row without a query (past the
+    // block's queries or the pair's rows) loads the block's last query: its
+    // products are masked by position (pass 1) or weighted by
+    // exp2(-lse) = 0 (pass 2)
     bf16x8 qb[RTW][4];
     int qpos[RTW];  // query position of this lane's row r in each tile (-1: none)
 #pragma unroll
     for (int u = 0; u < RTW; ++u) {
         const int row = (row_tile0 + u) * 16 + r;
         const int qi = row / a.G, h = row % a.G;
-        const bool ok = !P.empty && row < a.rows && qi < P.nq;
+        const bool ok = row < a.rows && qi < P.nq;
         qpos[u] = ok ? P.p0 + qi : -1;
-        const uint16_t* qr = a.q + ((size_t)(P.q0 + kQB * P.r + (ok ? qi : 0)) * a.Hq + P.g * a.G + h) * D;
+        const uint16_t* qr =
+            a.q + ((size_t)(P.q0 + kQB * P.r + min(qi, P.nq - 1)) * a.Hq + P.g * a.G + h) * D + kq * 8;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            uint4 w = ok ? ldg16(qr + st * 32 + kq * 8) : make_uint4(0, 0, 0, 0);
-            qb[u][st] = as_bf16x8(w);
-        }
+        for (int st = 0; st < 4; ++st) qb[u][st] = as_bf16x8(ldg16(qr + st * 32));
     }
-    // per row tile: does every row hold a query, and the first query position
-    // (the rows of a tile are 16 consecutive (query, head) pairs)
-    bool all_vis[RTW];
-    int tile_p0[RTW];
-#pragma unroll
-    for (int u = 0; u < RTW; ++u) {
-        all_vis[u] = __ballot(qpos[u] < 0) == 0;  // wave-uniform
-        int p = qpos[u] < 0 ? 0x7fffffff : qpos[u];
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) p = min(p, __shfl_xor(p, off));
-        tile_p0[u] = __builtin_amdgcn_readfirstlane(p);
-    }
+    // The wave's rows ascend with the query: every row holds a query when its
+    // last row does, and its first row's query is the earliest.
+    const int wave_row_last = (row_tile0 + RTW) * 16 - 1;
+    const bool wave_full = wave_row_last < a.rows && wave_row_last / a.G < P.nq;
+    const int wave_p0 = P.p0 + row_tile0 * 16 / a.G;
 #pragma unroll
     for (int i = 0; i < kKPS / SL / 4; ++i) sh.kc[wave + 4 * i][lane] = pgv[i];
     __syncthreads();
-    float lse_r[RTW];
-    if (PASS == 2) {
-#pragma unroll
-        for (int u = 0; u < RTW; ++u) lse_r[u] = sh.lse[(wave * RTW + u) * 16 + r];
-    }
-    float m_run[RTW], s_run[RTW];
-#pragma unroll
-    for (int u = 0; u < RTW; ++u) {
-        m_run[u] = -INFINITY;
-        s_run[u] = 0.f;
-    }
-
-    // Two key tiles in flight: the loads of tile kt + 16 are issued before
-    // tile kt is computed.  Rows past key_hi load the last key again (their
-    // logits are masked).
-    auto load_tile = [&](int kt, uint4 (&kf)[4]) {
-        const int key = min(kt + r, key_hi - 1);
-        const uint4* kp = sh.kc[(key - key_lo) / SL];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) kf[st] = kp[(st * 4 + kq) * SL + key % SL];
+    const float sc = a.scale_log2;
+    // Is the pair of key tiles from kt (32 keys) visible to every row of the
+    // wave?  Then no element is tested (key < n_c(p + 1)  <=>  16 key + 32 <=
+    // p + 1); tiles near the diagonal, the split's end and absent rows take
+    // the tested path.
+    auto pair_fast = [&](int kt) {
+        return wave_full && kt + 32 <= key_hi && (kt + 31) * kPoolS + kPoolK <= wave_p0 + 1;
     };
-    auto tile = [&](int kt, const uint4 (&kf)[4]) {
-        float colacc[4] = {0.f, 0.f, 0.f, 0.f};
+    // Operand of the key tile from kt: lane r holds key kt + r, chunk 4 st + kq.
+    // kt - key_lo is a multiple of 16, so the key sits in staged page
+    // (kt - key_lo) / SL + r / SL, slot r % SL; every tile of the split lies
+    // inside the staged pages (keys past key_hi are masked or unused).
+    const uint4* kl = &sh.kc[r / SL][kq * SL + r % SL];
+    auto load_tile = [&](int kt, uint4 (&kf)[4]) {
+        const uint4* kp = kl + ((kt - key_lo) / SL) * kPfPageStride;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) kf[st] = kp[st * 4 * SL];
+    };
+    // the next pair's operands are read once the current pair's products are
+    // issued (the read past the split's last pair repeats it)
+    auto next_pair = [&](int kt) { return min(kt + 32, key_lo + kKPS - 32); };
+
+    if (PASS == 1) {
+        // Products as (key, row) tiles: lane r holds row r, keys 4 kq + i.
+        // Running state per row of every tile: the maximum of the raw
+        // products seen (the scale is positive) and the sum of
+        // exp2((z - max) * scale), the scale folded into the exponent's fma;
+        // the maximum is updated once per 8 products of a lane.
+        float m_raw[RTW], s_run[RTW];
 #pragma unroll
         for (int u = 0; u < RTW; ++u) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            m_raw[u] = -INFINITY;
+            s_run[u] = 0.f;
+        }
+        auto tested = [&](int kt, const uint4 (&kf)[4]) {
 #pragma unroll
-            for (int st = 0; st < 4; ++st) acc = mfma16(as_bf16x8(kf[st]), qb[u][st], acc);
-            // visible: key < n_c(p + 1)  <=>  16 * key + 32 <= p + 1; when every
-            // key of the tile is visible to every row of the tile (the common
-            // case) the per-element test is skipped
-            float zz[4];
-            float tmax = -INFINITY;
-            if (all_vis[u] && kt + 16 <= key_hi && (kt + 15) * kPoolS + kPoolK <= tile_p0[u] + 1) {
-                // every key visible to every row: the scale folded into the
-                // exponent's fma, the maximum taken on the raw products
-                // (the scale is positive)
-                if (PASS == 1) {
-                    const float mn = fmaxf(m_run[u], fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])) *
-                                                         a.scale_log2);
-                    float add = 0.f;
+            for (int u = 0; u < RTW; ++u) {
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) add += fexp2(__builtin_fmaf(acc[i], a.scale_log2, -mn));
-                    s_run[u] = s_run[u] * fexp2(m_run[u] - mn) + add;
-                    m_run[u] = mn;
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        colacc[i] += fexp2(__builtin_fmaf(acc[i], a.scale_log2, -lse_r[u]));
-                }
-                continue;
-            } else {
+                for (int st = 0; st < 4; ++st) c = mfma16(as_bf16x8(kf[st]), qb[u][st], c);
+                float z[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int kj = kt + 4 * kq + i;
                     const bool vis = qpos[u] >= 0 && kj < key_hi && kj * kPoolS + kPoolK <= qpos[u] + 1;
-                    zz[i] = vis ? acc[i] * a.scale_log2 : -INFINITY;
-                    tmax = fmaxf(tmax, zz[i]);
+                    z[i] = vis ? c[i] : -INFINITY;
+                }
+                const float tmax = vmax3(vmax3(z[0], z[1], z[2]), z[3], -INFINITY);
+                if (tmax != -INFINITY) {
+                    const float mx = vmax3(m_raw[u], tmax, -INFINITY);
+                    const float nm = -(mx * sc);
+                    const float e = (fexp2(fmaf(z[0], sc, nm)) + fexp2(fmaf(z[1], sc, nm))) +
+                                    (fexp2(fmaf(z[2], sc, nm)) + fexp2(fmaf(z[3], sc, nm)));
+                    s_run[u] = fmaf(s_run[u], fexp2(fmaf(m_raw[u], sc, nm)), e);
+                    m_raw[u] = mx;
                 }
             }
-            if (PASS == 1) {
-                if (tmax != -INFINITY) {
-                    const float mn = fmaxf(m_run[u], tmax);
-                    float add = 0.f;
+        };
+        uint4 kf0[4], kf1[4];
+        load_tile(key_lo, kf0);
+        load_tile(key_lo + 16, kf1);
+        for (int kt = key_lo; kt < key_hi; kt += 32) {
+            if (pair_fast(kt)) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) add += fexp2(zz[i] - mn);
-                    s_run[u] = s_run[u] * fexp2(m_run[u] - mn) + add;
-                    m_run[u] = mn;
+                for (int u = 0; u < RTW; ++u) {
+                    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) c0 = mfma16(as_bf16x8(kf0[st]), qb[u][st], c0);
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) c1 = mfma16(as_bf16x8(kf1[st]), qb[u][st], c1);
+                    const float mx = vmax3(vmax3(vmax3(vmax3(m_raw[u], c0[0], c0[1]), c0[2], c0[3]), c1[0], c1[1]),
+                                           c1[2], c1[3]);
+                    const float nm = -(mx * sc);
+                    const float e0 = (fexp2(fmaf(c0[0], sc, nm)) + fexp2(fmaf(c0[1], sc, nm))) +
+                                     (fexp2(fmaf(c0[2], sc, nm)) + fexp2(fmaf(c0[3], sc, nm)));
+                    const float e1 = (fexp2(fmaf(c1[0], sc, nm)) + fexp2(fmaf(c1[1], sc, nm))) +
+                                     (fexp2(fmaf(c1[2], sc, nm)) + fexp2(fmaf(c1[3], sc, nm)));
+                    s_run[u] = fmaf(s_run[u], fexp2(fmaf(m_raw[u], sc, nm)), e0 + e1);
+                    m_raw[u] = mx;
                 }
             } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) colacc[i] += fexp2(zz[i] - lse_r[u]);
+                tested(kt, kf0);
+                if (kt + 16 < key_hi) tested(kt + 16, kf1);
             }
+            load_tile(next_pair(kt), kf0);
+            load_tile(next_pair(kt) + 16, kf1);
         }
-        if (PASS == 2) {
-            // sum over the 16 rows (lanes r) of each key; lane r == 15 holds it
-#pragma unroll
-            for (int i = 0; i < 4; ++i) colacc[i] = row16_sum_to_last(colacc[i]);
-            if (r == 15)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sh.ksum[wave][kt - key_lo + 4 * kq + i] = colacc[i];
-        }
-    };
-    // (the loads are issued unconditionally -- past key_hi they repeat the
-    // last key -- so no branch makes the compiler wait for all of them)
-    if (key_lo < key_hi) {
-        uint4 kfa[4], kfb[4];
-        load_tile(key_lo, kfa);
-        for (int kt = key_lo; kt < key_hi; kt += 32) {
-            load_tile(kt + 16, kfb);
-            tile(kt, kfa);
-            load_tile(kt + 32, kfa);
-            if (kt + 16 < key_hi) tile(kt + 16, kfb);
-        }
-    }
-
-    if (PASS == 1) {
+        // per row: combine the four lanes (kq) that hold its keys, in log2 units
 #pragma unroll
         for (int u = 0; u < RTW; ++u) {
-            float m = m_run[u], s = s_run[u];
+            float m = m_raw[u] * sc, s = s_run[u];
 #pragma unroll
             for (int off = 16; off < 64; off <<= 1) {
                 const float mo = __shfl_xor(m, off), so = __shfl_xor(s, off);
@@ -336,6 +290,73 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
                 a.part[((size_t)pair * a.rows + row) * a.key_splits + ks] = make_float2(m, s);
         }
     } else {
+        // Products as (row, key) tiles (operands swapped): lane r holds key r,
+        // rows 4 kq + e, so a key's sum over rows adds within the lane and
+        // then over the four lanes of the key.  The lse of those rows (the
+        // four of a lane are adjacent in LDS) is read per tile.
+        const float4* lse4 = reinterpret_cast<const float4*>(sh.lse) + wave * RTW * 4 + kq;
+        auto neg_lse = [&](int u, float (&nl)[4]) {
+            const float4 l = lse4[u * 4];
+            nl[0] = -l.x;
+            nl[1] = -l.y;
+            nl[2] = -l.z;
+            nl[3] = -l.w;
+        };
+        // row (query qi = row / G, position p0 + qi) sees key j when
+        // 16 j + 32 <= p0 + qi + 1, i.e. when row >= (16 j + 31 - p0) G
+        const int row_l = row_tile0 * 16 + 4 * kq;  // the lane's first row
+        auto tested = [&](int kt, const uint4 (&kf)[4]) {
+            const int key = kt + r;
+            const int rmin = key < key_hi ? (key * kPoolS + kPoolK - 1 - P.p0) * a.G : 0x7fffffff;
+            float cs = 0.f;
+#pragma unroll
+            for (int u = 0; u < RTW; ++u) {
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < 4; ++st) c = mfma16(qb[u][st], as_bf16x8(kf[st]), c);
+                float nl[4];
+                neg_lse(u, nl);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cs += row_l + 16 * u + e >= rmin ? fexp2(fmaf(c[e], sc, nl[e])) : 0.f;
+            }
+            return cs;
+        };
+        // sum over the four lanes of a key (lanes r, r + 16, r + 32, r + 48):
+        // the halves swapped and added, then the odd and even rows
+        auto lanes4_sum = [](float x) {
+            const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+            const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+        };
+        // one key tile at a time, the other buffer's tile read meanwhile
+        auto step = [&](int kt, const uint4 (&kf)[4]) {
+            float cs = 0.f;
+            if (wave_full && kt + 16 <= key_hi && (kt + 15) * kPoolS + kPoolK <= wave_p0 + 1) {
+#pragma unroll
+                for (int u = 0; u < RTW; ++u) {
+                    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) c = mfma16(qb[u][st], as_bf16x8(kf[st]), c);
+                    float nl[4];
+                    neg_lse(u, nl);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) cs += fexp2(fmaf(c[e], sc, nl[e]));
+                }
+            } else {
+                cs = tested(kt, kf);
+            }
+            cs = lanes4_sum(cs);
+            if (kq == 0) sh.ksum[wave][kt - key_lo + r] = cs;
+        };
+        uint4 kf0[4], kf1[4];
+        load_tile(key_lo, kf0);
+        for (int kt = key_lo; kt < key_hi; kt += 32) {
+            load_tile(kt + 16, kf1);
+            step(kt, kf0);
+            load_tile(next_pair(kt), kf0);
+            if (kt + 16 < key_hi) step(kt + 16, kf1);
+        }
         __syncthreads();
         float* dst = a.colsum + ((size_t)pair * a.row_groups + rg) * a.zlen + key_lo;
         for (int x = tid; x < kKPS; x += 256) {
@@ -345,6 +366,38 @@ __global__ __launch_bounds__(256) void pf_score_kernel(PfArgs a)
             dst[x] = v;
         }
     }
+}
+
+// lse (log2 units) of every row's scoring softmax from the pass-1 partials
+// of its key splits, combined in split order; +inf for a row without visible
+// keys (pass 2 then adds nothing for it).  One thread per (pair, row).
+__global__ __launch_bounds__(256) void pf_lse_kernel(PfArgs a, int total)
+{
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= total) return;
+    const int pair = t / a.rows, row = t % a.rows;
+    const PfPair P = pf_pair(a, pair);
+    float m = -INFINITY, acc = 0.f;
+    if (!P.empty) {
+        // partials read 16 at a time, all loads of a batch in flight
+        const float2* pp = a.part + (size_t)t * a.key_splits;
+        for (int i0 = 0; i0 < a.key_splits; i0 += 16) {
+            float2 v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = i0 + u < a.key_splits ? pp[i0 + u] : make_float2(-INFINITY, 0.f);
+            float mb = m;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (v[u].y > 0.f) mb = fmaxf(mb, v[u].x);
+            if (mb == -INFINITY) continue;
+            acc = m == -INFINITY ? 0.f : acc * fexp2(m - mb);
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (v[u].y > 0.f) acc += v[u].y * fexp2(v[u].x - mb);
+            m = mb;
+        }
+    }
+    a.rlse[t] = acc > 0.f ? m + log2f(acc) : INFINITY;
 }
 
 // Block importance of a pair: sigma[j] = sum over row groups (fixed order) of
@@ -698,6 +751,7 @@ hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_k
     a.qbase = qbase;
     a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + pf.off_part);
     a.colsum = reinterpret_cast<float*>(static_cast<char*>(ws) + pf.off_colsum);
+    a.rlse = reinterpret_cast<float*>(static_cast<char*>(ws) + pf.off_rlse);
     a.scores = scores;
     const dim3 grid(pf.npairs * pf.row_groups * pf.key_splits);
 #define NOSA_PF(PASS, R) hipLaunchKernelGGL((pf_score_kernel<PASS, R>), grid, dim3(256), 0, stream, a)
@@ -710,6 +764,12 @@ hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_k
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (pass == 1) {
+            const int total = pf.npairs * pf.rows;
+            hipLaunchKernelGGL(pf_lse_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, a, total);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
 #undef NOSA_PF
     const size_t lds = sizeof(float) * (size_t)(pl.max_nb > 0 ? pl.max_nb : 1);

@@ -27,6 +27,7 @@ namespace nosa {
 
 constexpr int kQB = 64;   // queries per query block
 constexpr int kKPS = 256; // pooled keys per split of the scoring passes
+constexpr float kPfRescale = 8.f;  // exponent headroom before the attention rescales (log2)
 
 struct PfArgs {
     const uint16_t* q;
@@ -543,11 +544,24 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) pmin = min(pmin, __shfl_xor(pmin, off));
     pmin = __builtin_amdgcn_readfirstlane(pmin);  // per wave (its own rows)
+    const float sc = a.scale_log2;
+    // maximum over the four lanes of a row (lanes r, r + 16, r + 32, r + 48)
+    auto lanes4_max = [](float x) {
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = vmax3(__uint_as_float(h[0]), __uint_as_float(h[1]), -INFINITY);
+        const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return vmax3(__uint_as_float(q[0]), __uint_as_float(q[1]), -INFINITY);
+    };
+    // Softmax state per row (lane r of each row tile): m_run, the reference
+    // point of the exponentials (log2 units), and l_run, the lane's part of
+    // sum 2^(z - m_run).  The reference moves only when a row's maximum
+    // passes it by more than kPfRescale, so exponentials stay below
+    // 2^kPfRescale and the accumulators are rarely rescaled; any reference
+    // gives the same quotient O / l and lse = m + log2 l.
     auto compute = [&](int buf, int b_cur) {
-        // S^T = K q^T for both row tiles: K fragments from LDS, shared
+        // S^T = K q^T, raw products: lane holds row r, keys of tile t as
+        // mapped by the K page layout; K fragments from LDS, shared
         float x[2][4][4];
-        float bmax[2] = {-INFINITY, -INFINITY};
-        const bool full = rows_full && b_cur * BS + BS - 1 <= pmin && b_cur * BS + BS <= P.L;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             bf16x8 kf[4];
@@ -559,52 +573,53 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int st = 0; st < 4; ++st) acc = mfma16(kf[st], qb[u][st], acc);
-                if (full) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        x[u][t][i] = acc[i] * a.scale_log2;
-                        bmax[u] = fmaxf(bmax[u], x[u][t][i]);
-                    }
-                } else {
+                for (int i = 0; i < 4; ++i) x[u][t][i] = acc[i];
+            }
+        }
+        if (!(rows_full && b_cur * BS + BS - 1 <= pmin && b_cur * BS + BS <= P.L)) {
+            // causal and length mask (page near the diagonal, the sequence
+            // end, or rows without a query)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int tk = b_cur * BS + 32 * (t >> 1) + 8 * kq + 4 * (t & 1) + i;
-                        const bool vis = qpos[u] >= 0 && tk <= qpos[u] && tk < P.L;
-                        x[u][t][i] = vis ? acc[i] * a.scale_log2 : -INFINITY;
-                        bmax[u] = fmaxf(bmax[u], x[u][t][i]);
+                        if (!(qpos[u] >= 0 && tk <= qpos[u] && tk < P.L)) x[u][t][i] = -INFINITY;
                     }
-                }
-            }
         }
         bf16x8 pa[2][2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            float bm = bmax[u];
-            bm = fmaxf(bm, __shfl_xor(bm, 16));
-            bm = fmaxf(bm, __shfl_xor(bm, 32));
-            const float m_new = fmaxf(m_run[u], bm);
-            // a row with nothing visible yet keeps m = -inf and adds nothing
-            const float alpha = m_new == -INFINITY ? 1.f : fexp2(m_run[u] - m_new);
+            float bm = vmax3(vmax3(x[u][0][0], x[u][0][1], x[u][0][2]), x[u][0][3], -INFINITY);
+#pragma unroll
+            for (int t = 1; t < 4; ++t) bm = vmax3(vmax3(bm, x[u][t][0], x[u][t][1]), x[u][t][2], x[u][t][3]);
+            bm = lanes4_max(bm) * sc;  // the row's maximum, log2 units
+            if (__ballot(bm > m_run[u] + kPfRescale) != 0) {
+                const float m_new = fmaxf(m_run[u], bm);
+                // 1 for an unmoved row (also one still at -inf), 0 from -inf
+                const float alpha = m_new == m_run[u] ? 1.f : fexp2(m_run[u] - m_new);
+                l_run[u] *= alpha;
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[u][nt][e] *= alpha;
+                m_run[u] = m_new;
+            }
+            // a row with nothing visible yet (m_run = -inf) has every z = -inf
+            const float nm = m_run[u] == -INFINITY ? 0.f : -m_run[u];
             float psum = 0.f;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float e = m_new == -INFINITY ? 0.f : fexp2(x[u][t][i] - m_new);
+                    const float e = fexp2(fmaf(x[u][t][i], sc, nm));
                     x[u][t][i] = e;
                     psum += e;
                 }
-            l_run[u] = l_run[u] * alpha + psum;
-            // the accumulators are rescaled only when some row's maximum moved
-            if (__ballot(m_new != m_run[u]) != 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float ai = __shfl(alpha, 4 * kq + i);
-#pragma unroll
-                    for (int nt = 0; nt < 8; ++nt) o[u][nt][i] *= ai;
-                }
-            }
-            m_run[u] = m_new;
+            l_run[u] += psum;
 #pragma unroll
             for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
@@ -613,7 +628,8 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
                     pa[u][uu][4 + i] = (__bf16)x[u][2 * uu + 1][i];
                 }
         }
-        // O += P V: V fragments from LDS, shared by both row tiles
+        // O^T += V^T P^T (operands swapped): lane holds row r, channels
+        // 16 nt + 4 kq + e; V fragments from LDS, shared by both row tiles
 #pragma unroll
         for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
@@ -621,7 +637,7 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
                 const bf16x8 vf =
                     as_bf16x8(*reinterpret_cast<const uint4*>(&sh.v[buf][((uu * 8 + nt) * 64 + lane) * 8]));
 #pragma unroll
-                for (int u = 0; u < 2; ++u) o[u][nt] = mfma16(pa[u][uu], vf, o[u][nt]);
+                for (int u = 0; u < 2; ++u) o[u][nt] = mfma16(vf, pa[u][uu], o[u][nt]);
             }
     };
 
@@ -646,37 +662,32 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
             float l = l_run[u];
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
+            if (qpos[u] < 0) continue;
             const int row0 = ((ag * 4 + wave) * 2 + u) * 16;  // the row tile in the pair
-            const size_t pr0 = (size_t)pair * a.rp + row0;
-            if (kq == 0 && qpos[u] >= 0) a.pml[(pr0 + r) * 2 + ks] = make_float2(m_run[u], l);
+            const size_t pr = (size_t)pair * a.rp + row0 + r;
+            if (kq == 0) a.pml[pr * 2 + ks] = make_float2(m_run[u], l);
+            float* dst = a.po + (pr * 2 + ks) * D + 4 * kq;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (__shfl(qpos[u], 4 * kq + i) < 0) continue;
-#pragma unroll
-                for (int nt = 0; nt < 8; ++nt)
-                    a.po[((pr0 + 4 * kq + i) * 2 + ks) * D + nt * 16 + r] = o[u][nt][i];
-            }
+            for (int nt = 0; nt < 8; ++nt)
+                *reinterpret_cast<float4*>(dst + nt * 16) = make_float4(o[u][nt][0], o[u][nt][1], o[u][nt][2], o[u][nt][3]);
         }
         return;
     }
 
-    // normalise and store: lane holds O[rows 4kq + i][channels 16nt + r]
+    // normalise and store: lane holds O[row r][channels 16 nt + 4 kq + e]
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         float l = l_run[u];
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
+        if (qrow[u] < 0) continue;
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        if (kq == 0 && qrow[u] >= 0 && a.lse)
-            a.lse[qrow[u]] = l > 0.f ? (m_run[u] + log2f(l)) * 0.69314718055994531f : -INFINITY;
+        if (kq == 0 && a.lse) a.lse[qrow[u]] = l > 0.f ? (m_run[u] + log2f(l)) * 0.69314718055994531f : -INFINITY;
+        float* dst = a.out + (size_t)qrow[u] * D + 4 * kq;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float inv_i = __shfl(inv, 4 * kq + i);
-            const int row_i = __shfl(qrow[u], 4 * kq + i);
-            if (row_i < 0) continue;
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) a.out[(size_t)row_i * D + nt * 16 + r] = o[u][nt][i] * inv_i;
-        }
+        for (int nt = 0; nt < 8; ++nt)
+            *reinterpret_cast<float4*>(dst + nt * 16) =
+                make_float4(o[u][nt][0] * inv, o[u][nt][1] * inv, o[u][nt][2] * inv, o[u][nt][3] * inv);
     }
 }
 

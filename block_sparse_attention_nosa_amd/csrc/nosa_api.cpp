@@ -196,12 +196,22 @@ void make_pf_plan(const Plan& pl, int max_seqlen_q, PfPlan* pf)
     F.rows = 64 * pl.G;
     F.rtw = pl.G <= 1 ? 1 : pl.G <= 2 ? 2 : pl.G <= 4 ? 4 : 8;
     F.row_groups = ceil_div(4 * pl.G, 4 * F.rtw);
-    F.key_splits = ceil_div(pl.max_nc > 0 ? pl.max_nc : 1, 256);
+    // scoring workgroups: the pooled keys of a row group in chunks of 128,
+    // spans of whole chunks (at most 16) sized for about two workgroups per
+    // CU over the launch
+    const int chunks = ceil_div(pl.max_nc > 0 ? pl.max_nc : 1, 128);
+    const long long row_sets = (long long)F.npairs * F.row_groups;
+    const long long want = row_sets > 0 ? (kPfScoreWorkgroups + row_sets - 1) / row_sets : 1;
+    const int spans = (int)(want < chunks ? want : chunks);
+    int per_span = ceil_div(chunks, spans > 0 ? spans : 1);
+    per_span = per_span < 16 ? per_span : 16;
+    F.span = 128 * per_span;
+    F.key_splits = ceil_div(chunks, per_span);
     F.attn_groups = ceil_div(4 * pl.G, 8);
     const size_t np = (size_t)F.npairs;
     size_t off = 0;
     F.off_part = off;   off += align256(np * F.rows * (size_t)F.key_splits * sizeof(float2));
-    F.off_colsum = off; off += align256(np * F.row_groups * (size_t)F.key_splits * 256 * sizeof(float));
+    F.off_colsum = off; off += align256(np * F.row_groups * (size_t)F.key_splits * F.span * sizeof(float));
     F.off_rlse = off;   off += align256(np * F.rows * sizeof(float));
     F.bytes = off > 256 ? off : 256;
     const size_t groups = np * (size_t)F.attn_groups;

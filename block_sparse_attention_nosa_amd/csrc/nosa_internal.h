@@ -70,6 +70,7 @@ struct PfPlan {
     int rtw = 1;          // row tiles of 16 per wave in the scoring passes
     int row_groups = 0;   // scoring workgroups over the rows of a pair
     int key_splits = 0;   // scoring workgroups over the pooled keys of a pair
+    int span = 0;         // pooled keys per such workgroup (a multiple of 128)
     int attn_groups = 0;  // attention workgroups (128 rows each) per pair
     size_t off_part = 0, off_colsum = 0, off_rlse = 0, bytes = 0;
     // split attention (launches of at most kPfSplitGroups workgroups): the
@@ -78,6 +79,7 @@ struct PfPlan {
     size_t off_po = 0, off_pml = 0, bytes_split = 0;
     int split_rows = 0;  // rows per pair in the partials: min(64, max_seqlen_q) * G
 };
+constexpr int kPfScoreWorkgroups = 512;  // scoring workgroups a launch aims for
 constexpr int kPfSplitGroups = 256;  // one workgroup per CU or fewer: split the pages
 
 // Offloaded KV (device pointers; the host pools as the device sees them).

@@ -26,7 +26,9 @@
 namespace nosa {
 
 constexpr int kQB = 64;   // queries per query block
-constexpr int kKPS = 256; // pooled keys per split of the scoring passes
+constexpr int kChunk = 128;      // pooled keys staged in LDS at a time by the scoring passes
+constexpr int kMaxSpan = 2048;   // pooled keys per scoring workgroup at most
+constexpr int kPfFoldSplits = 16;  // key splits up to which pass 2 merges the row partials itself
 constexpr float kPfRescale = 8.f;  // exponent headroom before the attention rescales (log2)
 
 struct PfArgs {
@@ -40,10 +42,12 @@ struct PfArgs {
     const int32_t* qbase;  // [B] first q / out row of each sequence, or null: cu_q
     int max_blocks, Lmax, Lqmax, B, Hq, Hkv, G, max_qblk;
     float scale_log2;
+    float inv_g;     // 1 / G (rounded)
     int rows;        // 64 * G rows per pair: row = query * G + head
     int row_groups;  // workgroups over the rows of a pair
     int key_splits;  // workgroups over the pooled keys of a pair
-    int zlen;        // key_splits * kKPS
+    int span;        // pooled keys per such workgroup, a multiple of kChunk
+    int zlen;        // key_splits * span
     float2* part;    // [pairs][rows][key_splits] per-row (max, sum exp2)
     float* rlse;     // [pairs][rows] lse (log2 units) of each row's scoring softmax
     float* colsum;   // [pairs][row_groups][zlen] per-key sums over a row group
@@ -96,18 +100,21 @@ __device__ __forceinline__ PfPair pf_pair(const PfArgs& a, int pair)
 
 // ------------------------------------------------------------- scoring ---
 
-// The split's pooled-key pages are staged in LDS once per workgroup (its four
-// waves multiply the same keys with different rows), each 1 KB page padded to
-// kPfPageStride uint4: a key tile's operand reads (16 keys over four pages,
-// four chunks) then fall on distinct banks in every group of eight lanes.
+// The pooled-key pages of a workgroup's span go through LDS a chunk of
+// kChunk keys (32 pages) at a time, in two buffers: chunk c + 1 is copied by
+// direct global-to-LDS loads while chunk c is multiplied.  Each 1 KB page is
+// padded to kPfPageStride uint4, so a key tile's operand reads (16 keys over
+// four pages, four chunks) fall on distinct banks in every group of eight
+// lanes.
 constexpr int kPfPageStride = (1024 + 64) / 16;
+constexpr int kChunkPages = kChunk / SL;
 
 struct PfScoreLds {
-    float lse[32 * 16];          // per row of the workgroup (pass 2)
-    float ksum[4][kKPS];         // per wave, per key of the split (pass 2)
-    int32_t pages[kKPS / SL];    // page of each group of SL pooled keys of the split
-    uint4 kc[kKPS / SL][kPfPageStride];  // the split's pooled-key pages
+    float lse[32 * 16];                  // per row of the workgroup (pass 2)
+    float ksum[2][4][kChunk];            // per chunk parity, wave and key (pass 2)
+    int32_t pages[kMaxSpan / SL];        // page of each group of SL pooled keys of the span
 };
+typedef uint4 PfChunkBuf[kChunkPages][kPfPageStride];
 
 // max(a, b, c) without canonicalising the operands (NaN propagates, which
 // the products never are); gfx950 issues it as one v_maximum3_f32.
@@ -116,14 +123,41 @@ __device__ __forceinline__ float vmax3(float a, float b, float c)
     return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
-// Workgroup = 4 waves x RTW row tiles of 16 rows, over the kKPS pooled keys of
-// one split.  PASS 1 writes per-row (max, sum exp2) over the split's visible
-// keys; PASS 2 writes, for every key, sum over the workgroup's rows of
+// lse (log2 units) of one row's scoring softmax from its n pass-1 partials
+// (max, sum exp2), merged in split order 16 at a time (a batch's loads all in
+// flight); +inf for a row without visible keys (pass 2 then adds nothing).
+__device__ __forceinline__ float row_lse(const float2* __restrict__ pp, int n)
+{
+    float m = -INFINITY, acc = 0.f;
+    for (int i0 = 0; i0 < n; i0 += 16) {
+        float2 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = i0 + u < n ? pp[i0 + u] : make_float2(-INFINITY, 0.f);
+        float mb = m;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            if (v[u].y > 0.f) mb = fmaxf(mb, v[u].x);
+        if (mb == -INFINITY) continue;
+        acc = m == -INFINITY ? 0.f : acc * fexp2(m - mb);
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            if (v[u].y > 0.f) acc += v[u].y * fexp2(v[u].x - mb);
+        m = mb;
+    }
+    return acc > 0.f ? m + log2f(acc) : INFINITY;
+}
+
+// Workgroup = 4 waves x RTW row tiles of 16 rows, over the `span` pooled keys
+// of one key split.  PASS 1 writes per-row (max, sum exp2) over the split's
+// visible keys; PASS 2 writes, for every key, sum over the workgroup's rows of
 // exp2(z - lse_row) (lse from pf_lse_kernel), in a fixed order.
 template <int PASS, int RTW>
 __global__ __launch_bounds__(256, 2) void pf_score_kernel(PfArgs a)
 {
     __shared__ PfScoreLds sh;
+    // the two chunk buffers are distinct objects: a read of one is then known
+    // not to wait for the copy in flight into the other
+    __shared__ PfChunkBuf kc_even, kc_odd;
     const int per_pair = a.row_groups * a.key_splits;
     const int pair = blockIdx.x / per_pair;
     const int rg = (blockIdx.x % per_pair) / a.key_splits;
@@ -133,46 +167,57 @@ __global__ __launch_bounds__(256, 2) void pf_score_kernel(PfArgs a)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, kq = lane >> 4;
-    const int key_lo = ks * kKPS;
-    const int key_hi = min(key_lo + kKPS, P.nck);
+    const int key_lo = ks * a.span;
+    const int key_hi = min(key_lo + a.span, P.nck);
+    const int nchunks = key_hi > key_lo ? (key_hi - key_lo + kChunk - 1) / kChunk : 0;
     const int32_t* trow = a.table + (size_t)P.s * a.max_blocks;
     const int row_tile0 = (rg * 4 + wave) * RTW;  // first row tile of this wave
     const int wg_row0 = rg * 4 * RTW * 16;        // first row of the workgroup
-    // page ids of the split's pooled keys first: a table load queued behind
-    // key loads would wait for them
-    for (int x = tid; x < kKPS / SL; x += 256) {
+    // page ids of the span's pooled keys (page 0 past key_hi: read, masked)
+    for (int x = tid; x < nchunks * kChunkPages; x += 256) {
         const int key = key_lo + SL * x;
         sh.pages[x] = key < key_hi ? trow[key / SL] : 0;
     }
     if (PASS == 2) {
         // lse of every row of the workgroup (+inf past the pair's rows: the
-        // row adds exp2(-inf) = 0)
+        // row adds exp2(-inf) = 0), from pf_lse_kernel or, with few key
+        // splits, from the partials here
         for (int x = tid; x < 4 * RTW * 16; x += 256) {
             const int row = wg_row0 + x;
-            sh.lse[x] = row < a.rows ? a.rlse[(size_t)pair * a.rows + row] : INFINITY;
+            const size_t pr = (size_t)pair * a.rows + row;
+            float l = INFINITY;
+            if (row < a.rows) l = a.rlse ? a.rlse[pr] : row_lse(a.part + pr * a.key_splits, a.key_splits);
+            sh.lse[x] = l;
         }
     }
     __syncthreads();
-
-    // the split's pooled-key pages into LDS: wave w copies pages w, w + 4, ...,
-    // a contiguous kilobyte per load (pages past the split's keys repeat
-    // page 0's row of the table entry; their keys are masked)
-    uint4 pgv[kKPS / SL / 4];
+    // chunk c into buffer c & 1: wave w copies pages w, w + 4, ..., each page
+    // one 1 KB load straight into LDS
+    const uint16_t* kc_lane = a.kc_pool + (size_t)P.g * SL * D + lane * 8;
+    const size_t page_elems = (size_t)a.Hkv * SL * D;
+    auto copy_chunk = [&](int c, uint4* __restrict__ dst) {
 #pragma unroll
-    for (int i = 0; i < kKPS / SL / 4; ++i) {
-        const int x = wave + 4 * i;
-        pgv[i] = ldg16(a.kc_pool + ((size_t)sh.pages[x] * a.Hkv + P.g) * SL * D + lane * 8);
-    }
+        for (int i = 0; i < kChunkPages / 4; ++i) {
+            const int x = wave + 4 * i;
+            const int pg = __builtin_amdgcn_readfirstlane(sh.pages[c * kChunkPages + x]);
+            __builtin_amdgcn_global_load_lds(kc_lane + (size_t)pg * page_elems,
+                                             (__attribute__((address_space(3))) void*)(dst + x * kPfPageStride), 16,
+                                             0, 0);
+        }
+    };
+    if (nchunks > 0) copy_chunk(0, &kc_even[0][0]);
+
     // query operand of the wave's row tiles; a row without a query (past the
     // block's queries or the pair's rows) loads the block's last query: its
     // products are masked by position (pass 1) or weighted by
-    // exp2(-lse) = 0 (pass 2)
+    // exp2(-lse) = 0 (pass 2).  qi = row / G from a float reciprocal: exact,
+    // the quotient being at least 1 / (2G) from an integer.
     bf16x8 qb[RTW][4];
     int qpos[RTW];  // query position of this lane's row r in each tile (-1: none)
 #pragma unroll
     for (int u = 0; u < RTW; ++u) {
         const int row = (row_tile0 + u) * 16 + r;
-        const int qi = row / a.G, h = row % a.G;
+        const int qi = (int)(((float)row + 0.5f) * a.inv_g), h = row - qi * a.G;
         const bool ok = row < a.rows && qi < P.nq;
         qpos[u] = ok ? P.p0 + qi : -1;
         const uint16_t* qr =
@@ -185,37 +230,35 @@ __global__ __launch_bounds__(256, 2) void pf_score_kernel(PfArgs a)
     const int wave_row_last = (row_tile0 + RTW) * 16 - 1;
     const bool wave_full = wave_row_last < a.rows && wave_row_last / a.G < P.nq;
     const int wave_p0 = P.p0 + row_tile0 * 16 / a.G;
-#pragma unroll
-    for (int i = 0; i < kKPS / SL / 4; ++i) sh.kc[wave + 4 * i][lane] = pgv[i];
-    __syncthreads();
     const float sc = a.scale_log2;
     // Is the pair of key tiles from kt (32 keys) visible to every row of the
     // wave?  Then no element is tested (key < n_c(p + 1)  <=>  16 key + 32 <=
-    // p + 1); tiles near the diagonal, the split's end and absent rows take
+    // p + 1); tiles near the diagonal, the span's end and absent rows take
     // the tested path.
     auto pair_fast = [&](int kt) {
         return wave_full && kt + 32 <= key_hi && (kt + 31) * kPoolS + kPoolK <= wave_p0 + 1;
     };
-    // Operand of the key tile from kt: lane r holds key kt + r, chunk 4 st + kq.
-    // kt - key_lo is a multiple of 16, so the key sits in staged page
-    // (kt - key_lo) / SL + r / SL, slot r % SL; every tile of the split lies
-    // inside the staged pages (keys past key_hi are masked or unused).
-    const uint4* kl = &sh.kc[r / SL][kq * SL + r % SL];
-    auto load_tile = [&](int kt, uint4 (&kf)[4]) {
-        const uint4* kp = kl + ((kt - key_lo) / SL) * kPfPageStride;
+    // Operand of the key tile from kt in the chunk from c0 (buffer cb): lane r
+    // holds key kt + r, chunk 4 st + kq.  kt - c0 is a multiple of 16, so the
+    // key sits in staged page (kt - c0) / SL + r / SL, slot r % SL; every tile
+    // of the chunk lies inside its staged pages.
+    const int kl = (r / SL) * kPfPageStride + kq * SL + r % SL;
+    auto load_tile = [&](const uint4* __restrict__ buf, int rel, uint4 (&kf)[4]) {
+        const uint4* kp = buf + kl + (rel / SL) * kPfPageStride;
 #pragma unroll
         for (int st = 0; st < 4; ++st) kf[st] = kp[st * 4 * SL];
     };
-    // the next pair's operands are read once the current pair's products are
-    // issued (the read past the split's last pair repeats it)
-    auto next_pair = [&](int kt) { return min(kt + 32, key_lo + kKPS - 32); };
 
     if (PASS == 1) {
         // Products as (key, row) tiles: lane r holds row r, keys 4 kq + i.
-        // Running state per row of every tile: the maximum of the raw
-        // products seen (the scale is positive) and the sum of
-        // exp2((z - max) * scale), the scale folded into the exponent's fma;
-        // the maximum is updated once per 8 products of a lane.
+        // Running state per row of every tile: a reference m_raw (a maximum
+        // of raw products; the scale is positive) and s_run = sum of
+        // exp2((z - m_raw) * scale), the scale folded into the exponent's fma.
+        // The first pair of key tiles visible to the whole wave sets the
+        // reference to the row maxima; later such pairs keep it (no maximum
+        // is taken) unless a chunk's sums stop being finite -- a product more
+        // than 2^128 above the reference -- when the chunk is done again
+        // from its checkpoint with the maximum updated at every pair.
         float m_raw[RTW], s_run[RTW];
 #pragma unroll
         for (int u = 0; u < RTW; ++u) {
@@ -246,49 +289,118 @@ __global__ __launch_bounds__(256, 2) void pf_score_kernel(PfArgs a)
                 }
             }
         };
-        uint4 kf0[4], kf1[4];
-        load_tile(key_lo, kf0);
-        load_tile(key_lo + 16, kf1);
-        for (int kt = key_lo; kt < key_hi; kt += 32) {
-            if (pair_fast(kt)) {
+        // a visible pair with the maximum updated (sets the reference)
+        auto pair_max = [&](const uint4 (&kf0)[4], const uint4 (&kf1)[4]) {
+#pragma unroll
+            for (int u = 0; u < RTW; ++u) {
+                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < 4; ++st) s0 = mfma16(as_bf16x8(kf0[st]), qb[u][st], s0);
+#pragma unroll
+                for (int st = 0; st < 4; ++st) s1 = mfma16(as_bf16x8(kf1[st]), qb[u][st], s1);
+                const float mx =
+                    vmax3(vmax3(vmax3(vmax3(m_raw[u], s0[0], s0[1]), s0[2], s0[3]), s1[0], s1[1]), s1[2], s1[3]);
+                const float nm = -(mx * sc);
+                const float e0 = (fexp2(fmaf(s0[0], sc, nm)) + fexp2(fmaf(s0[1], sc, nm))) +
+                                 (fexp2(fmaf(s0[2], sc, nm)) + fexp2(fmaf(s0[3], sc, nm)));
+                const float e1 = (fexp2(fmaf(s1[0], sc, nm)) + fexp2(fmaf(s1[1], sc, nm))) +
+                                 (fexp2(fmaf(s1[2], sc, nm)) + fexp2(fmaf(s1[3], sc, nm)));
+                s_run[u] = fmaf(s_run[u], fexp2(fmaf(m_raw[u], sc, nm)), e0 + e1);
+                m_raw[u] = mx;
+            }
+        };
+        // a visible pair against the fixed reference
+        auto pair_ref = [&](const uint4 (&kf0)[4], const uint4 (&kf1)[4]) {
+#pragma unroll
+            for (int u = 0; u < RTW; ++u) {
+                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < 4; ++st) s0 = mfma16(as_bf16x8(kf0[st]), qb[u][st], s0);
+#pragma unroll
+                for (int st = 0; st < 4; ++st) s1 = mfma16(as_bf16x8(kf1[st]), qb[u][st], s1);
+                const float nm = -(m_raw[u] * sc);
+                const float e0 = (fexp2(fmaf(s0[0], sc, nm)) + fexp2(fmaf(s0[1], sc, nm))) +
+                                 (fexp2(fmaf(s0[2], sc, nm)) + fexp2(fmaf(s0[3], sc, nm)));
+                const float e1 = (fexp2(fmaf(s1[0], sc, nm)) + fexp2(fmaf(s1[1], sc, nm))) +
+                                 (fexp2(fmaf(s1[2], sc, nm)) + fexp2(fmaf(s1[3], sc, nm)));
+                s_run[u] += e0 + e1;
+            }
+        };
+        bool have_ref = false;  // wave-uniform
+        auto chunk = [&](int c, const uint4* __restrict__ cur, uint4* __restrict__ nxt) {
+            __syncthreads();  // chunk c in LDS; every wave done with chunk c - 1
+            if (c + 1 < nchunks) copy_chunk(c + 1, nxt);
+            const int c0 = key_lo + c * kChunk, c1 = min(c0 + kChunk, key_hi);
+            float m_chk[RTW], s_chk[RTW];
+#pragma unroll
+            for (int u = 0; u < RTW; ++u) {
+                m_chk[u] = m_raw[u];
+                s_chk[u] = s_run[u];
+            }
+            const bool ref_chk = have_ref;
+            auto pass = [&](bool careful) {
+                uint4 kf0[4], kf1[4];
+                load_tile(cur, 0, kf0);
+                load_tile(cur, 16, kf1);
+                for (int kt = c0; kt < c1; kt += 32) {
+                    if (pair_fast(kt)) {
+                        if (have_ref && !careful) {
+                            pair_ref(kf0, kf1);
+                        } else {
+                            pair_max(kf0, kf1);
+                            have_ref = true;
+                        }
+                    } else {
+                        tested(kt, kf0);
+                        if (kt + 16 < key_hi) tested(kt + 16, kf1);
+                    }
+                    // the next pair of the chunk (the last pair reads itself again)
+                    const int nx = min(kt - c0 + 32, kChunk - 32);
+                    load_tile(cur, nx, kf0);
+                    load_tile(cur, nx + 16, kf1);
+                }
+            };
+            pass(false);
+            bool bad = false;
+#pragma unroll
+            for (int u = 0; u < RTW; ++u) bad = bad || !(s_run[u] < INFINITY);
+            if (__ballot(bad) != 0) {  // rare: from the checkpoint, maximum at every pair
 #pragma unroll
                 for (int u = 0; u < RTW; ++u) {
-                    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int st = 0; st < 4; ++st) c0 = mfma16(as_bf16x8(kf0[st]), qb[u][st], c0);
-#pragma unroll
-                    for (int st = 0; st < 4; ++st) c1 = mfma16(as_bf16x8(kf1[st]), qb[u][st], c1);
-                    const float mx = vmax3(vmax3(vmax3(vmax3(m_raw[u], c0[0], c0[1]), c0[2], c0[3]), c1[0], c1[1]),
-                                           c1[2], c1[3]);
-                    const float nm = -(mx * sc);
-                    const float e0 = (fexp2(fmaf(c0[0], sc, nm)) + fexp2(fmaf(c0[1], sc, nm))) +
-                                     (fexp2(fmaf(c0[2], sc, nm)) + fexp2(fmaf(c0[3], sc, nm)));
-                    const float e1 = (fexp2(fmaf(c1[0], sc, nm)) + fexp2(fmaf(c1[1], sc, nm))) +
-                                     (fexp2(fmaf(c1[2], sc, nm)) + fexp2(fmaf(c1[3], sc, nm)));
-                    s_run[u] = fmaf(s_run[u], fexp2(fmaf(m_raw[u], sc, nm)), e0 + e1);
-                    m_raw[u] = mx;
+                    m_raw[u] = m_chk[u];
+                    s_run[u] = s_chk[u];
                 }
-            } else {
-                tested(kt, kf0);
-                if (kt + 16 < key_hi) tested(kt + 16, kf1);
+                have_ref = ref_chk;
+                pass(true);
             }
-            load_tile(next_pair(kt), kf0);
-            load_tile(next_pair(kt) + 16, kf1);
+        };
+        for (int c = 0; c < nchunks; c += 2) {
+            chunk(c, &kc_even[0][0], &kc_odd[0][0]);
+            if (c + 1 < nchunks) chunk(c + 1, &kc_odd[0][0], &kc_even[0][0]);
         }
-        // per row: combine the four lanes (kq) that hold its keys, in log2 units
+        // per row: combine the four lanes (kq) that hold its keys, in log2
+        // units: the halves swapped and merged, then the odd and even rows
+        auto merge = [](float m, float s, float mo, float so, float& mr, float& sr) {
+            const float mn = fmaxf(m, mo);
+            sr = mn == -INFINITY ? 0.f : s * fexp2(m - mn) + so * fexp2(mo - mn);
+            mr = mn;
+        };
+        auto swap32 = [](float x) {
+            return __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        };
+        auto swap16 = [](float x) {
+            return __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        };
+        float2* prow = a.part + ((size_t)pair * a.rows + row_tile0 * 16 + r) * a.key_splits + ks;
 #pragma unroll
         for (int u = 0; u < RTW; ++u) {
             float m = m_raw[u] * sc, s = s_run[u];
-#pragma unroll
-            for (int off = 16; off < 64; off <<= 1) {
-                const float mo = __shfl_xor(m, off), so = __shfl_xor(s, off);
-                const float mn = fmaxf(m, mo);
-                s = mn == -INFINITY ? 0.f : s * fexp2(m - mn) + so * fexp2(mo - mn);
-                m = mn;
-            }
+            const auto hm = swap32(m), hs = swap32(s);
+            merge(__uint_as_float(hm[0]), __uint_as_float(hs[0]), __uint_as_float(hm[1]), __uint_as_float(hs[1]), m, s);
+            const auto qm = swap16(m), qs = swap16(s);
+            merge(__uint_as_float(qm[0]), __uint_as_float(qs[0]), __uint_as_float(qm[1]), __uint_as_float(qs[1]), m, s);
             const int row = (row_tile0 + u) * 16 + r;
-            if (kq == 0 && row < a.rows)
-                a.part[((size_t)pair * a.rows + row) * a.key_splits + ks] = make_float2(m, s);
+            if (kq == 0 && row < a.rows) prow[(size_t)u * 16 * a.key_splits] = make_float2(m, s);
         }
     } else {
         // Products as (row, key) tiles (operands swapped): lane r holds key r,
@@ -330,8 +442,8 @@ __global__ __launch_bounds__(256, 2) void pf_score_kernel(PfArgs a)
             const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
             return __uint_as_float(q[0]) + __uint_as_float(q[1]);
         };
-        // one key tile at a time, the other buffer's tile read meanwhile
-        auto step = [&](int kt, const uint4 (&kf)[4]) {
+        // one key tile at a time
+        auto step = [&](int kt, int rel, int cb, const uint4 (&kf)[4]) {
             float cs = 0.f;
             if (wave_full && kt + 16 <= key_hi && (kt + 15) * kPoolS + kPoolK <= wave_p0 + 1) {
 #pragma unroll
@@ -348,57 +460,45 @@ __global__ __launch_bounds__(256, 2) void pf_score_kernel(PfArgs a)
                 cs = tested(kt, kf);
             }
             cs = lanes4_sum(cs);
-            if (kq == 0) sh.ksum[wave][kt - key_lo + r] = cs;
+            if (kq == 0) sh.ksum[cb][wave][rel + r] = cs;
         };
-        uint4 kf0[4], kf1[4];
-        load_tile(key_lo, kf0);
-        for (int kt = key_lo; kt < key_hi; kt += 32) {
-            load_tile(kt + 16, kf1);
-            step(kt, kf0);
-            load_tile(next_pair(kt), kf0);
-            if (kt + 16 < key_hi) step(kt + 16, kf1);
+        // a chunk's column sums leave once every wave has written them
+        float* dst = a.colsum + ((size_t)pair * a.row_groups + rg) * a.zlen;
+        auto store_chunk = [&](int c) {
+            const int x = tid, kj = key_lo + c * kChunk + x;
+            if (x < kChunk && kj < key_hi) {
+                const int cb = c & 1;
+                dst[kj] = ((sh.ksum[cb][0][x] + sh.ksum[cb][1][x]) + sh.ksum[cb][2][x]) + sh.ksum[cb][3][x];
+            }
+        };
+        auto chunk = [&](int c, const uint4* __restrict__ cur, uint4* __restrict__ nxt) {
+            __syncthreads();  // chunk c in LDS; every wave done with chunk c - 1
+            if (c + 1 < nchunks) copy_chunk(c + 1, nxt);
+            if (c > 0) store_chunk(c - 1);
+            const int c0 = key_lo + c * kChunk, c1 = min(c0 + kChunk, key_hi), cb = c & 1;
+            for (int kt = c0; kt < c1; kt += 16) {
+                uint4 kf[4];
+                load_tile(cur, kt - c0, kf);
+                step(kt, kt - c0, cb, kf);
+            }
+        };
+        for (int c = 0; c < nchunks; c += 2) {
+            chunk(c, &kc_even[0][0], &kc_odd[0][0]);
+            if (c + 1 < nchunks) chunk(c + 1, &kc_odd[0][0], &kc_even[0][0]);
         }
         __syncthreads();
-        float* dst = a.colsum + ((size_t)pair * a.row_groups + rg) * a.zlen + key_lo;
-        for (int x = tid; x < kKPS; x += 256) {
-            const int kj = key_lo + x;
-            float v = 0.f;
-            if (kj < key_hi) v = ((sh.ksum[0][x] + sh.ksum[1][x]) + sh.ksum[2][x]) + sh.ksum[3][x];
-            dst[x] = v;
-        }
+        if (nchunks > 0) store_chunk(nchunks - 1);
     }
 }
 
-// lse (log2 units) of every row's scoring softmax from the pass-1 partials
-// of its key splits, combined in split order; +inf for a row without visible
-// keys (pass 2 then adds nothing for it).  One thread per (pair, row).
+// lse of every row's scoring softmax (row_lse), one thread per (pair, row);
+// used when the pairs have many key splits.
 __global__ __launch_bounds__(256) void pf_lse_kernel(PfArgs a, int total)
 {
     const int t = blockIdx.x * 256 + threadIdx.x;
     if (t >= total) return;
-    const int pair = t / a.rows, row = t % a.rows;
-    const PfPair P = pf_pair(a, pair);
-    float m = -INFINITY, acc = 0.f;
-    if (!P.empty) {
-        // partials read 16 at a time, all loads of a batch in flight
-        const float2* pp = a.part + (size_t)t * a.key_splits;
-        for (int i0 = 0; i0 < a.key_splits; i0 += 16) {
-            float2 v[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) v[u] = i0 + u < a.key_splits ? pp[i0 + u] : make_float2(-INFINITY, 0.f);
-            float mb = m;
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                if (v[u].y > 0.f) mb = fmaxf(mb, v[u].x);
-            if (mb == -INFINITY) continue;
-            acc = m == -INFINITY ? 0.f : acc * fexp2(m - mb);
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                if (v[u].y > 0.f) acc += v[u].y * fexp2(v[u].x - mb);
-            m = mb;
-        }
-    }
-    a.rlse[t] = acc > 0.f ? m + log2f(acc) : INFINITY;
+    const PfPair P = pf_pair(a, t / a.rows);
+    a.rlse[t] = P.empty ? INFINITY : row_lse(a.part + (size_t)t * a.key_splits, a.key_splits);
 }
 
 // Block importance of a pair: sigma[j] = sum over row groups (fixed order) of
@@ -415,18 +515,36 @@ __global__ __launch_bounds__(256) void pf_pool_kernel(PfArgs a)
     const int nb = P.empty ? 0 : P.nb;
     for (int b = tid; b < nb; b += 256) sI[b] = 0.f;
     __syncthreads();
+    // thread t takes keys 4t .. 4t + 3 of every 1024, eight such groups per
+    // batch with all their loads in flight (a group's 16 bytes lie inside
+    // the column sums; keys past n_c are masked)
     const float* cs = a.colsum + (size_t)pair * a.row_groups * a.zlen;
-    for (int j0 = 4 * tid; j0 < (P.empty ? 0 : P.nck); j0 += 4 * 256) {
-        float sg[4];
+    const int nck = P.empty ? 0 : P.nck;
+    for (int j00 = 0; j00 < nck; j00 += 8 * 1024) {
+        float4 v[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float v = 0.f;
-            for (int q = 0; q < a.row_groups; ++q) v += cs[(size_t)q * a.zlen + j0 + e];
-            sg[e] = j0 + e < P.nck ? v : 0.f;
+        for (int k = 0; k < 8; ++k) {
+            const int j0 = j00 + 1024 * k + 4 * tid;
+            v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j0 < nck)
+                for (int q = 0; q < a.row_groups; ++q) {
+                    const float4 w = *reinterpret_cast<const float4*>(cs + (size_t)q * a.zlen + j0);
+                    v[k].x += w.x;
+                    v[k].y += w.y;
+                    v[k].z += w.z;
+                    v[k].w += w.w;
+                }
         }
-        const int b = j0 >> 2;
-        atomicAdd(&sI[b], (sg[0] + sg[1]) + (sg[2] + sg[3]));
-        if (j0 + 3 < P.nck && b + 1 < nb) atomicAdd(&sI[b + 1], sg[3]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int j0 = j00 + 1024 * k + 4 * tid;
+            if (j0 >= nck) continue;
+            const float sg[4] = {v[k].x, j0 + 1 < nck ? v[k].y : 0.f, j0 + 2 < nck ? v[k].z : 0.f,
+                                 j0 + 3 < nck ? v[k].w : 0.f};
+            const int b = j0 >> 2;
+            atomicAdd(&sI[b], (sg[0] + sg[1]) + (sg[2] + sg[3]));
+            if (j0 + 3 < nck && b + 1 < nb) atomicAdd(&sI[b + 1], sg[3]);
+        }
     }
     __syncthreads();
     for (int b = tid; b < a.max_nb; b += 256) {
@@ -643,19 +761,30 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
 
     // this workgroup's pages: all, or half of them
     const int i0 = n * ks / a.ksplit, i1 = n * (ks + 1) / a.ksplit;
+    uint4 stk2[4], stv2[4];
     if (i1 > i0) {
         fetch(i0, stk, stv);
         stash(0, stk, stv);
+        fetch(i0 + 1, stk, stv);
         __syncthreads();
     }
-    for (int idx = i0; idx < i1; ++idx) {
+    // two pages in flight: page idx + 1, loaded while page idx - 1 was
+    // computed, is stashed after page idx; page idx + 2 loads meanwhile (the
+    // two register sets alternate, hence the unrolled pair of steps)
+    auto step = [&](int idx, const uint4 (&ka)[4], const uint4 (&va)[4], uint4 (&kb)[4], uint4 (&vb)[4]) {
         const int buf = (idx - i0) & 1;
-        fetch(idx + 1, stk, stv);  // in flight while page idx is computed
+        fetch(idx + 2, kb, vb);
         const int b = list[idx].x;
         if (b >= 0) compute(buf, b);
-        if (idx + 1 < i1) stash(buf ^ 1, stk, stv);
+        if (idx + 1 < i1) stash(buf ^ 1, ka, va);
         __syncthreads();
+    };
+    int idx = i0;
+    for (; idx + 1 < i1; idx += 2) {
+        step(idx, stk, stv, stk2, stv2);
+        step(idx + 1, stk2, stv2, stk, stv);
     }
+    if (idx < i1) step(idx, stk, stv, stk2, stv2);
     if (a.ksplit > 1) {  // unnormalised partial of this half, rows holding a query
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -748,7 +877,9 @@ static PfArgs pf_args(const Plan& pl, const PfPlan& pf, const nosa_paged_kv* kv,
     a.rows = pf.rows;
     a.row_groups = pf.row_groups;
     a.key_splits = pf.key_splits;
-    a.zlen = pf.key_splits * kKPS;
+    a.span = pf.span;
+    a.zlen = pf.key_splits * pf.span;
+    a.inv_g = (float)(1.0 / pl.G);
     a.max_nb = pl.max_nb;
     a.max_sel = pl.max_sel;
     return a;
@@ -762,7 +893,10 @@ hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_k
     a.qbase = qbase;
     a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + pf.off_part);
     a.colsum = reinterpret_cast<float*>(static_cast<char*>(ws) + pf.off_colsum);
-    a.rlse = reinterpret_cast<float*>(static_cast<char*>(ws) + pf.off_rlse);
+    // the rows' lse by its own kernel only when pass 2 would merge many
+    // partials per row
+    a.rlse = pf.key_splits > kPfFoldSplits ? reinterpret_cast<float*>(static_cast<char*>(ws) + pf.off_rlse)
+                                            : nullptr;
     a.scores = scores;
     const dim3 grid(pf.npairs * pf.row_groups * pf.key_splits);
 #define NOSA_PF(PASS, R) hipLaunchKernelGGL((pf_score_kernel<PASS, R>), grid, dim3(256), 0, stream, a)
@@ -775,7 +909,7 @@ hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_k
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        if (pass == 1) {
+        if (pass == 1 && a.rlse) {
             const int total = pf.npairs * pf.rows;
             hipLaunchKernelGGL(pf_lse_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, a, total);
             e = hipGetLastError();

@@ -12,7 +12,8 @@ import torch
 from block_sparse_attention_nosa_amd import nosa, synth
 from oracle import oracle as ora
 
-from helpers import OUT_MAX_ABS, OUT_MEAN_ABS, TIE_BAND, build_kc, local_blocks, log, make_case
+from helpers import (OUT_MAX_ABS, OUT_MEAN_ABS, TIE_BAND, DecodeCase, build_kc, local_blocks, log,
+                     make_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -169,6 +170,35 @@ def test_prefill_locality(locality):
     log(f"case: prefill locality {locality}")
     c = make_case(_wl([6000, 2200], [400, 130], topk=12, seed=int(locality * 8), locality=locality))
     _full(c, f"pf loc {locality}")
+
+
+def test_prefill_logits_far_below_the_span_start():
+    """Logits spread far beyond the float range of exp2: every query and,
+    negated, the keys of tokens 0 .. 527 share a direction u (entries +-1) at
+    3.5 times the noise, so pooled keys 0 .. 31 -- the first pair of key
+    tiles of the first span -- score 180 or more (log2 units) below the
+    span's later keys for every row.  The scoring pass's reference taken from
+    that pair overflows on the later keys and the span is redone with the
+    maximum tracked.  The blocks that compete for the top-k keep ordinary
+    scores (the pushed-down ones only lose), so everything must match the
+    reference."""
+    log("case: prefill with logits far below the span start")
+    w = _wl([3000], [200], seed=41)
+    inp = synth.make_inputs(w)
+    gen = torch.Generator().manual_seed(41)
+    u = torch.randint(0, 2, (w.head_dim,), generator=gen).float() * 2 - 1
+    inp["q"] = (inp["q"].float() + 3.5 * u).to(torch.bfloat16)
+    k = inp["k"].float()
+    k[0:528] -= 3.5 * u
+    inp["k"] = k.to(torch.bfloat16)
+    pg = synth.to_paged(inp, w, permute=True, device="cuda")
+    p = nosa.params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.kernel, w.stride,
+                    w.topk, w.window, locality=w.locality)
+    op = ora.Params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.kernel, w.stride,
+                    w.topk, w.window, locality=w.locality)
+    kv = nosa.paged_kv(pg["k_pool"], pg["v_pool"], pg["kc_pool"], pg["block_table"])
+    c = DecodeCase(w, inp, pg, p, op, kv)
+    _full(c, "pf far below")
 
 
 def test_prefill_131072_sampled_query_blocks():

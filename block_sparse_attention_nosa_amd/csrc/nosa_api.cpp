@@ -196,16 +196,16 @@ void make_pf_plan(const Plan& pl, int max_seqlen_q, PfPlan* pf)
     F.rows = 64 * pl.G;
     F.rtw = pl.G <= 1 ? 1 : pl.G <= 2 ? 2 : pl.G <= 4 ? 4 : 8;
     F.row_groups = ceil_div(4 * pl.G, 4 * F.rtw);
-    // scoring workgroups: the pooled keys of a row group in chunks of 128,
-    // spans of whole chunks (at most 16) sized for about two workgroups per
-    // CU over the launch
-    const int chunks = ceil_div(pl.max_nc > 0 ? pl.max_nc : 1, 128);
+    // scoring workgroups: the pooled keys of a row group in chunks of
+    // kPfChunk, spans of whole chunks (at most kPfMaxSpanChunks) sized for
+    // about kPfScoreWorkgroups workgroups over the launch
+    const int chunks = ceil_div(pl.max_nc > 0 ? pl.max_nc : 1, kPfChunk);
     const long long row_sets = (long long)F.npairs * F.row_groups;
     const long long want = row_sets > 0 ? (kPfScoreWorkgroups + row_sets - 1) / row_sets : 1;
     const int spans = (int)(want < chunks ? want : chunks);
     int per_span = ceil_div(chunks, spans > 0 ? spans : 1);
-    per_span = per_span < 16 ? per_span : 16;
-    F.span = 128 * per_span;
+    per_span = per_span < kPfMaxSpanChunks ? per_span : kPfMaxSpanChunks;
+    F.span = kPfChunk * per_span;
     F.key_splits = ceil_div(chunks, per_span);
     F.attn_groups = ceil_div(4 * pl.G, 8);
     const size_t np = (size_t)F.npairs;

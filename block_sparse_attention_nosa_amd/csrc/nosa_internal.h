@@ -80,6 +80,8 @@ struct PfPlan {
     int split_rows = 0;  // rows per pair in the partials: min(64, max_seqlen_q) * G
 };
 constexpr int kPfScoreWorkgroups = 512;  // scoring workgroups a launch aims for
+constexpr int kPfChunk = 128;           // pooled keys the scoring passes stage in LDS at a time
+constexpr int kPfMaxSpanChunks = 16;    // chunks per scoring workgroup at most
 constexpr int kPfSplitGroups = 256;  // one workgroup per CU or fewer: split the pages
 
 // Offloaded KV (device pointers; the host pools as the device sees them).

@@ -26,8 +26,8 @@
 namespace nosa {
 
 constexpr int kQB = 64;   // queries per query block
-constexpr int kChunk = 128;      // pooled keys staged in LDS at a time by the scoring passes
-constexpr int kMaxSpan = 2048;   // pooled keys per scoring workgroup at most
+constexpr int kChunk = kPfChunk;                       // pooled keys staged in LDS at a time
+constexpr int kMaxSpan = kPfChunk * kPfMaxSpanChunks;  // pooled keys per scoring workgroup at most
 constexpr int kPfFoldSplits = 16;  // key splits up to which pass 2 merges the row partials itself
 constexpr float kPfRescale = 8.f;  // exponent headroom before the attention rescales (log2)
 
@@ -563,16 +563,14 @@ __global__ __launch_bounds__(256) void pf_pool_kernel(PfArgs a)
 // the fragment of QK^T tile t, k-step st is run 4t + st, that of PV k-step
 // u, channel tile nt is run 8u + nt, lane l at byte 16 l of its run, so a
 // wave's fragment read is 1 KB of consecutive LDS.
-struct PfAttnLds {
-    uint16_t k[2][BS * D];
-    uint16_t v[2][BS * D];
-};
+typedef uint16_t PfPageBuf[BS * D];
 
 // Workgroup = 4 waves x 2 row tiles (128 rows) of one pair; loops over the
 // pair's kept pages, each staged once through LDS for all 8 row tiles.  The
-// (block, page) list goes to LDS first; page i + 1's loads are issued before
-// page i is computed and land in the other LDS buffer after it, so one
-// barrier per page suffices.
+// (block, page) list goes to LDS first; page i + 1 is copied by direct
+// global-to-LDS loads into the other buffer while page i is computed, so one
+// barrier per page suffices (the two buffers are distinct objects: a read
+// of one is known not to wait for the copy into the other).
 //
 // Workgroups are dealt to the eight XCDs round-robin by index, so index b is
 // mapped to the logical workgroup (b % 8) * per_xcd + b / 8: the attn_groups
@@ -586,7 +584,7 @@ struct PfAttnLds {
 __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_groups, int total,
                                                         int per_xcd)
 {
-    __shared__ PfAttnLds sh;
+    __shared__ PfPageBuf k_even, v_even, k_odd, v_odd;
     extern __shared__ __align__(16) char smem[];
     int2* list = reinterpret_cast<int2*>(smem);  // [max_sel] (block, page)
     const int lid_k = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
@@ -630,29 +628,19 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
         for (int nt = 0; nt < 8; ++nt) o[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();  // the list
 
-    // thread tid moves the 16-byte chunks tid + 256c (c < 4) of a K and a V
-    // page: the same offsets in global memory and in LDS
-    uint4 stk[4], stv[4];
-    // (unconditional loads: past the list, or for a dropped entry, page 0 is
-    // read and never used; a branch around the loads makes the compiler wait
-    // for every outstanding load at the loop head)
-    auto fetch = [&](int idx, uint4 (&k4)[4], uint4 (&v4)[4]) {
-        const int page = idx < n ? list[idx].y : 0;
-        const uint16_t* kb = a.k_pool + ((size_t)page * a.Hkv + P.g) * BS * D;
-        const uint16_t* vb = a.v_pool + ((size_t)page * a.Hkv + P.g) * D * BS;
+    // page idx of the list into LDS: wave w copies the 1 KB runs w, w + 4,
+    // w + 8, w + 12 of the K and of the V page (past the list, page 0 is
+    // copied and never used)
+    auto copy_page = [&](int idx, uint16_t* __restrict__ kd, uint16_t* __restrict__ vd) {
+        const int page = __builtin_amdgcn_readfirstlane(idx < n ? list[idx].y : 0);
+        const size_t base = ((size_t)page * a.Hkv + P.g) * BS * D + lane * 8;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int ch = tid + 256 * c;
-            k4[c] = ldg16(kb + ch * 8);
-            v4[c] = ldg16(vb + ch * 8);
-        }
-    };
-    auto stash = [&](int buf, const uint4 (&k4)[4], const uint4 (&v4)[4]) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int ch = tid + 256 * c;
-            *reinterpret_cast<uint4*>(&sh.k[buf][ch * 8]) = k4[c];
-            *reinterpret_cast<uint4*>(&sh.v[buf][ch * 8]) = v4[c];
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const int c = __builtin_amdgcn_readfirstlane(wave) + 4 * c4;
+            __builtin_amdgcn_global_load_lds(a.k_pool + base + c * 512,
+                                             (__attribute__((address_space(3))) void*)(kd + c * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(a.v_pool + base + c * 512,
+                                             (__attribute__((address_space(3))) void*)(vd + c * 512), 16, 0, 0);
         }
     };
     // every row of the workgroup holds a query, and the smallest position:
@@ -676,7 +664,7 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
     // passes it by more than kPfRescale, so exponentials stay below
     // 2^kPfRescale and the accumulators are rarely rescaled; any reference
     // gives the same quotient O / l and lse = m + log2 l.
-    auto compute = [&](int buf, int b_cur) {
+    auto compute = [&](const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int b_cur) {
         // S^T = K q^T, raw products: lane holds row r, keys of tile t as
         // mapped by the K page layout; K fragments from LDS, shared
         float x[2][4][4];
@@ -685,7 +673,7 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
             bf16x8 kf[4];
 #pragma unroll
             for (int st = 0; st < 4; ++st)
-                kf[st] = as_bf16x8(*reinterpret_cast<const uint4*>(&sh.k[buf][((t * 4 + st) * 64 + lane) * 8]));
+                kf[st] = as_bf16x8(*reinterpret_cast<const uint4*>(kc + ((t * 4 + st) * 64 + lane) * 8));
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -753,7 +741,7 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
                 const bf16x8 vf =
-                    as_bf16x8(*reinterpret_cast<const uint4*>(&sh.v[buf][((uu * 8 + nt) * 64 + lane) * 8]));
+                    as_bf16x8(*reinterpret_cast<const uint4*>(vc + ((uu * 8 + nt) * 64 + lane) * 8));
 #pragma unroll
                 for (int u = 0; u < 2; ++u) o[u][nt] = mfma16(vf, pa[u][uu], o[u][nt]);
             }
@@ -761,30 +749,18 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
 
     // this workgroup's pages: all, or half of them
     const int i0 = n * ks / a.ksplit, i1 = n * (ks + 1) / a.ksplit;
-    uint4 stk2[4], stv2[4];
-    if (i1 > i0) {
-        fetch(i0, stk, stv);
-        stash(0, stk, stv);
-        fetch(i0 + 1, stk, stv);
-        __syncthreads();
-    }
-    // two pages in flight: page idx + 1, loaded while page idx - 1 was
-    // computed, is stashed after page idx; page idx + 2 loads meanwhile (the
-    // two register sets alternate, hence the unrolled pair of steps)
-    auto step = [&](int idx, const uint4 (&ka)[4], const uint4 (&va)[4], uint4 (&kb)[4], uint4 (&vb)[4]) {
-        const int buf = (idx - i0) & 1;
-        fetch(idx + 2, kb, vb);
+    if (i1 > i0) copy_page(i0, k_even, v_even);
+    auto step = [&](int idx, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                    uint16_t* __restrict__ kn, uint16_t* __restrict__ vn) {
+        __syncthreads();  // page idx in LDS; every wave done with page idx - 1
+        if (idx + 1 < i1) copy_page(idx + 1, kn, vn);
         const int b = list[idx].x;
-        if (b >= 0) compute(buf, b);
-        if (idx + 1 < i1) stash(buf ^ 1, ka, va);
-        __syncthreads();
+        if (b >= 0) compute(kc, vc, b);
     };
-    int idx = i0;
-    for (; idx + 1 < i1; idx += 2) {
-        step(idx, stk, stv, stk2, stv2);
-        step(idx + 1, stk2, stv2, stk, stv);
+    for (int idx = i0; idx < i1; idx += 2) {
+        step(idx, k_even, v_even, k_odd, v_odd);
+        if (idx + 1 < i1) step(idx + 1, k_odd, v_odd, k_even, v_even);
     }
-    if (idx < i1) step(idx, stk, stv, stk2, stv2);
     if (a.ksplit > 1) {  // unnormalised partial of this half, rows holding a query
 #pragma unroll
         for (int u = 0; u < 2; ++u) {

@@ -124,6 +124,7 @@ int nosa_ref_check_params(const nosa_ref_params* p)
 int nosa_ref_compress_keys(const nosa_ref_params* p, const uint16_t* k, const int32_t* cu_k,
                            int B, int max_nc, uint16_t* kc)
 {
+    if (B < 0 || (B > 0 && (!k || !cu_k || !kc))) return -9;
     if (nosa_ref_check_params(p)) return -1;
     const int Hkv = p->num_kv_heads, d = p->head_dim;
     for (int s = 0; s < B; ++s)
@@ -154,6 +155,7 @@ int nosa_ref_compress_keys(const nosa_ref_params* p, const uint16_t* k, const in
 int nosa_ref_append_keys(const nosa_ref_params* p, const uint16_t* k, const int32_t* cu_k,
                          const int32_t* valid_len, int B, int max_nc, uint16_t* kc)
 {
+    if (B < 0 || (B > 0 && (!k || !cu_k || !valid_len || !kc))) return -9;
     if (nosa_ref_check_params(p)) return -1;
     const int Hkv = p->num_kv_heads, d = p->head_dim;
     for (int s = 0; s < B; ++s) {
@@ -199,6 +201,8 @@ int nosa_ref_block_scores(const nosa_ref_params* p, const uint16_t* q, const int
                           const uint16_t* kc, int max_nc, const int32_t* cu_k, int B,
                           int max_qblk, int max_nb, double* scores)
 {
+    /* required pointers (cu_q may be NULL: one query per sequence) */
+    if (B < 0 || (B > 0 && (!q || !kc || !cu_k || !scores))) return -9;
     if (nosa_ref_check_params(p)) return -1;
     const int Hq = p->num_q_heads, Hkv = p->num_kv_heads, G = Hq / Hkv, d = p->head_dim;
     const int bs = p->block_size;
@@ -301,6 +305,8 @@ int nosa_ref_select_blocks(const nosa_ref_params* p, const double* scores, const
                            const int32_t* cu_k, int B, int max_qblk, int max_nb, int max_sel,
                            int32_t* sel, int32_t* count)
 {
+    /* required pointers (cu_q may be NULL: one query per sequence) */
+    if (B < 0 || (B > 0 && (!scores || !cu_k || !sel || !count))) return -9;
     if (nosa_ref_check_params(p)) return -1;
     const int Hkv = p->num_kv_heads, bs = p->block_size, w = p->window / p->block_size;
     if (max_sel < p->topk + w) return -2;
@@ -366,6 +372,8 @@ int nosa_ref_sparse_attend(const nosa_ref_params* p, const uint16_t* q, const in
                            const int32_t* sel, const int32_t* count, int max_qblk, int max_sel,
                            double* out, double* lse)
 {
+    /* required pointers (cu_q may be NULL: one query per sequence) */
+    if (B < 0 || (B > 0 && (!q || !k || !v || !cu_k || !sel || !count || !out || !lse))) return -9;
     if (nosa_ref_check_params(p)) return -1;
     const int Hq = p->num_q_heads, Hkv = p->num_kv_heads, G = Hq / Hkv, d = p->head_dim;
     const int bs = p->block_size;
@@ -437,13 +445,13 @@ int nosa_ref_forward(const nosa_ref_params* p, const uint16_t* q, const int32_t*
                      double* scores, int32_t* sel, int32_t* count, double* out, double* lse)
 {
     int rc = nosa_ref_compress_keys(p, k, cu_k, B, max_nc, kc);
-    if (rc) return 10 + rc;
+    if (rc) return rc - 10;
     rc = nosa_ref_block_scores(p, q, cu_q, kc, max_nc, cu_k, B, max_qblk, max_nb, scores);
-    if (rc) return 20 + rc;
+    if (rc) return rc - 20;
     rc = nosa_ref_select_blocks(p, scores, cu_q, cu_k, B, max_qblk, max_nb, max_sel, sel, count);
-    if (rc) return 30 + rc;
+    if (rc) return rc - 30;
     rc = nosa_ref_sparse_attend(p, q, cu_q, k, v, cu_k, B, sel, count, max_qblk, max_sel, out, lse);
-    if (rc) return 40 + rc;
+    if (rc) return rc - 40;
     return 0;
 }
 
@@ -465,6 +473,7 @@ int nosa_ref_qkv_rope(const nosa_ref_params* p, int hidden, double theta, const 
                       const uint16_t* x, const uint16_t* w, const int32_t* pos, int B,
                       uint16_t* q, uint16_t* k, uint16_t* v)
 {
+    if (B < 0 || (B > 0 && (!x || !w || !pos || !q || !k || !v))) return -9;
     if (nosa_ref_check_params(p)) return -1;
     const int Hq = p->num_q_heads, Hkv = p->num_kv_heads, d = p->head_dim, half = d / 2;
     if (hidden <= 0 || B < 0 || d % 2) return -2;

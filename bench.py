@@ -18,14 +18,16 @@ graph of the steps), bracketed by device synchronisations; inputs are
 resident in HBM before it starts.
 
 Printed: one JSON line with the throughput (decode tokens/s = batch / step
-time), the roofline of the dominant kernel (the sparse attention, timed with
-HIP events around its own launches on the launch stream) and the CPU
-reference's throughput on a bounded sample of the same workload.
+time), the roofline of the timed step (its algorithmic bytes over the step
+time; the dominant kernel, top_kernel, named with its share from the
+committed kernel trace), the stand-alone attention entry point timed with
+HIP events on its own stream as a secondary figure, and the CPU reference's
+throughput on a bounded sample of the same workload.
 
 Traffic counters (kept out of the timed run):
     rocprofv3 --pmc FETCH_SIZE -d DIR_F -o run --output-format csv -- python bench.py --pmc-probe
     rocprofv3 --pmc WRITE_SIZE -d DIR_W -o run --output-format csv -- python bench.py --pmc-probe
-    python bench.py --pmc-summary DIR_F DIR_W > profiles/attention-decode-b8-16k_traffic.md
+    python bench.py --pmc-summary DIR_F DIR_W > profiles/decode-b8-16k_traffic.md
 The probe runs a plain copy of 256 MiB (calibration: bytes per counter unit)
 and the library's kernels on the default workload; the summary scales each
 kernel's counters by the copy's factors.  The JSON line reports that traffic
@@ -299,6 +301,9 @@ def main():
                     help="run the calibration copy and the kernels once each for counters")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs of --pmc-probe")
+    ap.add_argument("--counter-table", nargs="+", metavar="DIR",
+                    help="print a markdown table of the library kernels' counters from "
+                         "rocprofv3 --pmc output directories")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="table of a rocprofv3 --kernel-trace --stats csv run")
     args = ap.parse_args()
@@ -306,6 +311,8 @@ def main():
         return pmc_summary(*args.pmc_summary)
     if args.trace_summary:
         return trace_summary(args.trace_summary)
+    if args.counter_table:
+        return counter_table(args.counter_table)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -975,6 +982,16 @@ def pmc_summary(fetch_dir, write_dir):
         return traffic[ks[0]]
     step_t = pick("score_kernel") + pick("top_kernel") + pick("merge_kernel (decode step)")
     attn_t = pick("attend_kernel") + pick("merge_kernel (attention)")
+    # the pooled-key build of each layer cache at setup reads every K token
+    # once: B * L * Hkv * d bf16
+    kcb = [k for k in per if "kc_build_kernel" in k]
+    kc_lines = []
+    if kcb:
+        unique_k = w.batch * w.lens[0] * w.num_kv_heads * w.head_dim * 2
+        fb = float(np.mean(per[kcb[0]]["FETCH_SIZE"])) * 1024 * f_fetch
+        kc_lines = [f"- kc_build_fetch_bytes: {int(fb)} (one layer's full build)",
+                    f"- kc_build_unique_k_bytes: {unique_k}",
+                    f"- kc_build_fetch_over_unique_k: {fb / unique_k:.3f}"]
     lines += ["", "A decode step is its scoring, top and merge dispatches; the stand-alone "
               "attention its attention and merge dispatches (each merge dispatch is attributed "
               "to the launch before it).", "",
@@ -984,8 +1001,54 @@ def pmc_summary(fetch_dir, write_dir):
               f"- attention_traffic_bytes: {int(attn_t)}",
               f"- attention_algorithmic_bytes: {int(attn_alg)}",
               f"- attention_traffic_over_algorithmic: {attn_t / attn_alg:.3f}",
+              *kc_lines,
               f"- sources_sha256: {sources_sha256()}"]
     print("\n".join(lines))
+
+
+def counter_table(dirs):
+    """Markdown table of rocprofv3 counter runs: per library kernel, the mean
+    per dispatch of every counter found in the given directories, then the
+    figures derived from them where the counters are there (per SIMD of the
+    1024; VALU busy counts one issue cycle per 4 clocks, as the quad-cycle
+    counters do)."""
+    import collections
+    import numpy as np
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    order = []
+    for d in dirs:
+        for r in _csv_rows(d, "*counter_collection.csv"):
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            if "nosa::" not in name:
+                continue
+            if name not in order:
+                order.append(name)
+            acc[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    counters = sorted({c for k in acc for c in acc[k]})
+    print("| kernel | " + " | ".join(counters) + " |")
+    print("|---|" + "---:|" * len(counters))
+    for k in order:
+        cells = [f"{np.mean(acc[k][c]):.4g}" if c in acc[k] else "" for c in counters]
+        print(f"| `{k}` | " + " | ".join(cells) + " |")
+    print("")
+    for k in order:
+        m = {c: float(np.mean(v)) for c, v in acc[k].items()}
+        parts = []
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m:
+            parts.append(f"bf16 MFMA work {m['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.2f} GFLOP")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            parts.append(f"MFMA busy {m['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / 1e3:.1f}K cycles per SIMD")
+        if "SQ_ACTIVE_INST_VALU" in m:
+            parts.append(f"VALU issue {m['SQ_ACTIVE_INST_VALU'] * 4 / 1024 / 1e3:.1f}K cycles per SIMD")
+        if "SQ_INSTS_VALU_TRANS_F32" in m and "SQ_INSTS_VALU" in m:
+            parts.append(f"transcendental share of VALU instructions "
+                         f"{m['SQ_INSTS_VALU_TRANS_F32'] / m['SQ_INSTS_VALU']:.2f}")
+        if "GRBM_GUI_ACTIVE" in m:
+            parts.append(f"GPU busy {m['GRBM_GUI_ACTIVE'] / 8 / 1e3:.1f}K cycles per XCD")
+        if parts:
+            print(f"- `{k}`: " + "; ".join(parts))
+    print("")
+    print(f"- sources_sha256: {sources_sha256()}")
 
 
 def trace_summary(d):

@@ -301,6 +301,9 @@ def main():
                     help="run the calibration copy and the kernels once each for counters")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs of --pmc-probe")
+    ap.add_argument("--chip-probes", action="store_true",
+                    help="measure the chip costs the design rests on (instruction-mix overlap, LDS "
+                         "bandwidth, in-launch hand-off, dependent-load latency)")
     ap.add_argument("--counter-table", nargs="+", metavar="DIR",
                     help="print a markdown table of the library kernels' counters from "
                          "rocprofv3 --pmc output directories")
@@ -322,6 +325,8 @@ def main():
     import torch
     from block_sparse_attention_nosa_amd import nosa, synth
 
+    if args.chip_probes:
+        return chip_probes_main(args)
     if args.ceiling:
         return ceiling_main(args)
     w = synth.config(args.config)
@@ -1211,6 +1216,105 @@ def ceiling_main(args):
            "peak_gbs": HBM_PEAK_GBS,
            "device": torch.cuda.get_device_name(0)}
     print(json.dumps(out), flush=True)
+
+
+def chip_probes_main(args):
+    """Costs of this chip that the design rests on (the machine probes of
+    libnosa_ceiling.so; medians of repeated launches): how far VALU work and
+    MFMAs overlap in the prefill scoring step's instruction mix, the LDS read
+    bandwidth, a hand-off of partials inside one launch against a second
+    launch, and the latency of a dependent device-memory load."""
+    import ctypes
+    import numpy as np
+    import torch
+    from block_sparse_attention_nosa_amd import build
+    if not os.path.exists(build.PROBE_LIB):
+        raise SystemExit(f"{build.PROBE_LIB} is missing: build it first")
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.nosa_probe_mix.argtypes = [i32, i32, i32, vp, vp]
+    lib.nosa_probe_lds_read.argtypes = [i32, i32, vp, vp]
+    lib.nosa_probe_handoff.argtypes = [i32, i32, vp, vp, vp, vp]
+    lib.nosa_probe_chase.argtypes = [vp, i32, i32, vp, vp]
+    for f in ("nosa_probe_mix", "nosa_probe_lds_read", "nosa_probe_handoff", "nosa_probe_chase"):
+        getattr(lib, f).restype = ctypes.c_int
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def timed(launch, reps=5):
+        assert launch() == 0
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            assert launch() == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)  # us
+        return float(np.median(ts))
+
+    # instruction mix: 512 workgroups (two per CU, two waves per SIMD); per
+    # wave and iteration 64 MFMAs (1024 MFMA cycles) and the VALU work of
+    # 64 products; per SIMD an iteration runs two waves' worth
+    wgs, iters = 512, 2000
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    names = {0: "mfma_and_dependent_valu", 1: "mfma_only", 2: "valu_only", 3: "mfma_and_independent_valu"}
+    mix = {}
+    for m, name in names.items():
+        us = timed(lambda: lib.nosa_probe_mix(m, wgs, iters, sink.data_ptr(), sh))
+        mix[name] = round(us * 1e3 / iters, 1)  # ns per iteration per SIMD
+    t1, t2, t3 = mix["mfma_only"], mix["valu_only"], mix["mfma_and_independent_valu"]
+    mix["unit"] = "ns per iteration per SIMD (two waves, 128 MFMAs)"
+    mix["independent_overlap_of_mfma_time"] = round((t1 + t2 - t3) / t1, 3)
+    # LDS reads: 512 workgroups, 32 KB per wave per iteration
+    lsink = torch.empty(wgs * 256, dtype=torch.int32, device="cuda")
+    liters = 4000
+    us = timed(lambda: lib.nosa_probe_lds_read(wgs, liters, lsink.data_ptr(), sh))
+    lds_bytes = wgs * 4 * liters * 32 * 1024
+    lds = {"bytes_per_ns_per_cu": round(lds_bytes / (us * 1e3) / torch.cuda.get_device_properties(0).multi_processor_count, 1),
+           "total_tb_s": round(lds_bytes / (us * 1e-6) / 1e12, 1)}
+    # hand-off of 16 groups of 16 workgroups' 4 KB partials
+    groups = 16
+    part = torch.zeros(groups * 16 * 1024, dtype=torch.float32, device="cuda")
+    counter = torch.zeros(groups, dtype=torch.int32, device="cuda")
+    out = torch.zeros(groups * 1024, dtype=torch.float32, device="cuda")
+    want = torch.tensor([16 * 16 * g + 136 for g in range(groups)], dtype=torch.float32)
+    hand = {}
+    for mode, name in ((0, "release_acquire_fences"), (1, "coherent_stores_no_fence"), (2, "two_launches")):
+        out.zero_()
+        us = timed(lambda: lib.nosa_probe_handoff(mode, groups, part.data_ptr(), counter.data_ptr(),
+                                                  out.data_ptr(), sh), reps=11)
+        ok = bool(torch.equal(out.view(groups, 1024).cpu(), want[:, None].expand(groups, 1024)))
+        hand[name] = {"us": round(us, 2), "sums_correct": ok}
+    # dependent loads through a random cycle over 1 GiB (beyond the 256 MB
+    # Infinity Cache, which the writes of the cycle would otherwise fill)
+    n = 256 << 20
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    perm = torch.randperm(n, generator=gen, device="cuda")
+    nxt = torch.empty(n, dtype=torch.int32, device="cuda")
+    nxt[perm] = torch.roll(perm, -1).to(torch.int32)
+    steps = 20000
+    chase = {"buffer_mb": n * 4 >> 20}
+    ends = []
+    for vec, name in ((1, "vector_load_ns"), (0, "scalar_load_ns")):
+        csink = torch.zeros(64, dtype=torch.int32, device="cuda")
+        us = timed(lambda: lib.nosa_probe_chase(nxt.data_ptr(), steps, vec, csink.data_ptr(), sh), reps=3)
+        chase[name] = round(us * 1e3 / steps, 1)
+        csink.zero_()
+        assert lib.nosa_probe_chase(nxt.data_ptr(), steps, vec, csink.data_ptr(), sh) == 0
+        torch.cuda.synchronize()
+        ends.append(int(csink[0].item()))
+    i = 0
+    for _ in range(steps):  # the chain's end, followed on the host one load at a time
+        i = int(nxt[i].item())
+    chase["ends_match_host_walk"] = ends == [i, i]
+    res = {"metric": "chip probes", "value": mix["mfma_and_dependent_valu"], "unit": mix["unit"],
+           "n_gpus": 1, "higher_is_better": False, "dtype": "bf16/fp32", "data": "synthetic",
+           "config": {"workload": "chip-probes", "workgroups": wgs},
+           "instruction_mix": mix, "lds_read": lds, "handoff_16x16_workgroups": hand,
+           "dependent_load": chase, "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

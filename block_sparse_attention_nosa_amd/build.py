@@ -25,8 +25,8 @@ def hipcc_cmd(out=LIB):
             "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", out]
 
 
-# The benchmark's read-ceiling probe: a library of its own, not part of libnosa.so.
-PROBE_SOURCES = [os.path.join(CSRC, "probe_ceiling.hip")]
+# The benchmark's machine probes (read ceilings, chip costs): a library of its own, not part of libnosa.so.
+PROBE_SOURCES = [os.path.join(CSRC, "probe_ceiling.hip"), os.path.join(CSRC, "probe_chip.hip")]
 PROBE_LIB = os.path.join(PKG, "libnosa_ceiling.so")
 
 

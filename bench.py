@@ -53,11 +53,14 @@ CALIB_BYTES = 256 << 20   # bytes read (and written) by the calibration copy
 
 
 def sources_sha256():
-    """Hash of the kernel sources (the traffic figures are valid for these)."""
+    """Hash of the NOSA library's sources (the traffic figures are valid for
+    these; the machine probes, a library of their own, are not hashed)."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "block_sparse_attention_nosa_amd", "csrc")
     for f in sorted(os.listdir(d)):
+        if f.startswith("probe_"):
+            continue
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
@@ -307,6 +310,9 @@ def main():
     ap.add_argument("--counter-table", nargs="+", metavar="DIR",
                     help="print a markdown table of the library kernels' counters from "
                          "rocprofv3 --pmc output directories")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-phase timeline of the decode step from the wall-clock stamps of "
+                         "libnosa_timeline.so (the same kernels with stamps)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="table of a rocprofv3 --kernel-trace --stats csv run")
     args = ap.parse_args()
@@ -327,6 +333,8 @@ def main():
 
     if args.chip_probes:
         return chip_probes_main(args)
+    if args.timeline:
+        return timeline_main(synth.config(args.config), args)
     if args.ceiling:
         return ceiling_main(args)
     w = synth.config(args.config)
@@ -1218,6 +1226,109 @@ def ceiling_main(args):
     print(json.dumps(out), flush=True)
 
 
+def timeline_main(w, args):
+    """Where a decode step's time goes: the decode kernels built with
+    wall-clock stamps (libnosa_timeline.so) run graph-captured steps of
+    workload w over 16 layer caches; the stamps of a replay's last step
+    (thread 0 of each workgroup at fixed points of its launch) give, relative
+    to the first scoring workgroup's start, each phase's median over the
+    workgroups and the launch ends.  Medians over 20 decode positions."""
+    import ctypes
+    import numpy as np
+    import torch
+    from block_sparse_attention_nosa_amd import build, nosa, synth
+    if not os.path.exists(build.TIMELINE_LIB):
+        raise SystemExit(f"{build.TIMELINE_LIB} is missing: build it first")
+    nosa.LIB_PATH = build.TIMELINE_LIB
+    L = nosa.lib()
+    L.nosa_timeline_read.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    for f in ("nosa_timeline_read", "nosa_timeline_clear", "nosa_timeline_clock_khz"):
+        getattr(L, f).restype = ctypes.c_int
+    khz = L.nosa_timeline_clock_khz()
+    assert khz > 0
+    nl = 16
+    nsteps = w.extra_tokens + 1
+    layers = build_layers(w, nsteps, nlayers=nl, full_kc=True)
+    B, Hq, d = w.batch, w.num_q_heads, w.head_dim
+    cu_at = [synth.cu_from_lens([x + t for x in w.lens], "cuda") for t in range(nsteps)]
+    maxL = max(w.lens) + nsteps - 1
+    ws = torch.zeros(nosa.nosa_workspace_size(layers[0]["p"], B, 1, maxL), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty(B, Hq, d, device="cuda")
+    lse = torch.empty(B, Hq, device="cuda")
+
+    def step(i, t):
+        ly = layers[i % nl]
+        nosa.nosa_decode_step(ly["p"], ly["kv"], ly["inp"]["q"], cu_at[t], B, maxL, out, lse, ws)
+
+    for i in range(32):
+        step(i, i % nsteps)
+    torch.cuda.synchronize()
+    stamps = np.zeros((3, 8192, 16), dtype=np.uint64)
+    stream = torch.cuda.current_stream()
+    per_rep, step_us = [], []
+    for rep in range(20):
+        t = (rep * 13) % nsteps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(nl):
+                step(i, t)
+        g.replay()
+        torch.cuda.synchronize()
+        assert L.nosa_timeline_clear() == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        step_us.append(e0.elapsed_time(e1) * 1e3 / nl)
+        for k in range(3):
+            assert L.nosa_timeline_read(k, stamps[k].ctypes.data) == 0
+        us = stamps.astype(np.float64) * 1e3 / khz  # ticks -> us
+        sc, tp, mg = us[0], us[1], us[2]
+        sc_done = sc[sc[:, 2] > 0]
+        score_rows = sc_done[sc_done[:, 7] == 0]
+        top_done = tp[tp[:, 5] > 0]
+        top_rows = top_done[top_done[:, 7] == 0]
+        win_rows = top_done[top_done[:, 7] > 0]
+        mg_done = mg[mg[:, 1] > 0]
+        t0 = sc_done[:, 0].min()
+        r = {"scoring_start_median": np.median(score_rows[:, 0]) - t0,
+             "scoring_keys_multiplied": np.median(score_rows[:, 1]) - t0,
+             "scoring_end": sc_done[:, 2].max() - t0,
+             "attention_start": top_done[:, 0].min() - t0,
+             "top_start_median": np.median(top_rows[:, 0]) - t0,
+             "top_bounds_in": np.median(top_rows[:, 12]) - t0,
+             "top_wave0_log_sum_exp": np.median(top_rows[:, 6]) - t0,
+             "top_log_sum_exp": np.median(top_rows[:, 1]) - t0,
+             "top_importance": np.median(top_rows[:, 2]) - t0,
+             "select_range": np.median(top_rows[:, 8]) - t0,
+             "select_first_digit": np.median(top_rows[:, 9]) - t0,
+             "select_last_digit": np.median(top_rows[:, 10]) - t0,
+             "select_counts_shared": np.median(top_rows[:, 11]) - t0,
+             "select_more_levels_share": float(np.mean(top_rows[:, 10] - top_rows[:, 9] > 0.05)),
+             "top_selection": np.median(top_rows[:, 3]) - t0,
+             "top_pages_attended": np.median(top_rows[:, 4]) - t0,
+             "top_partial_stored": np.median(top_rows[:, 5]) - t0,
+             "top_end": top_rows[:, 5].max() - t0,
+             "window_end": win_rows[:, 5].max() - t0 if len(win_rows) else float("nan"),
+             "attention_end": top_done[:, 5].max() - t0,
+             "merge_start": mg_done[:, 0].min() - t0,
+             "merge_end": mg_done[:, 1].max() - t0}
+        r["gap_scoring_to_attention"] = r["attention_start"] - r["scoring_end"]
+        r["gap_attention_to_merge"] = r["merge_start"] - r["attention_end"]
+        per_rep.append(r)
+    med = {k: round(float(np.median([r[k] for r in per_rep])), 2) for k in per_rep[0]}
+    med["select_more_levels_share"] = round(float(np.mean([r["select_more_levels_share"] for r in per_rep])), 3)
+    res = {"metric": "decode step timeline", "value": med["merge_end"], "unit": "us from the first scoring workgroup's start",
+           "n_gpus": 1, "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": w.name, "batch": w.batch, "context": max(w.lens), "positions": 20,
+                      "layer_caches": nl},
+           "phases_us": med, "instrumented_us_per_step": round(float(np.median(step_us)), 2),
+           "wall_clock_khz": khz}
+    print(json.dumps(res), flush=True)
+
+
 def chip_probes_main(args):
     """Costs of this chip that the design rests on (the machine probes of
     libnosa_ceiling.so; medians of repeated launches): how far VALU work and
@@ -1235,8 +1346,10 @@ def chip_probes_main(args):
     lib.nosa_probe_mix.argtypes = [i32, i32, i32, vp, vp]
     lib.nosa_probe_lds_read.argtypes = [i32, i32, vp, vp]
     lib.nosa_probe_handoff.argtypes = [i32, i32, vp, vp, vp, vp]
-    lib.nosa_probe_chase.argtypes = [vp, i32, i32, vp, vp]
-    for f in ("nosa_probe_mix", "nosa_probe_lds_read", "nosa_probe_handoff", "nosa_probe_chase"):
+    lib.nosa_probe_chase.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.nosa_probe_wall_clock_khz.argtypes = []
+    for f in ("nosa_probe_mix", "nosa_probe_lds_read", "nosa_probe_handoff", "nosa_probe_chase",
+              "nosa_probe_wall_clock_khz"):
         getattr(lib, f).restype = ctypes.c_int
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
@@ -1287,28 +1400,46 @@ def chip_probes_main(args):
                                                   out.data_ptr(), sh), reps=11)
         ok = bool(torch.equal(out.view(groups, 1024).cpu(), want[:, None].expand(groups, 1024)))
         hand[name] = {"us": round(us, 2), "sums_correct": ok}
-    # dependent loads through a random cycle over 1 GiB (beyond the 256 MB
-    # Infinity Cache, which the writes of the cycle would otherwise fill)
-    n = 256 << 20
-    gen = torch.Generator(device="cuda").manual_seed(11)
-    perm = torch.randperm(n, generator=gen, device="cuda")
-    nxt = torch.empty(n, dtype=torch.int32, device="cuda")
-    nxt[perm] = torch.roll(perm, -1).to(torch.int32)
-    steps = 20000
-    chase = {"buffer_mb": n * 4 >> 20}
-    ends = []
-    for vec, name in ((1, "vector_load_ns"), (0, "scalar_load_ns")):
-        csink = torch.zeros(64, dtype=torch.int32, device="cuda")
-        us = timed(lambda: lib.nosa_probe_chase(nxt.data_ptr(), steps, vec, csink.data_ptr(), sh), reps=3)
-        chase[name] = round(us * 1e3 / steps, 1)
-        csink.zero_()
-        assert lib.nosa_probe_chase(nxt.data_ptr(), steps, vec, csink.data_ptr(), sh) == 0
-        torch.cuda.synchronize()
-        ends.append(int(csink[0].item()))
-    i = 0
-    for _ in range(steps):  # the chain's end, followed on the host one load at a time
-        i = int(nxt[i].item())
-    chase["ends_match_host_walk"] = ends == [i, i]
+    # dependent loads: a random cycle through an array, walked by one wave
+    # and timed inside the launch.  Lines in the XCD's L2: a 1 MB array, the
+    # timed hops walked once before (all its lines fit); in the Infinity
+    # Cache: 64 MB, 100000 hops walked once before (12.8 MB of lines, beyond
+    # the 4 MB L2, within the 256 MB Infinity Cache); in HBM only: 1 GiB, a
+    # part of the cycle that no walk has touched.  The chain's end is
+    # checked against the cycle: next[perm[j]] = perm[j + 1].
+    khz = lib.nosa_probe_wall_clock_khz()
+    assert khz > 0
+    zero = torch.zeros(64, dtype=torch.int32, device="cuda")
+    cout = torch.zeros(2, dtype=torch.int64, device="cuda")
+    chase = {"wall_clock_khz": khz}
+    ends_ok = True
+    for level, n, steps, warm in (("l2", 1 << 18, 20000, True), ("infinity_cache", 1 << 24, 100000, True),
+                                  ("hbm", 1 << 28, 20000, False)):
+        gen = torch.Generator(device="cuda").manual_seed(11)
+        perm = torch.randperm(n, generator=gen, device="cuda").to(torch.int32)
+        nxt = torch.empty(n, dtype=torch.int32, device="cuda")
+        nxt[perm.long()] = torch.roll(perm, -1)
+        permh = perm.cpu()
+        if not warm:  # evict the writes and reads above from the Infinity Cache
+            flush = torch.ones(1 << 27, dtype=torch.int32, device="cuda")
+            assert int(flush.sum()) == 1 << 27
+            del flush
+        res_l = {"array_mb": n * 4 / 2**20, "hops": steps}
+        for vec, name in ((1, "vector_load_ns"), (0, "scalar_load_ns")):
+            ns = []
+            for rep in range(3):
+                j = rep * 2 * steps + (0 if vec else 6 * steps)  # a fresh part of the cycle (hbm)
+                start = int(permh[j])
+                assert lib.nosa_probe_chase(nxt.data_ptr(), start, steps if warm else 0, start, steps, vec,
+                                            zero.data_ptr(), cout.data_ptr(), sh) == 0
+                torch.cuda.synchronize()
+                end, ticks = (int(v) for v in cout.cpu())
+                ends_ok &= end == int(permh[(j + steps) % n])
+                ns.append(ticks * 1e6 / khz / steps)
+            res_l[name] = round(float(np.median(ns)), 1)
+        chase[level] = res_l
+        del perm, nxt, permh
+    chase["ends_match_cycle"] = ends_ok
     res = {"metric": "chip probes", "value": mix["mfma_and_dependent_valu"], "unit": mix["unit"],
            "n_gpus": 1, "higher_is_better": False, "dtype": "bf16/fp32", "data": "synthetic",
            "config": {"workload": "chip-probes", "workgroups": wgs},

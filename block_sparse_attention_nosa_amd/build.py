@@ -30,22 +30,39 @@ PROBE_SOURCES = [os.path.join(CSRC, "probe_ceiling.hip"), os.path.join(CSRC, "pr
 PROBE_LIB = os.path.join(PKG, "libnosa_ceiling.so")
 
 
-def _compile(cmd, tmp, lib, what, verbose):
-    r = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed building {what}")
-    if verbose:
-        sys.stderr.write(r.stderr)
-    os.replace(tmp, lib)
+# The benchmark's timeline mode: the same sources with wall-clock stamps in the
+# decode kernels (NOSA_TIMELINE), a library of its own.
+TIMELINE_LIB = os.path.join(PKG, "libnosa_timeline.so")
+
+
+def _compile(cmds, verbose):
+    """Runs the (cmd, tmp, lib, what) compilations in parallel; each library
+    is moved into place when its compilation succeeded."""
+    procs = [(subprocess.Popen(cmd, cwd=ROOT, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True),
+              tmp, lib, what) for cmd, tmp, lib, what in cmds]
+    failed = []
+    for p, tmp, lib, what in procs:
+        out, err = p.communicate()
+        if p.returncode != 0:
+            sys.stderr.write(out + err)
+            failed.append(what)
+            continue
+        if verbose:
+            sys.stderr.write(err)
+        os.replace(tmp, lib)
+    if failed:
+        raise RuntimeError("hipcc failed building " + ", ".join(failed))
 
 
 def build(verbose: bool = False) -> str:
-    _compile(hipcc_cmd(LIB + ".tmp"), LIB + ".tmp", LIB, "libnosa.so", verbose)
     probe = hipcc_cmd(PROBE_LIB + ".tmp")
     probe = [a for a in probe if a not in SOURCES]
     probe[probe.index("-o"):probe.index("-o")] = PROBE_SOURCES
-    _compile(probe, PROBE_LIB + ".tmp", PROBE_LIB, "libnosa_ceiling.so", verbose)
+    timeline = hipcc_cmd(TIMELINE_LIB + ".tmp")
+    timeline.insert(timeline.index("-I"), "-DNOSA_TIMELINE")
+    _compile([(hipcc_cmd(LIB + ".tmp"), LIB + ".tmp", LIB, "libnosa.so"),
+              (probe, PROBE_LIB + ".tmp", PROBE_LIB, "libnosa_ceiling.so"),
+              (timeline, TIMELINE_LIB + ".tmp", TIMELINE_LIB, "libnosa_timeline.so")], verbose)
     return LIB
 
 

@@ -389,12 +389,20 @@ __device__ __forceinline__ float wave_sum_f(float x)
 // keys usually happens at the first level.  The taken candidates are then
 // compacted in ascending order from per-wave ballot counts (one barrier, two
 // when tied keys straddle the cut).
-template <int NW, bool KEYS_GIVEN>
+// Mark, called with 0 .. 3 as the selector passes its stages (the range
+// known, the first digit found, the last digit found, the compaction's
+// counts shared): a hook for instrumented builds, a no-op by default.
+struct NoMark {
+    __device__ void operator()(int) const {}
+};
+
+template <int NW, bool KEYS_GIVEN, class Mark = NoMark>
 __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds], const float* sI, int nb,
                                                  int wblocks, int topk, SelectLds& sh,
                                                  int32_t* __restrict__ sel_out, int32_t* __restrict__ cnt_out,
                                                  int max_sel, int2* list, int list_lo, int list_n,
-                                                 const int32_t* pages, bool range_known = false)
+                                                 const int32_t* pages, bool range_known = false,
+                                                 Mark mark = Mark())
 {
     static_assert(NW >= 4 && NW <= 8, "per-round counts are sized for 4 to 8 waves");
     constexpr int NT = NW * 64;
@@ -459,6 +467,7 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
             kmax = max(kmax, sh.mm[1][w]);
         }
         const uint32_t range = kmax - kmin;
+        mark(0);
         n_eq = ncand;
         need = kk;
         if (range != 0u) {
@@ -519,13 +528,16 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
                 need = kk - above;
                 return n_eq == need || sh_lo == 0;  // taken exactly, or u fully resolved
             };
-            if (!level_pass(sh.hist0, std::integral_constant<int, 16>{})) {
+            const bool done = level_pass(sh.hist0, std::integral_constant<int, 16>{});
+            mark(1);
+            if (!done) {
 #pragma unroll 1
                 for (int level = 0; level < 3; ++level) {
                     sh_lo = sh_lo > 8 ? sh_lo - 8 : 0;
                     if (level_pass(sh.hist[level], std::integral_constant<int, 4>{})) break;
                 }
             }
+            mark(2);
         }
     }
     // Ascending compaction: candidate i*NT + tid in round i; per (round,
@@ -575,6 +587,7 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
         });
     }
     __syncthreads();
+    mark(3);
     int sel_base = 0;
     for_rounds([&](int i, uint32_t) {
         const bool take = (takebits >> i) & 1u;

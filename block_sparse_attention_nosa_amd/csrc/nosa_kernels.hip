@@ -36,6 +36,36 @@
 
 namespace nosa {
 
+// Timeline build: compiled with NOSA_TIMELINE, a library of its own for the
+// benchmark's timeline mode (the NOSA library has none of this).  Thread 0
+// of a workgroup stamps the constant-rate wall clock at points of its
+// launch (0: scoring, 1: selection + attention, 2: merge) into
+// tl_stamps[launch][workgroup][point]; point 7 holds the workgroup's role.
+// The scheduling barriers keep each stamp between the instructions around
+// it.
+#ifdef NOSA_TIMELINE
+constexpr int kTlGroups = 8192;
+__device__ unsigned long long tl_stamps[3][kTlGroups][16];
+#define NOSA_TL(launch, point)                                                           \
+    do {                                                                                 \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        if (threadIdx.x == 0 && blockIdx.x < kTlGroups)                                  \
+            tl_stamps[launch][blockIdx.x][point] = wall_clock64();                       \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+    } while (0)
+#define NOSA_TL_ROLE(launch, role)                                                       \
+    do {                                                                                 \
+        if (threadIdx.x == 0 && blockIdx.x < kTlGroups) tl_stamps[launch][blockIdx.x][7] = (role); \
+    } while (0)
+#else
+#define NOSA_TL(launch, point) \
+    do {                       \
+    } while (0)
+#define NOSA_TL_ROLE(launch, role) \
+    do {                           \
+    } while (0)
+#endif
+
 // ------------------------------------------------------- pooled keys ---
 
 // Round a double to bf16, nearest-even, in one step from its bit pattern.
@@ -583,7 +613,9 @@ __global__ __launch_bounds__(kScoreWaves * 64, CPW) void score_kernel(ScoreArgs 
     // workgroups use in the next launch: slot b is scoring workgroup
     // (b % 8) * spx + b / 8 (spx = ceil(nscore / 8); past nscore: idle).
     const int spx = (nscore + 7) >> 3;
+    NOSA_TL(0, 0);
     if ((int)blockIdx.x >= 8 * spx) {  // window workgroup
+        NOSA_TL_ROLE(0, 1);
         const int w = (int)blockIdx.x - 8 * spx;
         const int pair = w / a.wgroups;
         if constexpr (T == 8) {
@@ -592,16 +624,19 @@ __global__ __launch_bounds__(kScoreWaves * 64, CPW) void score_kernel(ScoreArgs 
                              a.Hq, a.Hkv, a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv,
                              w % a.wgroups, a.nsplit, a.split0, a.po, a.pml,
                              *reinterpret_cast<CombineLds*>(smem));
+                NOSA_TL(0, 2);
                 return;
             }
         }
         window_slot(a.q, a.k_pool, a.v_pool, a.table, a.ring, a.cu_k, a.max_blocks, a.Lmax, a.Hq,
                     a.Hkv, a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv, w % a.wgroups,
                     a.nsplit, a.split0, a.po, a.pml, *reinterpret_cast<SplitPageLds*>(smem));
+        NOSA_TL(0, 2);
         return;
     }
     const int sid = ((int)blockIdx.x & 7) * spx + ((int)blockIdx.x >> 3);
     if (sid >= nscore) return;  // (whole workgroup)
+    NOSA_TL_ROLE(0, 0);
     const int cpp = (nchunks + CPW - 1) / CPW;  // scoring workgroups per pair
     const int pair = sid / cpp, c0 = (sid % cpp) * CPW;
     const int s = pair / Hkv, g = pair % Hkv;
@@ -698,6 +733,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, CPW) void score_kernel(ScoreArgs 
             *reinterpret_cast<float4*>(zl + r * ZS + (wave * T + t) * 16 + kq * 4) =
                 make_float4(zv[t][0], zv[t][1], zv[t][2], zv[t][3]);
     }
+    if (j == 0) NOSA_TL(0, 1);  // the first chunk's keys in and multiplied
     const bool next = j + 1 < CPW && c + 1 < nchunks && k0 + CK < nc;  // (whole workgroup)
     if (next) table_entries(c + 1);  // the next chunk's, now that kv is free
     if (m_l != -INFINITY) {
@@ -751,6 +787,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, CPW) void score_kernel(ScoreArgs 
     }
     if (j + 1 < CPW) __syncthreads();  // zl, wm and wsum are rewritten by the next chunk
     }
+    NOSA_TL(0, 2);
 }
 
 
@@ -928,6 +965,8 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     const bool window = pos >= disp.x;
     const int lid = window ? xcd * disp.y + (pos - disp.x) : xcd * disp.x + pos;
     if (lid >= (window ? disp.w : disp.z)) return;  // whole workgroup
+    NOSA_TL(1, 0);
+    NOSA_TL_ROLE(1, window ? 1 : 0);
     // the chunk partials' addresses, in the argument batch that follows (a
     // load of their own later would also wait for the sequence bounds)
     GlobalF2 cml = (GlobalF2)a.cml;
@@ -939,6 +978,7 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
         window_slot(a.q, a.wk, a.wv, a.table, a.ring, a.cu_k, a.max_blocks, a.Lmax, a.Hq, a.Hkv,
                     a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv, lid % a.wgroups,
                     a.nsplit, a.groups, a.po, a.pml, sh.page);
+        NOSA_TL(1, 5);
         return;
     }
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -1022,6 +1062,7 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     nb = (L + BS - 1) / BS;
     nc = dev_num_keys(L);
     const int nvalid = (nc + CK - 1) / CK;  // chunks holding keys of this pair, <= 64
+    NOSA_TL(1, 12);  // the sequence bounds in
     select_lds_clear<NT>(sh.sel);
     // per-head log2-sum-exp2 over the chunks, then each chunk's weight
 #pragma unroll
@@ -1043,10 +1084,12 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
         sh.f[lane][h] = f;
         sh.fs[lane][h] = ok ? f * sv[u] : 0.f;
     }
+    NOSA_TL(1, 6);  // this wave's log-sum-exp (its loads in)
 #pragma unroll
     for (int i = 0; i < KRB; ++i)
         if (i * NT + tid < a.max_nb) spg[i * NT + tid] = tv[i];
     __syncthreads();
+    NOSA_TL(1, 1);  // log-sum-exp and chunk weights
     uint32_t keys[kSelKeyRounds];
 #pragma unroll
     for (int i = 0; i < kSelKeyRounds; ++i) keys[i] = 0u;
@@ -1080,13 +1123,15 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     const bool in_regs = ncand <= KRB * NT;  // every candidate's key is in keys[]
     if (in_regs) select_wave_range<NT, kSelKeyRounds>(keys, ncand, sh.sel);
     __syncthreads();  // sI, the rest of the row, the key ranges
+    NOSA_TL(1, 2);  // block importance
     const int lo = k * a.rounds * kStep2Waves;
     select_blocks_wg<kStep2Waves, true>(keys, sI, nb, a.wblocks, a.topk, sh.sel,
                                         a.sel_out && k == 0 ? a.sel_out + (size_t)pair * a.max_sel : nullptr,
                                         a.cnt_out && k == 0 ? a.cnt_out + pair : nullptr, a.max_sel,
                                         sh.list, OFF ? 0 : lo, OFF ? kMaxCacheSlots : a.rounds * kStep2Waves,
-                                        spg, in_regs);
+                                        spg, in_regs, [](int m) { NOSA_TL(1, 8 + m); });
     __syncthreads();  // the list
+    NOSA_TL(1, 3);  // selection
     rounds = a.rounds;
     if (OFF) {
         // picks 0 .. npk - 1 in sh.list, ascending block ids
@@ -1184,7 +1229,9 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
         }
         attend_page(kb, vb, L - e.x * BS, qb, a.scale_log2, r, kq, A);
     }
+    NOSA_TL(1, 4);  // pages attended
     store_wg_partial(sh.comb, A, a.G, head_row0, a.nsplit, window ? a.groups + k : k, a.po, a.pml);
+    NOSA_TL(1, 5);
 }
 
 // ------------------------------------------------ attention (alone) ---
@@ -1240,6 +1287,7 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ po
     const int rpx = (int)gridDim.x >> 3;
     const size_t row = (size_t)(((int)blockIdx.x & 7) * rpx + ((int)blockIdx.x >> 3));
     if (row >= rows) return;  // (whole workgroup)
+    NOSA_TL(2, 0);
     const int c = threadIdx.x, lane = c & 63;
     const float2* ml = pml + row * nsplit;
     const float* op = po + row * nsplit * D + c;
@@ -1276,6 +1324,7 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ po
     const bool empty = !(L > 0.f);
     out[row * D + c] = empty ? 0.f : acc / L;
     if (lse && c == 0) lse[row] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
+    NOSA_TL(2, 1);
 }
 
 static hipError_t launch_merge(const Plan& pl, const Workspace& w, int nsplit, float* out, float* lse,
@@ -1717,3 +1766,38 @@ hipError_t launch_select(const Plan& pl, const int32_t* cu_k, const int32_t* cu_
 }
 
 }  // namespace nosa
+
+#ifdef NOSA_TIMELINE
+// Readout of the timeline build's stamps (not part of the NOSA C ABI).
+extern "C" {
+
+// Copies launch `launch`'s stamps ([8192][16] unsigned 64-bit) to host memory.
+int nosa_timeline_read(int launch, unsigned long long* host)
+{
+    if (launch < 0 || launch > 2 || !host) return (int)hipErrorInvalidValue;
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(nosa::tl_stamps), sizeof(nosa::tl_stamps[0]),
+                                    (size_t)launch * sizeof(nosa::tl_stamps[0]), hipMemcpyDeviceToHost);
+}
+
+// Zeroes every stamp (synchronous).
+int nosa_timeline_clear(void)
+{
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(nosa::tl_stamps));
+    if (e != hipSuccess) return (int)e;
+    e = hipMemset(p, 0, sizeof(nosa::tl_stamps));
+    if (e != hipSuccess) return (int)e;
+    return (int)hipDeviceSynchronize();
+}
+
+// The wall clock's rate in kHz, or 0 on an error.
+int nosa_timeline_clock_khz(void)
+{
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+    return khz;
+}
+
+}  // extern "C"
+#endif

@@ -11,8 +11,9 @@
 //   * nosa_probe_handoff: partials of 16 workgroups handed to the last of
 //     them inside one launch (device-scope release/acquire, or coherent
 //     stores and loads with no fence) against a second launch;
-//   * nosa_probe_chase: the latency of a dependent load from device memory
-//     (vector and scalar loads).
+//   * nosa_probe_chase: the latency of a dependent load (vector and scalar
+//     loads) with its lines in the XCD's L2, in the Infinity Cache, or in
+//     HBM only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -166,22 +167,46 @@ __global__ __launch_bounds__(256) void handoff_sum_kernel(const float* __restric
     for (int e = 0; e < 4; ++e) out[(size_t)g * 1024 + 4 * t + e] = s[e];
 }
 
-// A chain of `steps` dependent loads through next[]: with VECTOR, every lane
-// of one wave follows it from its own start read from sink (all start at 0:
-// vector loads, the lanes' addresses coinciding); else one lane follows it
-// from 0 (a uniform index: the compiler issues scalar loads).
+// A chain of dependent loads through next[] (a cycle through the array),
+// timed inside the launch with the constant-rate wall clock: `warm` hops from
+// `warm_start` first (untimed: they bring the timed hops' lines into the
+// caches when warm_start == start), then `steps` hops from `start`, timed.
+// With VECTOR, every lane of one wave follows the chain (the index comes
+// from memory, so the loads are vector loads, the lanes' addresses
+// coinciding); else a uniform index (scalar loads).  out[0] = the chain's end,
+// out[1] = the timed hops' wall-clock ticks.
 template <bool VECTOR>
-__global__ void chase_kernel(const int* __restrict__ next, int steps, int* __restrict__ sink)
+__global__ void chase_kernel(const int* __restrict__ next, int warm_start, int warm, int start,
+                             int steps, const int* __restrict__ zero, long long* __restrict__ out)
 {
     if (VECTOR) {
-        int i = sink[threadIdx.x];
-        for (int s = 0; s < steps; ++s) i = __builtin_nontemporal_load(next + i);
-        sink[threadIdx.x] = i;
+        int i = warm_start + zero[threadIdx.x];
+        for (int s = 0; s < warm; ++s) i = next[i];
+        asm volatile("" ::"v"(i));
+        i = start + zero[threadIdx.x];
+        asm volatile("" : "+v"(i));
+        const long long t0 = wall_clock64();
+        for (int s = 0; s < steps; ++s) i = next[i];
+        asm volatile("" ::"v"(i));
+        const long long t1 = wall_clock64();
+        if (threadIdx.x == 0) {
+            out[0] = i;
+            out[1] = t1 - t0;
+        }
     } else {
-        if (threadIdx.x != 0) return;
-        int i = 0;
-        for (int s = 0; s < steps; ++s) i = __builtin_nontemporal_load(next + i);
-        sink[0] = i;
+        int i = warm_start;
+        for (int s = 0; s < warm; ++s) i = next[i];
+        asm volatile("" ::"s"(i));
+        i = start;
+        asm volatile("" : "+s"(i));
+        const long long t0 = wall_clock64();
+        for (int s = 0; s < steps; ++s) i = next[i];
+        asm volatile("" ::"s"(i));
+        const long long t1 = wall_clock64();
+        if (threadIdx.x == 0) {
+            out[0] = i;
+            out[1] = t1 - t0;
+        }
     }
 }
 
@@ -235,16 +260,30 @@ int nosa_probe_handoff(int mode, int groups, float* part, int* counter, float* o
     return (int)hipGetLastError();
 }
 
-// Dependent-load probe: `steps` hops through next[] (device, a cycle through
-// the array) by vector loads (vector != 0; sink: 64 ints, zero, the lanes'
-// starts and ends) or scalar loads (sink[0] receives the end).
-int nosa_probe_chase(const int* next, int steps, int vector, int* sink, void* stream)
+// Dependent-load probe (chase_kernel above): one wave; zero: 64 device
+// ints, all zero; out: 2 device long longs.  Returns the hipError_t of the
+// launch.
+int nosa_probe_chase(const int* next, int warm_start, int warm, int start, int steps, int vector,
+                     const int* zero, long long* out, void* stream)
 {
-    if (!next || !sink || steps < 0) return (int)hipErrorInvalidValue;
+    if (!next || !zero || !out || steps < 0 || warm < 0) return (int)hipErrorInvalidValue;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (vector) hipLaunchKernelGGL(chase_kernel<true>, dim3(1), dim3(64), 0, s, next, steps, sink);
-    else hipLaunchKernelGGL(chase_kernel<false>, dim3(1), dim3(64), 0, s, next, steps, sink);
+    if (vector)
+        hipLaunchKernelGGL(chase_kernel<true>, dim3(1), dim3(64), 0, s, next, warm_start, warm, start,
+                           steps, zero, out);
+    else
+        hipLaunchKernelGGL(chase_kernel<false>, dim3(1), dim3(64), 0, s, next, warm_start, warm, start,
+                           steps, zero, out);
     return (int)hipGetLastError();
+}
+
+// The wall clock's rate in kHz (chase_kernel's ticks), or 0 on an error.
+int nosa_probe_wall_clock_khz(void)
+{
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+    return khz;
 }
 
 }  // extern "C"

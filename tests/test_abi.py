@@ -32,6 +32,20 @@ def test_exports_every_declared_function(L):
         assert hasattr(L, n), n
 
 
+def test_timeline_build_is_a_library_of_its_own(L):
+    """The stamped build of the decode kernels exports the ABI and its
+    readout; the library itself has no readout."""
+    from block_sparse_attention_nosa_amd import build
+    if not os.path.exists(build.TIMELINE_LIB):
+        build.build()
+    T = ctypes.CDLL(build.TIMELINE_LIB)
+    for n in ("nosa_timeline_read", "nosa_timeline_clear", "nosa_timeline_clock_khz"):
+        assert hasattr(T, n), n
+        assert not hasattr(L, n), n
+    for n in nosa.header_functions():
+        assert hasattr(T, n), n
+
+
 def test_version_and_status_strings(L):
     assert nosa.abi_version() == 4
     for s in range(6):

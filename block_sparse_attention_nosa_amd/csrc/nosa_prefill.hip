@@ -118,6 +118,13 @@ typedef uint4 PfChunkBuf[kChunkPages][kPfPageStride];
 
 // max(a, b, c) without canonicalising the operands (NaN propagates, which
 // the products never are); gfx950 issues it as one v_maximum3_f32.
+// Waits until every global-to-LDS copy this wave has issued has written the
+// LDS.  Such a copy is counted by the vector-memory counter, and a barrier
+// does not wait for it; every wave therefore waits for its own copies before
+// the barrier after which the other waves read them (the compiler waits only
+// where the same wave reads what it copied).
+__device__ __forceinline__ void wait_lds_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ float vmax3(float a, float b, float c)
 {
     return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
@@ -328,6 +335,7 @@ __global__ __launch_bounds__(256, 2) void pf_score_kernel(PfArgs a)
         };
         bool have_ref = false;  // wave-uniform
         auto chunk = [&](int c, const uint4* __restrict__ cur, uint4* __restrict__ nxt) {
+            wait_lds_copies();
             __syncthreads();  // chunk c in LDS; every wave done with chunk c - 1
             if (c + 1 < nchunks) copy_chunk(c + 1, nxt);
             const int c0 = key_lo + c * kChunk, c1 = min(c0 + kChunk, key_hi);
@@ -472,6 +480,7 @@ __global__ __launch_bounds__(256, 2) void pf_score_kernel(PfArgs a)
             }
         };
         auto chunk = [&](int c, const uint4* __restrict__ cur, uint4* __restrict__ nxt) {
+            wait_lds_copies();
             __syncthreads();  // chunk c in LDS; every wave done with chunk c - 1
             if (c + 1 < nchunks) copy_chunk(c + 1, nxt);
             if (c > 0) store_chunk(c - 1);
@@ -752,6 +761,7 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
     if (i1 > i0) copy_page(i0, k_even, v_even);
     auto step = [&](int idx, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                     uint16_t* __restrict__ kn, uint16_t* __restrict__ vn) {
+        wait_lds_copies();
         __syncthreads();  // page idx in LDS; every wave done with page idx - 1
         if (idx + 1 < i1) copy_page(idx + 1, kn, vn);
         const int b = list[idx].x;

@@ -1315,11 +1315,45 @@ def timeline_main(w, args):
              "attention_end": top_done[:, 5].max() - t0,
              "merge_start": mg_done[:, 0].min() - t0,
              "merge_end": mg_done[:, 1].max() - t0}
+        # placement: the XCD of each workgroup against blockIdx % 8, and the
+        # top workgroups' ends per XCD and per count of them sharing a CU
+        idx = np.nonzero((stamps[1][:, 5] > 0) & (stamps[1][:, 7] == 0))[0]
+        xcc = stamps[1][idx, 13].astype(np.int64) & 15
+        hw = stamps[1][idx, 14].astype(np.int64)
+        cu_key = xcc * 256 + ((hw >> 8) & 0xff)  # XCD, engine, array, compute unit
+        _, inv, cnt = np.unique(cu_key, return_inverse=True, return_counts=True)
+        ends = tp[idx, 5] - t0
+        r["top_on_blockidx_xcd"] = float(np.mean(xcc == (idx % 8)))
+        # XCD of blockIdx 0 .. 7 in each launch (the same blockIdx % 8 runs on
+        # one XCD within a launch; the first one's XCD may differ per launch)
+        for k, name in ((0, "scoring"), (1, "attention"), (2, "merge")):
+            done = stamps[k][:, 2 if k == 0 else (5 if k == 1 else 1)] > 0
+            ids = [int(stamps[k][b, 13]) & 15 if done[b] else -1 for b in range(8)]
+            r[f"xcd_of_blockidx0_{name}"] = ids[0]
+            r[f"xcd_rotation_consistent_{name}"] = float(all(
+                i < 0 or i == (ids[0] + b) % 8 for b, i in enumerate(ids)))
+        offs = [r[f"xcd_of_blockidx0_{n}"] for n in ("scoring", "attention", "merge")]
+        r["xcd_offsets_equal_share"] = float(len(set(offs)) == 1)
+        print(json.dumps({"rep": rep, "xcd_of_blockidx0": offs}), file=sys.stderr, flush=True)
+        if rep == 0:
+            xmap = {int(b): sorted({int(v) for v in xcc[idx % 8 == b]}) for b in range(8)}
+            raw = [(int(i), int(stamps[1][i, 13]), int(stamps[1][i, 14])) for i in idx[:16]]
+            print(json.dumps({"blockidx_mod8_to_xcc": xmap, "raw_id_hw": raw}), file=sys.stderr,
+                  flush=True)
+        for x in range(8):
+            sel = xcc == x
+            r[f"top_end_xcd{x}"] = float(ends[sel].max()) if sel.any() else float("nan")
+        for n in (1, 2, 3):
+            sel = cnt[inv] == n
+            r[f"top_end_median_cu_with_{n}"] = float(np.median(ends[sel])) if sel.any() else float("nan")
+            r[f"top_share_cu_with_{n}"] = float(np.mean(sel))
         r["gap_scoring_to_attention"] = r["attention_start"] - r["scoring_end"]
         r["gap_attention_to_merge"] = r["merge_start"] - r["attention_end"]
         per_rep.append(r)
     med = {k: round(float(np.median([r[k] for r in per_rep])), 2) for k in per_rep[0]}
-    med["select_more_levels_share"] = round(float(np.mean([r["select_more_levels_share"] for r in per_rep])), 3)
+    for k in list(med):
+        if "share" in k or k.startswith("top_on_") or k.startswith("xcd_rotation"):
+            med[k] = round(float(np.mean([r[k] for r in per_rep])), 3)
     res = {"metric": "decode step timeline", "value": med["merge_end"], "unit": "us from the first scoring workgroup's start",
            "n_gpus": 1, "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": w.name, "batch": w.batch, "context": max(w.lens), "positions": 20,

@@ -53,9 +53,15 @@ __device__ unsigned long long tl_stamps[3][kTlGroups][16];
             tl_stamps[launch][blockIdx.x][point] = wall_clock64();                       \
         __builtin_amdgcn_sched_barrier(0);                                               \
     } while (0)
+// point 7: the role; 13: the XCD (hardware register XCC_ID); 14: HW_ID
+// (compute unit, shader array and engine of the wave)
 #define NOSA_TL_ROLE(launch, role)                                                       \
     do {                                                                                 \
-        if (threadIdx.x == 0 && blockIdx.x < kTlGroups) tl_stamps[launch][blockIdx.x][7] = (role); \
+        if (threadIdx.x == 0 && blockIdx.x < kTlGroups) {                                \
+            tl_stamps[launch][blockIdx.x][7] = (role);                                   \
+            tl_stamps[launch][blockIdx.x][13] = (unsigned)__builtin_amdgcn_s_getreg(30740); \
+            tl_stamps[launch][blockIdx.x][14] = (unsigned)__builtin_amdgcn_s_getreg(63492); \
+        }                                                                                \
     } while (0)
 #else
 #define NOSA_TL(launch, point) \
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void kc_build_kernel(
         {
             const uint16_t* pg = k_pool + ((size_t)p_cur * Hkv + g) * BS * D + lane * 8;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) v[r] = ldg16(pg + r * 512);
+            for (int r = 0; r < 16; ++r) v[r] = ldg16_stream(pg + r * 512);
         }
         for (int q = 0; q < npg; ++q) {
             // The tile is the wave's own: LDS operations of a wave execute in
@@ -211,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void kc_build_kernel(
             if (q + 1 < npg) {  // the next page into the freed buffer
                 const uint16_t* pg = k_pool + ((size_t)p_n1 * Hkv + g) * BS * D + lane * 8;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) v[r] = ldg16(pg + r * 512);
+                for (int r = 0; r < 16; ++r) v[r] = ldg16_stream(pg + r * 512);
             } else if (spill && u == 0) {  // the next page's first group, chunk c8
                 const uint16_t* pg = k_pool + ((size_t)p_n1 * Hkv + g) * BS * D;
 #pragma unroll
@@ -360,11 +366,11 @@ __device__ void attend_page_split4(const uint16_t* __restrict__ kb, const uint16
     const int lane8 = lane * 8;
     uint4 ka[4], va[2][2];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) ka[st] = ldg16(kb + (wave * 4 + st) * 512 + lane8);
+    for (int st = 0; st < 4; ++st) ka[st] = ldg16_stream(kb + (wave * 4 + st) * 512 + lane8);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) va[u][j] = ldg16(vb + (u * 8 + 2 * wave + j) * 512 + lane8);
+        for (int j = 0; j < 2; ++j) va[u][j] = ldg16_stream(vb + (u * 8 + 2 * wave + j) * 512 + lane8);
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1288,6 +1294,7 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ po
     const size_t row = (size_t)(((int)blockIdx.x & 7) * rpx + ((int)blockIdx.x >> 3));
     if (row >= rows) return;  // (whole workgroup)
     NOSA_TL(2, 0);
+    NOSA_TL_ROLE(2, 0);
     const int c = threadIdx.x, lane = c & 63;
     const float2* ml = pml + row * nsplit;
     const float* op = po + row * nsplit * D + c;

@@ -551,6 +551,7 @@ struct ScoreArgs {
     int max_blocks, num_pages, Lmax, Hq, Hkv, G, gp;
     float scale_log2;
     int append;  // pool the key completed by the current token
+    int stream_kc;  // stream the pooled-key loads (non-temporal)
     int nchunks, nbk;
     float2* cml;
     float* spill;
@@ -576,17 +577,31 @@ inline size_t score_lds_bytes(int T, int G, bool per_wave)
 
 // This lane's pooled keys of T tiles of 16 (tile t: page pgj[t], keys
 // kwj + 16 t + r), as MFMA operands; page ids clamped into the pool.
+// Streamed (non-temporal) when a step's pooled keys are too many to stay
+// cached until the next step (stream: wave-uniform).
 template <int T>
 __device__ __forceinline__ void load_chunk_keys(uint4 (&kv)[T][4], const int (&pgj)[T], int kwj,
                                                 const uint16_t* kc_pool, int num_pages, int Hkv,
-                                                int g, int r, int kq)
+                                                int g, int r, int kq, bool stream)
 {
+    const uint16_t* kp[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const int p = min(max(pgj[t], 0), num_pages - 1);
-        const uint16_t* kp = kc_pool + ((size_t)p * Hkv + g) * SL * D;
+        kp[t] = kc_pool + ((size_t)p * Hkv + g) * SL * D;
+    }
+    if (stream) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) kv[t][st] = ldg16(kp + kc_chunk((kwj + t * 16 + r) % SL, st * 4 + kq));
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                kv[t][st] = ldg16_stream(kp[t] + kc_chunk((kwj + t * 16 + r) % SL, st * 4 + kq));
+    } else {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                kv[t][st] = ldg16(kp[t] + kc_chunk((kwj + t * 16 + r) % SL, st * 4 + kq));
     }
 }
 
@@ -613,7 +628,8 @@ __global__ __launch_bounds__(kScoreWaves * 64, CPW) void score_kernel(ScoreArgs 
     // registers through an empty asm: read in the first batch of argument
     // loads, not in later batches that each wait for the one before.
     int nscore = a.nscore, nchunks = a.nchunks, Hkv = a.Hkv, max_blocks = a.max_blocks;
-    asm("" : "+s"(nscore), "+s"(nchunks), "+s"(Hkv), "+s"(max_blocks));
+    int stream_kc = a.stream_kc;
+    asm("" : "+s"(nscore), "+s"(nchunks), "+s"(Hkv), "+s"(max_blocks), "+s"(stream_kc));
     // Scoring workgroups are dealt to the eight XCDs (round-robin by index)
     // so that a pair's chunks run on one XCD, the one its attention
     // workgroups use in the next launch: slot b is scoring workgroup
@@ -670,7 +686,8 @@ __global__ __launch_bounds__(kScoreWaves * 64, CPW) void score_kernel(ScoreArgs 
     asm volatile("" ::"v"(pg[0]));
     if (c0 * CK >= nc) return;  // the pair has no key in these chunks (whole workgroup)
     uint4 kv[T][4];
-    load_chunk_keys<T>(kv, pg, c0 * CK + wave * T * 16, a.kc_pool, a.num_pages, Hkv, g, r, kq);
+    load_chunk_keys<T>(kv, pg, c0 * CK + wave * T * 16, a.kc_pool, a.num_pages, Hkv, g, r, kq,
+                       stream_kc != 0);
     const int jn = nc - 1;
     const bool appending = a.append && L >= kPoolK && (L - kPoolK) % kPoolS == 0;
 #pragma unroll
@@ -761,7 +778,8 @@ __global__ __launch_bounds__(kScoreWaves * 64, CPW) void score_kernel(ScoreArgs 
     }
     __syncthreads();
     if (next)  // its keys stream while this chunk's block sums and partials are made
-        load_chunk_keys<T>(kv, pg, k0 + CK + wave * T * 16, a.kc_pool, a.num_pages, Hkv, g, r, kq);
+        load_chunk_keys<T>(kv, pg, k0 + CK + wave * T * 16, a.kc_pool, a.num_pages, Hkv, g, r, kq,
+                           stream_kc != 0);
     // per (block, head): the block's keys in this chunk, relative to the
     // chunk maximum (finite: key k0 exists for every head)
     const size_t prow = (size_t)pair * a.nbk + (size_t)c * CB;
@@ -1531,6 +1549,10 @@ static hipError_t launch_score(const Plan& pl, const nosa_paged_kv& kv, const no
     a.gp = pl.gp;
     a.scale_log2 = pl.scale_log2;
     a.append = append;
+    // A step's pooled keys are read again at the next step; when they take
+    // more than an eighth of the 256 MB Infinity Cache (so that a model's
+    // layers could not keep theirs there), they are streamed instead.
+    a.stream_kc = (long long)pl.B * pl.Hkv * pl.max_nc * D * 2 > (32LL << 20) ? 1 : 0;
     a.nchunks = pl.nchunks;
     a.nbk = pl.nbk;
     a.cml = w.cml;

@@ -41,10 +41,11 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // The same load with the non-temporal hint, for data streamed once per use
-// whose volume across a model's layers is far beyond the caches (K and V
-// pages): the stream then leaves the L2 and the Infinity Cache to what is
-// reused or written -- the partials, the pooled keys and the tables of the
-// step, the pooled keys a build writes.
+// whose volume across a model's layers is far beyond the caches (the K and V
+// pages of a large decode step, every K page of a pooled-key build): the
+// stream then leaves the L2 and the Infinity Cache to what is reused or
+// written -- the partials, pooled keys and tables of the step, the pooled
+// keys a build writes.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ldg16_stream(const void* p)
 {
@@ -157,19 +158,32 @@ struct PageRegs {
 };
 
 // Issues every load of a page: operand blocks in lane order (k_chunk /
-// v_chunk), 1 KB per load, streamed (non-temporal).  `lane8` is the lane's element offset in a block,
-// (16 kq + r) * 8 (0 makes every lane read the block's first 16 bytes).
+// v_chunk), 1 KB per load, streamed (non-temporal) when `stream` (uniform).
+// `lane8` is the lane's element offset in a block, (16 kq + r) * 8 (0 makes
+// every lane read the block's first 16 bytes).
 __device__ __forceinline__ void load_page(const uint16_t* __restrict__ kb,
-                                          const uint16_t* __restrict__ vb, int lane8, PageRegs& p)
+                                          const uint16_t* __restrict__ vb, int lane8, PageRegs& p,
+                                          bool stream)
 {
+    if (stream) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int st = 0; st < 4; ++st) p.k[t][st] = ldg16_stream(kb + (t * 4 + st) * 512 + lane8);
+            for (int st = 0; st < 4; ++st) p.k[t][st] = ldg16_stream(kb + (t * 4 + st) * 512 + lane8);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) p.v[u][nt] = ldg16_stream(vb + (u * 8 + nt) * 512 + lane8);
+            for (int nt = 0; nt < 8; ++nt) p.v[u][nt] = ldg16_stream(vb + (u * 8 + nt) * 512 + lane8);
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int st = 0; st < 4; ++st) p.k[t][st] = ldg16(kb + (t * 4 + st) * 512 + lane8);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) p.v[u][nt] = ldg16(vb + (u * 8 + nt) * 512 + lane8);
+    }
 }
 
 // The page held in p back to memory at kb / vb, in the same order (a copy of
@@ -195,10 +209,10 @@ __device__ __forceinline__ void attend_loaded(const PageRegs& p, int limit, cons
 __device__ __forceinline__ void attend_page(const uint16_t* __restrict__ kb,
                                             const uint16_t* __restrict__ vb, int limit,
                                             const bf16x8 (&qb)[4], float scale_log2, int r,
-                                            int kq, AttnState& A)
+                                            int kq, AttnState& A, bool stream)
 {
     PageRegs p;
-    load_page(kb, vb, (16 * kq + r) * 8, p);
+    load_page(kb, vb, (16 * kq + r) * 8, p, stream);
     // Keep every load of the page in flight before the first use: a wave that
     // attends one page pays one memory latency instead of one per few loads.
     __builtin_amdgcn_sched_barrier(0);

@@ -356,6 +356,7 @@ struct SplitPageLds {
     uint4 p[2][64];  // PV A operand per k-step and lane (8 bf16)
 };
 
+template <bool STREAM>
 __device__ void attend_page_split4(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
                                    int limit, const bf16x8 (&qb)[4], float scale_log2, int G,
                                    size_t head_row0, int nsplit, int split, float* __restrict__ po,
@@ -365,12 +366,21 @@ __device__ void attend_page_split4(const uint16_t* __restrict__ kb, const uint16
     const int r = lane & 15, kq = lane >> 4;
     const int lane8 = lane * 8;
     uint4 ka[4], va[2][2];
+    if constexpr (STREAM) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) ka[st] = ldg16_stream(kb + (wave * 4 + st) * 512 + lane8);
+        for (int st = 0; st < 4; ++st) ka[st] = ldg16_stream(kb + (wave * 4 + st) * 512 + lane8);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) va[u][j] = ldg16_stream(vb + (u * 8 + 2 * wave + j) * 512 + lane8);
+            for (int j = 0; j < 2; ++j) va[u][j] = ldg16_stream(vb + (u * 8 + 2 * wave + j) * 512 + lane8);
+    } else {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) ka[st] = ldg16(kb + (wave * 4 + st) * 512 + lane8);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) va[u][j] = ldg16(vb + (u * 8 + 2 * wave + j) * 512 + lane8);
+    }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -449,6 +459,7 @@ __device__ __forceinline__ int window_page(const int32_t* table, int max_blocks,
 // empty partial past wn).  All 256 threads.
 __device__ void store_empty_partial(int G, size_t head_row0, int nsplit, int split,
                                     float* __restrict__ po, float2* __restrict__ pml);
+template <bool STREAM>
 __device__ void window_slot(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
                             const int32_t* table, int ring, const int32_t* cu_k, int max_blocks, int Lmax,
                             int Hq, int Hkv, int G, float scale_log2, int wblocks, int s, int g,
@@ -465,7 +476,7 @@ __device__ void window_slot(const uint16_t* q, const uint16_t* k_pool, const uin
         load_q(q, Hq, s, g * G, G, r, kq, qb);
         const int b = nb - wn + x;
         const int page = window_page(table, max_blocks, ring, s, b);
-        attend_page_split4(k_pool + ((size_t)page * Hkv + g) * BS * D,
+        attend_page_split4<STREAM>(k_pool + ((size_t)page * Hkv + g) * BS * D,
                            v_pool + ((size_t)page * Hkv + g) * D * BS, L - b * BS, qb, scale_log2, G,
                            head_row0, nsplit, split0 + x, po, pml, sh);
     } else {
@@ -482,7 +493,7 @@ __device__ __forceinline__ void window_group(const uint16_t* q, const uint16_t* 
                              const int32_t* table, int ring, const int32_t* cu_k, int max_blocks,
                              int Lmax, int Hq, int Hkv, int G, float scale_log2, int wblocks, int s,
                              int g, int j, int nsplit, int split0, float* po, float2* pml,
-                             CombineLds& sh)
+                             CombineLds& sh, bool stream)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
     const int L = seq_len(cu_k, s, Lmax);
@@ -497,7 +508,7 @@ __device__ __forceinline__ void window_group(const uint16_t* q, const uint16_t* 
         const int b = nb - wn + x;
         const int page = window_page(table, max_blocks, ring, s, b);
         attend_page(k_pool + ((size_t)page * Hkv + g) * BS * D, v_pool + ((size_t)page * Hkv + g) * D * BS,
-                    L - b * BS, qb, scale_log2, r, kq, A);
+                    L - b * BS, qb, scale_log2, r, kq, A, stream);
     }
     store_wg_partial(sh, A, G, (size_t)s * Hq + g * G, nsplit, split0 + j, po, pml);
 }
@@ -645,14 +656,15 @@ __global__ __launch_bounds__(kScoreWaves * 64, CPW) void score_kernel(ScoreArgs 
                 window_group(a.q, a.k_pool, a.v_pool, a.table, a.ring, a.cu_k, a.max_blocks, a.Lmax,
                              a.Hq, a.Hkv, a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv,
                              w % a.wgroups, a.nsplit, a.split0, a.po, a.pml,
-                             *reinterpret_cast<CombineLds*>(smem));
+                             *reinterpret_cast<CombineLds*>(smem), true);
                 NOSA_TL(0, 2);
                 return;
             }
         }
-        window_slot(a.q, a.k_pool, a.v_pool, a.table, a.ring, a.cu_k, a.max_blocks, a.Lmax, a.Hq,
-                    a.Hkv, a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv, w % a.wgroups,
-                    a.nsplit, a.split0, a.po, a.pml, *reinterpret_cast<SplitPageLds*>(smem));
+        window_slot<true>(a.q, a.k_pool, a.v_pool, a.table, a.ring, a.cu_k, a.max_blocks, a.Lmax,
+                          a.Hq, a.Hkv, a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv,
+                          w % a.wgroups, a.nsplit, a.split0, a.po, a.pml,
+                          *reinterpret_cast<SplitPageLds*>(smem));
         NOSA_TL(0, 2);
         return;
     }
@@ -873,6 +885,7 @@ struct TopArgs {
     int4 disp;           // top / window workgroups per XCD, top / window workgroups of the
                          // launch (one argument, so one scalar load gates the early exit)
     int scores_only;     // importance only (no selection, no attention)
+    int stream;          // the host's choice of instantiation: page loads streamed
     float* scores_out;   // [pairs][max_nb] or null (workgroup 0 of a pair writes)
     int32_t* sel_out;    // [pairs][max_sel] or null (workgroup 0 of a pair writes)
     int32_t* cnt_out;    // [pairs] or null
@@ -966,7 +979,7 @@ typedef const __attribute__((address_space(1))) int32_t* GlobalI1;
 // first, and are read from host memory, attended and written into their slot
 // in one pass.
 // Cached blocks lie before the window, so they are complete and never change.
-template <int KRB, int GP4, bool OFF>
+template <int KRB, int GP4, bool OFF, bool STREAM>
 __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
 {
     constexpr int NT = kStep2Waves * 64;
@@ -999,9 +1012,9 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
     asm("" : "+s"(cml), "+s"(spill), "+s"(bpart4));
     if (window && a.wgroups == a.wslots) {  // one window page, the four waves together
         const int pair = lid / a.wgroups;
-        window_slot(a.q, a.wk, a.wv, a.table, a.ring, a.cu_k, a.max_blocks, a.Lmax, a.Hq, a.Hkv,
-                    a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv, lid % a.wgroups,
-                    a.nsplit, a.groups, a.po, a.pml, sh.page);
+        window_slot<STREAM>(a.q, a.wk, a.wv, a.table, a.ring, a.cu_k, a.max_blocks, a.Lmax, a.Hq,
+                            a.Hkv, a.G, a.scale_log2, a.wblocks, pair / a.Hkv, pair % a.Hkv,
+                            lid % a.wgroups, a.nsplit, a.groups, a.po, a.pml, sh.page);
         NOSA_TL(1, 5);
         return;
     }
@@ -1239,7 +1252,7 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
                 const int lane8 = (16 * kq + r) * 8;
                 PageRegs pr;
                 load_page(a.k_pool + ((size_t)pg * a.Hkv + g) * BS * D,
-                          a.v_pool + ((size_t)pg * a.Hkv + g) * D * BS, lane8, pr);
+                          a.v_pool + ((size_t)pg * a.Hkv + g) * D * BS, lane8, pr, STREAM);
                 __builtin_amdgcn_sched_barrier(0);
                 store_page(ck, cv, lane8, pr);
                 attend_loaded(pr, L - e.x * BS, qb, a.scale_log2, r, kq, A);
@@ -1251,7 +1264,7 @@ __global__ __launch_bounds__(kStep2Waves * 64, 2) void top_kernel(TopArgs a)
             kb = a.k_pool + ((size_t)e.y * a.Hkv + g) * BS * D;
             vb = a.v_pool + ((size_t)e.y * a.Hkv + g) * D * BS;
         }
-        attend_page(kb, vb, L - e.x * BS, qb, a.scale_log2, r, kq, A);
+        attend_page(kb, vb, L - e.x * BS, qb, a.scale_log2, r, kq, A, STREAM);
     }
     NOSA_TL(1, 4);  // pages attended
     store_wg_partial(sh.comb, A, a.G, head_row0, a.nsplit, window ? a.groups + k : k, a.po, a.pml);
@@ -1272,6 +1285,7 @@ struct AttendArgs {
     const int32_t* sel;  // [pairs][max_sel] block ids
     const int32_t* cnt;  // [pairs]
     int max_sel;
+    int stream;          // the host's choice of instantiation: page loads streamed
     float* po;
     float2* pml;
 };
@@ -1371,7 +1385,7 @@ static hipError_t launch_merge(const Plan& pl, const Workspace& w, int nsplit, f
 // workgroup gets the same number of pages, give or take one; one 64-token
 // block at a time, and the workgroup stores one partial per head at slot grp.
 static_assert(kStep2Waves == 4, "store_wg_partial combines four waves");
-template <int R>
+template <int R, bool STREAM>
 __global__ __launch_bounds__(kStep2Waves * 64) void attend_kernel(AttendArgs a)
 {
     __shared__ CombineLds sh;
@@ -1420,7 +1434,7 @@ __global__ __launch_bounds__(kStep2Waves * 64) void attend_kernel(AttendArgs a)
         if (b < 0) continue;
         const uint16_t* kb = a.k_pool + ((size_t)page * a.Hkv + g) * BS * D;
         const uint16_t* vb = a.v_pool + ((size_t)page * a.Hkv + g) * D * BS;
-        attend_page(kb, vb, L - b * BS, qb, a.scale_log2, r, kq, A);
+        attend_page(kb, vb, L - b * BS, qb, a.scale_log2, r, kq, A, STREAM);
     }
     store_wg_partial(sh, A, a.G, (size_t)s * a.Hq + g * a.G, groups, grp, a.po, a.pml);
 }
@@ -1525,6 +1539,22 @@ hipError_t static_scratch(void** ptr)
     return hipSuccess;
 }
 
+// A step's pooled keys and its K and V pages are mostly read again at the
+// next step.  Where a step reads more of either than an eighth of the 256 MB
+// Infinity Cache (so that a model's layers could not keep theirs there), the
+// loads are streamed (non-temporal) and leave the caches to what is reused;
+// below that they are ordinary loads, which the next step may find cached.
+constexpr long long kStreamBytes = 32LL << 20;
+static int stream_keys(const Plan& pl)
+{
+    return (long long)pl.B * pl.Hkv * pl.max_nc * D * 2 > kStreamBytes ? 1 : 0;
+}
+static int stream_pages(const Plan& pl)
+{
+    const int pages = pl.max_sel < pl.max_nb ? pl.max_sel : pl.max_nb;
+    return (long long)pl.B * pl.Hkv * pages * BS * D * 2 * 2 > kStreamBytes ? 1 : 0;
+}
+
 // wgroups > 0: also the window workgroups, wgroups per pair (pl.wslots: a
 // page each; fewer: a page per wave, score_tiles = 8 only), their partials
 // at slots top_groups .. of nsplit.
@@ -1549,10 +1579,7 @@ static hipError_t launch_score(const Plan& pl, const nosa_paged_kv& kv, const no
     a.gp = pl.gp;
     a.scale_log2 = pl.scale_log2;
     a.append = append;
-    // A step's pooled keys are read again at the next step; when they take
-    // more than an eighth of the 256 MB Infinity Cache (so that a model's
-    // layers could not keep theirs there), they are streamed instead.
-    a.stream_kc = (long long)pl.B * pl.Hkv * pl.max_nc * D * 2 > (32LL << 20) ? 1 : 0;
+    a.stream_kc = stream_keys(pl);
     a.nchunks = pl.nchunks;
     a.nbk = pl.nbk;
     a.cml = w.cml;
@@ -1591,6 +1618,7 @@ static TopArgs top_args(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16
                         const int32_t* cu_k, const Workspace& w)
 {
     TopArgs a{};
+    a.stream = stream_pages(pl);
     a.q = q;
     a.k_pool = kv.k_pool;
     a.v_pool = kv.v_pool;
@@ -1622,26 +1650,31 @@ static TopArgs top_args(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16
     return a;
 }
 
-template <int KRB, int GP4, bool OFF>
+template <int KRB, int GP4, bool OFF, bool STREAM>
 static void launch_top_t(dim3 grid, size_t lds, const TopArgs& a, hipStream_t stream)
 {
     if (lds > 64 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&top_kernel<KRB, GP4, OFF>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&top_kernel<KRB, GP4, OFF, STREAM>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL((top_kernel<KRB, GP4, OFF>), grid, dim3(kStep2Waves * 64), lds, stream, a);
+    hipLaunchKernelGGL((top_kernel<KRB, GP4, OFF, STREAM>), grid, dim3(kStep2Waves * 64), lds, stream, a);
+}
+
+// Offloaded KV: always streamed (its picks come from host memory).
+template <int KRB, int GP4>
+static void launch_top_s(dim3 grid, size_t lds, const TopArgs& a, hipStream_t stream)
+{
+    if (a.cap > 0) launch_top_t<KRB, GP4, true, true>(grid, lds, a, stream);
+    else if (a.stream) launch_top_t<KRB, GP4, false, true>(grid, lds, a, stream);
+    else launch_top_t<KRB, GP4, false, false>(grid, lds, a, stream);
 }
 
 template <int KRB>
 static void launch_top_k(dim3 grid, size_t lds, int gp4, const TopArgs& a, hipStream_t stream)
 {
-    const bool off = a.cap > 0;
     switch (gp4) {
-        case 1: off ? launch_top_t<KRB, 1, true>(grid, lds, a, stream)
-                    : launch_top_t<KRB, 1, false>(grid, lds, a, stream); break;
-        case 2: off ? launch_top_t<KRB, 2, true>(grid, lds, a, stream)
-                    : launch_top_t<KRB, 2, false>(grid, lds, a, stream); break;
-        default: off ? launch_top_t<KRB, 4, true>(grid, lds, a, stream)
-                     : launch_top_t<KRB, 4, false>(grid, lds, a, stream); break;
+        case 1: launch_top_s<KRB, 1>(grid, lds, a, stream); break;
+        case 2: launch_top_s<KRB, 2>(grid, lds, a, stream); break;
+        default: launch_top_s<KRB, 4>(grid, lds, a, stream); break;
     }
 }
 
@@ -1747,11 +1780,19 @@ hipError_t launch_decode(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
     return launch_merge(pl, w, nsplit, out, lse, stream, off);
 }
 
+template <int R>
+static void launch_attend_r(dim3 grid, dim3 block, const AttendArgs& b, hipStream_t stream)
+{
+    if (b.stream) hipLaunchKernelGGL((attend_kernel<R, true>), grid, block, 0, stream, b);
+    else hipLaunchKernelGGL((attend_kernel<R, false>), grid, block, 0, stream, b);
+}
+
 hipError_t launch_attend(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf16* q,
                          const int32_t* cu_k, const int32_t* sel, const int32_t* cnt,
                          const Workspace& w, float* out, float* lse, hipStream_t stream)
 {
     AttendArgs b{};
+    b.stream = stream_pages(pl);
     b.q = q;
     b.k_pool = kv.k_pool;
     b.v_pool = kv.v_pool;
@@ -1771,12 +1812,12 @@ hipError_t launch_attend(const Plan& pl, const nosa_paged_kv& kv, const nosa_bf1
     b.pml = w.pml;
     const dim3 grid(pl.B * pl.Hkv * pl.attend_groups), block(kStep2Waves * 64);
     switch (pl.attend_rounds) {
-        case 1: hipLaunchKernelGGL(attend_kernel<1>, grid, block, 0, stream, b); break;
-        case 2: hipLaunchKernelGGL(attend_kernel<2>, grid, block, 0, stream, b); break;
-        case 3: hipLaunchKernelGGL(attend_kernel<3>, grid, block, 0, stream, b); break;
-        case 4: hipLaunchKernelGGL(attend_kernel<4>, grid, block, 0, stream, b); break;
-        case 6: hipLaunchKernelGGL(attend_kernel<6>, grid, block, 0, stream, b); break;
-        default: hipLaunchKernelGGL(attend_kernel<8>, grid, block, 0, stream, b); break;
+        case 1: launch_attend_r<1>(grid, block, b, stream); break;
+        case 2: launch_attend_r<2>(grid, block, b, stream); break;
+        case 3: launch_attend_r<3>(grid, block, b, stream); break;
+        case 4: launch_attend_r<4>(grid, block, b, stream); break;
+        case 6: launch_attend_r<6>(grid, block, b, stream); break;
+        default: launch_attend_r<8>(grid, block, b, stream); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

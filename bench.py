@@ -1306,7 +1306,8 @@ def timeline_main(w, args):
              "select_first_digit": np.median(top_rows[:, 9]) - t0,
              "select_last_digit": np.median(top_rows[:, 10]) - t0,
              "select_counts_shared": np.median(top_rows[:, 11]) - t0,
-             "select_more_levels_share": float(np.mean(top_rows[:, 10] - top_rows[:, 9] > 0.05)),
+             # point 15: stamped when the selector runs a digit level after the first
+             "select_more_levels_share": float(np.mean(top_rows[:, 15] > 0)),
              "top_selection": np.median(top_rows[:, 3]) - t0,
              "top_pages_attended": np.median(top_rows[:, 4]) - t0,
              "top_partial_stored": np.median(top_rows[:, 5]) - t0,

@@ -416,7 +416,8 @@ __device__ __forceinline__ float wave_sum_f(float x)
 // when tied keys straddle the cut).
 // Mark, called with 0 .. 3 as the selector passes its stages (the range
 // known, the first digit found, the last digit found, the compaction's
-// counts shared): a hook for instrumented builds, a no-op by default.
+// counts shared), and with 7 when a digit level after the first runs: a
+// hook for instrumented builds, a no-op by default.
 struct NoMark {
     __device__ void operator()(int) const {}
 };
@@ -558,6 +559,7 @@ __device__ __forceinline__ void select_blocks_wg(uint32_t (&keys)[kSelKeyRounds]
             if (!done) {
 #pragma unroll 1
                 for (int level = 0; level < 3; ++level) {
+                    mark(7);
                     sh_lo = sh_lo > 8 ? sh_lo - 8 : 0;
                     if (level_pass(sh.hist[level], std::integral_constant<int, 4>{})) break;
                 }

@@ -11,7 +11,7 @@
 
 namespace nosa {
 
-// Shapes with a kernel in this build.
+// Shapes the library has kernels for.
 constexpr int kHeadDim = 128;
 constexpr int kBlock = 64;   // tokens per KV block = per page
 constexpr int kPoolK = 32;   // pooling window

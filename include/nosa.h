@@ -31,7 +31,7 @@
  *     entries are clamped into the pool and never used).
  *   - Host-checkable arguments are validated before anything is enqueued: a
  *     NULL required pointer gives NOSA_ERR_NULL, inconsistent sizes
- *     NOSA_ERR_INVALID, a shape this build has no kernel for
+ *     NOSA_ERR_INVALID, a shape the library has no kernel for
  *     NOSA_ERR_UNSUPPORTED, a short workspace NOSA_ERR_WORKSPACE, and a failed
  *     HIP launch NOSA_ERR_HIP.  Nothing aborts.
  *   - Global state: a per-device cache of two device attributes (LDS per

@@ -131,15 +131,16 @@ __device__ __forceinline__ uint4 round8(const double (&acc)[8])
 // page, lanes u = 0 read the first group of the next page for the last key.
 // Keys [n_c(prev), n_c(L)) are written, prev = valid_len[s] or 0 for a full
 // build.  Long runs per wave keep a page of loads in flight from start to
-// end (a wave fills and drains its pipeline once), so the grid is sized to
-// about two waves per SIMD.
+// end (a wave fills and drains its pipeline once); the grid is sized to
+// about four waves per SIMD (two resident at a time, two workgroups per CU),
+// so that the second half of the waves starts as the first ones end.
 //
 // LDS slot of (token x, chunk c8): 16 x + (c8 ^ swz(x)), swz(x) = (x & 3) |
 // ((x & 8) >> 1).  A wave's store of one operand run (lanes: 16 tokens x 4
 // chunks) and its loads of one token per lane group (16 chunks) then touch
 // eight different 16-byte bank groups in every group of eight lanes.
 constexpr int kKcMinPagesPerWave = 2;
-constexpr int kKcTargetWaves = 2048;
+constexpr int kKcTargetWaves = 4096;
 
 __device__ __forceinline__ int kc_lds_slot(int x, int c8)
 {

@@ -334,7 +334,10 @@ def main():
     if args.chip_probes:
         return chip_probes_main(args)
     if args.timeline:
-        return timeline_main(synth.config(args.config), args)
+        w = synth.config(args.config)
+        if w.q_lens is not None and max(w.q_lens) > 1:
+            return timeline_prefill_main(w, args)
+        return timeline_main(w, args)
     if args.ceiling:
         return ceiling_main(args)
     w = synth.config(args.config)
@@ -1361,6 +1364,90 @@ def timeline_main(w, args):
                       "layer_caches": nl},
            "phases_us": med, "instrumented_us_per_step": round(float(np.median(step_us)), 2),
            "wall_clock_khz": khz}
+    print(json.dumps(res), flush=True)
+
+
+def timeline_prefill_main(w, args):
+    """Where a prefill chunk's time goes: the chain nosa_block_scores ->
+    nosa_select_blocks -> nosa_sparse_attend with the prefill kernels built
+    with wall-clock stamps (libnosa_timeline.so): per launch, when its
+    workgroups start and leave (first, median, last) and the share of the
+    launch each workgroup is resident on average.  Medians over 5 runs of the
+    chain."""
+    import ctypes
+    import math
+    import numpy as np
+    import torch
+    from block_sparse_attention_nosa_amd import build, nosa, synth
+    if not os.path.exists(build.TIMELINE_LIB):
+        raise SystemExit(f"{build.TIMELINE_LIB} is missing: build it first")
+    nosa.LIB_PATH = build.TIMELINE_LIB
+    L = nosa.lib()
+    L.nosa_timeline_read_prefill.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    for f in ("nosa_timeline_read_prefill", "nosa_timeline_clear_prefill", "nosa_timeline_clock_khz"):
+        getattr(L, f).restype = ctypes.c_int
+    khz = L.nosa_timeline_clock_khz()
+    assert khz > 0
+    dev = torch.device("cuda", 0)
+    inp = synth.make_inputs(w, device="cuda")
+    pg = synth.to_paged(inp, w, device="cuda")
+    kv = nosa.paged_kv(pg["k_pool"], pg["v_pool"], pg["kc_pool"], pg["block_table"])
+    p = nosa.params(w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.kernel, w.stride,
+                    w.topk, w.window, locality=w.locality)
+    B, maxL, maxLq = w.batch, max(w.lens), max(w.q_lens)
+    cu_k = synth.cu_from_lens(w.lens, "cuda")
+    cu_q = inp["cu_q"].cuda().to(torch.int32)
+    nosa.nosa_compress_keys(p, kv, cu_k, None, B, maxL)
+    mq, max_nb = math.ceil(maxLq / 64), math.ceil(maxL / 64)
+    scores = torch.empty(B, mq, w.num_kv_heads, max_nb, device=dev)
+    sel = torch.empty(B, mq, w.num_kv_heads, w.topk + w.window // 64, dtype=torch.int32, device=dev)
+    cnt = torch.empty(B, mq, w.num_kv_heads, dtype=torch.int32, device=dev)
+    out = torch.empty(inp["q"].shape[0], w.num_q_heads, w.head_dim, device=dev)
+    lse = torch.empty(inp["q"].shape[0], w.num_q_heads, device=dev)
+    ws = torch.zeros(nosa.nosa_workspace_size(p, B, maxLq, maxL), dtype=torch.uint8, device=dev)
+
+    def chain():
+        nosa.nosa_block_scores(p, kv, inp["q"], cu_q, cu_k, B, maxLq, maxL, scores, ws)
+        nosa.nosa_select_blocks(p, scores, cu_q, cu_k, B, maxLq, maxL, sel, cnt)
+        nosa.nosa_sparse_attend(p, kv, inp["q"], cu_q, cu_k, B, maxLq, maxL, sel, cnt, out, lse, ws)
+
+    for _ in range(3):
+        chain()
+    torch.cuda.synchronize()
+    names = {0: "scoring_pass1", 1: "scoring_pass2", 3: "pooling", 2: "attention", 4: "merge"}
+    stamps = np.zeros((8192, 4), dtype=np.uint64)
+    runs = []
+    for rep in range(5):
+        assert L.nosa_timeline_clear_prefill() == 0
+        chain()
+        torch.cuda.synchronize()
+        t0, r = None, {}
+        for k in (0, 1, 3, 2, 4):
+            assert L.nosa_timeline_read_prefill(k, stamps.ctypes.data) == 0
+            done = stamps[(stamps[:, 0] > 0) & (stamps[:, 1] > 0)].astype(np.float64) * 1e3 / khz
+            if len(done) == 0:
+                continue
+            if t0 is None:
+                t0 = done[:, 0].min()
+            st, en = done[:, 0] - t0, done[:, 1] - t0
+            xcc = stamps[(stamps[:, 0] > 0) & (stamps[:, 1] > 0)][:, 2].astype(np.int64) & 15
+            span = en.max() - st.min()
+            r[names[k]] = {"workgroups": int(len(done)), "first_start": st.min(),
+                           "median_start": float(np.median(st)), "last_start": st.max(),
+                           "median_end": float(np.median(en)), "last_end": en.max(),
+                           "resident_share": float(np.mean(en - st) / span) if span > 0 else 1.0}
+            for x in range(8):
+                sel_x = xcc == x
+                r[names[k]][f"median_end_xcd{x}"] = float(np.median(en[sel_x])) if sel_x.any() else float("nan")
+                r[names[k]][f"last_end_xcd{x}"] = float(en[sel_x].max()) if sel_x.any() else float("nan")
+        runs.append(r)
+    med = {n: {k: round(float(np.median([r[n][k] for r in runs])), 3) for k in runs[0][n]}
+           for n in runs[0]}
+    res = {"metric": "prefill chunk timeline", "value": med[list(med)[-1]]["last_end"],
+           "unit": "us from the first scoring workgroup's start", "n_gpus": 1,
+           "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": w.name, "queries": maxLq, "context": maxL, "runs": 5},
+           "launches_us": med, "wall_clock_khz": khz}
     print(json.dumps(res), flush=True)
 
 

@@ -1469,12 +1469,33 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
         nb = left > 0 ? (L - Lq + 64 * qb + (left < 64 ? left : 64) - 1) / BS + 1 : 0;
     }
     const size_t pair = (size_t)sr * Hkv + g;
-    for (int b = threadIdx.x; b < nb; b += 256) sI[b] = scores_in[pair * max_nb + b];
+    // the scores in batches of kSelKeyRounds per thread, every load of a
+    // batch in flight before the first is used; the first batch's order keys
+    // go to the selector in registers, every score to LDS
+    const float* row = scores_in + pair * max_nb;
+    uint32_t keys[kSelKeyRounds];
+    for (int b0 = 0; b0 < nb; b0 += kSelKeyRounds * 256) {
+        float v[kSelKeyRounds];
+#pragma unroll
+        for (int i = 0; i < kSelKeyRounds; ++i) {
+            const int b = b0 + i * 256 + (int)threadIdx.x;
+            v[i] = b < nb ? row[b] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < kSelKeyRounds; ++i) {
+            const int b = b0 + i * 256 + (int)threadIdx.x;
+            if (b < nb) sI[b] = v[i];
+            if (b0 == 0) keys[i] = order_key(v[i]);
+        }
+    }
+    if (nb <= 0) {
+#pragma unroll
+        for (int i = 0; i < kSelKeyRounds; ++i) keys[i] = 0u;
+    }
     select_lds_clear<256>(sh);
     __syncthreads();
-    uint32_t keys[kSelKeyRounds];
-    select_blocks_wg<4, false>(keys, sI, nb, wblocks, topk, sh, sel + pair * max_sel, cnt + pair,
-                               max_sel, nullptr, 0, 0, nullptr);
+    select_blocks_wg<4, true>(keys, sI, nb, wblocks, topk, sh, sel + pair * max_sel, cnt + pair,
+                              max_sel, nullptr, 0, 0, nullptr);
 }
 
 // ---------------------------------------------------------- launchers ---

@@ -25,6 +25,39 @@
 
 namespace nosa {
 
+// Timeline build (NOSA_TIMELINE, the benchmark's timeline mode; the NOSA
+// library has none of this): thread 0 of each workgroup of the prefill
+// launches (0: scoring pass 1, 1: pass 2, 2: attention, 3: pooling,
+// 4: merge of split attention) stamps the wall clock when the workgroup
+// starts and when it leaves the kernel, and records its XCD, in
+// pf_tl[launch][workgroup][0 .. 2].
+#ifdef NOSA_TIMELINE
+constexpr int kPfTlGroups = 8192;
+__device__ unsigned long long pf_tl[5][kPfTlGroups][4];
+struct PfTlScope {
+    int launch;
+    __device__ explicit PfTlScope(int l) : launch(l)
+    {
+        __builtin_amdgcn_sched_barrier(0);
+        if (threadIdx.x == 0 && blockIdx.x < kPfTlGroups) {
+            pf_tl[launch][blockIdx.x][0] = wall_clock64();
+            pf_tl[launch][blockIdx.x][2] = (unsigned)__builtin_amdgcn_s_getreg(30740);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __device__ ~PfTlScope()
+    {
+        __builtin_amdgcn_sched_barrier(0);
+        if (threadIdx.x == 0 && blockIdx.x < kPfTlGroups) pf_tl[launch][blockIdx.x][1] = wall_clock64();
+    }
+};
+#define PF_TL_SCOPE(launch) PfTlScope pf_tl_scope_(launch)
+#else
+#define PF_TL_SCOPE(launch) \
+    do {                    \
+    } while (0)
+#endif
+
 constexpr int kQB = 64;   // queries per query block
 constexpr int kChunk = kPfChunk;                       // pooled keys staged in LDS at a time
 constexpr int kMaxSpan = kPfChunk * kPfMaxSpanChunks;  // pooled keys per scoring workgroup at most
@@ -161,6 +194,7 @@ __device__ __forceinline__ float row_lse(const float2* __restrict__ pp, int n)
 template <int PASS, int RTW>
 __global__ __launch_bounds__(256, 2) void pf_score_kernel(PfArgs a)
 {
+    PF_TL_SCOPE(PASS - 1);
     __shared__ PfScoreLds sh;
     // the two chunk buffers are distinct objects: a read of one is then known
     // not to wait for the copy in flight into the other
@@ -515,6 +549,7 @@ __global__ __launch_bounds__(256) void pf_lse_kernel(PfArgs a, int total)
 // 4b+3 that the block's last query sees.  One workgroup per pair.
 __global__ __launch_bounds__(256) void pf_pool_kernel(PfArgs a)
 {
+    PF_TL_SCOPE(3);
     extern __shared__ __align__(16) char smem[];
     float* sI = reinterpret_cast<float*>(smem);
     const int pair = blockIdx.x;
@@ -525,24 +560,30 @@ __global__ __launch_bounds__(256) void pf_pool_kernel(PfArgs a)
     for (int b = tid; b < nb; b += 256) sI[b] = 0.f;
     __syncthreads();
     // thread t takes keys 4t .. 4t + 3 of every 1024, eight such groups per
-    // batch with all their loads in flight (a group's 16 bytes lie inside
-    // the column sums; keys past n_c are masked)
+    // batch; per row group, the eight groups' loads are all in flight before
+    // the first is summed (a group's 16 bytes lie inside the column sums;
+    // keys past n_c are masked).  Row groups are summed in ascending order.
     const float* cs = a.colsum + (size_t)pair * a.row_groups * a.zlen;
     const int nck = P.empty ? 0 : P.nck;
     for (int j00 = 0; j00 < nck; j00 += 8 * 1024) {
         float4 v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int j0 = j00 + 1024 * k + 4 * tid;
-            v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j0 < nck)
-                for (int q = 0; q < a.row_groups; ++q) {
-                    const float4 w = *reinterpret_cast<const float4*>(cs + (size_t)q * a.zlen + j0);
-                    v[k].x += w.x;
-                    v[k].y += w.y;
-                    v[k].z += w.z;
-                    v[k].w += w.w;
-                }
+        for (int k = 0; k < 8; ++k) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int q = 0; q < a.row_groups; ++q) {
+            float4 w[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int j0 = j00 + 1024 * k + 4 * tid;
+                w[k] = j0 < nck ? *reinterpret_cast<const float4*>(cs + (size_t)q * a.zlen + j0)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                v[k].x += w[k].x;
+                v[k].y += w[k].y;
+                v[k].z += w[k].z;
+                v[k].w += w[k].w;
+            }
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -593,6 +634,7 @@ typedef uint16_t PfPageBuf[BS * D];
 __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_groups, int total,
                                                         int per_xcd)
 {
+    PF_TL_SCOPE(2);
     __shared__ PfPageBuf k_even, v_even, k_odd, v_odd;
     extern __shared__ __align__(16) char smem[];
     int2* list = reinterpret_cast<int2*>(smem);  // [max_sel] (block, page)
@@ -813,6 +855,7 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
 // thread per (row, 4 channels).
 __global__ __launch_bounds__(256) void pf_merge_kernel(PfArgs a, int attn_groups, int total)
 {
+    PF_TL_SCOPE(4);
     const int lid = blockIdx.x;
     if (lid >= total) return;
     const int pair = lid / attn_groups, ag = lid % attn_groups;
@@ -986,3 +1029,29 @@ hipError_t launch_chunk_setup(const int32_t* cu, int B, int Lmax, int c, int C, 
 }
 
 }  // namespace nosa
+
+#ifdef NOSA_TIMELINE
+// Readout of the prefill launches' stamps (not part of the NOSA C ABI).
+extern "C" {
+
+// Copies launch `launch`'s stamps ([8192][4] unsigned 64-bit) to host memory.
+int nosa_timeline_read_prefill(int launch, unsigned long long* host)
+{
+    if (launch < 0 || launch > 4 || !host) return (int)hipErrorInvalidValue;
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(nosa::pf_tl), sizeof(nosa::pf_tl[0]),
+                                    (size_t)launch * sizeof(nosa::pf_tl[0]), hipMemcpyDeviceToHost);
+}
+
+// Zeroes every prefill stamp (synchronous).
+int nosa_timeline_clear_prefill(void)
+{
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(nosa::pf_tl));
+    if (e != hipSuccess) return (int)e;
+    e = hipMemset(p, 0, sizeof(nosa::pf_tl));
+    if (e != hipSuccess) return (int)e;
+    return (int)hipDeviceSynchronize();
+}
+
+}  // extern "C"
+#endif

@@ -546,65 +546,65 @@ __global__ __launch_bounds__(256) void pf_lse_kernel(PfArgs a, int total)
 
 // Block importance of a pair: sigma[j] = sum over row groups (fixed order) of
 // the column sums; importance of block b = mean of sigma over the keys 4b-1 ..
-// 4b+3 that the block's last query sees.  One workgroup per pair.
-__global__ __launch_bounds__(256) void pf_pool_kernel(PfArgs a)
+// 4b+3 that the block's last query sees.  A workgroup per (pair, 256 blocks):
+// thread t takes block b = 256 s + t, sums its own keys 4b .. 4b+3 (one
+// 16-byte load per row group, all in flight together) and takes key 4b-1 from
+// its left neighbour through LDS; thread 0 of a later slice sums that key
+// itself, in the same order, so every sigma[j] is one fixed sum.  The loads
+// need only the workspace bounds (keys past n_c are masked afterwards), so they
+// leave before the pair's lengths are in.
+constexpr int kPoolBlocks = 256;
+
+__global__ __launch_bounds__(256) void pf_pool_kernel(PfArgs a, int slices)
 {
     PF_TL_SCOPE(3);
-    extern __shared__ __align__(16) char smem[];
-    float* sI = reinterpret_cast<float*>(smem);
-    const int pair = blockIdx.x;
-    const PfPair P = pf_pair(a, pair);
+    __shared__ float key_w[kPoolBlocks];
     const int tid = threadIdx.x;
-    float* out = a.scores + (size_t)pair * a.max_nb;
-    const int nb = P.empty ? 0 : P.nb;
-    for (int b = tid; b < nb; b += 256) sI[b] = 0.f;
-    __syncthreads();
-    // thread t takes keys 4t .. 4t + 3 of every 1024, eight such groups per
-    // batch; per row group, the eight groups' loads are all in flight before
-    // the first is summed (a group's 16 bytes lie inside the column sums;
-    // keys past n_c are masked).  Row groups are summed in ascending order.
+    const int pair = blockIdx.x / slices;
+    const int b = (blockIdx.x - pair * slices) * kPoolBlocks + tid;
+    const int j0 = 4 * b;
     const float* cs = a.colsum + (size_t)pair * a.row_groups * a.zlen;
-    const int nck = P.empty ? 0 : P.nck;
-    for (int j00 = 0; j00 < nck; j00 += 8 * 1024) {
-        float4 v[8];
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    float left = 0.f;  // sigma[j0 - 1], summed here by thread 0 of a later slice
+    const bool own = j0 < a.zlen, edge = tid == 0 && b > 0 && j0 - 1 < a.zlen;
+    for (int q0 = 0; q0 < a.row_groups; q0 += 8) {
+        float4 w[8];
+        float e[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int q = 0; q < a.row_groups; ++q) {
-            float4 w[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int j0 = j00 + 1024 * k + 4 * tid;
-                w[k] = j0 < nck ? *reinterpret_cast<const float4*>(cs + (size_t)q * a.zlen + j0)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                v[k].x += w[k].x;
-                v[k].y += w[k].y;
-                v[k].z += w[k].z;
-                v[k].w += w[k].w;
-            }
+        for (int k = 0; k < 8; ++k) {
+            const bool in = q0 + k < a.row_groups;
+            const float* row = cs + (size_t)(q0 + k) * a.zlen;
+            w[k] = in && own ? *reinterpret_cast<const float4*>(row + j0) : make_float4(0.f, 0.f, 0.f, 0.f);
+            e[k] = in && edge ? row[j0 - 1] : 0.f;
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const int j0 = j00 + 1024 * k + 4 * tid;
-            if (j0 >= nck) continue;
-            const float sg[4] = {v[k].x, j0 + 1 < nck ? v[k].y : 0.f, j0 + 2 < nck ? v[k].z : 0.f,
-                                 j0 + 3 < nck ? v[k].w : 0.f};
-            const int b = j0 >> 2;
-            atomicAdd(&sI[b], (sg[0] + sg[1]) + (sg[2] + sg[3]));
-            if (j0 + 3 < nck && b + 1 < nb) atomicAdd(&sI[b + 1], sg[3]);
+            if (q0 + k >= a.row_groups) break;
+            v.x += w[k].x;
+            v.y += w[k].y;
+            v.z += w[k].z;
+            v.w += w[k].w;
+            left += e[k];
         }
     }
+    key_w[tid] = v.w;
+    const PfPair P = pf_pair(a, pair);
+    const int nb = P.empty ? 0 : P.nb;
+    const int nck = P.empty ? 0 : P.nck;
     __syncthreads();
-    for (int b = tid; b < a.max_nb; b += 256) {
-        float I = -INFINITY;
-        if (b < nb) {
-            const int jlo = max(4 * b - 1, 0), jhi = min(4 * b + 3, P.nck - 1);
-            if (jlo <= jhi) I = sI[b] / (float)(jhi - jlo + 1);
+    if (tid > 0) left = key_w[tid - 1];
+    float I = -INFINITY;
+    if (b < nb) {
+        const int jlo = max(j0 - 1, 0), jhi = min(j0 + 3, P.nck - 1);
+        if (jlo <= jhi) {
+            const float mine = j0 < nck ? (v.x + (j0 + 1 < nck ? v.y : 0.f)) +
+                                              ((j0 + 2 < nck ? v.z : 0.f) + (j0 + 3 < nck ? v.w : 0.f))
+                                        : 0.f;
+            const float prev = b > 0 && j0 - 1 < nck ? left : 0.f;
+            I = (mine + prev) / (float)(jhi - jlo + 1);
         }
-        out[b] = I;
     }
+    if (b < a.max_nb) a.scores[(size_t)pair * a.max_nb + b] = I;
 }
 
 // ------------------------------------------------------------ attention ---
@@ -946,8 +946,9 @@ hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_k
         }
     }
 #undef NOSA_PF
-    const size_t lds = sizeof(float) * (size_t)(pl.max_nb > 0 ? pl.max_nb : 1);
-    hipLaunchKernelGGL(pf_pool_kernel, dim3(pf.npairs), dim3(256), lds, stream, a);
+    const int slices = (pl.max_nb + kPoolBlocks - 1) / kPoolBlocks;
+    if (slices == 0 || pf.npairs == 0) return hipSuccess;
+    hipLaunchKernelGGL(pf_pool_kernel, dim3(pf.npairs * slices), dim3(256), 0, stream, a, slices);
     return hipGetLastError();
 }
 

@@ -1446,7 +1446,9 @@ __global__ __launch_bounds__(kStep2Waves * 64) void attend_kernel(AttendArgs a)
 // (sequence, or sequence x q-block, times KV head).  For a decode row the
 // blocks are those of the L tokens; for q-block r of a chunk of Lq queries
 // they end at the block of the q-block's last query, L - Lq + min(64r + 64, Lq) - 1.
-__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ scores_in,
+constexpr int kSelThreads = 512;  // eight waves: a row of up to 4096 blocks in registers
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ scores_in,
                                                      int32_t* __restrict__ sel,
                                                      int32_t* __restrict__ cnt,
                                                      const int32_t* __restrict__ cu_k,
@@ -1474,16 +1476,16 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
     // go to the selector in registers, every score to LDS
     const float* row = scores_in + pair * max_nb;
     uint32_t keys[kSelKeyRounds];
-    for (int b0 = 0; b0 < nb; b0 += kSelKeyRounds * 256) {
+    for (int b0 = 0; b0 < nb; b0 += kSelKeyRounds * kSelThreads) {
         float v[kSelKeyRounds];
 #pragma unroll
         for (int i = 0; i < kSelKeyRounds; ++i) {
-            const int b = b0 + i * 256 + (int)threadIdx.x;
+            const int b = b0 + i * kSelThreads + (int)threadIdx.x;
             v[i] = b < nb ? row[b] : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < kSelKeyRounds; ++i) {
-            const int b = b0 + i * 256 + (int)threadIdx.x;
+            const int b = b0 + i * kSelThreads + (int)threadIdx.x;
             if (b < nb) sI[b] = v[i];
             if (b0 == 0) keys[i] = order_key(v[i]);
         }
@@ -1492,9 +1494,9 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
 #pragma unroll
         for (int i = 0; i < kSelKeyRounds; ++i) keys[i] = 0u;
     }
-    select_lds_clear<256>(sh);
+    select_lds_clear<kSelThreads>(sh);
     __syncthreads();
-    select_blocks_wg<4, true>(keys, sI, nb, wblocks, topk, sh, sel + pair * max_sel, cnt + pair,
+    select_blocks_wg<kSelThreads / 64, true>(keys, sI, nb, wblocks, topk, sh, sel + pair * max_sel, cnt + pair,
                               max_sel, nullptr, 0, 0, nullptr);
 }
 
@@ -1851,7 +1853,7 @@ hipError_t launch_select(const Plan& pl, const int32_t* cu_k, const int32_t* cu_
 {
     const size_t lds = sizeof(float) * (size_t)(pl.max_nb > 0 ? pl.max_nb : 1);
     const int max_qblk = cu_q ? ceil_div(max_seqlen_q, 64) : 1;
-    hipLaunchKernelGGL(select_kernel, dim3(pl.Hkv, pl.B * max_qblk), dim3(256), lds, stream,
+    hipLaunchKernelGGL(select_kernel, dim3(pl.Hkv, pl.B * max_qblk), dim3(kSelThreads), lds, stream,
                        scores_in, sel, cnt, cu_k, cu_q, max_seqlen_q, max_qblk, pl.Lmax, pl.Hkv,
                        pl.max_nb, pl.max_sel, pl.topk, pl.wblocks);
     return hipGetLastError();

@@ -29,8 +29,8 @@ namespace nosa {
 // library has none of this): thread 0 of each workgroup of the prefill
 // launches (0: scoring pass 1, 1: pass 2, 2: attention, 3: pooling,
 // 4: merge of split attention) stamps the wall clock when the workgroup
-// starts and when it leaves the kernel, and records its XCD, in
-// pf_tl[launch][workgroup][0 .. 2].
+// starts and when it leaves the kernel, and records its XCD and its
+// hardware id (CU, SIMD, wave slot), in pf_tl[launch][workgroup][0 .. 3].
 #ifdef NOSA_TIMELINE
 constexpr int kPfTlGroups = 8192;
 __device__ unsigned long long pf_tl[5][kPfTlGroups][4];
@@ -41,7 +41,8 @@ struct PfTlScope {
         __builtin_amdgcn_sched_barrier(0);
         if (threadIdx.x == 0 && blockIdx.x < kPfTlGroups) {
             pf_tl[launch][blockIdx.x][0] = wall_clock64();
-            pf_tl[launch][blockIdx.x][2] = (unsigned)__builtin_amdgcn_s_getreg(30740);
+            pf_tl[launch][blockIdx.x][2] = (unsigned)__builtin_amdgcn_s_getreg(30740);  // XCC_ID
+            pf_tl[launch][blockIdx.x][3] = (unsigned)__builtin_amdgcn_s_getreg(63492);  // HW_ID
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -185,6 +186,25 @@ __device__ __forceinline__ float row_lse(const float2* __restrict__ pp, int n)
         m = mb;
     }
     return acc > 0.f ? m + log2f(acc) : INFINITY;
+}
+
+// Wave priority from a workgroup's progress through its steps (done of
+// total, wave-uniform): 3 in the first half, 2 to three quarters, 1 to seven
+// eighths, 0 in the last eighth.  Two workgroups share each CU, and at equal
+// priority a SIMD issues the older wave first: the first-dispatched
+// workgroup of every CU would finish well ahead of the other, which then runs
+// alone on the CU.  Ranking the waves by progress lets the one behind catch
+// up at each threshold, so they part only in the last eighth.
+__device__ __forceinline__ void progress_priority(int done, int total)
+{
+    if (2 * done < total)
+        __builtin_amdgcn_s_setprio(3);
+    else if (4 * done < 3 * total)
+        __builtin_amdgcn_s_setprio(2);
+    else if (8 * done < 7 * total)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
 }
 
 // Workgroup = 4 waves x RTW row tiles of 16 rows, over the `span` pooled keys
@@ -371,6 +391,7 @@ __global__ __launch_bounds__(256, 2) void pf_score_kernel(PfArgs a)
         auto chunk = [&](int c, const uint4* __restrict__ cur, uint4* __restrict__ nxt) {
             wait_lds_copies();
             __syncthreads();  // chunk c in LDS; every wave done with chunk c - 1
+            progress_priority(c, nchunks);
             if (c + 1 < nchunks) copy_chunk(c + 1, nxt);
             const int c0 = key_lo + c * kChunk, c1 = min(c0 + kChunk, key_hi);
             float m_chk[RTW], s_chk[RTW];
@@ -516,6 +537,7 @@ __global__ __launch_bounds__(256, 2) void pf_score_kernel(PfArgs a)
         auto chunk = [&](int c, const uint4* __restrict__ cur, uint4* __restrict__ nxt) {
             wait_lds_copies();
             __syncthreads();  // chunk c in LDS; every wave done with chunk c - 1
+            progress_priority(c, nchunks);
             if (c + 1 < nchunks) copy_chunk(c + 1, nxt);
             if (c > 0) store_chunk(c - 1);
             const int c0 = key_lo + c * kChunk, c1 = min(c0 + kChunk, key_hi), cb = c & 1;
@@ -805,6 +827,7 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
                     uint16_t* __restrict__ kn, uint16_t* __restrict__ vn) {
         wait_lds_copies();
         __syncthreads();  // page idx in LDS; every wave done with page idx - 1
+        progress_priority(idx - i0, i1 - i0);
         if (idx + 1 < i1) copy_page(idx + 1, kn, vn);
         const int b = list[idx].x;
         if (b >= 0) compute(kc, vc, b);

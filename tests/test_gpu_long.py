@@ -82,8 +82,8 @@ def test_block_scores_decode_mode_varlen():
 def test_select_long_shared_scores(lens, topk):
     """The stand-alone selection on fp32 scores shared with the reference,
     values in a handful of levels (heavy exact ties: lower block index wins),
-    up to 8192 blocks (32 candidate rounds of the selector, 24 of them read
-    from LDS): identical sets and counts."""
+    up to 8192 blocks (16 candidate rounds of the eight-wave selector, 8 of
+    them read from LDS): identical sets and counts."""
     log(f"case: select on shared scores, lengths {lens}, topk {topk}")
     rng = np.random.default_rng(topk)
     max_nb = (max(lens) + 63) // 64

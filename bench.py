@@ -1414,7 +1414,7 @@ def timeline_prefill_main(w, args):
     for _ in range(3):
         chain()
     torch.cuda.synchronize()
-    names = {0: "scoring_pass1", 1: "scoring_pass2", 3: "pooling", 2: "attention", 4: "merge"}
+    names = {0: "scoring_pass1", 1: "scoring_pass2", 3: "pooling", 2: "attention"}
     stamps = np.zeros((8192, 4), dtype=np.uint64)
     runs = []
     for rep in range(5):
@@ -1422,7 +1422,7 @@ def timeline_prefill_main(w, args):
         chain()
         torch.cuda.synchronize()
         t0, r = None, {}
-        for k in (0, 1, 3, 2, 4):
+        for k in (0, 1, 3, 2):
             assert L.nosa_timeline_read_prefill(k, stamps.ctypes.data) == 0
             done = stamps[(stamps[:, 0] > 0) & (stamps[:, 1] > 0)].astype(np.float64) * 1e3 / khz
             if len(done) == 0:

@@ -73,16 +73,12 @@ struct PfPlan {
     int span = 0;         // pooled keys per such workgroup (a multiple of 128)
     int attn_groups = 0;  // attention workgroups (128 rows each) per pair
     size_t off_part = 0, off_colsum = 0, off_rlse = 0, bytes = 0;
-    // split attention (launches of at most kPfSplitGroups workgroups): the
-    // halves' partials after the scoring scratch; bytes_split = the workspace
-    // that holds them (bytes when no launch of this plan can split)
-    size_t off_po = 0, off_pml = 0, bytes_split = 0;
-    int split_rows = 0;  // rows per pair in the partials: min(64, max_seqlen_q) * G
 };
 constexpr int kPfScoreWorkgroups = 512;  // scoring workgroups a launch aims for
 constexpr int kPfChunk = 128;           // pooled keys the scoring passes stage in LDS at a time
 constexpr int kPfMaxSpanChunks = 16;    // chunks per scoring workgroup at most
-constexpr int kPfSplitGroups = 256;  // one workgroup per CU or fewer: split the pages
+constexpr int kPfSplitGroups = 256;  // one workgroup per CU or fewer: split each row group's pages
+constexpr size_t kPfLdsBytes = 160 * 1024;  // LDS a gfx950 workgroup may use
 
 // Offloaded KV (device pointers; the host pools as the device sees them).
 struct Offload {
@@ -136,13 +132,11 @@ hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_k
                             const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
                             void* ws, float* scores, hipStream_t stream,
                             const int32_t* qbase = nullptr);
-// ws / ws_bytes: workspace for the split attention's partials (may be null:
-// then the attention is not split).
+// Needs no workspace.
 hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
                             const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
                             const int32_t* sel, const int32_t* cnt, float* out, float* lse,
-                            void* ws, size_t ws_bytes, hipStream_t stream,
-                            const int32_t* qbase = nullptr);
+                            hipStream_t stream, const int32_t* qbase = nullptr);
 
 // Whole-prompt prefill, chunk by chunk (nosa_prefill.hip).
 hipError_t launch_chunk_setup(const int32_t* cu, int B, int Lmax, int c, int C, int32_t* cu_k_c,

@@ -14,7 +14,8 @@
 //   * exact attention of every query over the kept blocks, causal (t <= p).
 // Kernels: pf_score_kernel<1> (per-row (max, sum exp2) partials per key
 // split), pf_score_kernel<2> (column sums of exp2(z - lse_row) per key),
-// pf_pool_kernel (block importance), the shared selector, pf_attend_kernel.
+// pf_pool_kernel (block importance), the shared selector, pf_attend_kernel
+// or, for launches of one workgroup per CU or fewer, pf_attend_halves_kernel.
 // All contractions run on v_mfma_f32_16x16x32_bf16 with rows = (query, head)
 // pairs of the block in tiles of 16.
 #include <hip/hip_runtime.h>
@@ -27,13 +28,13 @@ namespace nosa {
 
 // Timeline build (NOSA_TIMELINE, the benchmark's timeline mode; the NOSA
 // library has none of this): thread 0 of each workgroup of the prefill
-// launches (0: scoring pass 1, 1: pass 2, 2: attention, 3: pooling,
-// 4: merge of split attention) stamps the wall clock when the workgroup
+// launches (0: scoring pass 1, 1: pass 2, 2: attention, 3: pooling)
+// stamps the wall clock when the workgroup
 // starts and when it leaves the kernel, and records its XCD and its
 // hardware id (CU, SIMD, wave slot), in pf_tl[launch][workgroup][0 .. 3].
 #ifdef NOSA_TIMELINE
 constexpr int kPfTlGroups = 8192;
-__device__ unsigned long long pf_tl[5][kPfTlGroups][4];
+__device__ unsigned long long pf_tl[4][kPfTlGroups][4];
 struct PfTlScope {
     int launch;
     __device__ explicit PfTlScope(int l) : launch(l)
@@ -92,12 +93,6 @@ struct PfArgs {
     int max_sel;
     float* out;  // [total_q][Hq][D]
     float* lse;  // [total_q][Hq] or null
-    // attention split over two workgroups per row group (ksplit = 2): each
-    // attends half of the kept pages and leaves unnormalised partials
-    int ksplit;
-    int rp;       // rows per pair in the partials: min(64, Lqmax) * G
-    float* po;    // [pairs][rp][2][D]
-    float2* pml;  // [pairs][rp][2] (max, sum) in log2 units
 };
 
 // Geometry of one pair.
@@ -637,22 +632,214 @@ __global__ __launch_bounds__(256) void pf_pool_kernel(PfArgs a, int slices)
 // wave's fragment read is 1 KB of consecutive LDS.
 typedef uint16_t PfPageBuf[BS * D];
 
+// One wave's rows of a row group: two row tiles of 16 (query, head) rows, the
+// query operand of each, and the online-softmax state of each row (lane r of
+// each tile): m_run, the reference point of the exponentials (log2 units),
+// l_run, the lane's part of sum 2^(z - m_run), and O^T (lane: row r, channels
+// 16 nt + 4 kq + e).  The reference moves only when a row's maximum passes it
+// by more than kPfRescale, so exponentials stay below 2^kPfRescale and the
+// accumulators are rarely rescaled; any reference gives the same quotient
+// O / l and lse = m + log2 l.
+struct PfAttnRows {
+    bf16x8 qb[2][4];
+    int qpos[2];  // query position of the row (-1: no query)
+    int qrow[2];  // its row of q, out and lse (-1: no query)
+    float m_run[2], l_run[2];
+    f32x4 o[2][8];
+};
+
+// The pair's (block, page) list into LDS (entries outside the pair's blocks
+// become (-1, 0)); returns the number of entries.
+__device__ __forceinline__ int pf_attn_list(const PfArgs& a, const PfPair& P, int pair, int2* list,
+                                            int tid, int nt)
+{
+    const int32_t* trow = a.table + (size_t)P.s * a.max_blocks;
+    const int n = P.empty ? 0 : min(a.cnt[pair], a.max_sel);
+    const int32_t* sl = a.sel + (size_t)pair * a.max_sel;
+    for (int x = tid; x < n; x += nt) {
+        int b = sl[x];
+        if (b < 0 || b >= P.nb) b = -1;
+        list[x] = make_int2(b, b >= 0 ? trow[b] : 0);
+    }
+    return n;
+}
+
+// Query operands of row tiles tile0 and tile0 + 1 of the pair, and an empty
+// softmax state.
+__device__ __forceinline__ void pf_attn_rows_init(PfAttnRows& R, const PfArgs& a, const PfPair& P,
+                                                  int tile0, int r, int kq)
+{
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int row = (tile0 + u) * 16 + r;
+        const int qi = row / a.G, h = row % a.G;
+        const bool ok = !P.empty && row < a.rows && qi < P.nq;
+        R.qpos[u] = ok ? P.p0 + qi : -1;
+        R.qrow[u] = ok ? (P.q0 + kQB * P.r + qi) * a.Hq + P.g * a.G + h : -1;
+        const uint16_t* qr = a.q + (size_t)(ok ? R.qrow[u] : 0) * D;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            uint4 w = ok ? ldg16(qr + st * 32 + kq * 8) : make_uint4(0, 0, 0, 0);
+            R.qb[u][st] = as_bf16x8(w);
+        }
+        R.m_run[u] = -INFINITY;
+        R.l_run[u] = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) R.o[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// Smallest query position of the wave's rows (pages entirely at or before it
+// need no causal mask), wave-uniform.
+__device__ __forceinline__ int pf_attn_pmin(const PfAttnRows& R)
+{
+    int pmin = min(R.qpos[0] < 0 ? 0x7fffffff : R.qpos[0], R.qpos[1] < 0 ? 0x7fffffff : R.qpos[1]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) pmin = min(pmin, __shfl_xor(pmin, off));
+    return __builtin_amdgcn_readfirstlane(pmin);
+}
+
+// Page idx of the list into LDS by the four waves wq = 0 .. 3 of a page's
+// readers: wave wq copies the 1 KB runs wq, wq + 4, wq + 8, wq + 12 of the K
+// and of the V page (past the list, page 0 is copied and never used).
+__device__ __forceinline__ void pf_copy_page(const PfArgs& a, const PfPair& P, const int2* list, int n,
+                                             int idx, int wq, int lane, uint16_t* __restrict__ kd,
+                                             uint16_t* __restrict__ vd)
+{
+    const int page = __builtin_amdgcn_readfirstlane(idx < n ? list[idx].y : 0);
+    const size_t base = ((size_t)page * a.Hkv + P.g) * BS * D + lane * 8;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+        const int c = __builtin_amdgcn_readfirstlane(wq) + 4 * c4;
+        __builtin_amdgcn_global_load_lds(a.k_pool + base + c * 512,
+                                         (__attribute__((address_space(3))) void*)(kd + c * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(a.v_pool + base + c * 512,
+                                         (__attribute__((address_space(3))) void*)(vd + c * 512), 16, 0, 0);
+    }
+}
+
+// maximum over the four lanes of a row (lanes r, r + 16, r + 32, r + 48)
+__device__ __forceinline__ float lanes4_max(float x)
+{
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = vmax3(__uint_as_float(h[0]), __uint_as_float(h[1]), -INFINITY);
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return vmax3(__uint_as_float(q[0]), __uint_as_float(q[1]), -INFINITY);
+}
+
+// The wave's rows over block b_cur, whose K and V pages are in LDS (kc, vc):
+// rows_full = every row of the workgroup holds a query, pmin = the wave's
+// smallest query position.
+__device__ __forceinline__ void pf_attn_page(PfAttnRows& R, const PfPair& P, float sc, bool rows_full,
+                                             int pmin, int lane, const uint16_t* __restrict__ kc,
+                                             const uint16_t* __restrict__ vc, int b_cur)
+{
+    const int kq = lane >> 4;
+    // S^T = K q^T, raw products: lane holds row r, keys of tile t as
+    // mapped by the K page layout; K fragments from LDS, shared
+    float x[2][4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        bf16x8 kf[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            kf[st] = as_bf16x8(*reinterpret_cast<const uint4*>(kc + ((t * 4 + st) * 64 + lane) * 8));
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) acc = mfma16(kf[st], R.qb[u][st], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[u][t][i] = acc[i];
+        }
+    }
+    if (!(rows_full && b_cur * BS + BS - 1 <= pmin && b_cur * BS + BS <= P.L)) {
+        // causal and length mask (page near the diagonal, the sequence
+        // end, or rows without a query)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tk = b_cur * BS + 32 * (t >> 1) + 8 * kq + 4 * (t & 1) + i;
+                    if (!(R.qpos[u] >= 0 && tk <= R.qpos[u] && tk < P.L)) x[u][t][i] = -INFINITY;
+                }
+    }
+    bf16x8 pa[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        float bm = vmax3(vmax3(x[u][0][0], x[u][0][1], x[u][0][2]), x[u][0][3], -INFINITY);
+#pragma unroll
+        for (int t = 1; t < 4; ++t) bm = vmax3(vmax3(bm, x[u][t][0], x[u][t][1]), x[u][t][2], x[u][t][3]);
+        bm = lanes4_max(bm) * sc;  // the row's maximum, log2 units
+        if (__ballot(bm > R.m_run[u] + kPfRescale) != 0) {
+            const float m_new = fmaxf(R.m_run[u], bm);
+            // 1 for an unmoved row (also one still at -inf), 0 from -inf
+            const float alpha = m_new == R.m_run[u] ? 1.f : fexp2(R.m_run[u] - m_new);
+            R.l_run[u] *= alpha;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) R.o[u][nt][e] *= alpha;
+            R.m_run[u] = m_new;
+        }
+        // a row with nothing visible yet (m_run = -inf) has every z = -inf
+        const float nm = R.m_run[u] == -INFINITY ? 0.f : -R.m_run[u];
+        float psum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = fexp2(fmaf(x[u][t][i], sc, nm));
+                x[u][t][i] = e;
+                psum += e;
+            }
+        R.l_run[u] += psum;
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pa[u][uu][i] = (__bf16)x[u][2 * uu][i];
+                pa[u][uu][4 + i] = (__bf16)x[u][2 * uu + 1][i];
+            }
+    }
+    // O^T += V^T P^T (operands swapped): lane holds row r, channels
+    // 16 nt + 4 kq + e; V fragments from LDS, shared by both row tiles
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4*>(vc + ((uu * 8 + nt) * 64 + lane) * 8));
+#pragma unroll
+            for (int u = 0; u < 2; ++u) R.o[u][nt] = mfma16(vf, pa[u][uu], R.o[u][nt]);
+        }
+}
+
+// A row's sum of 2^(z - m_run) over its four lanes.
+__device__ __forceinline__ float pf_row_sum(float l)
+{
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    return l;
+}
+
+// Workgroups are dealt to the eight XCDs round-robin by index, so index b is
+// mapped to the logical workgroup (b % 8) * per_xcd + b / 8: the attn_groups
+// workgroups of a pair, which read the same pages, run on one XCD and share
+// its L2.  Indices past the last logical workgroup exit at once.
+__device__ __forceinline__ int pf_attn_lid(int per_xcd)
+{
+    return (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+}
+
 // Workgroup = 4 waves x 2 row tiles (128 rows) of one pair; loops over the
 // pair's kept pages, each staged once through LDS for all 8 row tiles.  The
 // (block, page) list goes to LDS first; page i + 1 is copied by direct
 // global-to-LDS loads into the other buffer while page i is computed, so one
 // barrier per page suffices (the two buffers are distinct objects: a read
-// of one is known not to wait for the copy into the other).
-//
-// Workgroups are dealt to the eight XCDs round-robin by index, so index b is
-// mapped to the logical workgroup (b % 8) * per_xcd + b / 8: the attn_groups
-// workgroups of a pair, which read the same pages, run on one XCD and share
-// its L2.  Indices past the last logical workgroup exit at once.
-//
-// With ksplit = 2 (a launch that would not give every CU two workgroups:
-// one workgroup's pages are then a latency-bound chain), logical workgroup
-// 2w + k attends the k-th half of row group w's pages and stores its
-// unnormalised partial; pf_merge_kernel combines the two.
+// of one is known not to wait for the copy into the other).  For launches of
+// more than kPfSplitGroups workgroups (two or more per CU).
 __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_groups, int total,
                                                         int per_xcd)
 {
@@ -660,246 +847,157 @@ __global__ __launch_bounds__(256, 2) void pf_attend_kernel(PfArgs a, int attn_gr
     __shared__ PfPageBuf k_even, v_even, k_odd, v_odd;
     extern __shared__ __align__(16) char smem[];
     int2* list = reinterpret_cast<int2*>(smem);  // [max_sel] (block, page)
-    const int lid_k = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-    if (lid_k >= total * a.ksplit) return;
-    const int lid = lid_k / a.ksplit, ks = lid_k % a.ksplit;
+    const int lid = pf_attn_lid(per_xcd);
+    if (lid >= total) return;
     const int pair = lid / attn_groups, ag = lid % attn_groups;
     const PfPair P = pf_pair(a, pair);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int r = lane & 15, kq = lane >> 4;
-    const int32_t* trow = a.table + (size_t)P.s * a.max_blocks;
-    const int n = P.empty ? 0 : min(a.cnt[pair], a.max_sel);
-    const int32_t* sl = a.sel + (size_t)pair * a.max_sel;
-    for (int x = tid; x < n; x += 256) {
-        int b = sl[x];
-        if (b < 0 || b >= P.nb) b = -1;
-        list[x] = make_int2(b, b >= 0 ? trow[b] : 0);
-    }
-
-    bf16x8 qb[2][4];
-    int qpos[2];
-    int qrow[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int row = ((ag * 4 + wave) * 2 + u) * 16 + r;
-        const int qi = row / a.G, h = row % a.G;
-        const bool ok = !P.empty && row < a.rows && qi < P.nq;
-        qpos[u] = ok ? P.p0 + qi : -1;
-        qrow[u] = ok ? (P.q0 + kQB * P.r + qi) * a.Hq + P.g * a.G + h : -1;
-        const uint16_t* qr = a.q + (size_t)(ok ? qrow[u] : 0) * D;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            uint4 w = ok ? ldg16(qr + st * 32 + kq * 8) : make_uint4(0, 0, 0, 0);
-            qb[u][st] = as_bf16x8(w);
-        }
-    }
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-    f32x4 o[2][8];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) o[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int n = pf_attn_list(a, P, pair, list, tid, 256);
+    PfAttnRows R;
+    pf_attn_rows_init(R, a, P, (ag * 4 + wave) * 2, lane & 15, lane >> 4);
     __syncthreads();  // the list
-
-    // page idx of the list into LDS: wave w copies the 1 KB runs w, w + 4,
-    // w + 8, w + 12 of the K and of the V page (past the list, page 0 is
-    // copied and never used)
-    auto copy_page = [&](int idx, uint16_t* __restrict__ kd, uint16_t* __restrict__ vd) {
-        const int page = __builtin_amdgcn_readfirstlane(idx < n ? list[idx].y : 0);
-        const size_t base = ((size_t)page * a.Hkv + P.g) * BS * D + lane * 8;
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            const int c = __builtin_amdgcn_readfirstlane(wave) + 4 * c4;
-            __builtin_amdgcn_global_load_lds(a.k_pool + base + c * 512,
-                                             (__attribute__((address_space(3))) void*)(kd + c * 512), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(a.v_pool + base + c * 512,
-                                             (__attribute__((address_space(3))) void*)(vd + c * 512), 16, 0, 0);
-        }
-    };
-    // every row of the workgroup holds a query, and the smallest position:
-    // pages entirely at or before it need no causal mask
-    const bool rows_full = __syncthreads_and(qpos[0] >= 0 && qpos[1] >= 0);
-    int pmin = min(qpos[0] < 0 ? 0x7fffffff : qpos[0], qpos[1] < 0 ? 0x7fffffff : qpos[1]);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) pmin = min(pmin, __shfl_xor(pmin, off));
-    pmin = __builtin_amdgcn_readfirstlane(pmin);  // per wave (its own rows)
+    const bool rows_full = __syncthreads_and(R.qpos[0] >= 0 && R.qpos[1] >= 0);
+    const int pmin = pf_attn_pmin(R);
     const float sc = a.scale_log2;
-    // maximum over the four lanes of a row (lanes r, r + 16, r + 32, r + 48)
-    auto lanes4_max = [](float x) {
-        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        x = vmax3(__uint_as_float(h[0]), __uint_as_float(h[1]), -INFINITY);
-        const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        return vmax3(__uint_as_float(q[0]), __uint_as_float(q[1]), -INFINITY);
-    };
-    // Softmax state per row (lane r of each row tile): m_run, the reference
-    // point of the exponentials (log2 units), and l_run, the lane's part of
-    // sum 2^(z - m_run).  The reference moves only when a row's maximum
-    // passes it by more than kPfRescale, so exponentials stay below
-    // 2^kPfRescale and the accumulators are rarely rescaled; any reference
-    // gives the same quotient O / l and lse = m + log2 l.
-    auto compute = [&](const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int b_cur) {
-        // S^T = K q^T, raw products: lane holds row r, keys of tile t as
-        // mapped by the K page layout; K fragments from LDS, shared
-        float x[2][4][4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            bf16x8 kf[4];
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-                kf[st] = as_bf16x8(*reinterpret_cast<const uint4*>(kc + ((t * 4 + st) * 64 + lane) * 8));
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int st = 0; st < 4; ++st) acc = mfma16(kf[st], qb[u][st], acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x[u][t][i] = acc[i];
-            }
-        }
-        if (!(rows_full && b_cur * BS + BS - 1 <= pmin && b_cur * BS + BS <= P.L)) {
-            // causal and length mask (page near the diagonal, the sequence
-            // end, or rows without a query)
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int tk = b_cur * BS + 32 * (t >> 1) + 8 * kq + 4 * (t & 1) + i;
-                        if (!(qpos[u] >= 0 && tk <= qpos[u] && tk < P.L)) x[u][t][i] = -INFINITY;
-                    }
-        }
-        bf16x8 pa[2][2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            float bm = vmax3(vmax3(x[u][0][0], x[u][0][1], x[u][0][2]), x[u][0][3], -INFINITY);
-#pragma unroll
-            for (int t = 1; t < 4; ++t) bm = vmax3(vmax3(bm, x[u][t][0], x[u][t][1]), x[u][t][2], x[u][t][3]);
-            bm = lanes4_max(bm) * sc;  // the row's maximum, log2 units
-            if (__ballot(bm > m_run[u] + kPfRescale) != 0) {
-                const float m_new = fmaxf(m_run[u], bm);
-                // 1 for an unmoved row (also one still at -inf), 0 from -inf
-                const float alpha = m_new == m_run[u] ? 1.f : fexp2(m_run[u] - m_new);
-                l_run[u] *= alpha;
-#pragma unroll
-                for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[u][nt][e] *= alpha;
-                m_run[u] = m_new;
-            }
-            // a row with nothing visible yet (m_run = -inf) has every z = -inf
-            const float nm = m_run[u] == -INFINITY ? 0.f : -m_run[u];
-            float psum = 0.f;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float e = fexp2(fmaf(x[u][t][i], sc, nm));
-                    x[u][t][i] = e;
-                    psum += e;
-                }
-            l_run[u] += psum;
-#pragma unroll
-            for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pa[u][uu][i] = (__bf16)x[u][2 * uu][i];
-                    pa[u][uu][4 + i] = (__bf16)x[u][2 * uu + 1][i];
-                }
-        }
-        // O^T += V^T P^T (operands swapped): lane holds row r, channels
-        // 16 nt + 4 kq + e; V fragments from LDS, shared by both row tiles
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                const bf16x8 vf =
-                    as_bf16x8(*reinterpret_cast<const uint4*>(vc + ((uu * 8 + nt) * 64 + lane) * 8));
-#pragma unroll
-                for (int u = 0; u < 2; ++u) o[u][nt] = mfma16(vf, pa[u][uu], o[u][nt]);
-            }
-    };
-
-    // this workgroup's pages: all, or half of them
-    const int i0 = n * ks / a.ksplit, i1 = n * (ks + 1) / a.ksplit;
-    if (i1 > i0) copy_page(i0, k_even, v_even);
+    if (n > 0) pf_copy_page(a, P, list, n, 0, wave, lane, k_even, v_even);
     auto step = [&](int idx, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                     uint16_t* __restrict__ kn, uint16_t* __restrict__ vn) {
         wait_lds_copies();
         __syncthreads();  // page idx in LDS; every wave done with page idx - 1
-        progress_priority(idx - i0, i1 - i0);
-        if (idx + 1 < i1) copy_page(idx + 1, kn, vn);
+        progress_priority(idx, n);
+        if (idx + 1 < n) pf_copy_page(a, P, list, n, idx + 1, wave, lane, kn, vn);
         const int b = list[idx].x;
-        if (b >= 0) compute(kc, vc, b);
+        if (b >= 0) pf_attn_page(R, P, sc, rows_full, pmin, lane, kc, vc, b);
     };
-    for (int idx = i0; idx < i1; idx += 2) {
+    for (int idx = 0; idx < n; idx += 2) {
         step(idx, k_even, v_even, k_odd, v_odd);
-        if (idx + 1 < i1) step(idx + 1, k_odd, v_odd, k_even, v_even);
+        if (idx + 1 < n) step(idx + 1, k_odd, v_odd, k_even, v_even);
     }
-    if (a.ksplit > 1) {  // unnormalised partial of this half, rows holding a query
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            float l = l_run[u];
-            l += __shfl_xor(l, 16);
-            l += __shfl_xor(l, 32);
-            if (qpos[u] < 0) continue;
-            const int row0 = ((ag * 4 + wave) * 2 + u) * 16;  // the row tile in the pair
-            const size_t pr = (size_t)pair * a.rp + row0 + r;
-            if (kq == 0) a.pml[pr * 2 + ks] = make_float2(m_run[u], l);
-            float* dst = a.po + (pr * 2 + ks) * D + 4 * kq;
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
-                *reinterpret_cast<float4*>(dst + nt * 16) = make_float4(o[u][nt][0], o[u][nt][1], o[u][nt][2], o[u][nt][3]);
-        }
-        return;
-    }
-
     // normalise and store: lane holds O[row r][channels 16 nt + 4 kq + e]
+    const int kq = lane >> 4;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        float l = l_run[u];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        if (qrow[u] < 0) continue;
+        const float l = pf_row_sum(R.l_run[u]);
+        if (R.qrow[u] < 0) continue;
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        if (kq == 0 && a.lse) a.lse[qrow[u]] = l > 0.f ? (m_run[u] + log2f(l)) * 0.69314718055994531f : -INFINITY;
-        float* dst = a.out + (size_t)qrow[u] * D + 4 * kq;
+        if (kq == 0 && a.lse) a.lse[R.qrow[u]] = l > 0.f ? (R.m_run[u] + log2f(l)) * kLn2 : -INFINITY;
+        float* dst = a.out + (size_t)R.qrow[u] * D + 4 * kq;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt)
             *reinterpret_cast<float4*>(dst + nt * 16) =
-                make_float4(o[u][nt][0] * inv, o[u][nt][1] * inv, o[u][nt][2] * inv, o[u][nt][3] * inv);
+                make_float4(R.o[u][nt][0] * inv, R.o[u][nt][1] * inv, R.o[u][nt][2] * inv, R.o[u][nt][3] * inv);
     }
 }
 
-// The two halves of a split attention: row x of row group w from partials
-// (m_k, l_k, o_k), k < 2, in log2 units: out = sum 2^(m_k - M) o_k / L,
-// L = sum 2^(m_k - M) l_k, lse = (M + log2 L) ln 2; a row that saw nothing
-// gets 0 and -inf.  Workgroup (w, y): rows 8y .. 8y + 7 of row group w, a
-// thread per (row, 4 channels).
-__global__ __launch_bounds__(256) void pf_merge_kernel(PfArgs a, int attn_groups, int total)
+// Static LDS of pf_attend_halves_kernel, rounded up: eight page buffers, half
+// 1's row states and alignment (the pick list comes on top, dynamically).
+constexpr size_t kPfHalvesLds = 8 * sizeof(PfPageBuf) + 4096;
+
+// For launches of at most kPfSplitGroups workgroups (one per CU or fewer, so
+// one row group's pages would be a latency-bound chain): workgroup = 8 waves
+// over the same 128 rows as pf_attend_kernel's, waves 0-3 (half 0) attending
+// the first n/2 kept pages and waves 4-7 (half 1) the rest, each half double
+// buffered in its own four page buffers.  Every wave runs the same number of
+// steps -- that of half 1, the longer half -- and of barriers, all outside
+// the branch on the half; a step past a half's last page only waits at the
+// barrier.  At the end half 1 leaves each row's (m, l) and O^T in LDS, and
+// half 0 combines the two states (a row's weights 2^(m_k - M), M the larger
+// reference), normalises and stores.  The two halves of a row group thus
+// share one CU and end together, and no partial goes through memory.
+__global__ __launch_bounds__(512, 1) void pf_attend_halves_kernel(PfArgs a, int attn_groups, int total,
+                                                               int per_xcd)
 {
-    PF_TL_SCOPE(4);
-    const int lid = blockIdx.x;
+    PF_TL_SCOPE(2);
+    __shared__ PfPageBuf k_even0, v_even0, k_odd0, v_odd0, k_even1, v_even1, k_odd1, v_odd1;
+    __shared__ float2 ml1[4][2][16];  // half 1's (m_run, row sum) per wave, row tile, row
+    extern __shared__ __align__(16) char smem[];
+    int2* list = reinterpret_cast<int2*>(smem);  // [max_sel] (block, page)
+    const int lid = pf_attn_lid(per_xcd);
     if (lid >= total) return;
     const int pair = lid / attn_groups, ag = lid % attn_groups;
     const PfPair P = pf_pair(a, pair);
-    const int row = ag * 128 + (int)blockIdx.y * 8 + (threadIdx.x >> 5), c4 = threadIdx.x & 31;
-    const int qi = row / a.G, h = row % a.G;
-    if (P.empty || row >= a.rows || qi >= P.nq) return;  // rows past the block's queries
-    const size_t pr = (size_t)pair * a.rp + row;
-    const float2 p0 = a.pml[pr * 2], p1 = a.pml[pr * 2 + 1];
-    const float4 o0 = reinterpret_cast<const float4*>(a.po + (pr * 2) * D)[c4];
-    const float4 o1 = reinterpret_cast<const float4*>(a.po + (pr * 2 + 1) * D)[c4];
-    const float M = fmaxf(p0.x, p1.x);
-    const float w0 = p0.x == -INFINITY ? 0.f : fexp2(p0.x - M);
-    const float w1 = p1.x == -INFINITY ? 0.f : fexp2(p1.x - M);
-    const float L = w0 * p0.y + w1 * p1.y;
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const size_t qrow = (size_t)(P.q0 + kQB * P.r + qi) * a.Hq + P.g * a.G + h;
-    reinterpret_cast<float4*>(a.out + qrow * D)[c4] =
-        make_float4((w0 * o0.x + w1 * o1.x) * inv, (w0 * o0.y + w1 * o1.y) * inv,
-                    (w0 * o0.z + w1 * o1.z) * inv, (w0 * o0.w + w1 * o1.w) * inv);
-    if (a.lse && c4 == 0) a.lse[qrow] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = wave >> 2, wq = wave & 3;
+    const int r = lane & 15, kq = lane >> 4;
+    const int n = pf_attn_list(a, P, pair, list, tid, 512);
+    PfAttnRows R;
+    pf_attn_rows_init(R, a, P, (ag * 4 + wq) * 2, r, kq);
+    __syncthreads();  // the list
+    const bool rows_full = __syncthreads_and(R.qpos[0] >= 0 && R.qpos[1] >= 0);
+    const int pmin = pf_attn_pmin(R);
+    const float sc = a.scale_log2;
+    const int i0 = half ? n / 2 : 0, i1 = half ? n : n / 2;  // this half's list entries
+    const int steps = n - n / 2;                             // half 1's count, >= half 0's
+    // step j of this half without its barrier: the next page's copy, then
+    // entry i0 + j (if the half has it) from kc, vc
+    auto work = [&](int j, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                    uint16_t* __restrict__ kn, uint16_t* __restrict__ vn) {
+        const int idx = i0 + j;
+        if (idx + 1 < i1) pf_copy_page(a, P, list, n, idx + 1, wq, lane, kn, vn);
+        if (idx < i1) {
+            const int b = list[idx].x;
+            if (b >= 0) pf_attn_page(R, P, sc, rows_full, pmin, lane, kc, vc, b);
+        }
+    };
+    // one copy of the step for both halves, on pointers selected by the half
+    // (two inlined copies, one per half, would not fit the registers); each
+    // pointer is one of two distinct buffers, so a read of the current page
+    // is still known not to wait for the copy into the other
+    uint16_t* const ke = half ? k_even1 : k_even0;
+    uint16_t* const ve = half ? v_even1 : v_even0;
+    uint16_t* const ko = half ? k_odd1 : k_odd0;
+    uint16_t* const vo = half ? v_odd1 : v_odd0;
+    if (i1 > i0) pf_copy_page(a, P, list, n, i0, wq, lane, ke, ve);
+    for (int j = 0; j < steps; j += 2) {
+        wait_lds_copies();
+        __syncthreads();  // step j's page in LDS; every wave done with step j - 1
+        work(j, ke, ve, ko, vo);
+        if (j + 1 < steps) {
+            wait_lds_copies();
+            __syncthreads();
+            work(j + 1, ko, vo, ke, ve);
+        }
+    }
+    float lsum[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) lsum[u] = pf_row_sum(R.l_run[u]);
+    wait_lds_copies();
+    __syncthreads();  // every wave done with the page buffers
+    // half 1's O^T of wave wq in its page buffer wq: float4 (u * 8 + nt) * 64 + lane
+    uint16_t* hand = wq == 0 ? k_even1 : wq == 1 ? v_even1 : wq == 2 ? k_odd1 : v_odd1;
+    float4* h4 = reinterpret_cast<float4*>(hand);
+    if (half) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+                h4[(u * 8 + nt) * 64 + lane] = make_float4(R.o[u][nt][0], R.o[u][nt][1], R.o[u][nt][2], R.o[u][nt][3]);
+            if (kq == 0) ml1[wq][u][r] = make_float2(R.m_run[u], lsum[u]);
+        }
+    }
+    __syncthreads();  // half 1's states in LDS
+    if (half) return;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        if (R.qrow[u] < 0) continue;
+        const float2 p1 = ml1[wq][u][r];
+        const float m0 = R.m_run[u];
+        const float M = fmaxf(m0, p1.x);
+        const float w0 = m0 == -INFINITY ? 0.f : fexp2(m0 - M);
+        const float w1 = p1.x == -INFINITY ? 0.f : fexp2(p1.x - M);
+        const float L = w0 * lsum[u] + w1 * p1.y;
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        if (kq == 0 && a.lse) a.lse[R.qrow[u]] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+        float* dst = a.out + (size_t)R.qrow[u] * D + 4 * kq;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const float4 o1 = h4[(u * 8 + nt) * 64 + lane];
+            *reinterpret_cast<float4*>(dst + nt * 16) =
+                make_float4((w0 * R.o[u][nt][0] + w1 * o1.x) * inv, (w0 * R.o[u][nt][1] + w1 * o1.y) * inv,
+                            (w0 * R.o[u][nt][2] + w1 * o1.z) * inv, (w0 * R.o[u][nt][3] + w1 * o1.w) * inv);
+        }
+    }
 }
 
 // ---------------------------------------------------------- launchers ---
@@ -978,7 +1076,7 @@ hipError_t launch_pf_scores(const Plan& pl, const PfPlan& pf, const nosa_paged_k
 hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_kv& kv,
                             const nosa_bf16* q, const int32_t* cu_q, const int32_t* cu_k,
                             const int32_t* sel, const int32_t* cnt, float* out, float* lse,
-                            void* ws, size_t ws_bytes, hipStream_t stream, const int32_t* qbase)
+                            hipStream_t stream, const int32_t* qbase)
 {
     PfArgs a = pf_args(pl, pf, &kv, q, cu_q, cu_k);
     a.qbase = qbase;
@@ -988,21 +1086,16 @@ hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_k
     a.lse = lse;
     const size_t lds = (size_t)(pl.max_sel > 0 ? pl.max_sel : 1) * sizeof(int2);
     const int total = pf.npairs * pf.attn_groups;
-    // split the pages of each row group over two workgroups when the launch
-    // has at most kPfSplitGroups of them and the workspace holds the partials
-    a.ksplit = total <= kPfSplitGroups && ws && ws_bytes >= pf.bytes_split ? 2 : 1;
-    if (a.ksplit > 1) {
-        a.rp = pf.split_rows;
-        a.po = reinterpret_cast<float*>(static_cast<char*>(ws) + pf.off_po);
-        a.pml = reinterpret_cast<float2*>(static_cast<char*>(ws) + pf.off_pml);
-    }
-    const int per_xcd = (total * a.ksplit + 7) / 8;
-    hipLaunchKernelGGL(pf_attend_kernel, dim3(8 * per_xcd), dim3(256), lds, stream, a, pf.attn_groups,
-                       total, per_xcd);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.ksplit == 1 || total == 0) return e;
-    hipLaunchKernelGGL(pf_merge_kernel, dim3(total, 16), dim3(256), 0, stream, a, pf.attn_groups,
-                       total);
+    const int per_xcd = (total + 7) / 8;
+    // the halves of each row group on one 8-wave workgroup when the launch
+    // would not give every CU two workgroups (and the pick list fits beside
+    // its page buffers)
+    if (total <= kPfSplitGroups && kPfHalvesLds + lds <= kPfLdsBytes)
+        hipLaunchKernelGGL(pf_attend_halves_kernel, dim3(8 * per_xcd), dim3(512), lds, stream, a,
+                           pf.attn_groups, total, per_xcd);
+    else
+        hipLaunchKernelGGL(pf_attend_kernel, dim3(8 * per_xcd), dim3(256), lds, stream, a,
+                           pf.attn_groups, total, per_xcd);
     return hipGetLastError();
 }
 
@@ -1061,7 +1154,7 @@ extern "C" {
 // Copies launch `launch`'s stamps ([8192][4] unsigned 64-bit) to host memory.
 int nosa_timeline_read_prefill(int launch, unsigned long long* host)
 {
-    if (launch < 0 || launch > 4 || !host) return (int)hipErrorInvalidValue;
+    if (launch < 0 || launch > 3 || !host) return (int)hipErrorInvalidValue;
     return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(nosa::pf_tl), sizeof(nosa::pf_tl[0]),
                                     (size_t)launch * sizeof(nosa::pf_tl[0]), hipMemcpyDeviceToHost);
 }

@@ -268,9 +268,7 @@ nosa_status nosa_select_blocks(const nosa_params* params, const float* block_sco
  * lse: device fp32 [total queries][Hq] (natural log of the softmax
  * denominator, -inf for a query that sees no token) or NULL.  Block ids must
  * be distinct and < nb_r.  Needs a `workspace` (see above) in decode; with
- * cu_seqlens_q the workspace is optional: given, a launch of few workgroups
- * splits each one's pages over two (their partials kept in it) and merges
- * them; NULL attends each row group's pages in one workgroup. */
+ * cu_seqlens_q none is used (workspace may be NULL). */
 nosa_status nosa_sparse_attend(const nosa_params* params, const nosa_paged_kv* kv,
                                const nosa_bf16* q, const int32_t* cu_seqlens_q,
                                const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,

@@ -33,8 +33,8 @@ hipError_t launch_pf_scores(const Plan&, const PfPlan&, const nosa_paged_kv&, co
                             const int32_t*, void*, float*, hipStream_t, const int32_t*)
 { reached("launch_pf_scores"); }
 hipError_t launch_pf_attend(const Plan&, const PfPlan&, const nosa_paged_kv&, const nosa_bf16*, const int32_t*,
-                            const int32_t*, const int32_t*, const int32_t*, float*, float*, void*, size_t,
-                            hipStream_t, const int32_t*)
+                            const int32_t*, const int32_t*, const int32_t*, float*, float*, hipStream_t,
+                            const int32_t*)
 { reached("launch_pf_attend"); }
 hipError_t launch_chunk_setup(const int32_t*, int, int, int, int, int32_t*, int32_t*, int32_t*, int32_t*, hipStream_t)
 { reached("launch_chunk_setup"); }

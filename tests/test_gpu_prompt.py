@@ -5,9 +5,9 @@ queries and keys; query blocks whose selection sits on a near-tie (relative
 gap below the tie band, where fp32 and fp64 may order two blocks differently)
 are compared through the stand-alone chain instead.  Different chunk sizes
 and the stand-alone chain select the same blocks; their outputs agree within
-the rounding of the attention weights (a launch of few workgroups splits each
-one's pages over two and merges the halves, and each half rounds its weights
-to bf16 relative to its own running maximum)."""
+the rounding of the attention weights (a launch of few workgroups attends each
+row group's pages in two halves and combines them, and each half rounds its
+weights to bf16 relative to its own running maximum)."""
 import math
 
 import numpy as np

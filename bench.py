@@ -245,6 +245,20 @@ def copy_bandwidth(nbytes=2 << 30, reps=5):
     return 2 * nbytes / (float(np.median(ts)) * 1e-3) / 1e9
 
 
+def device_record():
+    """The device's own figures as the HIP runtime reports them (hipDeviceProp
+    through torch), recorded beside the vendor peaks the fractions use."""
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    rec = {"name": pr.name, "arch": getattr(pr, "gcnArchName", None),
+           "compute_units": pr.multi_processor_count,
+           "hbm_bytes": int(pr.total_memory),
+           "l2_bytes": getattr(pr, "L2_cache_size", None),
+           "lds_bytes_per_workgroup": getattr(pr, "shared_memory_per_block", None),
+           "wave_size": getattr(pr, "warp_size", None)}
+    return {k: v for k, v in rec.items() if v is not None}
+
+
 def trace_average_us(path, kernel_prefix):
     """Average duration of a kernel in a committed kernel-trace summary, if
     the summary was taken on the current kernel sources."""
@@ -494,6 +508,7 @@ def main():
                         "traffic": recorded_traffic(w.name, "attention")},
         "other_workloads": extra or None,
         "cpu_baseline": cpu,
+        "device": device_record(),
     }
     print(json.dumps(res), flush=True)
 

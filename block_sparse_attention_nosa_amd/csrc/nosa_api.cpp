@@ -431,6 +431,25 @@ nosa_status nosa_block_scores(const nosa_params* params, const nosa_paged_kv* kv
                                          block_scores, as_stream(stream)));
 }
 
+nosa_status nosa_check_inputs(const nosa_params* params, const nosa_paged_kv* kv,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int32_t* flags, void* stream)
+{
+    nosa_status st = check_params(params);
+    if (st != NOSA_OK) return st;
+    st = check_sizes(batch, max_seqlen_q, max_seqlen_k);
+    if (st != NOSA_OK) return st;
+    if (!kv || !kv->block_table || !cu_seqlens_k || !flags) return NOSA_ERR_NULL;
+    if (kv->max_blocks_per_seq <= 0 || kv->num_pages <= 0) return NOSA_ERR_INVALID;
+    if ((long long)kv->max_blocks_per_seq * kBlock < (long long)max_seqlen_k) return NOSA_ERR_INVALID;
+    st = check_queries(cu_seqlens_q, max_seqlen_q);
+    if (st != NOSA_OK) return st;
+    return hip_status(launch_check_inputs(cu_seqlens_k, cu_seqlens_q, kv->block_table,
+                                          kv->max_blocks_per_seq, kv->num_pages, max_seqlen_k,
+                                          max_seqlen_q, batch, flags, as_stream(stream)));
+}
+
 nosa_status nosa_select_blocks(const nosa_params* params, const float* block_scores,
                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,

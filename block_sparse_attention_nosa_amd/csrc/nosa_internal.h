@@ -138,6 +138,12 @@ hipError_t launch_pf_attend(const Plan& pl, const PfPlan& pf, const nosa_paged_k
                             const int32_t* sel, const int32_t* cnt, float* out, float* lse,
                             hipStream_t stream, const int32_t* qbase = nullptr);
 
+// The device-side input checks of nosa_check_inputs: flags cleared, then one
+// workgroup per sequence ORs in the bits it finds.
+hipError_t launch_check_inputs(const int32_t* cu_k, const int32_t* cu_q, const int32_t* table,
+                               int max_blocks, int num_pages, int Lmax, int Lqmax, int batch,
+                               int32_t* flags, hipStream_t stream);
+
 // Whole-prompt prefill, chunk by chunk (nosa_prefill.hip).
 hipError_t launch_chunk_setup(const int32_t* cu, int B, int Lmax, int c, int C, int32_t* cu_k_c,
                               int32_t* cu_q_c, int32_t* valid_c, int32_t* qbase_c,

@@ -1502,6 +1502,53 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
 
 // ---------------------------------------------------------- launchers ---
 
+// Device-side input checks (nosa_check_inputs).  check_clear_kernel zeroes
+// the flags (a kernel, not a memset, so that a captured graph replays it
+// like the rest); then workgroup s of check_inputs_kernel tests sequence s:
+// its cu_seqlens entries and length (every thread, the same loads), and the
+// block-table entries of the blocks its clamped length holds (a thread per
+// entry), and ORs the bits found into *flags.  The table row is read only up
+// to nb(min(L_s, Lmax)) <= max_blocks entries.
+__global__ void check_clear_kernel(int32_t* flags) { *flags = 0; }
+
+__global__ __launch_bounds__(256) void check_inputs_kernel(const int32_t* __restrict__ cu_k,
+                                                           const int32_t* __restrict__ cu_q,
+                                                           const int32_t* __restrict__ table,
+                                                           int max_blocks, int num_pages, int Lmax,
+                                                           int Lqmax, int32_t* __restrict__ flags)
+{
+    const int s = blockIdx.x;
+    int f = 0;
+    const int k0 = cu_k[s], k1 = cu_k[s + 1];
+    if ((s == 0 && k0 != 0) || k1 < k0) f |= NOSA_CHECK_CU_K;
+    const long long Ls = (long long)k1 - k0;
+    if (Ls < 1 || Ls > Lmax) f |= NOSA_CHECK_LEN_K;
+    const int L = Ls < 0 ? 0 : (Ls > Lmax ? Lmax : (int)Ls);
+    if (cu_q) {
+        const int q0 = cu_q[s], q1 = cu_q[s + 1];
+        const long long Lq = (long long)q1 - q0;
+        if ((s == 0 && q0 != 0) || Lq < 0 || Lq > Lqmax || Lq > L) f |= NOSA_CHECK_CU_Q;
+    }
+    const int nb = (L + BS - 1) / BS;
+    const int32_t* row = table + (size_t)s * max_blocks;
+    for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+        const int pg = row[b];
+        if (pg < 0 || pg >= num_pages) f |= NOSA_CHECK_TABLE;
+    }
+    if (f) atomicOr(flags, f);
+}
+
+hipError_t launch_check_inputs(const int32_t* cu_k, const int32_t* cu_q, const int32_t* table,
+                               int max_blocks, int num_pages, int Lmax, int Lqmax, int batch,
+                               int32_t* flags, hipStream_t stream)
+{
+    hipLaunchKernelGGL(check_clear_kernel, dim3(1), dim3(1), 0, stream, flags);
+    if (batch > 0)
+        hipLaunchKernelGGL(check_inputs_kernel, dim3(batch), dim3(256), 0, stream, cu_k, cu_q, table,
+                           max_blocks, num_pages, Lmax, Lqmax, flags);
+    return hipGetLastError();
+}
+
 // Per-device attribute caches: an attribute is read once per device and kept
 // in an atomic slot (0 = not read yet), so concurrent first calls on several
 // threads at worst read it twice and store the same value.

@@ -93,6 +93,7 @@ def lib() -> ctypes.CDLL:
                                        i32, vp, vp, vp, vp, vp, vp, sz, vp],
             "nosa_offload_decode_step": [P, ctypes.POINTER(nosa_offload_kv), vp, vp, i32, i32, vp,
                                          vp, vp, vp, vp, vp, sz, vp],
+            "nosa_check_inputs": [P, KV, vp, vp, i32, i32, i32, vp, vp],
         }
         for name, argtypes in sigs.items():
             f = getattr(L, name)
@@ -182,6 +183,13 @@ def nosa_select_blocks(p, block_scores, cu_seqlens_q, cu_seqlens_k, batch, max_s
     _check("nosa_select_blocks", lib().nosa_select_blocks(
         ctypes.byref(p), _ptr(block_scores), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch,
         max_seqlen_q, max_seqlen_k, _ptr(sel_idx), _ptr(sel_count), _stream(stream)))
+
+
+def nosa_check_inputs(p, kv, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k,
+                      flags, stream=None):
+    _check("nosa_check_inputs", lib().nosa_check_inputs(
+        ctypes.byref(p), ctypes.byref(kv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch,
+        max_seqlen_q, max_seqlen_k, _ptr(flags), _stream(stream)))
 
 
 def nosa_sparse_attend(p, kv, q, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k,

@@ -26,7 +26,8 @@
  *     size grids without a device-to-host copy.  A device length above its
  *     bound, a non-monotone cu_seqlens or a block_table entry outside
  *     [0, num_pages) for a block the sequence holds is a contract violation
- *     that the library does not detect.  Entries past a sequence's last
+ *     that the other entry points do not detect (nosa_check_inputs does,
+ *     on the device, when asked).  Entries past a sequence's last
  *     block may hold anything (the row is read ahead of the length, and such
  *     entries are clamped into the pool and never used).
  *   - Host-checkable arguments are validated before anything is enqueued: a
@@ -76,7 +77,7 @@
 extern "C" {
 #endif
 
-#define NOSA_ABI_VERSION 4
+#define NOSA_ABI_VERSION 5
 
 typedef uint16_t nosa_bf16; /* bf16 bit pattern */
 
@@ -435,6 +436,34 @@ nosa_status nosa_layer_decode_step(const nosa_params* params, const nosa_front_p
                                    int32_t batch, int32_t max_seqlen_k, nosa_bf16* q_out,
                                    float* out, float* lse, int32_t* sel_idx, int32_t* sel_count,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Checks, on the device, the inputs the other entry points take on trust (the
+ * contract stated at the top of this header; no page defines it): for every
+ * sequence s, in one launch of a workgroup per sequence,
+ *   bit 0 (NOSA_CHECK_CU_K):  cu_seqlens_k[0] != 0 or cu_seqlens_k[s+1] <
+ *                             cu_seqlens_k[s];
+ *   bit 1 (NOSA_CHECK_LEN_K): L_s outside [1, max_seqlen_k];
+ *   bit 2 (NOSA_CHECK_TABLE): block_table[s][b] outside [0, num_pages) for a
+ *                             block b < nb(min(max(L_s, 0), max_seqlen_k));
+ *   bit 3 (NOSA_CHECK_CU_Q):  with cu_seqlens_q: cu_seqlens_q[0] != 0, a
+ *                             decreasing entry, or Lq_s outside
+ *                             [0, min(max_seqlen_q, L_s)].
+ * flags: device int32, set to the OR of the bits found (0: every check
+ * passed) when the work queued on `stream` is done; the caller reads it
+ * after synchronising.  Only the length arrays and the table entries of the
+ * blocks checked are read; no page is.  kv: only block_table,
+ * max_blocks_per_seq and num_pages are used (the pools may be NULL).
+ * cu_seqlens_q NULL checks a decode batch.  Errors: NOSA_ERR_NULL,
+ * NOSA_ERR_INVALID (sizes as in the other calls), NOSA_ERR_UNSUPPORTED,
+ * NOSA_ERR_HIP. */
+#define NOSA_CHECK_CU_K 1
+#define NOSA_CHECK_LEN_K 2
+#define NOSA_CHECK_TABLE 4
+#define NOSA_CHECK_CU_Q 8
+nosa_status nosa_check_inputs(const nosa_params* params, const nosa_paged_kv* kv,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int32_t* flags, void* stream);
 
 #ifdef __cplusplus
 }

@@ -43,6 +43,9 @@ hipError_t launch_front(const Plan&, const nosa_paged_kv&, const nosa_bf16*, con
                         const float*, const int32_t*, nosa_bf16*, hipStream_t)
 { reached("launch_front"); }
 hipError_t static_scratch(void**) { reached("static_scratch"); }
+hipError_t launch_check_inputs(const int32_t*, const int32_t*, const int32_t*, int, int, int, int, int, int32_t*,
+                               hipStream_t)
+{ reached("launch_check_inputs"); }
 }  // namespace nosa
 
 // no device: every pointer is "not device-readable host memory"
@@ -132,6 +135,11 @@ int main()
     EXPECT(nosa_block_scores(&p, &kv, fb, fi, fi, 8, 2048, 16384, nullptr, ws, 1 << 30, nullptr) == NOSA_ERR_NULL);
     EXPECT(nosa_block_scores(&p, &kv, fb, fi, fi, 8, 2048, 16384, ff, ws, 16, nullptr) == NOSA_ERR_WORKSPACE);
     EXPECT(nosa_select_blocks(&p, nullptr, fi, fi, 8, 2048, 16384, fi, fi, nullptr) == NOSA_ERR_NULL);
+    EXPECT(nosa_check_inputs(&p, &kv, nullptr, fi, 8, 1, 16384, nullptr, nullptr) == NOSA_ERR_NULL);
+    EXPECT(nosa_check_inputs(&p, nullptr, nullptr, fi, 8, 1, 16384, fi, nullptr) == NOSA_ERR_NULL);
+    EXPECT(nosa_check_inputs(&p, &kv, nullptr, fi, 8, 64, 16384, fi, nullptr) == NOSA_ERR_INVALID);
+    EXPECT(nosa_check_inputs(&p, &kv, nullptr, fi, 8, 1, 256 * 64 + 1, fi, nullptr) == NOSA_ERR_INVALID);
+    EXPECT(nosa_check_inputs(&bad, &kv, nullptr, fi, 8, 1, 16384, fi, nullptr) != NOSA_OK);
     EXPECT(nosa_select_blocks(&bad, ff, fi, fi, 8, 2048, 16384, fi, fi, nullptr) != NOSA_OK);
     EXPECT(nosa_sparse_attend(&p, &kv, fb, fi, fi, 8, 2048, 16384, fi, fi, nullptr, ff, ws, 1 << 30, nullptr) ==
            NOSA_ERR_NULL);

@@ -47,7 +47,7 @@ def test_timeline_build_is_a_library_of_its_own(L):
 
 
 def test_version_and_status_strings(L):
-    assert nosa.abi_version() == 4
+    assert nosa.abi_version() == 5
     for s in range(6):
         assert nosa.status_string(s)
     assert nosa.status_string(0) == "ok"

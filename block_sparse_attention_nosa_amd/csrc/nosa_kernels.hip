@@ -54,13 +54,16 @@ __device__ unsigned long long tl_stamps[3][kTlGroups][16];
         __builtin_amdgcn_sched_barrier(0);                                               \
     } while (0)
 // point 7: the role; 13: the XCD (hardware register XCC_ID); 14: HW_ID
-// (compute unit, shader array and engine of the wave)
+// (compute unit, shader array and engine of the wave); 15 (selection: set
+// when a digit level after the first runs) is cleared here, so that every
+// step of a replay leaves its own value, not one of an earlier step
 #define NOSA_TL_ROLE(launch, role)                                                       \
     do {                                                                                 \
         if (threadIdx.x == 0 && blockIdx.x < kTlGroups) {                                \
             tl_stamps[launch][blockIdx.x][7] = (role);                                   \
             tl_stamps[launch][blockIdx.x][13] = (unsigned)__builtin_amdgcn_s_getreg(30740); \
             tl_stamps[launch][blockIdx.x][14] = (unsigned)__builtin_amdgcn_s_getreg(63492); \
+            tl_stamps[launch][blockIdx.x][15] = 0;                                       \
         }                                                                                \
     } while (0)
 #else
